@@ -1,0 +1,202 @@
+"""CPU oracle for paged KV-cache attention -- TEST INFRASTRUCTURE ONLY.
+
+Only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The HIP library never calls it and shares
+no code with it.
+
+The arithmetic lives in ``pa_oracle.c`` (plain C, fp64, two-pass softmax,
+explicit per-token gather through the block table).  This file compiles it with
+gcc, wraps it with ctypes and adds numpy-level helpers that build a cache the
+way a caller would (poisoned pool, then scatter) before attending over it.
+
+Every function here follows "AI Infra入门干货总结：大模型是如何高效推理的":
+section "Paged Attention" for slots and the scatter, section "Attention
+(FlashAttention, Scaled Dot-Product Attention)" for the attention itself.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "pa_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libpa_oracle.so")
+_lib = None
+_lock = threading.Lock()
+
+F32, BF16 = 0, 1
+
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+_f64p = ctypes.POINTER(ctypes.c_double)
+
+
+def build(force: bool = True) -> str:
+    """Compile pa_oracle.c into libpa_oracle.so with gcc (OpenMP over rows)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC,
+                        "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = os.environ.get("PA_ORACLE_LIB")      # a deliberately broken build, for the pin tests
+            if not path:
+                build(force=False)
+                path = _LIB_PATH
+            L = ctypes.CDLL(path)
+            L.oracle_slot.restype = ctypes.c_int64
+            L.oracle_slot.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32]
+            L.oracle_slot_mapping.restype = None
+            L.oracle_slot_mapping.argtypes = [_i32p, ctypes.c_int64, _i32p, _i32p, ctypes.c_int64,
+                                              ctypes.c_int32, _i64p]
+            L.oracle_reshape_and_cache.restype = None
+            L.oracle_reshape_and_cache.argtypes = [
+                ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                ctypes.c_void_p, ctypes.c_void_p, _i64p, ctypes.c_int64,
+                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+            L.oracle_attention.restype = None
+            L.oracle_attention.argtypes = [
+                _f64p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+                _i32p, ctypes.c_int64, _i32p, _i32p, ctypes.c_int32,
+                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                ctypes.c_double, ctypes.c_int32, ctypes.c_int32, _f64p, ctypes.c_int64]
+            _lib = L
+    return _lib
+
+
+def _p(a, t):
+    return a.ctypes.data_as(t)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------ slots --
+def slot(bt_row, pos: int, block_size: int = 16) -> int:
+    row = _c(bt_row, np.int32)
+    return int(lib().oracle_slot(_p(row, _i32p), int(pos), int(block_size)))
+
+
+def slot_mapping(block_table, token_seq, token_pos, block_size: int = 16) -> np.ndarray:
+    bt = _c(block_table, np.int32)
+    seq = _c(token_seq, np.int32)
+    pos = _c(token_pos, np.int32)
+    out = np.empty(len(seq), np.int64)
+    lib().oracle_slot_mapping(_p(bt, _i32p), bt.shape[1], _p(seq, _i32p), _p(pos, _i32p),
+                              len(seq), int(block_size), _p(out, _i64p))
+    return out
+
+
+# ---------------------------------------------------------------- scatter --
+def reshape_and_cache(key, value, key_cache, value_cache, slots, block_size: int = 16):
+    """In-place scatter into numpy caches [num_blocks, block_size, Hkv, D].
+
+    key/value: [num_tokens, Hkv, D] in the cache's storage dtype (uint16 bf16
+    bits or float32); rows may be strided along the token axis."""
+    assert key_cache.flags.c_contiguous and value_cache.flags.c_contiguous
+    assert key.dtype == key_cache.dtype == value.dtype == value_cache.dtype
+    n = key.shape[0]
+    if n == 0:
+        return
+    hkv, d = key_cache.shape[2], key_cache.shape[3]
+    assert key.strides[1:] == (d * key.itemsize, key.itemsize)
+    assert value.strides[1:] == (d * value.itemsize, value.itemsize)
+    sm = _c(slots, np.int64)
+    lib().oracle_reshape_and_cache(
+        key.ctypes.data, key.strides[0] // key.itemsize, value.ctypes.data,
+        value.strides[0] // value.itemsize, key_cache.ctypes.data, value_cache.ctypes.data,
+        _p(sm, _i64p), n, int(block_size), hkv, d, key.itemsize)
+
+
+# -------------------------------------------------------------- attention --
+def attention(query, key_cache, value_cache, block_table, cu_query_lens, seq_lens,
+              num_heads: int, scale: float, causal: bool, return_probs: bool = False):
+    """fp64 attention over the paged cache; returns out [num_q_tokens, Hq, D]
+    (and the probability rows [num_q_tokens, Hq, max_seq_len] if asked)."""
+    dtype = BF16 if key_cache.dtype == np.uint16 else F32
+    q = query
+    assert q.dtype == key_cache.dtype and q.strides[1:] == (q.shape[2] * q.itemsize, q.itemsize)
+    bt = _c(block_table, np.int32)
+    cu = _c(cu_query_lens, np.int32)
+    sl = _c(seq_lens, np.int32)
+    nq, _, d = q.shape
+    hkv = key_cache.shape[2]
+    out = np.zeros((nq, num_heads, d), np.float64)
+    probs = None
+    pstride = 0
+    if return_probs:
+        pstride = int(sl.max()) if len(sl) else 0
+        probs = np.zeros((nq, num_heads, max(pstride, 1)), np.float64)
+    if nq:
+        lib().oracle_attention(
+            _p(out, _f64p), q.ctypes.data, q.strides[0] // q.itemsize,
+            key_cache.ctypes.data, value_cache.ctypes.data, _p(bt, _i32p), bt.shape[1],
+            _p(cu, _i32p), _p(sl, _i32p), len(sl), num_heads, hkv, d, key_cache.shape[1],
+            float(scale), int(bool(causal)), dtype,
+            _p(probs, _f64p) if probs is not None else None, pstride)
+    return (out, probs) if return_probs else out
+
+
+# ------------------------------------------------- whole-workload helpers --
+def build_cache(w, which: str = "all", caches=None):
+    """Caller-side cache construction for a workload: a NaN-poisoned pool, then
+    the scatter of the chosen tokens through slots computed from the block
+    table.  Returns (key_cache, value_cache) in storage format."""
+    if caches is None:
+        kc, vc = w.poisoned_cache(), w.poisoned_cache()
+    else:
+        kc, vc = caches
+    seq, pos = w.tokens(which)
+    if len(seq):
+        slots = slot_mapping(w.block_table, seq, pos, w.block_size)
+        k, v = w.token_kv(seq, pos)
+        reshape_and_cache(w.encode(k), w.encode(v), kc, vc, slots, w.block_size)
+    return kc, vc
+
+
+def run(w, return_probs: bool = False):
+    """Oracle output for a whole workload: [num_q_tokens, Hq, D] fp64."""
+    kc, vc = build_cache(w, "all")
+    q = w.encode(w.queries())
+    return attention(q, kc, vc, w.block_table, w.cu_query_lens, w.seq_lens, w.num_heads,
+                     w.scale, w.causal, return_probs)
+
+
+def run_sequences(w, seqs):
+    """Oracle output for a few sequences of a large workload.
+
+    The chosen sequences' blocks are relabelled into a compact pool (the result
+    does not depend on the physical block ids) so that the oracle never holds
+    the whole pool.  Returns {seq: [query_len, Hq, D] fp64}."""
+    res = {}
+    for b in seqs:
+        b = int(b)
+        L = int(w.seq_lens[b])
+        nblk = (L + w.block_size - 1) // w.block_size
+        table = np.arange(max(nblk, 1), dtype=np.int32)[None, :]
+        shape = (max(nblk, 1), w.block_size, w.num_kv_heads, w.head_dim)
+        if w.dtype == "bf16":
+            kc = np.full(shape, 0x7FC0, np.uint16)
+        else:
+            kc = np.full(shape, np.nan, np.float32)
+        vc = kc.copy()
+        k, v = w.kv(b)
+        pos = np.arange(L, dtype=np.int32)
+        slots = slot_mapping(table, np.zeros(L, np.int32), pos, w.block_size)
+        reshape_and_cache(w.encode(k), w.encode(v), kc, vc, slots, w.block_size)
+        q = w.encode(w.query(b))
+        cu = np.array([0, q.shape[0]], np.int32)
+        res[b] = attention(q, kc, vc, table, cu, np.array([L], np.int32), w.num_heads,
+                           w.scale, w.causal)
+    return res

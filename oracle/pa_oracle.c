@@ -1,0 +1,188 @@
+/*
+ * CPU oracle for paged KV-cache attention.  TEST INFRASTRUCTURE ONLY: the
+ * tests, the smoke check and the benchmark's CPU-baseline leg call it; the
+ * product path never does.  It shares no code, header or helper with the HIP
+ * library.
+ *
+ * It is the plain definition, written for a reader to check by eye:
+ *   - slot of a token: the page table lookup and the block/offset split of
+ *     "AI Infra入门干货总结：大模型是如何高效推理的", section "Paged Attention"
+ *     (slot_idx = block_idx * block_size + block_offset, worked example
+ *     block_table [5, 8, 12], position 25 -> slot 137);
+ *   - scatter: copy each new token's K and V rows into the slot its
+ *     slot_mapping entry names (same section, reshape_and_cache);
+ *   - attention: softmax(Q K^T / sqrt(d_k) + M) V per query head, with the
+ *     grouped-query map kv_head = q_head / (num_heads / num_kv_heads), the K/V
+ *     rows gathered token by token through block_table, and M the causal mask
+ *     (same article, section "Attention (FlashAttention, Scaled Dot-Product
+ *     Attention)", its formula and its step table).
+ *
+ * The softmax is the naive two-pass one (max, then exp / sum) in fp64.  There is
+ * no online softmax, no tiling and no split here: those are the GPU's
+ * reformulations and are checked against this.
+ *
+ * Inputs are the exact storage the GPU reads: dtype 0 = float32, dtype 1 =
+ * bf16 bit patterns (uint16).  Both are widened to double before any
+ * arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_F32 0
+#define ORACLE_BF16 1
+
+static double widen(const void *base, int64_t idx, int dtype)
+{
+    if (dtype == ORACLE_F32)
+        return (double)((const float *)base)[idx];
+    uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;   /* bf16 is the top half of a float32 */
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Slot of logical position `pos` of the request whose block_table row is
+ * `bt_row`: the logical block pos / block_size is looked up in the page table,
+ * then slot = physical_block * block_size + pos % block_size. */
+int64_t oracle_slot(const int32_t *bt_row, int64_t pos, int32_t block_size)
+{
+    int64_t logical_block = pos / block_size;
+    int64_t physical_block = bt_row[logical_block];
+    int64_t block_offset = pos % block_size;
+    return physical_block * block_size + block_offset;
+}
+
+/* slot_mapping for a list of (request, position) tokens.  A negative position
+ * or request marks a padding token (slot -1, skipped by the scatter); a table
+ * entry < 0 (no block allocated) also yields -1. */
+void oracle_slot_mapping(const int32_t *block_table, int64_t bt_row_stride,
+                         const int32_t *token_seq, const int32_t *token_pos, int64_t num_tokens,
+                         int32_t block_size, int64_t *slot_mapping)
+{
+    for (int64_t i = 0; i < num_tokens; i++) {
+        if (token_seq[i] < 0 || token_pos[i] < 0) {
+            slot_mapping[i] = -1;
+            continue;
+        }
+        const int32_t *row = block_table + (int64_t)token_seq[i] * bt_row_stride;
+        if (row[token_pos[i] / block_size] < 0) {
+            slot_mapping[i] = -1;
+            continue;
+        }
+        slot_mapping[i] = oracle_slot(row, token_pos[i], block_size);
+    }
+}
+
+/* reshape_and_cache: for every token with slot s >= 0, split s back into
+ * (block, offset) and copy the token's [num_kv_heads, head_dim] K row and V row
+ * into cache[block, offset, :, :].  Bit copy; nothing else in the cache
+ * changes.  Token rows are `key_stride` / `value_stride` elements apart. */
+void oracle_reshape_and_cache(const void *key, int64_t key_stride,
+                              const void *value, int64_t value_stride,
+                              void *key_cache, void *value_cache,
+                              const int64_t *slot_mapping, int64_t num_tokens,
+                              int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t elem_bytes)
+{
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    for (int64_t i = 0; i < num_tokens; i++) {
+        int64_t s = slot_mapping[i];
+        if (s < 0)
+            continue;
+        int64_t block = s / block_size;
+        int64_t offset = s % block_size;
+        int64_t dst = (block * block_size + offset) * row_elems;   /* [num_blocks, block_size, Hkv, D] */
+        memcpy((char *)key_cache + dst * elem_bytes,
+               (const char *)key + i * key_stride * elem_bytes, (size_t)(row_elems * elem_bytes));
+        memcpy((char *)value_cache + dst * elem_bytes,
+               (const char *)value + i * value_stride * elem_bytes, (size_t)(row_elems * elem_bytes));
+    }
+}
+
+/* Attention over the paged cache, one function for decode and chunked prefill.
+ *
+ * Request b has query_len_b = cu_query_lens[b+1] - cu_query_lens[b] query rows
+ * (flattened at rows cu_query_lens[b] ..) and seq_lens[b] KV tokens, this
+ * step's tokens included.  Query row j sits at absolute position
+ * seq_lens[b] - query_len_b + j; with `causal` it sees keys 0 .. that position,
+ * otherwise all seq_lens[b] keys.  A row that sees no key outputs zeros.
+ *
+ * out:   double [num_q_tokens, num_heads, head_dim]
+ * query: [num_q_tokens, num_heads, head_dim], rows q_stride elements apart
+ * key_cache, value_cache: [num_blocks, block_size, num_kv_heads, head_dim]
+ * probs (optional): the softmax row of every (query row, head), at
+ *        probs[(row * num_heads + h) * probs_stride + t]
+ */
+void oracle_attention(double *out, const void *query, int64_t q_stride,
+                      const void *key_cache, const void *value_cache,
+                      const int32_t *block_table, int64_t bt_row_stride,
+                      const int32_t *cu_query_lens, const int32_t *seq_lens, int32_t num_seqs,
+                      int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                      int32_t block_size, double scale, int32_t causal, int32_t dtype,
+                      double *probs, int64_t probs_stride)
+{
+    const int32_t group = num_heads / num_kv_heads;
+    const int64_t num_q_tokens = cu_query_lens[num_seqs];
+    const int64_t n_rows = num_q_tokens * num_heads;
+
+#pragma omp parallel for schedule(dynamic, 4)
+    for (int64_t row_head = 0; row_head < n_rows; row_head++) {
+        const int64_t row = row_head / num_heads;
+        const int32_t h = (int32_t)(row_head % num_heads);
+
+        int32_t b = 0;                                   /* request owning this query row */
+        while (cu_query_lens[b + 1] <= row)
+            b++;
+        const int64_t qlen = cu_query_lens[b + 1] - cu_query_lens[b];
+        const int64_t j = row - cu_query_lens[b];
+        const int64_t L = seq_lens[b];
+        const int64_t pos_q = L - qlen + j;
+        const int64_t n = causal ? pos_q + 1 : L;        /* keys 0 .. n-1 are visible */
+        const int32_t kvh = h / group;                   /* grouped-query head map */
+        const int32_t *bt_row = block_table + (int64_t)b * bt_row_stride;
+
+        double *o = out + row_head * head_dim;
+        for (int32_t d = 0; d < head_dim; d++)
+            o[d] = 0.0;
+        if (n <= 0)
+            continue;
+
+        double *s = (double *)malloc(sizeof(double) * (size_t)n);
+        const int64_t qbase = row * q_stride + (int64_t)h * head_dim;
+
+        /* pass 1: scores s_t = scale * <q, k_t>, with k_t gathered through the
+         * page table, and their maximum */
+        double m = -INFINITY;
+        for (int64_t t = 0; t < n; t++) {
+            int64_t blk = bt_row[t / block_size];
+            int64_t off = t % block_size;
+            int64_t kbase = ((blk * block_size + off) * num_kv_heads + kvh) * (int64_t)head_dim;
+            double dot = 0.0;
+            for (int32_t d = 0; d < head_dim; d++)
+                dot += widen(query, qbase + d, dtype) * widen(key_cache, kbase + d, dtype);
+            s[t] = scale * dot;
+            if (s[t] > m)
+                m = s[t];
+        }
+
+        /* pass 2: p_t = exp(s_t - m), l = sum p_t, out = sum p_t v_t / l */
+        double l = 0.0;
+        for (int64_t t = 0; t < n; t++) {
+            s[t] = exp(s[t] - m);
+            l += s[t];
+        }
+        for (int64_t t = 0; t < n; t++) {
+            int64_t blk = bt_row[t / block_size];
+            int64_t off = t % block_size;
+            int64_t vbase = ((blk * block_size + off) * num_kv_heads + kvh) * (int64_t)head_dim;
+            double w = s[t] / l;
+            for (int32_t d = 0; d < head_dim; d++)
+                o[d] += w * widen(value_cache, vbase + d, dtype);
+            if (probs)
+                probs[row_head * probs_stride + t] = w;
+        }
+        free(s);
+    }
+}

@@ -1,0 +1,45 @@
+"""Plant a plausible mistake in a copy of the oracle's C source, build it, and
+check that the pins in test_oracle.py catch it.  CPU only; the oracle in the
+tree is never modified."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "pa_oracle.c")
+
+MUTANTS = {
+    "gqa_head_map": ("const int32_t kvh = h / group;", "const int32_t kvh = h % num_kv_heads;"),
+    "dropped_scale": ("s[t] = scale * dot;", "s[t] = dot;"),
+    "slot_offset": ("int64_t block_offset = pos % block_size;",
+                    "int64_t block_offset = (pos + 1) % block_size;"),
+    "causal_off_by_one": ("const int64_t n = causal ? pos_q + 1 : L;",
+                          "const int64_t n = causal ? pos_q : L;"),
+    "keys_read_from_values": ("widen(key_cache, kbase + d, dtype)", "widen(value_cache, kbase + d, dtype)"),
+    "gather_offset": ("int64_t off = t % block_size;", "int64_t off = (t + 1) % block_size;"),
+    "scatter_reversed_offset": ("int64_t dst = (block * block_size + offset) * row_elems;",
+                                "int64_t dst = (block * block_size + (block_size - 1 - offset)) * row_elems;"),
+    "exp_sign": ("s[t] = exp(s[t] - m);", "s[t] = exp(m - s[t]);"),
+    "missing_normalisation": ("double w = s[t] / l;", "double w = s[t];"),
+    "transposed_query_index": ("const int64_t qbase = row * q_stride + (int64_t)h * head_dim;",
+                               "const int64_t qbase = (int64_t)h * q_stride + row * head_dim;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert old in src, f"mutation site for {name} not found"
+    mutant_c = tmp_path / "mutant.c"
+    mutant_c.write_text(src.replace(old, new, 1))
+    so = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-std=c99", str(mutant_c), "-o", str(so), "-lm"],
+                   check=True)
+    env = dict(os.environ, PA_ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        os.path.join(ROOT, "tests", "test_oracle.py")],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
