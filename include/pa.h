@@ -1,0 +1,165 @@
+/*
+ * pa.h -- C ABI of libpa.so: paged KV-cache attention for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * The operations and the tensor layouts follow the Tencent engineering article
+ * "AI Infra入门干货总结：大模型是如何高效推理的":
+ *   - section "Paged Attention": the per-layer caches
+ *     key_cache / value_cache [num_blocks, block_size, num_kv_heads, head_dim],
+ *     block_table [max_num_reqs, max_num_blocks_per_req] of physical block ids,
+ *     slot_mapping [num_tokens] of int64 slots, slot = block * block_size + offset,
+ *     and the default block_size of 16;
+ *   - section "Reshape & Cache": new K and V rows are column slices of the fused
+ *     QKV output, reshaped to [num_tokens, num_kv_heads, head_dim] and scattered
+ *     into the cache by slot_mapping before attention reads them;
+ *   - section "Attention (FlashAttention, Scaled Dot-Product Attention)":
+ *     softmax(Q K^T / sqrt(d_k) + M) V with kv_head = q_head / (num_heads /
+ *     num_kv_heads), Q [query_lens, num_heads, head_dim], K/V gathered through
+ *     block_table, seq_lens counting every KV token including this step's, the
+ *     online softmax that fuses the steps into one kernel, and Flash-Decoding's
+ *     split of the KV axis merged with log-sum-exp (its closing summary).
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller.  The library
+ *     never allocates device memory and keeps no pointer after a call returns;
+ *     buffers must stay alive until the work enqueued on `stream` completes.
+ *   - All work is enqueued on `stream` (0 = the default stream) without host
+ *     synchronisation.  Calls are ordered by the stream: a scatter must be
+ *     enqueued before the attention call that reads the tokens it writes.
+ *   - Host-side argument checks run before any launch; a failed check launches
+ *     nothing and returns a status; pa_last_error_message() gives the detail.
+ *   - The contents of device arrays are the caller's contract and are not
+ *     checked (that would need a host sync): block ids in [0, num_blocks) for
+ *     every block a sequence uses, seq_lens[b] <= max_seq_len <=
+ *     max_blocks_per_req * block_size, distinct non-negative slots in one
+ *     scatter.  Kernels still never touch memory outside the arrays they are
+ *     given for out-of-range positions, request indices or slots; they skip
+ *     such tokens instead.
+ *   - Supported now: block_size 16, head_dim 128, num_heads / num_kv_heads in
+ *     {1, 2, 4, 8}, dtype PA_F32 or PA_BF16 (Q, K, V, caches and outputs all of
+ *     that dtype; arithmetic in fp32).  Other values return PA_ERR_UNSUPPORTED.
+ *   - Functions are thread-safe; the only global state is a per-thread error
+ *     message.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_ABI_VERSION 1
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shapes, misaligned rows */
+    PA_ERR_UNSUPPORTED = 2,   /* a shape or dtype this build does not implement */
+    PA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query function's size */
+    PA_ERR_HIP = 4            /* a kernel launch failed (hipGetLastError) */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+int32_t pa_abi_version(void);
+const char *pa_status_string(pa_status status);
+/* Detail of the calling thread's last non-OK status (empty string if none). */
+const char *pa_last_error_message(void);
+
+/*
+ * pa_slot_mapping -- the page-table lookup of section "Paged Attention":
+ *   slot_mapping[i] = block_table[token_seq[i], token_pos[i] / block_size] * block_size
+ *                     + token_pos[i] % block_size
+ * for every token i (worked example on the page: row [5, 8, 12], position 25
+ * -> slot 137).
+ *
+ * slot_mapping  out, int64 [num_tokens]
+ * block_table   int32 [num_seqs, max_blocks_per_req], row-major
+ * token_seq     int32 [num_tokens]: request index of each token
+ * token_pos     int32 [num_tokens]: logical position of each token in its request
+ * A token whose request index or position is negative or out of range, or whose
+ * table entry is negative, gets slot -1 (the scatter skips it).
+ * num_tokens == 0 is a no-op.
+ */
+pa_status pa_slot_mapping(int64_t *slot_mapping, const int32_t *block_table,
+                          int32_t max_blocks_per_req, int32_t num_seqs,
+                          const int32_t *token_seq, const int32_t *token_pos,
+                          int64_t num_tokens, int32_t block_size, hipStream_t stream);
+
+/*
+ * pa_reshape_and_cache -- the scatter of section "Paged Attention" /
+ * "Reshape & Cache": for each token i with s = slot_mapping[i] >= 0, copy
+ *   key[i, :, :]   -> key_cache[s / block_size, s % block_size, :, :]
+ *   value[i, :, :] -> value_cache[s / block_size, s % block_size, :, :]
+ * bit for bit.  Slots < 0 (padding) and slots >= num_blocks * block_size are
+ * skipped.
+ *
+ * key, value      [num_tokens, num_kv_heads, head_dim]; token rows are
+ *                 key_token_stride / value_token_stride ELEMENTS apart (e.g. the
+ *                 K and V column slices of a [num_tokens, 6144] fused QKV
+ *                 output); heads and dims are contiguous.  Row starts must be
+ *                 16-byte aligned.
+ * key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim], contiguous
+ */
+pa_status pa_reshape_and_cache(const void *key, int64_t key_token_stride,
+                               const void *value, int64_t value_token_stride,
+                               void *key_cache, void *value_cache,
+                               const int64_t *slot_mapping, int64_t num_tokens,
+                               int64_t num_blocks, int32_t block_size,
+                               int32_t num_kv_heads, int32_t head_dim,
+                               pa_dtype dtype, hipStream_t stream);
+
+/*
+ * Workspace bytes pa_decode needs for these arguments (0 when no sequence is
+ * split).  Same partition rule as pa_decode: partition_tokens > 0 is used as
+ * given (a multiple of block_size), 0 picks a size from the shapes, -1 never
+ * splits.
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len,
+                                 int32_t partition_tokens);
+
+/* Partition size pa_decode will use for these arguments (tokens per split). */
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads,
+                                   int32_t max_seq_len, int32_t partition_tokens);
+
+/*
+ * pa_decode -- one query token per sequence (query_lens = 1) attending to all
+ * seq_lens[b] tokens of its paged K/V:
+ *   out[b, h, :] = sum_t softmax_t(scale * <q[b, h], k_t>) v_t,
+ *   k_t, v_t = cache[block_table[b, t / 16], t % 16, h / (num_heads / num_kv_heads), :]
+ * computed in one pass with the online softmax (running max and sum, rescaled
+ * by exp(m_old - m_new)).  A sequence longer than the partition size is split
+ * into partitions whose partial (max, sum, unnormalised output) are merged with
+ * log-sum-exp weights in a second kernel.  seq_lens[b] == 0 gives zeros.
+ *
+ * out          [num_seqs, num_heads, head_dim], contiguous, dtype
+ * query        [num_seqs, num_heads, head_dim]; token rows q_token_stride
+ *              ELEMENTS apart, heads and dims contiguous, rows 16-byte aligned
+ * key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim]
+ * block_table  int32 [num_seqs, max_blocks_per_req]
+ * seq_lens     int32 [num_seqs], this step's token included
+ * max_seq_len  host-side upper bound of seq_lens (sizes the grid)
+ * workspace    device scratch of at least pa_decode_workspace_bytes(...) bytes
+ *              (may be NULL when that is 0); its contents need no
+ *              initialisation and are overwritten.
+ */
+pa_status pa_decode(void *out, const void *query, int64_t q_token_stride,
+                    const void *key_cache, const void *value_cache,
+                    const int32_t *block_table, int32_t max_blocks_per_req,
+                    const int32_t *seq_lens, int32_t num_seqs,
+                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t block_size, int64_t num_blocks, float scale,
+                    int32_t max_seq_len, int32_t partition_tokens,
+                    void *workspace, size_t workspace_bytes,
+                    pa_dtype dtype, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,210 @@
+"""Python binding of libpa.so, the MI355X (gfx950) paged KV-cache attention library.
+
+Argument marshalling only: every function here checks the tensors it is
+handed, turns them into device pointers, sizes and the current HIP stream,
+and calls the C entry point of the same name (declared in include/pa.h).  All
+computation happens in the library's kernels; PyTorch only provides device
+memory and streams.  There is no fallback: if libpa.so is missing the first
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
+    "pa_slot_mapping", "pa_reshape_and_cache", "pa_decode_workspace_bytes",
+    "pa_decode_partition_tokens", "pa_decode", "decode_workspace",
+]
+
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
+PA_F32, PA_BF16 = 0, 1
+BLOCK_SIZE = 16
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+_lock = threading.Lock()
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        self.status = status
+        super().__init__(f"{fn}: {_status_name(status)}: {detail}")
+
+
+def lib_path() -> str:
+    return os.path.join(_DIR, "libpa.so")
+
+
+def lib():
+    """Load libpa.so (built in tree by __graft_entry__.build())."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run __graft_entry__.build() "
+                               "(or python paged_kv_cache_432_amd/_build.py)")
+        L = ctypes.CDLL(path)
+        L.pa_abi_version.restype = _i32
+        L.pa_abi_version.argtypes = []
+        L.pa_status_string.restype = ctypes.c_char_p
+        L.pa_status_string.argtypes = [ctypes.c_int]
+        L.pa_last_error_message.restype = ctypes.c_char_p
+        L.pa_last_error_message.argtypes = []
+        L.pa_slot_mapping.restype = ctypes.c_int
+        L.pa_slot_mapping.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _i64, _i32, _vp]
+        L.pa_reshape_and_cache.restype = ctypes.c_int
+        L.pa_reshape_and_cache.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32,
+                                           _i32, _i32, ctypes.c_int, _vp]
+        L.pa_decode_workspace_bytes.restype = ctypes.c_size_t
+        L.pa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+        L.pa_decode_partition_tokens.restype = _i32
+        L.pa_decode_partition_tokens.argtypes = [_i32, _i32, _i32, _i32]
+        L.pa_decode.restype = ctypes.c_int
+        L.pa_decode.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                _i32, _i64, ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t,
+                                ctypes.c_int, _vp]
+        _lib = L
+        return L
+
+
+def _status_name(s: int) -> str:
+    try:
+        return lib().pa_status_string(int(s)).decode()
+    except Exception:                                     # noqa: BLE001 -- message only
+        return f"status {s}"
+
+
+def _check(status: int, fn: str) -> None:
+    if status != PA_OK:
+        raise PaError(status, fn, lib().pa_last_error_message().decode())
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream) if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else int(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PA_BF16
+    if t.dtype == torch.float32:
+        return PA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def pa_abi_version() -> int:
+    return int(lib().pa_abi_version())
+
+
+def pa_status_string(status: int) -> str:
+    return lib().pa_status_string(int(status)).decode()
+
+
+def pa_last_error_message() -> str:
+    return lib().pa_last_error_message().decode()
+
+
+# ------------------------------------------------------------ entry points --
+def pa_slot_mapping(slot_mapping: torch.Tensor, block_table: torch.Tensor, token_seq: torch.Tensor,
+                    token_pos: torch.Tensor, block_size: int = BLOCK_SIZE, stream=None) -> torch.Tensor:
+    """slot_mapping[i] = block_table[token_seq[i], token_pos[i] // 16] * 16 + token_pos[i] % 16
+    (int64 out), -1 for padding or unallocated tokens."""
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous(), "slot_mapping: contiguous int64")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
+          "block_table: contiguous int32 [num_seqs, max_blocks_per_req]")
+    _need(token_seq.dtype == torch.int32 and token_pos.dtype == torch.int32, "token_seq/token_pos: int32")
+    _need(token_seq.is_contiguous() and token_pos.is_contiguous(), "token_seq/token_pos: contiguous")
+    n = slot_mapping.numel()
+    _need(token_seq.numel() == n and token_pos.numel() == n, "token lists of different lengths")
+    s = lib().pa_slot_mapping(_ptr(slot_mapping), _ptr(block_table), block_table.shape[1],
+                              block_table.shape[0], _ptr(token_seq), _ptr(token_pos), n, block_size,
+                              _stream(stream, slot_mapping.device))
+    _check(s, "pa_slot_mapping")
+    return slot_mapping
+
+
+def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                         value_cache: torch.Tensor, slot_mapping: torch.Tensor, stream=None) -> None:
+    """Scatter key/value [num_tokens, Hkv, D] (token stride free, e.g. QKV column
+    slices) into caches [num_blocks, 16, Hkv, D] at slot_mapping (int64)."""
+    _need(key.dim() == 3 and value.dim() == 3 and key.shape == value.shape, "key/value: [num_tokens, Hkv, D]")
+    _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
+    _need(key.dtype == value.dtype == key_cache.dtype == value_cache.dtype, "dtype mismatch")
+    n, hkv, d = key.shape
+    _need(key_cache.shape[2] == hkv and key_cache.shape[3] == d, "cache head shape differs from key")
+    _need(key.stride(2) == 1 and key.stride(1) == d and value.stride(2) == 1 and value.stride(1) == d,
+          "key/value heads and dims must be contiguous")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == n and slot_mapping.is_contiguous(),
+          "slot_mapping: contiguous int64 [num_tokens]")
+    s = lib().pa_reshape_and_cache(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
+                                   _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), n,
+                                   key_cache.shape[0], key_cache.shape[1], hkv, d, _dtype_code(key),
+                                   _stream(stream, key_cache.device))
+    _check(s, "pa_reshape_and_cache")
+
+
+def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                              max_seq_len: int, partition_tokens: int = 0) -> int:
+    return int(lib().pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                               max_seq_len, partition_tokens))
+
+
+def pa_decode_partition_tokens(num_seqs: int, num_kv_heads: int, max_seq_len: int,
+                               partition_tokens: int = 0) -> int:
+    return int(lib().pa_decode_partition_tokens(num_seqs, num_kv_heads, max_seq_len, partition_tokens))
+
+
+def decode_workspace(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                     max_seq_len: int, partition_tokens: int = 0, device="cuda") -> torch.Tensor | None:
+    """Allocate (with torch) the scratch pa_decode needs, or None if it needs none."""
+    nbytes = pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len,
+                                       partition_tokens)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+              block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float, max_seq_len: int,
+              partition_tokens: int = 0, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention: out [B, Hq, D] for query [B, Hq, D] (one token per sequence)."""
+    _need(query.dim() == 3 and out.shape == query.shape and out.is_contiguous(),
+          "query/out: [num_seqs, num_heads, head_dim], out contiguous")
+    _need(query.stride(2) == 1 and query.stride(1) == query.shape[2], "query heads/dims must be contiguous")
+    _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
+    _need(query.dtype == out.dtype == key_cache.dtype == value_cache.dtype, "dtype mismatch")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
+          "block_table: contiguous int32 [num_seqs, max_blocks_per_req]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.is_contiguous(), "seq_lens: contiguous int32")
+    b, hq, d = query.shape
+    _need(block_table.shape[0] >= b and seq_lens.numel() >= b, "block_table/seq_lens shorter than batch")
+    nb, bs, hkv, _ = key_cache.shape
+    ws = workspace
+    s = lib().pa_decode(_ptr(out), _ptr(query), query.stride(0), _ptr(key_cache), _ptr(value_cache),
+                        _ptr(block_table), block_table.shape[1], _ptr(seq_lens), b, hq, hkv, d, bs, nb,
+                        float(scale), int(max_seq_len), int(partition_tokens), _ptr(ws),
+                        0 if ws is None else ws.numel() * ws.element_size(), _dtype_code(query),
+                        _stream(stream, out.device))
+    _check(s, "pa_decode")
+    return out

@@ -1,0 +1,49 @@
+"""Build libpa.so (the HIP kernels and the C ABI) for gfx950 with hipcc, in tree."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB = os.path.join(PKG, "libpa.so")
+
+SOURCES = ["abi.cpp", "cache_kernels.hip", "decode_kernel.hip"]
+
+# Packed fp32 VALU ops are disabled for all device code: scalar and float2 code
+# is compiled to plain v_fma/v_mul/v_add.
+DEVICE_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-munsafe-fp-atomics"]
+
+
+def hipcc() -> str:
+    for cand in (shutil.which("hipcc"), "/opt/rocm/bin/hipcc"):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found (ROCm is required to build libpa.so)")
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source into paged_kv_cache_432_amd/libpa.so; returns its path."""
+    tmp = LIB + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *DEVICE_FLAGS, *(extra_flags or []), "-shared", f"-I{INCLUDE}", f"-I{CSRC}",
+           "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    msgs = "\n".join(x for x in (r.stdout + r.stderr).splitlines()
+                     if "packed-fp32-ops' is not a recognized feature" not in x)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
+    if verbose and msgs.strip():
+        print(msgs)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

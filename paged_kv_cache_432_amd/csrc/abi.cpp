@@ -1,0 +1,212 @@
+// C ABI of libpa.so: argument checks, partition choice, workspace layout and
+// dispatch to the gfx950 kernels.  Declarations and the contract are in
+// include/pa.h.
+#include "pa.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+pa_status fail(pa_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pa_status ok() {
+    g_err[0] = '\0';
+    return PA_OK;
+}
+
+pa_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
+
+// Tokens per partition.  An explicit size is used as given; 0 picks one from
+// the shapes: the smallest of 256 / 512 / 1024 tokens that still gives every
+// compute unit several waves at the longest sequence; -1 (or a size at least
+// max_seq_len) keeps every sequence in one partition.
+int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                         int32_t requested) {
+    const int32_t whole = max_seq_len > 0 ? ((max_seq_len + 15) / 16) * 16 : 16;
+    if (requested < 0) return whole;
+    if (requested > 0) return requested < whole ? requested : whole;
+    const int64_t units = (int64_t)num_seqs * num_kv_heads;
+    int32_t pt = 256;
+    while (pt < 1024 && units * ((max_seq_len + pt - 1) / pt) > 16384) pt *= 2;
+    return pt < whole ? pt : whole;
+}
+
+int32_t num_partitions(int32_t max_seq_len, int32_t pt) {
+    return max_seq_len <= 0 ? 1 : (max_seq_len + pt - 1) / pt;
+}
+
+size_t decode_ws_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t nparts) {
+    if (nparts <= 1) return 0;
+    const size_t rows = (size_t)num_seqs * num_heads * nparts;
+    const size_t acc = rows * head_dim * sizeof(float);
+    const size_t acc_aligned = (acc + 255) & ~(size_t)255;
+    return acc_aligned + rows * 2 * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_abi_version(void) { return PA_ABI_VERSION; }
+
+const char* pa_status_string(pa_status s) {
+    switch (s) {
+        case PA_OK: return "PA_OK";
+        case PA_ERR_INVALID_ARG: return "PA_ERR_INVALID_ARG";
+        case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+        case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
+        case PA_ERR_HIP: return "PA_ERR_HIP";
+    }
+    return "PA_ERR_UNKNOWN";
+}
+
+const char* pa_last_error_message(void) { return g_err; }
+
+pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
+                          int32_t max_blocks_per_req, int32_t num_seqs,
+                          const int32_t* token_seq, const int32_t* token_pos,
+                          int64_t num_tokens, int32_t block_size, hipStream_t stream) {
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens < 0");
+    if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
+    if (num_tokens == 0) return ok();
+    if (!slot_mapping || !token_seq || !token_pos) return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (num_seqs < 0 || max_blocks_per_req < 0) return fail(PA_ERR_INVALID_ARG, "negative table shape");
+    if (num_seqs > 0 && max_blocks_per_req > 0 && !block_table)
+        return fail(PA_ERR_INVALID_ARG, "null block_table");
+    if (num_tokens > ((int64_t)1 << 31) * 256 - 1) return fail(PA_ERR_INVALID_ARG, "num_tokens too large");
+    return hip_status(pa::launch_slot_mapping(slot_mapping, block_table, max_blocks_per_req, num_seqs,
+                                              token_seq, token_pos, num_tokens, stream),
+                      "slot_mapping launch");
+}
+
+pa_status pa_reshape_and_cache(const void* key, int64_t key_token_stride, const void* value,
+                               int64_t value_token_stride, void* key_cache, void* value_cache,
+                               const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                               int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                               pa_dtype dtype, hipStream_t stream) {
+    if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
+    if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size");
+    if (num_tokens == 0) return ok();
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t row_bytes = row_elems * eb;
+    if (row_bytes % 16 != 0 || row_bytes > (1 << 30))
+        return fail(PA_ERR_UNSUPPORTED, "row of %lld bytes (must be a multiple of 16)", (long long)row_bytes);
+    if (key_token_stride < row_elems || value_token_stride < row_elems)
+        return fail(PA_ERR_INVALID_ARG, "token stride smaller than num_kv_heads * head_dim");
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        (key_token_stride * eb) % 16 || (value_token_stride * eb) % 16)
+        return fail(PA_ERR_INVALID_ARG, "rows must start on 16-byte boundaries");
+    if (num_tokens > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "num_tokens too large");
+    return hip_status(pa::launch_reshape_and_cache(key, key_token_stride * eb, value,
+                                                   value_token_stride * eb, key_cache, value_cache,
+                                                   slot_mapping, num_tokens, num_blocks * 16,
+                                                   (int32_t)row_bytes, stream),
+                      "reshape_and_cache launch");
+}
+
+int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
+                                   int32_t partition_tokens) {
+    return choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                 int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens) {
+    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+    const int32_t pt = choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+    return decode_ws_bytes(num_seqs, num_heads, head_dim, num_partitions(max_seq_len, pt));
+}
+
+pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+                    const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                    int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, pa_dtype dtype, hipStream_t stream) {
+    if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
+    if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (only 128)", head_dim);
+    if (num_seqs < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_req < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative size");
+    if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads)
+        return fail(PA_ERR_INVALID_ARG, "num_heads %d not a multiple of num_kv_heads %d", num_heads,
+                    num_kv_heads);
+    const int32_t group = num_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return fail(PA_ERR_UNSUPPORTED, "group size %d (supported: 1, 2, 4, 8)", group);
+    if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % 16))
+        return fail(PA_ERR_INVALID_ARG, "partition_tokens %d (0, -1 or a positive multiple of 16)",
+                    partition_tokens);
+    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
+        return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
+    if (num_seqs == 0) return ok();
+    if (num_blocks == 0 && max_seq_len > 0) return fail(PA_ERR_INVALID_ARG, "empty cache pool");
+    if (!out || !query || !seq_lens || !key_cache || !value_cache || (max_seq_len > 0 && !block_table))
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    const int64_t eb = elem_bytes(dtype);
+    if (q_token_stride < (int64_t)num_heads * head_dim)
+        return fail(PA_ERR_INVALID_ARG, "q_token_stride smaller than num_heads * head_dim");
+    if (!aligned16(query) || (q_token_stride * eb) % 16 || !aligned16(out) || !aligned16(key_cache) ||
+        !aligned16(value_cache))
+        return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
+
+    const int32_t pt = choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+    const int32_t nparts = num_partitions(max_seq_len, pt);
+    const size_t need = decode_ws_bytes(num_seqs, num_heads, head_dim, nparts);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0,
+                    need);
+    if (need > 0 && !aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+    const int64_t items = (int64_t)num_seqs * nparts * num_kv_heads;
+    if ((items + 3) / 4 > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "grid too large");
+
+    pa::DecodeArgs a{};
+    a.out = out;
+    a.query = query;
+    a.q_stride = q_token_stride;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.block_table = block_table;
+    a.bt_stride = max_blocks_per_req;
+    a.num_blocks = num_blocks;
+    a.seq_lens = seq_lens;
+    a.num_seqs = num_seqs;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.partition_tokens = pt;
+    a.max_partitions = nparts;
+    if (need > 0) {
+        const size_t rows = (size_t)num_seqs * num_heads * nparts;
+        const size_t acc_aligned = (rows * head_dim * sizeof(float) + 255) & ~(size_t)255;
+        a.part_acc = reinterpret_cast<float*>(workspace);
+        a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + acc_aligned);
+    }
+    return hip_status(pa::launch_decode(a, dtype == PA_BF16 ? 1 : 0, group, stream), "decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Device helpers shared by the gfx950 kernels of libpa.so: element storage
+// types, 8-element chunks (one 16-byte or two 16-byte loads per lane), bf16
+// conversions and wave-level lane exchanges.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+constexpr int kWave = 64;        // CDNA wavefront width
+constexpr int kBlock = 16;       // tokens per physical cache block
+constexpr int kHeadDim = 128;    // head_dim this build implements
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 a = (__bf16)lo, b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Eight consecutive elements of one K/V/Q row, as one lane holds them.
+struct ChunkBF16 {
+    u32x4_t w;                                   // 8 x bf16 = 16 bytes
+    static constexpr int kBytes = 16;
+};
+struct ChunkF32 {
+    f32x4_t a, b;                                // 8 x fp32 = 32 bytes
+    static constexpr int kBytes = 32;
+};
+
+template <bool NT>
+__device__ __forceinline__ void load_chunk(ChunkBF16& c, const void* p) {
+    if constexpr (NT) c.w = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+    else c.w = *reinterpret_cast<const u32x4_t*>(p);
+}
+template <bool NT>
+__device__ __forceinline__ void load_chunk(ChunkF32& c, const void* p) {
+    const f32x4_t* q = reinterpret_cast<const f32x4_t*>(p);
+    if constexpr (NT) { c.a = __builtin_nontemporal_load(q); c.b = __builtin_nontemporal_load(q + 1); }
+    else { c.a = q[0]; c.b = q[1]; }
+}
+
+__device__ __forceinline__ void to_f32(const ChunkBF16& c, float f[8]) {
+    f[0] = bf16_lo(c.w.x); f[1] = bf16_hi(c.w.x);
+    f[2] = bf16_lo(c.w.y); f[3] = bf16_hi(c.w.y);
+    f[4] = bf16_lo(c.w.z); f[5] = bf16_hi(c.w.z);
+    f[6] = bf16_lo(c.w.w); f[7] = bf16_hi(c.w.w);
+}
+__device__ __forceinline__ void to_f32(const ChunkF32& c, float f[8]) {
+    f[0] = c.a.x; f[1] = c.a.y; f[2] = c.a.z; f[3] = c.a.w;
+    f[4] = c.b.x; f[5] = c.b.y; f[6] = c.b.z; f[7] = c.b.w;
+}
+
+// <q, k> over one chunk, accumulated into acc.  bf16 products are exact in
+// fp32; v_dot2_f32_bf16 adds two of them per instruction.
+__device__ __forceinline__ float dot_chunk(const ChunkBF16& q, const ChunkBF16& k, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.x),
+                                          __builtin_bit_cast(bf16x2_t, k.w.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.y),
+                                          __builtin_bit_cast(bf16x2_t, k.w.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.z),
+                                          __builtin_bit_cast(bf16x2_t, k.w.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.w),
+                                          __builtin_bit_cast(bf16x2_t, k.w.w), acc, false);
+    return acc;
+}
+__device__ __forceinline__ float dot_chunk(const ChunkF32& q, const ChunkF32& k, float acc) {
+    acc = fmaf(q.a.x, k.a.x, acc); acc = fmaf(q.a.y, k.a.y, acc);
+    acc = fmaf(q.a.z, k.a.z, acc); acc = fmaf(q.a.w, k.a.w, acc);
+    acc = fmaf(q.b.x, k.b.x, acc); acc = fmaf(q.b.y, k.b.y, acc);
+    acc = fmaf(q.b.z, k.b.z, acc); acc = fmaf(q.b.w, k.b.w, acc);
+    return acc;
+}
+
+// Store eight fp32 values as one row chunk of the output dtype.
+__device__ __forceinline__ void store_chunk(uint16_t* p, const float f[8]) {
+    u32x4_t w;
+    w.x = pack_bf16x2(f[0], f[1]); w.y = pack_bf16x2(f[2], f[3]);
+    w.z = pack_bf16x2(f[4], f[5]); w.w = pack_bf16x2(f[6], f[7]);
+    *reinterpret_cast<u32x4_t*>(p) = w;
+}
+__device__ __forceinline__ void store_chunk(float* p, const float f[8]) {
+    reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{f[0], f[1], f[2], f[3]};
+    reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{f[4], f[5], f[6], f[7]};
+}
+
+// ---- lane exchanges ---------------------------------------------------------
+// DPP controls (CDNA): quad_perm selects within groups of 4 lanes, row_ror
+// rotates within rows of 16 lanes.
+constexpr int kQuadSwap1 = 0xB1;   // quad_perm [1,0,3,2]: partner lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;   // quad_perm [2,3,0,1]: partner lane ^ 2
+constexpr int kRowRor4 = 0x124;
+constexpr int kRowRor8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float shfl_xor_f(float x, int mask) {
+    int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+__device__ __forceinline__ float readlane_f(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+}  // namespace pa

@@ -1,0 +1,92 @@
+"""Caller-side staging of a synthetic workload on the GPU.
+
+This plays the part of an inference engine around the library: it uploads a
+workload's inputs (block tables, lengths, queries, the K/V rows of every
+token) and builds the paged cache the way an engine does, by computing slots
+with ``pa_slot_mapping`` and writing rows with ``pa_reshape_and_cache``.  The
+earlier context of every sequence is written once, before any timing; the
+step itself then scatters only this step's tokens and attends.  Torch is used
+for allocation and uploads only.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import (decode_workspace, pa_decode, pa_reshape_and_cache, pa_slot_mapping)
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
+
+
+def _upload(x: np.ndarray, dtype, device) -> torch.Tensor:
+    # values drawn for a bf16 workload are exactly representable: the cast is exact
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device).to(dtype)
+
+
+class DeviceWorkload:
+    """Device-resident inputs and paged cache of one workload step."""
+
+    def __init__(self, w, device="cuda", fill_history: bool = True, poison: bool = True):
+        self.w = w
+        self.device = torch.device(device)
+        self.dtype = _TORCH_DTYPE[w.dtype]
+        shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+        fill = float("nan") if poison else 0.0
+        self.key_cache = torch.full(shape, fill, dtype=self.dtype, device=self.device)
+        self.value_cache = torch.full(shape, fill, dtype=self.dtype, device=self.device)
+        self.block_table = torch.from_numpy(np.ascontiguousarray(w.block_table, np.int32)).to(self.device)
+        self.seq_lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens, np.int32)).to(self.device)
+        self.cu_query_lens = torch.from_numpy(w.cu_query_lens).to(self.device)
+        self.query = _upload(w.queries(), self.dtype, self.device)
+        seq, pos = w.tokens("new")
+        self.new_seq = torch.from_numpy(seq).to(self.device)
+        self.new_pos = torch.from_numpy(pos).to(self.device)
+        self.slot_mapping = torch.empty(len(seq), dtype=torch.int64, device=self.device)
+        n, hkv, d = len(seq), w.num_kv_heads, w.head_dim
+        new_k = np.empty((n, hkv, d), np.float32)
+        new_v = np.empty((n, hkv, d), np.float32)
+        cursor = 0
+        for b in range(w.num_seqs):
+            h, L = int(w.history_lens[b]), int(w.seq_lens[b])
+            if L == 0:
+                continue
+            k, v = w.kv(b)
+            if fill_history and h > 0:
+                self._write(b, k[:h], v[:h], 0)
+            q = L - h
+            new_k[cursor:cursor + q] = k[h:L]
+            new_v[cursor:cursor + q] = v[h:L]
+            cursor += q
+        assert cursor == n
+        self.new_k = _upload(new_k, self.dtype, self.device)
+        self.new_v = _upload(new_v, self.dtype, self.device)
+
+    def _write(self, b: int, k: np.ndarray, v: np.ndarray, start: int) -> None:
+        n = k.shape[0]
+        seq = torch.full((n,), b, dtype=torch.int32, device=self.device)
+        pos = torch.arange(start, start + n, dtype=torch.int32, device=self.device)
+        slots = torch.empty(n, dtype=torch.int64, device=self.device)
+        pa_slot_mapping(slots, self.block_table, seq, pos)
+        pa_reshape_and_cache(_upload(k, self.dtype, self.device), _upload(v, self.dtype, self.device),
+                             self.key_cache, self.value_cache, slots)
+
+    # ---- the step
+    def scatter_new(self, stream=None) -> None:
+        """Rows a1-a2 of the step: slots of this step's tokens, then their scatter."""
+        pa_slot_mapping(self.slot_mapping, self.block_table, self.new_seq, self.new_pos, stream=stream)
+        pa_reshape_and_cache(self.new_k, self.new_v, self.key_cache, self.value_cache,
+                             self.slot_mapping, stream=stream)
+
+    def decode_workspace(self, partition_tokens: int = 0):
+        w = self.w
+        return decode_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq_len,
+                                partition_tokens, device=self.device)
+
+    def decode(self, out=None, partition_tokens: int = 0, workspace=None, stream=None) -> torch.Tensor:
+        w = self.w
+        if out is None:
+            out = torch.empty_like(self.query)
+        if workspace is None:
+            workspace = self.decode_workspace(partition_tokens)
+        return pa_decode(out, self.query, self.key_cache, self.value_cache, self.block_table,
+                         self.seq_lens, w.scale, w.max_seq_len, partition_tokens, workspace, stream)

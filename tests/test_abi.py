@@ -1,0 +1,92 @@
+"""The C ABI without a GPU: libpa.so loads, exports every function include/pa.h
+declares, and its host-side argument checks answer before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_cache_432_amd as pa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "pa.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(pa.lib_path()):
+        import __graft_entry__
+        __graft_entry__.build()
+    return pa.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = _declared()
+    assert {"pa_slot_mapping", "pa_reshape_and_cache", "pa_decode"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libpa.so does not export {n}"
+    assert pa.pa_abi_version() == 1
+
+
+def test_status_strings(L):
+    assert pa.pa_status_string(0) == "PA_OK"
+    assert pa.pa_status_string(3) == "PA_ERR_WORKSPACE"
+
+
+def _decode(L, **kw):
+    args = dict(out=16, query=16, q_token_stride=4096, key_cache=16, value_cache=16, block_table=16,
+                max_blocks_per_req=8, seq_lens=16, num_seqs=2, num_heads=32, num_kv_heads=8,
+                head_dim=128, block_size=16, num_blocks=10, scale=0.088, max_seq_len=100,
+                partition_tokens=0, workspace=None, workspace_bytes=0, dtype=1, stream=None)
+    args.update(kw)
+    return L.pa_decode(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_heads=24, num_kv_heads=8), pa.PA_ERR_UNSUPPORTED),       # group 3
+    (dict(num_heads=30, num_kv_heads=8), pa.PA_ERR_INVALID_ARG),       # not a multiple
+    (dict(dtype=7), pa.PA_ERR_UNSUPPORTED),
+    (dict(out=None), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=100), pa.PA_ERR_INVALID_ARG),               # not a multiple of 16
+    (dict(max_seq_len=200), pa.PA_ERR_INVALID_ARG),                    # beyond the table
+    (dict(q_token_stride=100), pa.PA_ERR_INVALID_ARG),
+    (dict(query=24), pa.PA_ERR_INVALID_ARG),                           # misaligned
+    (dict(scale=float("nan")), pa.PA_ERR_INVALID_ARG),
+    (dict(partition_tokens=32), pa.PA_ERR_WORKSPACE),                  # split without workspace
+    (dict(num_seqs=-1), pa.PA_ERR_INVALID_ARG),
+])
+def test_decode_rejects_before_launch(L, kw, status):
+    assert _decode(L, **kw) == status
+    assert pa.pa_last_error_message()
+
+
+def test_decode_empty_batch_is_ok(L):
+    assert _decode(L, num_seqs=0) == pa.PA_OK
+
+
+def test_workspace_query(L):
+    assert pa.pa_decode_workspace_bytes(4, 32, 8, 128, 100, -1) == 0
+    assert pa.pa_decode_workspace_bytes(4, 32, 8, 128, 100, 16) > 0
+    pt = pa.pa_decode_partition_tokens(64, 8, 8192, 0)
+    assert pt % 16 == 0 and 256 <= pt <= 1024
+    nparts = -(-8192 // pt)
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 8192, 0) >= 64 * 32 * nparts * 130 * 4
+    assert pa.pa_decode_partition_tokens(4, 8, 100, -1) == 112
+
+
+def test_scatter_and_slot_checks(L):
+    # every call here fails its checks (or is empty) and so launches nothing
+    assert L.pa_reshape_and_cache(16, 1024, 16, 1024, 16, 16, 16, 0, 10, 16, 8, 128, 1, None) == pa.PA_OK
+    assert L.pa_reshape_and_cache(16, 1000, 16, 1024, 16, 16, 16, 5, 10, 16, 8, 128, 1, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_reshape_and_cache(16, 1024, 16, 1024, 16, 16, 16, 5, 10, 8, 8, 128, 1, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_reshape_and_cache(None, 1024, 16, 1024, 16, 16, 16, 5, 10, 16, 8, 128, 1, None) == pa.PA_ERR_INVALID_ARG
+    assert L.pa_slot_mapping(16, 16, 4, 2, 16, 16, 0, 16, None) == pa.PA_OK
+    assert L.pa_slot_mapping(16, 16, 4, 2, 16, 16, 3, 8, None) == pa.PA_ERR_UNSUPPORTED
+    assert L.pa_slot_mapping(None, 16, 4, 2, 16, 16, 3, 16, None) == pa.PA_ERR_INVALID_ARG

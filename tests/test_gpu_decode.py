@@ -1,0 +1,128 @@
+"""Rows a3-a9 on the GPU: paged decode attention (single pass and split +
+merge) against the oracle, element by element at small sizes and on sampled
+sequences at the full workload sizes."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import assert_parity, storage_bits, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def staging():
+    import paged_kv_cache_432_amd as pa
+    pa.lib()
+    from paged_kv_cache_432_amd import staging
+    return staging
+
+
+def _run(staging, w, partition_tokens=0):
+    dw = staging.DeviceWorkload(w)
+    dw.scatter_new()
+    out = dw.decode(partition_tokens=partition_tokens)
+    torch.cuda.synchronize()
+    return dw, out
+
+
+@pytest.mark.parametrize("step", ["A", "B"])
+@pytest.mark.parametrize("pt", [-1, 0, 16, 32])
+def test_tiny_fp32(staging, step, pt):
+    w = W.tiny(step)
+    _, out = _run(staging, w, pt)
+    assert_parity(to_numpy(out), oracle.run(w), "f32", f"tiny{step} pt={pt}")
+
+
+RAGGED = [1, 2, 15, 16, 17, 31, 33, 100, 255, 256, 257, 1000, 1024, 2049, 4095]
+
+
+@pytest.mark.parametrize("pt", [-1, 0, 16, 256, 512, 2048])
+def test_ragged_bf16(staging, pt):
+    w = W.custom("ragged", seq_lens=RAGGED, dtype="bf16", seed=31, sigma=1.0)
+    _, out = _run(staging, w, pt)
+    assert_parity(to_numpy(out), oracle.run(w), "bf16", f"ragged pt={pt}")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("hq,hkv", [(8, 8), (8, 4), (8, 2), (8, 1), (32, 4), (64, 8), (16, 16)])
+def test_group_sizes(staging, dtype, hq, hkv):
+    w = W.custom("gqa", seq_lens=[5, 64, 130, 700], num_heads=hq, num_kv_heads=hkv, dtype=dtype,
+                 seed=hq + hkv)
+    for pt in (-1, 64):
+        _, out = _run(staging, w, pt)
+        assert_parity(to_numpy(out), oracle.run(w), dtype, f"G={hq // hkv} Hkv={hkv} pt={pt}")
+
+
+def test_padding_sequences_output_zero(staging):
+    w = W.custom("pad", seq_lens=[0, 40, 0, 300], dtype="bf16", seed=3)
+    for pt in (-1, 64):
+        _, out = _run(staging, w, pt)
+        o = to_numpy(out)
+        assert np.all(o[0] == 0) and np.all(o[2] == 0)
+        assert_parity(o, oracle.run(w), "bf16", f"padding pt={pt}")
+
+
+def test_deterministic_and_permutation_invariant(staging):
+    w = W.custom("perm", seq_lens=[77, 300, 1234, 16], dtype="bf16", seed=5, num_blocks=200)
+    dw, out1 = _run(staging, w, 128)
+    out2 = dw.decode(partition_tokens=128)
+    torch.cuda.synchronize()
+    assert np.array_equal(storage_bits(out1), storage_bits(out2))
+    perm = np.random.default_rng(1).permutation(300)
+    table = np.where(w.block_table >= 0, perm[np.maximum(w.block_table, 0)], -1)
+    _, out3 = _run(staging, w.with_block_table(table, num_blocks=300), 128)
+    assert np.array_equal(storage_bits(out1), storage_bits(out3))
+
+
+def test_single_token_returns_value_row(staging):
+    w = W.custom("one", seq_lens=[1, 1, 1], dtype="bf16", seed=8)
+    _, out = _run(staging, w, 0)
+    got = storage_bits(out)
+    for b in range(3):
+        _, v = w.kv(b)
+        want = W.bf16_bits(np.repeat(v[0], w.group, axis=0))
+        assert np.array_equal(got[b], want)
+
+
+def _sampled(staging, w, seqs, pt=0):
+    """Full-size workload on the GPU in the benchmark's launch configuration;
+    the oracle recomputes a few sequences one by one."""
+    dw, out = _run(staging, w, pt)
+    o = to_numpy(out)
+    assert np.all(np.isfinite(o))
+    ref = oracle.run_sequences(w, seqs)
+    for b in seqs:
+        assert_parity(o[b:b + 1], ref[b], w.dtype, f"{w.name} seq {b} (L={int(w.seq_lens[b])})")
+    return dw, o
+
+
+def test_llama8b_decode_full_size(staging):
+    w = W.llama8b_decode()
+    seqs = [int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 7, 33]
+    _sampled(staging, w, seqs)
+
+
+def test_llama8b_decode_8k_full_size(staging):
+    w = W.llama8b_decode_8k()
+    _sampled(staging, w, [0, 63])
+
+
+def test_long_context_full_size(staging):
+    w = W.long_context()
+    for pt in (0, 2048):
+        _sampled(staging, w, [0, 15], pt)
+
+
+def test_continuous_batching_full_size(staging):
+    w = W.continuous_batching()
+    seqs = [int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 100, 200]
+    _sampled(staging, w, seqs)
+
+
+def test_chunked_mix_decode_part_split_mode(staging):
+    """The decodes of the mixed batch, run through pa_decode (split-call mode)."""
+    w = W.decode_part(W.chunked_prefill_mix())
+    _sampled(staging, w, [0, 50, 95])
