@@ -58,17 +58,18 @@ __device__ __forceinline__ void to_f32(const ChunkF32& c, float f[8]) {
     f[4] = c.b.x; f[5] = c.b.y; f[6] = c.b.z; f[7] = c.b.w;
 }
 
+// Reinterpret one 32-bit word as two bf16.  It takes the word by value: clang
+// (ROCm 7.2) mis-lowers __builtin_bit_cast applied directly to an ext-vector
+// component such as w.y, reading component 0 instead.
+__device__ __forceinline__ bf16x2_t as_bf16x2(uint32_t word) { return __builtin_bit_cast(bf16x2_t, word); }
+
 // <q, k> over one chunk, accumulated into acc.  bf16 products are exact in
 // fp32; v_dot2_f32_bf16 adds two of them per instruction.
 __device__ __forceinline__ float dot_chunk(const ChunkBF16& q, const ChunkBF16& k, float acc) {
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.x),
-                                          __builtin_bit_cast(bf16x2_t, k.w.x), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.y),
-                                          __builtin_bit_cast(bf16x2_t, k.w.y), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.z),
-                                          __builtin_bit_cast(bf16x2_t, k.w.z), acc, false);
-    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w.w),
-                                          __builtin_bit_cast(bf16x2_t, k.w.w), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w.x), as_bf16x2(k.w.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w.y), as_bf16x2(k.w.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w.z), as_bf16x2(k.w.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(q.w.w), as_bf16x2(k.w.w), acc, false);
     return acc;
 }
 __device__ __forceinline__ float dot_chunk(const ChunkF32& q, const ChunkF32& k, float acc) {
