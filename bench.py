@@ -1,0 +1,184 @@
+"""Benchmark: one decode step of paged attention on one MI355X.
+
+A step is the whole hot path over one batch: compute the slots of this step's
+new tokens (pa_slot_mapping), scatter their K/V rows into the paged cache
+(pa_reshape_and_cache), and run decode attention over every sequence's cache
+(pa_decode: the partitioned kernel and, when sequences are split, the
+log-sum-exp merge).  Inputs are synthetic, seeded, and resident in HBM before
+timing starts; the earlier context of every sequence is written before timing.
+
+Default workload: Llama-3-8B decode layer, batch 64, context lengths uniform
+in [1024, 8192], bf16 (32 query heads, 8 KV heads, head_dim 128, 16-token
+blocks).  Prints one JSON line.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + seq-steps/s, 1 GPU"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=500)
+    p.add_argument("--warmup", type=int, default=50)
+    p.add_argument("--workload", default="llama8b_decode",
+                   choices=["llama8b_decode", "llama8b_decode_8k", "long_context", "continuous_batching"])
+    p.add_argument("--partition-tokens", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-seqs", type=int, default=16)
+    return p.parse_args()
+
+
+def cpu_baseline(w, nseq: int):
+    """The oracle, untuned, on the host cores: the first `nseq` sequences of the
+    workload (their K/V gathered through block tables into a compact pool built
+    before timing), timed over the same step: slots and scatter of their new
+    tokens, then attention."""
+    import oracle
+    import workloads as W
+    idx = np.arange(min(nseq, w.num_seqs))
+    sub = W._subset(w, idx, "cpu_sample")
+    counts = W.blocks_needed(sub.seq_lens)
+    table = np.full((len(idx), int(counts.max())), -1, np.int32)
+    cursor = 0
+    for i, c in enumerate(counts):
+        table[i, :c] = np.arange(cursor, cursor + c)
+        cursor += c
+    sub = sub.with_block_table(table, num_blocks=int(cursor))
+    kc, vc = oracle.build_cache(sub, "history")
+    seq, pos = sub.tokens("new")
+    k_new, v_new = (sub.encode(x) for x in sub.token_kv(seq, pos))
+    q = sub.encode(sub.queries())
+    oracle.lib()
+    times = []
+    for _ in range(3):                               # median of three runs of the step
+        t0 = time.perf_counter()
+        slots = oracle.slot_mapping(sub.block_table, seq, pos)
+        oracle.reshape_and_cache(k_new, v_new, kc, vc, slots)
+        oracle.attention(q, kc, vc, sub.block_table, sub.cu_query_lens, sub.seq_lens, sub.num_heads,
+                         sub.scale, sub.causal)
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
+    return {
+        "value": round(sub.kv_bytes() / dt / 1e9, 4),
+        "unit": "GB/s",
+        "seq_steps_per_s": round(len(idx) / dt, 3),
+        "seconds": round(dt, 3),
+        "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"first {len(idx)} of {w.num_seqs} sequences ({int(sub.seq_lens.sum())} KV tokens, "
+                  f"{sub.kv_bytes() / 1e9:.3f} GB of KV), one step (slots + scatter + attention), fp64, median of 3",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(each GPU would run its own shard of sequences or KV heads).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import paged_kv_cache_432_amd as pa
+    from paged_kv_cache_432_amd.staging import DeviceWorkload
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    pa.lib()
+    w = W.CONFIGS[args.workload]()
+    t_setup = time.perf_counter()
+    dw = DeviceWorkload(w)
+    pt = pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_seq_len, args.partition_tokens)
+    ws = dw.decode_workspace(args.partition_tokens)
+    out = torch.empty_like(dw.query)
+    torch.cuda.synchronize()
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s: {w.name}, {w.num_seqs} seqs, "
+          f"{w.kv_bytes() / 1e9:.3f} GB KV, partition {pt} tokens", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        dw.scatter_new(stream)
+        if ev is not None:
+            ev[0].record(stream)
+        dw.decode(out, args.partition_tokens, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    dec_ms = np.array([a.elapsed_time(b) for a, b in events])
+    dec_avg_ms = float(dec_ms.mean())
+
+    kv = w.kv_bytes()
+    gbps = kv / (ms_step * 1e-3) / 1e9
+    dec_gbps = kv / (dec_avg_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1)*sigma values, random block placement; no dataset)",
+        "config": {
+            "workload": w.name,
+            "batch": w.num_seqs,
+            "context_lens": f"min {int(w.seq_lens.min())} mean {float(w.seq_lens.mean()):.1f} "
+                            f"max {int(w.seq_lens.max())}",
+            "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "pool_blocks": w.num_blocks,
+            "new_tokens_per_step": int(w.num_q_tokens), "partition_tokens": pt,
+            "kv_bytes_per_step": kv,
+        },
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "roofline": {
+            "kernel": "pa_decode (partitioned decode kernel + log-sum-exp merge kernel)",
+            "bound": "hbm",
+            "achieved": round(dec_gbps, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(dec_avg_ms * 1e3, 2),
+            "algorithmic_bytes_per_launch": kv,
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -54,6 +54,8 @@ def lib():
                 build(force=False)
                 path = _LIB_PATH
             L = ctypes.CDLL(path)
+            L.oracle_max_threads.restype = ctypes.c_int32
+            L.oracle_max_threads.argtypes = []
             L.oracle_slot.restype = ctypes.c_int64
             L.oracle_slot.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32]
             L.oracle_slot_mapping.restype = None
@@ -72,6 +74,10 @@ def lib():
                 ctypes.c_double, ctypes.c_int32, ctypes.c_int32, _f64p, ctypes.c_int64]
             _lib = L
     return _lib
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
 
 
 def _p(a, t):

@@ -26,12 +26,25 @@
  * arithmetic.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+
+/* Number of threads the attention loop uses (OpenMP), for reporting. */
+int oracle_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 static double widen(const void *base, int64_t idx, int dtype)
 {

@@ -210,6 +210,9 @@ class Workload:
         if num_blocks is not None:
             w.num_blocks = int(num_blocks)
         w._kv_cache = self._kv_cache
+        for attr in ("kv", "query"):                 # keep per-instance value sources (subsets)
+            if attr in self.__dict__:
+                w.__dict__[attr] = self.__dict__[attr]
         return w
 
 
