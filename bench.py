@@ -107,7 +107,8 @@ def main():
     out = torch.empty_like(dw.query)
     torch.cuda.synchronize()
     print(f"# setup {time.perf_counter() - t_setup:.1f}s: {w.name}, {w.num_seqs} seqs, "
-          f"{w.kv_bytes() / 1e9:.3f} GB KV, partition {pt} tokens", file=sys.stderr, flush=True)
+          f"{w.kv_bytes() / 1e9:.3f} GB KV, partition {pt} tokens (0: balanced stream)",
+          file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
 
@@ -158,7 +159,9 @@ def main():
                             f"max {int(w.seq_lens.max())}",
             "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "block_size": w.block_size, "pool_blocks": w.num_blocks,
-            "new_tokens_per_step": int(w.num_q_tokens), "partition_tokens": pt,
+            "new_tokens_per_step": int(w.num_q_tokens),
+            "decode_split": "balanced stream (equal block shares per workgroup)" if pt == 0
+                            else f"partitions of {pt} tokens",
             "kv_bytes_per_step": kv,
         },
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),

@@ -158,6 +158,25 @@ pa_status pa_decode(void *out, const void *query, int64_t q_token_stride,
                     void *workspace, size_t workspace_bytes,
                     pa_dtype dtype, hipStream_t stream);
 
+/*
+ * Memory probes.  They are not part of the attention path: they give its
+ * HBM-bound roofline a measured denominator on the same GPU (decode reads the
+ * whole KV cache and is bound by memory, per the article's section "Attention
+ * (FlashAttention, Scaled Dot-Product Attention)"), and a transfer of known
+ * size for scaling hardware traffic counters.
+ *
+ * pa_probe_stream_read reads `bytes` from `src` once (16-byte loads over a
+ * grid-stride loop) and writes nothing in practice (`sink`, one uint32, is
+ * written only if the XOR of all words equals a fixed 32-bit constant).
+ * pa_probe_copy copies `bytes` from `src` to `dst` (non-overlapping).
+ * bytes: a multiple of 16; pointers 16-byte aligned; workgroups: grid size in
+ * 256-thread workgroups, 0 = automatic.  bytes == 0 is a no-op.
+ */
+pa_status pa_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, int32_t workgroups,
+                               hipStream_t stream);
+pa_status pa_probe_copy(void *dst, const void *src, int64_t bytes, int32_t workgroups,
+                        hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -18,7 +18,8 @@ import torch
 __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
     "pa_slot_mapping", "pa_reshape_and_cache", "pa_decode_workspace_bytes",
-    "pa_decode_partition_tokens", "pa_decode", "decode_workspace",
+    "pa_decode_partition_tokens", "pa_decode", "decode_workspace", "pa_probe_stream_read",
+    "pa_probe_copy",
 ]
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
@@ -74,6 +75,10 @@ def lib():
         L.pa_decode.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                 _i32, _i64, ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t,
                                 ctypes.c_int, _vp]
+        L.pa_probe_stream_read.restype = ctypes.c_int
+        L.pa_probe_stream_read.argtypes = [_vp, _i64, _vp, _i32, _vp]
+        L.pa_probe_copy.restype = ctypes.c_int
+        L.pa_probe_copy.argtypes = [_vp, _vp, _i64, _i32, _vp]
         _lib = L
         return L
 
@@ -208,3 +213,24 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
                         _stream(stream, out.device))
     _check(s, "pa_decode")
     return out
+
+
+# ------------------------------------------------------------------ probes --
+def pa_probe_stream_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int = 0, stream=None) -> None:
+    """Read every byte of `src` once (HBM read-bandwidth probe); `sink` is a
+    1-element int32/uint32 device tensor that is written only by a fluke."""
+    _need(src.is_contiguous() and sink.numel() >= 1, "src contiguous, sink of one element")
+    nbytes = src.numel() * src.element_size()
+    s = lib().pa_probe_stream_read(_ptr(src), nbytes - nbytes % 16, _ptr(sink), workgroups,
+                                   _stream(stream, src.device))
+    _check(s, "pa_probe_stream_read")
+
+
+def pa_probe_copy(dst: torch.Tensor, src: torch.Tensor, workgroups: int = 0, stream=None) -> None:
+    """dst[:] = src[:] bytewise (copy-bandwidth probe, and the known-size
+    transfer for scaling traffic counters)."""
+    _need(src.is_contiguous() and dst.is_contiguous(), "contiguous tensors")
+    nbytes = src.numel() * src.element_size()
+    _need(dst.numel() * dst.element_size() >= nbytes, "dst smaller than src")
+    s = lib().pa_probe_copy(_ptr(dst), _ptr(src), nbytes - nbytes % 16, workgroups, _stream(stream, src.device))
+    _check(s, "pa_probe_copy")

@@ -7,6 +7,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "launch.h"
 
 namespace {
@@ -35,10 +37,18 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
 
-// Tokens per partition.  An explicit size is used as given; 0 picks one from
-// the shapes: the smallest of 256 / 512 / 1024 tokens that still gives every
-// compute unit several waves at the longest sequence; -1 (or a size at least
-// max_seq_len) keeps every sequence in one partition.
+// Sequences at most this many use the balanced stream mode when the caller
+// leaves the split to the library (its workgroups keep a block-count prefix of
+// every sequence in LDS).
+constexpr int32_t kStreamMaxSeqs = 4096;
+// Fewest blocks a stream workgroup takes, so that tiny batches are not cut
+// into pieces smaller than the merge is worth.
+constexpr int32_t kStreamMinQuantum = 8;
+
+// Tokens per partition for the partitioned mode.  An explicit size is used as
+// given; 0 (when the stream mode does not apply) picks the smallest of 256 /
+// 512 / 1024 tokens that still gives every compute unit several waves; -1 (or
+// a size at least max_seq_len) keeps every sequence in one partition.
 int32_t choose_partition(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                          int32_t requested) {
     const int32_t whole = max_seq_len > 0 ? ((max_seq_len + 15) / 16) * 16 : 16;
@@ -54,12 +64,61 @@ int32_t num_partitions(int32_t max_seq_len, int32_t pt) {
     return max_seq_len <= 0 ? 1 : (max_seq_len + pt - 1) / pt;
 }
 
-size_t decode_ws_bytes(int32_t num_seqs, int32_t num_heads, int32_t head_dim, int32_t nparts) {
+bool use_stream(int32_t num_seqs, int32_t partition_tokens) {
+    return partition_tokens == 0 && num_seqs <= kStreamMaxSeqs;
+}
+
+// KV heads per stream workgroup (one wave each): the largest divisor of
+// num_kv_heads that is at most 8.
+int32_t stream_waves(int32_t num_kv_heads) {
+    for (int32_t w = 8; w > 1; --w)
+        if (num_kv_heads % w == 0) return w;
+    return 1;
+}
+
+// Stream-mode grid: every workgroup the current device holds at once.
+int32_t stream_num_wg(int dtype, int32_t group, int32_t waves, int32_t num_seqs) {
+    struct Entry { int dev, dtype, group, waves, lds_kib, wg; };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int ncache = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const int lds_kib = (int)(((int64_t)num_seqs + 1) * 4 + 1023) / 1024;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < ncache; ++i)
+            if (cache[i].dev == dev && cache[i].dtype == dtype && cache[i].group == group &&
+                cache[i].waves == waves && cache[i].lds_kib == lds_kib)
+                return cache[i].wg;
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return 0;
+    const int per_cu = pa::decode_stream_blocks_per_cu(dtype, group, waves, lds_kib * 256 - 1);
+    if (per_cu <= 0) return 0;
+    const int wg = cus * per_cu;
+    std::lock_guard<std::mutex> lock(mu);
+    if (ncache < 64) cache[ncache++] = Entry{dev, dtype, group, waves, lds_kib, wg};
+    return wg;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of the partitioned mode: partial records of every split
+// (sequence, head, partition).
+size_t partition_ws_bytes(int32_t num_seqs, int32_t num_heads, int32_t nparts) {
     if (nparts <= 1) return 0;
-    const size_t rows = (size_t)num_seqs * num_heads * nparts;
-    const size_t acc = rows * head_dim * sizeof(float);
-    const size_t acc_aligned = (acc + 255) & ~(size_t)255;
-    return acc_aligned + rows * 2 * sizeof(float);
+    return (size_t)num_seqs * num_heads * nparts * pa::kDecodeRecordFloats * sizeof(float);
+}
+
+// Workspace of the stream mode: the block prefix, then two partial records per
+// (workgroup, query head of its waves).
+size_t stream_ws_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t num_wg) {
+    const int32_t waves = stream_waves(num_kv_heads);
+    const int32_t group = num_heads / num_kv_heads;
+    return align256(((size_t)num_seqs + 1) * sizeof(int32_t)) +
+           (size_t)num_wg * 2 * waves * group * pa::kDecodeRecordFloats * sizeof(float);
 }
 
 }  // namespace
@@ -130,14 +189,25 @@ pa_status pa_reshape_and_cache(const void* key, int64_t key_token_stride, const 
 
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                                    int32_t partition_tokens) {
+    if (use_stream(num_seqs, partition_tokens)) return 0;
     return choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_seq_len, int32_t partition_tokens) {
-    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0) return 0;
+    if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_heads % num_kv_heads)
+        return 0;
+    if (use_stream(num_seqs, partition_tokens)) {
+        const int32_t group = num_heads / num_kv_heads, waves = stream_waves(num_kv_heads);
+        int32_t wg = 0;
+        for (int dtype = 0; dtype < 2; ++dtype) {          // the larger grid of the two dtypes
+            const int32_t n = stream_num_wg(dtype, group, waves, num_seqs);
+            wg = n > wg ? n : wg;
+        }
+        return stream_ws_bytes(num_seqs, num_heads, num_kv_heads, wg);
+    }
     const int32_t pt = choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
-    return decode_ws_bytes(num_seqs, num_heads, head_dim, num_partitions(max_seq_len, pt));
+    return partition_ws_bytes(num_seqs, num_heads, num_partitions(max_seq_len, pt));
 }
 
 pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
@@ -174,16 +244,6 @@ pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const 
         !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
 
-    const int32_t pt = choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
-    const int32_t nparts = num_partitions(max_seq_len, pt);
-    const size_t need = decode_ws_bytes(num_seqs, num_heads, head_dim, nparts);
-    if (need > 0 && (!workspace || workspace_bytes < need))
-        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0,
-                    need);
-    if (need > 0 && !aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-    const int64_t items = (int64_t)num_seqs * nparts * num_kv_heads;
-    if ((items + 3) / 4 > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "grid too large");
-
     pa::DecodeArgs a{};
     a.out = out;
     a.query = query;
@@ -198,15 +258,55 @@ pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const 
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
-    a.partition_tokens = pt;
-    a.max_partitions = nparts;
-    if (need > 0) {
-        const size_t rows = (size_t)num_seqs * num_heads * nparts;
-        const size_t acc_aligned = (rows * head_dim * sizeof(float) + 255) & ~(size_t)255;
-        a.part_acc = reinterpret_cast<float*>(workspace);
-        a.part_ml = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + acc_aligned);
+    const int dt = dtype == PA_BF16 ? 1 : 0;
+
+    size_t need = 0;
+    if (use_stream(num_seqs, partition_tokens)) {
+        const int32_t waves = stream_waves(num_kv_heads);
+        const int32_t wg = stream_num_wg(dt, group, waves, num_seqs);
+        if (wg <= 0) return fail(PA_ERR_HIP, "cannot size the decode grid for the current device");
+        need = stream_ws_bytes(num_seqs, num_heads, num_kv_heads, wg);
+        a.mode = pa::kDecodeStream;
+        a.waves_per_group = waves;
+        a.num_wg = wg;
+        a.min_quantum = kStreamMinQuantum;
+        if (workspace) {
+            a.prefix = reinterpret_cast<int32_t*>(workspace);
+            a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +
+                                              align256(((size_t)num_seqs + 1) * sizeof(int32_t)));
+        }
+    } else {
+        const int32_t pt = choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
+        const int32_t nparts = num_partitions(max_seq_len, pt);
+        need = partition_ws_bytes(num_seqs, num_heads, nparts);
+        const int64_t items = (int64_t)num_seqs * nparts * num_kv_heads;
+        if ((items + 3) / 4 > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "grid too large");
+        a.mode = pa::kDecodePartitions;
+        a.partition_tokens = pt;
+        a.max_partitions = nparts;
+        a.part = reinterpret_cast<float*>(workspace);
     }
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0,
+                    need);
+    if (need > 0 && !aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
     return hip_status(pa::launch_decode(a, dtype == PA_BF16 ? 1 : 0, group, stream), "decode launch");
+}
+
+pa_status pa_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,
+                               hipStream_t stream) {
+    if (bytes < 0 || bytes % 16 || workgroups < 0) return fail(PA_ERR_INVALID_ARG, "bytes %lld", (long long)bytes);
+    if (bytes == 0) return ok();
+    if (!src || !sink || !aligned16(src)) return fail(PA_ERR_INVALID_ARG, "null or misaligned pointer");
+    return hip_status(pa::launch_stream_read(src, bytes, sink, workgroups, stream), "stream_read launch");
+}
+
+pa_status pa_probe_copy(void* dst, const void* src, int64_t bytes, int32_t workgroups, hipStream_t stream) {
+    if (bytes < 0 || bytes % 16 || workgroups < 0) return fail(PA_ERR_INVALID_ARG, "bytes %lld", (long long)bytes);
+    if (bytes == 0) return ok();
+    if (!src || !dst || !aligned16(src) || !aligned16(dst))
+        return fail(PA_ERR_INVALID_ARG, "null or misaligned pointer");
+    return hip_status(pa::launch_stream_copy(dst, src, bytes, workgroups, stream), "stream_copy launch");
 }
 
 }  // extern "C"

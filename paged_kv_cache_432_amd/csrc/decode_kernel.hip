@@ -1,6 +1,6 @@
 // Paged decode attention for gfx950: one query token per sequence against its
-// paged K/V, with the online softmax and a split of long contexts into
-// partitions merged by log-sum-exp weights.
+// paged K/V, with the online softmax, and long contexts split into pieces whose
+// partial results are merged with log-sum-exp weights.
 //
 // What is computed follows "AI Infra入门干货总结：大模型是如何高效推理的":
 //   section "Attention (FlashAttention, Scaled Dot-Product Attention)" -- scores
@@ -11,25 +11,40 @@
 //   its closing summary -- Flash-Decoding splits the KV axis to occupy more
 //   compute units and merges the pieces with log-sum-exp.
 //
-// Work decomposition (one wavefront = one (sequence, kv head, partition)):
-//   * The G query heads of a KV head share every K/V row the wave loads, so
+// One wavefront attends one KV head of one sequence over a contiguous range of
+// its 16-token blocks (attend() below):
+//   * The G query heads of the KV head share every K/V row the wave loads, so
 //     each cache byte is read once per call.
-//   * A 16-token block of one KV head is 16 rows of 256 B (bf16), 2 KiB apart.
-//     Two lane layouts read it with 16-byte loads:
+//   * A 16-token block of one KV head is 16 rows of 256 B (bf16), Hkv*256 B
+//     apart.  Two lane layouts read it with 16-byte loads:
 //       K layout: lane = 4*t + c holds token t, dims {32j + 8c .. +8 : j<4}; a
 //         quad of lanes covers one row, so <q_h, k_t> needs a 2-step quad
 //         reduction only;
 //       V layout: lane = 16*g + d holds dims 8d .. 8d+7 of tokens 4g .. 4g+3;
 //         every load instruction covers 4 whole rows, and each lane's running
 //         output is G x 8 fp32 values that need no exchange until the end.
-//     The probabilities move from the K layout to the V layout through 64
+//     The probabilities move from the K layout to the V layout through 16*G
 //     floats of LDS per wave.
 //   * The running max is shared by the whole wave per head; a wave-uniform
 //     branch skips the max reduction and the rescale unless some score of the
 //     block exceeds it.  Exponentials are base 2 with log2(e) folded into the
 //     scale.
-//   * Block ids are loaded once per 64 blocks (one per lane) and broadcast with
-//     v_readlane; K/V loads of block i+1 are in flight while block i is used.
+//   * Block ids are loaded 64 at a time (one per lane) and broadcast with
+//     v_readlane.  K/V are read with buffer loads whose resource is the block:
+//     two blocks are in flight while one is consumed, and a load past the
+//     range gets an empty resource (no memory access, zeros), so that every
+//     load in the loop is unconditional and the compiler's wait counts stay
+//     exact.
+//
+// Two ways of cutting the work into wavefronts:
+//   * partitions (partition_tokens > 0 or -1): one wave per (sequence, KV
+//     head, partition of a fixed number of tokens);
+//   * balanced stream (the automatic choice): the grid is exactly as many
+//     workgroups as the GPU holds at once; the (sequence, block) space is
+//     flattened and every workgroup takes an equal contiguous share of it, one
+//     wave per KV head of a group.  A sequence cut between workgroups leaves
+//     a partial result in each, merged afterwards; a workgroup holds at most
+//     two such pieces (its first and its last).
 #include <math.h>
 
 #include "device_common.h"
@@ -39,91 +54,123 @@ namespace pa {
 
 namespace {
 
-constexpr int kWavesPerGroup = 4;
+constexpr int kWavesPerGroup = 4;        // partitioned mode: waves per workgroup
+constexpr int kRec = kDecodeRecordFloats; // partial record: 128 acc, max, sum, pad
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer, 32-bit data format (gfx9)
 
-template <typename Chunk, typename Elem, int G, bool NT>
-__global__ void __launch_bounds__(256)
-decode_kernel(DecodeArgs a) {
-    constexpr int D = kHeadDim;
-    constexpr int NSEL = (G + 3) / 4;          // heads whose probability a K-layout lane produces
-    constexpr int EPC = 8;                     // elements per chunk
-    __shared__ __attribute__((aligned(16))) float p_lds[kWavesPerGroup][kBlock * G];
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
-    const int Hkv = a.num_kv_heads;
-    const int64_t item = (int64_t)blockIdx.x * kWavesPerGroup + wave;
-    const int kvh = (int)(item % Hkv);
-    const int64_t rest = item / Hkv;
-    const int part = (int)(rest % a.max_partitions);
-    const int64_t b = rest / a.max_partitions;
-    if (b >= a.num_seqs) return;
-    // Lengths beyond the block table's row are cut to it, so that no table entry
-    // outside the row is read even when seq_lens breaks the contract.
-    const int L = min(a.seq_lens[b], a.bt_stride * kBlock);
-    const int PT = a.partition_tokens;
-    const int nparts = L <= 0 ? 1 : min((L + PT - 1) / PT, a.max_partitions);
-    if (part >= nparts) return;
-    const int tok_begin = part * PT;
-    const int tok_end = min(L, tok_begin + PT);
-    const int nblk = tok_end > tok_begin ? (tok_end - tok_begin + kBlock - 1) / kBlock : 0;
+template <bool NT>
+__device__ __forceinline__ void buffer_chunk(ChunkBF16& c, rsrc_t r, uint32_t off) {
+    c.w = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, NT ? 2 : 0));
+}
+template <bool NT>
+__device__ __forceinline__ void buffer_chunk(ChunkF32& c, rsrc_t r, uint32_t off) {
+    c.a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, NT ? 2 : 0));
+    c.b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off + 16, 0, NT ? 2 : 0));
+}
 
-    const int64_t tok_stride = (int64_t)Hkv * D;                 // elements between tokens of a block
-    const int64_t blk_stride = tok_stride * kBlock;              // elements between physical blocks
+// Per-wave state of one (sequence, KV head) range: the G query rows (in
+// registers, in the K layout, or -- QL -- in the wave's LDS slot, read back
+// per block: lanes of one dim chunk read the same address, a broadcast), the
+// running max / sum of each head (lane c keeps heads c and c+4), and the
+// unnormalised output in the V layout.
+template <typename Chunk, typename Elem, int G, bool QL>
+struct WaveState {
+    static constexpr int NSEL = (G + 3) / 4;
+    Chunk q[QL ? 1 : G][4];
+    Elem* qs;                      // QL: this wave's [G][128] query rows in LDS
+    float m[NSEL], l[NSEL];
+    float acc[G][8];
+};
 
-    // K layout
-    const int t = lane >> 2;
+__device__ __forceinline__ void store_chunk_raw(uint16_t* p, const ChunkBF16& c) {
+    *reinterpret_cast<u32x4_t*>(p) = c.w;
+}
+__device__ __forceinline__ void store_chunk_raw(float* p, const ChunkF32& c) {
+    reinterpret_cast<f32x4_t*>(p)[0] = c.a;
+    reinterpret_cast<f32x4_t*>(p)[1] = c.b;
+}
+
+template <typename Chunk, typename Elem, int G, bool QL>
+__device__ __forceinline__ void load_query(const DecodeArgs& a, int64_t b, int kvh, int lane,
+                                           WaveState<Chunk, Elem, G, QL>& st) {
     const int c = lane & 3;
-    const uint32_t koff = (uint32_t)((t * tok_stride + (int64_t)kvh * D + c * EPC) * sizeof(Elem));
-    // V layout
-    const int g = lane >> 4;
-    const int dch = lane & 15;
-    const uint32_t voff = (uint32_t)((4 * g * tok_stride + (int64_t)kvh * D + dch * EPC) * sizeof(Elem));
-    const uint32_t vrow = (uint32_t)(tok_stride * sizeof(Elem));
-
-    // Query of the G heads sharing this KV head, in the K layout.
-    Chunk q[G][4];
-    {
-        const Elem* qp = reinterpret_cast<const Elem*>(a.query) + b * a.q_stride + (int64_t)kvh * G * D;
+    const Elem* qp = reinterpret_cast<const Elem*>(a.query) + b * a.q_stride + (int64_t)kvh * G * kHeadDim;
+    if constexpr (QL) {
+        // G*16 chunks of 8 elements, spread over the lanes, copied to LDS
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int i0 = 0; i0 < G * 16; i0 += kWave) {
+            const int i = i0 + lane;
+            if (i < G * 16) {
+                Chunk x;
+                load_chunk<false>(x, qp + i * 8);
+                store_chunk_raw(st.qs + i * 8, x);
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
 #pragma unroll
         for (int h = 0; h < G; ++h)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) load_chunk<false>(q[h][j], qp + h * D + j * 32 + c * EPC);
+            for (int j = 0; j < 4; ++j) load_chunk<false>(st.q[h][j], qp + h * kHeadDim + j * 32 + c * 8);
     }
-
-    float m[NSEL], l[NSEL];
 #pragma unroll
-    for (int r = 0; r < NSEL; ++r) { m[r] = -INFINITY; l[r] = 0.f; }
-    float acc[G][EPC];
+    for (int r = 0; r < WaveState<Chunk, Elem, G, QL>::NSEL; ++r) { st.m[r] = -INFINITY; st.l[r] = 0.f; }
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) acc[h][e] = 0.f;
+        for (int e = 0; e < 8; ++e) st.acc[h][e] = 0.f;
+}
 
+// Online-softmax attention of one wave over blocks [0, nblk) of the table row
+// `bt` (its first entry is the range's first block); `tok_first` is the token
+// position of that block and `tok_end` the sequence length (tokens at or past
+// it are masked out).
+template <typename Chunk, typename Elem, int G, bool QL, bool NT>
+__device__ __forceinline__ void attend(const DecodeArgs& a, int kvh, const int32_t* __restrict__ bt,
+                                       int nblk, int tok_first, int tok_end, float* pl, int lane,
+                                       WaveState<Chunk, Elem, G, QL>& st) {
+    constexpr int NSEL = WaveState<Chunk, Elem, G, QL>::NSEL;
+    constexpr int EPC = 8;
+    const int Hkv = a.num_kv_heads;
+    const uint32_t eb = sizeof(Elem);
+    const uint32_t tok_bytes = (uint32_t)Hkv * kHeadDim * eb;       // between tokens of a block
+    const uint32_t blk_bytes = tok_bytes * kBlock;
+    const int t = lane >> 2, c = lane & 3;                          // K layout
+    const int g = lane >> 4, dch = lane & 15;                       // V layout
+    const uint32_t koff = t * tok_bytes + (uint32_t)kvh * kHeadDim * eb + c * EPC * eb;
+    const uint32_t voff = 4 * g * tok_bytes + (uint32_t)kvh * kHeadDim * eb + dch * EPC * eb;
     const char* kc = reinterpret_cast<const char*>(a.key_cache);
     const char* vc = reinterpret_cast<const char*>(a.value_cache);
-    const int32_t* bt = a.block_table + b * a.bt_stride + tok_begin / kBlock;
-    float* pl = p_lds[wave];
 
     for (int cb = 0; cb < nblk; cb += kWave) {
         const int nb = min(kWave, nblk - cb);
         const int bid = lane < nb ? bt[cb + lane] : 0;
 
         auto issue = [&](Chunk (&kb)[4], Chunk (&vb)[4], int i) {
-            // an id outside the pool (a caller error) is clamped into it: wrong
-            // values, but no access outside the cache
-            const int64_t phys = min(max((int64_t)__builtin_amdgcn_readlane(bid, i), (int64_t)0),
+            // Past the range: an empty resource, so the loads touch no memory.
+            // An id outside the pool (a caller error) is clamped into it: wrong
+            // values, but no access outside the cache.
+            const int64_t phys = min(max((int64_t)__builtin_amdgcn_readlane(bid, min(i, nb - 1)), (int64_t)0),
                                      a.num_blocks - 1);
-            const char* kbase = kc + phys * blk_stride * (int64_t)sizeof(Elem);
-            const char* vbase = vc + phys * blk_stride * (int64_t)sizeof(Elem);
+            const int nrec = i < nb ? (int)blk_bytes : 0;
+            const int64_t off = phys * (int64_t)blk_bytes;
+            const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
+            const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) load_chunk<NT>(kb[j], kbase + koff + j * 32 * sizeof(Elem));
+            for (int j = 0; j < 4; ++j) buffer_chunk<NT>(kb[j], rk, koff + j * 32 * eb);
 #pragma unroll
-            for (int i4 = 0; i4 < 4; ++i4) load_chunk<NT>(vb[i4], vbase + voff + i4 * vrow);
+            for (int i4 = 0; i4 < 4; ++i4) buffer_chunk<NT>(vb[i4], rv, voff + i4 * tok_bytes);
         };
 
         auto process = [&](const Chunk (&kb)[4], const Chunk (&vb)[4], int i) {
-            const int tok0 = tok_begin + (cb + i) * kBlock;
+            const int tok0 = tok_first + (cb + i) * kBlock;
             const bool tail = tok0 + kBlock > tok_end;
 
             // scores of token t for every head of the group (quad reduction)
@@ -131,8 +178,16 @@ decode_kernel(DecodeArgs a) {
 #pragma unroll
             for (int h = 0; h < G; ++h) {
                 float x = 0.f;
+                if constexpr (QL) {
+                    Chunk qh[4];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) x = dot_chunk(q[h][j], kb[j], x);
+                    for (int j = 0; j < 4; ++j) load_chunk<false>(qh[j], st.qs + h * kHeadDim + j * 32 + c * 8);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x = dot_chunk(qh[j], kb[j], x);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) x = dot_chunk(st.q[h][j], kb[j], x);
+                }
                 x += dpp<kQuadSwap1>(x);
                 x += dpp<kQuadSwap2>(x);
                 s[h] = x;
@@ -152,7 +207,7 @@ decode_kernel(DecodeArgs a) {
 
             bool grow = false;
 #pragma unroll
-            for (int r = 0; r < NSEL; ++r) grow |= ss[r] > m[r];
+            for (int r = 0; r < NSEL; ++r) grow |= ss[r] > st.m[r];
             if (__builtin_amdgcn_ballot_w64(grow)) {
                 float alpha[NSEL];
 #pragma unroll
@@ -162,24 +217,24 @@ decode_kernel(DecodeArgs a) {
                     bm = fmaxf(bm, dpp<kRowRor8>(bm));
                     bm = fmaxf(bm, shfl_xor_f(bm, 16));
                     bm = fmaxf(bm, shfl_xor_f(bm, 32));
-                    const float mn = fmaxf(m[r], bm);
-                    alpha[r] = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[r] - mn);
-                    l[r] *= alpha[r];
-                    m[r] = mn;
+                    const float mn = fmaxf(st.m[r], bm);
+                    alpha[r] = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(st.m[r] - mn);
+                    st.l[r] *= alpha[r];
+                    st.m[r] = mn;
                 }
 #pragma unroll
                 for (int h = 0; h < G; ++h) {
                     const float ah = readlane_f(alpha[h / 4], h % 4);
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e) acc[h][e] *= ah;
+                    for (int e = 0; e < EPC; ++e) st.acc[h][e] *= ah;
                 }
             }
 
 #pragma unroll
             for (int r = 0; r < NSEL; ++r) {
                 if (c + 4 * r < G) {
-                    const float p = __builtin_amdgcn_exp2f(ss[r] - m[r]);
-                    l[r] += p;
+                    const float p = __builtin_amdgcn_exp2f(ss[r] - st.m[r]);
+                    st.l[r] += p;
                     pl[t * G + c + 4 * r] = p;
                 }
             }
@@ -202,7 +257,7 @@ decode_kernel(DecodeArgs a) {
 #pragma unroll
                 for (int h = 0; h < G; ++h)
 #pragma unroll
-                    for (int e = 0; e < EPC; ++e) acc[h][e] = fmaf(pr[h], vf[e], acc[h][e]);
+                    for (int e = 0; e < EPC; ++e) st.acc[h][e] = fmaf(pr[h], vf[e], st.acc[h][e]);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -211,69 +266,242 @@ decode_kernel(DecodeArgs a) {
 
         Chunk ka[4], va[4], kb2[4], vb2[4];
         issue(ka, va, 0);
-        int i = 0;
-        for (; i + 1 < nb; i += 2) {
-            issue(kb2, vb2, i + 1);
+        issue(kb2, vb2, 1);
+        for (int i = 0; i < nb; i += 2) {
             process(ka, va, i);
-            if (i + 2 < nb) issue(ka, va, i + 2);
-            process(kb2, vb2, i + 1);
-        }
-        if (i < nb) process(ka, va, i);
-    }
-
-    // ---- epilogue: combine the per-lane partial sums
-#pragma unroll
-    for (int h = 0; h < G; ++h)
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-            acc[h][e] += shfl_xor_f(acc[h][e], 16);
-            acc[h][e] += shfl_xor_f(acc[h][e], 32);
-        }
-#pragma unroll
-    for (int r = 0; r < NSEL; ++r) {
-        l[r] += dpp<kRowRor4>(l[r]);
-        l[r] += dpp<kRowRor8>(l[r]);
-        l[r] += shfl_xor_f(l[r], 16);
-        l[r] += shfl_xor_f(l[r], 32);
-    }
-    float lh[G], mh[G];
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-        lh[h] = readlane_f(l[h / 4], h % 4);
-        mh[h] = readlane_f(m[h / 4], h % 4);
-    }
-
-    if (g == 0) {
-        const int Hq = a.num_heads;
-        if (nparts == 1) {
-            Elem* o = reinterpret_cast<Elem*>(a.out) + (b * Hq + (int64_t)kvh * G) * D + dch * EPC;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const float inv = lh[h] > 0.f ? 1.f / lh[h] : 0.f;
-                float f[EPC];
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) f[e] = acc[h][e] * inv;
-                store_chunk(o + h * D, f);
-            }
-        } else {
-            const int P = a.max_partitions;
-#pragma unroll
-            for (int h = 0; h < G; ++h) {
-                const int64_t slot = (b * Hq + (int64_t)kvh * G + h) * P + part;
-                store_chunk(a.part_acc + slot * D + dch * EPC, acc[h]);
-                if (dch == h) *reinterpret_cast<float2*>(a.part_ml + slot * 2) = make_float2(mh[h], lh[h]);
-            }
+            issue(ka, va, i + 2);
+            if (i + 1 < nb) process(kb2, vb2, i + 1);
+            issue(kb2, vb2, i + 3);
         }
     }
 }
 
-// Log-sum-exp merge of the partitions of every (sequence, head) that was split:
-// with M = max_p m_p, out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
-// One wave per (sequence, head), two dims per lane.
+// Finish a range: sum the per-lane pieces, then either normalise and store the
+// G output rows at `out` (out[h * 128 + d]), or store the unnormalised rows
+// with their (max, sum) as partial records at `rec` (record h at rec + h * kRec).
+template <typename Chunk, typename Elem, int G, bool QL>
+__device__ __forceinline__ void finish(WaveState<Chunk, Elem, G, QL>& st, int lane, Elem* out, float* rec) {
+    const int g = lane >> 4, dch = lane & 15;
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            st.acc[h][e] += shfl_xor_f(st.acc[h][e], 16);
+            st.acc[h][e] += shfl_xor_f(st.acc[h][e], 32);
+        }
+#pragma unroll
+    for (int r = 0; r < WaveState<Chunk, Elem, G, QL>::NSEL; ++r) {
+        st.l[r] += dpp<kRowRor4>(st.l[r]);
+        st.l[r] += dpp<kRowRor8>(st.l[r]);
+        st.l[r] += shfl_xor_f(st.l[r], 16);
+        st.l[r] += shfl_xor_f(st.l[r], 32);
+    }
+    float lh[G], mh[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+        lh[h] = readlane_f(st.l[h / 4], h % 4);
+        mh[h] = readlane_f(st.m[h / 4], h % 4);
+    }
+    if (g != 0) return;
+    if (out) {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            const float inv = lh[h] > 0.f ? 1.f / lh[h] : 0.f;
+            float f[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) f[e] = st.acc[h][e] * inv;
+            store_chunk(out + h * kHeadDim + dch * 8, f);
+        }
+    } else {
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+            store_chunk(rec + h * kRec + dch * 8, st.acc[h]);
+            if (dch == h) *reinterpret_cast<float2*>(rec + h * kRec + kHeadDim) = make_float2(mh[h], lh[h]);
+        }
+    }
+}
+
+__device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int64_t b) {
+    // Lengths beyond the block table's row are cut to it, so that no table entry
+    // outside the row is read even when seq_lens breaks the contract.
+    return max(min(a.seq_lens[b], a.bt_stride * kBlock), 0);
+}
+
+// ---- partitioned mode ------------------------------------------------------
+template <typename Chunk, typename Elem, int G, bool QL, bool NT>
+__global__ void __launch_bounds__(256)
+decode_partition_kernel(DecodeArgs a) {
+    __shared__ __attribute__((aligned(16))) float p_lds[kWavesPerGroup][kBlock * G];
+    __shared__ __attribute__((aligned(16))) Elem q_lds[QL ? kWavesPerGroup : 1][QL ? G * kHeadDim : 8];
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int Hkv = a.num_kv_heads;
+    const int64_t item = (int64_t)blockIdx.x * kWavesPerGroup + wave;
+    const int kvh = (int)(item % Hkv);
+    const int64_t rest = item / Hkv;
+    const int part = (int)(rest % a.max_partitions);
+    const int64_t b = rest / a.max_partitions;
+    if (b >= a.num_seqs) return;
+    const int L = seq_len_of(a, b);
+    const int PT = a.partition_tokens;
+    const int nparts = L <= 0 ? 1 : min((L + PT - 1) / PT, a.max_partitions);
+    if (part >= nparts) return;
+    const int tok_begin = part * PT;
+    const int tok_end = min(L, tok_begin + PT);
+    const int nblk = tok_end > tok_begin ? (tok_end - tok_begin + kBlock - 1) / kBlock : 0;
+
+    WaveState<Chunk, Elem, G, QL> st;
+    st.qs = q_lds[QL ? wave : 0];
+    load_query<Chunk, Elem, G, QL>(a, b, kvh, lane, st);
+    attend<Chunk, Elem, G, QL, NT>(a, kvh, a.block_table + b * a.bt_stride + tok_begin / kBlock, nblk,
+                                   tok_begin, L, p_lds[wave], lane, st);
+    if (nparts == 1) {
+        const int64_t h0 = b * a.num_heads + (int64_t)kvh * G;
+        finish<Chunk, Elem, G, QL>(st, lane, reinterpret_cast<Elem*>(a.out) + h0 * kHeadDim, nullptr);
+    } else {
+        const int64_t r0 = ((b * Hkv + kvh) * a.max_partitions + part) * G;
+        finish<Chunk, Elem, G, QL>(st, lane, nullptr, a.part + r0 * kRec);
+    }
+}
+
+// Partial record of (sequence b, query head h, partition p): the G heads of
+// one KV head and partition are consecutive records.
+__device__ __forceinline__ int64_t partition_record(const DecodeArgs& a, int64_t b, int h, int p) {
+    const int G = a.num_heads / a.num_kv_heads;
+    return ((b * a.num_kv_heads + h / G) * a.max_partitions + p) * G + (h % G);
+}
+
+// ---- balanced stream mode --------------------------------------------------
+// Number of blocks per KV head of each sequence, as an inclusive prefix in
+// s_pref[0..B] (s_pref[0] = 0); computed by the whole workgroup.
+__device__ __forceinline__ void block_prefix(const DecodeArgs& a, int32_t* s_pref, int32_t* s_wsum) {
+    const int B = a.num_seqs;
+    const int nthr = blockDim.x;
+    const int tid = threadIdx.x;
+    const int per = (B + nthr - 1) / nthr;
+    const int lo = min(tid * per, B), hi = min(lo + per, B);
+    int sum = 0;
+    for (int i = lo; i < hi; ++i) {
+        const int n = (seq_len_of(a, i) + kBlock - 1) / kBlock;
+        s_pref[i + 1] = n;
+        sum += n;
+    }
+    // inclusive scan of the per-thread sums: within the wave, then across waves
+    const int lane = tid & 63, wave = tid >> 6;
+    int x = sum;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int y = __shfl_up(x, d, kWave);
+        if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) s_wsum[wave] = x;
+    __syncthreads();
+    int before = x - sum;
+    for (int w = 0; w < wave; ++w) before += s_wsum[w];
+    for (int i = lo; i < hi; ++i) {
+        before += s_pref[i + 1];
+        s_pref[i + 1] = before;
+    }
+    if (tid == 0) s_pref[0] = 0;
+    __syncthreads();
+}
+
+__device__ __forceinline__ int64_t stream_quantum(const DecodeArgs& a, int64_t units) {
+    const int64_t q = (units + a.num_wg - 1) / a.num_wg;
+    return q > a.min_quantum ? q : (int64_t)a.min_quantum;
+}
+
+template <typename Chunk, typename Elem, int G, bool QL, bool NT>
+__global__ void __launch_bounds__(512)
+decode_stream_kernel(DecodeArgs a) {
+    extern __shared__ __attribute__((aligned(16))) int32_t s_pref[];          // [num_seqs + 1]
+    __shared__ int32_t s_wsum[8];
+    __shared__ __attribute__((aligned(16))) float p_lds[8][kBlock * G];
+    __shared__ __attribute__((aligned(16))) Elem q_lds[QL ? 8 : 1][QL ? G * kHeadDim : 8];
+    block_prefix(a, s_pref, s_wsum);
+    const int B = a.num_seqs;
+    const int W = a.waves_per_group;
+    const int NG = a.num_kv_heads / W;
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i <= B; i += blockDim.x) a.prefix[i] = s_pref[i];
+    const int64_t units = (int64_t)s_pref[B] * NG;
+    const int64_t Q = stream_quantum(a, units);
+    const int64_t u0 = (int64_t)blockIdx.x * Q;
+    const int64_t u1 = min(u0 + Q, units);
+    const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    float* pl = p_lds[wi];
+
+    for (int64_t u = u0; u < u1;) {
+        // the sequence holding unit u: the largest b with NG * prefix[b] <= u
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)NG * s_pref[mid] <= u) lo = mid; else hi = mid - 1;
+        }
+        const int b = lo;
+        const int nblk_b = s_pref[b + 1] - s_pref[b];
+        const int64_t r = u - (int64_t)NG * s_pref[b];
+        const int grp = (int)(r / nblk_b);
+        const int blk0 = (int)(r % nblk_b);
+        const int n = (int)min((int64_t)(nblk_b - blk0), u1 - u);
+        const int kvh = grp * W + wi;
+        const int L = seq_len_of(a, b);
+
+        WaveState<Chunk, Elem, G, QL> st;
+        st.qs = q_lds[QL ? wi : 0];
+        load_query<Chunk, Elem, G, QL>(a, b, kvh, lane, st);
+        attend<Chunk, Elem, G, QL, NT>(a, kvh, a.block_table + (int64_t)b * a.bt_stride + blk0, n,
+                                       blk0 * kBlock, L, pl, lane, st);
+        if (blk0 == 0 && n == nblk_b) {
+            finish<Chunk, Elem, G, QL>(st, lane,
+                                   reinterpret_cast<Elem*>(a.out) + ((int64_t)b * a.num_heads + (int64_t)kvh * G) * kHeadDim,
+                                   nullptr);
+        } else {
+            const int slot = u == u0 ? 0 : 1;
+            finish<Chunk, Elem, G, QL>(st, lane, nullptr,
+                                   a.part + ((((int64_t)blockIdx.x * 2 + slot) * W + wi) * G) * kRec);
+        }
+        u += n;
+    }
+}
+
+// ---- merges ----------------------------------------------------------------
+// Log-sum-exp merge of the pieces of one (sequence, head):
+//   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
+// One wave per (sequence, head), two dims per lane; `rec_of(p)` gives the
+// record index of piece p of n.
+template <typename Elem, typename RecOf>
+__device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec_of, int lane, Elem* o) {
+    float M = -INFINITY;
+    for (int p0 = 0; p0 < n; p0 += kWave) {
+        const int p = p0 + lane;
+        const float mp = p < n ? part[rec_of(p) * kRec + kHeadDim] : -INFINITY;
+        M = fmaxf(M, mp);
+    }
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));
+    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int p = 0; p < n; ++p) {
+        const float* r = part + rec_of(p) * kRec;
+        const float2 ml = *reinterpret_cast<const float2*>(r + kHeadDim);
+        const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+        lsum = fmaf(w, ml.y, lsum);
+        const float2 v = *reinterpret_cast<const float2*>(r + 2 * lane);
+        o0 = fmaf(w, v.x, o0);
+        o1 = fmaf(w, v.y, o1);
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if constexpr (sizeof(Elem) == 2) {
+        *reinterpret_cast<uint32_t*>(o + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+    } else {
+        *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(o0 * inv, o1 * inv);
+    }
+}
+
 template <typename Elem>
 __global__ void __launch_bounds__(256)
-merge_kernel(DecodeArgs a) {
-    constexpr int D = kHeadDim;
+merge_partitions_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int Hq = a.num_heads;
@@ -281,44 +509,81 @@ merge_kernel(DecodeArgs a) {
     const int64_t b = item / Hq;
     const int h = (int)(item % Hq);
     if (b >= a.num_seqs) return;
-    const int L = min(a.seq_lens[b], a.bt_stride * kBlock);
+    const int L = seq_len_of(a, b);
     const int PT = a.partition_tokens;
     const int nparts = L <= 0 ? 1 : min((L + PT - 1) / PT, a.max_partitions);
     if (nparts <= 1) return;
-    const int P = a.max_partitions;
-    const int64_t base = (b * Hq + h) * P;
-    const float* ml = a.part_ml + base * 2;
-    float M = -INFINITY;
-    for (int p = 0; p < nparts; ++p) M = fmaxf(M, ml[2 * p]);
-    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-    const float* pa = a.part_acc + base * D + 2 * lane;
-    for (int p = 0; p < nparts; ++p) {
-        const float w = __builtin_amdgcn_exp2f(ml[2 * p] - M);
-        lsum = fmaf(w, ml[2 * p + 1], lsum);
-        const float2 v = *reinterpret_cast<const float2*>(pa + (int64_t)p * D);
-        o0 = fmaf(w, v.x, o0);
-        o1 = fmaf(w, v.y, o1);
-    }
-    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-    Elem* o = reinterpret_cast<Elem*>(a.out) + (b * Hq + h) * D + 2 * lane;
-    if constexpr (sizeof(Elem) == 2) {
-        *reinterpret_cast<uint32_t*>(o) = pack_bf16x2(o0 * inv, o1 * inv);
-    } else {
-        *reinterpret_cast<float2*>(o) = make_float2(o0 * inv, o1 * inv);
-    }
+    merge_pieces<Elem>(a.part, nparts, [&](int p) { return partition_record(a, b, h, p); }, lane,
+                       reinterpret_cast<Elem*>(a.out) + (b * Hq + h) * kHeadDim);
 }
+
+template <typename Elem>
+__global__ void __launch_bounds__(256)
+merge_stream_kernel(DecodeArgs a) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int Hq = a.num_heads;
+    const int64_t item = (int64_t)blockIdx.x * kWavesPerGroup + wave;
+    const int64_t b = item / Hq;
+    const int h = (int)(item % Hq);
+    if (b >= a.num_seqs) return;
+    const int G = Hq / a.num_kv_heads;
+    const int W = a.waves_per_group;
+    const int NG = a.num_kv_heads / W;
+    const int kvh = h / G, hg = h % G, grp = kvh / W, wi = kvh % W;
+    const int32_t pb = a.prefix[b];
+    const int nblk = a.prefix[b + 1] - pb;
+    Elem* o = reinterpret_cast<Elem*>(a.out) + (b * Hq + h) * kHeadDim;
+    if (nblk == 0) {                                   // empty sequence: zeros
+        if constexpr (sizeof(Elem) == 2) *reinterpret_cast<uint32_t*>(o + 2 * lane) = 0u;
+        else *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(0.f, 0.f);
+        return;
+    }
+    const int64_t units = (int64_t)a.prefix[a.num_seqs] * NG;
+    const int64_t Q = stream_quantum(a, units);
+    const int64_t S = (int64_t)NG * pb + (int64_t)grp * nblk;
+    const int64_t E = S + nblk;
+    const int64_t w_lo = S / Q, w_hi = (E - 1) / Q;
+    if (w_lo == w_hi) return;                          // one workgroup wrote it whole
+    const bool lo_is_last = S != w_lo * Q;             // the piece in w_lo is that workgroup's second
+    merge_pieces<Elem>(a.part, (int)(w_hi - w_lo + 1),
+                       [&](int p) {
+                           const int64_t w = w_lo + p;
+                           const int slot = (p == 0 && lo_is_last) ? 1 : 0;
+                           return (((w * 2 + slot) * W + wi) * G + hg);
+                       },
+                       lane, o);
+}
+
+// Query rows live in LDS when registers would hold G x 16 bf16 of them per lane
+// (G = 8); below that they stay in registers.
+template <int G>
+constexpr bool kQueryInLds = G >= 8;
 
 template <typename Chunk, typename Elem, int G>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
+    constexpr bool QL = kQueryInLds<G>;
+    if (a.mode == kDecodeStream) {
+        const size_t lds = sizeof(int32_t) * ((size_t)a.num_seqs + 1);
+        hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, true>), dim3((unsigned)a.num_wg),
+                           dim3(64 * a.waves_per_group), lds, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t mitems = (int64_t)a.num_seqs * a.num_heads;
+        hipLaunchKernelGGL((merge_stream_kernel<Elem>),
+                           dim3((unsigned)((mitems + kWavesPerGroup - 1) / kWavesPerGroup)), dim3(256), 0,
+                           stream, a);
+        return hipGetLastError();
+    }
     const int64_t items = (int64_t)a.num_seqs * a.max_partitions * a.num_kv_heads;
     const int64_t grid = (items + kWavesPerGroup - 1) / kWavesPerGroup;
-    hipLaunchKernelGGL((decode_kernel<Chunk, Elem, G, true>), dim3((unsigned)grid), dim3(256), 0,
+    hipLaunchKernelGGL((decode_partition_kernel<Chunk, Elem, G, QL, true>), dim3((unsigned)grid), dim3(256), 0,
                        stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.max_partitions <= 1) return e;
     const int64_t mitems = (int64_t)a.num_seqs * a.num_heads;
-    hipLaunchKernelGGL((merge_kernel<Elem>), dim3((unsigned)((mitems + kWavesPerGroup - 1) / kWavesPerGroup)),
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((merge_partitions_kernel<Elem>),
+                       dim3((unsigned)((mitems + kWavesPerGroup - 1) / kWavesPerGroup)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
@@ -333,11 +598,37 @@ hipError_t launch_group(const DecodeArgs& a, int group, hipStream_t stream) {
     }
 }
 
+template <typename Chunk, typename Elem, int G>
+int stream_blocks_per_cu(int waves_per_group, size_t lds) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, true>,
+                                                     64 * waves_per_group, lds) != hipSuccess)
+        return 0;
+    return n;
+}
+
+template <typename Chunk, typename Elem>
+int stream_blocks_group(int group, int waves_per_group, size_t lds) {
+    switch (group) {
+        case 1: return stream_blocks_per_cu<Chunk, Elem, 1>(waves_per_group, lds);
+        case 2: return stream_blocks_per_cu<Chunk, Elem, 2>(waves_per_group, lds);
+        case 4: return stream_blocks_per_cu<Chunk, Elem, 4>(waves_per_group, lds);
+        case 8: return stream_blocks_per_cu<Chunk, Elem, 8>(waves_per_group, lds);
+        default: return 0;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t stream) {
     if (dtype == 1) return launch_group<ChunkBF16, uint16_t>(a, group, stream);
     return launch_group<ChunkF32, float>(a, group, stream);
+}
+
+int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int num_seqs) {
+    const size_t lds = sizeof(int32_t) * ((size_t)num_seqs + 1);
+    if (dtype == 1) return stream_blocks_group<ChunkBF16, uint16_t>(group, waves_per_group, lds);
+    return stream_blocks_group<ChunkF32, float>(group, waves_per_group, lds);
 }
 
 }  // namespace pa

@@ -18,6 +18,14 @@ hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const v
                                     const int64_t* slot_mapping, int64_t num_tokens,
                                     int64_t num_slots, int32_t row_bytes, hipStream_t stream);
 
+// Floats per partial record of one (piece, query head): 128 unnormalised
+// outputs, the running max (base 2), the running sum, two pad floats (records
+// stay 16-byte aligned).
+constexpr int kDecodeRecordFloats = 132;
+
+constexpr int kDecodePartitions = 0;   // one wave per (sequence, KV head, fixed partition)
+constexpr int kDecodeStream = 1;       // equal shares of the flattened (sequence, block) space
+
 struct DecodeArgs {
     void* out;
     const void* query;
@@ -32,13 +40,29 @@ struct DecodeArgs {
     int32_t num_heads;
     int32_t num_kv_heads;
     float scale_log2;              // softmax scale * log2(e): exponentials are taken base 2
+    int32_t mode;                  // kDecodePartitions or kDecodeStream
+    // partitions
     int32_t partition_tokens;      // tokens per split (multiple of 16), >= max_seq_len if unsplit
     int32_t max_partitions;        // ceil(max_seq_len / partition_tokens), >= 1
-    float* part_acc;               // [num_seqs, num_heads, max_partitions, 128] (split only)
-    float* part_ml;                // [num_seqs, num_heads, max_partitions, 2]   (split only)
+    // stream
+    int32_t waves_per_group;       // KV heads (one wave each) per workgroup; divides num_kv_heads
+    int32_t num_wg;                // grid size: workgroups resident at once
+    int32_t min_quantum;           // fewest blocks per workgroup
+    int32_t* prefix;               // [num_seqs + 1] blocks-per-KV-head prefix (written, then read)
+    // partial records (split sequences only)
+    float* part;
 };
 
 // dtype: 0 = fp32, 1 = bf16.  group = num_heads / num_kv_heads in {1,2,4,8}.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t stream);
+
+// Workgroups of the stream-mode decode kernel one compute unit holds at once.
+int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int num_seqs);
+
+// Memory probes (bytes a multiple of 16, pointers 16-byte aligned).
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,
+                              hipStream_t stream);
+hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, int32_t workgroups,
+                              hipStream_t stream);
 
 }  // namespace pa

@@ -74,11 +74,15 @@ def test_decode_empty_batch_is_ok(L):
 def test_workspace_query(L):
     assert pa.pa_decode_workspace_bytes(4, 32, 8, 128, 100, -1) == 0
     assert pa.pa_decode_workspace_bytes(4, 32, 8, 128, 100, 16) > 0
-    pt = pa.pa_decode_partition_tokens(64, 8, 8192, 0)
-    assert pt % 16 == 0 and 256 <= pt <= 1024
-    nparts = -(-8192 // pt)
-    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 8192, 0) >= 64 * 32 * nparts * 130 * 4
+    # explicit partitions: one 132-float record per (sequence, head, partition)
+    assert pa.pa_decode_workspace_bytes(64, 32, 8, 128, 8192, 512) == 64 * 32 * 16 * 132 * 4
     assert pa.pa_decode_partition_tokens(4, 8, 100, -1) == 112
+    assert pa.pa_decode_partition_tokens(64, 8, 8192, 256) == 256
+    # automatic: the balanced stream mode (reported as 0 tokens per partition);
+    # past 4096 sequences, automatic fixed partitions of 256..1024 tokens
+    assert pa.pa_decode_partition_tokens(64, 8, 8192, 0) == 0
+    pt = pa.pa_decode_partition_tokens(5000, 8, 8192, 0)
+    assert pt % 16 == 0 and 256 <= pt <= 1024
 
 
 def test_scatter_and_slot_checks(L):
