@@ -159,6 +159,51 @@ pa_status pa_decode(void *out, const void *query, int64_t q_token_stride,
                     pa_dtype dtype, hipStream_t stream);
 
 /*
+ * pa_chunked_prefill -- attention of a mixed batch in one call: chunks of
+ * query_len >= 2 rows (chunked prefill) next to single-row decodes, all
+ * reading K/V from the paged cache after this step's rows were scattered
+ * (the article's section "Attention (FlashAttention, Scaled Dot-Product
+ * Attention)": a varlen call over the flattened batch, cu_seqlens isolating
+ * requests, the causal mask M, and v1's rule that prefill too reads the paged
+ * cache).  For request b with q_b = cu_query_lens[b+1] - cu_query_lens[b]
+ * rows and L_b = seq_lens[b] tokens, query row j (flattened row
+ * cu_query_lens[b] + j) sits at position L_b - q_b + j and attends keys
+ * 0 .. L_b - q_b + j when causal (all L_b keys otherwise; a row that sees no
+ * key outputs zeros):
+ *   out[row, h, :] = sum_t softmax_t(scale * <q[row, h], k_t>) v_t,
+ *   kv_head = h / (num_heads / num_kv_heads).
+ * Requests with q_b == 1 run through the decode kernel (as pa_decode with
+ * automatic splitting); requests with q_b >= 2 run on the matrix cores
+ * (bf16 MFMA, fp32 accumulation, probabilities carried as a bf16 hi/lo pair);
+ * q_b == 0 requests produce nothing.
+ *
+ * out          [num_q_tokens, num_heads, head_dim] bf16, contiguous
+ * query        [num_q_tokens, num_heads, head_dim] bf16; rows q_token_stride
+ *              ELEMENTS apart (heads/dims contiguous, rows 16-byte aligned)
+ * key_cache, value_cache, block_table, block_size, num_blocks: as pa_decode
+ * cu_query_lens int32 [num_seqs + 1], cu_query_lens[0] == 0,
+ *              cu_query_lens[num_seqs] == num_q_tokens, non-decreasing
+ * seq_lens     int32 [num_seqs]: tokens in the cache for the request, this
+ *              step's rows included (seq_lens[b] >= q_b)
+ * max_query_len, max_seq_len: host-side upper bounds of q_b and seq_lens
+ * causal       1 (the chunked-prefill case) or 0
+ * workspace    >= pa_chunked_prefill_workspace_bytes(...) bytes of device
+ *              scratch (no initialisation needed)
+ * dtype        PA_BF16 only (PA_ERR_UNSUPPORTED otherwise)
+ */
+size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t max_seq_len);
+pa_status pa_chunked_prefill(void *out, const void *query, int64_t q_token_stride,
+                             const void *key_cache, const void *value_cache,
+                             const int32_t *block_table, int32_t max_blocks_per_req,
+                             const int32_t *cu_query_lens, const int32_t *seq_lens,
+                             int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,
+                             int32_t max_seq_len, int32_t num_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                             int32_t causal, void *workspace, size_t workspace_bytes,
+                             pa_dtype dtype, hipStream_t stream);
+
+/*
  * Memory probes.  They are not part of the attention path: they give its
  * HBM-bound roofline a measured denominator on the same GPU (decode reads the
  * whole KV cache and is bound by memory, per the article's section "Attention

@@ -18,8 +18,8 @@ import torch
 __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
     "pa_slot_mapping", "pa_reshape_and_cache", "pa_decode_workspace_bytes",
-    "pa_decode_partition_tokens", "pa_decode", "decode_workspace", "pa_probe_stream_read",
-    "pa_probe_copy",
+    "pa_decode_partition_tokens", "pa_decode", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
+    "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy",
 ]
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
@@ -75,6 +75,12 @@ def lib():
         L.pa_decode.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                 _i32, _i64, ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t,
                                 ctypes.c_int, _vp]
+        L.pa_chunked_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.pa_chunked_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+        L.pa_chunked_prefill.restype = ctypes.c_int
+        L.pa_chunked_prefill.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32,
+                                         _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _vp,
+                                         ctypes.c_size_t, ctypes.c_int, _vp]
         L.pa_probe_stream_read.restype = ctypes.c_int
         L.pa_probe_stream_read.argtypes = [_vp, _i64, _vp, _i32, _vp]
         L.pa_probe_copy.restype = ctypes.c_int
@@ -212,6 +218,48 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
                         0 if ws is None else ws.numel() * ws.element_size(), _dtype_code(query),
                         _stream(stream, out.device))
     _check(s, "pa_decode")
+    return out
+
+
+def pa_chunked_prefill_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                                       max_seq_len: int) -> int:
+    return int(lib().pa_chunked_prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+                                                        max_seq_len))
+
+
+def chunked_prefill_workspace(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
+                              max_seq_len: int, device="cuda") -> torch.Tensor | None:
+    nbytes = pa_chunked_prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def pa_chunked_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,
+                       value_cache: torch.Tensor, block_table: torch.Tensor, cu_query_lens: torch.Tensor,
+                       seq_lens: torch.Tensor, scale: float, max_query_len: int, max_seq_len: int,
+                       causal: bool = True, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Mixed-batch attention: out [num_q_tokens, Hq, D] for flattened query rows
+    [num_q_tokens, Hq, D] (bf16), requests delimited by cu_query_lens."""
+    _need(query.dim() == 3 and out.shape == query.shape and out.is_contiguous(),
+          "query/out: [num_q_tokens, num_heads, head_dim], out contiguous")
+    _need(query.stride(2) == 1 and query.stride(1) == query.shape[2], "query heads/dims must be contiguous")
+    _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
+    _need(query.dtype == out.dtype == key_cache.dtype == value_cache.dtype, "dtype mismatch")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
+          "block_table: contiguous int32 [num_seqs, max_blocks_per_req]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.is_contiguous(), "seq_lens: contiguous int32")
+    _need(cu_query_lens.dtype == torch.int32 and cu_query_lens.is_contiguous(), "cu_query_lens: contiguous int32")
+    b = seq_lens.numel()
+    _need(cu_query_lens.numel() == b + 1 and block_table.shape[0] >= b, "cu_query_lens/block_table sizes")
+    nq, hq, d = query.shape
+    nb, bs, hkv, _ = key_cache.shape
+    ws = workspace
+    s = lib().pa_chunked_prefill(_ptr(out), _ptr(query), query.stride(0), _ptr(key_cache), _ptr(value_cache),
+                                 _ptr(block_table), block_table.shape[1], _ptr(cu_query_lens), _ptr(seq_lens),
+                                 b, nq, int(max_query_len), int(max_seq_len), hq, hkv, d, bs, nb, float(scale),
+                                 int(bool(causal)), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                 _dtype_code(query), _stream(stream, out.device))
+    _check(s, "pa_chunked_prefill")
     return out
 
 

@@ -68,39 +68,56 @@ bool use_stream(int32_t num_seqs, int32_t partition_tokens) {
     return partition_tokens == 0 && num_seqs <= kStreamMaxSeqs;
 }
 
-// KV heads per stream workgroup (one wave each): the largest divisor of
-// num_kv_heads that is at most 8.
-int32_t stream_waves(int32_t num_kv_heads) {
-    for (int32_t w = 8; w > 1; --w)
-        if (num_kv_heads % w == 0) return w;
-    return 1;
-}
-
-// Stream-mode grid: every workgroup the current device holds at once.
-int32_t stream_num_wg(int dtype, int32_t group, int32_t waves, int32_t num_seqs) {
-    struct Entry { int dev, dtype, group, waves, lds_kib, wg; };
+// Stream-mode workgroups one compute unit of the current device holds at
+// once, for `waves` KV heads (one wave each) per workgroup; cached.
+int32_t stream_blocks_per_cu(int dtype, int32_t group, int32_t waves, int32_t num_seqs) {
+    struct Entry { int dev, dtype, group, waves, lds_kib, n; };
     static std::mutex mu;
-    static Entry cache[64];
+    static Entry cache[128];
     static int ncache = 0;
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
-    const int lds_kib = (int)(((int64_t)num_seqs + 1) * 4 + 1023) / 1024;
+    const int lds_kib = (int)((((int64_t)num_seqs + 1) * 4 + 1023) / 1024);
     {
         std::lock_guard<std::mutex> lock(mu);
         for (int i = 0; i < ncache; ++i)
             if (cache[i].dev == dev && cache[i].dtype == dtype && cache[i].group == group &&
                 cache[i].waves == waves && cache[i].lds_kib == lds_kib)
-                return cache[i].wg;
+                return cache[i].n;
     }
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return 0;
-    const int per_cu = pa::decode_stream_blocks_per_cu(dtype, group, waves, lds_kib * 256 - 1);
-    if (per_cu <= 0) return 0;
-    const int wg = cus * per_cu;
+    const int n = pa::decode_stream_blocks_per_cu(dtype, group, waves, lds_kib * 256 - 1);
     std::lock_guard<std::mutex> lock(mu);
-    if (ncache < 64) cache[ncache++] = Entry{dev, dtype, group, waves, lds_kib, wg};
-    return wg;
+    if (ncache < 128) cache[ncache++] = Entry{dev, dtype, group, waves, lds_kib, n};
+    return n;
+}
+
+int32_t device_cus() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return cus;
+}
+
+// Stream-mode layout: the KV heads per workgroup (a divisor of num_kv_heads,
+// at most 8) that keep the most waves resident per compute unit (ties go to
+// the wider workgroup, whose waves read neighbouring rows of the same blocks),
+// and the grid: every such workgroup the device holds at once.
+struct StreamShape { int32_t waves, num_wg; };
+
+StreamShape stream_shape(int dtype, int32_t group, int32_t num_kv_heads, int32_t num_seqs) {
+    StreamShape best{1, 0};
+    int32_t best_resident = 0;
+    const int32_t cus = device_cus();
+    if (cus <= 0) return best;
+    for (int32_t w = 8; w >= 1; --w) {
+        if (num_kv_heads % w) continue;
+        const int32_t per_cu = stream_blocks_per_cu(dtype, group, w, num_seqs);
+        if (per_cu * w > best_resident) {
+            best_resident = per_cu * w;
+            best = StreamShape{w, per_cu * cus};
+        }
+    }
+    return best;
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -114,8 +131,8 @@ size_t partition_ws_bytes(int32_t num_seqs, int32_t num_heads, int32_t nparts) {
 
 // Workspace of the stream mode: the block prefix, then two partial records per
 // (workgroup, query head of its waves).
-size_t stream_ws_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t num_wg) {
-    const int32_t waves = stream_waves(num_kv_heads);
+size_t stream_ws_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, StreamShape sh) {
+    const int32_t waves = sh.waves, num_wg = sh.num_wg;
     const int32_t group = num_heads / num_kv_heads;
     return align256(((size_t)num_seqs + 1) * sizeof(int32_t)) +
            (size_t)num_wg * 2 * waves * group * pa::kDecodeRecordFloats * sizeof(float);
@@ -198,52 +215,32 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
     if (num_seqs <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || num_heads % num_kv_heads)
         return 0;
     if (use_stream(num_seqs, partition_tokens)) {
-        const int32_t group = num_heads / num_kv_heads, waves = stream_waves(num_kv_heads);
-        int32_t wg = 0;
-        for (int dtype = 0; dtype < 2; ++dtype) {          // the larger grid of the two dtypes
-            const int32_t n = stream_num_wg(dtype, group, waves, num_seqs);
-            wg = n > wg ? n : wg;
+        const int32_t group = num_heads / num_kv_heads;
+        size_t bytes = 0;
+        for (int dtype = 0; dtype < 2; ++dtype) {          // the larger of the two dtypes' layouts
+            const size_t n = stream_ws_bytes(num_seqs, num_heads, num_kv_heads,
+                                             stream_shape(dtype, group, num_kv_heads, num_seqs));
+            bytes = n > bytes ? n : bytes;
         }
-        return stream_ws_bytes(num_seqs, num_heads, num_kv_heads, wg);
+        return bytes;
     }
     const int32_t pt = choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
     return partition_ws_bytes(num_seqs, num_heads, num_partitions(max_seq_len, pt));
 }
 
-pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
-                    const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
-                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                    int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
-                    int32_t max_seq_len, int32_t partition_tokens, void* workspace,
-                    size_t workspace_bytes, pa_dtype dtype, hipStream_t stream) {
-    if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
-    if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
-    if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (only 128)", head_dim);
-    if (num_seqs < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_req < 0)
-        return fail(PA_ERR_INVALID_ARG, "negative size");
-    if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads)
-        return fail(PA_ERR_INVALID_ARG, "num_heads %d not a multiple of num_kv_heads %d", num_heads,
-                    num_kv_heads);
-    const int32_t group = num_heads / num_kv_heads;
-    if (group != 1 && group != 2 && group != 4 && group != 8)
-        return fail(PA_ERR_UNSUPPORTED, "group size %d (supported: 1, 2, 4, 8)", group);
-    if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % 16))
-        return fail(PA_ERR_INVALID_ARG, "partition_tokens %d (0, -1 or a positive multiple of 16)",
-                    partition_tokens);
-    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
-    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
-        return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
-    if (num_seqs == 0) return ok();
-    if (num_blocks == 0 && max_seq_len > 0) return fail(PA_ERR_INVALID_ARG, "empty cache pool");
-    if (!out || !query || !seq_lens || !key_cache || !value_cache || (max_seq_len > 0 && !block_table))
-        return fail(PA_ERR_INVALID_ARG, "null pointer");
-    const int64_t eb = elem_bytes(dtype);
-    if (q_token_stride < (int64_t)num_heads * head_dim)
-        return fail(PA_ERR_INVALID_ARG, "q_token_stride smaller than num_heads * head_dim");
-    if (!aligned16(query) || (q_token_stride * eb) % 16 || !aligned16(out) || !aligned16(key_cache) ||
-        !aligned16(value_cache))
-        return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
+}  // extern "C"
 
+namespace {
+
+// Checks shared by pa_decode and pa_chunked_prefill, then the decode launch
+// (cu_q != nullptr: only the single-row sequences of a mixed batch).
+pa_status decode_common(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+                        const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
+                        const int32_t* seq_lens, const int32_t* cu_q, int32_t num_seqs, int32_t num_heads,
+                        int32_t num_kv_heads, int64_t num_blocks, float scale, int32_t max_seq_len,
+                        int32_t partition_tokens, void* workspace, size_t workspace_bytes, pa_dtype dtype,
+                        hipStream_t stream) {
+    const int32_t group = num_heads / num_kv_heads;
     pa::DecodeArgs a{};
     a.out = out;
     a.query = query;
@@ -258,17 +255,17 @@ pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const 
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
     a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.cu_q = cu_q;
     const int dt = dtype == PA_BF16 ? 1 : 0;
 
     size_t need = 0;
     if (use_stream(num_seqs, partition_tokens)) {
-        const int32_t waves = stream_waves(num_kv_heads);
-        const int32_t wg = stream_num_wg(dt, group, waves, num_seqs);
-        if (wg <= 0) return fail(PA_ERR_HIP, "cannot size the decode grid for the current device");
-        need = stream_ws_bytes(num_seqs, num_heads, num_kv_heads, wg);
+        const StreamShape sh = stream_shape(dt, group, num_kv_heads, num_seqs);
+        if (sh.num_wg <= 0) return fail(PA_ERR_HIP, "cannot size the decode grid for the current device");
+        need = stream_ws_bytes(num_seqs, num_heads, num_kv_heads, sh);
         a.mode = pa::kDecodeStream;
-        a.waves_per_group = waves;
-        a.num_wg = wg;
+        a.waves_per_group = sh.waves;
+        a.num_wg = sh.num_wg;
         a.min_quantum = kStreamMinQuantum;
         if (workspace) {
             a.prefix = reinterpret_cast<int32_t*>(workspace);
@@ -290,7 +287,125 @@ pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const 
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0,
                     need);
     if (need > 0 && !aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-    return hip_status(pa::launch_decode(a, dtype == PA_BF16 ? 1 : 0, group, stream), "decode launch");
+    return hip_status(pa::launch_decode(a, dt, group, stream), "decode launch");
+}
+
+// Shape checks shared by the attention entry points.
+pa_status check_heads(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size) {
+    if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
+    if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (only 128)", head_dim);
+    if (num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads)
+        return fail(PA_ERR_INVALID_ARG, "num_heads %d not a multiple of num_kv_heads %d", num_heads,
+                    num_kv_heads);
+    const int32_t group = num_heads / num_kv_heads;
+    if (group != 1 && group != 2 && group != 4 && group != 8)
+        return fail(PA_ERR_UNSUPPORTED, "group size %d (supported: 1, 2, 4, 8)", group);
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+                    const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
+                    const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                    int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                    int32_t max_seq_len, int32_t partition_tokens, void* workspace,
+                    size_t workspace_bytes, pa_dtype dtype, hipStream_t stream) {
+    if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    const pa_status hs = check_heads(num_heads, num_kv_heads, head_dim, block_size);
+    if (hs != PA_OK) return hs;
+    if (num_seqs < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_req < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative size");
+    if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % 16))
+        return fail(PA_ERR_INVALID_ARG, "partition_tokens %d (0, -1 or a positive multiple of 16)",
+                    partition_tokens);
+    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
+        return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
+    if (num_seqs == 0) return ok();
+    if (num_blocks == 0 && max_seq_len > 0) return fail(PA_ERR_INVALID_ARG, "empty cache pool");
+    if (!out || !query || !seq_lens || !key_cache || !value_cache || (max_seq_len > 0 && !block_table))
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    const int64_t eb = elem_bytes(dtype);
+    if (q_token_stride < (int64_t)num_heads * head_dim)
+        return fail(PA_ERR_INVALID_ARG, "q_token_stride smaller than num_heads * head_dim");
+    if (!aligned16(query) || (q_token_stride * eb) % 16 || !aligned16(out) || !aligned16(key_cache) ||
+        !aligned16(value_cache))
+        return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
+    return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
+                         seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len,
+                         partition_tokens, workspace, workspace_bytes, dtype, stream);
+}
+
+size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, int32_t max_seq_len) {
+    return pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len, 0);
+}
+
+pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+                             const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
+                             const int32_t* cu_query_lens, const int32_t* seq_lens, int32_t num_seqs,
+                             int64_t num_q_tokens, int32_t max_query_len, int32_t max_seq_len,
+                             int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                             int64_t num_blocks, float scale, int32_t causal, void* workspace,
+                             size_t workspace_bytes, pa_dtype dtype, hipStream_t stream) {
+    if (dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d (chunked prefill is bf16 only)", (int)dtype);
+    const pa_status hs = check_heads(num_heads, num_kv_heads, head_dim, block_size);
+    if (hs != PA_OK) return hs;
+    if (num_seqs < 0 || num_q_tokens < 0 || num_blocks < 0 || max_seq_len < 0 || max_query_len < 0 ||
+        max_blocks_per_req < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative size");
+    if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal %d (0 or 1)", causal);
+    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
+        return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
+    if (num_seqs == 0 || num_q_tokens == 0) return ok();
+    if (num_q_tokens > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "num_q_tokens too large");
+    if (num_blocks == 0 && max_seq_len > 0) return fail(PA_ERR_INVALID_ARG, "empty cache pool");
+    if (!out || !query || !seq_lens || !cu_query_lens || !key_cache || !value_cache ||
+        (max_seq_len > 0 && !block_table))
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (q_token_stride < (int64_t)num_heads * head_dim)
+        return fail(PA_ERR_INVALID_ARG, "q_token_stride smaller than num_heads * head_dim");
+    if (!aligned16(query) || (q_token_stride * 2) % 16 || !aligned16(out) || !aligned16(key_cache) ||
+        !aligned16(value_cache))
+        return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
+
+    // single-row sequences: the decode kernel, reading its rows through cu_query_lens
+    pa_status st = decode_common(out, query, q_token_stride, key_cache, value_cache, block_table,
+                                 max_blocks_per_req, seq_lens, cu_query_lens, num_seqs, num_heads, num_kv_heads,
+                                 num_blocks, scale, max_seq_len, 0, workspace, workspace_bytes, dtype, stream);
+    if (st != PA_OK) return st;
+    if (max_query_len < 2) return ok();
+
+    // sequences of two or more rows: the MFMA prefill kernel, one workgroup per
+    // (query tile, KV head); the grid bounds the tile count from the host-side sizes
+    const int32_t group = num_heads / num_kv_heads;
+    const int64_t tq = pa::kPrefillRows / group;
+    const int64_t by_tokens = (num_q_tokens + tq - 1) / tq + (num_seqs < num_q_tokens / 2 ? num_seqs : num_q_tokens / 2);
+    const int64_t by_seqs = (int64_t)num_seqs * ((max_query_len + tq - 1) / tq);
+    const int64_t tiles = by_tokens < by_seqs ? by_tokens : by_seqs;
+    if (tiles * num_kv_heads > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "grid too large");
+    pa::PrefillArgs p{};
+    p.out = out;
+    p.query = query;
+    p.q_stride = q_token_stride;
+    p.key_cache = key_cache;
+    p.value_cache = value_cache;
+    p.block_table = block_table;
+    p.bt_stride = max_blocks_per_req;
+    p.num_blocks = num_blocks;
+    p.cu_query_lens = cu_query_lens;
+    p.seq_lens = seq_lens;
+    p.num_seqs = num_seqs;
+    p.num_heads = num_heads;
+    p.num_kv_heads = num_kv_heads;
+    p.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    p.causal = causal;
+    p.tiles_bound = (int32_t)tiles;
+    return hip_status(pa::launch_prefill(p, group, stream), "prefill launch");
 }
 
 pa_status pa_probe_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,

@@ -93,10 +93,10 @@ __device__ __forceinline__ void store_chunk_raw(float* p, const ChunkF32& c) {
 }
 
 template <typename Chunk, typename Elem, int G, bool QL>
-__device__ __forceinline__ void load_query(const DecodeArgs& a, int64_t b, int kvh, int lane,
+__device__ __forceinline__ void load_query(const DecodeArgs& a, int64_t row, int kvh, int lane,
                                            WaveState<Chunk, Elem, G, QL>& st) {
     const int c = lane & 3;
-    const Elem* qp = reinterpret_cast<const Elem*>(a.query) + b * a.q_stride + (int64_t)kvh * G * kHeadDim;
+    const Elem* qp = reinterpret_cast<const Elem*>(a.query) + row * a.q_stride + (int64_t)kvh * G * kHeadDim;
     if constexpr (QL) {
         // G*16 chunks of 8 elements, spread over the lanes, copied to LDS
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -321,6 +321,14 @@ __device__ __forceinline__ void finish(WaveState<Chunk, Elem, G, QL>& st, int la
     }
 }
 
+// Query (and output) row of sequence b, or -1 when b is not a single-row
+// sequence of a mixed batch (the prefill kernel attends those).
+__device__ __forceinline__ int64_t decode_row(const DecodeArgs& a, int64_t b) {
+    if (!a.cu_q) return b;
+    const int32_t r = a.cu_q[b];
+    return a.cu_q[b + 1] - r == 1 ? (int64_t)r : -1;
+}
+
 __device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int64_t b) {
     // Lengths beyond the block table's row are cut to it, so that no table entry
     // outside the row is read even when seq_lens breaks the contract.
@@ -342,6 +350,8 @@ decode_partition_kernel(DecodeArgs a) {
     const int part = (int)(rest % a.max_partitions);
     const int64_t b = rest / a.max_partitions;
     if (b >= a.num_seqs) return;
+    const int64_t row = decode_row(a, b);
+    if (row < 0) return;
     const int L = seq_len_of(a, b);
     const int PT = a.partition_tokens;
     const int nparts = L <= 0 ? 1 : min((L + PT - 1) / PT, a.max_partitions);
@@ -352,11 +362,11 @@ decode_partition_kernel(DecodeArgs a) {
 
     WaveState<Chunk, Elem, G, QL> st;
     st.qs = q_lds[QL ? wave : 0];
-    load_query<Chunk, Elem, G, QL>(a, b, kvh, lane, st);
+    load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
     attend<Chunk, Elem, G, QL, NT>(a, kvh, a.block_table + b * a.bt_stride + tok_begin / kBlock, nblk,
                                    tok_begin, L, p_lds[wave], lane, st);
     if (nparts == 1) {
-        const int64_t h0 = b * a.num_heads + (int64_t)kvh * G;
+        const int64_t h0 = row * a.num_heads + (int64_t)kvh * G;
         finish<Chunk, Elem, G, QL>(st, lane, reinterpret_cast<Elem*>(a.out) + h0 * kHeadDim, nullptr);
     } else {
         const int64_t r0 = ((b * Hkv + kvh) * a.max_partitions + part) * G;
@@ -382,7 +392,7 @@ __device__ __forceinline__ void block_prefix(const DecodeArgs& a, int32_t* s_pre
     const int lo = min(tid * per, B), hi = min(lo + per, B);
     int sum = 0;
     for (int i = lo; i < hi; ++i) {
-        const int n = (seq_len_of(a, i) + kBlock - 1) / kBlock;
+        const int n = decode_row(a, i) < 0 ? 0 : (seq_len_of(a, i) + kBlock - 1) / kBlock;
         s_pref[i + 1] = n;
         sum += n;
     }
@@ -447,16 +457,17 @@ decode_stream_kernel(DecodeArgs a) {
         const int n = (int)min((int64_t)(nblk_b - blk0), u1 - u);
         const int kvh = grp * W + wi;
         const int L = seq_len_of(a, b);
+        const int64_t row = decode_row(a, b);          // >= 0: only decode rows own blocks
 
         WaveState<Chunk, Elem, G, QL> st;
         st.qs = q_lds[QL ? wi : 0];
-        load_query<Chunk, Elem, G, QL>(a, b, kvh, lane, st);
+        load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
         attend<Chunk, Elem, G, QL, NT>(a, kvh, a.block_table + (int64_t)b * a.bt_stride + blk0, n,
                                        blk0 * kBlock, L, pl, lane, st);
         if (blk0 == 0 && n == nblk_b) {
             finish<Chunk, Elem, G, QL>(st, lane,
-                                   reinterpret_cast<Elem*>(a.out) + ((int64_t)b * a.num_heads + (int64_t)kvh * G) * kHeadDim,
-                                   nullptr);
+                                       reinterpret_cast<Elem*>(a.out) + (row * a.num_heads + (int64_t)kvh * G) * kHeadDim,
+                                       nullptr);
         } else {
             const int slot = u == u0 ? 0 : 1;
             finish<Chunk, Elem, G, QL>(st, lane, nullptr,
@@ -509,12 +520,14 @@ merge_partitions_kernel(DecodeArgs a) {
     const int64_t b = item / Hq;
     const int h = (int)(item % Hq);
     if (b >= a.num_seqs) return;
+    const int64_t row = decode_row(a, b);
+    if (row < 0) return;
     const int L = seq_len_of(a, b);
     const int PT = a.partition_tokens;
     const int nparts = L <= 0 ? 1 : min((L + PT - 1) / PT, a.max_partitions);
     if (nparts <= 1) return;
     merge_pieces<Elem>(a.part, nparts, [&](int p) { return partition_record(a, b, h, p); }, lane,
-                       reinterpret_cast<Elem*>(a.out) + (b * Hq + h) * kHeadDim);
+                       reinterpret_cast<Elem*>(a.out) + (row * Hq + h) * kHeadDim);
 }
 
 template <typename Elem>
@@ -531,9 +544,11 @@ merge_stream_kernel(DecodeArgs a) {
     const int W = a.waves_per_group;
     const int NG = a.num_kv_heads / W;
     const int kvh = h / G, hg = h % G, grp = kvh / W, wi = kvh % W;
+    const int64_t row = decode_row(a, b);
+    if (row < 0) return;
     const int32_t pb = a.prefix[b];
     const int nblk = a.prefix[b + 1] - pb;
-    Elem* o = reinterpret_cast<Elem*>(a.out) + (b * Hq + h) * kHeadDim;
+    Elem* o = reinterpret_cast<Elem*>(a.out) + (row * Hq + h) * kHeadDim;
     if (nblk == 0) {                                   // empty sequence: zeros
         if constexpr (sizeof(Elem) == 2) *reinterpret_cast<uint32_t*>(o + 2 * lane) = 0u;
         else *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(0.f, 0.f);
@@ -555,10 +570,11 @@ merge_stream_kernel(DecodeArgs a) {
                        lane, o);
 }
 
-// Query rows live in LDS when registers would hold G x 16 bf16 of them per lane
-// (G = 8); below that they stay in registers.
+// Query rows live in LDS from G = 4 up: registers would hold G x 16 bf16 of
+// them per lane (16 copies of each, one per token lane), which at G = 4 costs a
+// third wave per SIMD.
 template <int G>
-constexpr bool kQueryInLds = G >= 8;
+constexpr bool kQueryInLds = G >= 4;
 
 template <typename Chunk, typename Elem, int G>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {

@@ -51,6 +51,29 @@ struct DecodeArgs {
     int32_t* prefix;               // [num_seqs + 1] blocks-per-KV-head prefix (written, then read)
     // partial records (split sequences only)
     float* part;
+    // Mixed batches: when set, [num_seqs + 1] offsets of each sequence's query
+    // rows; only sequences with exactly one query row are attended (their row
+    // and output row are cu_q[b]), the others are left to the prefill kernel.
+    const int32_t* cu_q;
+};
+
+struct PrefillArgs {
+    void* out;                     // [num_q_tokens, num_heads, 128]
+    const void* query;
+    int64_t q_stride;              // elements between query rows
+    const void* key_cache;
+    const void* value_cache;
+    const int32_t* block_table;
+    int32_t bt_stride;
+    int64_t num_blocks;
+    const int32_t* cu_query_lens;  // [num_seqs + 1]
+    const int32_t* seq_lens;       // [num_seqs]
+    int32_t num_seqs;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+    float scale_log2;
+    int32_t causal;
+    int32_t tiles_bound;           // >= number of query tiles: the grid is tiles_bound * num_kv_heads
 };
 
 // dtype: 0 = fp32, 1 = bf16.  group = num_heads / num_kv_heads in {1,2,4,8}.
@@ -58,6 +81,11 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t 
 
 // Workgroups of the stream-mode decode kernel one compute unit holds at once.
 int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int num_seqs);
+
+// Attention of every sequence with two or more query rows (bf16 only).
+hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
+// Query rows (tokens x grouped heads) per prefill workgroup tile.
+constexpr int kPrefillRows = 256;
 
 // Memory probes (bytes a multiple of 16, pointers 16-byte aligned).
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,

@@ -13,7 +13,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (decode_workspace, pa_decode, pa_reshape_and_cache, pa_slot_mapping)
+from . import (chunked_prefill_workspace, decode_workspace, pa_chunked_prefill, pa_decode,
+               pa_reshape_and_cache, pa_slot_mapping)
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -90,3 +91,19 @@ class DeviceWorkload:
             workspace = self.decode_workspace(partition_tokens)
         return pa_decode(out, self.query, self.key_cache, self.value_cache, self.block_table,
                          self.seq_lens, w.scale, w.max_seq_len, partition_tokens, workspace, stream)
+
+    def prefill_workspace(self):
+        w = self.w
+        return chunked_prefill_workspace(w.num_seqs, w.num_heads, w.num_kv_heads, w.head_dim, w.max_seq_len,
+                                         device=self.device)
+
+    def chunked_prefill(self, out=None, workspace=None, stream=None) -> torch.Tensor:
+        """Row a10: one call over the whole mixed batch (chunks and decodes)."""
+        w = self.w
+        if out is None:
+            out = torch.empty_like(self.query)
+        if workspace is None:
+            workspace = self.prefill_workspace()
+        return pa_chunked_prefill(out, self.query, self.key_cache, self.value_cache, self.block_table,
+                                  self.cu_query_lens, self.seq_lens, w.scale, w.max_query_len, w.max_seq_len,
+                                  w.causal, workspace, stream)

@@ -94,3 +94,35 @@ def test_scatter_and_slot_checks(L):
     assert L.pa_slot_mapping(16, 16, 4, 2, 16, 16, 0, 16, None) == pa.PA_OK
     assert L.pa_slot_mapping(16, 16, 4, 2, 16, 16, 3, 8, None) == pa.PA_ERR_UNSUPPORTED
     assert L.pa_slot_mapping(None, 16, 4, 2, 16, 16, 3, 16, None) == pa.PA_ERR_INVALID_ARG
+
+
+def _prefill(L, **kw):
+    args = dict(out=16, query=16, q_token_stride=4096, key_cache=16, value_cache=16, block_table=16,
+                max_blocks_per_req=8, cu_query_lens=16, seq_lens=16, num_seqs=2, num_q_tokens=40,
+                max_query_len=39, max_seq_len=100, num_heads=32, num_kv_heads=8, head_dim=128,
+                block_size=16, num_blocks=10, scale=0.088, causal=1, workspace=None, workspace_bytes=0,
+                dtype=1, stream=None)
+    args.update(kw)
+    return L.pa_chunked_prefill(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=0), pa.PA_ERR_UNSUPPORTED),                            # bf16 only
+    (dict(head_dim=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=8), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_heads=24), pa.PA_ERR_UNSUPPORTED),
+    (dict(causal=2), pa.PA_ERR_INVALID_ARG),
+    (dict(cu_query_lens=None), pa.PA_ERR_INVALID_ARG),
+    (dict(max_seq_len=200), pa.PA_ERR_INVALID_ARG),
+    (dict(query=8), pa.PA_ERR_INVALID_ARG),
+    (dict(num_q_tokens=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=float("inf")), pa.PA_ERR_INVALID_ARG),
+])
+def test_chunked_prefill_rejects_before_launch(L, kw, status):
+    assert _prefill(L, **kw) == status
+    assert pa.pa_last_error_message()
+
+
+def test_chunked_prefill_empty_is_ok(L):
+    assert _prefill(L, num_seqs=0) == pa.PA_OK
+    assert _prefill(L, num_q_tokens=0) == pa.PA_OK
