@@ -28,6 +28,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + seq-steps/s, 1 GPU"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+# Sources that define the decode kernels; the HBM traffic recorded under
+# profiles/ is reported only while they hash to the value recorded with it.
+DECODE_SOURCES = ["paged_kv_cache_432_amd/csrc/decode_kernel.hip", "paged_kv_cache_432_amd/csrc/device_common.h",
+                  "paged_kv_cache_432_amd/csrc/launch.h"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama8b_b64_1k-8k_traffic.json")
 
 
 def parse():
@@ -39,8 +44,56 @@ def parse():
                    choices=["llama8b_decode", "llama8b_decode_8k", "long_context", "continuous_batching"])
     p.add_argument("--partition-tokens", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-probes", action="store_true")
     p.add_argument("--cpu-sample-seqs", type=int, default=16)
     return p.parse_args()
+
+
+def decode_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for rel in DECODE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per pa_decode call from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    passes recorded under profiles/ (already scaled by the copy-kernel
+    factors), or None if they were taken on other kernel sources or another
+    workload."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != decode_sources_sha256() or rec.get("workload") != workload:
+        return None
+    return rec.get("hbm_bytes_per_call")
+
+
+def probes(pa, torch, nbytes: int = 2 << 30, iters: int = 10):
+    """The library's streaming read and copy probes on the same GPU: the
+    achievable HBM rate the decode kernel is set against."""
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, fn, moved in (("stream_read", lambda: pa.pa_probe_stream_read(buf, sink, 16384), nbytes),
+                            ("copy", lambda: pa.pa_probe_copy(buf[nbytes // 2:], buf[:nbytes // 2], 8192), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for a, b in ev:
+            a.record()
+            fn()
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+        out[name] = {"GBps": round(moved / us / 1e3, 1), "us": round(us, 1), "bytes": moved}
+    del buf
+    torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(w, nseq: int):
@@ -139,6 +192,8 @@ def main():
     kv = w.kv_bytes()
     gbps = kv / (ms_step * 1e-3) / 1e9
     dec_gbps = kv / (dec_avg_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(w.name)
+    probe = None if args.no_probes else probes(pa, torch)
     res = {
         "metric": METRIC,
         "value": round(gbps, 2),
@@ -167,17 +222,21 @@ def main():
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "roofline": {
-            "kernel": "pa_decode (partitioned decode kernel + log-sum-exp merge kernel)",
+            "kernel": "pa_decode: decode_stream_kernel + merge_stream_kernel (one call)" if pt == 0
+                      else "pa_decode: decode_partition_kernel + merge_partitions_kernel (one call)",
             "bound": "hbm",
             "achieved": round(dec_gbps, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": traffic,
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
             "algorithmic_bytes_per_launch": kv,
         },
     }
+    if probe is not None:
+        res["probes"] = probe
+        res["roofline"]["frac_of_read_probe"] = round(dec_gbps / probe["stream_read"]["GBps"], 4)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs)
     print(json.dumps(res), flush=True)

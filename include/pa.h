@@ -174,8 +174,9 @@ pa_status pa_decode(void *out, const void *query, int64_t q_token_stride,
  *   kv_head = h / (num_heads / num_kv_heads).
  * Requests with q_b == 1 run through the decode kernel (as pa_decode with
  * automatic splitting); requests with q_b >= 2 run on the matrix cores
- * (bf16 MFMA, fp32 accumulation, probabilities carried as a bf16 hi/lo pair);
- * q_b == 0 requests produce nothing.
+ * (bf16 MFMA, fp32 accumulation, probabilities carried as a bf16 hi/lo pair),
+ * long key ranges cut into pieces that the resident workgroups share evenly
+ * and merged with log-sum-exp weights; q_b == 0 requests produce nothing.
  *
  * out          [num_q_tokens, num_heads, head_dim] bf16, contiguous
  * query        [num_q_tokens, num_heads, head_dim] bf16; rows q_token_stride
@@ -188,11 +189,13 @@ pa_status pa_decode(void *out, const void *query, int64_t q_token_stride,
  * max_query_len, max_seq_len: host-side upper bounds of q_b and seq_lens
  * causal       1 (the chunked-prefill case) or 0
  * workspace    >= pa_chunked_prefill_workspace_bytes(...) bytes of device
- *              scratch (no initialisation needed)
+ *              scratch (no initialisation needed; 16-byte aligned); required
+ *              even when no request is split
  * dtype        PA_BF16 only (PA_ERR_UNSUPPORTED otherwise)
  */
-size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                          int32_t head_dim, int32_t max_seq_len);
+size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,
+                                          int32_t max_seq_len, int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim);
 pa_status pa_chunked_prefill(void *out, const void *query, int64_t q_token_stride,
                              const void *key_cache, const void *value_cache,
                              const int32_t *block_table, int32_t max_blocks_per_req,

@@ -76,7 +76,7 @@ def lib():
                                 _i32, _i64, ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t,
                                 ctypes.c_int, _vp]
         L.pa_chunked_prefill_workspace_bytes.restype = ctypes.c_size_t
-        L.pa_chunked_prefill_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32]
+        L.pa_chunked_prefill_workspace_bytes.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32]
         L.pa_chunked_prefill.restype = ctypes.c_int
         L.pa_chunked_prefill.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32,
                                          _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _vp,
@@ -221,16 +221,17 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
     return out
 
 
-def pa_chunked_prefill_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
-                                       max_seq_len: int) -> int:
-    return int(lib().pa_chunked_prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
-                                                        max_seq_len))
+def pa_chunked_prefill_workspace_bytes(num_seqs: int, num_q_tokens: int, max_query_len: int, max_seq_len: int,
+                                       num_heads: int, num_kv_heads: int, head_dim: int) -> int:
+    return int(lib().pa_chunked_prefill_workspace_bytes(num_seqs, num_q_tokens, max_query_len, max_seq_len,
+                                                        num_heads, num_kv_heads, head_dim))
 
 
-def chunked_prefill_workspace(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,
-                              max_seq_len: int, device="cuda") -> torch.Tensor | None:
-    nbytes = pa_chunked_prefill_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len)
-    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+def chunked_prefill_workspace(num_seqs: int, num_q_tokens: int, max_query_len: int, max_seq_len: int,
+                              num_heads: int, num_kv_heads: int, head_dim: int, device="cuda") -> torch.Tensor:
+    nbytes = pa_chunked_prefill_workspace_bytes(num_seqs, num_q_tokens, max_query_len, max_seq_len, num_heads,
+                                                num_kv_heads, head_dim)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
 def pa_chunked_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor,

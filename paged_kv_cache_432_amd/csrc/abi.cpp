@@ -138,6 +138,57 @@ size_t stream_ws_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
            (size_t)num_wg * 2 * waves * group * pa::kDecodeRecordFloats * sizeof(float);
 }
 
+
+// Prefill grid: query tiles (bounded from the host-side sizes) and KV-split
+// pieces, at most tiles + slots / num_kv_heads per KV head.
+struct PrefillShape { int64_t tiles, pieces_per_kvh; int32_t slots; };
+
+constexpr int32_t kPrefillMinPiece = 8;    // key tiles (512 keys)
+
+PrefillShape prefill_shape(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len, int32_t num_heads,
+                           int32_t num_kv_heads) {
+    const int32_t group = num_heads / num_kv_heads;
+    const int64_t tq = pa::kPrefillRows / group;
+    const int64_t half = num_q_tokens / 2;
+    const int64_t by_tokens = (num_q_tokens + tq - 1) / tq + (num_seqs < half ? num_seqs : half);
+    const int64_t by_seqs = (int64_t)num_seqs * ((max_query_len + tq - 1) / tq);
+    PrefillShape p{};
+    p.tiles = by_tokens < by_seqs ? by_tokens : by_seqs;
+    int32_t per_cu = 0;
+    {
+        static std::mutex mu;
+        static int cached_dev = -1, cached_group = 0, cached_kib = 0, cached_n = 0;
+        int dev = 0;
+        const int kib = (int)((((int64_t)num_seqs + 1) * 4 + 1023) / 1024);
+        if (hipGetDevice(&dev) == hipSuccess) {
+            std::lock_guard<std::mutex> lock(mu);
+            if (dev != cached_dev || group != cached_group || kib != cached_kib) {
+                cached_n = pa::prefill_blocks_per_cu(group, kib * 256 - 1);
+                cached_dev = dev, cached_group = group, cached_kib = kib;
+            }
+            per_cu = cached_n;
+        }
+    }
+    const int32_t cus = device_cus();
+    p.slots = per_cu > 0 && cus > 0 ? per_cu * cus : 0;
+    p.pieces_per_kvh = p.tiles + (p.slots + num_kv_heads - 1) / num_kv_heads;
+    return p;
+}
+
+// Prefill scratch: the pieces' partial records, then the split-tile list (a
+// count, then one 16-byte entry per possible split tile).
+size_t prefill_records_bytes(const PrefillShape& p, int32_t num_kv_heads) {
+    return (size_t)p.pieces_per_kvh * num_kv_heads * pa::kPrefillRows * pa::kDecodeRecordFloats * sizeof(float);
+}
+
+size_t prefill_list_entries(const PrefillShape& p, int32_t num_kv_heads) {
+    return (size_t)(p.pieces_per_kvh * num_kv_heads + 1) / 2;
+}
+
+size_t prefill_part_bytes(const PrefillShape& p, int32_t num_kv_heads) {
+    return prefill_records_bytes(p, num_kv_heads) + 16 + 16 * prefill_list_entries(p, num_kv_heads);
+}
+
 }  // namespace
 
 extern "C" {
@@ -339,9 +390,15 @@ pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const 
                          partition_tokens, workspace, workspace_bytes, dtype, stream);
 }
 
-size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                                          int32_t head_dim, int32_t max_seq_len) {
-    return pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len, 0);
+size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,
+                                          int32_t max_seq_len, int32_t num_heads, int32_t num_kv_heads,
+                                          int32_t head_dim) {
+    if (num_seqs <= 0 || num_q_tokens <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads)
+        return 0;
+    const size_t dec = align256(pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len, 0));
+    if (max_query_len < 2) return dec;
+    const PrefillShape ps = prefill_shape(num_seqs, num_q_tokens, max_query_len, num_heads, num_kv_heads);
+    return dec + prefill_part_bytes(ps, num_kv_heads);
 }
 
 pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
@@ -358,6 +415,7 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
         max_blocks_per_req < 0)
         return fail(PA_ERR_INVALID_ARG, "negative size");
     if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal %d (0 or 1)", causal);
+    if (num_kv_heads > 255) return fail(PA_ERR_UNSUPPORTED, "num_kv_heads %d (at most 255)", num_kv_heads);
     if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
         return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
@@ -373,21 +431,32 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
         !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
 
+    // workspace: the decode part's, then the prefill pieces' partial records
+    const size_t dec_bytes =
+        align256(pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len, 0));
+    PrefillShape ps{};
+    size_t need = dec_bytes;
+    if (max_query_len >= 2) {
+        ps = prefill_shape(num_seqs, num_q_tokens, max_query_len, num_heads, num_kv_heads);
+        if (ps.slots <= 0) return fail(PA_ERR_HIP, "cannot size the prefill grid for the current device");
+        if (ps.pieces_per_kvh * num_kv_heads > 0x7fffffff || ps.tiles * num_kv_heads > 0x7fffffff)
+            return fail(PA_ERR_INVALID_ARG, "grid too large");
+        need += prefill_part_bytes(ps, num_kv_heads);
+    }
+    if (!workspace || workspace_bytes < need)
+        return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0, need);
+    if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+
     // single-row sequences: the decode kernel, reading its rows through cu_query_lens
     pa_status st = decode_common(out, query, q_token_stride, key_cache, value_cache, block_table,
                                  max_blocks_per_req, seq_lens, cu_query_lens, num_seqs, num_heads, num_kv_heads,
-                                 num_blocks, scale, max_seq_len, 0, workspace, workspace_bytes, dtype, stream);
+                                 num_blocks, scale, max_seq_len, 0, workspace, dec_bytes, dtype, stream);
     if (st != PA_OK) return st;
     if (max_query_len < 2) return ok();
 
-    // sequences of two or more rows: the MFMA prefill kernel, one workgroup per
-    // (query tile, KV head); the grid bounds the tile count from the host-side sizes
+    // requests of two or more rows: the MFMA prefill kernel, one workgroup per
+    // (KV-split piece of a query tile, KV head), then the merge of split tiles
     const int32_t group = num_heads / num_kv_heads;
-    const int64_t tq = pa::kPrefillRows / group;
-    const int64_t by_tokens = (num_q_tokens + tq - 1) / tq + (num_seqs < num_q_tokens / 2 ? num_seqs : num_q_tokens / 2);
-    const int64_t by_seqs = (int64_t)num_seqs * ((max_query_len + tq - 1) / tq);
-    const int64_t tiles = by_tokens < by_seqs ? by_tokens : by_seqs;
-    if (tiles * num_kv_heads > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "grid too large");
     pa::PrefillArgs p{};
     p.out = out;
     p.query = query;
@@ -404,7 +473,14 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
     p.num_kv_heads = num_kv_heads;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);
     p.causal = causal;
-    p.tiles_bound = (int32_t)tiles;
+    p.tiles_bound = (int32_t)ps.tiles;
+    p.num_slots = ps.slots;
+    p.min_piece = kPrefillMinPiece;
+    p.pieces_per_kvh = (int32_t)ps.pieces_per_kvh;
+    p.part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + dec_bytes);
+    char* list = reinterpret_cast<char*>(workspace) + dec_bytes + prefill_records_bytes(ps, num_kv_heads);
+    p.split_count = reinterpret_cast<int32_t*>(list);
+    p.split_list = reinterpret_cast<int4*>(list + 16);
     return hip_status(pa::launch_prefill(p, group, stream), "prefill launch");
 }
 

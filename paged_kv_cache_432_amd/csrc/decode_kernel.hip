@@ -484,6 +484,7 @@ decode_stream_kernel(DecodeArgs a) {
 // record index of piece p of n.
 template <typename Elem, typename RecOf>
 __device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec_of, int lane, Elem* o) {
+    // pass over the pieces' (max, sum), 64 at a time, one per lane
     float M = -INFINITY;
     for (int p0 = 0; p0 < n; p0 += kWave) {
         const int p = p0 + lane;
@@ -493,15 +494,26 @@ __device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));
     float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-    for (int p = 0; p < n; ++p) {
-        const float* r = part + rec_of(p) * kRec;
-        const float2 ml = *reinterpret_cast<const float2*>(r + kHeadDim);
-        const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-        lsum = fmaf(w, ml.y, lsum);
-        const float2 v = *reinterpret_cast<const float2*>(r + 2 * lane);
-        o0 = fmaf(w, v.x, o0);
-        o1 = fmaf(w, v.y, o1);
+    for (int p0 = 0; p0 < n; p0 += kWave) {
+        // this lane's piece weight and weighted sum, then every piece's rows
+        // with weights broadcast by v_readlane (independent loads)
+        const int p = p0 + lane;
+        float w = 0.f;
+        if (p < n) {
+            const float2 ml = *reinterpret_cast<const float2*>(part + rec_of(p) * kRec + kHeadDim);
+            w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+            lsum = fmaf(w, ml.y, lsum);
+        }
+        const int cnt = min(kWave, n - p0);
+        for (int q = 0; q < cnt; ++q) {
+            const float wq = readlane_f(w, q);
+            const float2 v = *reinterpret_cast<const float2*>(part + rec_of(p0 + q) * kRec + 2 * lane);
+            o0 = fmaf(wq, v.x, o0);
+            o1 = fmaf(wq, v.y, o1);
+        }
     }
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) lsum += shfl_xor_f(lsum, d);
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
     if constexpr (sizeof(Elem) == 2) {
         *reinterpret_cast<uint32_t*>(o + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
@@ -570,11 +582,13 @@ merge_stream_kernel(DecodeArgs a) {
                        lane, o);
 }
 
-// Query rows live in LDS from G = 4 up: registers would hold G x 16 bf16 of
-// them per lane (16 copies of each, one per token lane), which at G = 4 costs a
-// third wave per SIMD.
+// Query rows live in LDS at G = 8, where registers would hold 8 x 16 bf16 of
+// them per lane (16 copies of each, one per token lane) and leave one wave per
+// SIMD.  At G = 4 they stay in registers: LDS reads on every block cost more
+// than the third wave per SIMD they would free (measured on the Llama-3-8B
+// decode shapes).
 template <int G>
-constexpr bool kQueryInLds = G >= 4;
+constexpr bool kQueryInLds = G >= 8;
 
 template <typename Chunk, typename Elem, int G>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {

@@ -19,10 +19,12 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (gfx950 converts in hardware).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> two bf16 in one word (lo in bits 0-15), round to nearest even:
+// one v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    __bf16 a = (__bf16)lo, b = (__bf16)hi;
-    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // Eight consecutive elements of one K/V/Q row, as one lane holds them.

@@ -73,7 +73,18 @@ struct PrefillArgs {
     int32_t num_kv_heads;
     float scale_log2;
     int32_t causal;
-    int32_t tiles_bound;           // >= number of query tiles: the grid is tiles_bound * num_kv_heads
+    int32_t tiles_bound;           // >= number of query tiles
+    // KV split: a query tile's key range is cut into pieces of at most P key
+    // tiles, P = max(min_piece, ceil(total key tiles / num_slots)), so that the
+    // resident workgroups share the work evenly; pieces of a split tile leave
+    // partial records merged by a second kernel.
+    int32_t num_slots;             // prefill workgroups resident on the device at once
+    int32_t min_piece;             // fewest key tiles per piece
+    int32_t pieces_per_kvh;        // grid = pieces_per_kvh * num_kv_heads >= pieces
+    float* part;                   // [pieces_per_kvh * num_kv_heads][256 rows][132] partial records
+    int32_t* split_count;          // number of split (tile, KV head) pairs listed (written by workgroup 0)
+    int4* split_list;              // [pieces_per_kvh * num_kv_heads / 2 + 1]: first piece, pieces, first row,
+                                   // (tokens << 8) | KV head
 };
 
 // dtype: 0 = fp32, 1 = bf16.  group = num_heads / num_kv_heads in {1,2,4,8}.
@@ -86,6 +97,8 @@ int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int n
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
 // Query rows (tokens x grouped heads) per prefill workgroup tile.
 constexpr int kPrefillRows = 256;
+// Prefill workgroups one compute unit holds at once (bf16, group size G).
+int prefill_blocks_per_cu(int group, int num_seqs);
 
 // Memory probes (bytes a multiple of 16, pointers 16-byte aligned).
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,

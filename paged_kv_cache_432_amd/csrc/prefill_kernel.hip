@@ -23,14 +23,22 @@
 //     4 keys of ONE query row, which is exactly the lane layout of the B
 //     operand of the next product, so the probabilities feed O^T += V^T P^T
 //     without another pass through LDS.
-//   * P is fed as two bf16 operands, hi = bf16(p) and lo = bf16(p - hi), so the
-//     product keeps ~16 bits of p: a single bf16 rounding of p alone would use
-//     most of the output's error budget on top of the bf16 output rounding.
+//   * P is fed as two bf16 operands, hi = p truncated to bf16 and
+//     lo = bf16(p - hi), so the product keeps ~16 bits of p: a single bf16
+//     rounding of p alone would use most of the output's error budget on top
+//     of the bf16 output rounding.
 //   * Causal masking selects -inf only on tiles that cross a row's limit; keys
 //     past seq_len are zero-filled in LDS (stale cache slots may hold NaN, and
 //     0 * NaN is NaN), and tiles wholly past a wave's rows are skipped.
-//   * Workgroups are numbered heaviest tile first (later tiles of a chunk see
-//     more keys), with the KV head as the fastest index, so the tiles of one
+//   * Work is balanced by cutting long key ranges: every workgroup computes
+//     the total number of 64-key tiles U the batch needs and a piece size
+//     P = max(min_piece, ceil(U / resident workgroups)); a query tile whose
+//     range exceeds P is cut into near-equal pieces, each its own workgroup,
+//     which leave (max, sum, unnormalised output) records per row, merged by
+//     a second kernel (log-sum-exp weights, the same merge as split decode)
+//     over a compact list of the split tiles (slot: split tiles before it).
+//   * Workgroups are numbered last piece first (later tiles of a chunk see
+//     more keys), with the KV head as the fastest index, so the pieces of one
 //     KV head land on one XCD and share its L2.
 #include <math.h>
 
@@ -56,82 +64,158 @@ constexpr int kThreads = kWaves * kWave;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
 
-__device__ __forceinline__ uint16_t bf16_bits(float f) {
-    return __builtin_bit_cast(uint16_t, (__bf16)f);
-}
+constexpr int kRec = 132;                    // partial record floats per row: 128 O, max, sum, pad
 
-// hi/lo bf16 pair of a probability: hi = bf16(p), lo = bf16(p - hi).
-__device__ __forceinline__ void split_bf16(float p, uint16_t& hi, uint16_t& lo) {
-    const __bf16 h = (__bf16)p;
-    hi = __builtin_bit_cast(uint16_t, h);
-    lo = bf16_bits(p - (float)h);
-}
-
-// Prefix over sequences of the number of query tiles each needs (sequences with
-// fewer than two query rows need none), in s_pref[0..B].
-__device__ __forceinline__ void tile_prefix(const PrefillArgs& a, int tq, int32_t* s_pref, int32_t* s_wsum) {
-    const int B = a.num_seqs;
-    const int tid = threadIdx.x;
-    const int per = (B + kThreads - 1) / kThreads;
-    const int lo = min(tid * per, B), hi = min(lo + per, B);
-    int sum = 0;
-    for (int i = lo; i < hi; ++i) {
-        const int q = a.cu_query_lens[i + 1] - a.cu_query_lens[i];
-        const int n = q >= 2 ? (q + tq - 1) / tq : 0;
-        s_pref[i + 1] = n;
-        sum += n;
-    }
-    const int lane = tid & 63, wave = tid >> 6;
-    int x = sum;
+// Exclusive prefix over the workgroup's threads of `x` (every thread calls).
+__device__ __forceinline__ int block_exclusive_scan(int x, int32_t* s_wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int y = x;
 #pragma unroll
     for (int d = 1; d < kWave; d <<= 1) {
-        const int y = __shfl_up(x, d, kWave);
-        if (lane >= d) x += y;
+        const int t = __shfl_up(y, d, kWave);
+        if (lane >= d) y += t;
     }
-    if (lane == kWave - 1) s_wsum[wave] = x;
+    __syncthreads();                                   // s_wsum free from any earlier use
+    if (lane == kWave - 1) s_wsum[wave] = y;
     __syncthreads();
-    int before = x - sum;
+    int before = y - x;
     for (int w = 0; w < wave; ++w) before += s_wsum[w];
-    for (int i = lo; i < hi; ++i) {
-        before += s_pref[i + 1];
-        s_pref[i + 1] = before;
-    }
-    if (tid == 0) s_pref[0] = 0;
+    return before;
+}
+
+__device__ __forceinline__ int block_sum(int x, int32_t* s_wsum) {
+    const int before = block_exclusive_scan(x, s_wsum);
     __syncthreads();
+    if (threadIdx.x == blockDim.x - 1) s_wsum[0] = before + x;
+    __syncthreads();
+    return s_wsum[0];
+}
+
+struct SeqShape {
+    int q0, qlen, L;
+};
+
+__device__ __forceinline__ SeqShape seq_shape(const PrefillArgs& a, int b) {
+    SeqShape sh;
+    sh.q0 = a.cu_query_lens[b];
+    sh.qlen = a.cu_query_lens[b + 1] - sh.q0;
+    sh.L = max(min(a.seq_lens[b], a.bt_stride * kBlock), 0);
+    return sh;
+}
+
+__device__ __forceinline__ int tiles_of(const SeqShape& sh, int tq) {
+    return sh.qlen >= 2 ? (sh.qlen + tq - 1) / tq : 0;
+}
+
+// Key limit of query tile t (one past the last key any of its rows sees).
+__device__ __forceinline__ int tile_kend(const PrefillArgs& a, const SeqShape& sh, int t, int tq) {
+    if (!a.causal) return sh.L;
+    const int last = min(sh.qlen, (t + 1) * tq);         // rows t*tq .. last-1
+    return max(min(sh.L - sh.qlen + last, sh.L), 0);
+}
+
+__device__ __forceinline__ int tile_pieces(int nkt, int P) { return nkt > 0 ? (nkt + P - 1) / P : 1; }
+
+// The batch's piece map, built by every workgroup: s_pp[b] = first piece of
+// sequence b (s_pp[B] = total), s_sp[b] = split tiles (more than one piece)
+// before sequence b (s_sp[B] = total).  Returns the piece size P in key tiles.
+__device__ __forceinline__ int build_piece_map(const PrefillArgs& a, int tq, int32_t* s_pp, int32_t* s_sp,
+                                               int32_t* s_wsum) {
+    const int B = a.num_seqs;
+    const int nthr = blockDim.x;
+    const int per = (B + nthr - 1) / nthr;
+    const int lo = min((int)threadIdx.x * per, B), hi = min(lo + per, B);
+    int units = 0;
+    for (int b = lo; b < hi; ++b) {
+        const SeqShape sh = seq_shape(a, b);
+        const int nt = tiles_of(sh, tq);
+        for (int t = 0; t < nt; ++t) units += (tile_kend(a, sh, t, tq) + kKeys - 1) / kKeys;
+    }
+    const int total = block_sum(units, s_wsum);       // key tiles per KV head
+    const int64_t all = (int64_t)total * a.num_kv_heads;
+    const int P = max(a.min_piece, (int)((all + a.num_slots - 1) / a.num_slots));
+    int pieces = 0, splits = 0;
+    for (int b = lo; b < hi; ++b) {
+        const SeqShape sh = seq_shape(a, b);
+        const int nt = tiles_of(sh, tq);
+        int pb = 0, sb = 0;
+        for (int t = 0; t < nt; ++t) {
+            const int np = tile_pieces((tile_kend(a, sh, t, tq) + kKeys - 1) / kKeys, P);
+            pb += np;
+            sb += np > 1;
+        }
+        s_pp[b + 1] = pb;
+        s_sp[b + 1] = sb;
+        pieces += pb;
+        splits += sb;
+    }
+    int run = block_exclusive_scan(pieces, s_wsum);
+    for (int b = lo; b < hi; ++b) {
+        run += s_pp[b + 1];
+        s_pp[b + 1] = run;
+    }
+    run = block_exclusive_scan(splits, s_wsum);
+    for (int b = lo; b < hi; ++b) {
+        run += s_sp[b + 1];
+        s_sp[b + 1] = run;
+    }
+    if (threadIdx.x == 0) {
+        s_pp[0] = 0;
+        s_sp[0] = 0;
+    }
+    __syncthreads();
+    return P;
+}
+
+// The largest b with pref[b] <= x (pref non-decreasing, pref[0] = 0 <= x).
+__device__ __forceinline__ int find_seq(const int32_t* pref, int B, int x) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pref[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
 }
 
 template <int G>
 __global__ void __launch_bounds__(kThreads)
 prefill_kernel(PrefillArgs a) {
     constexpr int TQ = kPrefillRows / G;               // tokens per tile
-    extern __shared__ __attribute__((aligned(16))) int32_t s_pref[];      // [num_seqs + 1]
+    extern __shared__ __attribute__((aligned(16))) int32_t s_dyn[];
+    int32_t* s_pref = s_dyn;                           // [num_seqs + 1] piece prefix
+    int32_t* s_split = s_dyn + a.num_seqs + 1;         // [num_seqs + 1] split-tile prefix
     __shared__ int32_t s_wsum[kWaves];
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kVTileElems];
 
-    tile_prefix(a, TQ, s_pref, s_wsum);
+    const int P = build_piece_map(a, TQ, s_pref, s_split, s_wsum);
     const int B = a.num_seqs;
     const int Hkv = a.num_kv_heads;
-    const int T = s_pref[B];
+    const int npieces = s_pref[B];
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.split_count = s_split[B] * Hkv;
     const int kvh = (int)(blockIdx.x % Hkv);
-    const int t_rev = (int)(blockIdx.x / Hkv);
-    if (t_rev >= T) return;                            // whole workgroup: no barrier is left behind
-    const int t = T - 1 - t_rev;
-    int lo = 0, hi = B - 1;                            // the largest b with s_pref[b] <= t
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pref[mid] <= t) lo = mid; else hi = mid - 1;
+    const int rev = (int)(blockIdx.x / Hkv);
+    if (rev >= npieces) return;                        // whole workgroup: no barrier is left behind
+    const int piece = npieces - 1 - rev;
+    const int b = find_seq(s_pref, B, piece);
+    const SeqShape sh = seq_shape(a, b);
+    // the tile and the piece within it
+    int tile = 0, j = piece - s_pref[b], nkt = 0, np = 1, split_before = s_split[b];
+    for (const int nt = tiles_of(sh, TQ); tile < nt; ++tile) {
+        nkt = (tile_kend(a, sh, tile, TQ) + kKeys - 1) / kKeys;
+        np = tile_pieces(nkt, P);
+        if (j < np) break;
+        j -= np;
+        split_before += np > 1;
     }
-    const int b = lo;
-    const int tile = t - s_pref[b];
-    const int q0 = a.cu_query_lens[b];
-    const int qlen = a.cu_query_lens[b + 1] - q0;
-    const int L = max(min(a.seq_lens[b], a.bt_stride * kBlock), 0);
+    const int psz = (nkt + np - 1) / np;
+    const int kt_begin = j * psz;
+    const int kt_end = min(nkt, kt_begin + psz);
+    const int q0 = sh.q0, qlen = sh.qlen, L = sh.L;
     const int tok_begin = tile * TQ;
     const int ntok = min(TQ, qlen - tok_begin);
     const int prior = L - qlen;                        // position of query row 0
-    const int kend_wg = a.causal ? max(min(L, prior + tok_begin + ntok), 0) : L;
-    const int nkt = (kend_wg + kKeys - 1) / kKeys;
+    const int kend_wg = tile_kend(a, sh, tile, TQ);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -176,26 +260,56 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int n = 0; n < 2; ++n) oacc[dt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-    // ---- K/V tile staging: 1024 16-byte chunks per tensor, two per thread
+    // ---- K/V tile staging.  K: 1024 16-byte chunks (row, 16-byte part), two per
+    // thread, stored row-major.  V: thread (dim pair dp, key quads kq, kq + 8)
+    // loads the 4-byte (dims 2dp, 2dp+1) word of each key of its quads -- a
+    // wave reads whole 256-byte rows -- and packs them into 4-key runs of the
+    // two V^T rows, stored with 8-byte writes.
     const char* kc = reinterpret_cast<const char*>(a.key_cache);
     const char* vc = reinterpret_cast<const char*>(a.value_cache);
     const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
     const int64_t tok_bytes = (int64_t)Hkv * kHeadDim * 2;
-    u32x4_t kreg[2], vreg[2];
+    const int64_t head_off = (int64_t)kvh * kHeadDim * 2;
+    const int dp = tid & 63, kq = tid >> 6;
+    u32x4_t kreg[2];
+    uint32_t vw[2][4];
+    // Block ids of the key range, 64 at a time (one per lane): a wave's loads
+    // of a tile need 2 ids for K and 2 for V, each the same for all its lanes,
+    // broadcast with v_readlane, so that the tile's 10 loads issue back to
+    // back instead of each waiting on its own table read.
+    const int nblk_wg = (kend_wg + kBlock - 1) / kBlock;
+    int bid_base = -kWave;                             // first block held in bid
+    int bid = 0;
+    auto block_of = [&](int blk) -> int64_t {          // blk in [bid_base, bid_base + 64)
+        const int64_t id = __builtin_amdgcn_readlane(bid, blk - bid_base);
+        return min(max(id, (int64_t)0), a.num_blocks - 1);
+    };
     auto stage = [&](int kt) {
+        if (4 * kt + 3 >= bid_base + kWave) {          // wave-uniform: the tile's ids are not all held
+            bid_base = 4 * kt;
+            bid = bid_base + lane < nblk_wg ? bt[bid_base + lane] : 0;
+        }
+        const int kwave_blk = 4 * kt + (tid >> 8);     // K chunk j covers block kwave_blk + 2j
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c = tid + j * kThreads;
             const int key = kt * kKeys + (c >> 4);
-            const int part = c & 15;
-            if (key < kend_wg) {
-                const int64_t phys = min(max((int64_t)bt[key / kBlock], (int64_t)0), a.num_blocks - 1);
-                const int64_t off = (phys * kBlock + key % kBlock) * tok_bytes + (int64_t)kvh * kHeadDim * 2 + part * 16;
-                kreg[j] = *reinterpret_cast<const u32x4_t*>(kc + off);
-                vreg[j] = *reinterpret_cast<const u32x4_t*>(vc + off);
-            } else {
-                kreg[j] = u32x4_t{0u, 0u, 0u, 0u};         // past the keys: zeros, never stale data
-                vreg[j] = u32x4_t{0u, 0u, 0u, 0u};
+            const int64_t phys = block_of(kwave_blk + 2 * j);
+            kreg[j] = key < kend_wg
+                          ? *reinterpret_cast<const u32x4_t*>(kc + (phys * kBlock + key % kBlock) * tok_bytes +
+                                                              head_off + (c & 15) * 16)
+                          : u32x4_t{0u, 0u, 0u, 0u};   // past the keys: zeros, never stale data
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int q = kq + 8 * j;                  // key quad of the tile; block 4kt + q/4
+            const int64_t phys = block_of(4 * kt + q / 4);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int key = kt * kKeys + 4 * q + i;
+                vw[j][i] = key < kend_wg ? *reinterpret_cast<const uint32_t*>(
+                                               vc + (phys * kBlock + key % kBlock) * tok_bytes + head_off + dp * 4)
+                                         : 0u;
             }
         }
     };
@@ -203,30 +317,28 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c = tid + j * kThreads;
-            const int key = c >> 4, part = c & 15;
-            *reinterpret_cast<u32x4_t*>(&k_lds[buf][key * kKStride + part * 8]) = kreg[j];
-            uint16_t* vt = &v_lds[buf][(part * 8) * kVStride + key];
-            const u32x4_t w = vreg[j];
-            vt[0 * kVStride] = (uint16_t)(w.x & 0xffffu);
-            vt[1 * kVStride] = (uint16_t)(w.x >> 16);
-            vt[2 * kVStride] = (uint16_t)(w.y & 0xffffu);
-            vt[3 * kVStride] = (uint16_t)(w.y >> 16);
-            vt[4 * kVStride] = (uint16_t)(w.z & 0xffffu);
-            vt[5 * kVStride] = (uint16_t)(w.z >> 16);
-            vt[6 * kVStride] = (uint16_t)(w.w & 0xffffu);
-            vt[7 * kVStride] = (uint16_t)(w.w >> 16);
+            *reinterpret_cast<u32x4_t*>(&k_lds[buf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t* w = vw[j];
+            const u32x2_t even = u32x2_t{(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
+            const u32x2_t odd = u32x2_t{(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
+            uint16_t* vt = &v_lds[buf][(2 * dp) * kVStride + 4 * (kq + 8 * j)];
+            *reinterpret_cast<u32x2_t*>(vt) = even;
+            *reinterpret_cast<u32x2_t*>(vt + kVStride) = odd;
         }
     };
 
-    if (nkt > 0) {
-        stage(0);
+    if (kt_begin < kt_end) {
+        stage(kt_begin);
         commit(0);
     }
     __syncthreads();
 
-    for (int kt = 0; kt < nkt; ++kt) {
-        const int buf = kt & 1;
-        if (kt + 1 < nkt) stage(kt + 1);
+    for (int kt = kt_begin; kt < kt_end; ++kt) {
+        const int buf = (kt - kt_begin) & 1;
+        if (kt + 1 < kt_end) stage(kt + 1);
         const int key0 = kt * kKeys;
         if (key0 < kmax) {
             // S^T = K Q^T over this tile: 4 key tiles x 2 row tiles x 4 dim steps
@@ -248,53 +360,64 @@ prefill_kernel(PrefillArgs a) {
                 }
             }
 
-            // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr
-            const bool masked = key0 + kKeys > kmin;
+            // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr.
+            // The max is taken on raw scores (scale > 0) and the scale folded
+            // into the exponent: p = 2^(s * scale_log2 - m).
+            if (key0 + kKeys > kmin) {                 // a row's limit falls in this tile
+#pragma unroll
+                for (int n = 0; n < 2; ++n)
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int r = 0; r < 4; ++r)
+                            if (key0 + 16 * mt + 4 * g + r >= kend[n]) sacc[mt][n][r] = -INFINITY;
+            }
             u32x4_t phi[2][2], plo[2][2];              // B operands of P^T: [row tile][key step]
             bool rescale = false;
             float alpha[2];
 #pragma unroll
             for (int n = 0; n < 2; ++n) {
-                float s[4][4];
                 float mx = -INFINITY;
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        float v = sacc[mt][n][r] * a.scale_log2;
-                        if (masked && key0 + 16 * mt + 4 * g + r >= kend[n]) v = -INFINITY;
-                        s[mt][r] = v;
-                        mx = fmaxf(mx, v);
-                    }
+                    mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][n][0], sacc[mt][n][1])),
+                               fmaxf(sacc[mt][n][2], sacc[mt][n][3]));
                 mx = fmaxf(mx, shfl_xor_f(mx, 16));
                 mx = fmaxf(mx, shfl_xor_f(mx, 32));
-                const float mn = fmaxf(m[n], mx);
+                const float mn = fmaxf(m[n], mx * a.scale_log2);
                 const bool none = mn == -INFINITY;     // nothing visible yet in this row
+                const float msafe = none ? 0.f : mn;   // then every score is -inf and p = 0
                 alpha[n] = none ? 1.f : __builtin_amdgcn_exp2f(m[n] - mn);
                 rescale |= alpha[n] != 1.f;
                 m[n] = mn;
                 float sum = 0.f;
-                uint16_t hb[4][4], lb[4][4];
+                float pv[4][4];
 #pragma unroll
                 for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                     for (int r = 0; r < 4; ++r) {
-                        const float p = none ? 0.f : __builtin_amdgcn_exp2f(s[mt][r] - mn);
-                        sum += p;
-                        split_bf16(p, hb[mt][r], lb[mt][r]);
+                        pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][r], a.scale_log2, -msafe));
+                        sum += pv[mt][r];
                     }
                 lp[n] = lp[n] * alpha[n] + sum;
+                // hi = p truncated to bf16 (its top 16 bits), lo = bf16(p - hi):
+                // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
 #pragma unroll
                 for (int ks = 0; ks < 2; ++ks) {
-                    // key slots: 4 keys of tile 2ks, then 4 keys of tile 2ks+1
-                    phi[n][ks] = u32x4_t{(uint32_t)hb[2 * ks][0] | ((uint32_t)hb[2 * ks][1] << 16),
-                                         (uint32_t)hb[2 * ks][2] | ((uint32_t)hb[2 * ks][3] << 16),
-                                         (uint32_t)hb[2 * ks + 1][0] | ((uint32_t)hb[2 * ks + 1][1] << 16),
-                                         (uint32_t)hb[2 * ks + 1][2] | ((uint32_t)hb[2 * ks + 1][3] << 16)};
-                    plo[n][ks] = u32x4_t{(uint32_t)lb[2 * ks][0] | ((uint32_t)lb[2 * ks][1] << 16),
-                                         (uint32_t)lb[2 * ks][2] | ((uint32_t)lb[2 * ks][3] << 16),
-                                         (uint32_t)lb[2 * ks + 1][0] | ((uint32_t)lb[2 * ks + 1][1] << 16),
-                                         (uint32_t)lb[2 * ks + 1][2] | ((uint32_t)lb[2 * ks + 1][3] << 16)};
+                    uint32_t hw[4], lw[4];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {          // key tile 2ks + h: slots 4h .. 4h+3
+                        const float* q4 = pv[2 * ks + h];
+#pragma unroll
+                        for (int r2 = 0; r2 < 2; ++r2) {
+                            const uint32_t u0 = __float_as_uint(q4[2 * r2]), u1 = __float_as_uint(q4[2 * r2 + 1]);
+                            hw[2 * h + r2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+                            lw[2 * h + r2] = pack_bf16x2(q4[2 * r2] - __uint_as_float(u0 & 0xffff0000u),
+                                                         q4[2 * r2 + 1] - __uint_as_float(u1 & 0xffff0000u));
+                        }
+                    }
+                    phi[n][ks] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+                    plo[n][ks] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                 }
             }
             if (__builtin_amdgcn_ballot_w64(rescale)) {
@@ -324,36 +447,109 @@ prefill_kernel(PrefillArgs a) {
                 }
             }
         }
-        if (kt + 1 < nkt) commit(buf ^ 1);
+        if (kt + 1 < kt_end) commit(buf ^ 1);
         __syncthreads();
     }
 
-    // ---- normalise and store: lane holds dims 16dt + 4g .. +4 of row 16n + lr
+    // ---- finish: lane holds dims 16dt + 4g .. +4 of row 16n + lr.  A whole
+    // tile normalises and writes bf16 rows.  A piece of a split tile writes its
+    // (unnormalised rows, max, sum) record, and the tile's first piece lists the
+    // tile for the merge kernel.
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
         float l = lp[n];
         l += shfl_xor_f(l, 16);
         l += shfl_xor_f(l, 32);
         if (!active[n]) continue;
-        const float inv = l > 0.f ? 1.f / l : 0.f;
         const int r = wave * kRowsPerWave + 16 * n + lr;
-        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(q0 + tok_begin + tq[n]) * Hq * kHeadDim +
-                      (int64_t)(kvh * G + r % G) * kHeadDim + 4 * g;
+        if (np == 1) {
+            const float inv = l > 0.f ? 1.f / l : 0.f;
+            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(q0 + tok_begin + tq[n]) * Hq * kHeadDim +
+                          (int64_t)(kvh * G + r % G) * kHeadDim + 4 * g;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt) {
-            const f32x4_t v = oacc[dt][n];
-            *reinterpret_cast<u32x2_t*>(o + 16 * dt) =
-                u32x2_t{pack_bf16x2(v.x * inv, v.y * inv), pack_bf16x2(v.z * inv, v.w * inv)};
+            for (int dt = 0; dt < 8; ++dt) {
+                const f32x4_t v = oacc[dt][n];
+                *reinterpret_cast<u32x2_t*>(o + 16 * dt) =
+                    u32x2_t{pack_bf16x2(v.x * inv, v.y * inv), pack_bf16x2(v.z * inv, v.w * inv)};
+            }
+        } else {
+            float* rec = a.part + (((int64_t)piece * Hkv + kvh) * kPrefillRows + r) * kRec;
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = oacc[dt][n];
+            if (g == 0) *reinterpret_cast<float2*>(rec + kHeadDim) = make_float2(m[n], l);
         }
+    }
+    if (np > 1 && j == 0 && tid == 0)
+        a.split_list[split_before * Hkv + kvh] = int4{piece, np, q0 + tok_begin, (ntok << 8) | kvh};
+}
+
+// Log-sum-exp merge of the pieces of every split query tile: per row,
+// M = max_p m_p, out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p, taken in
+// one pass with a running max.  Four workgroups per listed (tile, KV head),
+// 64 rows each; thread i covers dims 4(i % 32) .. +4 of rows i / 32 + 8k.
+template <int G>
+__global__ void __launch_bounds__(256)
+prefill_merge_kernel(PrefillArgs a) {
+    const int e = (int)(blockIdx.x >> 2);
+    if (e >= *a.split_count) return;
+    const int4 d = a.split_list[e];
+    const int first = d.x, np = d.y, row0 = d.z, ntok = d.w >> 8, kvh = d.w & 255;
+    const int Hkv = a.num_kv_heads;
+    const int d4 = 4 * (threadIdx.x & 31);
+    const int rbeg = 64 * (int)(blockIdx.x & 3);
+    for (int r = rbeg + (int)(threadIdx.x >> 5); r < rbeg + 64; r += 8) {
+        const int tq = r / G;
+        if (tq >= ntok) break;                         // rows are token-major: the rest are inactive
+        float mrun = -INFINITY, lrun = 0.f;
+        f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int p0 = 0; p0 < np; p0 += 4) {
+            float2 ml[4];
+            f32x4_t ov[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (p0 + i < np) {
+                    const float* rec = a.part + (((int64_t)(first + p0 + i) * Hkv + kvh) * kPrefillRows + r) * kRec;
+                    ml[i] = *reinterpret_cast<const float2*>(rec + kHeadDim);
+                    ov[i] = *reinterpret_cast<const f32x4_t*>(rec + d4);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (p0 + i < np) {
+                    const float mn = fmaxf(mrun, ml[i].x);
+                    const float wa = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+                    const float wb = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[i].x - mn);
+                    lrun = wa * lrun + wb * ml[i].y;
+                    o = wa * o + wb * ov[i];
+                    mrun = mn;
+                }
+            }
+        }
+        const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(row0 + tq) * a.num_heads * kHeadDim +
+                        (int64_t)(kvh * G + r % G) * kHeadDim + d4;
+        *reinterpret_cast<u32x2_t*>(out) = u32x2_t{pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv)};
     }
 }
 
 template <int G>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
-    const size_t lds = sizeof(int32_t) * ((size_t)a.num_seqs + 1);
-    const int64_t grid = (int64_t)a.tiles_bound * a.num_kv_heads;
+    const size_t lds = 2 * sizeof(int32_t) * ((size_t)a.num_seqs + 1);
+    const int64_t grid = (int64_t)a.pieces_per_kvh * a.num_kv_heads;
     hipLaunchKernelGGL((prefill_kernel<G>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // a split tile has at least two pieces: at most grid / 2 tiles are listed
+    hipLaunchKernelGGL((prefill_merge_kernel<G>), dim3((unsigned)(4 * ((grid + 1) / 2))), dim3(256), 0, stream, a);
     return hipGetLastError();
+}
+
+template <int G>
+int blocks_per_cu(int num_seqs) {
+    int n = 0;
+    const size_t lds = 2 * sizeof(int32_t) * ((size_t)num_seqs + 1);
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, prefill_kernel<G>, kThreads, lds) != hipSuccess) return 0;
+    return n;
 }
 
 }  // namespace
@@ -365,6 +561,16 @@ hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream) {
         case 4: return launch_typed<4>(a, stream);
         case 8: return launch_typed<8>(a, stream);
         default: return hipErrorInvalidValue;
+    }
+}
+
+int prefill_blocks_per_cu(int group, int num_seqs) {
+    switch (group) {
+        case 1: return blocks_per_cu<1>(num_seqs);
+        case 2: return blocks_per_cu<2>(num_seqs);
+        case 4: return blocks_per_cu<4>(num_seqs);
+        case 8: return blocks_per_cu<8>(num_seqs);
+        default: return 0;
     }
 }
 
