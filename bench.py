@@ -11,7 +11,11 @@ Default workload: Llama-3-8B decode layer, batch 64, context lengths uniform
 in [1024, 8192], bf16 (32 query heads, 8 KV heads, head_dim 128, 16-token
 blocks).  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-probes]
+
+With --workload chunked_prefill_mix a step is the scatter plus one
+pa_chunked_prefill call over 4 prefill chunks and 96 decodes; the chunks are
+also reported against the bf16 matrix peak.
 """
 from __future__ import annotations
 
@@ -28,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + seq-steps/s, 1 GPU"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 # Sources that define the decode kernels; the HBM traffic recorded under
 # profiles/ is reported only while they hash to the value recorded with it.
 DECODE_SOURCES = ["paged_kv_cache_432_amd/csrc/decode_kernel.hip", "paged_kv_cache_432_amd/csrc/device_common.h",
@@ -41,7 +46,8 @@ def parse():
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=50)
     p.add_argument("--workload", default="llama8b_decode",
-                   choices=["llama8b_decode", "llama8b_decode_8k", "long_context", "continuous_batching"])
+                   choices=["llama8b_decode", "llama8b_decode_8k", "long_context", "continuous_batching",
+                            "chunked_prefill_mix"])
     p.add_argument("--partition-tokens", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probes", action="store_true")
@@ -73,14 +79,17 @@ def recorded_traffic(workload: str):
     return rec.get("hbm_bytes_per_call")
 
 
-def probes(pa, torch, nbytes: int = 2 << 30, iters: int = 10):
-    """The library's streaming read and copy probes on the same GPU: the
-    achievable HBM rate the decode kernel is set against."""
+def probes(pa, torch, nbytes: int = 4 << 30, iters: int = 10):
+    """The library's streaming read probe (all of a 4 GiB buffer, 16384
+    workgroups) and copy probe (1 GiB each way) on the same GPU: the achievable
+    HBM rates the decode kernel is set against.  The copy is also the transfer
+    of known size that the traffic counters are scaled by."""
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    gib = 1 << 30
     out = {}
     for name, fn, moved in (("stream_read", lambda: pa.pa_probe_stream_read(buf, sink, 16384), nbytes),
-                            ("copy", lambda: pa.pa_probe_copy(buf[nbytes // 2:], buf[:nbytes // 2], 8192), nbytes)):
+                            ("copy", lambda: pa.pa_probe_copy(buf[gib:2 * gib], buf[:gib], 8192), 2 * gib)):
         fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
@@ -138,6 +147,119 @@ def cpu_baseline(w, nseq: int):
     }
 
 
+def event_timed(torch, fn, steps: int, warmup: int, stream):
+    """Mean HIP-event time (ms) of fn() over `steps` calls on `stream`, after
+    `warmup` untimed calls."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean([a.elapsed_time(b) for a, b in ev]))
+
+
+def causal_flops(w) -> int:
+    """Algorithmic flops of the multi-row requests: 4 * head_dim per (query,
+    key) pair each row attends, per query head (QK^T and PV)."""
+    pairs = 0
+    for b in range(w.num_seqs):
+        q, L = int(w.query_lens[b]), int(w.seq_lens[b])
+        if q < 2:
+            continue
+        pairs += sum(min(L, L - q + j + 1) for j in range(q)) if w.causal else q * L
+    return pairs * w.num_heads * w.head_dim * 4
+
+
+def main_mixed(args, w, torch, pa, W, DeviceWorkload):
+    """The chunked-prefill + decode mix: one step is the scatter of every new
+    row and one pa_chunked_prefill call over the whole batch.  The chunks and
+    the decodes are also timed as the two calls of the split-call mode, the
+    chunks against the bf16 matrix peak and the decodes against HBM."""
+    stream = torch.cuda.current_stream()
+    dw = DeviceWorkload(w)
+    out = torch.empty_like(dw.query)
+    ws = dw.prefill_workspace()
+    torch.cuda.synchronize()
+
+    def step(ev=None):
+        dw.scatter_new(stream)
+        if ev is not None:
+            ev[0].record(stream)
+        dw.chunked_prefill(out, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    call_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
+    del dw, out, ws
+    torch.cuda.empty_cache()
+
+    pre, dec = W.prefill_part(w), W.decode_part(w)
+    dpre = DeviceWorkload(pre)
+    dpre.scatter_new(stream)
+    opre, wspre = torch.empty_like(dpre.query), dpre.prefill_workspace()
+    pre_ms = event_timed(torch, lambda: dpre.chunked_prefill(opre, wspre, stream), args.steps, args.warmup, stream)
+    del dpre, opre, wspre
+    torch.cuda.empty_cache()
+    ddec = DeviceWorkload(dec)
+    ddec.scatter_new(stream)
+    odec, wsdec = torch.empty_like(ddec.query), ddec.decode_workspace(0)
+    dec_ms = event_timed(torch, lambda: ddec.decode(odec, 0, wsdec, stream), args.steps, args.warmup, stream)
+    del ddec, odec, wsdec
+    torch.cuda.empty_cache()
+
+    kv = w.kv_bytes()
+    flops = causal_flops(pre)
+    tflops = flops / (pre_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(kv / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded N(0,1) values, random block placement; no dataset)",
+        "config": {
+            "workload": w.name, "batch": w.num_seqs, "query_rows": int(w.num_q_tokens),
+            "chunks": int(np.sum(w.query_lens > 1)), "decodes": int(np.sum(w.query_lens == 1)),
+            "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "pool_blocks": w.num_blocks, "kv_bytes_per_step": kv,
+        },
+        "unified_call_us": round(call_ms * 1e3, 2),
+        "roofline": {
+            "kernel": "pa_chunked_prefill over the chunks: prefill_kernel + prefill_merge_kernel",
+            "bound": "mfma",
+            "achieved": round(tflops, 2),
+            "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "avg_launch_us": round(pre_ms * 1e3, 2),
+            "algorithmic_flops_per_launch": flops,
+        },
+        "decode_part": {
+            "kernel": "pa_decode over the single-row requests",
+            "bound": "hbm", "avg_launch_us": round(dec_ms * 1e3, 2),
+            "GBps": round(dec.kv_bytes() / (dec_ms * 1e-3) / 1e9, 2),
+            "frac": round(dec.kv_bytes() / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes_per_launch": dec.kv_bytes(),
+        },
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -153,6 +275,8 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pa.lib()
     w = W.CONFIGS[args.workload]()
+    if not w.is_decode:
+        return main_mixed(args, w, torch, pa, W, DeviceWorkload)
     t_setup = time.perf_counter()
     dw = DeviceWorkload(w)
     pt = pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_seq_len, args.partition_tokens)
