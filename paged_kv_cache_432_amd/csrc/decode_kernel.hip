@@ -31,10 +31,10 @@
 //     scale.
 //   * Block ids are loaded 64 at a time (one per lane) and broadcast with
 //     v_readlane.  K/V are read with buffer loads whose resource is the block:
-//     two blocks are in flight while one is consumed, and a load past the
-//     range gets an empty resource (no memory access, zeros), so that every
-//     load in the loop is unconditional and the compiler's wait counts stay
-//     exact.
+//     two blocks are in flight (the next one's loads are issued as soon as a
+//     block is consumed), and a load past the range gets an empty resource (no
+//     memory access, zeros), so that every load in the loop is unconditional
+//     and the compiler's wait counts stay exact.
 //
 // Two ways of cutting the work into wavefronts:
 //   * partitions (partition_tokens > 0 or -1): one wave per (sequence, KV
@@ -69,6 +69,26 @@ __device__ __forceinline__ void buffer_chunk(ChunkF32& c, rsrc_t r, uint32_t off
     c.a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, NT ? 2 : 0));
     c.b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off + 16, 0, NT ? 2 : 0));
 }
+
+#ifndef PA_DECODE_QUERY_IN_LDS_FROM
+#define PA_DECODE_QUERY_IN_LDS_FROM 8
+#endif
+#ifndef PA_DECODE_PIPELINE_DEPTH
+#define PA_DECODE_PIPELINE_DEPTH 2
+#endif
+// Query rows live in LDS at G = 8, where registers would hold 8 x 16 bf16 of
+// them per lane (16 copies of each, one per token lane) and leave one wave per
+// SIMD.  At G = 4 they stay in registers: LDS reads on every block cost more
+// than the third wave per SIMD they would free (measured on the Llama-3-8B
+// decode shapes).
+template <int G>
+constexpr bool kQueryInLds = G >= PA_DECODE_QUERY_IN_LDS_FROM;
+
+// Blocks each wave keeps in flight.  Three also fit two waves per SIMD (252
+// VGPRs at G = 4) but measured the same as two on the Llama-3-8B and G = 8
+// decode shapes, so two it is (239 VGPRs).
+template <int G>
+constexpr int kPipelineDepth = PA_DECODE_PIPELINE_DEPTH;
 
 // Per-wave state of one (sequence, KV head) range: the G query rows (in
 // registers, in the K layout, or -- QL -- in the wave's LDS slot, read back
@@ -132,7 +152,7 @@ __device__ __forceinline__ void load_query(const DecodeArgs& a, int64_t row, int
 // `bt` (its first entry is the range's first block); `tok_first` is the token
 // position of that block and `tok_end` the sequence length (tokens at or past
 // it are masked out).
-template <typename Chunk, typename Elem, int G, bool QL, bool NT>
+template <typename Chunk, typename Elem, int G, bool QL, bool NT, int NBUF>
 __device__ __forceinline__ void attend(const DecodeArgs& a, int kvh, const int32_t* __restrict__ bt,
                                        int nblk, int tok_first, int tok_end, float* pl, int lane,
                                        WaveState<Chunk, Elem, G, QL>& st) {
@@ -264,14 +284,17 @@ __device__ __forceinline__ void attend(const DecodeArgs& a, int kvh, const int32
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         };
 
-        Chunk ka[4], va[4], kb2[4], vb2[4];
-        issue(ka, va, 0);
-        issue(kb2, vb2, 1);
-        for (int i = 0; i < nb; i += 2) {
-            process(ka, va, i);
-            issue(ka, va, i + 2);
-            if (i + 1 < nb) process(kb2, vb2, i + 1);
-            issue(kb2, vb2, i + 3);
+        // NBUF blocks in flight: block i + NBUF is issued as soon as block i is
+        // consumed.
+        Chunk kbuf[NBUF][4], vbuf[NBUF][4];
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) issue(kbuf[b], vbuf[b], b);
+        for (int i = 0; i < nb; i += NBUF) {
+#pragma unroll
+            for (int b = 0; b < NBUF; ++b) {
+                if (b == 0 || i + b < nb) process(kbuf[b], vbuf[b], i + b);
+                issue(kbuf[b], vbuf[b], i + b + NBUF);
+            }
         }
     }
 }
@@ -363,7 +386,7 @@ decode_partition_kernel(DecodeArgs a) {
     WaveState<Chunk, Elem, G, QL> st;
     st.qs = q_lds[QL ? wave : 0];
     load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
-    attend<Chunk, Elem, G, QL, NT>(a, kvh, a.block_table + b * a.bt_stride + tok_begin / kBlock, nblk,
+    attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, a.block_table + b * a.bt_stride + tok_begin / kBlock, nblk,
                                    tok_begin, L, p_lds[wave], lane, st);
     if (nparts == 1) {
         const int64_t h0 = row * a.num_heads + (int64_t)kvh * G;
@@ -462,7 +485,7 @@ decode_stream_kernel(DecodeArgs a) {
         WaveState<Chunk, Elem, G, QL> st;
         st.qs = q_lds[QL ? wi : 0];
         load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
-        attend<Chunk, Elem, G, QL, NT>(a, kvh, a.block_table + (int64_t)b * a.bt_stride + blk0, n,
+        attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, a.block_table + (int64_t)b * a.bt_stride + blk0, n,
                                        blk0 * kBlock, L, pl, lane, st);
         if (blk0 == 0 && n == nblk_b) {
             finish<Chunk, Elem, G, QL>(st, lane,
@@ -582,13 +605,7 @@ merge_stream_kernel(DecodeArgs a) {
                        lane, o);
 }
 
-// Query rows live in LDS at G = 8, where registers would hold 8 x 16 bf16 of
-// them per lane (16 copies of each, one per token lane) and leave one wave per
-// SIMD.  At G = 4 they stay in registers: LDS reads on every block cost more
-// than the third wave per SIMD they would free (measured on the Llama-3-8B
-// decode shapes).
-template <int G>
-constexpr bool kQueryInLds = G >= 8;
+
 
 template <typename Chunk, typename Elem, int G>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
