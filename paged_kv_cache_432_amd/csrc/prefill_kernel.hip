@@ -347,17 +347,22 @@ prefill_kernel(PrefillArgs a) {
             for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
                 for (int n = 0; n < 2; ++n) sacc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // operands read one step ahead of the products that use them, so
+            // that LDS latency overlaps the matrix work
             const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * g];
+            auto k_operand = [&](int i) {                  // step i: dim step i / 4, key tile i % 4
+                return *reinterpret_cast<const u32x4_t*>(kl + (i & 3) * 16 * kKStride + 32 * (i >> 2));
+            };
+            u32x4_t ka[2];
+            ka[0] = k_operand(0);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+            for (int i = 0; i < 16; ++i) {
+                if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
+                const int ks = i >> 2, mt = i & 3;
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt) {
-                    const u32x4_t ka = *reinterpret_cast<const u32x4_t*>(kl + mt * 16 * kKStride + 32 * ks);
-#pragma unroll
-                    for (int n = 0; n < 2; ++n)
-                        sacc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qop[n][ks]),
-                                                                              sacc[mt][n], 0, 0, 0);
-                }
+                for (int n = 0; n < 2; ++n)
+                    sacc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[i & 1]), as_bf16x8(qop[n][ks]),
+                                                                          sacc[mt][n], 0, 0, 0);
             }
 
             // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr.
@@ -429,23 +434,35 @@ prefill_kernel(PrefillArgs a) {
 
             // O^T += V^T P^T: 8 dim tiles x 2 key steps, hi and lo parts of P
             const uint16_t* vl = &v_lds[buf][lr * kVStride + 4 * g];
+            auto v_operand = [&](int i) {                  // step i: dim tile i / 2, key step i % 2
+                const uint16_t* vrow = vl + (i >> 1) * 16 * kVStride + 32 * (i & 1);
+                const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
+                const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+                return u32x4_t{v0.x, v0.y, v1.x, v1.y};
+            };
+            u32x4_t va[2];
+            va[0] = v_operand(0);
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
+            for (int i = 0; i < 16; ++i) {
+                if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
+                const int dt = i >> 1, ks = i & 1;
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const uint16_t* vrow = vl + dt * 16 * kVStride + 32 * ks;
-                    const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
-                    const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-                    const u32x4_t va = u32x4_t{v0.x, v0.y, v1.x, v1.y};
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(phi[n][ks]),
-                                                                              oacc[dt][n], 0, 0, 0);
-                        oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va), as_bf16x8(plo[n][ks]),
-                                                                              oacc[dt][n], 0, 0, 0);
-                    }
+                for (int n = 0; n < 2; ++n) {
+                    oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[i & 1]), as_bf16x8(phi[n][ks]),
+                                                                          oacc[dt][n], 0, 0, 0);
+                    oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[i & 1]), as_bf16x8(plo[n][ks]),
+                                                                          oacc[dt][n], 0, 0, 0);
                 }
             }
+            // keep the schedule as written: two operand reads ahead, then one
+            // LDS read per four products
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+            for (int i = 0; i < 15; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
         }
         if (kt + 1 < kt_end) commit(buf ^ 1);
         __syncthreads();
