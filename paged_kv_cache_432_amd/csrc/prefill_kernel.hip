@@ -23,10 +23,14 @@
 //     4 keys of ONE query row, which is exactly the lane layout of the B
 //     operand of the next product, so the probabilities feed O^T += V^T P^T
 //     without another pass through LDS.
-//   * P is fed as two bf16 operands, hi = p truncated to bf16 and
-//     lo = bf16(p - hi), so the product keeps ~16 bits of p: a single bf16
-//     rounding of p alone would use most of the output's error budget on top
-//     of the bf16 output rounding.
+//   * P.V runs in fp16 (v_mfma_f32_16x16x32_f16): V^T is staged to LDS as
+//     fp16, exact for bf16 magnitudes below 2^16, and p in [0, 1] is rounded
+//     once to fp16 (11 significant bits, subnormals kept).  A single bf16
+//     rounding of p would use most of the output's error budget on top of the
+//     bf16 output rounding.  A workgroup that stages a V magnitude of 2^16 or
+//     more redoes its piece on an exact bf16 path that feeds P as two
+//     operands, hi = p truncated to bf16 and lo = bf16(p - hi) (~16 bits of
+//     p, twice the P.V products).
 //   * Causal masking selects -inf only on tiles that cross a row's limit; keys
 //     past seq_len are zero-filled in LDS (stale cache slots may hold NaN, and
 //     0 * NaN is NaN), and tiles wholly past a wave's rows are skipped.
@@ -42,6 +46,8 @@
 //     KV head land on one XCD and share its L2.
 #include <math.h>
 
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -50,6 +56,8 @@ namespace pa {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
@@ -63,6 +71,13 @@ constexpr int kVTileElems = kHeadDim * kVStride;
 constexpr int kThreads = kWaves * kWave;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
+__device__ __forceinline__ f16x8_t as_f16x8(u32x4_t w) { return __builtin_bit_cast(f16x8_t, w); }
+
+// Two fp32 -> two fp16 in one word (lo in bits 0-15), round to nearest even:
+// one v_cvt_pk_f16_f32.
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
+}
 
 constexpr int kRec = 132;                    // partial record floats per row: 128 O, max, sum, pad
 
@@ -252,13 +267,9 @@ prefill_kernel(PrefillArgs a) {
         kmax = max(kmax, __shfl_xor(kmax, d, kWave));
     }
 
-    float m[2] = {-INFINITY, -INFINITY};
-    float lp[2] = {0.f, 0.f};                          // this lane's part of each row's sum
+    float m[2];
+    float lp[2];                                       // this lane's part of each row's sum
     f32x4_t oacc[8][2];                                // O^T: dims 16dt + 4g + r, row 16n + lr
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int n = 0; n < 2; ++n) oacc[dt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
     // ---- K/V tile staging.  K: 1024 16-byte chunks (row, 16-byte part), two per
     // thread, stored row-major.  V: thread (dim pair dp, key quads kq, kq + 8)
@@ -313,7 +324,14 @@ prefill_kernel(PrefillArgs a) {
             }
         }
     };
-    auto commit = [&](int buf) {
+    // V^T goes to LDS as bf16 (exact path) or fp16 (fast path).  The fp16
+    // copy is exact for every bf16 magnitude below 2^16 (fp16 subnormals
+    // included, up to a rounding far below the output's); vmax tracks the
+    // largest magnitude staged so that a workgroup that met a larger one
+    // can redo its piece on the exact path.
+    float vmax = 0.f;
+    auto commit = [&](int buf, auto half) {
+        constexpr bool kHalf = decltype(half)::value;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int c = tid + j * kThreads;
@@ -322,152 +340,197 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const uint32_t* w = vw[j];
-            const u32x2_t even = u32x2_t{(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
-            const u32x2_t odd = u32x2_t{(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
+            u32x2_t even, odd;
+            if constexpr (kHalf) {
+                float e[4], o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    e[i] = bf16_lo(w[i]);
+                    o[i] = bf16_hi(w[i]);
+                    vmax = fmaxf(vmax, fmaxf(fabsf(e[i]), fabsf(o[i])));
+                }
+                even = u32x2_t{pack_f16x2(e[0], e[1]), pack_f16x2(e[2], e[3])};
+                odd = u32x2_t{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
+            } else {
+                even = u32x2_t{(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
+                odd = u32x2_t{(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
+            }
             uint16_t* vt = &v_lds[buf][(2 * dp) * kVStride + 4 * (kq + 8 * j)];
             *reinterpret_cast<u32x2_t*>(vt) = even;
             *reinterpret_cast<u32x2_t*>(vt + kVStride) = odd;
         }
     };
 
-    if (kt_begin < kt_end) {
-        stage(kt_begin);
-        commit(0);
-    }
-    __syncthreads();
+    // One pass over the piece's key tiles.  Fast path: P is rounded once to
+    // fp16 (11 significant bits) against V^T in fp16.  Exact path: P is fed as
+    // two bf16 operands against V^T in bf16, hi = p truncated to bf16 and
+    // lo = bf16(p - hi), keeping ~16 bits of p; a single bf16 rounding of p
+    // would use most of the output's error budget on top of the bf16 output
+    // rounding.
+    auto run = [&](auto half) {
+        constexpr bool kHalf = decltype(half)::value;
+#pragma unroll
+        for (int n = 0; n < 2; ++n) {
+            m[n] = -INFINITY;
+            lp[n] = 0.f;
+        }
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+            for (int n = 0; n < 2; ++n) oacc[dt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        bid_base = -kWave;
+        if (kt_begin < kt_end) {
+            stage(kt_begin);
+            commit(0, half);
+        }
+        __syncthreads();
 
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        const int buf = (kt - kt_begin) & 1;
-        if (kt + 1 < kt_end) stage(kt + 1);
-        const int key0 = kt * kKeys;
-        if (key0 < kmax) {
-            // S^T = K Q^T over this tile: 4 key tiles x 2 row tiles x 4 dim steps
-            f32x4_t sacc[4][2];
+        for (int kt = kt_begin; kt < kt_end; ++kt) {
+            const int buf = (kt - kt_begin) & 1;
+            if (kt + 1 < kt_end) stage(kt + 1);
+            const int key0 = kt * kKeys;
+            if (key0 < kmax) {
+                // S^T = K Q^T over this tile: 4 key tiles x 2 row tiles x 4 dim steps
+                f32x4_t sacc[4][2];
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                for (int n = 0; n < 2; ++n) sacc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            // operands read one step ahead of the products that use them, so
-            // that LDS latency overlaps the matrix work
-            const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * g];
-            auto k_operand = [&](int i) {                  // step i: dim step i / 4, key tile i % 4
-                return *reinterpret_cast<const u32x4_t*>(kl + (i & 3) * 16 * kKStride + 32 * (i >> 2));
-            };
-            u32x4_t ka[2];
-            ka[0] = k_operand(0);
+                    for (int n = 0; n < 2; ++n) sacc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                // operands read one step ahead of the products that use them, so
+                // that LDS latency overlaps the matrix work
+                const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * g];
+                auto k_operand = [&](int i) {              // step i: dim step i / 4, key tile i % 4
+                    return *reinterpret_cast<const u32x4_t*>(kl + (i & 3) * 16 * kKStride + 32 * (i >> 2));
+                };
+                u32x4_t ka[2];
+                ka[0] = k_operand(0);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
-                const int ks = i >> 2, mt = i & 3;
+                for (int i = 0; i < 16; ++i) {
+                    if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
+                    const int ks = i >> 2, mt = i & 3;
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
-                    sacc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[i & 1]), as_bf16x8(qop[n][ks]),
-                                                                          sacc[mt][n], 0, 0, 0);
-            }
+                    for (int n = 0; n < 2; ++n)
+                        sacc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[i & 1]),
+                                                                              as_bf16x8(qop[n][ks]), sacc[mt][n], 0, 0, 0);
+                }
 
-            // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr.
-            // The max is taken on raw scores (scale > 0) and the scale folded
-            // into the exponent: p = 2^(s * scale_log2 - m).
-            if (key0 + kKeys > kmin) {                 // a row's limit falls in this tile
+                // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr.
+                // The max is taken on raw scores (scale > 0) and the scale folded
+                // into the exponent: p = 2^(s * scale_log2 - m).
+                if (key0 + kKeys > kmin) {             // a row's limit falls in this tile
 #pragma unroll
-                for (int n = 0; n < 2; ++n)
+                    for (int n = 0; n < 2; ++n)
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (key0 + 16 * mt + 4 * g + r >= kend[n]) sacc[mt][n][r] = -INFINITY;
+                }
+                u32x4_t phi[2][2], plo[2][2];          // B operands of P^T: [row tile][key step]
+                bool rescale = false;
+                float alpha[2];
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][n][0], sacc[mt][n][1])),
+                                   fmaxf(sacc[mt][n][2], sacc[mt][n][3]));
+                    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+                    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+                    const float mn = fmaxf(m[n], mx * a.scale_log2);
+                    const bool none = mn == -INFINITY; // nothing visible yet in this row
+                    const float msafe = none ? 0.f : mn;  // then every score is -inf and p = 0
+                    alpha[n] = none ? 1.f : __builtin_amdgcn_exp2f(m[n] - mn);
+                    rescale |= alpha[n] != 1.f;
+                    m[n] = mn;
+                    float sum = 0.f;
+                    float pv[4][4];
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            if (key0 + 16 * mt + 4 * g + r >= kend[n]) sacc[mt][n][r] = -INFINITY;
-            }
-            u32x4_t phi[2][2], plo[2][2];              // B operands of P^T: [row tile][key step]
-            bool rescale = false;
-            float alpha[2];
+                        for (int r = 0; r < 4; ++r) {
+                            pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][r], a.scale_log2, -msafe));
+                            sum += pv[mt][r];
+                        }
+                    lp[n] = lp[n] * alpha[n] + sum;
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                float mx = -INFINITY;
+                    for (int ks = 0; ks < 2; ++ks) {
+                        uint32_t hw[4], lw[4];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-                    mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][n][0], sacc[mt][n][1])),
-                               fmaxf(sacc[mt][n][2], sacc[mt][n][3]));
-                mx = fmaxf(mx, shfl_xor_f(mx, 16));
-                mx = fmaxf(mx, shfl_xor_f(mx, 32));
-                const float mn = fmaxf(m[n], mx * a.scale_log2);
-                const bool none = mn == -INFINITY;     // nothing visible yet in this row
-                const float msafe = none ? 0.f : mn;   // then every score is -inf and p = 0
-                alpha[n] = none ? 1.f : __builtin_amdgcn_exp2f(m[n] - mn);
-                rescale |= alpha[n] != 1.f;
-                m[n] = mn;
-                float sum = 0.f;
-                float pv[4][4];
+                        for (int h = 0; h < 2; ++h) {      // key tile 2ks + h: slots 4h .. 4h+3
+                            const float* q4 = pv[2 * ks + h];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][r], a.scale_log2, -msafe));
-                        sum += pv[mt][r];
+                            for (int r2 = 0; r2 < 2; ++r2) {
+                                if constexpr (kHalf) {
+                                    hw[2 * h + r2] = pack_f16x2(q4[2 * r2], q4[2 * r2 + 1]);
+                                } else {
+                                    // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
+                                    const uint32_t u0 = __float_as_uint(q4[2 * r2]);
+                                    const uint32_t u1 = __float_as_uint(q4[2 * r2 + 1]);
+                                    hw[2 * h + r2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+                                    lw[2 * h + r2] = pack_bf16x2(q4[2 * r2] - __uint_as_float(u0 & 0xffff0000u),
+                                                                 q4[2 * r2 + 1] - __uint_as_float(u1 & 0xffff0000u));
+                                }
+                            }
+                        }
+                        phi[n][ks] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+                        if constexpr (!kHalf) plo[n][ks] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                     }
-                lp[n] = lp[n] * alpha[n] + sum;
-                // hi = p truncated to bf16 (its top 16 bits), lo = bf16(p - hi):
-                // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
+                }
+                if (__builtin_amdgcn_ballot_w64(rescale)) {
 #pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    uint32_t hw[4], lw[4];
+                    for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {          // key tile 2ks + h: slots 4h .. 4h+3
-                        const float* q4 = pv[2 * ks + h];
+                        for (int n = 0; n < 2; ++n) oacc[dt][n] *= alpha[n];
+                }
+
+                // O^T += V^T P^T: 8 dim tiles x 2 key steps (x hi and lo parts of P
+                // on the exact path)
+                const uint16_t* vl = &v_lds[buf][lr * kVStride + 4 * g];
+                auto v_operand = [&](int i) {              // step i: dim tile i / 2, key step i % 2
+                    const uint16_t* vrow = vl + (i >> 1) * 16 * kVStride + 32 * (i & 1);
+                    const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
+                    const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+                    return u32x4_t{v0.x, v0.y, v1.x, v1.y};
+                };
+                u32x4_t va[2];
+                va[0] = v_operand(0);
 #pragma unroll
-                        for (int r2 = 0; r2 < 2; ++r2) {
-                            const uint32_t u0 = __float_as_uint(q4[2 * r2]), u1 = __float_as_uint(q4[2 * r2 + 1]);
-                            hw[2 * h + r2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-                            lw[2 * h + r2] = pack_bf16x2(q4[2 * r2] - __uint_as_float(u0 & 0xffff0000u),
-                                                         q4[2 * r2 + 1] - __uint_as_float(u1 & 0xffff0000u));
+                for (int i = 0; i < 16; ++i) {
+                    if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
+                    const int dt = i >> 1, ks = i & 1;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        if constexpr (kHalf) {
+                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(va[i & 1]),
+                                                                                 as_f16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
+                        } else {
+                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf16x8(va[i & 1]), as_bf16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
+                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf16x8(va[i & 1]), as_bf16x8(plo[n][ks]), oacc[dt][n], 0, 0, 0);
                         }
                     }
-                    phi[n][ks] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-                    plo[n][ks] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                 }
-            }
-            if (__builtin_amdgcn_ballot_w64(rescale)) {
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) oacc[dt][n] *= alpha[n];
-            }
-
-            // O^T += V^T P^T: 8 dim tiles x 2 key steps, hi and lo parts of P
-            const uint16_t* vl = &v_lds[buf][lr * kVStride + 4 * g];
-            auto v_operand = [&](int i) {                  // step i: dim tile i / 2, key step i % 2
-                const uint16_t* vrow = vl + (i >> 1) * 16 * kVStride + 32 * (i & 1);
-                const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
-                const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-                return u32x4_t{v0.x, v0.y, v1.x, v1.y};
-            };
-            u32x4_t va[2];
-            va[0] = v_operand(0);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
-                const int dt = i >> 1, ks = i & 1;
-#pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[i & 1]), as_bf16x8(phi[n][ks]),
-                                                                          oacc[dt][n], 0, 0, 0);
-                    oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(va[i & 1]), as_bf16x8(plo[n][ks]),
-                                                                          oacc[dt][n], 0, 0, 0);
-                }
-            }
-            // keep the schedule as written: two operand reads ahead, then one
-            // LDS read per four products
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-            for (int i = 0; i < 15; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+                // keep the schedule as written: two operand reads ahead, then one
+                // LDS read per step's products
+                constexpr int kPerStep = kHalf ? 2 : 4;
                 __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int i = 0; i < 15; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+            if (kt + 1 < kt_end) commit(buf ^ 1, half);
+            __syncthreads();
         }
-        if (kt + 1 < kt_end) commit(buf ^ 1);
-        __syncthreads();
-    }
+    };
 
+    run(std::true_type{});
+    if (__syncthreads_or(vmax > 65504.f)) run(std::false_type{});   // a V value overflows fp16
     // ---- finish: lane holds dims 16dt + 4g .. +4 of row 16n + lr.  A whole
     // tile normalises and writes bf16 rows.  A piece of a split tile writes its
     // (unnormalised rows, max, sum) record, and the tile's first piece lists the

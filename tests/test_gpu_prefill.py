@@ -110,3 +110,69 @@ def test_chunked_prefill_mix_full_size(staging):
                       f"chunk {b} last {k} rows (L={int(w.seq_lens[b])})")
     for b in (10, 57, 99):
         assert_parity(o[cu[b]:cu[b + 1]], ref[b], "bf16", f"decode {b} (L={int(w.seq_lens[b])})")
+
+
+def _with_values(w, kv_fn, q_fn=None):
+    """w with K/V (and Q) of every sequence replaced by kv_fn(b, k, v) -> (k, v)
+    of the drawn values; the oracle and the device staging read the same ones."""
+    draw = w.kv
+    memo = {}
+
+    def kv(b, length=None):
+        key = (b, length)
+        if key not in memo:
+            k, v = draw(b)
+            k, v = kv_fn(b, k.copy(), v.copy())
+            n = int(w.seq_lens[b]) if length is None else int(length)
+            memo[key] = (k[:n], v[:n])
+        return memo[key]
+
+    w.kv = kv
+    if q_fn is not None:
+        drawq = w.query
+        w.query = lambda b: q_fn(b, drawq(b).copy())
+    return w
+
+
+def test_tiny_probabilities_keep_their_weight(staging):
+    """One key per sequence scores ~10.4 nats above all others, so every other
+    probability is ~3e-5: below fp16's normal range.  The many small terms
+    still carry ~9% of the weight at 3000 keys; dropping them (a flush of
+    subnormals) moves the output by several hundredths."""
+    w = W.custom("spike", seq_lens=[3000, 700], query_lens=[600, 700], dtype="bf16", seed=16)
+
+    def kv_fn(b, k, v):
+        rng = np.random.default_rng([16, b])
+        k[:, :, 0] = W.bf16_round(0.05 * rng.standard_normal(k.shape[:2]).astype(np.float32))
+        k[0, :, 0] = 14.75                             # the spike key: position 0
+        v[:] = W.bf16_round(-1.0 + 0.1 * rng.standard_normal(v.shape).astype(np.float32))
+        v[0] = 1.0
+        return k, v
+
+    def q_fn(b, q):
+        q[:] = 0.0
+        q[:, :, 0] = 8.0                               # score = scale * 8 * k[., 0]
+        return q
+
+    w = _with_values(w, kv_fn, q_fn)
+    _, out = _run(staging, w)
+    assert_parity(to_numpy(out), oracle.run(w), "bf16", "spike + subnormal tail")
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8)])
+def test_values_beyond_half_range(staging, hq, hkv):
+    """V of one sequence scaled by 2^17 (exact in bf16): most of its values
+    exceed fp16's range, while the other sequences' do not.  The scaled
+    sequence's rows divided by 2^17 match the oracle on the unscaled values."""
+    lens, qlens = [900, 300, 1200], [300, 300, 129]
+    base = W.custom("big", seq_lens=lens, query_lens=qlens, num_heads=hq, num_kv_heads=hkv,
+                    dtype="bf16", seed=17)
+    ref = oracle.run(base)
+    big = _with_values(W.custom("big", seq_lens=lens, query_lens=qlens, num_heads=hq, num_kv_heads=hkv,
+                                dtype="bf16", seed=17),
+                       lambda b, k, v: (k, v * np.float32(2.0 ** 17) if b == 0 else v))
+    _, out = _run(staging, big)
+    o = to_numpy(out)
+    cu = base.cu_query_lens
+    o[cu[0]:cu[1]] /= 2.0 ** 17
+    assert_parity(o, ref, "bf16", f"V x 2^17 in sequence 0, G={hq // hkv}")
