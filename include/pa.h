@@ -174,9 +174,12 @@ pa_status pa_decode(void *out, const void *query, int64_t q_token_stride,
  *   kv_head = h / (num_heads / num_kv_heads).
  * Requests with q_b == 1 run through the decode kernel (as pa_decode with
  * automatic splitting); requests with q_b >= 2 run on the matrix cores
- * (bf16 MFMA, fp32 accumulation, probabilities carried as a bf16 hi/lo pair),
- * long key ranges cut into pieces that the resident workgroups share evenly
- * and merged with log-sum-exp weights; q_b == 0 requests produce nothing.
+ * (Q.K^T in bf16 MFMA, P.V in fp16 MFMA with V exact in fp16, fp32
+ * accumulation; a workgroup that meets |V| >= 2^16 redoes its work with the
+ * probabilities carried as a bf16 hi/lo pair), their (query tile, key tile)
+ * work shared evenly by the resident workgroups and tiles cut by a share
+ * boundary merged with log-sum-exp weights; q_b == 0 requests produce
+ * nothing.
  *
  * out          [num_q_tokens, num_heads, head_dim] bf16, contiguous
  * query        [num_q_tokens, num_heads, head_dim] bf16; rows q_token_stride

@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "launch.h"
@@ -139,11 +140,12 @@ size_t stream_ws_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads
 }
 
 
-// Prefill grid: query tiles (bounded from the host-side sizes) and KV-split
-// pieces, at most tiles + slots / num_kv_heads per KV head.
-struct PrefillShape { int64_t tiles, pieces_per_kvh; int32_t slots; };
+// Prefill grid: slots_per_kvh workgroups per KV head, filling the workgroups
+// the device holds at once (at least one per KV head).  tiles bounds the
+// query tiles from the host-side sizes.
+struct PrefillShape { int64_t tiles; int32_t slots_per_kvh; };
 
-constexpr int32_t kPrefillMinPiece = 8;    // key tiles (512 keys)
+constexpr int32_t kPrefillMinShare = 8;    // key tiles (512 keys)
 
 PrefillShape prefill_shape(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len, int32_t num_heads,
                            int32_t num_kv_heads) {
@@ -169,20 +171,19 @@ PrefillShape prefill_shape(int32_t num_seqs, int64_t num_q_tokens, int32_t max_q
             per_cu = cached_n;
         }
     }
-    const int32_t cus = device_cus();
-    p.slots = per_cu > 0 && cus > 0 ? per_cu * cus : 0;
-    p.pieces_per_kvh = p.tiles + (p.slots + num_kv_heads - 1) / num_kv_heads;
+    const int64_t slots = (int64_t)per_cu * device_cus();
+    p.slots_per_kvh = slots > 0 ? (int32_t)std::max<int64_t>(1, slots / num_kv_heads) : 0;
     return p;
 }
 
-// Prefill scratch: the pieces' partial records, then the split-tile list (a
-// count, then one 16-byte entry per possible split tile).
+// Prefill scratch: two partial records per workgroup, then the list of tiles
+// to merge (a count, then one 16-byte entry per share boundary).
 size_t prefill_records_bytes(const PrefillShape& p, int32_t num_kv_heads) {
-    return (size_t)p.pieces_per_kvh * num_kv_heads * pa::kPrefillRows * pa::kDecodeRecordFloats * sizeof(float);
+    return (size_t)p.slots_per_kvh * num_kv_heads * 2 * pa::kPrefillRows * pa::kDecodeRecordFloats * sizeof(float);
 }
 
 size_t prefill_list_entries(const PrefillShape& p, int32_t num_kv_heads) {
-    return (size_t)(p.pieces_per_kvh * num_kv_heads + 1) / 2;
+    return (size_t)(p.slots_per_kvh - 1) * num_kv_heads + 1;
 }
 
 size_t prefill_part_bytes(const PrefillShape& p, int32_t num_kv_heads) {
@@ -431,16 +432,17 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
         !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
 
-    // workspace: the decode part's, then the prefill pieces' partial records
+    // workspace: the decode part's, then the prefill partial records and merge list
     const size_t dec_bytes =
         align256(pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len, 0));
     PrefillShape ps{};
     size_t need = dec_bytes;
     if (max_query_len >= 2) {
         ps = prefill_shape(num_seqs, num_q_tokens, max_query_len, num_heads, num_kv_heads);
-        if (ps.slots <= 0) return fail(PA_ERR_HIP, "cannot size the prefill grid for the current device");
-        if (ps.pieces_per_kvh * num_kv_heads > 0x7fffffff || ps.tiles * num_kv_heads > 0x7fffffff)
-            return fail(PA_ERR_INVALID_ARG, "grid too large");
+        if (ps.slots_per_kvh <= 0) return fail(PA_ERR_HIP, "cannot size the prefill grid for the current device");
+        // units per KV head stay below 2^30: at most tiles x (key tiles + 1)
+        if (ps.tiles * ((int64_t)max_seq_len / 64 + 2) >= (int64_t)1 << 30)
+            return fail(PA_ERR_INVALID_ARG, "too many query tiles x key tiles");
         need += prefill_part_bytes(ps, num_kv_heads);
     }
     if (!workspace || workspace_bytes < need)
@@ -454,8 +456,9 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
     if (st != PA_OK) return st;
     if (max_query_len < 2) return ok();
 
-    // requests of two or more rows: the MFMA prefill kernel, one workgroup per
-    // (KV-split piece of a query tile, KV head), then the merge of split tiles
+    // requests of two or more rows: the MFMA prefill kernel, each resident
+    // workgroup taking an equal share of a KV head's (query tile, key tile)
+    // units, then the merge of the tiles cut by a share boundary
     const int32_t group = num_heads / num_kv_heads;
     pa::PrefillArgs p{};
     p.out = out;
@@ -473,10 +476,8 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
     p.num_kv_heads = num_kv_heads;
     p.scale_log2 = (float)((double)scale * 1.4426950408889634);
     p.causal = causal;
-    p.tiles_bound = (int32_t)ps.tiles;
-    p.num_slots = ps.slots;
-    p.min_piece = kPrefillMinPiece;
-    p.pieces_per_kvh = (int32_t)ps.pieces_per_kvh;
+    p.slots_per_kvh = ps.slots_per_kvh;
+    p.min_share = kPrefillMinShare;
     p.part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + dec_bytes);
     char* list = reinterpret_cast<char*>(workspace) + dec_bytes + prefill_records_bytes(ps, num_kv_heads);
     p.split_count = reinterpret_cast<int32_t*>(list);

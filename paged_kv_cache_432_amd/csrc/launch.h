@@ -73,18 +73,17 @@ struct PrefillArgs {
     int32_t num_kv_heads;
     float scale_log2;
     int32_t causal;
-    int32_t tiles_bound;           // >= number of query tiles
-    // KV split: a query tile's key range is cut into pieces of at most P key
-    // tiles, P = max(min_piece, ceil(total key tiles / num_slots)), so that the
-    // resident workgroups share the work evenly; pieces of a split tile leave
-    // partial records merged by a second kernel.
-    int32_t num_slots;             // prefill workgroups resident on the device at once
-    int32_t min_piece;             // fewest key tiles per piece
-    int32_t pieces_per_kvh;        // grid = pieces_per_kvh * num_kv_heads >= pieces
-    float* part;                   // [pieces_per_kvh * num_kv_heads][256 rows][132] partial records
-    int32_t* split_count;          // number of split (tile, KV head) pairs listed (written by workgroup 0)
-    int4* split_list;              // [pieces_per_kvh * num_kv_heads / 2 + 1]: first piece, pieces, first row,
-                                   // (tokens << 8) | KV head
+    // Work split: the (query tile, 64-key tile) units of a KV head, U of them
+    // in (sequence, tile, key tile) order, are shared by slots_per_kvh
+    // workgroups, max(min_share, ceil(U / slots_per_kvh)) consecutive units
+    // each; grid = slots_per_kvh * num_kv_heads, KV head fastest.
+    int32_t slots_per_kvh;
+    int32_t min_share;             // fewest units per workgroup
+    float* part;                   // [grid][2][256 rows][132] partial records (a workgroup's first and
+                                   // last segment)
+    int32_t* split_count;          // number of listed (tile, KV head) pairs (written by workgroup 0)
+    int4* split_list;              // [(slots_per_kvh - 1) * num_kv_heads]: first slot, slots | (record of
+                                   // the first slot) << 24, first row, (tokens << 8) | KV head
 };
 
 // dtype: 0 = fp32, 1 = bf16.  group = num_heads / num_kv_heads in {1,2,4,8}.

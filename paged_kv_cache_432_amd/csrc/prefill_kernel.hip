@@ -28,22 +28,23 @@
 //     once to fp16 (11 significant bits, subnormals kept).  A single bf16
 //     rounding of p would use most of the output's error budget on top of the
 //     bf16 output rounding.  A workgroup that stages a V magnitude of 2^16 or
-//     more redoes its piece on an exact bf16 path that feeds P as two
+//     more redoes its segment on an exact bf16 path that feeds P as two
 //     operands, hi = p truncated to bf16 and lo = bf16(p - hi) (~16 bits of
 //     p, twice the P.V products).
 //   * Causal masking selects -inf only on tiles that cross a row's limit; keys
 //     past seq_len are zero-filled in LDS (stale cache slots may hold NaN, and
 //     0 * NaN is NaN), and tiles wholly past a wave's rows are skipped.
-//   * Work is balanced by cutting long key ranges: every workgroup computes
-//     the total number of 64-key tiles U the batch needs and a piece size
-//     P = max(min_piece, ceil(U / resident workgroups)); a query tile whose
-//     range exceeds P is cut into near-equal pieces, each its own workgroup,
-//     which leave (max, sum, unnormalised output) records per row, merged by
-//     a second kernel (log-sum-exp weights, the same merge as split decode)
-//     over a compact list of the split tiles (slot: split tiles before it).
-//   * Workgroups are numbered last piece first (later tiles of a chunk see
-//     more keys), with the KV head as the fastest index, so the pieces of one
-//     KV head land on one XCD and share its L2.
+//   * Work is balanced over the resident workgroups: the units of one KV
+//     head are its (query tile, 64-key tile) pairs in (sequence, tile, key
+//     tile) order, U of them, and each of the slots_per_kvh workgroups of a KV
+//     head takes a contiguous share of max(min_share, ceil(U / slots_per_kvh))
+//     units, one segment per query tile it touches.  A tile inside one share
+//     writes its rows; the segments of a tile that crosses a share boundary
+//     leave (max, sum, unnormalised output) records per row, merged by a
+//     second kernel (log-sum-exp weights, the same merge as split decode)
+//     over a compact list of those tiles (slot: such tiles before it).
+//   * The KV head is the fastest index of the workgroup number, so the shares
+//     of one KV head land on one XCD and share its L2.
 #include <math.h>
 
 #include <type_traits>
@@ -80,6 +81,9 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 }
 
 constexpr int kRec = 132;                    // partial record floats per row: 128 O, max, sum, pad
+constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
+
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Exclusive prefix over the workgroup's threads of `x` (every thread calls).
 __device__ __forceinline__ int block_exclusive_scan(int x, int32_t* s_wsum) {
@@ -98,17 +102,18 @@ __device__ __forceinline__ int block_exclusive_scan(int x, int32_t* s_wsum) {
     return before;
 }
 
-__device__ __forceinline__ int block_sum(int x, int32_t* s_wsum) {
-    const int before = block_exclusive_scan(x, s_wsum);
-    __syncthreads();
-    if (threadIdx.x == blockDim.x - 1) s_wsum[0] = before + x;
-    __syncthreads();
-    return s_wsum[0];
-}
-
 struct SeqShape {
     int q0, qlen, L;
 };
+
+// The same shape held in scalar registers (for a sequence index that is the
+// same for the whole workgroup).
+__device__ __forceinline__ SeqShape uniform(SeqShape sh) {
+    sh.q0 = __builtin_amdgcn_readfirstlane(sh.q0);
+    sh.qlen = __builtin_amdgcn_readfirstlane(sh.qlen);
+    sh.L = __builtin_amdgcn_readfirstlane(sh.L);
+    return sh;
+}
 
 __device__ __forceinline__ SeqShape seq_shape(const PrefillArgs& a, int b) {
     SeqShape sh;
@@ -129,13 +134,23 @@ __device__ __forceinline__ int tile_kend(const PrefillArgs& a, const SeqShape& s
     return max(min(sh.L - sh.qlen + last, sh.L), 0);
 }
 
-__device__ __forceinline__ int tile_pieces(int nkt, int P) { return nkt > 0 ? (nkt + P - 1) / P : 1; }
+// Work units of query tile t: its key tiles, and at least one, since a tile
+// that sees no key still writes its (zero) rows.
+__device__ __forceinline__ int tile_units(const PrefillArgs& a, const SeqShape& sh, int t, int tq) {
+    return max(1, (tile_kend(a, sh, t, tq) + kKeys - 1) / kKeys);
+}
 
-// The batch's piece map, built by every workgroup: s_pp[b] = first piece of
-// sequence b (s_pp[B] = total), s_sp[b] = split tiles (more than one piece)
-// before sequence b (s_sp[B] = total).  Returns the piece size P in key tiles.
-__device__ __forceinline__ int build_piece_map(const PrefillArgs& a, int tq, int32_t* s_pp, int32_t* s_sp,
-                                               int32_t* s_wsum) {
+// Does a tile whose units are [u0, u0 + n) cross a share boundary?
+__device__ __forceinline__ bool crosses(int u0, int n, int share) { return u0 / share != (u0 + n - 1) / share; }
+
+// The batch's unit map, built by every workgroup.  Units are the (query tile,
+// key tile) pairs of one KV head in (sequence, tile, key tile) order;
+// s_pu[b] = first unit of sequence b (s_pu[B] = U), s_sp[b] = tiles before
+// sequence b that cross a share boundary (s_sp[B] = total).  Returns the
+// share: the units each workgroup of a KV head takes,
+// max(min_share, ceil(U / slots_per_kvh)).
+__device__ __forceinline__ int build_unit_map(const PrefillArgs& a, int tq, int32_t* s_pu, int32_t* s_sp,
+                                              int32_t* s_wsum) {
     const int B = a.num_seqs;
     const int nthr = blockDim.x;
     const int per = (B + nthr - 1) / nthr;
@@ -143,43 +158,40 @@ __device__ __forceinline__ int build_piece_map(const PrefillArgs& a, int tq, int
     int units = 0;
     for (int b = lo; b < hi; ++b) {
         const SeqShape sh = seq_shape(a, b);
-        const int nt = tiles_of(sh, tq);
-        for (int t = 0; t < nt; ++t) units += (tile_kend(a, sh, t, tq) + kKeys - 1) / kKeys;
+        int ub = 0;
+        for (int t = 0, nt = tiles_of(sh, tq); t < nt; ++t) ub += tile_units(a, sh, t, tq);
+        s_pu[b + 1] = ub;
+        units += ub;
     }
-    const int total = block_sum(units, s_wsum);       // key tiles per KV head
-    const int64_t all = (int64_t)total * a.num_kv_heads;
-    const int P = max(a.min_piece, (int)((all + a.num_slots - 1) / a.num_slots));
-    int pieces = 0, splits = 0;
+    int run = block_exclusive_scan(units, s_wsum);
+    for (int b = lo; b < hi; ++b) {
+        run += s_pu[b + 1];
+        s_pu[b + 1] = run;
+    }
+    if (threadIdx.x == 0) s_pu[0] = 0;
+    __syncthreads();
+    const int U = s_pu[B];
+    const int share = max(a.min_share, (U + a.slots_per_kvh - 1) / a.slots_per_kvh);
+    int splits = 0;
     for (int b = lo; b < hi; ++b) {
         const SeqShape sh = seq_shape(a, b);
-        const int nt = tiles_of(sh, tq);
-        int pb = 0, sb = 0;
-        for (int t = 0; t < nt; ++t) {
-            const int np = tile_pieces((tile_kend(a, sh, t, tq) + kKeys - 1) / kKeys, P);
-            pb += np;
-            sb += np > 1;
+        int u = s_pu[b], sb = 0;
+        for (int t = 0, nt = tiles_of(sh, tq); t < nt; ++t) {
+            const int n = tile_units(a, sh, t, tq);
+            sb += crosses(u, n, share);
+            u += n;
         }
-        s_pp[b + 1] = pb;
         s_sp[b + 1] = sb;
-        pieces += pb;
         splits += sb;
-    }
-    int run = block_exclusive_scan(pieces, s_wsum);
-    for (int b = lo; b < hi; ++b) {
-        run += s_pp[b + 1];
-        s_pp[b + 1] = run;
     }
     run = block_exclusive_scan(splits, s_wsum);
     for (int b = lo; b < hi; ++b) {
         run += s_sp[b + 1];
         s_sp[b + 1] = run;
     }
-    if (threadIdx.x == 0) {
-        s_pp[0] = 0;
-        s_sp[0] = 0;
-    }
+    if (threadIdx.x == 0) s_sp[0] = 0;
     __syncthreads();
-    return P;
+    return share;
 }
 
 // The largest b with pref[b] <= x (pref non-decreasing, pref[0] = 0 <= x).
@@ -197,40 +209,34 @@ __global__ void __launch_bounds__(kThreads)
 prefill_kernel(PrefillArgs a) {
     constexpr int TQ = kPrefillRows / G;               // tokens per tile
     extern __shared__ __attribute__((aligned(16))) int32_t s_dyn[];
-    int32_t* s_pref = s_dyn;                           // [num_seqs + 1] piece prefix
-    int32_t* s_split = s_dyn + a.num_seqs + 1;         // [num_seqs + 1] split-tile prefix
+    int32_t* s_pu = s_dyn;                             // [num_seqs + 1] unit prefix
+    int32_t* s_sp = s_dyn + a.num_seqs + 1;            // [num_seqs + 1] split-tile prefix
     __shared__ int32_t s_wsum[kWaves];
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kVTileElems];
 
-    const int P = build_piece_map(a, TQ, s_pref, s_split, s_wsum);
+    // values read from LDS are the same in every lane: kept in scalar registers
+    const int share = __builtin_amdgcn_readfirstlane(build_unit_map(a, TQ, s_pu, s_sp, s_wsum));
     const int B = a.num_seqs;
     const int Hkv = a.num_kv_heads;
-    const int npieces = s_pref[B];
-    if (blockIdx.x == 0 && threadIdx.x == 0) *a.split_count = s_split[B] * Hkv;
+    const int U = __builtin_amdgcn_readfirstlane(s_pu[B]);
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.split_count = s_sp[B] * Hkv;
     const int kvh = (int)(blockIdx.x % Hkv);
-    const int rev = (int)(blockIdx.x / Hkv);
-    if (rev >= npieces) return;                        // whole workgroup: no barrier is left behind
-    const int piece = npieces - 1 - rev;
-    const int b = find_seq(s_pref, B, piece);
-    const SeqShape sh = seq_shape(a, b);
-    // the tile and the piece within it
-    int tile = 0, j = piece - s_pref[b], nkt = 0, np = 1, split_before = s_split[b];
-    for (const int nt = tiles_of(sh, TQ); tile < nt; ++tile) {
-        nkt = (tile_kend(a, sh, tile, TQ) + kKeys - 1) / kKeys;
-        np = tile_pieces(nkt, P);
-        if (j < np) break;
-        j -= np;
-        split_before += np > 1;
+    const int slot = (int)(blockIdx.x / Hkv);
+    if ((int64_t)slot * share >= U) return;            // whole workgroup: no barrier is left behind
+    const int ub = slot * share, ue = min(U, ub + share);
+
+    // the tile holding unit ub
+    int b = __builtin_amdgcn_readfirstlane(find_seq(s_pu, B, ub));
+    SeqShape sh = uniform(seq_shape(a, b));
+    int nt = tiles_of(sh, TQ), tile = 0;
+    int tu0 = __builtin_amdgcn_readfirstlane(s_pu[b]);  // first unit of the tile
+    int split_before = __builtin_amdgcn_readfirstlane(s_sp[b]);
+    for (int n = tile_units(a, sh, 0, TQ); ub >= tu0 + n; n = tile_units(a, sh, tile, TQ)) {
+        split_before += crosses(tu0, n, share);
+        tu0 += n;
+        ++tile;
     }
-    const int psz = (nkt + np - 1) / np;
-    const int kt_begin = j * psz;
-    const int kt_end = min(nkt, kt_begin + psz);
-    const int q0 = sh.q0, qlen = sh.qlen, L = sh.L;
-    const int tok_begin = tile * TQ;
-    const int ntok = min(TQ, qlen - tok_begin);
-    const int prior = L - qlen;                        // position of query row 0
-    const int kend_wg = tile_kend(a, sh, tile, TQ);
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -239,331 +245,363 @@ prefill_kernel(PrefillArgs a) {
     const int g = lane >> 4;                           // lane group
     const int Hq = a.num_heads;
 
-    // ---- this lane's two query rows (one per 16-row tile) and their key limits
-    int tq[2], kend[2];
-    bool active[2];
-    u32x4_t qop[2][4];                                 // B operand of S^T: dims 32ks + 8g .. +8
-#pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        const int r = wave * kRowsPerWave + 16 * n + lr;
-        tq[n] = r / G;
-        active[n] = tq[n] < ntok;
-        const int pos = prior + tok_begin + tq[n];
-        kend[n] = !active[n] ? 0 : (a.causal ? max(min(L, pos + 1), 0) : L);
-        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
-                             (int64_t)(q0 + tok_begin + (active[n] ? tq[n] : 0)) * a.q_stride +
-                             (int64_t)(kvh * G + r % G) * kHeadDim + 8 * g;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            qop[n][ks] = active[n] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
-        }
-    }
-    // wave-wide key limits: tiles at or past kmax are skipped, tiles ending past
-    // kmin need the mask
-    int kmin = min(kend[0], kend[1]), kmax = max(kend[0], kend[1]);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        kmin = min(kmin, __shfl_xor(kmin, d, kWave));
-        kmax = max(kmax, __shfl_xor(kmax, d, kWave));
-    }
+    // One segment per query tile the share touches: the key tiles of the
+    // share that belong to that tile.
+    for (int u = ub, first = 1;; first = 0) {
+        const int units = tile_units(a, sh, tile, TQ);
+        const int kend_wg = tile_kend(a, sh, tile, TQ);
+        const int nkt = (kend_wg + kKeys - 1) / kKeys;
+        const int kt_begin = u - tu0;
+        const int seg_end = min(ue, tu0 + units) - tu0;
+        const int kt_end = min(seg_end, nkt);
+        const bool split = crosses(tu0, units, share);
+        const int q0 = sh.q0, qlen = sh.qlen, L = sh.L;
+        const int tok_begin = tile * TQ;
+        const int ntok = min(TQ, qlen - tok_begin);
+        const int prior = L - qlen;                        // position of query row 0
 
-    float m[2];
-    float lp[2];                                       // this lane's part of each row's sum
-    f32x4_t oacc[8][2];                                // O^T: dims 16dt + 4g + r, row 16n + lr
-
-    // ---- K/V tile staging.  K: 1024 16-byte chunks (row, 16-byte part), two per
-    // thread, stored row-major.  V: thread (dim pair dp, key quads kq, kq + 8)
-    // loads the 4-byte (dims 2dp, 2dp+1) word of each key of its quads -- a
-    // wave reads whole 256-byte rows -- and packs them into 4-key runs of the
-    // two V^T rows, stored with 8-byte writes.
-    const char* kc = reinterpret_cast<const char*>(a.key_cache);
-    const char* vc = reinterpret_cast<const char*>(a.value_cache);
-    const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
-    const int64_t tok_bytes = (int64_t)Hkv * kHeadDim * 2;
-    const int64_t head_off = (int64_t)kvh * kHeadDim * 2;
-    const int dp = tid & 63, kq = tid >> 6;
-    u32x4_t kreg[2];
-    uint32_t vw[2][4];
-    // Block ids of the key range, 64 at a time (one per lane): a wave's loads
-    // of a tile need 2 ids for K and 2 for V, each the same for all its lanes,
-    // broadcast with v_readlane, so that the tile's 10 loads issue back to
-    // back instead of each waiting on its own table read.
-    const int nblk_wg = (kend_wg + kBlock - 1) / kBlock;
-    int bid_base = -kWave;                             // first block held in bid
-    int bid = 0;
-    auto block_of = [&](int blk) -> int64_t {          // blk in [bid_base, bid_base + 64)
-        const int64_t id = __builtin_amdgcn_readlane(bid, blk - bid_base);
-        return min(max(id, (int64_t)0), a.num_blocks - 1);
-    };
-    auto stage = [&](int kt) {
-        if (4 * kt + 3 >= bid_base + kWave) {          // wave-uniform: the tile's ids are not all held
-            bid_base = 4 * kt;
-            bid = bid_base + lane < nblk_wg ? bt[bid_base + lane] : 0;
-        }
-        const int kwave_blk = 4 * kt + (tid >> 8);     // K chunk j covers block kwave_blk + 2j
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = tid + j * kThreads;
-            const int key = kt * kKeys + (c >> 4);
-            const int64_t phys = block_of(kwave_blk + 2 * j);
-            kreg[j] = key < kend_wg
-                          ? *reinterpret_cast<const u32x4_t*>(kc + (phys * kBlock + key % kBlock) * tok_bytes +
-                                                              head_off + (c & 15) * 16)
-                          : u32x4_t{0u, 0u, 0u, 0u};   // past the keys: zeros, never stale data
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int q = kq + 8 * j;                  // key quad of the tile; block 4kt + q/4
-            const int64_t phys = block_of(4 * kt + q / 4);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int key = kt * kKeys + 4 * q + i;
-                vw[j][i] = key < kend_wg ? *reinterpret_cast<const uint32_t*>(
-                                               vc + (phys * kBlock + key % kBlock) * tok_bytes + head_off + dp * 4)
-                                         : 0u;
-            }
-        }
-    };
-    // V^T goes to LDS as bf16 (exact path) or fp16 (fast path).  The fp16
-    // copy is exact for every bf16 magnitude below 2^16 (fp16 subnormals
-    // included, up to a rounding far below the output's); vmax tracks the
-    // largest magnitude staged so that a workgroup that met a larger one
-    // can redo its piece on the exact path.
-    float vmax = 0.f;
-    auto commit = [&](int buf, auto half) {
-        constexpr bool kHalf = decltype(half)::value;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int c = tid + j * kThreads;
-            *reinterpret_cast<u32x4_t*>(&k_lds[buf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[j];
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t* w = vw[j];
-            u32x2_t even, odd;
-            if constexpr (kHalf) {
-                float e[4], o[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    e[i] = bf16_lo(w[i]);
-                    o[i] = bf16_hi(w[i]);
-                    vmax = fmaxf(vmax, fmaxf(fabsf(e[i]), fabsf(o[i])));
-                }
-                even = u32x2_t{pack_f16x2(e[0], e[1]), pack_f16x2(e[2], e[3])};
-                odd = u32x2_t{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
-            } else {
-                even = u32x2_t{(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
-                odd = u32x2_t{(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
-            }
-            uint16_t* vt = &v_lds[buf][(2 * dp) * kVStride + 4 * (kq + 8 * j)];
-            *reinterpret_cast<u32x2_t*>(vt) = even;
-            *reinterpret_cast<u32x2_t*>(vt + kVStride) = odd;
-        }
-    };
-
-    // One pass over the piece's key tiles.  Fast path: P is rounded once to
-    // fp16 (11 significant bits) against V^T in fp16.  Exact path: P is fed as
-    // two bf16 operands against V^T in bf16, hi = p truncated to bf16 and
-    // lo = bf16(p - hi), keeping ~16 bits of p; a single bf16 rounding of p
-    // would use most of the output's error budget on top of the bf16 output
-    // rounding.
-    auto run = [&](auto half) {
-        constexpr bool kHalf = decltype(half)::value;
+        // ---- this lane's two query rows (one per 16-row tile) and their key limits
+        int tq[2], kend[2];
+        bool active[2];
+        u32x4_t qop[2][4];                                 // B operand of S^T: dims 32ks + 8g .. +8
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            m[n] = -INFINITY;
-            lp[n] = 0.f;
-        }
+            const int r = wave * kRowsPerWave + 16 * n + lr;
+            tq[n] = r / G;
+            active[n] = tq[n] < ntok;
+            const int pos = prior + tok_begin + tq[n];
+            kend[n] = !active[n] ? 0 : (a.causal ? max(min(L, pos + 1), 0) : L);
+            const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
+                                 (int64_t)(q0 + tok_begin + (active[n] ? tq[n] : 0)) * a.q_stride +
+                                 (int64_t)(kvh * G + r % G) * kHeadDim + 8 * g;
 #pragma unroll
-        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-            for (int n = 0; n < 2; ++n) oacc[dt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        bid_base = -kWave;
-        if (kt_begin < kt_end) {
-            stage(kt_begin);
-            commit(0, half);
+            for (int ks = 0; ks < 4; ++ks) {
+                qop[n][ks] = active[n] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+            }
         }
-        __syncthreads();
+        // wave-wide key limits: tiles at or past kmax are skipped, tiles ending past
+        // kmin need the mask
+        int kmin = min(kend[0], kend[1]), kmax = max(kend[0], kend[1]);
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            kmin = min(kmin, __shfl_xor(kmin, d, kWave));
+            kmax = max(kmax, __shfl_xor(kmax, d, kWave));
+        }
 
-        for (int kt = kt_begin; kt < kt_end; ++kt) {
-            const int buf = (kt - kt_begin) & 1;
-            if (kt + 1 < kt_end) stage(kt + 1);
-            const int key0 = kt * kKeys;
-            if (key0 < kmax) {
-                // S^T = K Q^T over this tile: 4 key tiles x 2 row tiles x 4 dim steps
-                f32x4_t sacc[4][2];
+        float m[2];
+        float lp[2];                                       // this lane's part of each row's sum
+        f32x4_t oacc[8][2];                                // O^T: dims 16dt + 4g + r, row 16n + lr
+
+        // ---- K/V tile staging.  K: 1024 16-byte chunks (row, 16-byte part), two per
+        // thread, stored row-major.  V: thread (dim pair dp, key quads kq, kq + 8)
+        // loads the 4-byte (dims 2dp, 2dp+1) word of each key of its quads -- a
+        // wave reads whole 256-byte rows -- and packs them into 4-key runs of the
+        // two V^T rows, stored with 8-byte writes.  A wave's loads of tile kt all
+        // fall in cache blocks 4kt + w4 and 4kt + w4 + 2 (w4 = wave / 4), at
+        // offsets within the block that do not change from tile to tile; each
+        // block is read through a buffer resource whose size is its valid keys'
+        // rows, so that keys past the range read as zeros (never stale data)
+        // without a branch or a per-lane test.
+        const char* kc = reinterpret_cast<const char*>(a.key_cache);
+        const char* vc = reinterpret_cast<const char*>(a.value_cache);
+        const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
+        const uint32_t tok_bytes = (uint32_t)Hkv * kHeadDim * 2;
+        const int64_t blk_bytes = (int64_t)kBlock * tok_bytes;
+        const uint32_t head_off = (uint32_t)kvh * kHeadDim * 2;
+        const int dp = tid & 63, kq = tid >> 6;
+        const int w4 = __builtin_amdgcn_readfirstlane(tid >> 8);   // the same for a whole wave
+        const uint32_t koff = ((tid >> 4) & 15) * tok_bytes + head_off + (tid & 15) * 16;
+        const uint32_t voff = 4 * (kq & 3) * tok_bytes + head_off + dp * 4;
+        u32x4_t kreg[2];
+        uint32_t vw[2][4];
+        // Block ids of the key range, 64 at a time (one per lane), broadcast with
+        // v_readlane, so that the tile's 10 loads issue back to back instead of
+        // each waiting on its own table read.
+        const int nblk_wg = (kend_wg + kBlock - 1) / kBlock;
+        int bid_base = -kWave;                             // first block held in bid
+        int bid = 0;
+        auto block_of = [&](int blk) -> int64_t {          // blk in [bid_base, bid_base + 64)
+            const int64_t id = __builtin_amdgcn_readlane(bid, blk - bid_base);
+            return min(max(id, (int64_t)0), a.num_blocks - 1);
+        };
+        auto stage = [&](int kt) {
+            if (4 * kt + 3 >= bid_base + kWave) {          // wave-uniform: the tile's ids are not all held
+                bid_base = 4 * kt;
+                bid = bid_base + lane < nblk_wg ? bt[bid_base + lane] : 0;
+            }
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+            for (int j = 0; j < 2; ++j) {
+                const int blk = 4 * kt + w4 + 2 * j;
+                const int64_t off = block_of(blk) * blk_bytes;
+                const int nrec = __builtin_amdgcn_readfirstlane(min(max(kend_wg - blk * kBlock, 0), kBlock) * (int)tok_bytes);
+                const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
+                const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
+                kreg[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff, 0, 0));
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) sacc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                // operands read one step ahead of the products that use them, so
-                // that LDS latency overlaps the matrix work
-                const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * g];
-                auto k_operand = [&](int i) {              // step i: dim step i / 4, key tile i % 4
-                    return *reinterpret_cast<const u32x4_t*>(kl + (i & 3) * 16 * kKStride + 32 * (i >> 2));
-                };
-                u32x4_t ka[2];
-                ka[0] = k_operand(0);
+                for (int i = 0; i < 4; ++i)
+                    vw[j][i] = __builtin_amdgcn_raw_buffer_load_b32(rv, (int)(voff + i * tok_bytes), 0, 0);
+            }
+        };
+        // V^T goes to LDS as bf16 (exact path) or fp16 (fast path).  The fp16
+        // copy is exact for every bf16 magnitude below 2^16 (fp16 subnormals
+        // included, up to a rounding far below the output's); vmax tracks the
+        // largest magnitude staged so that a workgroup that met a larger one
+        // can redo its segment on the exact path.
+        float vmax = 0.f;
+        auto commit = [&](int buf, auto half) {
+            constexpr bool kHalf = decltype(half)::value;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
-                    const int ks = i >> 2, mt = i & 3;
+            for (int j = 0; j < 2; ++j) {
+                const int c = tid + j * kThreads;
+                *reinterpret_cast<u32x4_t*>(&k_lds[buf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[j];
+            }
 #pragma unroll
-                    for (int n = 0; n < 2; ++n)
-                        sacc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[i & 1]),
-                                                                              as_bf16x8(qop[n][ks]), sacc[mt][n], 0, 0, 0);
+            for (int j = 0; j < 2; ++j) {
+                const uint32_t* w = vw[j];
+                u32x2_t even, odd;
+                if constexpr (kHalf) {
+                    float e[4], o[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        e[i] = bf16_lo(w[i]);
+                        o[i] = bf16_hi(w[i]);
+                        vmax = fmaxf(vmax, fmaxf(fabsf(e[i]), fabsf(o[i])));
+                    }
+                    even = u32x2_t{pack_f16x2(e[0], e[1]), pack_f16x2(e[2], e[3])};
+                    odd = u32x2_t{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
+                } else {
+                    even = u32x2_t{(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
+                    odd = u32x2_t{(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
                 }
+                uint16_t* vt = &v_lds[buf][(2 * dp) * kVStride + 4 * (kq + 8 * j)];
+                *reinterpret_cast<u32x2_t*>(vt) = even;
+                *reinterpret_cast<u32x2_t*>(vt + kVStride) = odd;
+            }
+        };
 
-                // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr.
-                // The max is taken on raw scores (scale > 0) and the scale folded
-                // into the exponent: p = 2^(s * scale_log2 - m).
-                if (key0 + kKeys > kmin) {             // a row's limit falls in this tile
+        // One pass over the segment's key tiles.  Fast path: P is rounded once to
+        // fp16 (11 significant bits) against V^T in fp16.  Exact path: P is fed as
+        // two bf16 operands against V^T in bf16, hi = p truncated to bf16 and
+        // lo = bf16(p - hi), keeping ~16 bits of p; a single bf16 rounding of p
+        // would use most of the output's error budget on top of the bf16 output
+        // rounding.
+        auto run = [&](auto half) {
+            constexpr bool kHalf = decltype(half)::value;
 #pragma unroll
-                    for (int n = 0; n < 2; ++n)
+            for (int n = 0; n < 2; ++n) {
+                m[n] = -INFINITY;
+                lp[n] = 0.f;
+            }
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                for (int n = 0; n < 2; ++n) oacc[dt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            bid_base = -kWave;
+            if (kt_begin < kt_end) {
+                stage(kt_begin);
+                commit(0, half);
+            }
+            __syncthreads();
+
+            for (int kt = kt_begin; kt < kt_end; ++kt) {
+                const int buf = (kt - kt_begin) & 1;
+                if (kt + 1 < kt_end) stage(kt + 1);
+                const int key0 = kt * kKeys;
+                if (key0 < kmax) {
+                    // S^T = K Q^T over this tile: 4 key tiles x 2 row tiles x 4 dim steps
+                    f32x4_t sacc[4][2];
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                        for (int n = 0; n < 2; ++n) sacc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    // operands read one step ahead of the products that use them, so
+                    // that LDS latency overlaps the matrix work
+                    const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * g];
+                    auto k_operand = [&](int i) {              // step i: dim step i / 4, key tile i % 4
+                        return *reinterpret_cast<const u32x4_t*>(kl + (i & 3) * 16 * kKStride + 32 * (i >> 2));
+                    };
+                    u32x4_t ka[2];
+                    ka[0] = k_operand(0);
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
+                        const int ks = i >> 2, mt = i & 3;
+#pragma unroll
+                        for (int n = 0; n < 2; ++n)
+                            sacc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[i & 1]),
+                                                                                  as_bf16x8(qop[n][ks]), sacc[mt][n], 0, 0, 0);
+                    }
+
+                    // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr.
+                    // The max is taken on raw scores (scale > 0) and the scale folded
+                    // into the exponent: p = 2^(s * scale_log2 - m).
+                    if (key0 + kKeys > kmin) {             // a row's limit falls in this tile
+#pragma unroll
+                        for (int n = 0; n < 2; ++n)
+#pragma unroll
+                            for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                                for (int r = 0; r < 4; ++r)
+                                    if (key0 + 16 * mt + 4 * g + r >= kend[n]) sacc[mt][n][r] = -INFINITY;
+                    }
+                    u32x4_t phi[2][2], plo[2][2];          // B operands of P^T: [row tile][key step]
+                    bool rescale = false;
+                    float alpha[2];
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        float mx = -INFINITY;
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+                            mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][n][0], sacc[mt][n][1])),
+                                       fmaxf(sacc[mt][n][2], sacc[mt][n][3]));
+                        mx = fmaxf(mx, shfl_xor_f(mx, 16));
+                        mx = fmaxf(mx, shfl_xor_f(mx, 32));
+                        const float mn = fmaxf(m[n], mx * a.scale_log2);
+                        const bool none = mn == -INFINITY; // nothing visible yet in this row
+                        const float msafe = none ? 0.f : mn;  // then every score is -inf and p = 0
+                        alpha[n] = none ? 1.f : __builtin_amdgcn_exp2f(m[n] - mn);
+                        rescale |= alpha[n] != 1.f;
+                        m[n] = mn;
+                        float sum = 0.f;
+                        float pv[4][4];
 #pragma unroll
                         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (key0 + 16 * mt + 4 * g + r >= kend[n]) sacc[mt][n][r] = -INFINITY;
-                }
-                u32x4_t phi[2][2], plo[2][2];          // B operands of P^T: [row tile][key step]
-                bool rescale = false;
-                float alpha[2];
+                            for (int r = 0; r < 4; ++r) {
+                                pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][r], a.scale_log2, -msafe));
+                                sum += pv[mt][r];
+                            }
+                        lp[n] = lp[n] * alpha[n] + sum;
 #pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    float mx = -INFINITY;
+                        for (int ks = 0; ks < 2; ++ks) {
+                            uint32_t hw[4], lw[4];
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-                        mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][n][0], sacc[mt][n][1])),
-                                   fmaxf(sacc[mt][n][2], sacc[mt][n][3]));
-                    mx = fmaxf(mx, shfl_xor_f(mx, 16));
-                    mx = fmaxf(mx, shfl_xor_f(mx, 32));
-                    const float mn = fmaxf(m[n], mx * a.scale_log2);
-                    const bool none = mn == -INFINITY; // nothing visible yet in this row
-                    const float msafe = none ? 0.f : mn;  // then every score is -inf and p = 0
-                    alpha[n] = none ? 1.f : __builtin_amdgcn_exp2f(m[n] - mn);
-                    rescale |= alpha[n] != 1.f;
-                    m[n] = mn;
-                    float sum = 0.f;
-                    float pv[4][4];
+                            for (int h = 0; h < 2; ++h) {      // key tile 2ks + h: slots 4h .. 4h+3
+                                const float* q4 = pv[2 * ks + h];
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                        for (int r = 0; r < 4; ++r) {
-                            pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][r], a.scale_log2, -msafe));
-                            sum += pv[mt][r];
-                        }
-                    lp[n] = lp[n] * alpha[n] + sum;
-#pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        uint32_t hw[4], lw[4];
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {      // key tile 2ks + h: slots 4h .. 4h+3
-                            const float* q4 = pv[2 * ks + h];
-#pragma unroll
-                            for (int r2 = 0; r2 < 2; ++r2) {
-                                if constexpr (kHalf) {
-                                    hw[2 * h + r2] = pack_f16x2(q4[2 * r2], q4[2 * r2 + 1]);
-                                } else {
-                                    // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
-                                    const uint32_t u0 = __float_as_uint(q4[2 * r2]);
-                                    const uint32_t u1 = __float_as_uint(q4[2 * r2 + 1]);
-                                    hw[2 * h + r2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-                                    lw[2 * h + r2] = pack_bf16x2(q4[2 * r2] - __uint_as_float(u0 & 0xffff0000u),
-                                                                 q4[2 * r2 + 1] - __uint_as_float(u1 & 0xffff0000u));
+                                for (int r2 = 0; r2 < 2; ++r2) {
+                                    if constexpr (kHalf) {
+                                        hw[2 * h + r2] = pack_f16x2(q4[2 * r2], q4[2 * r2 + 1]);
+                                    } else {
+                                        // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
+                                        const uint32_t u0 = __float_as_uint(q4[2 * r2]);
+                                        const uint32_t u1 = __float_as_uint(q4[2 * r2 + 1]);
+                                        hw[2 * h + r2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+                                        lw[2 * h + r2] = pack_bf16x2(q4[2 * r2] - __uint_as_float(u0 & 0xffff0000u),
+                                                                     q4[2 * r2 + 1] - __uint_as_float(u1 & 0xffff0000u));
+                                    }
                                 }
                             }
+                            phi[n][ks] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+                            if constexpr (!kHalf) plo[n][ks] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                         }
-                        phi[n][ks] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-                        if constexpr (!kHalf) plo[n][ks] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                     }
-                }
-                if (__builtin_amdgcn_ballot_w64(rescale)) {
+                    if (__builtin_amdgcn_ballot_w64(rescale)) {
 #pragma unroll
-                    for (int dt = 0; dt < 8; ++dt)
+                        for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-                        for (int n = 0; n < 2; ++n) oacc[dt][n] *= alpha[n];
-                }
+                            for (int n = 0; n < 2; ++n) oacc[dt][n] *= alpha[n];
+                    }
 
-                // O^T += V^T P^T: 8 dim tiles x 2 key steps (x hi and lo parts of P
-                // on the exact path)
-                const uint16_t* vl = &v_lds[buf][lr * kVStride + 4 * g];
-                auto v_operand = [&](int i) {              // step i: dim tile i / 2, key step i % 2
-                    const uint16_t* vrow = vl + (i >> 1) * 16 * kVStride + 32 * (i & 1);
-                    const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
-                    const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-                    return u32x4_t{v0.x, v0.y, v1.x, v1.y};
-                };
-                u32x4_t va[2];
-                va[0] = v_operand(0);
+                    // O^T += V^T P^T: 8 dim tiles x 2 key steps (x hi and lo parts of P
+                    // on the exact path)
+                    const uint16_t* vl = &v_lds[buf][lr * kVStride + 4 * g];
+                    auto v_operand = [&](int i) {              // step i: dim tile i / 2, key step i % 2
+                        const uint16_t* vrow = vl + (i >> 1) * 16 * kVStride + 32 * (i & 1);
+                        const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
+                        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+                        return u32x4_t{v0.x, v0.y, v1.x, v1.y};
+                    };
+                    u32x4_t va[2];
+                    va[0] = v_operand(0);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
-                    const int dt = i >> 1, ks = i & 1;
+                    for (int i = 0; i < 16; ++i) {
+                        if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
+                        const int dt = i >> 1, ks = i & 1;
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        if constexpr (kHalf) {
-                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(va[i & 1]),
-                                                                                 as_f16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
-                        } else {
-                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                as_bf16x8(va[i & 1]), as_bf16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
-                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                as_bf16x8(va[i & 1]), as_bf16x8(plo[n][ks]), oacc[dt][n], 0, 0, 0);
+                        for (int n = 0; n < 2; ++n) {
+                            if constexpr (kHalf) {
+                                oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(va[i & 1]),
+                                                                                     as_f16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
+                            } else {
+                                oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    as_bf16x8(va[i & 1]), as_bf16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
+                                oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                    as_bf16x8(va[i & 1]), as_bf16x8(plo[n][ks]), oacc[dt][n], 0, 0, 0);
+                            }
                         }
                     }
-                }
-                // keep the schedule as written: two operand reads ahead, then one
-                // LDS read per step's products
-                constexpr int kPerStep = kHalf ? 2 : 4;
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-                for (int i = 0; i < 15; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
+                    // keep the schedule as written: two operand reads ahead, then one
+                    // LDS read per step's products
+                    constexpr int kPerStep = kHalf ? 2 : 4;
                     __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                    for (int i = 0; i < 15; ++i) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
                 }
-                __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
+                if (kt + 1 < kt_end) commit(buf ^ 1, half);
+                __syncthreads();
             }
-            if (kt + 1 < kt_end) commit(buf ^ 1, half);
-            __syncthreads();
-        }
-    };
+        };
 
-    run(std::true_type{});
-    if (__syncthreads_or(vmax > 65504.f)) run(std::false_type{});   // a V value overflows fp16
-    // ---- finish: lane holds dims 16dt + 4g .. +4 of row 16n + lr.  A whole
-    // tile normalises and writes bf16 rows.  A piece of a split tile writes its
-    // (unnormalised rows, max, sum) record, and the tile's first piece lists the
-    // tile for the merge kernel.
+        run(std::true_type{});
+        if (__syncthreads_or(vmax > 65504.f)) run(std::false_type{});   // a V value overflows fp16
+        // ---- finish: lane holds dims 16dt + 4g .. +4 of row 16n + lr.  A tile
+        // within the share normalises and writes bf16 rows.  A segment of a tile
+        // that crosses a share boundary writes its (unnormalised rows, max, sum)
+        // record, in the workgroup's record 0 if the segment is its first, else in
+        // record 1; the segment holding the tile's first unit lists the tile for
+        // the merge kernel.
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-        float l = lp[n];
-        l += shfl_xor_f(l, 16);
-        l += shfl_xor_f(l, 32);
-        if (!active[n]) continue;
-        const int r = wave * kRowsPerWave + 16 * n + lr;
-        if (np == 1) {
-            const float inv = l > 0.f ? 1.f / l : 0.f;
-            uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(q0 + tok_begin + tq[n]) * Hq * kHeadDim +
-                          (int64_t)(kvh * G + r % G) * kHeadDim + 4 * g;
+        for (int n = 0; n < 2; ++n) {
+            float l = lp[n];
+            l += shfl_xor_f(l, 16);
+            l += shfl_xor_f(l, 32);
+            if (!active[n]) continue;
+            const int r = wave * kRowsPerWave + 16 * n + lr;
+            if (!split) {
+                const float inv = l > 0.f ? 1.f / l : 0.f;
+                uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(q0 + tok_begin + tq[n]) * Hq * kHeadDim +
+                              (int64_t)(kvh * G + r % G) * kHeadDim + 4 * g;
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                const f32x4_t v = oacc[dt][n];
-                *reinterpret_cast<u32x2_t*>(o + 16 * dt) =
-                    u32x2_t{pack_bf16x2(v.x * inv, v.y * inv), pack_bf16x2(v.z * inv, v.w * inv)};
+                for (int dt = 0; dt < 8; ++dt) {
+                    const f32x4_t v = oacc[dt][n];
+                    *reinterpret_cast<u32x2_t*>(o + 16 * dt) =
+                        u32x2_t{pack_bf16x2(v.x * inv, v.y * inv), pack_bf16x2(v.z * inv, v.w * inv)};
+                }
+            } else {
+                float* rec = a.part + (((int64_t)blockIdx.x * 2 + (first ? 0 : 1)) * kPrefillRows + r) * kRec;
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = oacc[dt][n];
+                if (g == 0) *reinterpret_cast<float2*>(rec + kHeadDim) = make_float2(m[n], l);
             }
-        } else {
-            float* rec = a.part + (((int64_t)piece * Hkv + kvh) * kPrefillRows + r) * kRec;
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = oacc[dt][n];
-            if (g == 0) *reinterpret_cast<float2*>(rec + kHeadDim) = make_float2(m[n], l);
+        }
+        // list entry: first slot, slots | (record of the first slot) << 24, first
+        // row, (tokens << 8) | KV head
+        if (split && u == tu0 && tid == 0) {
+            const int s0 = tu0 / share, s1 = (tu0 + units - 1) / share;
+            a.split_list[split_before * Hkv + kvh] =
+                int4{s0, (s1 - s0 + 1) | ((tu0 % share != 0) << 24), q0 + tok_begin, (ntok << 8) | kvh};
+        }
+
+        u = tu0 + seg_end;
+        if (u >= ue) break;
+        split_before += split;
+        tu0 += units;
+        ++tile;
+        while (tile >= nt && b + 1 < B) {                  // next sequence with query tiles
+            ++b;
+            sh = uniform(seq_shape(a, b));
+            nt = tiles_of(sh, TQ);
+            tile = 0;
         }
     }
-    if (np > 1 && j == 0 && tid == 0)
-        a.split_list[split_before * Hkv + kvh] = int4{piece, np, q0 + tok_begin, (ntok << 8) | kvh};
 }
 
-// Log-sum-exp merge of the pieces of every split query tile: per row,
+// Log-sum-exp merge of the segments of every listed query tile: per row,
 // M = max_p m_p, out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p, taken in
 // one pass with a running max.  Four workgroups per listed (tile, KV head),
 // 64 rows each; thread i covers dims 4(i % 32) .. +4 of rows i / 32 + 8k.
@@ -573,7 +611,7 @@ prefill_merge_kernel(PrefillArgs a) {
     const int e = (int)(blockIdx.x >> 2);
     if (e >= *a.split_count) return;
     const int4 d = a.split_list[e];
-    const int first = d.x, np = d.y, row0 = d.z, ntok = d.w >> 8, kvh = d.w & 255;
+    const int s0 = d.x, np = d.y & 0xffffff, rec0 = d.y >> 24, row0 = d.z, ntok = d.w >> 8, kvh = d.w & 255;
     const int Hkv = a.num_kv_heads;
     const int d4 = 4 * (threadIdx.x & 31);
     const int rbeg = 64 * (int)(blockIdx.x & 3);
@@ -588,7 +626,11 @@ prefill_merge_kernel(PrefillArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 if (p0 + i < np) {
-                    const float* rec = a.part + (((int64_t)(first + p0 + i) * Hkv + kvh) * kPrefillRows + r) * kRec;
+                    // segment p: slot s0 + p, record rec0 for p = 0 (the tile may
+                    // start inside that slot's share), else record 0
+                    const int p = p0 + i;
+                    const int64_t wg = (int64_t)(s0 + p) * Hkv + kvh;
+                    const float* rec = a.part + ((wg * 2 + (p == 0 ? rec0 : 0)) * kPrefillRows + r) * kRec;
                     ml[i] = *reinterpret_cast<const float2*>(rec + kHeadDim);
                     ov[i] = *reinterpret_cast<const f32x4_t*>(rec + d4);
                 }
@@ -615,12 +657,15 @@ prefill_merge_kernel(PrefillArgs a) {
 template <int G>
 hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     const size_t lds = 2 * sizeof(int32_t) * ((size_t)a.num_seqs + 1);
-    const int64_t grid = (int64_t)a.pieces_per_kvh * a.num_kv_heads;
+    const int64_t grid = (int64_t)a.slots_per_kvh * a.num_kv_heads;
     hipLaunchKernelGGL((prefill_kernel<G>), dim3((unsigned)grid), dim3(kThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    // a split tile has at least two pieces: at most grid / 2 tiles are listed
-    hipLaunchKernelGGL((prefill_merge_kernel<G>), dim3((unsigned)(4 * ((grid + 1) / 2))), dim3(256), 0, stream, a);
+    // a listed tile crosses one of the slots_per_kvh - 1 share boundaries of its
+    // KV head, each of which lies in one tile
+    const int64_t listed = (int64_t)(a.slots_per_kvh - 1) * a.num_kv_heads;
+    if (listed == 0) return hipSuccess;
+    hipLaunchKernelGGL((prefill_merge_kernel<G>), dim3((unsigned)(4 * listed)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 
