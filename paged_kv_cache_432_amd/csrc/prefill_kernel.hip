@@ -33,7 +33,7 @@
 //     p, twice the P.V products).
 //   * Causal masking selects -inf only on tiles that cross a row's limit; keys
 //     past seq_len are zero-filled in LDS (stale cache slots may hold NaN, and
-//     0 * NaN is NaN), and tiles wholly past a wave's rows are skipped.
+//     0 * NaN is NaN).
 //   * Work is balanced over the resident workgroups: the units of one KV
 //     head are its (query tile, 64-key tile) pairs in (sequence, tile, key
 //     tile) order, U of them, and each of the slots_per_kvh workgroups of a KV
@@ -82,6 +82,11 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 
 constexpr int kRec = 132;                    // partial record floats per row: 128 O, max, sum, pad
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
+constexpr float kSlack = 8.f;                // log2 headroom of the softmax reference max
+
+// IEEE-754 maximum (a NaN operand gives NaN): v_maximum3_f32 on gfx950, with
+// no quieting of the operands first.
+__device__ __forceinline__ float maximum(float x, float y) { return __builtin_elementwise_maximum(x, y); }
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -279,13 +284,14 @@ prefill_kernel(PrefillArgs a) {
                 qop[n][ks] = active[n] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
             }
         }
-        // wave-wide key limits: tiles at or past kmax are skipped, tiles ending past
-        // kmin need the mask
-        int kmin = min(kend[0], kend[1]), kmax = max(kend[0], kend[1]);
+        // wave-wide key limit: tiles ending past kmin need the mask.  (A tile
+        // wholly past the wave's rows is still computed, its scores all masked:
+        // skipping it would merge two versions of the accumulators at the join,
+        // which costs register copies on every tile.)
+        int kmin = min(kend[0], kend[1]);
 #pragma unroll
         for (int d = 1; d < kWave; d <<= 1) {
             kmin = min(kmin, __shfl_xor(kmin, d, kWave));
-            kmax = max(kmax, __shfl_xor(kmax, d, kWave));
         }
 
         float m[2];
@@ -365,7 +371,7 @@ prefill_kernel(PrefillArgs a) {
                     for (int i = 0; i < 4; ++i) {
                         e[i] = bf16_lo(w[i]);
                         o[i] = bf16_hi(w[i]);
-                        vmax = fmaxf(vmax, fmaxf(fabsf(e[i]), fabsf(o[i])));
+                        vmax = maximum(vmax, maximum(fabsf(e[i]), fabsf(o[i])));
                     }
                     even = u32x2_t{pack_f16x2(e[0], e[1]), pack_f16x2(e[2], e[3])};
                     odd = u32x2_t{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
@@ -407,148 +413,153 @@ prefill_kernel(PrefillArgs a) {
                 const int buf = (kt - kt_begin) & 1;
                 if (kt + 1 < kt_end) stage(kt + 1);
                 const int key0 = kt * kKeys;
-                if (key0 < kmax) {
-                    // S^T = K Q^T over this tile: 4 key tiles x 2 row tiles x 4 dim steps
-                    f32x4_t sacc[4][2];
+                // S^T = K Q^T over this tile: 4 key tiles x 2 row tiles x 4 dim steps
+                f32x4_t sacc[4][2];
+#pragma unroll
+                for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) sacc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                // operands read one step ahead of the products that use them, so
+                // that LDS latency overlaps the matrix work
+                const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * g];
+                auto k_operand = [&](int i) {              // step i: dim step i / 4, key tile i % 4
+                    return *reinterpret_cast<const u32x4_t*>(kl + (i & 3) * 16 * kKStride + 32 * (i >> 2));
+                };
+                u32x4_t ka[2];
+                ka[0] = k_operand(0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
+                    const int ks = i >> 2, mt = i & 3;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+                        sacc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[i & 1]),
+                                                                              as_bf16x8(qop[n][ks]), sacc[mt][n], 0, 0, 0);
+                }
+
+                // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr.
+                // The max is taken on raw scores (scale > 0) and the scale folded
+                // into the exponent: p = 2^(s * scale_log2 - m).  The reference m
+                // is raised only when a tile's maximum exceeds it by more than
+                // kSlack (log2 units), so p <= 2^kSlack (exact in fp16 and fp32)
+                // and the accumulator rescale is rare after the first tiles; the
+                // result is the same softmax, as O and l share the reference.
+                if (key0 + kKeys > kmin) {             // a row's limit falls in this tile
+#pragma unroll
+                    for (int n = 0; n < 2; ++n)
+#pragma unroll
+                        for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+                            for (int r = 0; r < 4; ++r)
+                                if (key0 + 16 * mt + 4 * g + r >= kend[n]) sacc[mt][n][r] = -INFINITY;
+                }
+                u32x4_t phi[2][2], plo[2][2];          // B operands of P^T: [row tile][key step]
+                bool rescale = false;
+                float alpha[2];
+#pragma unroll
+                for (int n = 0; n < 2; ++n) {
+                    float mx = -INFINITY;
+#pragma unroll
+                    for (int mt = 0; mt < 4; ++mt)
+                        mx = maximum(maximum(mx, maximum(sacc[mt][n][0], sacc[mt][n][1])),
+                                     maximum(sacc[mt][n][2], sacc[mt][n][3]));
+                    mx = maximum(mx, shfl_xor_f(mx, 16));
+                    mx = maximum(mx, shfl_xor_f(mx, 32));
+                    const float mtile = mx * a.scale_log2;
+                    const bool bump = mtile > m[n] + kSlack;
+                    const float mn = bump ? mtile : m[n];
+                    const bool none = mn == -INFINITY; // nothing visible yet in this row
+                    const float msafe = none ? 0.f : mn;  // then every score is -inf and p = 0
+                    alpha[n] = bump ? __builtin_amdgcn_exp2f(m[n] - mn) : 1.f;
+                    rescale |= bump && m[n] != -INFINITY;
+                    m[n] = mn;
+                    float sum = 0.f;
+                    float pv[4][4];
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                        for (int n = 0; n < 2; ++n) sacc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                    // operands read one step ahead of the products that use them, so
-                    // that LDS latency overlaps the matrix work
-                    const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * g];
-                    auto k_operand = [&](int i) {              // step i: dim step i / 4, key tile i % 4
-                        return *reinterpret_cast<const u32x4_t*>(kl + (i & 3) * 16 * kKStride + 32 * (i >> 2));
-                    };
-                    u32x4_t ka[2];
-                    ka[0] = k_operand(0);
+                        for (int r = 0; r < 4; ++r) {
+                            pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][r], a.scale_log2, -msafe));
+                            sum += pv[mt][r];
+                        }
+                    lp[n] = lp[n] * alpha[n] + sum;
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
-                        const int ks = i >> 2, mt = i & 3;
+                    for (int ks = 0; ks < 2; ++ks) {
+                        uint32_t hw[4], lw[4];
 #pragma unroll
-                        for (int n = 0; n < 2; ++n)
-                            sacc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[i & 1]),
-                                                                                  as_bf16x8(qop[n][ks]), sacc[mt][n], 0, 0, 0);
-                    }
-
-                    // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr.
-                    // The max is taken on raw scores (scale > 0) and the scale folded
-                    // into the exponent: p = 2^(s * scale_log2 - m).
-                    if (key0 + kKeys > kmin) {             // a row's limit falls in this tile
+                        for (int h = 0; h < 2; ++h) {      // key tile 2ks + h: slots 4h .. 4h+3
+                            const float* q4 = pv[2 * ks + h];
 #pragma unroll
-                        for (int n = 0; n < 2; ++n)
-#pragma unroll
-                            for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                                for (int r = 0; r < 4; ++r)
-                                    if (key0 + 16 * mt + 4 * g + r >= kend[n]) sacc[mt][n][r] = -INFINITY;
-                    }
-                    u32x4_t phi[2][2], plo[2][2];          // B operands of P^T: [row tile][key step]
-                    bool rescale = false;
-                    float alpha[2];
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        float mx = -INFINITY;
-#pragma unroll
-                        for (int mt = 0; mt < 4; ++mt)
-                            mx = fmaxf(fmaxf(mx, fmaxf(sacc[mt][n][0], sacc[mt][n][1])),
-                                       fmaxf(sacc[mt][n][2], sacc[mt][n][3]));
-                        mx = fmaxf(mx, shfl_xor_f(mx, 16));
-                        mx = fmaxf(mx, shfl_xor_f(mx, 32));
-                        const float mn = fmaxf(m[n], mx * a.scale_log2);
-                        const bool none = mn == -INFINITY; // nothing visible yet in this row
-                        const float msafe = none ? 0.f : mn;  // then every score is -inf and p = 0
-                        alpha[n] = none ? 1.f : __builtin_amdgcn_exp2f(m[n] - mn);
-                        rescale |= alpha[n] != 1.f;
-                        m[n] = mn;
-                        float sum = 0.f;
-                        float pv[4][4];
-#pragma unroll
-                        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r) {
-                                pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][r], a.scale_log2, -msafe));
-                                sum += pv[mt][r];
-                            }
-                        lp[n] = lp[n] * alpha[n] + sum;
-#pragma unroll
-                        for (int ks = 0; ks < 2; ++ks) {
-                            uint32_t hw[4], lw[4];
-#pragma unroll
-                            for (int h = 0; h < 2; ++h) {      // key tile 2ks + h: slots 4h .. 4h+3
-                                const float* q4 = pv[2 * ks + h];
-#pragma unroll
-                                for (int r2 = 0; r2 < 2; ++r2) {
-                                    if constexpr (kHalf) {
-                                        hw[2 * h + r2] = pack_f16x2(q4[2 * r2], q4[2 * r2 + 1]);
-                                    } else {
-                                        // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
-                                        const uint32_t u0 = __float_as_uint(q4[2 * r2]);
-                                        const uint32_t u1 = __float_as_uint(q4[2 * r2 + 1]);
-                                        hw[2 * h + r2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-                                        lw[2 * h + r2] = pack_bf16x2(q4[2 * r2] - __uint_as_float(u0 & 0xffff0000u),
-                                                                     q4[2 * r2 + 1] - __uint_as_float(u1 & 0xffff0000u));
-                                    }
+                            for (int r2 = 0; r2 < 2; ++r2) {
+                                if constexpr (kHalf) {
+                                    hw[2 * h + r2] = pack_f16x2(q4[2 * r2], q4[2 * r2 + 1]);
+                                } else {
+                                    // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
+                                    const uint32_t u0 = __float_as_uint(q4[2 * r2]);
+                                    const uint32_t u1 = __float_as_uint(q4[2 * r2 + 1]);
+                                    hw[2 * h + r2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+                                    lw[2 * h + r2] = pack_bf16x2(q4[2 * r2] - __uint_as_float(u0 & 0xffff0000u),
+                                                                 q4[2 * r2 + 1] - __uint_as_float(u1 & 0xffff0000u));
                                 }
                             }
-                            phi[n][ks] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-                            if constexpr (!kHalf) plo[n][ks] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                         }
+                        phi[n][ks] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+                        if constexpr (!kHalf) plo[n][ks] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                     }
-                    if (__builtin_amdgcn_ballot_w64(rescale)) {
-#pragma unroll
-                        for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                            for (int n = 0; n < 2; ++n) oacc[dt][n] *= alpha[n];
-                    }
-
-                    // O^T += V^T P^T: 8 dim tiles x 2 key steps (x hi and lo parts of P
-                    // on the exact path)
-                    const uint16_t* vl = &v_lds[buf][lr * kVStride + 4 * g];
-                    auto v_operand = [&](int i) {              // step i: dim tile i / 2, key step i % 2
-                        const uint16_t* vrow = vl + (i >> 1) * 16 * kVStride + 32 * (i & 1);
-                        const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
-                        const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
-                        return u32x4_t{v0.x, v0.y, v1.x, v1.y};
-                    };
-                    u32x4_t va[2];
-                    va[0] = v_operand(0);
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
-                        const int dt = i >> 1, ks = i & 1;
-#pragma unroll
-                        for (int n = 0; n < 2; ++n) {
-                            if constexpr (kHalf) {
-                                oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(va[i & 1]),
-                                                                                     as_f16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
-                            } else {
-                                oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    as_bf16x8(va[i & 1]), as_bf16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
-                                oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                    as_bf16x8(va[i & 1]), as_bf16x8(plo[n][ks]), oacc[dt][n], 0, 0, 0);
-                            }
-                        }
-                    }
-                    // keep the schedule as written: two operand reads ahead, then one
-                    // LDS read per step's products
-                    constexpr int kPerStep = kHalf ? 2 : 4;
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-                    for (int i = 0; i < 15; ++i) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
-                        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                    }
-                    __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
                 }
+                if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+                    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+                        for (int n = 0; n < 2; ++n) oacc[dt][n] *= alpha[n];
+                }
+
+                // O^T += V^T P^T: 8 dim tiles x 2 key steps (x hi and lo parts of P
+                // on the exact path)
+                const uint16_t* vl = &v_lds[buf][lr * kVStride + 4 * g];
+                auto v_operand = [&](int i) {              // step i: dim tile i / 2, key step i % 2
+                    const uint16_t* vrow = vl + (i >> 1) * 16 * kVStride + 32 * (i & 1);
+                    const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
+                    const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+                    return u32x4_t{v0.x, v0.y, v1.x, v1.y};
+                };
+                u32x4_t va[2];
+                va[0] = v_operand(0);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
+                    const int dt = i >> 1, ks = i & 1;
+#pragma unroll
+                    for (int n = 0; n < 2; ++n) {
+                        if constexpr (kHalf) {
+                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(va[i & 1]),
+                                                                                 as_f16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
+                        } else {
+                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf16x8(va[i & 1]), as_bf16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
+                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                as_bf16x8(va[i & 1]), as_bf16x8(plo[n][ks]), oacc[dt][n], 0, 0, 0);
+                        }
+                    }
+                }
+                // keep the schedule as written: two operand reads ahead, then one
+                // LDS read per step's products
+                constexpr int kPerStep = kHalf ? 2 : 4;
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+                for (int i = 0; i < 15; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
                 if (kt + 1 < kt_end) commit(buf ^ 1, half);
                 __syncthreads();
             }
         };
 
         run(std::true_type{});
-        if (__syncthreads_or(vmax > 65504.f)) run(std::false_type{});   // a V value overflows fp16
+        // a V magnitude beyond fp16 (or a NaN, which the exact path propagates)
+        if (__syncthreads_or(!(vmax <= 65504.f))) run(std::false_type{});
         // ---- finish: lane holds dims 16dt + 4g .. +4 of row 16n + lr.  A tile
         // within the share normalises and writes bf16 rows.  A segment of a tile
         // that crosses a share boundary writes its (unnormalised rows, max, sum)
