@@ -379,7 +379,9 @@ prefill_kernel(PrefillArgs a) {
                     even = u32x2_t{(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
                     odd = u32x2_t{(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
                 }
-                uint16_t* vt = &v_lds[buf][(2 * dp) * kVStride + 4 * (kq + 8 * j)];
+                // 4-key run q of V^T row d sits at run q ^ ((d >> 4) & 1): the 16
+                // rows 2dp a write instruction covers per cycle then span all banks
+                uint16_t* vt = &v_lds[buf][(2 * dp) * kVStride + 4 * ((kq + 8 * j) ^ ((dp >> 3) & 1))];
                 *reinterpret_cast<u32x2_t*>(vt) = even;
                 *reinterpret_cast<u32x2_t*>(vt + kVStride) = odd;
             }
@@ -473,16 +475,13 @@ prefill_kernel(PrefillArgs a) {
                     alpha[n] = bump ? __builtin_amdgcn_exp2f(m[n] - mn) : 1.f;
                     rescale |= bump && m[n] != -INFINITY;
                     m[n] = mn;
-                    float sum = 0.f;
                     float pv[4][4];
 #pragma unroll
                     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) {
+                        for (int r = 0; r < 4; ++r)
                             pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][r], a.scale_log2, -msafe));
-                            sum += pv[mt][r];
-                        }
-                    lp[n] = lp[n] * alpha[n] + sum;
+                    float sum = 0.f;
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks) {
                         uint32_t hw[4], lw[4];
@@ -492,7 +491,10 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
                             for (int r2 = 0; r2 < 2; ++r2) {
                                 if constexpr (kHalf) {
+                                    // the row sum adds the fp16 p that P.V uses
                                     hw[2 * h + r2] = pack_f16x2(q4[2 * r2], q4[2 * r2 + 1]);
+                                    sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hw[2 * h + r2]),
+                                                                 f16x2_t{1.f16, 1.f16}, sum, false);
                                 } else {
                                     // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
                                     const uint32_t u0 = __float_as_uint(q4[2 * r2]);
@@ -500,12 +502,14 @@ prefill_kernel(PrefillArgs a) {
                                     hw[2 * h + r2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
                                     lw[2 * h + r2] = pack_bf16x2(q4[2 * r2] - __uint_as_float(u0 & 0xffff0000u),
                                                                  q4[2 * r2 + 1] - __uint_as_float(u1 & 0xffff0000u));
+                                    sum += q4[2 * r2] + q4[2 * r2 + 1];
                                 }
                             }
                         }
                         phi[n][ks] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
                         if constexpr (!kHalf) plo[n][ks] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                     }
+                    lp[n] = lp[n] * alpha[n] + sum;
                 }
                 if (__builtin_amdgcn_ballot_w64(rescale)) {
 #pragma unroll
@@ -516,9 +520,11 @@ prefill_kernel(PrefillArgs a) {
 
                 // O^T += V^T P^T: 8 dim tiles x 2 key steps (x hi and lo parts of P
                 // on the exact path)
-                const uint16_t* vl = &v_lds[buf][lr * kVStride + 4 * g];
+                // rows 16dt + lr: runs swizzled by dt & 1 (see commit)
+                const uint16_t* vl0 = &v_lds[buf][lr * kVStride + 4 * g];
+                const uint16_t* vl1 = &v_lds[buf][lr * kVStride + 4 * (g ^ 1)];
                 auto v_operand = [&](int i) {              // step i: dim tile i / 2, key step i % 2
-                    const uint16_t* vrow = vl + (i >> 1) * 16 * kVStride + 32 * (i & 1);
+                    const uint16_t* vrow = ((i >> 1) & 1 ? vl1 : vl0) + (i >> 1) * 16 * kVStride + 32 * (i & 1);
                     const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
                     const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
                     return u32x4_t{v0.x, v0.y, v1.x, v1.y};
