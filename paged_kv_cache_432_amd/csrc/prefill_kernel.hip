@@ -88,6 +88,23 @@ constexpr float kSlack = 8.f;                // log2 headroom of the softmax ref
 // no quieting of the operands first.
 __device__ __forceinline__ float maximum(float x, float y) { return __builtin_elementwise_maximum(x, y); }
 
+// Across the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48), with
+// the gfx950 lane swaps (VALU, no LDS round trip): permlane32_swap(x, x)
+// returns the two 32-lane halves each broadcast to both, permlane16_swap(x, x)
+// the even and odd 16-lane rows each broadcast to their pair.
+__device__ __forceinline__ float max_across_rows(float x) {
+    auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = maximum(__uint_as_float(h[0]), __uint_as_float(h[1]));
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_rows(float x) {
+    auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
 // Exclusive prefix over the workgroup's threads of `x` (every thread calls).
@@ -465,8 +482,7 @@ prefill_kernel(PrefillArgs a) {
                     for (int mt = 0; mt < 4; ++mt)
                         mx = maximum(maximum(mx, maximum(sacc[mt][n][0], sacc[mt][n][1])),
                                      maximum(sacc[mt][n][2], sacc[mt][n][3]));
-                    mx = maximum(mx, shfl_xor_f(mx, 16));
-                    mx = maximum(mx, shfl_xor_f(mx, 32));
+                    mx = max_across_rows(mx);
                     const float mtile = mx * a.scale_log2;
                     const bool bump = mtile > m[n] + kSlack;
                     const float mn = bump ? mtile : m[n];
@@ -574,9 +590,7 @@ prefill_kernel(PrefillArgs a) {
         // the merge kernel.
 #pragma unroll
         for (int n = 0; n < 2; ++n) {
-            float l = lp[n];
-            l += shfl_xor_f(l, 16);
-            l += shfl_xor_f(l, 32);
+            const float l = sum_across_rows(lp[n]);
             if (!active[n]) continue;
             const int r = wave * kRowsPerWave + 16 * n + lr;
             if (!split) {
