@@ -12,7 +12,10 @@
 //   compute units and merges the pieces with log-sum-exp.
 //
 // One wavefront attends one KV head of one sequence over a contiguous range of
-// its 16-token blocks (attend() below):
+// its 16-token blocks.  For bf16 the products run on the matrix cores
+// (attend_mfma(): per block, S^T = K Q^T and O^T += V^T P^T as 16x16 MFMA tiles
+// whose lane layouts let P and V pass from the loads to the products without
+// any exchange; see there).  The vector path (attend() below, used for fp32):
 //   * The G query heads of the KV head share every K/V row the wave loads, so
 //     each cache byte is read once per call.
 //   * A 16-token block of one KV head is 16 rows of 256 B (bf16), Hkv*256 B
@@ -344,6 +347,201 @@ __device__ __forceinline__ void finish(WaveState<Chunk, Elem, G, QL>& st, int la
     }
 }
 
+// ---- matrix-core wave (bf16) ------------------------------------------------
+// The same attention of one wave over a block range, with the products on the
+// matrix cores: per 16-token block, S^T = K Q^T on v_mfma_f32_16x16x32_bf16
+// (16 tokens x 16 head columns, the G heads and zero padding) and
+// O^T += V^T P^T on v_mfma_f32_16x16x16_bf16.  Lane l = 16g + i:
+//   * K operand of product step ks: token i, dims 32ks + 8g .. +8, so that one
+//     load instruction reads 64 contiguous bytes of each of the 16 rows; Q is
+//     held in the same order;
+//   * S^T accumulator: head i, tokens 4g .. 4g+3 -- exactly the B-operand
+//     layout of P^T in the second product, so P stays in registers;
+//   * V operand: the V layout of the vector path (dims 8i .. 8i+7 of tokens
+//     4g .. 4g+3), read as output row i of dim tile dt meaning dim 8i + dt, so
+//     each operand is one byte permute of two loaded words, no transpose;
+//   * O^T accumulator: acc[dt][r] = O[head i][8 (4g + r) + dt].
+// P enters the second product as two bf16 operands, hi = p truncated to bf16
+// and lo = bf16(p - hi) (~16 bits of p).  The reference max is raised only when
+// a block's maximum exceeds it by more than 2^8 (log2 units), so the rescale of
+// the accumulators is rare; p stays below 256.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+constexpr float kMfmaSlack = 8.f;
+
+// Matrix-core path for bf16 at G >= this group size (the vector path below it
+// and for fp32).
+#ifndef PA_DECODE_MFMA_FROM
+#define PA_DECODE_MFMA_FROM 1
+#endif
+template <typename Elem, int G>
+constexpr bool kMfmaWave = sizeof(Elem) == 2 && G >= PA_DECODE_MFMA_FROM;
+
+// Blocks each matrix-core wave keeps in flight (its loop has far less vector
+// work per block than the vector path's, so more of the wave's time is spent
+// waiting on memory: three measured 4-7% faster than two).
+#ifndef PA_DECODE_MFMA_DEPTH
+#define PA_DECODE_MFMA_DEPTH 3
+#endif
+constexpr int kMfmaDepth = PA_DECODE_MFMA_DEPTH;
+
+struct MfmaState {
+    u32x4_t q[4];                  // B operand of S^T for product step ks: dims 32ks + 8g .. +8 (zero past G)
+    float m, l;                    // head i: reference max (log2 units); this lane's part of the sum
+    f32x4_t acc[8];
+};
+
+template <int G>
+__device__ __forceinline__ void load_query_mfma(const DecodeArgs& a, int64_t row, int kvh, int lane, MfmaState& st) {
+    const int i = lane & 15, g = lane >> 4;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) + row * a.q_stride +
+                         (int64_t)(kvh * G + (i < G ? i : 0)) * kHeadDim + 8 * g;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        st.q[ks] = i < G ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+    st.m = -INFINITY;
+    st.l = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) st.acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int G, bool NT, int NBUF>
+__device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int kvh, const int32_t* __restrict__ bt, int nblk,
+                                            int tok_first, int tok_end, int lane, MfmaState& st) {
+    const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;
+    const uint32_t blk_bytes = tok_bytes * kBlock;
+    const int i = lane & 15, g = lane >> 4;
+    const uint32_t koff = i * tok_bytes + (uint32_t)kvh * kHeadDim * 2 + g * 16;
+    const uint32_t voff = 4 * g * tok_bytes + (uint32_t)kvh * kHeadDim * 2 + i * 16;
+    const char* kc = reinterpret_cast<const char*>(a.key_cache);
+    const char* vc = reinterpret_cast<const char*>(a.value_cache);
+
+    for (int cb = 0; cb < nblk; cb += kWave) {
+        const int nb = min(kWave, nblk - cb);
+        const int bid = lane < nb ? bt[cb + lane] : 0;
+
+        auto issue = [&](u32x4_t (&kb)[4], u32x4_t (&vb)[4], int j) {
+            // The resource spans the block's valid tokens' rows: tokens past the
+            // end (stale or poisoned slots) and blocks past the range read as
+            // zeros without touching memory.  An id outside the pool is clamped
+            // into it.
+            const int64_t phys = min(max((int64_t)__builtin_amdgcn_readlane(bid, min(j, nb - 1)), (int64_t)0),
+                                     a.num_blocks - 1);
+            const int valid = j < nb ? min(max(tok_end - (tok_first + (cb + j) * kBlock), 0), kBlock) : 0;
+            const int nrec = __builtin_amdgcn_readfirstlane(valid * (int)tok_bytes);
+            const int64_t off = phys * (int64_t)blk_bytes;
+            const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
+            const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                kb[ks] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(koff + 64 * ks), 0,
+                                                                                             NT ? 2 : 0));
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                vb[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        rv, (int)(voff + r * tok_bytes), 0, NT ? 2 : 0));
+        };
+
+        auto process = [&](const u32x4_t (&kb)[4], const u32x4_t (&vb)[4], int j) {
+            // tokens of the block this lane's scores cover: 4g .. 4g+3; those past
+            // the end are masked (their K and V rows read as zeros)
+            const int nval = tok_end - (tok_first + (cb + j) * kBlock) - 4 * g;
+            f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[ks]),
+                                                            __builtin_bit_cast(bf16x8_t, st.q[ks]), s, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) s[r] = r < nval ? s[r] : -INFINITY;
+            const u32x4_t (&v)[4] = vb;
+            float mx = maximum(maximum(s[0], s[1]), maximum(s[2], s[3]));
+            mx = max_across_rows(mx);
+            const float mblk = mx * a.scale_log2;
+            const bool bump = mblk > st.m + kMfmaSlack;
+            const float mn = bump ? mblk : st.m;
+            const float msafe = mn == -INFINITY ? 0.f : mn;
+            const float alpha = bump ? __builtin_amdgcn_exp2f(st.m - mn) : 1.f;
+            if (__builtin_amdgcn_ballot_w64(bump && st.m != -INFINITY)) {
+#pragma unroll
+                for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= alpha;
+            }
+            st.m = mn;
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msafe));
+            st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+            uint32_t u[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) u[r] = __float_as_uint(p[r]);
+            // hi = p truncated to bf16 (top 16 bits); lo = bf16(p - hi), p - hi exact in fp32
+            const u32x2_t phi = u32x2_t{__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
+                                        __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
+            const u32x2_t plo = u32x2_t{pack_bf16x2(p[0] - __uint_as_float(u[0] & 0xffff0000u),
+                                                    p[1] - __uint_as_float(u[1] & 0xffff0000u)),
+                                        pack_bf16x2(p[2] - __uint_as_float(u[2] & 0xffff0000u),
+                                                    p[3] - __uint_as_float(u[3] & 0xffff0000u))};
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) {
+                // element dt of the four token chunks: word dt / 2, low or high half
+                const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+                const int w = dt >> 1;
+                const u32x2_t av = u32x2_t{__builtin_amdgcn_perm(v[1][w], v[0][w], sel),
+                                           __builtin_amdgcn_perm(v[3][w], v[2][w], sel)};
+                const s16x4_t A = __builtin_bit_cast(s16x4_t, av);
+                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(s16x4_t, phi), st.acc[dt],
+                                                                       0, 0, 0);
+                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(s16x4_t, plo), st.acc[dt],
+                                                                       0, 0, 0);
+            }
+        };
+
+        // Blocks are issued in the order they are consumed (the scheduling
+        // barriers keep it), so that each wait covers only the block it needs.
+        u32x4_t kbuf[NBUF][4], vbuf[NBUF][4];
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+            issue(kbuf[b], vbuf[b], b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int j = 0; j < nb; j += NBUF) {
+#pragma unroll
+            for (int b = 0; b < NBUF; ++b) {
+                if (b == 0 || j + b < nb) process(kbuf[b], vbuf[b], j + b);
+                issue(kbuf[b], vbuf[b], j + b + NBUF);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+}
+
+// Finish a range of the matrix-core wave: as finish(), lanes of head i < G
+// writing dims 32g + 8r .. +8 from acc[0..7][r].
+template <int G>
+__device__ __forceinline__ void finish_mfma(const MfmaState& st, int lane, uint16_t* out, float* rec) {
+    const int i = lane & 15, g = lane >> 4;
+    const float l = sum_across_rows(st.l);
+    if (i >= G) return;
+    if (out) {
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float f[8];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) f[dt] = st.acc[dt][r] * inv;
+            store_chunk(out + i * kHeadDim + 32 * g + 8 * r, f);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float f[8];
+#pragma unroll
+            for (int dt = 0; dt < 8; ++dt) f[dt] = st.acc[dt][r];
+            store_chunk(rec + i * kRec + 32 * g + 8 * r, f);
+        }
+        if (g == 0) *reinterpret_cast<float2*>(rec + i * kRec + kHeadDim) = make_float2(st.m, l);
+    }
+}
+
 // Query (and output) row of sequence b, or -1 when b is not a single-row
 // sequence of a mixed batch (the prefill kernel attends those).
 __device__ __forceinline__ int64_t decode_row(const DecodeArgs& a, int64_t b) {
@@ -362,8 +560,9 @@ __device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int64_t b) {
 template <typename Chunk, typename Elem, int G, bool QL, bool NT>
 __global__ void __launch_bounds__(256)
 decode_partition_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) float p_lds[kWavesPerGroup][kBlock * G];
-    __shared__ __attribute__((aligned(16))) Elem q_lds[QL ? kWavesPerGroup : 1][QL ? G * kHeadDim : 8];
+    constexpr bool MF = kMfmaWave<Elem, G>;
+    __shared__ __attribute__((aligned(16))) float p_lds[MF ? 1 : kWavesPerGroup][MF ? 4 : kBlock * G];
+    __shared__ __attribute__((aligned(16))) Elem q_lds[QL && !MF ? kWavesPerGroup : 1][QL && !MF ? G * kHeadDim : 8];
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int Hkv = a.num_kv_heads;
@@ -383,17 +582,22 @@ decode_partition_kernel(DecodeArgs a) {
     const int tok_end = min(L, tok_begin + PT);
     const int nblk = tok_end > tok_begin ? (tok_end - tok_begin + kBlock - 1) / kBlock : 0;
 
-    WaveState<Chunk, Elem, G, QL> st;
-    st.qs = q_lds[QL ? wave : 0];
-    load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
-    attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, a.block_table + b * a.bt_stride + tok_begin / kBlock, nblk,
-                                   tok_begin, L, p_lds[wave], lane, st);
-    if (nparts == 1) {
-        const int64_t h0 = row * a.num_heads + (int64_t)kvh * G;
-        finish<Chunk, Elem, G, QL>(st, lane, reinterpret_cast<Elem*>(a.out) + h0 * kHeadDim, nullptr);
+    const int64_t h0 = row * a.num_heads + (int64_t)kvh * G;
+    const int64_t r0 = ((b * Hkv + kvh) * a.max_partitions + part) * G;
+    const int32_t* bt = a.block_table + b * a.bt_stride + tok_begin / kBlock;
+    if constexpr (kMfmaWave<Elem, G>) {
+        MfmaState st;
+        load_query_mfma<G>(a, row, kvh, lane, st);
+        attend_mfma<G, NT, kMfmaDepth>(a, kvh, bt, nblk, tok_begin, L, lane, st);
+        if (nparts == 1) finish_mfma<G>(st, lane, reinterpret_cast<uint16_t*>(a.out) + h0 * kHeadDim, nullptr);
+        else finish_mfma<G>(st, lane, nullptr, a.part + r0 * kRec);
     } else {
-        const int64_t r0 = ((b * Hkv + kvh) * a.max_partitions + part) * G;
-        finish<Chunk, Elem, G, QL>(st, lane, nullptr, a.part + r0 * kRec);
+        WaveState<Chunk, Elem, G, QL> st;
+        st.qs = q_lds[QL ? wave : 0];
+        load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
+        attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, bt, nblk, tok_begin, L, p_lds[wave], lane, st);
+        if (nparts == 1) finish<Chunk, Elem, G, QL>(st, lane, reinterpret_cast<Elem*>(a.out) + h0 * kHeadDim, nullptr);
+        else finish<Chunk, Elem, G, QL>(st, lane, nullptr, a.part + r0 * kRec);
     }
 }
 
@@ -449,8 +653,9 @@ __global__ void __launch_bounds__(512)
 decode_stream_kernel(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) int32_t s_pref[];          // [num_seqs + 1]
     __shared__ int32_t s_wsum[8];
-    __shared__ __attribute__((aligned(16))) float p_lds[8][kBlock * G];
-    __shared__ __attribute__((aligned(16))) Elem q_lds[QL ? 8 : 1][QL ? G * kHeadDim : 8];
+    constexpr bool MF = kMfmaWave<Elem, G>;
+    __shared__ __attribute__((aligned(16))) float p_lds[MF ? 1 : 8][MF ? 4 : kBlock * G];
+    __shared__ __attribute__((aligned(16))) Elem q_lds[QL && !MF ? 8 : 1][QL && !MF ? G * kHeadDim : 8];
     block_prefix(a, s_pref, s_wsum);
     const int B = a.num_seqs;
     const int W = a.waves_per_group;
@@ -463,7 +668,7 @@ decode_stream_kernel(DecodeArgs a) {
     const int64_t u1 = min(u0 + Q, units);
     const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    float* pl = p_lds[wi];
+    float* pl = p_lds[MF ? 0 : wi];
 
     for (int64_t u = u0; u < u1;) {
         // the sequence holding unit u: the largest b with NG * prefix[b] <= u
@@ -482,19 +687,21 @@ decode_stream_kernel(DecodeArgs a) {
         const int L = seq_len_of(a, b);
         const int64_t row = decode_row(a, b);          // >= 0: only decode rows own blocks
 
-        WaveState<Chunk, Elem, G, QL> st;
-        st.qs = q_lds[QL ? wi : 0];
-        load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
-        attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, a.block_table + (int64_t)b * a.bt_stride + blk0, n,
-                                       blk0 * kBlock, L, pl, lane, st);
-        if (blk0 == 0 && n == nblk_b) {
-            finish<Chunk, Elem, G, QL>(st, lane,
-                                       reinterpret_cast<Elem*>(a.out) + (row * a.num_heads + (int64_t)kvh * G) * kHeadDim,
-                                       nullptr);
+        const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride + blk0;
+        const bool whole = blk0 == 0 && n == nblk_b;
+        Elem* out = reinterpret_cast<Elem*>(a.out) + (row * a.num_heads + (int64_t)kvh * G) * kHeadDim;
+        float* rec = a.part + ((((int64_t)blockIdx.x * 2 + (u == u0 ? 0 : 1)) * W + wi) * G) * kRec;
+        if constexpr (MF) {
+            MfmaState st;
+            load_query_mfma<G>(a, row, kvh, lane, st);
+            attend_mfma<G, NT, kMfmaDepth>(a, kvh, bt, n, blk0 * kBlock, L, lane, st);
+            finish_mfma<G>(st, lane, whole ? reinterpret_cast<uint16_t*>(out) : nullptr, whole ? nullptr : rec);
         } else {
-            const int slot = u == u0 ? 0 : 1;
-            finish<Chunk, Elem, G, QL>(st, lane, nullptr,
-                                   a.part + ((((int64_t)blockIdx.x * 2 + slot) * W + wi) * G) * kRec);
+            WaveState<Chunk, Elem, G, QL> st;
+            st.qs = q_lds[QL ? wi : 0];
+            load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
+            attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, bt, n, blk0 * kBlock, L, pl, lane, st);
+            finish<Chunk, Elem, G, QL>(st, lane, whole ? out : nullptr, whole ? nullptr : rec);
         }
         u += n;
     }

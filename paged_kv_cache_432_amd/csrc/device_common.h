@@ -13,6 +13,7 @@ constexpr int kBlock = 16;       // tokens per physical cache block
 constexpr int kHeadDim = 128;    // head_dim this build implements
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -110,6 +111,27 @@ __device__ __forceinline__ float dpp(float x) {
 __device__ __forceinline__ float shfl_xor_f(float x, int mask) {
     int lane = __lane_id();
     return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+// IEEE-754 maximum (a NaN operand gives NaN): v_maximum3_f32 on gfx950, with
+// no quieting of the operands first.
+__device__ __forceinline__ float maximum(float x, float y) { return __builtin_elementwise_maximum(x, y); }
+
+// Across the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48), with
+// the gfx950 lane swaps (VALU, no LDS round trip): permlane32_swap(x, x)
+// returns the two 32-lane halves each broadcast to both, permlane16_swap(x, x)
+// the even and odd 16-lane rows each broadcast to their pair.
+__device__ __forceinline__ float max_across_rows(float x) {
+    auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = maximum(__uint_as_float(h[0]), __uint_as_float(h[1]));
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_across_rows(float x) {
+    auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
+    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float readlane_f(float x, int lane) {

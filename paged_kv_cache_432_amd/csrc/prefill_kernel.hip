@@ -59,7 +59,6 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 8;
 constexpr int kRowsPerWave = 32;
@@ -83,27 +82,6 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 constexpr int kRec = 132;                    // partial record floats per row: 128 O, max, sum, pad
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
 constexpr float kSlack = 8.f;                // log2 headroom of the softmax reference max
-
-// IEEE-754 maximum (a NaN operand gives NaN): v_maximum3_f32 on gfx950, with
-// no quieting of the operands first.
-__device__ __forceinline__ float maximum(float x, float y) { return __builtin_elementwise_maximum(x, y); }
-
-// Across the four 16-lane rows of the wave (lanes l, l^16, l^32, l^48), with
-// the gfx950 lane swaps (VALU, no LDS round trip): permlane32_swap(x, x)
-// returns the two 32-lane halves each broadcast to both, permlane16_swap(x, x)
-// the even and odd 16-lane rows each broadcast to their pair.
-__device__ __forceinline__ float max_across_rows(float x) {
-    auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = maximum(__uint_as_float(h[0]), __uint_as_float(h[1]));
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return maximum(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_across_rows(float x) {
-    auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(h[0]) + __uint_as_float(h[1]);
-    auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
