@@ -714,6 +714,42 @@ decode_stream_kernel(DecodeArgs a) {
 // record index of piece p of n.
 template <typename Elem, typename RecOf>
 __device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec_of, int lane, Elem* o) {
+    constexpr int kFew = 8;
+    if (n <= kFew) {
+        // Few pieces (the usual case): every load is issued at once -- lane p's
+        // (max, sum) of piece p and this lane's two dims of every piece -- so
+        // the merge takes one round trip to memory.
+        float2 v[kFew];
+#pragma unroll
+        for (int q = 0; q < kFew; ++q)
+            v[q] = q < n ? *reinterpret_cast<const float2*>(part + rec_of(q) * kRec + 2 * lane) : make_float2(0.f, 0.f);
+        const float2 ml = lane < n ? *reinterpret_cast<const float2*>(part + rec_of(lane) * kRec + kHeadDim)
+                                   : make_float2(-INFINITY, 0.f);
+        float M = ml.x;
+#pragma unroll
+        for (int d = 1; d < kFew; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));   // lanes >= 8 hold -inf
+        M = readlane_f(M, 0);
+        const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+        float lsum = w * ml.y, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+        for (int d = 1; d < kFew; d <<= 1) lsum += shfl_xor_f(lsum, d);
+        lsum = readlane_f(lsum, 0);
+#pragma unroll
+        for (int q = 0; q < kFew; ++q) {
+            if (q < n) {
+                const float wq = readlane_f(w, q);
+                o0 = fmaf(wq, v[q].x, o0);
+                o1 = fmaf(wq, v[q].y, o1);
+            }
+        }
+        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+        if constexpr (sizeof(Elem) == 2) {
+            *reinterpret_cast<uint32_t*>(o + 2 * lane) = pack_bf16x2(o0 * inv, o1 * inv);
+        } else {
+            *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(o0 * inv, o1 * inv);
+        }
+        return;
+    }
     // pass over the pieces' (max, sum), 64 at a time, one per lane
     float M = -INFINITY;
     for (int p0 = 0; p0 < n; p0 += kWave) {
