@@ -517,8 +517,10 @@ prefill_kernel(PrefillArgs a) {
                 // rows 16dt + lr: runs swizzled by dt & 1 (see commit)
                 const uint16_t* vl0 = &v_lds[buf][lr * kVStride + 4 * g];
                 const uint16_t* vl1 = &v_lds[buf][lr * kVStride + 4 * (g ^ 1)];
-                auto v_operand = [&](int i) {              // step i: dim tile i / 2, key step i % 2
-                    const uint16_t* vrow = ((i >> 1) & 1 ? vl1 : vl0) + (i >> 1) * 16 * kVStride + 32 * (i & 1);
+                // step i: key step i / 8, dim tile i % 8 -- the two products into
+                // one accumulator are 16 products apart, which the MFMA latency needs
+                auto v_operand = [&](int i) {
+                    const uint16_t* vrow = ((i & 7) & 1 ? vl1 : vl0) + (i & 7) * 16 * kVStride + 32 * (i >> 3);
                     const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
                     const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
                     return u32x4_t{v0.x, v0.y, v1.x, v1.y};
@@ -528,7 +530,7 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
-                    const int dt = i >> 1, ks = i & 1;
+                    const int dt = i & 7, ks = i >> 3;
 #pragma unroll
                     for (int n = 0; n < 2; ++n) {
                         if constexpr (kHalf) {
