@@ -14,15 +14,19 @@
 //   * A workgroup owns 256 query rows of one (sequence, KV head): rows are
 //     (token, grouped head) pairs, token-major, so G = num_heads/num_kv_heads
 //     heads share every K/V tile and a tile spans 256/G tokens.  8 waves own
-//     32 rows each (two 16-row MFMA tiles).
+//     32 rows each, one 32-row MFMA tile.
 //   * K/V advance in tiles of 64 keys (4 cache blocks), double-buffered in LDS:
 //     K row-major with a padded row (conflict-free 16-byte operand reads), V
 //     transposed (dims x keys), as the P.V contraction runs over keys.
-//   * S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = K rows from LDS, B = the
-//     wave's query rows held in registers): each lane's accumulator then holds
-//     4 keys of ONE query row, which is exactly the lane layout of the B
-//     operand of the next product, so the probabilities feed O^T += V^T P^T
-//     without another pass through LDS.
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
+//     wave's query rows held in registers): lane l then holds query row l % 32
+//     and 16 of the tile's 32 keys per key tile, the lane pair (l, l ^ 32)
+//     covering the row, so row maxima and sums take one lane swap.  Eight of
+//     those scores form, in registers, the B operand of one 16-key step of
+//     O^T += V^T P^T (the V^T operand follows the same key order), so P never
+//     goes through LDS.  32x32x16 products sustain the matrix rate with one or
+//     two independent accumulators per wave, where 16x16x32 products need
+//     twelve or more (measured on MI355X).
 //   * P.V runs in fp16 (v_mfma_f32_16x16x32_f16): V^T is staged to LDS as
 //     fp16, exact for bf16 magnitudes below 2^16, and p in [0, 1] is rounded
 //     once to fp16 (11 significant bits, subnormals kept).  A single bf16
@@ -59,6 +63,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = 8;
 constexpr int kRowsPerWave = 32;
@@ -82,6 +87,17 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 constexpr int kRec = 132;                    // partial record floats per row: 128 O, max, sum, pad
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
 constexpr float kSlack = 8.f;                // log2 headroom of the softmax reference max
+
+// Between the two 32-lane halves of the wave (lanes l and l ^ 32):
+// permlane32_swap(x, x) returns each half broadcast to both.
+__device__ __forceinline__ float max_across_halves(float x) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return maximum(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_across_halves(float x) {
+    auto s = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -241,8 +257,8 @@ prefill_kernel(PrefillArgs a) {
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    const int lr = lane & 15;                          // MFMA row/column within a 16-tile
-    const int g = lane >> 4;                           // lane group
+    const int lr = lane & 31;                          // MFMA row/column within a 32-tile
+    const int h = lane >> 5;                           // lane half
     const int Hq = a.num_heads;
 
     // One segment per query tile the share touches: the key tiles of the
@@ -260,38 +276,33 @@ prefill_kernel(PrefillArgs a) {
         const int ntok = min(TQ, qlen - tok_begin);
         const int prior = L - qlen;                        // position of query row 0
 
-        // ---- this lane's two query rows (one per 16-row tile) and their key limits
-        int tq[2], kend[2];
-        bool active[2];
-        u32x4_t qop[2][4];                                 // B operand of S^T: dims 32ks + 8g .. +8
-#pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const int r = wave * kRowsPerWave + 16 * n + lr;
-            tq[n] = r / G;
-            active[n] = tq[n] < ntok;
-            const int pos = prior + tok_begin + tq[n];
-            kend[n] = !active[n] ? 0 : (a.causal ? max(min(L, pos + 1), 0) : L);
+        // ---- this lane's query row and its key limit.  Lane l of the wave holds
+        // row 32 * wave + l % 32; its two lanes (l, l ^ 32) each hold half of
+        // every tile's keys (h = l / 32 selects which).
+        const int r = wave * kRowsPerWave + lr;
+        const int tq = r / G;
+        const bool active = tq < ntok;
+        const int kend = !active ? 0 : (a.causal ? max(min(L, prior + tok_begin + tq + 1), 0) : L);
+        u32x4_t qop[8];                                    // B operand of S^T, dim step ks: dims 16ks + 8h .. +8
+        {
             const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
-                                 (int64_t)(q0 + tok_begin + (active[n] ? tq[n] : 0)) * a.q_stride +
-                                 (int64_t)(kvh * G + r % G) * kHeadDim + 8 * g;
+                                 (int64_t)(q0 + tok_begin + (active ? tq : 0)) * a.q_stride +
+                                 (int64_t)(kvh * G + r % G) * kHeadDim + 8 * h;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                qop[n][ks] = active[n] ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
-            }
+            for (int ks = 0; ks < 8; ++ks)
+                qop[ks] = active ? *reinterpret_cast<const u32x4_t*>(qp + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
         }
         // wave-wide key limit: tiles ending past kmin need the mask.  (A tile
         // wholly past the wave's rows is still computed, its scores all masked:
         // skipping it would merge two versions of the accumulators at the join,
         // which costs register copies on every tile.)
-        int kmin = min(kend[0], kend[1]);
+        int kmin = kend;
 #pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            kmin = min(kmin, __shfl_xor(kmin, d, kWave));
-        }
+        for (int d = 1; d < kWave; d <<= 1) kmin = min(kmin, __shfl_xor(kmin, d, kWave));
 
-        float m[2];
-        float lp[2];                                       // this lane's part of each row's sum
-        f32x4_t oacc[8][2];                                // O^T: dims 16dt + 4g + r, row 16n + lr
+        float m;
+        float lp;                                          // this lane's part of the row's sum
+        f32x16_t oacc[4];                                  // O^T: oacc[dt][4b + e] = dim 32dt + 8b + 4h + e
 
         // ---- K/V tile staging.  K: 1024 16-byte chunks (row, 16-byte part), two per
         // thread, stored row-major.  V: thread (dim pair dp, key quads kq, kq + 8)
@@ -390,15 +401,12 @@ prefill_kernel(PrefillArgs a) {
         // rounding.
         auto run = [&](auto half) {
             constexpr bool kHalf = decltype(half)::value;
+            m = -INFINITY;
+            lp = 0.f;
 #pragma unroll
-            for (int n = 0; n < 2; ++n) {
-                m[n] = -INFINITY;
-                lp[n] = 0.f;
-            }
+            for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                for (int n = 0; n < 2; ++n) oacc[dt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
             bid_base = -kWave;
             if (kt_begin < kt_end) {
                 stage(kt_begin);
@@ -410,119 +418,106 @@ prefill_kernel(PrefillArgs a) {
                 const int buf = (kt - kt_begin) & 1;
                 if (kt + 1 < kt_end) stage(kt + 1);
                 const int key0 = kt * kKeys;
-                // S^T = K Q^T over this tile: 4 key tiles x 2 row tiles x 4 dim steps
-                f32x4_t sacc[4][2];
+                // S^T = K Q^T over this tile: 2 key tiles of 32 x 8 dim steps of 16.
+                // sacc[mt][4b + e] is the score of key 32mt + 8b + 4h + e.
+                f32x16_t sacc[2];
 #pragma unroll
-                for (int mt = 0; mt < 4; ++mt)
+                for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int n = 0; n < 2; ++n) sacc[mt][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-                // operands read one step ahead of the products that use them, so
-                // that LDS latency overlaps the matrix work
-                const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * g];
-                auto k_operand = [&](int i) {              // step i: dim step i / 4, key tile i % 4
-                    return *reinterpret_cast<const u32x4_t*>(kl + (i & 3) * 16 * kKStride + 32 * (i >> 2));
+                    for (int v = 0; v < 16; ++v) sacc[mt][v] = 0.f;
+                // operands read one step ahead of the products that use them
+                const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * h];
+                auto k_operand = [&](int i) {              // step i: dim step i / 2, key tile i % 2
+                    return *reinterpret_cast<const u32x4_t*>(kl + (i & 1) * 32 * kKStride + 16 * (i >> 1));
                 };
                 u32x4_t ka[2];
                 ka[0] = k_operand(0);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
-                    const int ks = i >> 2, mt = i & 3;
-#pragma unroll
-                    for (int n = 0; n < 2; ++n)
-                        sacc[mt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[i & 1]),
-                                                                              as_bf16x8(qop[n][ks]), sacc[mt][n], 0, 0, 0);
+                    sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i & 1]), as_bf16x8(qop[i >> 1]),
+                                                                          sacc[i & 1], 0, 0, 0);
                 }
 
-                // online softmax per row; lane holds keys 16mt + 4g + r of row 16n + lr.
-                // The max is taken on raw scores (scale > 0) and the scale folded
-                // into the exponent: p = 2^(s * scale_log2 - m).  The reference m
-                // is raised only when a tile's maximum exceeds it by more than
-                // kSlack (log2 units), so p <= 2^kSlack (exact in fp16 and fp32)
-                // and the accumulator rescale is rare after the first tiles; the
-                // result is the same softmax, as O and l share the reference.
-                if (key0 + kKeys > kmin) {             // a row's limit falls in this tile
+                // online softmax of the row.  The max is taken on raw scores (scale
+                // > 0) and the scale folded into the exponent: p = 2^(s *
+                // scale_log2 - m).  The reference m is raised only when a tile's
+                // maximum exceeds it by more than kSlack (log2 units), so p <=
+                // 2^kSlack (exact in fp16 and fp32) and the accumulator rescale is
+                // rare after the first tiles; the result is the same softmax, as O
+                // and l share the reference.
+                if (key0 + kKeys > kmin) {                 // a row's limit falls in this tile
 #pragma unroll
-                    for (int n = 0; n < 2; ++n)
+                    for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-                            for (int r = 0; r < 4; ++r)
-                                if (key0 + 16 * mt + 4 * g + r >= kend[n]) sacc[mt][n][r] = -INFINITY;
+                        for (int v = 0; v < 16; ++v)
+                            if (key0 + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3) >= kend) sacc[mt][v] = -INFINITY;
                 }
-                u32x4_t phi[2][2], plo[2][2];          // B operands of P^T: [row tile][key step]
-                bool rescale = false;
-                float alpha[2];
+                float mx = -INFINITY;
 #pragma unroll
-                for (int n = 0; n < 2; ++n) {
-                    float mx = -INFINITY;
+                for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
-                        mx = maximum(maximum(mx, maximum(sacc[mt][n][0], sacc[mt][n][1])),
-                                     maximum(sacc[mt][n][2], sacc[mt][n][3]));
-                    mx = max_across_rows(mx);
-                    const float mtile = mx * a.scale_log2;
-                    const bool bump = mtile > m[n] + kSlack;
-                    const float mn = bump ? mtile : m[n];
-                    const bool none = mn == -INFINITY; // nothing visible yet in this row
-                    const float msafe = none ? 0.f : mn;  // then every score is -inf and p = 0
-                    alpha[n] = bump ? __builtin_amdgcn_exp2f(m[n] - mn) : 1.f;
-                    rescale |= bump && m[n] != -INFINITY;
-                    m[n] = mn;
-                    float pv[4][4];
+                    for (int v = 0; v < 16; v += 4)
+                        mx = maximum(maximum(mx, maximum(sacc[mt][v], sacc[mt][v + 1])),
+                                     maximum(sacc[mt][v + 2], sacc[mt][v + 3]));
+                mx = max_across_halves(mx);
+                const float mtile = mx * a.scale_log2;
+                const bool bump = mtile > m + kSlack;
+                const float mn = bump ? mtile : m;
+                const bool none = mn == -INFINITY;         // nothing visible yet in this row
+                const float msafe = none ? 0.f : mn;       // then every score is -inf and p = 0
+                const float alpha = bump ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+                const bool rescale = bump && m != -INFINITY;
+                m = mn;
+                // P^T as the B operand of key step s (keys 16s .. 16s+15): the 8
+                // scores sacc[s / 2][8 (s % 2) .. +8] of this lane, i.e. keys 16s +
+                // 8c + 4h + e for c, e -- the k order the V^T operand follows
+                u32x4_t phi[4], plo[4];
+                float sum = 0.f;
 #pragma unroll
-                    for (int mt = 0; mt < 4; ++mt)
+                for (int s = 0; s < 4; ++s) {
+                    float pv[8];
 #pragma unroll
-                        for (int r = 0; r < 4; ++r)
-                            pv[mt][r] = __builtin_amdgcn_exp2f(fmaf(sacc[mt][n][r], a.scale_log2, -msafe));
-                    float sum = 0.f;
+                    for (int e = 0; e < 8; ++e)
+                        pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], a.scale_log2, -msafe));
+                    uint32_t hw[4], lw[4];
 #pragma unroll
-                    for (int ks = 0; ks < 2; ++ks) {
-                        uint32_t hw[4], lw[4];
-#pragma unroll
-                        for (int h = 0; h < 2; ++h) {      // key tile 2ks + h: slots 4h .. 4h+3
-                            const float* q4 = pv[2 * ks + h];
-#pragma unroll
-                            for (int r2 = 0; r2 < 2; ++r2) {
-                                if constexpr (kHalf) {
-                                    // the row sum adds the fp16 p that P.V uses
-                                    hw[2 * h + r2] = pack_f16x2(q4[2 * r2], q4[2 * r2 + 1]);
-                                    sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hw[2 * h + r2]),
-                                                                 f16x2_t{1.f16, 1.f16}, sum, false);
-                                } else {
-                                    // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
-                                    const uint32_t u0 = __float_as_uint(q4[2 * r2]);
-                                    const uint32_t u1 = __float_as_uint(q4[2 * r2 + 1]);
-                                    hw[2 * h + r2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-                                    lw[2 * h + r2] = pack_bf16x2(q4[2 * r2] - __uint_as_float(u0 & 0xffff0000u),
-                                                                 q4[2 * r2 + 1] - __uint_as_float(u1 & 0xffff0000u));
-                                    sum += q4[2 * r2] + q4[2 * r2 + 1];
-                                }
-                            }
+                    for (int e2 = 0; e2 < 4; ++e2) {
+                        if constexpr (kHalf) {
+                            // the row sum adds the fp16 p that P.V uses
+                            hw[e2] = pack_f16x2(pv[2 * e2], pv[2 * e2 + 1]);
+                            sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hw[e2]), f16x2_t{1.f16, 1.f16}, sum,
+                                                         false);
+                        } else {
+                            // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
+                            const uint32_t u0 = __float_as_uint(pv[2 * e2]), u1 = __float_as_uint(pv[2 * e2 + 1]);
+                            hw[e2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+                            lw[e2] = pack_bf16x2(pv[2 * e2] - __uint_as_float(u0 & 0xffff0000u),
+                                                 pv[2 * e2 + 1] - __uint_as_float(u1 & 0xffff0000u));
+                            sum += pv[2 * e2] + pv[2 * e2 + 1];
                         }
-                        phi[n][ks] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-                        if constexpr (!kHalf) plo[n][ks] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                     }
-                    lp[n] = lp[n] * alpha[n] + sum;
+                    phi[s] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+                    if constexpr (!kHalf) plo[s] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                 }
+                lp = lp * alpha + sum;
                 if (__builtin_amdgcn_ballot_w64(rescale)) {
 #pragma unroll
-                    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-                        for (int n = 0; n < 2; ++n) oacc[dt][n] *= alpha[n];
+                    for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
                 }
 
-                // O^T += V^T P^T: 8 dim tiles x 2 key steps (x hi and lo parts of P
-                // on the exact path)
-                // rows 16dt + lr: runs swizzled by dt & 1 (see commit)
-                const uint16_t* vl0 = &v_lds[buf][lr * kVStride + 4 * g];
-                const uint16_t* vl1 = &v_lds[buf][lr * kVStride + 4 * (g ^ 1)];
-                // step i: key step i / 8, dim tile i % 8 -- the two products into
-                // one accumulator are 16 products apart, which the MFMA latency needs
-                auto v_operand = [&](int i) {
-                    const uint16_t* vrow = ((i & 7) & 1 ? vl1 : vl0) + (i & 7) * 16 * kVStride + 32 * (i >> 3);
-                    const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow);
-                    const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 16);
+                // O^T += V^T P^T: 4 key steps x 4 dim tiles of 32 (x hi and lo
+                // parts of P on the exact path).  The V^T operand of (dim tile dt,
+                // key step s): dim 32dt + l % 32, keys 16s + 4h .. +4 and
+                // 16s + 8 + 4h .. +4, i.e. 4-key runs 4s + h and 4s + 2 + h of the
+                // row, each swizzled by bit 4 of the dim (see commit).
+                const int sw = (lr >> 4) & 1;
+                const uint16_t* vl = &v_lds[buf][lr * kVStride];
+                auto v_operand = [&](int i) {              // step i: key step i / 4, dim tile i % 4
+                    const uint16_t* vrow = vl + (i & 3) * 32 * kVStride;
+                    const int s = i >> 2;
+                    const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow + 4 * ((4 * s + h) ^ sw));
+                    const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 4 * ((4 * s + 2 + h) ^ sw));
                     return u32x4_t{v0.x, v0.y, v1.x, v1.y};
                 };
                 u32x4_t va[2];
@@ -530,30 +525,17 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
-                    const int dt = i & 7, ks = i >> 3;
-#pragma unroll
-                    for (int n = 0; n < 2; ++n) {
-                        if constexpr (kHalf) {
-                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(va[i & 1]),
-                                                                                 as_f16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
-                        } else {
-                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                as_bf16x8(va[i & 1]), as_bf16x8(phi[n][ks]), oacc[dt][n], 0, 0, 0);
-                            oacc[dt][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                as_bf16x8(va[i & 1]), as_bf16x8(plo[n][ks]), oacc[dt][n], 0, 0, 0);
-                        }
+                    const int dt = i & 3, s = i >> 2;
+                    if constexpr (kHalf) {
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(va[i & 1]), as_f16x8(phi[s]), oacc[dt],
+                                                                          0, 0, 0);
+                    } else {
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[i & 1]), as_bf16x8(phi[s]),
+                                                                           oacc[dt], 0, 0, 0);
+                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[i & 1]), as_bf16x8(plo[s]),
+                                                                           oacc[dt], 0, 0, 0);
                     }
                 }
-                // keep the schedule as written: two operand reads ahead, then one
-                // LDS read per step's products
-                constexpr int kPerStep = kHalf ? 2 : 4;
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-                for (int i = 0; i < 15; ++i) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
-                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-                }
-                __builtin_amdgcn_sched_group_barrier(0x008, kPerStep, 0);
                 if (kt + 1 < kt_end) commit(buf ^ 1, half);
                 __syncthreads();
             }
@@ -562,32 +544,38 @@ prefill_kernel(PrefillArgs a) {
         run(std::true_type{});
         // a V magnitude beyond fp16 (or a NaN, which the exact path propagates)
         if (__syncthreads_or(!(vmax <= 65504.f))) run(std::false_type{});
-        // ---- finish: lane holds dims 16dt + 4g .. +4 of row 16n + lr.  A tile
+        // ---- finish: lane holds dims 32dt + 8b + 4h .. +4 of its row.  A tile
         // within the share normalises and writes bf16 rows.  A segment of a tile
         // that crosses a share boundary writes its (unnormalised rows, max, sum)
         // record, in the workgroup's record 0 if the segment is its first, else in
         // record 1; the segment holding the tile's first unit lists the tile for
         // the merge kernel.
+        {
+            const float l = sum_across_halves(lp);
+            if (active) {
+                if (!split) {
+                    const float inv = l > 0.f ? 1.f / l : 0.f;
+                    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(q0 + tok_begin + tq) * Hq * kHeadDim +
+                                  (int64_t)(kvh * G + r % G) * kHeadDim + 4 * h;
 #pragma unroll
-        for (int n = 0; n < 2; ++n) {
-            const float l = sum_across_rows(lp[n]);
-            if (!active[n]) continue;
-            const int r = wave * kRowsPerWave + 16 * n + lr;
-            if (!split) {
-                const float inv = l > 0.f ? 1.f / l : 0.f;
-                uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(q0 + tok_begin + tq[n]) * Hq * kHeadDim +
-                              (int64_t)(kvh * G + r % G) * kHeadDim + 4 * g;
+                    for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                for (int dt = 0; dt < 8; ++dt) {
-                    const f32x4_t v = oacc[dt][n];
-                    *reinterpret_cast<u32x2_t*>(o + 16 * dt) =
-                        u32x2_t{pack_bf16x2(v.x * inv, v.y * inv), pack_bf16x2(v.z * inv, v.w * inv)};
+                        for (int b4 = 0; b4 < 4; ++b4) {
+                            const f32x16_t& v = oacc[dt];
+                            *reinterpret_cast<u32x2_t*>(o + 32 * dt + 8 * b4) =
+                                u32x2_t{pack_bf16x2(v[4 * b4] * inv, v[4 * b4 + 1] * inv),
+                                        pack_bf16x2(v[4 * b4 + 2] * inv, v[4 * b4 + 3] * inv)};
+                        }
+                } else {
+                    float* rec = a.part + (((int64_t)blockIdx.x * 2 + (first ? 0 : 1)) * kPrefillRows + r) * kRec;
+#pragma unroll
+                    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                        for (int b4 = 0; b4 < 4; ++b4)
+                            *reinterpret_cast<f32x4_t*>(rec + 32 * dt + 8 * b4 + 4 * h) =
+                                f32x4_t{oacc[dt][4 * b4], oacc[dt][4 * b4 + 1], oacc[dt][4 * b4 + 2], oacc[dt][4 * b4 + 3]};
+                    if (h == 0) *reinterpret_cast<float2*>(rec + kHeadDim) = make_float2(m, l);
                 }
-            } else {
-                float* rec = a.part + (((int64_t)blockIdx.x * 2 + (first ? 0 : 1)) * kPrefillRows + r) * kRec;
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) *reinterpret_cast<f32x4_t*>(rec + 16 * dt + 4 * g) = oacc[dt][n];
-                if (g == 0) *reinterpret_cast<float2*>(rec + kHeadDim) = make_float2(m[n], l);
             }
         }
         // list entry: first slot, slots | (record of the first slot) << 24, first
