@@ -105,6 +105,24 @@ def probes(pa, torch, nbytes: int = 4 << 30, iters: int = 10):
     return out
 
 
+def mfma_probe(pa, torch, iters: int = 10):
+    """The library's matrix-core probe (4 independent v_mfma_f32_32x32x16_bf16
+    chains per wave, two 4-wave workgroups per compute unit): the matrix rate
+    the prefill kernel is set against next to the nominal peak."""
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    wgs = 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    flops = pa.pa_probe_mfma(sink, wgs, 4000)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for a, b in ev:
+        a.record()
+        pa.pa_probe_mfma(sink, wgs, 4000)
+        b.record()
+    torch.cuda.synchronize()
+    us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+    return {"TFLOPs": round(flops / us / 1e6, 1), "us": round(us, 1), "flops": flops, "workgroups": wgs}
+
+
 def cpu_baseline(w, nseq: int):
     """The oracle, untuned, on the host cores: the first `nseq` sequences of the
     workload (their K/V gathered through block tables into a compact pool built
@@ -223,6 +241,7 @@ def main_mixed(args, w, torch, pa, W, DeviceWorkload):
     kv = w.kv_bytes()
     flops = causal_flops(pre)
     tflops = flops / (pre_ms * 1e-3) / 1e12
+    mprobe = None if args.no_probes else mfma_probe(pa, torch)
     res = {
         "metric": METRIC,
         "value": round(kv / (ms_step * 1e-3) / 1e9, 2),
@@ -249,6 +268,7 @@ def main_mixed(args, w, torch, pa, W, DeviceWorkload):
             "avg_launch_us": round(pre_ms * 1e3, 2),
             "algorithmic_flops_per_launch": flops,
         },
+        "probes": {"mfma_32x32x16_bf16": mprobe} if mprobe else None,
         "decode_part": {
             "kernel": "pa_decode over the single-row requests",
             "bound": "hbm", "avg_launch_us": round(dec_ms * 1e3, 2),
@@ -257,6 +277,8 @@ def main_mixed(args, w, torch, pa, W, DeviceWorkload):
             "algorithmic_bytes_per_launch": dec.kv_bytes(),
         },
     }
+    if mprobe:
+        res["roofline"]["frac_of_mfma_probe"] = round(tflops / mprobe["TFLOPs"], 4)
     print(json.dumps(res), flush=True)
 
 

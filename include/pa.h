@@ -228,6 +228,19 @@ pa_status pa_probe_stream_read(const void *src, int64_t bytes, uint32_t *sink, i
 pa_status pa_probe_copy(void *dst, const void *src, int64_t bytes, int32_t workgroups,
                         hipStream_t stream);
 
+/*
+ * Matrix-core probe.  Not part of the attention path: it gives the MFMA-bound
+ * roofline of the chunked prefill (a dense contraction over the query rows,
+ * the article's section "Attention (FlashAttention, Scaled Dot-Product
+ * Attention)") the rate the matrix cores sustain on the same GPU, next to the
+ * nominal peak.  `workgroups` workgroups of 4 waves each run `iters` rounds of
+ * 4 independent v_mfma_f32_32x32x16_bf16 products: workgroups * 4 * iters * 4
+ * * 32768 flops.  `sink` (one uint32) is written only if the accumulators sum
+ * to a fixed value, which does not happen.  workgroups > 0, iters >= 0;
+ * PA_ERR_INVALID_ARG otherwise.
+ */
+pa_status pa_probe_mfma(uint32_t *sink, int32_t workgroups, int32_t iters, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

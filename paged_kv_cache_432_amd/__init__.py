@@ -19,7 +19,7 @@ __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
     "pa_slot_mapping", "pa_reshape_and_cache", "pa_decode_workspace_bytes",
     "pa_decode_partition_tokens", "pa_decode", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
-    "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy",
+    "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
 ]
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
@@ -85,6 +85,8 @@ def lib():
         L.pa_probe_stream_read.argtypes = [_vp, _i64, _vp, _i32, _vp]
         L.pa_probe_copy.restype = ctypes.c_int
         L.pa_probe_copy.argtypes = [_vp, _vp, _i64, _i32, _vp]
+        L.pa_probe_mfma.restype = ctypes.c_int
+        L.pa_probe_mfma.argtypes = [_vp, _i32, _i32, _vp]
         _lib = L
         return L
 
@@ -283,3 +285,12 @@ def pa_probe_copy(dst: torch.Tensor, src: torch.Tensor, workgroups: int = 0, str
     _need(dst.numel() * dst.element_size() >= nbytes, "dst smaller than src")
     s = lib().pa_probe_copy(_ptr(dst), _ptr(src), nbytes - nbytes % 16, workgroups, _stream(stream, src.device))
     _check(s, "pa_probe_copy")
+
+
+def pa_probe_mfma(sink: torch.Tensor, workgroups: int, iters: int, stream=None) -> int:
+    """Run the matrix-core rate probe; returns the flops it performs
+    (workgroups * 4 waves * iters * 4 * 32768)."""
+    _need(sink.numel() >= 1, "sink of one element")
+    s = lib().pa_probe_mfma(_ptr(sink), int(workgroups), int(iters), _stream(stream, sink.device))
+    _check(s, "pa_probe_mfma")
+    return int(workgroups) * 4 * int(iters) * 4 * 32768

@@ -501,4 +501,10 @@ pa_status pa_probe_copy(void* dst, const void* src, int64_t bytes, int32_t workg
     return hip_status(pa::launch_stream_copy(dst, src, bytes, workgroups, stream), "stream_copy launch");
 }
 
+pa_status pa_probe_mfma(uint32_t* sink, int32_t workgroups, int32_t iters, hipStream_t stream) {
+    if (workgroups <= 0 || iters < 0) return fail(PA_ERR_INVALID_ARG, "workgroups %d iters %d", workgroups, iters);
+    if (!sink) return fail(PA_ERR_INVALID_ARG, "null sink");
+    return hip_status(pa::launch_mfma_probe(sink, workgroups, iters, stream), "mfma probe launch");
+}
+
 }  // extern "C"

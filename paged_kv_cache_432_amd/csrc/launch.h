@@ -104,5 +104,7 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, in
                               hipStream_t stream);
 hipError_t launch_stream_copy(void* dst, const void* src, int64_t bytes, int32_t workgroups,
                               hipStream_t stream);
+// Matrix-core rate probe: workgroups x 4 waves x iters x 4 x 32768 flops.
+hipError_t launch_mfma_probe(uint32_t* sink, int32_t workgroups, int32_t iters, hipStream_t stream);
 
 }  // namespace pa

@@ -1,5 +1,5 @@
-// Memory probes for gfx950: a streaming read and a streaming copy of a flat
-// buffer.  They carry none of the attention arithmetic.  Decode attention is
+// Probes for gfx950: a streaming read and a streaming copy of a flat buffer,
+// and a matrix-core rate probe.  They carry none of the attention arithmetic.  Decode attention is
 // bound by HBM reads (the article "AI Infra入门干货总结：大模型是如何高效推理的",
 // section "Attention (FlashAttention, Scaled Dot-Product Attention)", on the
 // memory wall of reading the KV cache), so its roofline needs the bandwidth a
@@ -50,6 +50,39 @@ stream_copy_kernel(u32x4_t* __restrict__ dst, const u32x4_t* __restrict__ src, i
     for (; i < n16; i += stride) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// Matrix-core rate: every wave runs `iters` rounds of four independent
+// v_mfma_f32_32x32x16_bf16 accumulations (the instruction of the prefill's
+// S^T product; four chains keep it at its rate), 4 * 32768 flops a round.
+// The accumulators are reduced and stored only if the sum equals a value no
+// input produces, so the products cannot be dropped.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(kProbeThreads)
+mfma_rate_kernel(uint32_t* __restrict__ sink, int32_t iters) {
+    bf16x8_t x, y;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        x[e] = (__bf16)(0.001f * (float)(threadIdx.x + e));
+        y[e] = (__bf16)(0.002f * (float)(blockIdx.x % 7 + e));
+    }
+    f32x16_t c[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) c[j][v] = 0.f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) c[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) s += c[j][v];
+    if (s == 1234567.f) sink[0] = __float_as_uint(s);
+}
+
 int grid_for(int64_t n16, int32_t workgroups) {
     if (workgroups > 0) return workgroups;
     const int64_t want = (n16 + kProbeThreads - 1) / kProbeThreads;
@@ -57,6 +90,11 @@ int grid_for(int64_t n16, int32_t workgroups) {
 }
 
 }  // namespace
+
+hipError_t launch_mfma_probe(uint32_t* sink, int32_t workgroups, int32_t iters, hipStream_t stream) {
+    hipLaunchKernelGGL(mfma_rate_kernel, dim3(workgroups), dim3(kProbeThreads), 0, stream, sink, iters);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, int32_t workgroups,
                               hipStream_t stream) {

@@ -126,3 +126,13 @@ def test_chunked_prefill_rejects_before_launch(L, kw, status):
 def test_chunked_prefill_empty_is_ok(L):
     assert _prefill(L, num_seqs=0) == pa.PA_OK
     assert _prefill(L, num_q_tokens=0) == pa.PA_OK
+
+
+def test_probes_reject_before_launch(L):
+    """Probe arguments are checked on the host; none of these launches."""
+    assert L.pa_probe_mfma(None, 4, 10, None) == pa.PA_ERR_INVALID_ARG       # null sink
+    assert L.pa_probe_mfma(8, 0, 10, None) == pa.PA_ERR_INVALID_ARG          # no workgroups
+    assert L.pa_probe_mfma(8, 4, -1, None) == pa.PA_ERR_INVALID_ARG          # negative rounds
+    assert L.pa_probe_stream_read(8, 24, 8, 0, None) == pa.PA_ERR_INVALID_ARG  # not a multiple of 16
+    assert L.pa_probe_copy(16, 32, 16, -1, None) == pa.PA_ERR_INVALID_ARG      # negative grid
+    assert L.pa_probe_stream_read(None, 0, None, 0, None) == pa.PA_OK         # nothing to read
