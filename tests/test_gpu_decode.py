@@ -153,3 +153,34 @@ def test_chunked_mix_decode_part_split_mode(staging):
     """The decodes of the mixed batch, run through pa_decode (split-call mode)."""
     w = W.decode_part(W.chunked_prefill_mix())
     _sampled(staging, w, [0, 50, 95])
+
+
+@pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8), (8, 8)])
+def test_rising_scores_rescale(staging, hq, hkv):
+    """Scores that rise along the sequence (~50 log2 units over 2000 tokens):
+    the softmax reference is raised and the partial output rescaled many times
+    within one wave's range, in every split mode."""
+    w = W.custom("rise", seq_lens=[2000, 900, 37], num_heads=hq, num_kv_heads=hkv, dtype="bf16", seed=41)
+    draw_kv, draw_q = w.kv, w.query
+    memo = {}
+
+    def kv(b, length=None):
+        if (b, length) not in memo:
+            k, v = draw_kv(b)
+            k = k.copy()
+            k[:, :, 0] = W.bf16_round((0.05 * np.arange(k.shape[0], dtype=np.float32))[:, None]
+                                      * np.ones(k.shape[1], np.float32)[None, :])
+            n = int(w.seq_lens[b]) if length is None else int(length)
+            memo[(b, length)] = (k[:n], v[:n])
+        return memo[(b, length)]
+
+    def query(b):
+        q = draw_q(b).copy()
+        q[:, :, 0] = 4.0
+        return q
+
+    w.kv, w.query = kv, query
+    ref = oracle.run(w)
+    for pt in (0, -1, 256):
+        _, out = _run(staging, w, pt)
+        assert_parity(to_numpy(out), ref, "bf16", f"rising scores G={hq // hkv} pt={pt}")

@@ -176,3 +176,23 @@ def test_values_beyond_half_range(staging, hq, hkv):
     cu = base.cu_query_lens
     o[cu[0]:cu[1]] /= 2.0 ** 17
     assert_parity(o, ref, "bf16", f"V x 2^17 in sequence 0, G={hq // hkv}")
+
+
+def test_rising_scores_rescale(staging):
+    """Chunk rows whose scores rise along the keys (~40 log2 units over the
+    context): the softmax reference is raised, and the accumulators rescaled,
+    on many tiles, including across the pieces the merge combines."""
+    w = W.custom("rise", seq_lens=[1800, 700], query_lens=[300, 700], dtype="bf16", seed=18)
+
+    def kv_fn(b, k, v):
+        k[:, :, 0] = W.bf16_round((0.05 * np.arange(k.shape[0], dtype=np.float32))[:, None]
+                                  * np.ones(k.shape[1], np.float32)[None, :])
+        return k, v
+
+    def q_fn(b, q):
+        q[:, :, 0] = 4.0
+        return q
+
+    w = _with_values(w, kv_fn, q_fn)
+    _, out = _run(staging, w)
+    assert_parity(to_numpy(out), oracle.run(w), "bf16", "rising scores")
