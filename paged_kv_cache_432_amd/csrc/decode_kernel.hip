@@ -405,6 +405,51 @@ __device__ __forceinline__ void load_query_mfma(const DecodeArgs& a, int64_t row
     for (int dt = 0; dt < 8; ++dt) st.acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 }
 
+// One block's online softmax and O^T += V^T P^T for the matrix-core wave: s
+// holds the lane's scores (head i, tokens 4g .. 4g+3, masked ones -inf), v its
+// V chunks (tokens 4g .. 4g+3, dims 8i .. 8i+7).
+__device__ __forceinline__ void softmax_pv_mfma(const DecodeArgs& a, MfmaState& st, f32x4_t s, const u32x4_t (&v)[4]) {
+    float mx = maximum(maximum(s[0], s[1]), maximum(s[2], s[3]));
+    mx = max_across_rows(mx);
+    const float mblk = mx * a.scale_log2;
+    const bool bump = mblk > st.m + kMfmaSlack;
+    const float mn = bump ? mblk : st.m;
+    const float msafe = mn == -INFINITY ? 0.f : mn;
+    const float alpha = bump ? __builtin_amdgcn_exp2f(st.m - mn) : 1.f;
+    if (__builtin_amdgcn_ballot_w64(bump && st.m != -INFINITY)) {
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= alpha;
+    }
+    st.m = mn;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msafe));
+    st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
+    uint32_t u[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) u[r] = __float_as_uint(p[r]);
+    // hi = p truncated to bf16 (top 16 bits); lo = bf16(p - hi), p - hi exact in fp32
+    const u32x2_t phi = u32x2_t{__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
+                                __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
+    const u32x2_t plo = u32x2_t{pack_bf16x2(p[0] - __uint_as_float(u[0] & 0xffff0000u),
+                                            p[1] - __uint_as_float(u[1] & 0xffff0000u)),
+                                pack_bf16x2(p[2] - __uint_as_float(u[2] & 0xffff0000u),
+                                            p[3] - __uint_as_float(u[3] & 0xffff0000u))};
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+        // element dt of the four token chunks: word dt / 2, low or high half
+        const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+        const int w = dt >> 1;
+        const u32x2_t av = u32x2_t{__builtin_amdgcn_perm(v[1][w], v[0][w], sel),
+                                   __builtin_amdgcn_perm(v[3][w], v[2][w], sel)};
+        const s16x4_t A = __builtin_bit_cast(s16x4_t, av);
+        st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(s16x4_t, phi), st.acc[dt],
+                                                               0, 0, 0);
+        st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(s16x4_t, plo), st.acc[dt],
+                                                               0, 0, 0);
+    }
+}
+
 template <int G, bool NT, int NBUF>
 __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int kvh, const int32_t* __restrict__ bt, int nblk,
                                             int tok_first, int tok_end, int lane, MfmaState& st) {
@@ -453,46 +498,7 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int kvh, const 
                                                             __builtin_bit_cast(bf16x8_t, st.q[ks]), s, 0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r) s[r] = r < nval ? s[r] : -INFINITY;
-            const u32x4_t (&v)[4] = vb;
-            float mx = maximum(maximum(s[0], s[1]), maximum(s[2], s[3]));
-            mx = max_across_rows(mx);
-            const float mblk = mx * a.scale_log2;
-            const bool bump = mblk > st.m + kMfmaSlack;
-            const float mn = bump ? mblk : st.m;
-            const float msafe = mn == -INFINITY ? 0.f : mn;
-            const float alpha = bump ? __builtin_amdgcn_exp2f(st.m - mn) : 1.f;
-            if (__builtin_amdgcn_ballot_w64(bump && st.m != -INFINITY)) {
-#pragma unroll
-                for (int dt = 0; dt < 8; ++dt) st.acc[dt] *= alpha;
-            }
-            st.m = mn;
-            float p[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msafe));
-            st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
-            uint32_t u[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) u[r] = __float_as_uint(p[r]);
-            // hi = p truncated to bf16 (top 16 bits); lo = bf16(p - hi), p - hi exact in fp32
-            const u32x2_t phi = u32x2_t{__builtin_amdgcn_perm(u[1], u[0], 0x07060302u),
-                                        __builtin_amdgcn_perm(u[3], u[2], 0x07060302u)};
-            const u32x2_t plo = u32x2_t{pack_bf16x2(p[0] - __uint_as_float(u[0] & 0xffff0000u),
-                                                    p[1] - __uint_as_float(u[1] & 0xffff0000u)),
-                                        pack_bf16x2(p[2] - __uint_as_float(u[2] & 0xffff0000u),
-                                                    p[3] - __uint_as_float(u[3] & 0xffff0000u))};
-#pragma unroll
-            for (int dt = 0; dt < 8; ++dt) {
-                // element dt of the four token chunks: word dt / 2, low or high half
-                const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
-                const int w = dt >> 1;
-                const u32x2_t av = u32x2_t{__builtin_amdgcn_perm(v[1][w], v[0][w], sel),
-                                           __builtin_amdgcn_perm(v[3][w], v[2][w], sel)};
-                const s16x4_t A = __builtin_bit_cast(s16x4_t, av);
-                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(s16x4_t, phi), st.acc[dt],
-                                                                       0, 0, 0);
-                st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(A, __builtin_bit_cast(s16x4_t, plo), st.acc[dt],
-                                                                       0, 0, 0);
-            }
+            softmax_pv_mfma(a, st, s, vb);
         };
 
         // Blocks are issued in the order they are consumed (the scheduling
@@ -554,6 +560,186 @@ __device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int64_t b) {
     // Lengths beyond the block table's row are cut to it, so that no table entry
     // outside the row is read even when seq_lens breaks the contract.
     return max(min(a.seq_lens[b], a.bt_stride * kBlock), 0);
+}
+
+// The matrix-core wave over its whole share of the stream mode: units
+// u0 .. u1-1 (sequence, KV-head group, block), KV head grp * W + wi of each.
+// The share is a run of segments, one per (sequence, group), and its blocks
+// are loaded NBUF ahead straight across segment boundaries.  The workgroup
+// (whose waves all walk the same units) first writes an LDS table of the
+// share, up to kShareTable units at a time: per unit the physical block id,
+// its valid token count, the group, the query row and the blocks left in the
+// sequence.  The waves read it with LDS loads, whose wait count is apart from
+// that of the K/V loads in flight, so no step of the walk waits for memory
+// except on the data it is about to use.  Each segment's query is loaded when
+// the previous segment starts.  At a boundary the wave finishes one segment
+// (rows, or a partial record in the workgroup's slot 0 for its first segment
+// and slot 1 for its last) and starts the next with its blocks in flight.
+constexpr int kShareTable = 1024;
+constexpr int kFirstBlock = 1 << 30;                  // table flag: block 0 of its sequence
+
+template <int G, bool NT, int NBUF>
+__device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int32_t* s_pref, int4* s_tab, int64_t u0,
+                                                  int64_t u1, int W, int NG, int wi, int lane) {
+    const int total = (int)(u1 - u0);                  // the same for every wave of the workgroup
+    if (total <= 0) return;
+    const int B = a.num_seqs;
+    const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;
+    const uint32_t blk_bytes = tok_bytes * kBlock;
+    const int i = lane & 15, g = lane >> 4;
+    const uint32_t koff = i * tok_bytes + g * 16;       // the KV head's 256 bytes go in the base
+    const uint32_t voff = 4 * g * tok_bytes + i * 16;
+    const char* kc = reinterpret_cast<const char*>(a.key_cache);
+    const char* vc = reinterpret_cast<const char*>(a.value_cache);
+
+    int c0 = 0, c1 = 0;                                // the table holds blocks [c0, c1)
+    // the table entry of block j in [c0, c1), the same address in every lane
+    auto entry = [&](int j, int& id, int& valid, int& grp) {
+        const int2 e = *reinterpret_cast<const int2*>(&s_tab[j - c0]);
+        id = __builtin_amdgcn_readfirstlane(e.x);
+        const int vg = __builtin_amdgcn_readfirstlane(e.y);
+        valid = vg & 0xff;
+        grp = vg >> 8;
+    };
+
+    auto issue = [&](u32x4_t (&kb)[4], u32x4_t (&vb)[4], int j) {
+        int id = 0, valid = 0, grp = 0;
+        if (j < c1) entry(j, id, valid, grp);
+        const int64_t phys = min(max((int64_t)id, (int64_t)0), a.num_blocks - 1);   // an id outside the pool: clamped
+        // the resource spans the block's valid rows: past-the-end slots and
+        // blocks past the table read as zeros without touching memory
+        const int nrec = valid * (int)tok_bytes;
+        const int64_t off = phys * (int64_t)blk_bytes + (int64_t)(grp * W + wi) * kHeadDim * 2;
+        const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
+        const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            kb[ks] = __builtin_bit_cast(u32x4_t,
+                                        __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(koff + 64 * ks), 0, NT ? 2 : 0));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+            vb[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(voff + r * tok_bytes), 0,
+                                                                                         NT ? 2 : 0));
+    };
+
+    // the current segment, and the query of the segment starting at block qn_at
+    MfmaState st;
+    u32x4_t qn[4];
+    int qn_at = -1;
+    int seg_end = 0;                                   // first block past the current segment
+    bool seg_whole = false, seg_first = true;
+    uint16_t* seg_out = nullptr;
+    // (query row, KV head, blocks left in the sequence, first block?) of block j
+    auto segment_at = [&](int j, int64_t& row, int& kvh, int& rem, bool& first) {
+        const int4 e = s_tab[j - c0];
+        row = __builtin_amdgcn_readfirstlane(e.z);
+        kvh = (__builtin_amdgcn_readfirstlane(e.y) >> 8) * W + wi;
+        const int w = __builtin_amdgcn_readfirstlane(e.w);
+        rem = w & (kFirstBlock - 1);
+        first = (w & kFirstBlock) != 0;
+    };
+    auto query_of = [&](int j, u32x4_t (&q)[4]) {
+        int64_t row;
+        int kvh, rem;
+        bool first;
+        segment_at(j, row, kvh, rem, first);
+        const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) + row * a.q_stride +
+                             (int64_t)(kvh * G + (i < G ? i : 0)) * kHeadDim + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            q[ks] = i < G ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+    };
+    auto prefetch_query = [&]() {                      // the next segment's query, if it is in the table
+        if (seg_end < c1) {
+            query_of(seg_end, qn);
+            qn_at = seg_end;
+        }
+    };
+    auto finish_segment = [&]() {
+        float* rec = a.part + ((((int64_t)blockIdx.x * 2 + (seg_first ? 0 : 1)) * W + wi) * G) * kRec;
+        finish_mfma<G>(st, lane, seg_whole ? seg_out : nullptr, seg_whole ? nullptr : rec);
+    };
+    auto start_segment = [&](int j) {                  // block j begins a segment
+        int64_t row;
+        int kvh, rem;
+        bool first;
+        segment_at(j, row, kvh, rem, first);
+        if (qn_at == j) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) st.q[ks] = qn[ks];
+        } else {
+            // not prefetched (the share's first segment, or one past a table
+            // refill): load it here and wait for it on this path alone
+            query_of(j, st.q);
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        st.m = -INFINITY;
+        st.l = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) st.acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        seg_end = min(total, j + rem);
+        seg_whole = first && seg_end - j == rem;
+        seg_first = j == 0;
+        seg_out = reinterpret_cast<uint16_t*>(a.out) + (row * a.num_heads + (int64_t)kvh * G) * kHeadDim;
+        qn_at = -1;
+        prefetch_query();
+    };
+
+    auto process = [&](const u32x4_t (&kb)[4], const u32x4_t (&vb)[4], int j) {
+        if (j == seg_end) {                            // wave-uniform
+            if (j > 0) finish_segment();
+            start_segment(j);
+        }
+        int id, valid, grp;
+        entry(j, id, valid, grp);
+        const int nval = valid - 4 * g;                // this lane's tokens 4g .. 4g+3 of the block
+        f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kb[ks]),
+                                                        __builtin_bit_cast(bf16x8_t, st.q[ks]), s, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[r] = r < nval ? s[r] : -INFINITY;
+        softmax_pv_mfma(a, st, s, vb);
+    };
+
+    for (c0 = 0; c0 < total; c0 = c1) {
+        c1 = min(total, c0 + kShareTable);
+        __syncthreads();                               // the previous table is no longer read
+        for (int t = threadIdx.x; t < c1 - c0; t += blockDim.x) {
+            // unit -> (sequence b, group, block of b): b is the largest with NG * prefix[b] <= u
+            const int64_t u = u0 + c0 + t;
+            int lo = 0, hi = B - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if ((int64_t)NG * s_pref[mid] <= u) lo = mid; else hi = mid - 1;
+            }
+            const int nb = s_pref[lo + 1] - s_pref[lo];
+            const int64_t r = u - (int64_t)NG * s_pref[lo];
+            const int grp = (int)(r / nb), blk = (int)(r % nb);
+            const int id = a.block_table[(int64_t)lo * a.bt_stride + blk];
+            const int valid = min(max(seq_len_of(a, lo) - blk * kBlock, 0), kBlock);
+            const int row = (int)decode_row(a, lo);    // >= 0: only decode rows own blocks
+            s_tab[t] = int4{id, valid | (grp << 8), row, (nb - blk) | (blk == 0 ? kFirstBlock : 0)};
+        }
+        __syncthreads();
+        if (c0 > 0 && qn_at < 0) prefetch_query();    // the segment running on ends in this table
+        u32x4_t kbuf[NBUF][4], vbuf[NBUF][4];
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) {
+            issue(kbuf[b], vbuf[b], c0 + b);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int j = c0; j < c1; j += NBUF) {
+#pragma unroll
+            for (int b = 0; b < NBUF; ++b) {
+                if (b == 0 || j + b < c1) process(kbuf[b], vbuf[b], j + b);
+                issue(kbuf[b], vbuf[b], j + b + NBUF);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+    }
+    finish_segment();
 }
 
 // ---- partitioned mode ------------------------------------------------------
@@ -656,6 +842,7 @@ decode_stream_kernel(DecodeArgs a) {
     constexpr bool MF = kMfmaWave<Elem, G>;
     __shared__ __attribute__((aligned(16))) float p_lds[MF ? 1 : 8][MF ? 4 : kBlock * G];
     __shared__ __attribute__((aligned(16))) Elem q_lds[QL && !MF ? 8 : 1][QL && !MF ? G * kHeadDim : 8];
+    __shared__ int4 s_tab[MF ? kShareTable : 1];
     block_prefix(a, s_pref, s_wsum);
     const int B = a.num_seqs;
     const int W = a.waves_per_group;
@@ -669,6 +856,10 @@ decode_stream_kernel(DecodeArgs a) {
     const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     float* pl = p_lds[MF ? 0 : wi];
+    if constexpr (MF) {
+        stream_share_mfma<G, NT, kMfmaDepth>(a, s_pref, s_tab, u0, u1, W, NG, wi, lane);
+        return;
+    }
 
     for (int64_t u = u0; u < u1;) {
         // the sequence holding unit u: the largest b with NG * prefix[b] <= u
@@ -691,18 +882,11 @@ decode_stream_kernel(DecodeArgs a) {
         const bool whole = blk0 == 0 && n == nblk_b;
         Elem* out = reinterpret_cast<Elem*>(a.out) + (row * a.num_heads + (int64_t)kvh * G) * kHeadDim;
         float* rec = a.part + ((((int64_t)blockIdx.x * 2 + (u == u0 ? 0 : 1)) * W + wi) * G) * kRec;
-        if constexpr (MF) {
-            MfmaState st;
-            load_query_mfma<G>(a, row, kvh, lane, st);
-            attend_mfma<G, NT, kMfmaDepth>(a, kvh, bt, n, blk0 * kBlock, L, lane, st);
-            finish_mfma<G>(st, lane, whole ? reinterpret_cast<uint16_t*>(out) : nullptr, whole ? nullptr : rec);
-        } else {
-            WaveState<Chunk, Elem, G, QL> st;
-            st.qs = q_lds[QL ? wi : 0];
-            load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
-            attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, bt, n, blk0 * kBlock, L, pl, lane, st);
-            finish<Chunk, Elem, G, QL>(st, lane, whole ? out : nullptr, whole ? nullptr : rec);
-        }
+        WaveState<Chunk, Elem, G, QL> st;
+        st.qs = q_lds[QL ? wi : 0];
+        load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
+        attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, bt, n, blk0 * kBlock, L, pl, lane, st);
+        finish<Chunk, Elem, G, QL>(st, lane, whole ? out : nullptr, whole ? nullptr : rec);
         u += n;
     }
 }
