@@ -72,6 +72,13 @@ def lib():
                 _i32p, ctypes.c_int64, _i32p, _i32p, ctypes.c_int32,
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                 ctypes.c_double, ctypes.c_int32, ctypes.c_int32, _f64p, ctypes.c_int64]
+            L.oracle_rope_table.restype = None
+            L.oracle_rope_table.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
+            L.oracle_rope_qkv.restype = None
+            L.oracle_rope_qkv.argtypes = [
+                _f64p, _f64p, _f64p, ctypes.c_void_p, ctypes.c_int64, _i64p,
+                ctypes.POINTER(ctypes.c_float), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
+                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
             _lib = L
     return _lib
 
@@ -152,6 +159,41 @@ def attention(query, key_cache, value_cache, block_table, cu_query_lens, seq_len
             float(scale), int(bool(causal)), dtype,
             _p(probs, _f64p) if probs is not None else None, pstride)
     return (out, probs) if return_probs else out
+
+
+# ------------------------------------------------------ RoPE + QKV split --
+def rope_table(max_position: int, rotary_dim: int, base: float) -> np.ndarray:
+    """fp64 [max_position, rotary_dim]: cos(p * theta_i) then sin(p * theta_i),
+    theta_i = base^(-2i / rotary_dim)."""
+    t = np.empty((max_position, rotary_dim), np.float64)
+    lib().oracle_rope_table(_p(t, _f64p), int(max_position), int(rotary_dim), float(base))
+    return t
+
+
+def rope_qkv(qkv, positions, cos_sin, rotary_dim: int, neox_style: bool, num_heads: int,
+             num_kv_heads: int, head_dim: int):
+    """Split a fused projection qkv [num_tokens, (Hq + 2 Hkv) * D] (storage dtype:
+    uint16 bf16 bits or float32; rows may be strided) and rotate Q and K.
+
+    cos_sin is the float32 table the GPU reads.  Returns fp64 arrays
+    (q [n, Hq, D], k [n, Hkv, D], v [n, Hkv, D])."""
+    dtype = BF16 if qkv.dtype == np.uint16 else F32
+    assert qkv.strides[1] == qkv.itemsize
+    n = qkv.shape[0]
+    assert qkv.shape[1] >= (num_heads + 2 * num_kv_heads) * head_dim
+    pos = _c(positions, np.int64)
+    assert n == 0 or (pos.min() >= 0 and pos.max() < cos_sin.shape[0])
+    cs = _c(cos_sin, np.float32)
+    assert cs.shape[1] == rotary_dim
+    q = np.zeros((n, num_heads, head_dim), np.float64)
+    k = np.zeros((n, num_kv_heads, head_dim), np.float64)
+    v = np.zeros((n, num_kv_heads, head_dim), np.float64)
+    if n:
+        lib().oracle_rope_qkv(_p(q, _f64p), _p(k, _f64p), _p(v, _f64p), qkv.ctypes.data,
+                              qkv.strides[0] // qkv.itemsize, _p(pos, _i64p),
+                              cs.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), int(rotary_dim),
+                              int(bool(neox_style)), n, num_heads, num_kv_heads, head_dim, dtype)
+    return q, k, v
 
 
 # ------------------------------------------------- whole-workload helpers --

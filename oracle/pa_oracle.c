@@ -199,3 +199,88 @@ void oracle_attention(double *out, const void *query, int64_t q_stride,
         free(s);
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * The step just before attention: split a fused QKV projection row, rotate Q
+ * and K by their token's position (RoPE), and hand K and V to the scatter.
+ * "AI Infra入门干货总结：大模型是如何高效推理的", section "Reshape & Cache" and its
+ * table (Q is the first num_heads * head_dim columns of the projection, K the
+ * next num_kv_heads * head_dim, V the last; RoPE is applied elementwise from a
+ * cos/sin table of shape [max_position_embeddings, rotary_dim] looked up by
+ * position), and the RoPE summary near its opening (each pair of dimensions is
+ * a point in the complex plane, turned by the angle position * theta).
+ * ------------------------------------------------------------------------- */
+
+/* cos/sin table: row p holds cos(p * theta_i) in columns 0 .. R/2-1 and
+ * sin(p * theta_i) in columns R/2 .. R-1, with theta_i = base^(-2i / R) (the
+ * RoFormer frequency schedule; the pages give the base, 500000 for Llama-3-8B,
+ * and the table's shape). */
+void oracle_rope_table(double *table, int64_t max_position, int32_t rotary_dim, double base)
+{
+    const int32_t half = rotary_dim / 2;
+    for (int64_t p = 0; p < max_position; p++) {
+        for (int32_t i = 0; i < half; i++) {
+            double theta = pow(base, -2.0 * i / rotary_dim);
+            double angle = (double)p * theta;
+            table[p * rotary_dim + i] = cos(angle);
+            table[p * rotary_dim + half + i] = sin(angle);
+        }
+    }
+}
+
+/* Turn one head vector x (head_dim values, widened to double) by the angles of
+ * one table row.  Pair i (i < R/2) is the point (x[a], x[b]) with
+ * a = i, b = i + R/2 when neox_style (halves paired), or a = 2i, b = 2i + 1
+ * otherwise (neighbours paired); it becomes
+ *   (x[a] cos - x[b] sin,  x[b] cos + x[a] sin).
+ * Dimensions from rotary_dim on are not turned. */
+static void rotate_head(double *out, const double *x, const float *row, int32_t rotary_dim,
+                        int32_t neox_style, int32_t head_dim)
+{
+    const int32_t half = rotary_dim / 2;
+    for (int32_t d = 0; d < head_dim; d++)
+        out[d] = x[d];
+    for (int32_t i = 0; i < half; i++) {
+        int32_t a = neox_style ? i : 2 * i;
+        int32_t b = neox_style ? i + half : 2 * i + 1;
+        double c = (double)row[i];
+        double s = (double)row[half + i];
+        out[a] = x[a] * c - x[b] * s;
+        out[b] = x[b] * c + x[a] * s;
+    }
+}
+
+/* For each token t of a fused projection qkv [num_tokens, (Hq + 2 Hkv) * D]
+ * (rows qkv_stride elements apart, dtype 0 = float32, 1 = bf16 bits):
+ *   q_out[t, h, :] = rotate(Q head h of row t, position[t])       (fp64)
+ *   k_out[t, h, :] = rotate(K head h of row t, position[t])       (fp64)
+ *   v_out[t, h, :] = V head h of row t                            (fp64, as stored)
+ * cos_sin: float32 [max_position, rotary_dim], laid out as oracle_rope_table
+ * writes it; positions must lie in [0, max_position). */
+void oracle_rope_qkv(double *q_out, double *k_out, double *v_out, const void *qkv, int64_t qkv_stride,
+                     const int64_t *positions, const float *cos_sin, int32_t rotary_dim,
+                     int32_t neox_style, int64_t num_tokens, int32_t num_heads, int32_t num_kv_heads,
+                     int32_t head_dim, int32_t dtype)
+{
+    double *x = (double *)malloc(sizeof(double) * head_dim);
+    const int64_t k_col = (int64_t)num_heads * head_dim;
+    const int64_t v_col = k_col + (int64_t)num_kv_heads * head_dim;
+    for (int64_t t = 0; t < num_tokens; t++) {
+        const float *row = cos_sin + positions[t] * rotary_dim;
+        const int64_t base = t * qkv_stride;
+        for (int32_t h = 0; h < num_heads; h++) {
+            for (int32_t d = 0; d < head_dim; d++)
+                x[d] = widen(qkv, base + (int64_t)h * head_dim + d, dtype);
+            rotate_head(q_out + (t * num_heads + h) * head_dim, x, row, rotary_dim, neox_style, head_dim);
+        }
+        for (int32_t h = 0; h < num_kv_heads; h++) {
+            for (int32_t d = 0; d < head_dim; d++)
+                x[d] = widen(qkv, base + k_col + (int64_t)h * head_dim + d, dtype);
+            rotate_head(k_out + (t * num_kv_heads + h) * head_dim, x, row, rotary_dim, neox_style, head_dim);
+            for (int32_t d = 0; d < head_dim; d++)
+                v_out[(t * num_kv_heads + h) * head_dim + d] =
+                    widen(qkv, base + v_col + (int64_t)h * head_dim + d, dtype);
+        }
+    }
+    free(x);
+}

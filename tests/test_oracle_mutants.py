@@ -1,6 +1,6 @@
 """Plant a plausible mistake in a copy of the oracle's C source, build it, and
-check that the pins in test_oracle.py catch it.  CPU only; the oracle in the
-tree is never modified."""
+check that the pins in test_oracle.py and test_oracle_rope.py catch it.  CPU
+only; the oracle in the tree is never modified."""
 import os
 import subprocess
 import sys
@@ -25,7 +25,16 @@ MUTANTS = {
     "missing_normalisation": ("double w = s[t] / l;", "double w = s[t];"),
     "transposed_query_index": ("const int64_t qbase = row * q_stride + (int64_t)h * head_dim;",
                                "const int64_t qbase = (int64_t)h * q_stride + row * head_dim;"),
+    "rope_sign": ("out[a] = x[a] * c - x[b] * s;", "out[a] = x[a] * c + x[b] * s;"),
+    "rope_partner": ("int32_t b = neox_style ? i + half : 2 * i + 1;",
+                     "int32_t b = neox_style ? half - 1 - i + half : 2 * i + 1;"),
+    "rope_frequency": ("pow(base, -2.0 * i / rotary_dim)", "pow(base, -1.0 * i / rotary_dim)"),
+    "rope_cos_sin_swapped": ("table[p * rotary_dim + i] = cos(angle);", "table[p * rotary_dim + i] = sin(angle);"),
+    "rope_k_from_q_columns": ("x[d] = widen(qkv, base + k_col + (int64_t)h * head_dim + d, dtype);",
+                              "x[d] = widen(qkv, base + (int64_t)h * head_dim + d, dtype);"),
+    "rope_table_row": ("cos_sin + positions[t] * rotary_dim", "cos_sin + positions[t] * (rotary_dim / 2)"),
 }
+PIN_FILES = [os.path.join(ROOT, "tests", "test_oracle.py"), os.path.join(ROOT, "tests", "test_oracle_rope.py")]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
@@ -39,7 +48,6 @@ def test_pins_catch_planted_mistake(name, tmp_path):
     subprocess.run(["gcc", "-O1", "-fPIC", "-shared", "-std=c99", str(mutant_c), "-o", str(so), "-lm"],
                    check=True)
     env = dict(os.environ, PA_ORACLE_LIB=str(so), OMP_NUM_THREADS="2")
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        os.path.join(ROOT, "tests", "test_oracle.py")],
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PIN_FILES],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
