@@ -105,6 +105,67 @@ def probes(pa, torch, nbytes: int = 4 << 30, iters: int = 10):
     return out
 
 
+def rope_scatter_timing(pa, torch, token_counts=(64, 256, 2144, 16384), iters: int = 20, batch: int = 20):
+    """The fused step before attention (pa_rope_reshape_and_cache: QKV split,
+    RoPE on Q and K, K/V scatter) on Llama-3-8B shapes (32 Q heads, 8 KV heads,
+    6144-column bf16 projection, rope_theta 5e5, rotary_dim 128), one call per
+    count of new tokens.  Algorithmic bytes per token: the projection row read
+    (12288 B) + Q, K, V written (12288 B) + the table row (512 B) + position
+    and slot (16 B).  Each count is timed as a graph of `batch` calls back to
+    back (per-call GPU time, free of the host launch path)."""
+    hq, hkv, d, rot = 32, 8, 128, 128
+    dev = "cuda"
+    g = torch.Generator(device="cpu").manual_seed(21)
+    max_pos = 8192
+    inv = torch.pow(torch.tensor(500000.0, dtype=torch.float64),
+                    -2.0 * torch.arange(rot // 2, dtype=torch.float64) / rot)
+    ang = torch.arange(max_pos, dtype=torch.float64)[:, None] * inv[None, :]
+    table = torch.cat([ang.cos(), ang.sin()], 1).float().to(dev)
+    per_token = (hq + 2 * hkv) * d * 2 * 2 + rot * 4 + 16
+    rows = []
+    for n in token_counts:
+        nb = (n * 11 // 10 + 15) // 16 + 1
+        qkv = torch.randn(n, (hq + 2 * hkv) * d, generator=g).to(torch.bfloat16).to(dev)
+        qout = torch.empty(n, hq, d, dtype=torch.bfloat16, device=dev)
+        pos = torch.randint(0, max_pos, (n,), generator=g).to(dev)
+        slots = torch.randperm(nb * 16, generator=g)[:n].to(dev)
+        kc = torch.zeros(nb, 16, hkv, d, dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros_like(kc)
+
+        def call():
+            pa.pa_rope_reshape_and_cache(qout, qkv, pos, table, kc, vc, slots, hq, hkv)
+
+        for _ in range(5):
+            call()
+        torch.cuda.synchronize()
+        # a few small calls take less GPU time than their host launch path, so
+        # the calls are captured back to back in a graph and its replay timed
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(batch):
+                    call()
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for a, b in ev:
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / batch
+        gbps = n * per_token / us / 1e3
+        rows.append({"tokens": n, "us": round(us, 2), "GBps": round(gbps, 1),
+                     "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2), "bytes": n * per_token})
+        del qkv, qout, kc, vc, graph
+    torch.cuda.empty_cache()
+    return {"kernel": "rope_cache_kernel (pa_rope_reshape_and_cache)", "shapes": "Llama-3-8B, bf16",
+            "bytes_per_token": per_token, "calls": rows}
+
+
 def mfma_probe(pa, torch, iters: int = 10):
     """The library's matrix-core probe (4 independent v_mfma_f32_32x32x16_bf16
     chains per wave, two 4-wave workgroups per compute unit): the matrix rate
@@ -383,6 +444,7 @@ def main():
     if probe is not None:
         res["probes"] = probe
         res["roofline"]["frac_of_read_probe"] = round(dec_gbps / probe["stream_read"]["GBps"], 4)
+        res["rope_reshape_and_cache"] = rope_scatter_timing(pa, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs)
     print(json.dumps(res), flush=True)

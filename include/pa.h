@@ -114,6 +114,52 @@ pa_status pa_reshape_and_cache(const void *key, int64_t key_token_stride,
                                pa_dtype dtype, hipStream_t stream);
 
 /*
+ * The step just before attention, fused into one pass ("AI Infra入门干货总结：
+ * 大模型是如何高效推理的", section "Reshape & Cache" and its table, and the RoPE
+ * summary near its opening): split each token's fused QKV projection row into
+ * its Q | K | V column ranges, turn Q and K by the token's position (RoPE),
+ * write Q to query_out and scatter K and V into the paged cache exactly as
+ * pa_reshape_and_cache does.
+ *
+ * The turn: with R = rotary_dim and row = cos_sin_cache[positions[t], :]
+ * (cos of the R/2 angles in columns 0 .. R/2-1, their sin in R/2 .. R-1), pair
+ * i < R/2 of a head, (x[a], x[b]), becomes (x[a] cos_i - x[b] sin_i,
+ * x[b] cos_i + x[a] sin_i), where (a, b) = (i, i + R/2) when neox_style != 0
+ * (halves paired) and (2i, 2i + 1) otherwise (neighbours paired).  Dimensions
+ * R .. head_dim-1 are copied unchanged.  Arithmetic is fp32 (bf16 inputs are
+ * exact in fp32), each output rounded once to the storage dtype (nearest
+ * even).  V is copied bit for bit.
+ *
+ * query_out       [num_tokens, num_heads, head_dim], rows q_out_token_stride
+ *                 ELEMENTS apart.  May be qkv itself (same stride): Q is then
+ *                 turned in place.  No other overlap with any input is allowed.
+ * qkv             [num_tokens, (num_heads + 2 num_kv_heads) * head_dim], rows
+ *                 qkv_token_stride ELEMENTS apart (>= that width).
+ * positions       int64 [num_tokens]: the token's position in its sequence.  A
+ *                 position outside [0, max_position) breaks the caller's
+ *                 contract; it is clamped into the table so no read leaves it.
+ * cos_sin_cache   float32 [max_position, rotary_dim], contiguous, built once by
+ *                 the caller (e.g. theta_i = rope_theta^(-2i/R), row p =
+ *                 cos(p theta_i) then sin(p theta_i)).
+ * slot_mapping    int64 [num_tokens]; a slot < 0 (padding) or past the pool
+ *                 skips that token's K/V scatter; its Q is still written.
+ * key_cache, value_cache  [num_blocks, block_size, num_kv_heads, head_dim].
+ * rotary_dim      a multiple of 16 in [16, head_dim]; head_dim must be 128,
+ *                 block_size 16.
+ * All row starts (qkv, query_out, caches, cos_sin_cache) 16-byte aligned.
+ * num_tokens = 0 is a no-op.  One launch on `stream`, no allocation.
+ */
+pa_status pa_rope_reshape_and_cache(void *query_out, int64_t q_out_token_stride,
+                                    const void *qkv, int64_t qkv_token_stride,
+                                    const int64_t *positions, const float *cos_sin_cache,
+                                    int64_t max_position, int32_t rotary_dim, int32_t neox_style,
+                                    void *key_cache, void *value_cache,
+                                    const int64_t *slot_mapping, int64_t num_tokens,
+                                    int64_t num_blocks, int32_t block_size,
+                                    int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                    pa_dtype dtype, hipStream_t stream);
+
+/*
  * Workspace bytes pa_decode needs for these arguments (0 when no sequence is
  * split).  Same partition rule as pa_decode: partition_tokens > 0 is used as
  * given (a multiple of block_size), 0 picks a size from the shapes, -1 never

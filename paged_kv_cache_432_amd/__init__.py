@@ -17,7 +17,7 @@ import torch
 
 __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
-    "pa_slot_mapping", "pa_reshape_and_cache", "pa_decode_workspace_bytes",
+    "pa_slot_mapping", "pa_reshape_and_cache", "pa_rope_reshape_and_cache", "pa_decode_workspace_bytes",
     "pa_decode_partition_tokens", "pa_decode", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
     "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
 ]
@@ -67,6 +67,9 @@ def lib():
         L.pa_reshape_and_cache.restype = ctypes.c_int
         L.pa_reshape_and_cache.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32,
                                            _i32, _i32, ctypes.c_int, _vp]
+        L.pa_rope_reshape_and_cache.restype = ctypes.c_int
+        L.pa_rope_reshape_and_cache.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp,
+                                                _i64, _i64, _i32, _i32, _i32, _i32, ctypes.c_int, _vp]
         L.pa_decode_workspace_bytes.restype = ctypes.c_size_t
         L.pa_decode_workspace_bytes.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
         L.pa_decode_partition_tokens.restype = _i32
@@ -176,6 +179,41 @@ def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torc
                                    key_cache.shape[0], key_cache.shape[1], hkv, d, _dtype_code(key),
                                    _stream(stream, key_cache.device))
     _check(s, "pa_reshape_and_cache")
+
+
+def pa_rope_reshape_and_cache(query_out: torch.Tensor, qkv: torch.Tensor, positions: torch.Tensor,
+                              cos_sin_cache: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                              slot_mapping: torch.Tensor, num_heads: int, num_kv_heads: int,
+                              neox_style: bool = True, stream=None) -> torch.Tensor:
+    """Split qkv [num_tokens, (Hq + 2 Hkv) * D] (token stride free), turn Q and K
+    by positions (int64) through cos_sin_cache (float32 [max_position,
+    rotary_dim]), write Q to query_out [num_tokens, Hq, D] (token stride free;
+    may be the Q columns of qkv itself) and scatter K, V into the caches at
+    slot_mapping (int64)."""
+    _need(qkv.dim() == 2 and qkv.stride(1) == 1, "qkv: [num_tokens, width] with contiguous columns")
+    n = qkv.shape[0]
+    _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
+    d = key_cache.shape[3]
+    _need(key_cache.shape[2] == num_kv_heads, "cache KV heads differ from num_kv_heads")
+    _need(qkv.shape[1] >= (num_heads + 2 * num_kv_heads) * d, "qkv narrower than (Hq + 2 Hkv) * D")
+    _need(query_out.dim() == 3 and tuple(query_out.shape) == (n, num_heads, d), "query_out: [num_tokens, Hq, D]")
+    _need(query_out.stride(2) == 1 and query_out.stride(1) == d, "query_out heads and dims must be contiguous")
+    _need(qkv.dtype == query_out.dtype == key_cache.dtype == value_cache.dtype, "dtype mismatch")
+    _need(cos_sin_cache.dtype == torch.float32 and cos_sin_cache.dim() == 2 and cos_sin_cache.is_contiguous(),
+          "cos_sin_cache: contiguous float32 [max_position, rotary_dim]")
+    _need(positions.dtype == torch.int64 and positions.numel() == n and positions.is_contiguous(),
+          "positions: contiguous int64 [num_tokens]")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == n and slot_mapping.is_contiguous(),
+          "slot_mapping: contiguous int64 [num_tokens]")
+    s = lib().pa_rope_reshape_and_cache(_ptr(query_out), query_out.stride(0), _ptr(qkv), qkv.stride(0),
+                                        _ptr(positions), _ptr(cos_sin_cache), cos_sin_cache.shape[0],
+                                        cos_sin_cache.shape[1], int(bool(neox_style)), _ptr(key_cache),
+                                        _ptr(value_cache), _ptr(slot_mapping), n, key_cache.shape[0],
+                                        key_cache.shape[1], num_heads, num_kv_heads, d, _dtype_code(qkv),
+                                        _stream(stream, key_cache.device))
+    _check(s, "pa_rope_reshape_and_cache")
+    return query_out
 
 
 def pa_decode_workspace_bytes(num_seqs: int, num_heads: int, num_kv_heads: int, head_dim: int,

@@ -256,6 +256,57 @@ pa_status pa_reshape_and_cache(const void* key, int64_t key_token_stride, const 
                       "reshape_and_cache launch");
 }
 
+pa_status pa_rope_reshape_and_cache(void* query_out, int64_t q_out_token_stride, const void* qkv,
+                                    int64_t qkv_token_stride, const int64_t* positions, const float* cos_sin_cache,
+                                    int64_t max_position, int32_t rotary_dim, int32_t neox_style, void* key_cache,
+                                    void* value_cache, const int64_t* slot_mapping, int64_t num_tokens,
+                                    int64_t num_blocks, int32_t block_size, int32_t num_heads, int32_t num_kv_heads,
+                                    int32_t head_dim, pa_dtype dtype, hipStream_t stream) {
+    if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
+    if (head_dim != 128) return fail(PA_ERR_UNSUPPORTED, "head_dim %d (only 128)", head_dim);
+    if (rotary_dim < 16 || rotary_dim > head_dim || rotary_dim % 16)
+        return fail(PA_ERR_UNSUPPORTED, "rotary_dim %d (a multiple of 16 in [16, head_dim])", rotary_dim);
+    if (num_tokens < 0 || num_blocks < 0 || num_heads <= 0 || num_kv_heads <= 0 || max_position <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size");
+    if (num_tokens == 0) return ok();
+    if (!query_out || !qkv || !positions || !cos_sin_cache || !key_cache || !value_cache || !slot_mapping)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (num_tokens > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "num_tokens too large");
+    if ((int64_t)num_heads + 2 * (int64_t)num_kv_heads > (1 << 20))
+        return fail(PA_ERR_UNSUPPORTED, "too many heads");
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t width = ((int64_t)num_heads + 2 * (int64_t)num_kv_heads) * head_dim;
+    if (qkv_token_stride < width)
+        return fail(PA_ERR_INVALID_ARG, "qkv token stride %lld below (num_heads + 2 num_kv_heads) * head_dim",
+                    (long long)qkv_token_stride);
+    if (q_out_token_stride < (int64_t)num_heads * head_dim)
+        return fail(PA_ERR_INVALID_ARG, "query_out token stride below num_heads * head_dim");
+    if (!aligned16(query_out) || !aligned16(qkv) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        !aligned16(cos_sin_cache) || (qkv_token_stride * eb) % 16 || (q_out_token_stride * eb) % 16)
+        return fail(PA_ERR_INVALID_ARG, "rows must start on 16-byte boundaries");
+    if (query_out == qkv && q_out_token_stride != qkv_token_stride)
+        return fail(PA_ERR_INVALID_ARG, "in place, query_out must use the qkv row stride");
+    pa::RopeArgs a{};
+    a.query_out = query_out;
+    a.q_out_stride = q_out_token_stride;
+    a.qkv = qkv;
+    a.qkv_stride = qkv_token_stride;
+    a.positions = positions;
+    a.cos_sin = cos_sin_cache;
+    a.max_position = max_position;
+    a.rotary_dim = rotary_dim;
+    a.neox_style = neox_style ? 1 : 0;
+    a.key_cache = key_cache;
+    a.value_cache = value_cache;
+    a.slot_mapping = slot_mapping;
+    a.num_slots = num_blocks * 16;
+    a.num_tokens = num_tokens;
+    a.num_heads = num_heads;
+    a.num_kv_heads = num_kv_heads;
+    return hip_status(pa::launch_rope_cache(a, dtype == PA_BF16 ? 1 : 0, stream), "rope_reshape_and_cache launch");
+}
+
 int32_t pa_decode_partition_tokens(int32_t num_seqs, int32_t num_kv_heads, int32_t max_seq_len,
                                    int32_t partition_tokens) {
     if (use_stream(num_seqs, partition_tokens)) return 0;

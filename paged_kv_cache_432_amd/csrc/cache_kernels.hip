@@ -52,6 +52,110 @@ reshape_and_cache_kernel(const char* __restrict__ key, int64_t key_stride_bytes,
     }
 }
 
+// ---- RoPE + QKV split + scatter ---------------------------------------------
+// The step just before attention ("AI Infra入门干货总结：大模型是如何高效推理的",
+// section "Reshape & Cache" and its table; the RoPE summary near the article's
+// opening): the fused projection row of a token is split into its Q, K and V
+// column ranges, Q and K are turned pair by pair by the angles in row
+// positions[t] of a [max_position, rotary_dim] cos/sin table, Q goes to
+// query_out and K, V go straight into the paged cache at the token's slot.
+// One pass over the row: every byte of it is read once and written once.
+//
+// Work item = 16 elements of one head: for a turned range, both members of
+// eight pairs (halves paired: elements 8c.. and R/2 + 8c..; neighbours paired:
+// elements 16c .. 16c + 15); past rotary_dim, 16 elements copied as they are.
+// Each head has head_dim / 16 items; a token has (Hq + 2 Hkv) * 8 of them (Q
+// and K heads turned or copied, V heads copied), spread over one workgroup.
+template <typename Chunk, typename Elem>
+__global__ void __launch_bounds__(256)
+rope_cache_kernel(RopeArgs a) {
+    constexpr int kItems = kHeadDim / 16;              // items per head
+    const int64_t token = blockIdx.x;
+    const int R = a.rotary_dim, half = R / 2, turned = R / 16;
+    const int64_t p = min(max(a.positions[token], (int64_t)0), a.max_position - 1);
+    const float* cs = a.cos_sin + p * R;
+    const int64_t slot = a.slot_mapping[token];
+    const bool cached = slot >= 0 && slot < a.num_slots;
+    const int64_t cache_row = cached ? slot * (int64_t)a.num_kv_heads * kHeadDim : 0;
+    const Elem* row = reinterpret_cast<const Elem*>(a.qkv) + token * a.qkv_stride;
+    const int heads = a.num_heads + 2 * a.num_kv_heads;
+    for (int it = threadIdx.x; it < heads * kItems; it += blockDim.x) {
+        const int h = it / kItems, c = it % kItems;
+        const bool is_q = h < a.num_heads, is_v = h >= a.num_heads + a.num_kv_heads;
+        if (!is_q && !cached) continue;                // K and V of a padding token go nowhere
+        Elem* dst;
+        if (is_q) {
+            dst = reinterpret_cast<Elem*>(a.query_out) + token * a.q_out_stride + (int64_t)h * kHeadDim;
+        } else {
+            const int kvh = h - a.num_heads - (is_v ? a.num_kv_heads : 0);
+            dst = reinterpret_cast<Elem*>(is_v ? a.value_cache : a.key_cache) + cache_row + (int64_t)kvh * kHeadDim;
+        }
+        const Elem* src = row + (int64_t)h * kHeadDim;  // Q | K | V heads are consecutive in the row
+        int oa, ob;                                     // element offsets of the item's two 8-element chunks
+        if (is_v || c >= turned) {
+            oa = is_v ? 16 * c : R + 16 * (c - turned);
+            ob = oa + 8;
+        } else if (a.neox_style) {
+            oa = 8 * c;
+            ob = half + 8 * c;
+        } else {
+            oa = 16 * c;
+            ob = oa + 8;
+        }
+        Chunk ca, cb;
+        load_chunk<false>(ca, src + oa);
+        load_chunk<false>(cb, src + ob);
+        if (!is_v && c < turned) {
+            float x[8], y[8], co[8], si[8];
+            to_f32(ca, x);
+            to_f32(cb, y);
+            const f32x4_t* cp = reinterpret_cast<const f32x4_t*>(cs + 8 * c);
+            const f32x4_t* sp = reinterpret_cast<const f32x4_t*>(cs + half + 8 * c);
+            const f32x4_t c0 = cp[0], c1 = cp[1], s0 = sp[0], s1 = sp[1];
+            co[0] = c0.x; co[1] = c0.y; co[2] = c0.z; co[3] = c0.w;
+            co[4] = c1.x; co[5] = c1.y; co[6] = c1.z; co[7] = c1.w;
+            si[0] = s0.x; si[1] = s0.y; si[2] = s0.z; si[3] = s0.w;
+            si[4] = s1.x; si[5] = s1.y; si[6] = s1.z; si[7] = s1.w;
+            if (a.neox_style) {
+                // pair j = (x[j], y[j]) with angle j of the chunk
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float u = x[j], v = y[j];
+                    x[j] = fmaf(u, co[j], -v * si[j]);
+                    y[j] = fmaf(v, co[j], u * si[j]);
+                }
+            } else {
+                // pairs are neighbours: (x[0], x[1]) .. (x[6], x[7]) take angles
+                // 0 .. 3 of the chunk, (y[0], y[1]) .. (y[6], y[7]) angles 4 .. 7
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float u = x[2 * j], v = x[2 * j + 1];
+                    x[2 * j] = fmaf(u, co[j], -v * si[j]);
+                    x[2 * j + 1] = fmaf(v, co[j], u * si[j]);
+                    const float w = y[2 * j], z = y[2 * j + 1];
+                    y[2 * j] = fmaf(w, co[4 + j], -z * si[4 + j]);
+                    y[2 * j + 1] = fmaf(z, co[4 + j], w * si[4 + j]);
+                }
+            }
+            store_chunk(dst + oa, x);
+            store_chunk(dst + ob, y);
+        } else {
+            store_chunk_raw(dst + oa, ca);
+            store_chunk_raw(dst + ob, cb);
+        }
+    }
+}
+
+hipError_t launch_rope_cache(const RopeArgs& a, int dtype, hipStream_t stream) {
+    if (dtype == 1)
+        hipLaunchKernelGGL((rope_cache_kernel<ChunkBF16, uint16_t>), dim3((unsigned)a.num_tokens), dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL((rope_cache_kernel<ChunkF32, float>), dim3((unsigned)a.num_tokens), dim3(256), 0,
+                           stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
                                int32_t max_blocks_per_req, int32_t num_seqs,
                                const int32_t* token_seq, const int32_t* token_pos,

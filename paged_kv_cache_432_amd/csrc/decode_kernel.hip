@@ -107,14 +107,6 @@ struct WaveState {
     float acc[G][8];
 };
 
-__device__ __forceinline__ void store_chunk_raw(uint16_t* p, const ChunkBF16& c) {
-    *reinterpret_cast<u32x4_t*>(p) = c.w;
-}
-__device__ __forceinline__ void store_chunk_raw(float* p, const ChunkF32& c) {
-    reinterpret_cast<f32x4_t*>(p)[0] = c.a;
-    reinterpret_cast<f32x4_t*>(p)[1] = c.b;
-}
-
 template <typename Chunk, typename Elem, int G, bool QL>
 __device__ __forceinline__ void load_query(const DecodeArgs& a, int64_t row, int kvh, int lane,
                                            WaveState<Chunk, Elem, G, QL>& st) {

@@ -95,6 +95,15 @@ __device__ __forceinline__ void store_chunk(float* p, const float f[8]) {
     reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{f[4], f[5], f[6], f[7]};
 }
 
+// Store a chunk's bits unchanged.
+__device__ __forceinline__ void store_chunk_raw(uint16_t* p, const ChunkBF16& c) {
+    *reinterpret_cast<u32x4_t*>(p) = c.w;
+}
+__device__ __forceinline__ void store_chunk_raw(float* p, const ChunkF32& c) {
+    reinterpret_cast<f32x4_t*>(p)[0] = c.a;
+    reinterpret_cast<f32x4_t*>(p)[1] = c.b;
+}
+
 // ---- lane exchanges ---------------------------------------------------------
 // DPP controls (CDNA): quad_perm selects within groups of 4 lanes, row_ror
 // rotates within rows of 16 lanes.

@@ -13,6 +13,27 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
                                const int32_t* token_seq, const int32_t* token_pos,
                                int64_t num_tokens, hipStream_t stream);
 
+// RoPE + QKV split + scatter (rope_cache_kernel); sizes in elements.
+struct RopeArgs {
+    void* query_out;            // [num_tokens, num_heads, 128], rows q_out_stride apart
+    int64_t q_out_stride;
+    const void* qkv;            // [num_tokens, (num_heads + 2 num_kv_heads) * 128], rows qkv_stride apart
+    int64_t qkv_stride;
+    const int64_t* positions;   // [num_tokens]
+    const float* cos_sin;       // [max_position, rotary_dim]
+    int64_t max_position;
+    int32_t rotary_dim;
+    int32_t neox_style;
+    void* key_cache;
+    void* value_cache;
+    const int64_t* slot_mapping;
+    int64_t num_slots;          // num_blocks * 16
+    int64_t num_tokens;
+    int32_t num_heads;
+    int32_t num_kv_heads;
+};
+hipError_t launch_rope_cache(const RopeArgs& a, int dtype, hipStream_t stream);
+
 hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const void* value,
                                     int64_t value_stride, void* key_cache, void* value_cache,
                                     const int64_t* slot_mapping, int64_t num_tokens,

@@ -136,3 +136,41 @@ def test_probes_reject_before_launch(L):
     assert L.pa_probe_stream_read(8, 24, 8, 0, None) == pa.PA_ERR_INVALID_ARG  # not a multiple of 16
     assert L.pa_probe_copy(16, 32, 16, -1, None) == pa.PA_ERR_INVALID_ARG      # negative grid
     assert L.pa_probe_stream_read(None, 0, None, 0, None) == pa.PA_OK         # nothing to read
+
+
+def _rope(L, **kw):
+    a = dict(query_out=16, q_stride=4096, qkv=16, qkv_stride=6144, positions=16, cos_sin=16, max_position=8192,
+             rotary_dim=128, neox=1, key_cache=16, value_cache=16, slots=16, num_tokens=5, num_blocks=10,
+             block_size=16, num_heads=32, num_kv_heads=8, head_dim=128, dtype=1)
+    a.update(kw)
+    return L.pa_rope_reshape_and_cache(a["query_out"], a["q_stride"], a["qkv"], a["qkv_stride"], a["positions"],
+                                       a["cos_sin"], a["max_position"], a["rotary_dim"], a["neox"],
+                                       a["key_cache"], a["value_cache"], a["slots"], a["num_tokens"],
+                                       a["num_blocks"], a["block_size"], a["num_heads"], a["num_kv_heads"],
+                                       a["head_dim"], a["dtype"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rotary_dim=120), pa.PA_ERR_UNSUPPORTED),           # not a multiple of 16
+    (dict(rotary_dim=0), pa.PA_ERR_UNSUPPORTED),
+    (dict(rotary_dim=144), pa.PA_ERR_UNSUPPORTED),           # beyond head_dim
+    (dict(head_dim=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(dtype=7), pa.PA_ERR_UNSUPPORTED),
+    (dict(qkv_stride=6000), pa.PA_ERR_INVALID_ARG),          # narrower than Q | K | V
+    (dict(q_stride=4000), pa.PA_ERR_INVALID_ARG),
+    (dict(qkv_stride=6148), pa.PA_ERR_INVALID_ARG),          # bf16 rows off 16-byte boundaries
+    (dict(qkv=24), pa.PA_ERR_INVALID_ARG),
+    (dict(cos_sin=None), pa.PA_ERR_INVALID_ARG),
+    (dict(positions=None), pa.PA_ERR_INVALID_ARG),
+    (dict(max_position=0), pa.PA_ERR_INVALID_ARG),
+    (dict(num_tokens=-1), pa.PA_ERR_INVALID_ARG),
+    (dict(query_out=16, qkv=16, q_stride=4096, qkv_stride=6144), pa.PA_ERR_INVALID_ARG),   # in place, other stride
+])
+def test_rope_rejects_before_launch(L, kw, status):
+    assert _rope(L, **kw) == status
+    assert pa.pa_last_error_message()
+
+
+def test_rope_empty_is_ok(L):
+    assert _rope(L, num_tokens=0) == pa.PA_OK
