@@ -28,7 +28,7 @@ _LIB_PATH = os.path.join(_HERE, "libpa_oracle.so")
 _lib = None
 _lock = threading.Lock()
 
-F32, BF16 = 0, 1
+F32, BF16, E4M3 = 0, 1, 2
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -71,7 +71,17 @@ def lib():
                 _f64p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
                 _i32p, ctypes.c_int64, _i32p, _i32p, ctypes.c_int32,
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
-                ctypes.c_double, ctypes.c_int32, ctypes.c_int32, _f64p, ctypes.c_int64]
+                ctypes.c_double, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_double,
+                ctypes.c_double, _f64p, ctypes.c_int64]
+            L.oracle_e4m3_value.restype = ctypes.c_double
+            L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+            L.oracle_e4m3_encode.restype = ctypes.c_uint8
+            L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+            L.oracle_reshape_and_cache_fp8.restype = None
+            L.oracle_reshape_and_cache_fp8.argtypes = [
+                ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                ctypes.c_void_p, ctypes.c_void_p, _i64p, ctypes.c_int64,
+                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float]
             L.oracle_rope_table.restype = None
             L.oracle_rope_table.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
             L.oracle_rope_qkv.restype = None
@@ -133,13 +143,24 @@ def reshape_and_cache(key, value, key_cache, value_cache, slots, block_size: int
 
 
 # -------------------------------------------------------------- attention --
+def _dtype_of(a):
+    return {np.dtype(np.uint16): BF16, np.dtype(np.float32): F32, np.dtype(np.uint8): E4M3}[a.dtype]
+
+
 def attention(query, key_cache, value_cache, block_table, cu_query_lens, seq_lens,
-              num_heads: int, scale: float, causal: bool, return_probs: bool = False):
+              num_heads: int, scale: float, causal: bool, return_probs: bool = False,
+              k_scale: float = 1.0, v_scale: float = 1.0):
     """fp64 attention over the paged cache; returns out [num_q_tokens, Hq, D]
-    (and the probability rows [num_q_tokens, Hq, max_seq_len] if asked)."""
-    dtype = BF16 if key_cache.dtype == np.uint16 else F32
+    (and the probability rows [num_q_tokens, Hq, max_seq_len] if asked).
+
+    The query is bf16 bits (uint16) or float32; the caches are the same dtype,
+    or E4M3 codes (uint8) standing for code value * k_scale / v_scale."""
+    dtype = _dtype_of(query)
+    kv_dtype = _dtype_of(key_cache)
+    assert value_cache.dtype == key_cache.dtype and dtype != E4M3
+    assert kv_dtype == dtype or kv_dtype == E4M3
     q = query
-    assert q.dtype == key_cache.dtype and q.strides[1:] == (q.shape[2] * q.itemsize, q.itemsize)
+    assert q.strides[1:] == (q.shape[2] * q.itemsize, q.itemsize)
     bt = _c(block_table, np.int32)
     cu = _c(cu_query_lens, np.int32)
     sl = _c(seq_lens, np.int32)
@@ -156,9 +177,43 @@ def attention(query, key_cache, value_cache, block_table, cu_query_lens, seq_len
             _p(out, _f64p), q.ctypes.data, q.strides[0] // q.itemsize,
             key_cache.ctypes.data, value_cache.ctypes.data, _p(bt, _i32p), bt.shape[1],
             _p(cu, _i32p), _p(sl, _i32p), len(sl), num_heads, hkv, d, key_cache.shape[1],
-            float(scale), int(bool(causal)), dtype,
+            float(scale), int(bool(causal)), dtype, kv_dtype, float(k_scale), float(v_scale),
             _p(probs, _f64p) if probs is not None else None, pstride)
     return (out, probs) if return_probs else out
+
+
+# -------------------------------------------------------------- fp8 cache --
+def e4m3_value(code: int) -> float:
+    """The number an OCP E4M3 code stands for (NaN for 0x7F / 0xFF)."""
+    return float(lib().oracle_e4m3_value(int(code)))
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """E4M3 codes of float32 values: nearest, ties to even, saturating at 448."""
+    y = np.ascontiguousarray(y, np.float32)
+    enc = lib().oracle_e4m3_encode
+    return np.array([enc(float(v)) for v in y.ravel()], np.uint8).reshape(y.shape)
+
+
+def reshape_and_cache_fp8(key, value, key_cache, value_cache, slots, k_scale: float, v_scale: float,
+                          block_size: int = 16):
+    """In-place fp8 scatter into uint8 caches [num_blocks, block_size, Hkv, D]:
+    code = encode(x / scale) with the division in float32.  key/value are
+    bf16 bits (uint16) or float32, token rows may be strided."""
+    assert key_cache.dtype == value_cache.dtype == np.uint8
+    assert key_cache.flags.c_contiguous and value_cache.flags.c_contiguous
+    assert key.dtype == value.dtype
+    n = key.shape[0]
+    if n == 0:
+        return
+    hkv, d = key_cache.shape[2], key_cache.shape[3]
+    assert key.strides[1:] == (d * key.itemsize, key.itemsize)
+    assert value.strides[1:] == (d * value.itemsize, value.itemsize)
+    sm = _c(slots, np.int64)
+    lib().oracle_reshape_and_cache_fp8(
+        key.ctypes.data, key.strides[0] // key.itemsize, value.ctypes.data,
+        value.strides[0] // value.itemsize, key_cache.ctypes.data, value_cache.ctypes.data,
+        _p(sm, _i64p), n, int(block_size), hkv, d, _dtype_of(key), float(k_scale), float(v_scale))
 
 
 # ------------------------------------------------------ RoPE + QKV split --

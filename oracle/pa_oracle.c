@@ -35,6 +35,7 @@
 
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
+#define ORACLE_E4M3 2
 
 /* Number of threads the attention loop uses (OpenMP), for reporting. */
 int oracle_max_threads(void)
@@ -46,10 +47,14 @@ int oracle_max_threads(void)
 #endif
 }
 
+double oracle_e4m3_value(uint8_t code);
+
 static double widen(const void *base, int64_t idx, int dtype)
 {
     if (dtype == ORACLE_F32)
         return (double)((const float *)base)[idx];
+    if (dtype == ORACLE_E4M3)
+        return oracle_e4m3_value(((const uint8_t *)base)[idx]);
     uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;   /* bf16 is the top half of a float32 */
     float f;
     memcpy(&f, &u, sizeof f);
@@ -123,8 +128,12 @@ void oracle_reshape_and_cache(const void *key, int64_t key_stride,
  * otherwise all seq_lens[b] keys.  A row that sees no key outputs zeros.
  *
  * out:   double [num_q_tokens, num_heads, head_dim]
- * query: [num_q_tokens, num_heads, head_dim], rows q_stride elements apart
- * key_cache, value_cache: [num_blocks, block_size, num_kv_heads, head_dim]
+ * query: [num_q_tokens, num_heads, head_dim], rows q_stride elements apart,
+ *        storage dtype `dtype`
+ * key_cache, value_cache: [num_blocks, block_size, num_kv_heads, head_dim],
+ *        storage dtype `kv_dtype`; an element stands for its stored value
+ *        times k_scale (keys) or v_scale (values), the scales being 1 except
+ *        for an fp8 cache
  * probs (optional): the softmax row of every (query row, head), at
  *        probs[(row * num_heads + h) * probs_stride + t]
  */
@@ -134,6 +143,7 @@ void oracle_attention(double *out, const void *query, int64_t q_stride,
                       const int32_t *cu_query_lens, const int32_t *seq_lens, int32_t num_seqs,
                       int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                       int32_t block_size, double scale, int32_t causal, int32_t dtype,
+                      int32_t kv_dtype, double k_scale, double v_scale,
                       double *probs, int64_t probs_stride)
 {
     const int32_t group = num_heads / num_kv_heads;
@@ -174,7 +184,7 @@ void oracle_attention(double *out, const void *query, int64_t q_stride,
             int64_t kbase = ((blk * block_size + off) * num_kv_heads + kvh) * (int64_t)head_dim;
             double dot = 0.0;
             for (int32_t d = 0; d < head_dim; d++)
-                dot += widen(query, qbase + d, dtype) * widen(key_cache, kbase + d, dtype);
+                dot += widen(query, qbase + d, dtype) * (widen(key_cache, kbase + d, kv_dtype) * k_scale);
             s[t] = scale * dot;
             if (s[t] > m)
                 m = s[t];
@@ -192,7 +202,7 @@ void oracle_attention(double *out, const void *query, int64_t q_stride,
             int64_t vbase = ((blk * block_size + off) * num_kv_heads + kvh) * (int64_t)head_dim;
             double w = s[t] / l;
             for (int32_t d = 0; d < head_dim; d++)
-                o[d] += w * widen(value_cache, vbase + d, dtype);
+                o[d] += w * (widen(value_cache, vbase + d, kv_dtype) * v_scale);
             if (probs)
                 probs[row_head * probs_stride + t] = w;
         }
@@ -283,4 +293,77 @@ void oracle_rope_qkv(double *q_out, double *k_out, double *v_out, const void *qk
         }
     }
     free(x);
+}
+
+/* ---------------------------------------------------------------------------
+ * fp8 KV cache.  The pages say only that halving the bits per KV entry nearly
+ * halves decode time, and that e4m3 and e5m2 are both in use.  The format is
+ * taken from its published definition (OCP 8-bit floating point, E4M3): sign,
+ * 4 exponent bits with bias 7, 3 mantissa bits; exponent field 0 holds the
+ * subnormals m * 2^-9; S.1111.111 is NaN and there is no infinity, so the
+ * largest finite value is 1.75 * 2^8 = 448.  A cached value is
+ * code_value * scale, one float32 scale for K and one for V.
+ * ------------------------------------------------------------------------- */
+
+/* The real number a code stands for (NaN for the two NaN codes). */
+double oracle_e4m3_value(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        v = NAN;
+    else if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/* Encode y: the nearest of the 127 finite magnitudes 0x00 .. 0x7E, a tie going
+ * to the code whose mantissa is even, and magnitudes beyond 448 (infinity
+ * included) saturated to 448; NaN gives the NaN code.  The sign bit is y's. */
+uint8_t oracle_e4m3_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0;
+    if (isnan(y))
+        return sign | 0x7F;
+    double a = fabs((double)y);
+    if (a >= 448.0)
+        return sign | 0x7E;
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7E; c++) {
+        double d = fabs(oracle_e4m3_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+/* The fp8 scatter: like oracle_reshape_and_cache, but each element x of the
+ * token's K (V) row is stored as oracle_e4m3_encode(x / k_scale) (v_scale),
+ * the division done in float32.  key/value are float32 (dtype 0) or bf16 bits
+ * (dtype 1); the caches hold one byte per element. */
+void oracle_reshape_and_cache_fp8(const void *key, int64_t key_stride, const void *value, int64_t value_stride,
+                                  uint8_t *key_cache, uint8_t *value_cache, const int64_t *slot_mapping,
+                                  int64_t num_tokens, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                  int32_t dtype, float k_scale, float v_scale)
+{
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    for (int64_t i = 0; i < num_tokens; i++) {
+        int64_t s = slot_mapping[i];
+        if (s < 0)
+            continue;
+        int64_t dst = ((s / block_size) * block_size + s % block_size) * row_elems;
+        for (int64_t e = 0; e < row_elems; e++) {
+            float k = (float)widen(key, i * key_stride + e, dtype);
+            float v = (float)widen(value, i * value_stride + e, dtype);
+            key_cache[dst + e] = oracle_e4m3_encode(k / k_scale);
+            value_cache[dst + e] = oracle_e4m3_encode(v / v_scale);
+        }
+    }
 }

@@ -1,6 +1,7 @@
 """Plant a plausible mistake in a copy of the oracle's C source, build it, and
-check that the pins in test_oracle.py and test_oracle_rope.py catch it.  CPU
-only; the oracle in the tree is never modified."""
+check that the pins in test_oracle.py, test_oracle_rope.py and
+test_oracle_fp8.py catch it.  CPU only; the oracle in the tree is never
+modified."""
 import os
 import subprocess
 import sys
@@ -17,7 +18,7 @@ MUTANTS = {
                     "int64_t block_offset = (pos + 1) % block_size;"),
     "causal_off_by_one": ("const int64_t n = causal ? pos_q + 1 : L;",
                           "const int64_t n = causal ? pos_q : L;"),
-    "keys_read_from_values": ("widen(key_cache, kbase + d, dtype)", "widen(value_cache, kbase + d, dtype)"),
+    "keys_read_from_values": ("widen(key_cache, kbase + d, kv_dtype)", "widen(value_cache, kbase + d, kv_dtype)"),
     "gather_offset": ("int64_t off = t % block_size;", "int64_t off = (t + 1) % block_size;"),
     "scatter_reversed_offset": ("int64_t dst = (block * block_size + offset) * row_elems;",
                                 "int64_t dst = (block * block_size + (block_size - 1 - offset)) * row_elems;"),
@@ -33,8 +34,16 @@ MUTANTS = {
     "rope_k_from_q_columns": ("x[d] = widen(qkv, base + k_col + (int64_t)h * head_dim + d, dtype);",
                               "x[d] = widen(qkv, base + (int64_t)h * head_dim + d, dtype);"),
     "rope_table_row": ("cos_sin + positions[t] * rotary_dim", "cos_sin + positions[t] * (rotary_dim / 2)"),
+    "e4m3_bias": ("v = ldexp(1.0 + m / 8.0, e - 7);", "v = ldexp(1.0 + m / 8.0, e - 8);"),
+    "e4m3_subnormal_step": ("v = ldexp((double)m, -9);", "v = ldexp((double)m, -10);"),
+    "e4m3_ties_to_odd": ("(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    "e4m3_saturation_point": ("if (a >= 448.0)", "if (a >= 240.0)"),
+    "fp8_k_scale_dropped": ("(widen(key_cache, kbase + d, kv_dtype) * k_scale)",
+                            "widen(key_cache, kbase + d, kv_dtype)"),
+    "fp8_scatter_multiplies": ("oracle_e4m3_encode(k / k_scale)", "oracle_e4m3_encode(k * k_scale)"),
 }
-PIN_FILES = [os.path.join(ROOT, "tests", "test_oracle.py"), os.path.join(ROOT, "tests", "test_oracle_rope.py")]
+PIN_FILES = [os.path.join(ROOT, "tests", name)
+             for name in ("test_oracle.py", "test_oracle_rope.py", "test_oracle_fp8.py")]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
