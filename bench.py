@@ -11,11 +11,16 @@ Default workload: Llama-3-8B decode layer, batch 64, context lengths uniform
 in [1024, 8192], bf16 (32 query heads, 8 KV heads, head_dim 128, 16-token
 blocks).  Prints one JSON line.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline] [--no-probes]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-cache bf16|fp8]
+                  [--no-cpu-baseline] [--no-probes]
 
 With --workload chunked_prefill_mix a step is the scatter plus one
 pa_chunked_prefill call over 4 prefill chunks and 96 decodes; the chunks are
 also reported against the bf16 matrix peak.
+
+With --kv-cache fp8 the caches hold E4M3 codes: the step is pa_slot_mapping,
+pa_reshape_and_cache_fp8 and pa_decode_fp8, and KV bytes count one byte per
+element.
 """
 from __future__ import annotations
 
@@ -49,6 +54,8 @@ def parse():
                    choices=["llama8b_decode", "llama8b_decode_8k", "long_context", "continuous_batching",
                             "chunked_prefill_mix"])
     p.add_argument("--partition-tokens", type=int, default=0)
+    p.add_argument("--kv-cache", default="bf16", choices=["bf16", "fp8"],
+                   help="fp8: the caches hold E4M3 codes (pa_reshape_and_cache_fp8 / pa_decode_fp8)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probes", action="store_true")
     p.add_argument("--cpu-sample-seqs", type=int, default=16)
@@ -184,11 +191,11 @@ def mfma_probe(pa, torch, iters: int = 10):
     return {"TFLOPs": round(flops / us / 1e6, 1), "us": round(us, 1), "flops": flops, "workgroups": wgs}
 
 
-def cpu_baseline(w, nseq: int):
+def cpu_baseline(w, nseq: int, fp8: bool = False):
     """The oracle, untuned, on the host cores: the first `nseq` sequences of the
     workload (their K/V gathered through block tables into a compact pool built
     before timing), timed over the same step: slots and scatter of their new
-    tokens, then attention."""
+    tokens, then attention (over E4M3 codes when fp8)."""
     import oracle
     import workloads as W
     idx = np.arange(min(nseq, w.num_seqs))
@@ -200,7 +207,8 @@ def cpu_baseline(w, nseq: int):
         table[i, :c] = np.arange(cursor, cursor + c)
         cursor += c
     sub = sub.with_block_table(table, num_blocks=int(cursor))
-    kc, vc = oracle.build_cache(sub, "history")
+    ks, vs = sub.fp8_scales()
+    kc, vc = oracle.build_cache_fp8(sub, ks, vs, "history") if fp8 else oracle.build_cache(sub, "history")
     seq, pos = sub.tokens("new")
     k_new, v_new = (sub.encode(x) for x in sub.token_kv(seq, pos))
     q = sub.encode(sub.queries())
@@ -209,20 +217,24 @@ def cpu_baseline(w, nseq: int):
     for _ in range(3):                               # median of three runs of the step
         t0 = time.perf_counter()
         slots = oracle.slot_mapping(sub.block_table, seq, pos)
-        oracle.reshape_and_cache(k_new, v_new, kc, vc, slots)
+        if fp8:
+            oracle.reshape_and_cache_fp8(k_new, v_new, kc, vc, slots, ks, vs)
+        else:
+            oracle.reshape_and_cache(k_new, v_new, kc, vc, slots)
         oracle.attention(q, kc, vc, sub.block_table, sub.cu_query_lens, sub.seq_lens, sub.num_heads,
-                         sub.scale, sub.causal)
+                         sub.scale, sub.causal, k_scale=ks if fp8 else 1.0, v_scale=vs if fp8 else 1.0)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
+    kvb = sub.kv_bytes(1 if fp8 else None)
     return {
-        "value": round(sub.kv_bytes() / dt / 1e9, 4),
+        "value": round(kvb / dt / 1e9, 4),
         "unit": "GB/s",
         "seq_steps_per_s": round(len(idx) / dt, 3),
         "seconds": round(dt, 3),
         "cores": oracle.max_threads(),
         "kind": "oracle",
         "sample": f"first {len(idx)} of {w.num_seqs} sequences ({int(sub.seq_lens.sum())} KV tokens, "
-                  f"{sub.kv_bytes() / 1e9:.3f} GB of KV), one step (slots + scatter + attention), fp64, median of 3",
+                  f"{kvb / 1e9:.3f} GB of KV), one step (slots + scatter + attention), fp64, median of 3",
     }
 
 
@@ -361,7 +373,11 @@ def main():
     if not w.is_decode:
         return main_mixed(args, w, torch, pa, W, DeviceWorkload)
     t_setup = time.perf_counter()
-    dw = DeviceWorkload(w)
+    fp8 = args.kv_cache == "fp8"
+    if fp8 and args.partition_tokens != 0:
+        print("an fp8 cache is read in the stream mode only (--partition-tokens 0)", file=sys.stderr)
+        sys.exit(2)
+    dw = DeviceWorkload(w, kv_fp8=fp8)
     pt = pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_seq_len, args.partition_tokens)
     ws = dw.decode_workspace(args.partition_tokens)
     out = torch.empty_like(dw.query)
@@ -396,10 +412,10 @@ def main():
     dec_ms = np.array([a.elapsed_time(b) for a, b in events])
     dec_avg_ms = float(dec_ms.mean())
 
-    kv = w.kv_bytes()
+    kv = w.kv_bytes(1 if fp8 else None)
     gbps = kv / (ms_step * 1e-3) / 1e9
     dec_gbps = kv / (dec_avg_ms * 1e-3) / 1e9
-    traffic = recorded_traffic(w.name)
+    traffic = None if fp8 else recorded_traffic(w.name)
     probe = None if args.no_probes else probes(pa, torch)
     res = {
         "metric": METRIC,
@@ -412,7 +428,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "fp8_e4m3 KV, bf16 Q/out" if fp8 else w.dtype,
         "data": "synthetic (seeded N(0,1)*sigma values, random block placement; no dataset)",
         "config": {
             "workload": w.name,
@@ -425,11 +441,14 @@ def main():
             "decode_split": "balanced stream (equal block shares per workgroup)" if pt == 0
                             else f"partitions of {pt} tokens",
             "kv_bytes_per_step": kv,
+            "kv_cache": "fp8 E4M3 (1 byte/element), k_scale = v_scale = %.6g" % w.fp8_scales()[0] if fp8
+                        else w.dtype,
         },
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "roofline": {
-            "kernel": "pa_decode: decode_stream_kernel + merge_stream_kernel (one call)" if pt == 0
+            "kernel": "pa_decode_fp8: decode_stream_kernel<fp8> + merge_stream_kernel (one call)" if fp8
+                      else "pa_decode: decode_stream_kernel + merge_stream_kernel (one call)" if pt == 0
                       else "pa_decode: decode_partition_kernel + merge_partitions_kernel (one call)",
             "bound": "hbm",
             "achieved": round(dec_gbps, 2),
@@ -446,7 +465,7 @@ def main():
         res["roofline"]["frac_of_read_probe"] = round(dec_gbps / probe["stream_read"]["GBps"], 4)
         res["rope_reshape_and_cache"] = rope_scatter_timing(pa, torch)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, fp8)
     print(json.dumps(res), flush=True)
 
 

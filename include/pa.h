@@ -114,6 +114,57 @@ pa_status pa_reshape_and_cache(const void *key, int64_t key_token_stride,
                                pa_dtype dtype, hipStream_t stream);
 
 /*
+ * fp8 KV cache: the scatter.  ("AI Infra入门干货总结：大模型是如何高效推理的" and the
+ * inference field notes gathered with it name quantising the KV cache as the
+ * way to move fewer bytes per decoded token, e4m3 and e5m2 both in use; the
+ * format is its published definition, OCP 8-bit floating point E4M3: bias 7,
+ * 3 mantissa bits, subnormals m * 2^-9, S.1111.111 NaN, largest 448.)
+ *
+ * As pa_reshape_and_cache, but the caches hold one byte per element: element
+ * x of a token's K row is stored as E4M3(x / k_scale), V as E4M3(x / v_scale),
+ * where the division is float32 (correctly rounded), magnitudes beyond 448
+ * saturate to 448, NaN stays NaN, and the code is the nearest one, ties to the
+ * even mantissa.  A stored code c then stands for value(c) * scale.
+ *
+ * key, value      [num_tokens, num_kv_heads, head_dim] in `dtype` (PA_BF16 or
+ *                 PA_F32), token rows *_token_stride ELEMENTS apart, 16-byte
+ *                 aligned.
+ * key_cache, value_cache  uint8 [num_blocks, block_size, num_kv_heads, head_dim].
+ * k_scale, v_scale  finite, > 0: one scale per cache (per layer), chosen by
+ *                 the caller (e.g. the largest |x| expected over 448).
+ * num_kv_heads * head_dim must be a multiple of 16.  Slots < 0 or past the
+ * pool are skipped.  num_tokens = 0 is a no-op.
+ */
+pa_status pa_reshape_and_cache_fp8(const void *key, int64_t key_token_stride,
+                                   const void *value, int64_t value_token_stride,
+                                   void *key_cache, void *value_cache,
+                                   const int64_t *slot_mapping, int64_t num_tokens,
+                                   int64_t num_blocks, int32_t block_size,
+                                   int32_t num_kv_heads, int32_t head_dim,
+                                   pa_dtype dtype, float k_scale, float v_scale,
+                                   hipStream_t stream);
+
+/*
+ * fp8 KV cache: decode attention over caches written by
+ * pa_reshape_and_cache_fp8.  Same operation and arguments as pa_decode with
+ * query and out in bf16, each cached K element standing for value(code) *
+ * k_scale and each V element for value(code) * v_scale.  The codes are widened
+ * to bf16 exactly; k_scale is folded into the softmax scale and v_scale into
+ * the output, so the arithmetic is that of the bf16 path.  It always uses the
+ * balanced stream mode (no partition_tokens): num_seqs must be at most 4096.
+ * Workspace: pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads,
+ * head_dim, max_seq_len, 0) bytes, 16-byte aligned.
+ */
+pa_status pa_decode_fp8(void *out, const void *query, int64_t q_token_stride,
+                        const void *key_cache, const void *value_cache,
+                        const int32_t *block_table, int32_t max_blocks_per_req,
+                        const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                        int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                        int64_t num_blocks, float scale, float k_scale, float v_scale,
+                        int32_t max_seq_len, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
  * The step just before attention, fused into one pass ("AI Infra入门干货总结：
  * 大模型是如何高效推理的", section "Reshape & Cache" and its table, and the RoPE
  * summary near its opening): split each token's fused QKV projection row into

@@ -268,6 +268,27 @@ def build_cache(w, which: str = "all", caches=None):
     return kc, vc
 
 
+def build_cache_fp8(w, k_scale: float, v_scale: float, which: str = "all"):
+    """As build_cache, into E4M3 caches (uint8, every byte the NaN code 0x7F
+    first) through the fp8 scatter."""
+    shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
+    kc, vc = np.full(shape, 0x7F, np.uint8), np.full(shape, 0x7F, np.uint8)
+    seq, pos = w.tokens(which)
+    if len(seq):
+        slots = slot_mapping(w.block_table, seq, pos, w.block_size)
+        k, v = w.token_kv(seq, pos)
+        reshape_and_cache_fp8(w.encode(k), w.encode(v), kc, vc, slots, k_scale, v_scale, w.block_size)
+    return kc, vc
+
+
+def run_fp8(w, k_scale: float, v_scale: float):
+    """Oracle output over an fp8 cache of the workload: [num_q_tokens, Hq, D] fp64."""
+    kc, vc = build_cache_fp8(w, k_scale, v_scale, "all")
+    q = w.encode(w.queries())
+    return attention(q, kc, vc, w.block_table, w.cu_query_lens, w.seq_lens, w.num_heads, w.scale, w.causal,
+                     k_scale=k_scale, v_scale=v_scale)
+
+
 def run(w, return_probs: bool = False):
     """Oracle output for a whole workload: [num_q_tokens, Hq, D] fp64."""
     kc, vc = build_cache(w, "all")
@@ -276,12 +297,13 @@ def run(w, return_probs: bool = False):
                      w.scale, w.causal, return_probs)
 
 
-def run_sequences(w, seqs):
+def run_sequences(w, seqs, fp8_scales=None):
     """Oracle output for a few sequences of a large workload.
 
     The chosen sequences' blocks are relabelled into a compact pool (the result
     does not depend on the physical block ids) so that the oracle never holds
-    the whole pool.  Returns {seq: [query_len, Hq, D] fp64}."""
+    the whole pool.  With fp8_scales = (k_scale, v_scale) the cache is E4M3.
+    Returns {seq: [query_len, Hq, D] fp64}."""
     res = {}
     for b in seqs:
         b = int(b)
@@ -289,7 +311,9 @@ def run_sequences(w, seqs):
         nblk = (L + w.block_size - 1) // w.block_size
         table = np.arange(max(nblk, 1), dtype=np.int32)[None, :]
         shape = (max(nblk, 1), w.block_size, w.num_kv_heads, w.head_dim)
-        if w.dtype == "bf16":
+        if fp8_scales is not None:
+            kc = np.full(shape, 0x7F, np.uint8)
+        elif w.dtype == "bf16":
             kc = np.full(shape, 0x7FC0, np.uint16)
         else:
             kc = np.full(shape, np.nan, np.float32)
@@ -297,9 +321,14 @@ def run_sequences(w, seqs):
         k, v = w.kv(b)
         pos = np.arange(L, dtype=np.int32)
         slots = slot_mapping(table, np.zeros(L, np.int32), pos, w.block_size)
-        reshape_and_cache(w.encode(k), w.encode(v), kc, vc, slots, w.block_size)
+        if fp8_scales is not None:
+            reshape_and_cache_fp8(w.encode(k), w.encode(v), kc, vc, slots, fp8_scales[0], fp8_scales[1],
+                                  w.block_size)
+        else:
+            reshape_and_cache(w.encode(k), w.encode(v), kc, vc, slots, w.block_size)
         q = w.encode(w.query(b))
         cu = np.array([0, q.shape[0]], np.int32)
+        ks, vs = fp8_scales if fp8_scales is not None else (1.0, 1.0)
         res[b] = attention(q, kc, vc, table, cu, np.array([L], np.int32), w.num_heads,
-                           w.scale, w.causal)
+                           w.scale, w.causal, k_scale=ks, v_scale=vs)
     return res

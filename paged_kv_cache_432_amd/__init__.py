@@ -17,7 +17,8 @@ import torch
 
 __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
-    "pa_slot_mapping", "pa_reshape_and_cache", "pa_rope_reshape_and_cache", "pa_decode_workspace_bytes",
+    "pa_slot_mapping", "pa_reshape_and_cache", "pa_rope_reshape_and_cache", "pa_reshape_and_cache_fp8",
+    "pa_decode_fp8", "pa_decode_workspace_bytes",
     "pa_decode_partition_tokens", "pa_decode", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
     "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
 ]
@@ -67,6 +68,13 @@ def lib():
         L.pa_reshape_and_cache.restype = ctypes.c_int
         L.pa_reshape_and_cache.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32,
                                            _i32, _i32, ctypes.c_int, _vp]
+        L.pa_reshape_and_cache_fp8.restype = ctypes.c_int
+        L.pa_reshape_and_cache_fp8.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32,
+                                               _i32, _i32, ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp]
+        L.pa_decode_fp8.restype = ctypes.c_int
+        L.pa_decode_fp8.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                    _i32, _i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, _i32, _vp,
+                                    ctypes.c_size_t, _vp]
         L.pa_rope_reshape_and_cache.restype = ctypes.c_int
         L.pa_rope_reshape_and_cache.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _i64, _i32, _i32, _vp, _vp, _vp,
                                                 _i64, _i64, _i32, _i32, _i32, _i32, ctypes.c_int, _vp]
@@ -179,6 +187,56 @@ def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torc
                                    key_cache.shape[0], key_cache.shape[1], hkv, d, _dtype_code(key),
                                    _stream(stream, key_cache.device))
     _check(s, "pa_reshape_and_cache")
+
+
+def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
+                             value_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float, v_scale: float,
+                             stream=None) -> None:
+    """Scatter key/value [num_tokens, Hkv, D] (bf16 or fp32, token stride free)
+    into uint8 E4M3 caches [num_blocks, 16, Hkv, D] as codes of x / scale."""
+    _need(key.dim() == 3 and value.dim() == 3 and key.shape == value.shape, "key/value: [num_tokens, Hkv, D]")
+    _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
+    _need(key_cache.dtype == value_cache.dtype == torch.uint8, "fp8 caches are uint8 (E4M3 codes)")
+    _need(key.dtype == value.dtype, "key/value dtype mismatch")
+    n, hkv, d = key.shape
+    _need(key_cache.shape[2] == hkv and key_cache.shape[3] == d, "cache head shape differs from key")
+    _need(key.stride(2) == 1 and key.stride(1) == d and value.stride(2) == 1 and value.stride(1) == d,
+          "key/value heads and dims must be contiguous")
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == n and slot_mapping.is_contiguous(),
+          "slot_mapping: contiguous int64 [num_tokens]")
+    s = lib().pa_reshape_and_cache_fp8(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
+                                       _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), n,
+                                       key_cache.shape[0], key_cache.shape[1], hkv, d, _dtype_code(key),
+                                       float(k_scale), float(v_scale), _stream(stream, key_cache.device))
+    _check(s, "pa_reshape_and_cache_fp8")
+
+
+def pa_decode_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
+                  block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float, k_scale: float, v_scale: float,
+                  max_seq_len: int, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention over uint8 E4M3 caches: out [B, Hq, D] bf16 for query
+    [B, Hq, D] bf16; cached codes stand for value * k_scale / v_scale."""
+    _need(query.dim() == 3 and out.shape == query.shape and out.is_contiguous(),
+          "query/out: [num_seqs, num_heads, head_dim], out contiguous")
+    _need(query.stride(2) == 1 and query.stride(1) == query.shape[2], "query heads/dims must be contiguous")
+    _need(query.dtype == out.dtype == torch.bfloat16, "query/out: bfloat16")
+    _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
+    _need(key_cache.dtype == value_cache.dtype == torch.uint8, "fp8 caches are uint8 (E4M3 codes)")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
+          "block_table: contiguous int32 [num_seqs, max_blocks_per_req]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.is_contiguous(), "seq_lens: contiguous int32")
+    b, hq, d = query.shape
+    _need(block_table.shape[0] >= b and seq_lens.numel() >= b, "block_table/seq_lens shorter than batch")
+    nb, bs, hkv, _ = key_cache.shape
+    ws = workspace
+    s = lib().pa_decode_fp8(_ptr(out), _ptr(query), query.stride(0), _ptr(key_cache), _ptr(value_cache),
+                            _ptr(block_table), block_table.shape[1], _ptr(seq_lens), b, hq, hkv, d, bs, nb,
+                            float(scale), float(k_scale), float(v_scale), int(max_seq_len), _ptr(ws),
+                            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream, out.device))
+    _check(s, "pa_decode_fp8")
+    return out
 
 
 def pa_rope_reshape_and_cache(query_out: torch.Tensor, qkv: torch.Tensor, positions: torch.Tensor,

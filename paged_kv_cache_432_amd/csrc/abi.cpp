@@ -256,6 +256,36 @@ pa_status pa_reshape_and_cache(const void* key, int64_t key_token_stride, const 
                       "reshape_and_cache launch");
 }
 
+pa_status pa_reshape_and_cache_fp8(const void* key, int64_t key_token_stride, const void* value,
+                                   int64_t value_token_stride, void* key_cache, void* value_cache,
+                                   const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                                   int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                   float k_scale, float v_scale, hipStream_t stream) {
+    if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "source dtype %d", (int)dtype);
+    if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
+    if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size");
+    if (!(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+        return fail(PA_ERR_INVALID_ARG, "scales must be finite and positive");
+    if (num_tokens == 0) return ok();
+    if (!key || !value || !key_cache || !value_cache || !slot_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer");
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    const int64_t eb = elem_bytes(dtype);
+    if (row_elems % 16 != 0 || row_elems > (1 << 28))
+        return fail(PA_ERR_UNSUPPORTED, "row of %lld elements (must be a multiple of 16)", (long long)row_elems);
+    if (key_token_stride < row_elems || value_token_stride < row_elems)
+        return fail(PA_ERR_INVALID_ARG, "token stride smaller than num_kv_heads * head_dim");
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        (key_token_stride * eb) % 16 || (value_token_stride * eb) % 16)
+        return fail(PA_ERR_INVALID_ARG, "rows must start on 16-byte boundaries");
+    if (num_tokens > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "num_tokens too large");
+    return hip_status(pa::launch_reshape_and_cache_fp8(key, key_token_stride * eb, value, value_token_stride * eb,
+                                                       key_cache, value_cache, slot_mapping, num_tokens,
+                                                       num_blocks * 16, (int32_t)row_elems,
+                                                       dtype == PA_BF16 ? 1 : 0, k_scale, v_scale, stream),
+                      "reshape_and_cache_fp8 launch");
+}
+
 pa_status pa_rope_reshape_and_cache(void* query_out, int64_t q_out_token_stride, const void* qkv,
                                     int64_t qkv_token_stride, const int64_t* positions, const float* cos_sin_cache,
                                     int64_t max_position, int32_t rotary_dim, int32_t neox_style, void* key_cache,
@@ -320,7 +350,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
     if (use_stream(num_seqs, partition_tokens)) {
         const int32_t group = num_heads / num_kv_heads;
         size_t bytes = 0;
-        for (int dtype = 0; dtype < 2; ++dtype) {          // the larger of the two dtypes' layouts
+        for (int dtype = 0; dtype < 3; ++dtype) {          // the largest of the layouts (fp32, bf16, fp8 cache)
             const size_t n = stream_ws_bytes(num_seqs, num_heads, num_kv_heads,
                                              stream_shape(dtype, group, num_kv_heads, num_seqs));
             bytes = n > bytes ? n : bytes;
@@ -341,8 +371,9 @@ pa_status decode_common(void* out, const void* query, int64_t q_token_stride, co
                         const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
                         const int32_t* seq_lens, const int32_t* cu_q, int32_t num_seqs, int32_t num_heads,
                         int32_t num_kv_heads, int64_t num_blocks, float scale, int32_t max_seq_len,
-                        int32_t partition_tokens, void* workspace, size_t workspace_bytes, pa_dtype dtype,
-                        hipStream_t stream) {
+                        int32_t partition_tokens, void* workspace, size_t workspace_bytes, int dt, float k_scale,
+                        float v_scale, hipStream_t stream) {
+    // dt: 0 fp32, 1 bf16, 2 fp8 cache (bf16 query and output, stream mode only)
     const int32_t group = num_heads / num_kv_heads;
     pa::DecodeArgs a{};
     a.out = out;
@@ -357,9 +388,9 @@ pa_status decode_common(void* out, const void* query, int64_t q_token_stride, co
     a.num_seqs = num_seqs;
     a.num_heads = num_heads;
     a.num_kv_heads = num_kv_heads;
-    a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+    a.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634);
+    a.out_scale = v_scale;
     a.cu_q = cu_q;
-    const int dt = dtype == PA_BF16 ? 1 : 0;
 
     size_t need = 0;
     if (use_stream(num_seqs, partition_tokens)) {
@@ -410,6 +441,38 @@ pa_status check_heads(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
 
 extern "C" {
 
+pa_status pa_decode_fp8(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+                        const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, float k_scale,
+                        float v_scale, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    const pa_status hs = check_heads(num_heads, num_kv_heads, head_dim, block_size);
+    if (hs != PA_OK) return hs;
+    if (num_seqs < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_req < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative size");
+    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if (!(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+        return fail(PA_ERR_INVALID_ARG, "scales must be finite and positive");
+    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
+        return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
+    if (num_seqs == 0) return ok();
+    if (!use_stream(num_seqs, 0))
+        return fail(PA_ERR_UNSUPPORTED, "%d sequences: an fp8 cache is read in the stream mode, at most %d",
+                    num_seqs, kStreamMaxSeqs);
+    if (num_blocks == 0 && max_seq_len > 0) return fail(PA_ERR_INVALID_ARG, "empty cache pool");
+    if (!out || !query || !seq_lens || !key_cache || !value_cache || (max_seq_len > 0 && !block_table))
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (q_token_stride < (int64_t)num_heads * head_dim)
+        return fail(PA_ERR_INVALID_ARG, "q_token_stride smaller than num_heads * head_dim");
+    if (!aligned16(query) || (q_token_stride * 2) % 16 || !aligned16(out) || !aligned16(key_cache) ||
+        !aligned16(value_cache))
+        return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
+    return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
+                         seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len, 0,
+                         workspace, workspace_bytes, 2, k_scale, v_scale, stream);
+}
+
 pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
                     const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
                     const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
@@ -439,7 +502,7 @@ pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const 
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
     return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
                          seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len,
-                         partition_tokens, workspace, workspace_bytes, dtype, stream);
+                         partition_tokens, workspace, workspace_bytes, dtype == PA_BF16 ? 1 : 0, 1.f, 1.f, stream);
 }
 
 size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,
@@ -503,7 +566,8 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
     // single-row sequences: the decode kernel, reading its rows through cu_query_lens
     pa_status st = decode_common(out, query, q_token_stride, key_cache, value_cache, block_table,
                                  max_blocks_per_req, seq_lens, cu_query_lens, num_seqs, num_heads, num_kv_heads,
-                                 num_blocks, scale, max_seq_len, 0, workspace, dec_bytes, dtype, stream);
+                                 num_blocks, scale, max_seq_len, 0, workspace, dec_bytes, dtype == PA_BF16 ? 1 : 0,
+                                 1.f, 1.f, stream);
     if (st != PA_OK) return st;
     if (max_query_len < 2) return ok();
 

@@ -52,6 +52,71 @@ reshape_and_cache_kernel(const char* __restrict__ key, int64_t key_stride_bytes,
     }
 }
 
+// ---- fp8 (E4M3) scatter ------------------------------------------------------
+// As reshape_and_cache_kernel, but each element x of a K (V) row is stored as
+// the OCP E4M3 code of x / k_scale (v_scale): the division in float32
+// (correctly rounded), magnitudes beyond 448 saturated to 448, NaN kept, then
+// the hardware conversion to the nearest code, ties to even.  One workgroup
+// per token: threads 0-127 take the K row, 128-255 the V row, 16 elements
+// (16 output bytes) per step.
+template <typename Chunk>
+__global__ void __launch_bounds__(256)
+reshape_and_cache_fp8_kernel(const char* __restrict__ key, int64_t key_stride_bytes,
+                             const char* __restrict__ value, int64_t value_stride_bytes,
+                             uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache,
+                             const int64_t* __restrict__ slot_mapping, int64_t num_slots, int32_t row_elems,
+                             float k_scale, float v_scale) {
+    const int64_t token = blockIdx.x;
+    const int64_t slot = slot_mapping[token];
+    if (slot < 0 || slot >= num_slots) return;
+    const bool is_v = threadIdx.x >= 128;
+    const char* src = is_v ? value + token * value_stride_bytes : key + token * key_stride_bytes;
+    uint8_t* dst = (is_v ? value_cache : key_cache) + slot * (int64_t)row_elems;
+    const float scale = is_v ? v_scale : k_scale;
+    for (int32_t c = threadIdx.x & 127; c < row_elems / 16; c += 128) {
+        Chunk x0, x1;
+        load_chunk<false>(x0, src + (int64_t)c * 16 * Chunk::kBytes / 8);
+        load_chunk<false>(x1, src + ((int64_t)c * 16 + 8) * Chunk::kBytes / 8);
+        float f[16];
+        to_f32(x0, f);
+        to_f32(x1, f + 8);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float y = f[e] / scale;
+            f[e] = __builtin_fabsf(y) > 448.f ? __builtin_copysignf(448.f, y) : y;
+        }
+        u32x4_t w;
+        int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+        p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], p0, true);
+        int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+        p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], p1, true);
+        int p2 = __builtin_amdgcn_cvt_pk_fp8_f32(f[8], f[9], 0, false);
+        p2 = __builtin_amdgcn_cvt_pk_fp8_f32(f[10], f[11], p2, true);
+        int p3 = __builtin_amdgcn_cvt_pk_fp8_f32(f[12], f[13], 0, false);
+        p3 = __builtin_amdgcn_cvt_pk_fp8_f32(f[14], f[15], p3, true);
+        w.x = (uint32_t)p0; w.y = (uint32_t)p1; w.z = (uint32_t)p2; w.w = (uint32_t)p3;
+        *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = w;
+    }
+}
+
+hipError_t launch_reshape_and_cache_fp8(const void* key, int64_t key_stride_bytes, const void* value,
+                                        int64_t value_stride_bytes, void* key_cache, void* value_cache,
+                                        const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,
+                                        int32_t row_elems, int dtype, float k_scale, float v_scale,
+                                        hipStream_t stream) {
+    if (dtype == 1)
+        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<ChunkBF16>, dim3((unsigned)num_tokens), dim3(256), 0,
+                           stream, (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
+                           (uint8_t*)key_cache, (uint8_t*)value_cache, slot_mapping, num_slots, row_elems,
+                           k_scale, v_scale);
+    else
+        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<ChunkF32>, dim3((unsigned)num_tokens), dim3(256), 0,
+                           stream, (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
+                           (uint8_t*)key_cache, (uint8_t*)value_cache, slot_mapping, num_slots, row_elems,
+                           k_scale, v_scale);
+    return hipGetLastError();
+}
+
 // ---- RoPE + QKV split + scatter ---------------------------------------------
 // The step just before attention ("AI Infra入门干货总结：大模型是如何高效推理的",
 // section "Reshape & Cache" and its table; the RoPE summary near the article's

@@ -376,6 +376,12 @@ constexpr bool kMfmaWave = sizeof(Elem) == 2 && G >= PA_DECODE_MFMA_FROM;
 #define PA_DECODE_MFMA_DEPTH 3
 #endif
 constexpr int kMfmaDepth = PA_DECODE_MFMA_DEPTH;
+// Blocks in flight per wave over an fp8 cache: each holds half the bytes of a
+// bf16 block, so twice as many keep the same bytes in flight.
+#ifndef PA_DECODE_FP8_DEPTH
+#define PA_DECODE_FP8_DEPTH 6
+#endif
+constexpr int kFp8Depth = PA_DECODE_FP8_DEPTH;
 
 struct MfmaState {
     u32x4_t q[4];                  // B operand of S^T for product step ks: dims 32ks + 8g .. +8 (zero past G)
@@ -514,13 +520,16 @@ __device__ __forceinline__ void attend_mfma(const DecodeArgs& a, int kvh, const 
 
 // Finish a range of the matrix-core wave: as finish(), lanes of head i < G
 // writing dims 32g + 8r .. +8 from acc[0..7][r].
-template <int G>
-__device__ __forceinline__ void finish_mfma(const MfmaState& st, int lane, uint16_t* out, float* rec) {
+// SC: every output and partial accumulator is multiplied by oscale (the V
+// scale of an fp8 cache).
+template <int G, bool SC = false>
+__device__ __forceinline__ void finish_mfma(const MfmaState& st, int lane, uint16_t* out, float* rec,
+                                            float oscale = 1.f) {
     const int i = lane & 15, g = lane >> 4;
     const float l = sum_across_rows(st.l);
     if (i >= G) return;
     if (out) {
-        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float inv = (l > 0.f ? 1.f / l : 0.f) * (SC ? oscale : 1.f);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float f[8];
@@ -533,7 +542,7 @@ __device__ __forceinline__ void finish_mfma(const MfmaState& st, int lane, uint1
         for (int r = 0; r < 4; ++r) {
             float f[8];
 #pragma unroll
-            for (int dt = 0; dt < 8; ++dt) f[dt] = st.acc[dt][r];
+            for (int dt = 0; dt < 8; ++dt) f[dt] = SC ? st.acc[dt][r] * oscale : st.acc[dt][r];
             store_chunk(rec + i * kRec + 32 * g + 8 * r, f);
         }
         if (g == 0) *reinterpret_cast<float2*>(rec + i * kRec + kHeadDim) = make_float2(st.m, l);
@@ -570,17 +579,37 @@ __device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int64_t b) {
 constexpr int kShareTable = 1024;
 constexpr int kFirstBlock = 1 << 30;                  // table flag: block 0 of its sequence
 
-template <int G, bool NT, int NBUF>
+// One block's K and V rows of one KV head as a lane holds them in flight.
+// bf16: K dims 32ks + 8g .. +8 of token i for product step ks; V dims 8i .. +8
+// of tokens 4g .. 4g+3.  fp8 (one byte per element): K bytes 32g .. 32g+31 of
+// token i (dims 32g + 8ks .. +8 feed step ks: the query is loaded in the same
+// dim order, so the product is unchanged); V as bf16, 8 bytes per token.
+template <bool F8> struct KvBuf;
+template <> struct KvBuf<false> { u32x4_t k[4], v[4]; };
+template <> struct KvBuf<true> { u32x4_t k[2]; u32x2_t v[4]; };
+
+// Eight fp8 (E4M3) values in two words -> eight bf16, exactly (every E4M3
+// value is a bf16 value), byte e -> element e.
+__device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+    return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+}
+
+template <int G, bool NT, int NBUF, bool F8 = false>
 __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int32_t* s_pref, int4* s_tab, int64_t u0,
                                                   int64_t u1, int W, int NG, int wi, int lane) {
     const int total = (int)(u1 - u0);                  // the same for every wave of the workgroup
     if (total <= 0) return;
     const int B = a.num_seqs;
-    const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * 2;
+    constexpr int kEb = F8 ? 1 : 2;                    // cache bytes per element
+    const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * kEb;
     const uint32_t blk_bytes = tok_bytes * kBlock;
     const int i = lane & 15, g = lane >> 4;
-    const uint32_t koff = i * tok_bytes + g * 16;       // the KV head's 256 bytes go in the base
-    const uint32_t voff = 4 * g * tok_bytes + i * 16;
+    // the KV head's row start goes in the base
+    const uint32_t koff = i * tok_bytes + g * (F8 ? 32 : 16);
+    const uint32_t voff = 4 * g * tok_bytes + i * (F8 ? 8 : 16);
     const char* kc = reinterpret_cast<const char*>(a.key_cache);
     const char* vc = reinterpret_cast<const char*>(a.value_cache);
 
@@ -594,24 +623,35 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
         grp = vg >> 8;
     };
 
-    auto issue = [&](u32x4_t (&kb)[4], u32x4_t (&vb)[4], int j) {
+    auto issue = [&](KvBuf<F8>& buf, int j) {
         int id = 0, valid = 0, grp = 0;
         if (j < c1) entry(j, id, valid, grp);
         const int64_t phys = min(max((int64_t)id, (int64_t)0), a.num_blocks - 1);   // an id outside the pool: clamped
         // the resource spans the block's valid rows: past-the-end slots and
         // blocks past the table read as zeros without touching memory
         const int nrec = valid * (int)tok_bytes;
-        const int64_t off = phys * (int64_t)blk_bytes + (int64_t)(grp * W + wi) * kHeadDim * 2;
+        const int64_t off = phys * (int64_t)blk_bytes + (int64_t)(grp * W + wi) * kHeadDim * kEb;
         const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
         const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
+        if constexpr (F8) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            kb[ks] = __builtin_bit_cast(u32x4_t,
-                                        __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(koff + 64 * ks), 0, NT ? 2 : 0));
+            for (int h = 0; h < 2; ++h)
+                buf.k[h] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(koff + 16 * h), 0, NT ? 2 : 0));
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-            vb[r] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(voff + r * tok_bytes), 0,
-                                                                                         NT ? 2 : 0));
+            for (int r = 0; r < 4; ++r)
+                buf.v[r] = __builtin_bit_cast(
+                    u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(rv, (int)(voff + r * tok_bytes), 0, NT ? 2 : 0));
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                buf.k[ks] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)(koff + 64 * ks), 0, NT ? 2 : 0));
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                buf.v[r] = __builtin_bit_cast(
+                    u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rv, (int)(voff + r * tok_bytes), 0, NT ? 2 : 0));
+        }
     };
 
     // the current segment, and the query of the segment starting at block qn_at
@@ -635,11 +675,12 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
         int kvh, rem;
         bool first;
         segment_at(j, row, kvh, rem, first);
+        // dims of step ks: 32ks + 8g .. +8 (bf16 cache), 32g + 8ks .. +8 (fp8)
         const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) + row * a.q_stride +
-                             (int64_t)(kvh * G + (i < G ? i : 0)) * kHeadDim + 8 * g;
+                             (int64_t)(kvh * G + (i < G ? i : 0)) * kHeadDim + (F8 ? 32 : 8) * g;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            q[ks] = i < G ? *reinterpret_cast<const u32x4_t*>(qp + 32 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+            q[ks] = i < G ? *reinterpret_cast<const u32x4_t*>(qp + (F8 ? 8 : 32) * ks) : u32x4_t{0u, 0u, 0u, 0u};
     };
     auto prefetch_query = [&]() {                      // the next segment's query, if it is in the table
         if (seg_end < c1) {
@@ -649,7 +690,7 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
     };
     auto finish_segment = [&]() {
         float* rec = a.part + ((((int64_t)blockIdx.x * 2 + (seg_first ? 0 : 1)) * W + wi) * G) * kRec;
-        finish_mfma<G>(st, lane, seg_whole ? seg_out : nullptr, seg_whole ? nullptr : rec);
+        finish_mfma<G, F8>(st, lane, seg_whole ? seg_out : nullptr, seg_whole ? nullptr : rec, a.out_scale);
     };
     auto start_segment = [&](int j) {                  // block j begins a segment
         int64_t row;
@@ -677,7 +718,7 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
         prefetch_query();
     };
 
-    auto process = [&](const u32x4_t (&kb)[4], const u32x4_t (&vb)[4], int j) {
+    auto process = [&](const KvBuf<F8>& buf, int j) {
         if (j == seg_end) {                            // wave-uniform
             if (j > 0) finish_segment();
             start_segment(j);
@@ -685,6 +726,26 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
         int id, valid, grp;
         entry(j, id, valid, grp);
         const int nval = valid - 4 * g;                // this lane's tokens 4g .. 4g+3 of the block
+        u32x4_t kb[4], vb[4];
+        if constexpr (F8) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const u32x4_t w = buf.k[h];
+                kb[2 * h] = fp8x8_to_bf16(w.x, w.y);
+                kb[2 * h + 1] = fp8x8_to_bf16(w.z, w.w);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const u32x2_t w = buf.v[r];
+                vb[r] = fp8x8_to_bf16(w.x, w.y);
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                kb[k] = buf.k[k];
+                vb[k] = buf.v[k];
+            }
+        }
         f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -716,17 +777,17 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
         }
         __syncthreads();
         if (c0 > 0 && qn_at < 0) prefetch_query();    // the segment running on ends in this table
-        u32x4_t kbuf[NBUF][4], vbuf[NBUF][4];
+        KvBuf<F8> buf[NBUF];
 #pragma unroll
         for (int b = 0; b < NBUF; ++b) {
-            issue(kbuf[b], vbuf[b], c0 + b);
+            issue(buf[b], c0 + b);
             __builtin_amdgcn_sched_barrier(0);
         }
         for (int j = c0; j < c1; j += NBUF) {
 #pragma unroll
             for (int b = 0; b < NBUF; ++b) {
-                if (b == 0 || j + b < c1) process(kbuf[b], vbuf[b], j + b);
-                issue(kbuf[b], vbuf[b], j + b + NBUF);
+                if (b == 0 || j + b < c1) process(buf[b], j + b);
+                issue(buf[b], j + b + NBUF);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
@@ -826,7 +887,8 @@ __device__ __forceinline__ int64_t stream_quantum(const DecodeArgs& a, int64_t u
     return q > a.min_quantum ? q : (int64_t)a.min_quantum;
 }
 
-template <typename Chunk, typename Elem, int G, bool QL, bool NT>
+// F8: the caches hold fp8 (E4M3) codes; query and output stay bf16.
+template <typename Chunk, typename Elem, int G, bool QL, bool NT, bool F8 = false>
 __global__ void __launch_bounds__(512)
 decode_stream_kernel(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) int32_t s_pref[];          // [num_seqs + 1]
@@ -849,7 +911,7 @@ decode_stream_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63;
     float* pl = p_lds[MF ? 0 : wi];
     if constexpr (MF) {
-        stream_share_mfma<G, NT, kMfmaDepth>(a, s_pref, s_tab, u0, u1, W, NG, wi, lane);
+        stream_share_mfma<G, NT, F8 ? kFp8Depth : kMfmaDepth, F8>(a, s_pref, s_tab, u0, u1, W, NG, wi, lane);
         return;
     }
 
@@ -1026,12 +1088,12 @@ merge_stream_kernel(DecodeArgs a) {
 
 
 
-template <typename Chunk, typename Elem, int G>
+template <typename Chunk, typename Elem, int G, bool F8 = false>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     constexpr bool QL = kQueryInLds<G>;
     if (a.mode == kDecodeStream) {
         const size_t lds = sizeof(int32_t) * ((size_t)a.num_seqs + 1);
-        hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, true>), dim3((unsigned)a.num_wg),
+        hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, true, F8>), dim3((unsigned)a.num_wg),
                            dim3(64 * a.waves_per_group), lds, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1041,6 +1103,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
                            stream, a);
         return hipGetLastError();
     }
+    if constexpr (F8) return hipErrorInvalidValue;       // an fp8 cache is read in the stream mode only
     const int64_t items = (int64_t)a.num_seqs * a.max_partitions * a.num_kv_heads;
     const int64_t grid = (items + kWavesPerGroup - 1) / kWavesPerGroup;
     hipLaunchKernelGGL((decode_partition_kernel<Chunk, Elem, G, QL, true>), dim3((unsigned)grid), dim3(256), 0,
@@ -1053,46 +1116,49 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename Chunk, typename Elem>
+template <typename Chunk, typename Elem, bool F8 = false>
 hipError_t launch_group(const DecodeArgs& a, int group, hipStream_t stream) {
     switch (group) {
-        case 1: return launch_typed<Chunk, Elem, 1>(a, stream);
-        case 2: return launch_typed<Chunk, Elem, 2>(a, stream);
-        case 4: return launch_typed<Chunk, Elem, 4>(a, stream);
-        case 8: return launch_typed<Chunk, Elem, 8>(a, stream);
+        case 1: return launch_typed<Chunk, Elem, 1, F8>(a, stream);
+        case 2: return launch_typed<Chunk, Elem, 2, F8>(a, stream);
+        case 4: return launch_typed<Chunk, Elem, 4, F8>(a, stream);
+        case 8: return launch_typed<Chunk, Elem, 8, F8>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename Chunk, typename Elem, int G>
+template <typename Chunk, typename Elem, int G, bool F8>
 int stream_blocks_per_cu(int waves_per_group, size_t lds) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, true>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, true, F8>,
                                                      64 * waves_per_group, lds) != hipSuccess)
         return 0;
     return n;
 }
 
-template <typename Chunk, typename Elem>
+template <typename Chunk, typename Elem, bool F8 = false>
 int stream_blocks_group(int group, int waves_per_group, size_t lds) {
     switch (group) {
-        case 1: return stream_blocks_per_cu<Chunk, Elem, 1>(waves_per_group, lds);
-        case 2: return stream_blocks_per_cu<Chunk, Elem, 2>(waves_per_group, lds);
-        case 4: return stream_blocks_per_cu<Chunk, Elem, 4>(waves_per_group, lds);
-        case 8: return stream_blocks_per_cu<Chunk, Elem, 8>(waves_per_group, lds);
+        case 1: return stream_blocks_per_cu<Chunk, Elem, 1, F8>(waves_per_group, lds);
+        case 2: return stream_blocks_per_cu<Chunk, Elem, 2, F8>(waves_per_group, lds);
+        case 4: return stream_blocks_per_cu<Chunk, Elem, 4, F8>(waves_per_group, lds);
+        case 8: return stream_blocks_per_cu<Chunk, Elem, 8, F8>(waves_per_group, lds);
         default: return 0;
     }
 }
 
 }  // namespace
 
+// dtype: 0 fp32, 1 bf16, 2 fp8 (E4M3) cache with bf16 query and output.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t stream) {
+    if (dtype == 2) return launch_group<ChunkBF16, uint16_t, true>(a, group, stream);
     if (dtype == 1) return launch_group<ChunkBF16, uint16_t>(a, group, stream);
     return launch_group<ChunkF32, float>(a, group, stream);
 }
 
 int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int num_seqs) {
     const size_t lds = sizeof(int32_t) * ((size_t)num_seqs + 1);
+    if (dtype == 2) return stream_blocks_group<ChunkBF16, uint16_t, true>(group, waves_per_group, lds);
     if (dtype == 1) return stream_blocks_group<ChunkBF16, uint16_t>(group, waves_per_group, lds);
     return stream_blocks_group<ChunkF32, float>(group, waves_per_group, lds);
 }

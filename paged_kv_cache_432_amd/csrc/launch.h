@@ -13,6 +13,14 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
                                const int32_t* token_seq, const int32_t* token_pos,
                                int64_t num_tokens, hipStream_t stream);
 
+// fp8 (E4M3) scatter: K/V rows of `dtype` (0 fp32, 1 bf16) divided by their
+// scale, stored one byte per element.
+hipError_t launch_reshape_and_cache_fp8(const void* key, int64_t key_stride_bytes, const void* value,
+                                        int64_t value_stride_bytes, void* key_cache, void* value_cache,
+                                        const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,
+                                        int32_t row_elems, int dtype, float k_scale, float v_scale,
+                                        hipStream_t stream);
+
 // RoPE + QKV split + scatter (rope_cache_kernel); sizes in elements.
 struct RopeArgs {
     void* query_out;            // [num_tokens, num_heads, 128], rows q_out_stride apart
@@ -60,7 +68,8 @@ struct DecodeArgs {
     int32_t num_seqs;
     int32_t num_heads;
     int32_t num_kv_heads;
-    float scale_log2;              // softmax scale * log2(e): exponentials are taken base 2
+    float scale_log2;              // softmax scale (times the K scale of an fp8 cache) * log2(e): base-2 exponentials
+    float out_scale;               // fp8 cache: the V scale, multiplying outputs and partial accumulators
     int32_t mode;                  // kDecodePartitions or kDecodeStream
     // partitions
     int32_t partition_tokens;      // tokens per split (multiple of 16), >= max_seq_len if unsplit

@@ -13,8 +13,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (chunked_prefill_workspace, decode_workspace, pa_chunked_prefill, pa_decode,
-               pa_reshape_and_cache, pa_slot_mapping)
+from . import (chunked_prefill_workspace, decode_workspace, pa_chunked_prefill, pa_decode, pa_decode_fp8,
+               pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping)
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -27,14 +27,24 @@ def _upload(x: np.ndarray, dtype, device) -> torch.Tensor:
 class DeviceWorkload:
     """Device-resident inputs and paged cache of one workload step."""
 
-    def __init__(self, w, device="cuda", fill_history: bool = True, poison: bool = True):
+    def __init__(self, w, device="cuda", fill_history: bool = True, poison: bool = True, kv_fp8: bool = False):
+        """kv_fp8: the caches hold E4M3 codes (uint8) written by the fp8 scatter
+        with the workload's fp8_scales(); queries and outputs stay bf16."""
         self.w = w
         self.device = torch.device(device)
         self.dtype = _TORCH_DTYPE[w.dtype]
+        self.kv_fp8 = kv_fp8
+        if kv_fp8:
+            assert w.dtype == "bf16", "an fp8 cache goes with bf16 queries"
+            self.k_scale, self.v_scale = w.fp8_scales()
         shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
-        fill = float("nan") if poison else 0.0
-        self.key_cache = torch.full(shape, fill, dtype=self.dtype, device=self.device)
-        self.value_cache = torch.full(shape, fill, dtype=self.dtype, device=self.device)
+        if kv_fp8:
+            self.key_cache = torch.full(shape, 0x7F if poison else 0, dtype=torch.uint8, device=self.device)
+            self.value_cache = torch.full(shape, 0x7F if poison else 0, dtype=torch.uint8, device=self.device)
+        else:
+            fill = float("nan") if poison else 0.0
+            self.key_cache = torch.full(shape, fill, dtype=self.dtype, device=self.device)
+            self.value_cache = torch.full(shape, fill, dtype=self.dtype, device=self.device)
         self.block_table = torch.from_numpy(np.ascontiguousarray(w.block_table, np.int32)).to(self.device)
         self.seq_lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens, np.int32)).to(self.device)
         self.cu_query_lens = torch.from_numpy(w.cu_query_lens).to(self.device)
@@ -68,15 +78,20 @@ class DeviceWorkload:
         pos = torch.arange(start, start + n, dtype=torch.int32, device=self.device)
         slots = torch.empty(n, dtype=torch.int64, device=self.device)
         pa_slot_mapping(slots, self.block_table, seq, pos)
-        pa_reshape_and_cache(_upload(k, self.dtype, self.device), _upload(v, self.dtype, self.device),
-                             self.key_cache, self.value_cache, slots)
+        self._scatter(_upload(k, self.dtype, self.device), _upload(v, self.dtype, self.device), slots)
+
+    def _scatter(self, k, v, slots, stream=None) -> None:
+        if self.kv_fp8:
+            pa_reshape_and_cache_fp8(k, v, self.key_cache, self.value_cache, slots, self.k_scale, self.v_scale,
+                                     stream=stream)
+        else:
+            pa_reshape_and_cache(k, v, self.key_cache, self.value_cache, slots, stream=stream)
 
     # ---- the step
     def scatter_new(self, stream=None) -> None:
         """Rows a1-a2 of the step: slots of this step's tokens, then their scatter."""
         pa_slot_mapping(self.slot_mapping, self.block_table, self.new_seq, self.new_pos, stream=stream)
-        pa_reshape_and_cache(self.new_k, self.new_v, self.key_cache, self.value_cache,
-                             self.slot_mapping, stream=stream)
+        self._scatter(self.new_k, self.new_v, self.slot_mapping, stream=stream)
 
     def decode_workspace(self, partition_tokens: int = 0):
         w = self.w
@@ -89,6 +104,11 @@ class DeviceWorkload:
             out = torch.empty_like(self.query)
         if workspace is None:
             workspace = self.decode_workspace(partition_tokens)
+        if self.kv_fp8:
+            assert partition_tokens == 0, "an fp8 cache is read in the stream mode only"
+            return pa_decode_fp8(out, self.query, self.key_cache, self.value_cache, self.block_table,
+                                 self.seq_lens, w.scale, self.k_scale, self.v_scale, w.max_seq_len, workspace,
+                                 stream)
         return pa_decode(out, self.query, self.key_cache, self.value_cache, self.block_table,
                          self.seq_lens, w.scale, w.max_seq_len, partition_tokens, workspace, stream)
 

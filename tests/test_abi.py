@@ -174,3 +174,30 @@ def test_rope_rejects_before_launch(L, kw, status):
 
 def test_rope_empty_is_ok(L):
     assert _rope(L, num_tokens=0) == pa.PA_OK
+
+
+def test_fp8_entries_reject_before_launch(L):
+    """fp8 scatter and decode argument checks; none of these launches."""
+    sc = L.pa_reshape_and_cache_fp8
+    assert sc(16, 1024, 16, 1024, 16, 16, 16, 0, 10, 16, 8, 128, 1, 1.0, 1.0, None) == pa.PA_OK
+    assert sc(16, 1024, 16, 1024, 16, 16, 16, 5, 10, 16, 8, 128, 1, 0.0, 1.0, None) == pa.PA_ERR_INVALID_ARG
+    assert sc(16, 1024, 16, 1024, 16, 16, 16, 5, 10, 16, 8, 128, 1, 1.0, float("inf"), None) == pa.PA_ERR_INVALID_ARG
+    assert sc(16, 1024, 16, 1024, 16, 16, 16, 5, 10, 16, 8, 128, 3, 1.0, 1.0, None) == pa.PA_ERR_UNSUPPORTED
+    assert sc(16, 1000, 16, 1024, 16, 16, 16, 5, 10, 16, 8, 128, 1, 1.0, 1.0, None) == pa.PA_ERR_INVALID_ARG
+    assert sc(16, 1024, 16, 1024, 16, 16, 16, 5, 10, 32, 8, 128, 1, 1.0, 1.0, None) == pa.PA_ERR_UNSUPPORTED
+    dc = L.pa_decode_fp8
+
+    def dec(**kw):
+        a = dict(out=16, q=16, qs=4096, kc=16, vc=16, bt=16, mbr=512, sl=16, b=4, hq=32, hkv=8, d=128, bs=16,
+                 nb=100, scale=0.088, ks=1.0, vs=1.0, msl=8192)
+        a.update(kw)
+        return dc(a["out"], a["q"], a["qs"], a["kc"], a["vc"], a["bt"], a["mbr"], a["sl"], a["b"], a["hq"], a["hkv"],
+                  a["d"], a["bs"], a["nb"], a["scale"], a["ks"], a["vs"], a["msl"], None, 0, None)
+
+    assert dec(b=0) == pa.PA_OK
+    assert dec(ks=-1.0) == pa.PA_ERR_INVALID_ARG
+    assert dec(vs=float("nan")) == pa.PA_ERR_INVALID_ARG
+    assert dec(b=5000) == pa.PA_ERR_UNSUPPORTED              # past the stream mode's sequence limit
+    assert dec(d=64) == pa.PA_ERR_UNSUPPORTED
+    assert dec(qs=4000) == pa.PA_ERR_INVALID_ARG
+    assert dec(msl=8193) == pa.PA_ERR_INVALID_ARG

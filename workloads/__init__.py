@@ -119,10 +119,18 @@ class Workload:
     def is_decode(self) -> bool:
         return bool(np.all(self.query_lens == 1))
 
-    def kv_bytes(self) -> int:
+    def fp8_scales(self):
+        """(k_scale, v_scale) for an fp8 (E4M3) cache of this workload: sigma / 64,
+        so that values up to 7 sigma are representable (E4M3 reaches 448) and
+        values near sigma sit in the normal range."""
+        s = float(np.float32(self.sigma) / np.float32(64))
+        return s, s
+
+    def kv_bytes(self, elem_bytes: int | None = None) -> int:
         """Algorithmic KV bytes one attention call reads: each attended token's
         K and V row for every KV head, counted once (grouped query heads share it)."""
-        return int(self.seq_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * self.elem_bytes
+        eb = self.elem_bytes if elem_bytes is None else elem_bytes
+        return int(self.seq_lens.astype(np.int64).sum()) * 2 * self.num_kv_heads * self.head_dim * eb
 
     # ---- values
     def _round(self, x: np.ndarray) -> np.ndarray:
