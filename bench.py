@@ -173,6 +173,52 @@ def rope_scatter_timing(pa, torch, token_counts=(64, 256, 2144, 16384), iters: i
             "bytes_per_token": per_token, "calls": rows}
 
 
+def copy_blocks_timing(pa, torch, pair_counts=(1, 64, 1024), layers: int = 32, iters: int = 20, batch: int = 10):
+    """Copy-on-write (pa_copy_blocks) over a Llama-3-8B cache of all 32 layers
+    ([32, 2, 4096 blocks, 16, 8, 128] bf16, 8 GiB): each pair copies one
+    32 KiB block of K and one of V in every layer.  Algorithmic bytes per pair:
+    layers * 2 * 32 KiB read + as many written.  Timed as a graph of `batch`
+    calls back to back."""
+    nb, blk = 4096, 16 * 8 * 128
+    kv = torch.zeros(layers, 2, nb, blk, dtype=torch.bfloat16, device="cuda")
+    g = torch.Generator(device="cpu").manual_seed(5)
+    rows = []
+    for n in pair_counts:
+        perm = torch.randperm(nb, generator=g)
+        pairs = torch.stack([perm[:n], perm[n:2 * n]], 1).contiguous().to("cuda")
+
+        def call():
+            pa.pa_copy_blocks(kv, pairs)
+
+        call()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for _ in range(batch):
+                    call()
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+        for a, b in ev:
+            a.record()
+            graph.replay()
+            b.record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3 / batch
+        moved = n * layers * 2 * blk * 2 * 2
+        rows.append({"pairs": n, "us": round(us, 2), "GBps": round(moved / us / 1e3, 1),
+                     "pct_hbm_peak": round(100.0 * moved / us / 1e3 / HBM_PEAK_GBPS, 2), "bytes": moved})
+        del graph
+    del kv
+    torch.cuda.empty_cache()
+    return {"kernel": "copy_blocks_kernel (pa_copy_blocks)", "shapes": "Llama-3-8B, 32 layers, bf16",
+            "calls": rows}
+
+
 def mfma_probe(pa, torch, iters: int = 10):
     """The library's matrix-core probe (4 independent v_mfma_f32_32x32x16_bf16
     chains per wave, two 4-wave workgroups per compute unit): the matrix rate
@@ -464,6 +510,7 @@ def main():
         res["probes"] = probe
         res["roofline"]["frac_of_read_probe"] = round(dec_gbps / probe["stream_read"]["GBps"], 4)
         res["rope_reshape_and_cache"] = rope_scatter_timing(pa, torch)
+        res["copy_blocks"] = copy_blocks_timing(pa, torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, fp8)
     print(json.dumps(res), flush=True)

@@ -114,6 +114,30 @@ pa_status pa_reshape_and_cache(const void *key, int64_t key_token_stride,
                                pa_dtype dtype, hipStream_t stream);
 
 /*
+ * Copy-on-write of shared blocks.  Sequences that share a prefix point their
+ * block tables at the same physical blocks (prefix caching); before one of
+ * them writes into a shared block, the caller gives it a fresh block and this
+ * call copies the contents ("AI Infra入门干货总结：大模型是如何高效推理的", section
+ * "Paged Attention": the [num_layers, 2, num_blocks, block_size, num_kv_heads,
+ * head_dim] cache; the inference field notes' chapter on batching and memory
+ * management names copy-on-write and prefix caching).
+ *
+ * For each pair p of block_mapping (int64 [num_pairs][2] = (src, dst), device
+ * memory): block dst of every layer's K and V cache becomes a byte copy of
+ * block src.  Layer l's K cache starts layer_stride_bytes * l after
+ * key_cache, its V cache as far after value_cache (for the pages' unified
+ * tensor kv: key_cache = kv[0, 0], value_cache = kv[0, 1], layer_stride_bytes
+ * = 2 * num_blocks * block_bytes).  block_bytes = block_size * num_kv_heads *
+ * head_dim * element size (any dtype, fp8 included), a multiple of 16.
+ * Pairs with an id outside [0, num_blocks) are skipped.  Pairs run
+ * concurrently: no dst may appear as the src or dst of another pair in the
+ * same call.  One launch; num_pairs = 0 is a no-op.
+ */
+pa_status pa_copy_blocks(void *key_cache, void *value_cache, int64_t layer_stride_bytes,
+                         int32_t num_layers, int64_t num_blocks, int64_t block_bytes,
+                         const int64_t *block_mapping, int64_t num_pairs, hipStream_t stream);
+
+/*
  * fp8 KV cache: the scatter.  ("AI Infra入门干货总结：大模型是如何高效推理的" and the
  * inference field notes gathered with it name quantising the KV cache as the
  * way to move fewer bytes per decoded token, e4m3 and e5m2 both in use; the

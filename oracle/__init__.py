@@ -89,6 +89,9 @@ def lib():
                 _f64p, _f64p, _f64p, ctypes.c_void_p, ctypes.c_int64, _i64p,
                 ctypes.POINTER(ctypes.c_float), ctypes.c_int32, ctypes.c_int32, ctypes.c_int64,
                 ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+            L.oracle_copy_blocks.restype = None
+            L.oracle_copy_blocks.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                             ctypes.c_int64, ctypes.c_int64, _i64p, ctypes.c_int64]
             _lib = L
     return _lib
 
@@ -180,6 +183,21 @@ def attention(query, key_cache, value_cache, block_table, cu_query_lens, seq_len
             float(scale), int(bool(causal)), dtype, kv_dtype, float(k_scale), float(v_scale),
             _p(probs, _f64p) if probs is not None else None, pstride)
     return (out, probs) if return_probs else out
+
+
+# --------------------------------------------------------- copy-on-write --
+def copy_blocks(kv, block_mapping):
+    """In place on a numpy cache kv [num_layers, 2, num_blocks, ...] (the
+    pages' layout): for each (src, dst) pair in order, block dst of every
+    layer's K and V becomes a copy of block src; pairs outside the pool are
+    skipped."""
+    assert kv.flags.c_contiguous and kv.ndim >= 3 and kv.shape[1] == 2
+    num_layers, _, num_blocks = kv.shape[:3]
+    block_bytes = kv[0, 0, 0].nbytes
+    pairs = _c(block_mapping, np.int64).reshape(-1, 2)
+    base = kv.ctypes.data
+    lib().oracle_copy_blocks(base, base + num_blocks * block_bytes, 2 * num_blocks * block_bytes, num_layers,
+                             num_blocks, block_bytes, _p(pairs, _i64p), len(pairs))
 
 
 # -------------------------------------------------------------- fp8 cache --

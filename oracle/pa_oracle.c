@@ -367,3 +367,34 @@ void oracle_reshape_and_cache_fp8(const void *key, int64_t key_stride, const voi
         }
     }
 }
+
+/* ---------------------------------------------------------------------------
+ * Copy-on-write of shared blocks.  Sequences that share a prefix point their
+ * block tables at the same physical blocks (prefix caching); before one of
+ * them writes into a shared block it gets a private copy ("AI Infra入门干货总结：
+ * 大模型是如何高效推理的", section "Paged Attention": the cache is
+ * [num_layers, 2, num_blocks, block_size, num_kv_heads, head_dim]; the
+ * inference field notes' chapter on batching and memory management names
+ * copy-on-write and prefix caching).
+ *
+ * For each pair (src, dst) of block_mapping [num_pairs][2], in order, with
+ * both in [0, num_blocks): block dst of every layer's K and V cache becomes a
+ * byte copy of block src.  Layer l's K cache starts layer_stride_bytes * l
+ * after key_cache, its V cache as far after value_cache; a block is
+ * block_bytes long.  Pairs with an id outside the pool are skipped.
+ * ------------------------------------------------------------------------- */
+void oracle_copy_blocks(void *key_cache, void *value_cache, int64_t layer_stride_bytes, int32_t num_layers,
+                        int64_t num_blocks, int64_t block_bytes, const int64_t *block_mapping, int64_t num_pairs)
+{
+    for (int64_t p = 0; p < num_pairs; p++) {
+        int64_t src = block_mapping[2 * p], dst = block_mapping[2 * p + 1];
+        if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks)
+            continue;
+        for (int32_t l = 0; l < num_layers; l++) {
+            char *k = (char *)key_cache + l * layer_stride_bytes;
+            char *v = (char *)value_cache + l * layer_stride_bytes;
+            memmove(k + dst * block_bytes, k + src * block_bytes, (size_t)block_bytes);
+            memmove(v + dst * block_bytes, v + src * block_bytes, (size_t)block_bytes);
+        }
+    }
+}

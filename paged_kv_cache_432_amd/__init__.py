@@ -18,7 +18,7 @@ import torch
 __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
     "pa_slot_mapping", "pa_reshape_and_cache", "pa_rope_reshape_and_cache", "pa_reshape_and_cache_fp8",
-    "pa_decode_fp8", "pa_decode_workspace_bytes",
+    "pa_decode_fp8", "pa_copy_blocks", "pa_decode_workspace_bytes",
     "pa_decode_partition_tokens", "pa_decode", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
     "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
 ]
@@ -68,6 +68,8 @@ def lib():
         L.pa_reshape_and_cache.restype = ctypes.c_int
         L.pa_reshape_and_cache.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32,
                                            _i32, _i32, ctypes.c_int, _vp]
+        L.pa_copy_blocks.restype = ctypes.c_int
+        L.pa_copy_blocks.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i64, _vp]
         L.pa_reshape_and_cache_fp8.restype = ctypes.c_int
         L.pa_reshape_and_cache_fp8.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32,
                                                _i32, _i32, ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp]
@@ -187,6 +189,23 @@ def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torc
                                    key_cache.shape[0], key_cache.shape[1], hkv, d, _dtype_code(key),
                                    _stream(stream, key_cache.device))
     _check(s, "pa_reshape_and_cache")
+
+
+def pa_copy_blocks(kv_cache: torch.Tensor, block_mapping: torch.Tensor, stream=None) -> None:
+    """Copy-on-write over the pages' unified cache kv_cache [num_layers, 2,
+    num_blocks, ...] (contiguous, any dtype): for each (src, dst) row of
+    block_mapping (int64 [n, 2]), block dst of every layer's K and V becomes a
+    copy of block src."""
+    _need(kv_cache.dim() >= 4 and kv_cache.shape[1] == 2 and kv_cache.is_contiguous(),
+          "kv_cache: contiguous [num_layers, 2, num_blocks, ...]")
+    _need(block_mapping.dtype == torch.int64 and block_mapping.dim() == 2 and block_mapping.shape[1] == 2
+          and block_mapping.is_contiguous(), "block_mapping: contiguous int64 [n, 2]")
+    num_layers, _, num_blocks = kv_cache.shape[:3]
+    block_bytes = kv_cache[0, 0, 0].numel() * kv_cache.element_size()
+    s = lib().pa_copy_blocks(_ptr(kv_cache), _ptr(kv_cache) + num_blocks * block_bytes,
+                             2 * num_blocks * block_bytes, num_layers, num_blocks, block_bytes,
+                             _ptr(block_mapping), block_mapping.shape[0], _stream(stream, kv_cache.device))
+    _check(s, "pa_copy_blocks")
 
 
 def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,

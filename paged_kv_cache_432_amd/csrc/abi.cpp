@@ -256,6 +256,23 @@ pa_status pa_reshape_and_cache(const void* key, int64_t key_token_stride, const 
                       "reshape_and_cache launch");
 }
 
+pa_status pa_copy_blocks(void* key_cache, void* value_cache, int64_t layer_stride_bytes, int32_t num_layers,
+                         int64_t num_blocks, int64_t block_bytes, const int64_t* block_mapping, int64_t num_pairs,
+                         hipStream_t stream) {
+    if (num_layers < 0 || num_blocks < 0 || block_bytes <= 0 || num_pairs < 0 || layer_stride_bytes < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size");
+    if (num_pairs == 0 || num_layers == 0) return ok();
+    if (!key_cache || !value_cache || !block_mapping) return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (block_bytes % 16 || !aligned16(key_cache) || !aligned16(value_cache) || layer_stride_bytes % 16)
+        return fail(PA_ERR_INVALID_ARG, "blocks and layers must start on 16-byte boundaries");
+    if (num_layers > 1 && layer_stride_bytes < num_blocks * block_bytes)
+        return fail(PA_ERR_INVALID_ARG, "layer stride shorter than a layer's blocks");
+    if (num_pairs > 0x7fffffff || num_layers > 32767) return fail(PA_ERR_INVALID_ARG, "grid too large");
+    return hip_status(pa::launch_copy_blocks(key_cache, value_cache, layer_stride_bytes, num_layers, num_blocks,
+                                             block_bytes, block_mapping, num_pairs, stream),
+                      "copy_blocks launch");
+}
+
 pa_status pa_reshape_and_cache_fp8(const void* key, int64_t key_token_stride, const void* value,
                                    int64_t value_token_stride, void* key_cache, void* value_cache,
                                    const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,

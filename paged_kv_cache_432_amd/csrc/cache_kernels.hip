@@ -52,6 +52,35 @@ reshape_and_cache_kernel(const char* __restrict__ key, int64_t key_stride_bytes,
     }
 }
 
+// ---- copy-on-write of shared blocks ------------------------------------------
+// Block dst of every layer's K and V cache becomes a copy of block src, for
+// each (src, dst) pair ("AI Infra入门干货总结：大模型是如何高效推理的", section
+// "Paged Attention": the [num_layers, 2, num_blocks, ...] cache; copy-on-write
+// of blocks shared by a prefix).  Workgroup (pair, 2 * layer + K/V) moves one
+// block, 16 bytes per thread per step.  Pairs run concurrently: no dst may be
+// the src or dst of another pair in the same call.
+__global__ void __launch_bounds__(256)
+copy_blocks_kernel(char* __restrict__ key_cache, char* __restrict__ value_cache, int64_t layer_stride_bytes,
+                   int64_t num_blocks, int64_t block_bytes, const int64_t* __restrict__ block_mapping) {
+    const int64_t pair = blockIdx.x;
+    const int64_t src = block_mapping[2 * pair], dst = block_mapping[2 * pair + 1];
+    if (src < 0 || src >= num_blocks || dst < 0 || dst >= num_blocks || src == dst) return;
+    const int layer = blockIdx.y >> 1;
+    char* base = ((blockIdx.y & 1) ? value_cache : key_cache) + layer * layer_stride_bytes;
+    const u32x4_t* from = reinterpret_cast<const u32x4_t*>(base + src * block_bytes);
+    u32x4_t* to = reinterpret_cast<u32x4_t*>(base + dst * block_bytes);
+    for (int64_t c = threadIdx.x; c < block_bytes / 16; c += blockDim.x) to[c] = from[c];
+}
+
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, int64_t layer_stride_bytes, int32_t num_layers,
+                              int64_t num_blocks, int64_t block_bytes, const int64_t* block_mapping,
+                              int64_t num_pairs, hipStream_t stream) {
+    hipLaunchKernelGGL(copy_blocks_kernel, dim3((unsigned)num_pairs, (unsigned)(2 * num_layers)), dim3(256), 0,
+                       stream, (char*)key_cache, (char*)value_cache, layer_stride_bytes, num_blocks, block_bytes,
+                       block_mapping);
+    return hipGetLastError();
+}
+
 // ---- fp8 (E4M3) scatter ------------------------------------------------------
 // As reshape_and_cache_kernel, but each element x of a K (V) row is stored as
 // the OCP E4M3 code of x / k_scale (v_scale): the division in float32

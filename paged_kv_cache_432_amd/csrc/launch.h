@@ -13,6 +13,11 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
                                const int32_t* token_seq, const int32_t* token_pos,
                                int64_t num_tokens, hipStream_t stream);
 
+// Copy-on-write: block pairs (src, dst) of every layer's K and V caches.
+hipError_t launch_copy_blocks(void* key_cache, void* value_cache, int64_t layer_stride_bytes, int32_t num_layers,
+                              int64_t num_blocks, int64_t block_bytes, const int64_t* block_mapping,
+                              int64_t num_pairs, hipStream_t stream);
+
 // fp8 (E4M3) scatter: K/V rows of `dtype` (0 fp32, 1 bf16) divided by their
 // scale, stored one byte per element.
 hipError_t launch_reshape_and_cache_fp8(const void* key, int64_t key_stride_bytes, const void* value,

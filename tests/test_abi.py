@@ -201,3 +201,14 @@ def test_fp8_entries_reject_before_launch(L):
     assert dec(d=64) == pa.PA_ERR_UNSUPPORTED
     assert dec(qs=4000) == pa.PA_ERR_INVALID_ARG
     assert dec(msl=8193) == pa.PA_ERR_INVALID_ARG
+
+
+def test_copy_blocks_rejects_before_launch(L):
+    cb = L.pa_copy_blocks
+    assert cb(16, 16, 0, 1, 10, 32768, 16, 0, None) == pa.PA_OK                 # no pairs
+    assert cb(16, 16, 0, 0, 10, 32768, 16, 4, None) == pa.PA_OK                 # no layers
+    assert cb(16, 16, 0, 1, 10, 32760, 16, 4, None) == pa.PA_ERR_INVALID_ARG    # block not 16-byte sized
+    assert cb(16, 24, 0, 1, 10, 32768, 16, 4, None) == pa.PA_ERR_INVALID_ARG    # misaligned cache
+    assert cb(16, 16, 1000, 2, 10, 32768, 16, 4, None) == pa.PA_ERR_INVALID_ARG  # layers overlap
+    assert cb(16, 16, 0, 1, 10, 32768, None, 4, None) == pa.PA_ERR_INVALID_ARG  # null mapping
+    assert cb(16, 16, 0, 1, 10, -1, 16, 4, None) == pa.PA_ERR_INVALID_ARG

@@ -241,3 +241,20 @@ def test_kv_byte_accounting_matches_pages():
     w = W.custom(seq_lens=[g["context"]], num_heads=32, num_kv_heads=g["num_kv_heads"],
                  head_dim=g["head_dim"], dtype="bf16")
     assert g["num_layers"] * w.kv_bytes() == g["kv_bytes_all_layers"]
+
+
+def test_copy_blocks_copies_every_layer_and_nothing_else():
+    """Copy-on-write: block dst of every layer's K and V equals block src
+    afterwards, byte for byte; every other block is untouched; a pair outside
+    the pool does nothing; pairs apply in order (a later pair sees an earlier
+    copy)."""
+    rng = np.random.default_rng(0)
+    kv = rng.integers(0, 1 << 16, size=(3, 2, 10, 16, 2, 8), dtype=np.uint16)
+    before = kv.copy()
+    pairs = np.array([[1, 4], [7, 2], [4, 9], [3, 10], [-1, 5]], np.int64)
+    oracle.copy_blocks(kv, pairs)
+    want = before.copy()
+    want[:, :, 4] = before[:, :, 1]
+    want[:, :, 2] = before[:, :, 7]
+    want[:, :, 9] = before[:, :, 1]                    # via block 4, already a copy of 1
+    assert np.array_equal(kv, want)

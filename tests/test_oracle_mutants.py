@@ -41,6 +41,10 @@ MUTANTS = {
     "fp8_k_scale_dropped": ("(widen(key_cache, kbase + d, kv_dtype) * k_scale)",
                             "widen(key_cache, kbase + d, kv_dtype)"),
     "fp8_scatter_multiplies": ("oracle_e4m3_encode(k / k_scale)", "oracle_e4m3_encode(k * k_scale)"),
+    "copy_direction": ("memmove(k + dst * block_bytes, k + src * block_bytes, (size_t)block_bytes);",
+                       "memmove(k + src * block_bytes, k + dst * block_bytes, (size_t)block_bytes);"),
+    "copy_first_layer_only": ("for (int32_t l = 0; l < num_layers; l++) {\n            char *k",
+                              "for (int32_t l = 0; l < 1; l++) {\n            char *k"),
 }
 PIN_FILES = [os.path.join(ROOT, "tests", name)
              for name in ("test_oracle.py", "test_oracle_rope.py", "test_oracle_fp8.py")]
