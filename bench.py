@@ -219,6 +219,44 @@ def copy_blocks_timing(pa, torch, pair_counts=(1, 64, 1024), layers: int = 32, i
             "calls": rows}
 
 
+def kv_manager_timing(pa, steps: int = 200):
+    """Host cost of the block manager's step (pa_kvm_schedule + pa_kvm_commit,
+    through the Python binding) for 256 running decode requests with the
+    continuous-batching lengths (log-normal, median 900, clipped to [16,
+    16384]); the pool is 110% of the blocks they need.  The prompts are first
+    prefilled in chunks of at most 8192 tokens per step."""
+    rng = np.random.default_rng(3)
+    lens = np.clip(np.round(np.exp(rng.normal(np.log(900), 1.0, 256))), 16, 16384).astype(np.int64)
+    need = int(((lens + 200 + 15) // 16).sum())
+    m = pa.KvManager(int(need * 1.1), 256, 8192, 16384 + 256, prefix_caching=True)
+    for i, n in enumerate(lens):
+        m.add_request(i, rng.integers(0, 32000, int(n)))
+    prefill_steps = 0
+    while True:
+        st = m.schedule()
+        m.commit(np.full(st["num_seqs"], 11, np.int32))
+        prefill_steps += 1
+        if st["num_seqs"] == 256 and int(st["query_lens"].max()) == 1:
+            break
+    nxt = np.full(256, 11, np.int32)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        st = m.schedule()
+        m.commit(nxt)
+    us_py = (time.perf_counter() - t0) / steps * 1e6
+    import ctypes
+    L, raw = pa.lib(), pa._KvmStep()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        L.pa_kvm_schedule(m._h, ctypes.byref(raw))
+        L.pa_kvm_commit(m._h, nxt.ctypes.data, 256)
+    us_c = (time.perf_counter() - t0) / steps * 1e6
+    return {"what": "pa_kvm_schedule + pa_kvm_commit per decode step, host CPU", "requests": 256,
+            "tokens_per_step": int(st["num_tokens"]), "block_table_width": int(raw.max_blocks_per_req),
+            "us_per_step_c_abi": round(us_c, 1), "us_per_step_python_binding": round(us_py, 1),
+            "prefill_steps": prefill_steps}
+
+
 def mfma_probe(pa, torch, iters: int = 10):
     """The library's matrix-core probe (4 independent v_mfma_f32_32x32x16_bf16
     chains per wave, two 4-wave workgroups per compute unit): the matrix rate
@@ -511,6 +549,7 @@ def main():
         res["roofline"]["frac_of_read_probe"] = round(dec_gbps / probe["stream_read"]["GBps"], 4)
         res["rope_reshape_and_cache"] = rope_scatter_timing(pa, torch)
         res["copy_blocks"] = copy_blocks_timing(pa, torch)
+        res["kv_manager"] = kv_manager_timing(pa)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, fp8)
     print(json.dumps(res), flush=True)

@@ -114,6 +114,72 @@ pa_status pa_reshape_and_cache(const void *key, int64_t key_token_stride,
                                pa_dtype dtype, hipStream_t stream);
 
 /*
+ * Host-side block manager and step scheduler (the input side of the path; no
+ * GPU work, no device memory).  "AI Infra入门干货总结：大模型是如何高效推理的",
+ * sections "连续批处理 (Continuous Batching)" and "Paged Attention", and its
+ * appendix 4 on preemption; the inference field notes' prefix-caching entry.
+ *
+ * A request holds its tokens (prompt, then outputs) and the number it has
+ * computed; each pa_kvm_schedule call schedules, for every running request in
+ * arrival order and then for waiting requests first come first served, the
+ * tokens it has not computed yet, within max_num_batched_tokens per step,
+ * max_num_seqs running requests and max_model_len tokens per request, and
+ * allocates the 16-token blocks they need.  When a running request cannot get
+ * its blocks, the newest running request is preempted: all its blocks are
+ * freed, its computed count is reset to 0 and it goes to the front of the
+ * waiting queue (recomputation).  A waiting request that cannot get its
+ * blocks waits; no waiting request is admitted in a step that preempted.
+ * With prefix caching, full computed blocks are registered under a hash of
+ * their tokens and of the blocks before them; a new request starts from the
+ * longest run of its full prompt blocks found there (never covering its last
+ * prompt token), sharing those blocks.  pa_kvm_fork makes a request that
+ * shares all blocks of a running one; the first step that writes into a
+ * shared block gives the writer a fresh block and lists the (old, new) pair
+ * in copy_pairs, for pa_copy_blocks before the step's scatter.
+ *
+ * Use per step: pa_kvm_schedule -> (copy_pairs via pa_copy_blocks,
+ * slot_mapping via pa_reshape_and_cache, then attention over block_table,
+ * seq_lens, cu_query_lens) -> pa_kvm_commit with one next token per scheduled
+ * request (or -1): a request whose computed count reaches its token count
+ * appends it.  The step's arrays belong to the manager and stay valid until
+ * the next pa_kvm_schedule.  A manager is not thread-safe.
+ */
+typedef struct pa_kvm pa_kvm;
+
+typedef struct {
+    int32_t num_seqs;              /* scheduled requests: the step's batch rows */
+    int64_t num_tokens;            /* scheduled tokens, flattened */
+    int32_t max_blocks_per_req;    /* block_table row length: the most blocks a scheduled request holds */
+    const int64_t *request_ids;    /* [num_seqs] */
+    const int32_t *query_lens;     /* [num_seqs] tokens computed this step */
+    const int32_t *cu_query_lens;  /* [num_seqs + 1] */
+    const int32_t *seq_lens;       /* [num_seqs] tokens attended: computed + this step's */
+    const int32_t *block_table;    /* [num_seqs, max_blocks_per_req], -1 past the request's blocks */
+    const int32_t *token_ids;      /* [num_tokens] input tokens of the step, row by row */
+    const int32_t *positions;      /* [num_tokens] their positions */
+    const int64_t *slot_mapping;   /* [num_tokens] their slots */
+    const int64_t *copy_pairs;     /* [num_copies, 2] (src, dst) blocks to copy before the scatter */
+    int32_t num_copies;
+    const int64_t *preempted;      /* [num_preempted] requests preempted this step */
+    int32_t num_preempted;
+} pa_kvm_step;
+
+pa_kvm *pa_kvm_create(int32_t num_blocks, int32_t max_num_seqs, int32_t max_num_batched_tokens,
+                      int32_t max_model_len, int32_t enable_prefix_caching);
+void pa_kvm_destroy(pa_kvm *m);
+pa_status pa_kvm_add_request(pa_kvm *m, int64_t request_id, const int32_t *prompt, int32_t prompt_len);
+pa_status pa_kvm_fork(pa_kvm *m, int64_t parent_id, int64_t child_id);
+pa_status pa_kvm_finish(pa_kvm *m, int64_t request_id);
+pa_status pa_kvm_schedule(pa_kvm *m, pa_kvm_step *step);
+pa_status pa_kvm_commit(pa_kvm *m, const int32_t *next_tokens, int32_t num_seqs);
+int32_t pa_kvm_num_free_blocks(const pa_kvm *m);
+int32_t pa_kvm_num_cached_blocks(const pa_kvm *m);
+int32_t pa_kvm_block_ref(const pa_kvm *m, int32_t block);
+pa_status pa_kvm_request_info(const pa_kvm *m, int64_t request_id, int32_t *num_computed,
+                              int32_t *num_tokens, int32_t *running, int32_t *blocks,
+                              int32_t blocks_cap, int32_t *num_blocks);
+
+/*
  * Copy-on-write of shared blocks.  Sequences that share a prefix point their
  * block tables at the same physical blocks (prefix caching); before one of
  * them writes into a shared block, the caller gives it a fresh block and this

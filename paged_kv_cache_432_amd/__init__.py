@@ -13,12 +13,13 @@ import ctypes
 import os
 import threading
 
+import numpy as np
 import torch
 
 __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
     "pa_slot_mapping", "pa_reshape_and_cache", "pa_rope_reshape_and_cache", "pa_reshape_and_cache_fp8",
-    "pa_decode_fp8", "pa_copy_blocks", "pa_decode_workspace_bytes",
+    "pa_decode_fp8", "pa_copy_blocks", "KvManager", "pa_decode_workspace_bytes",
     "pa_decode_partition_tokens", "pa_decode", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
     "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
 ]
@@ -34,6 +35,13 @@ _lock = threading.Lock()
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
 _i64 = ctypes.c_int64
+
+
+class _KvmStep(ctypes.Structure):
+    _fields_ = [("num_seqs", _i32), ("num_tokens", _i64), ("max_blocks_per_req", _i32),
+                ("request_ids", _vp), ("query_lens", _vp), ("cu_query_lens", _vp), ("seq_lens", _vp),
+                ("block_table", _vp), ("token_ids", _vp), ("positions", _vp), ("slot_mapping", _vp),
+                ("copy_pairs", _vp), ("num_copies", _i32), ("preempted", _vp), ("num_preempted", _i32)]
 
 
 class PaError(RuntimeError):
@@ -68,6 +76,28 @@ def lib():
         L.pa_reshape_and_cache.restype = ctypes.c_int
         L.pa_reshape_and_cache.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32,
                                            _i32, _i32, ctypes.c_int, _vp]
+        L.pa_kvm_create.restype = _vp
+        L.pa_kvm_create.argtypes = [_i32, _i32, _i32, _i32, _i32]
+        L.pa_kvm_destroy.restype = None
+        L.pa_kvm_destroy.argtypes = [_vp]
+        L.pa_kvm_add_request.restype = ctypes.c_int
+        L.pa_kvm_add_request.argtypes = [_vp, _i64, _vp, _i32]
+        L.pa_kvm_fork.restype = ctypes.c_int
+        L.pa_kvm_fork.argtypes = [_vp, _i64, _i64]
+        L.pa_kvm_finish.restype = ctypes.c_int
+        L.pa_kvm_finish.argtypes = [_vp, _i64]
+        L.pa_kvm_schedule.restype = ctypes.c_int
+        L.pa_kvm_schedule.argtypes = [_vp, ctypes.POINTER(_KvmStep)]
+        L.pa_kvm_commit.restype = ctypes.c_int
+        L.pa_kvm_commit.argtypes = [_vp, _vp, _i32]
+        L.pa_kvm_num_free_blocks.restype = _i32
+        L.pa_kvm_num_free_blocks.argtypes = [_vp]
+        L.pa_kvm_num_cached_blocks.restype = _i32
+        L.pa_kvm_num_cached_blocks.argtypes = [_vp]
+        L.pa_kvm_block_ref.restype = _i32
+        L.pa_kvm_block_ref.argtypes = [_vp, _i32]
+        L.pa_kvm_request_info.restype = ctypes.c_int
+        L.pa_kvm_request_info.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp]
         L.pa_copy_blocks.restype = ctypes.c_int
         L.pa_copy_blocks.argtypes = [_vp, _vp, _i64, _i32, _i64, _i64, _vp, _i64, _vp]
         L.pa_reshape_and_cache_fp8.restype = ctypes.c_int
@@ -189,6 +219,82 @@ def pa_reshape_and_cache(key: torch.Tensor, value: torch.Tensor, key_cache: torc
                                    key_cache.shape[0], key_cache.shape[1], hkv, d, _dtype_code(key),
                                    _stream(stream, key_cache.device))
     _check(s, "pa_reshape_and_cache")
+
+
+def _host_array(ptr, n, dtype):
+    if n == 0 or not ptr:
+        return np.zeros(0, dtype)
+    ct = {np.int32: ctypes.c_int32, np.int64: ctypes.c_int64}[dtype]
+    return np.ctypeslib.as_array(ctypes.cast(ptr, ctypes.POINTER(ct)), shape=(n,)).copy()
+
+
+class KvManager:
+    """The host block manager and step scheduler (pa_kvm_*): see include/pa.h."""
+
+    def __init__(self, num_blocks: int, max_num_seqs: int, max_num_batched_tokens: int, max_model_len: int,
+                 prefix_caching: bool = True):
+        self._L = lib()
+        self._h = self._L.pa_kvm_create(num_blocks, max_num_seqs, max_num_batched_tokens, max_model_len,
+                                        int(bool(prefix_caching)))
+        if not self._h:
+            raise PaError(PA_ERR_INVALID_ARG, "pa_kvm_create", pa_last_error_message())
+
+    def __del__(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            self._L.pa_kvm_destroy(h)
+
+    def add_request(self, request_id: int, prompt) -> None:
+        p = np.ascontiguousarray(prompt, np.int32)
+        _check(self._L.pa_kvm_add_request(self._h, int(request_id), p.ctypes.data, len(p)), "pa_kvm_add_request")
+
+    def fork(self, parent_id: int, child_id: int) -> None:
+        _check(self._L.pa_kvm_fork(self._h, int(parent_id), int(child_id)), "pa_kvm_fork")
+
+    def finish(self, request_id: int) -> None:
+        _check(self._L.pa_kvm_finish(self._h, int(request_id)), "pa_kvm_finish")
+
+    def schedule(self) -> dict:
+        """One step: numpy copies of the step's arrays (block_table 2-D,
+        copy_pairs [n, 2])."""
+        st = _KvmStep()
+        _check(self._L.pa_kvm_schedule(self._h, ctypes.byref(st)), "pa_kvm_schedule")
+        n, t, w = st.num_seqs, st.num_tokens, st.max_blocks_per_req
+        return {
+            "num_seqs": n, "num_tokens": t, "max_blocks_per_req": w,
+            "request_ids": _host_array(st.request_ids, n, np.int64),
+            "query_lens": _host_array(st.query_lens, n, np.int32),
+            "cu_query_lens": _host_array(st.cu_query_lens, n + 1, np.int32),
+            "seq_lens": _host_array(st.seq_lens, n, np.int32),
+            "block_table": _host_array(st.block_table, n * w, np.int32).reshape(n, w),
+            "token_ids": _host_array(st.token_ids, t, np.int32),
+            "positions": _host_array(st.positions, t, np.int32),
+            "slot_mapping": _host_array(st.slot_mapping, t, np.int64),
+            "copy_pairs": _host_array(st.copy_pairs, 2 * st.num_copies, np.int64).reshape(-1, 2),
+            "preempted": _host_array(st.preempted, st.num_preempted, np.int64),
+        }
+
+    def commit(self, next_tokens) -> None:
+        t = np.ascontiguousarray(next_tokens, np.int32)
+        _check(self._L.pa_kvm_commit(self._h, t.ctypes.data if len(t) else None, len(t)), "pa_kvm_commit")
+
+    def num_free_blocks(self) -> int:
+        return int(self._L.pa_kvm_num_free_blocks(self._h))
+
+    def num_cached_blocks(self) -> int:
+        return int(self._L.pa_kvm_num_cached_blocks(self._h))
+
+    def block_ref(self, block: int) -> int:
+        return int(self._L.pa_kvm_block_ref(self._h, int(block)))
+
+    def request(self, request_id: int) -> dict:
+        nc, nt, run, nb = (ctypes.c_int32() for _ in range(4))
+        _check(self._L.pa_kvm_request_info(self._h, int(request_id), ctypes.byref(nc), ctypes.byref(nt),
+                                           ctypes.byref(run), None, 0, ctypes.byref(nb)), "pa_kvm_request_info")
+        blocks = np.zeros(nb.value, np.int32)
+        _check(self._L.pa_kvm_request_info(self._h, int(request_id), None, None, None, blocks.ctypes.data,
+                                           len(blocks), None), "pa_kvm_request_info")
+        return {"num_computed": nc.value, "num_tokens": nt.value, "running": bool(run.value), "blocks": blocks}
 
 
 def pa_copy_blocks(kv_cache: torch.Tensor, block_mapping: torch.Tensor, stream=None) -> None:

@@ -11,7 +11,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 
-SOURCES = ["abi.cpp", "cache_kernels.hip", "decode_kernel.hip", "prefill_kernel.hip", "probe_kernels.hip"]
+SOURCES = ["abi.cpp", "kv_manager.cpp", "cache_kernels.hip", "decode_kernel.hip", "prefill_kernel.hip",
+           "probe_kernels.hip"]
 
 # Packed fp32 VALU ops are disabled for all device code: scalar and float2 code
 # is compiled to plain v_fma/v_mul/v_add.

@@ -10,6 +10,7 @@
 #include <algorithm>
 #include <mutex>
 
+#include "host_status.h"
 #include "launch.h"
 
 namespace {
@@ -35,6 +36,24 @@ pa_status hip_status(hipError_t e, const char* what) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+}  // namespace
+
+namespace pa {
+
+pa_status report(pa_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+pa_status report_ok() { return ok(); }
+
+}  // namespace pa
+
+namespace {
 
 int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
 
