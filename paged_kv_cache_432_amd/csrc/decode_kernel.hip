@@ -358,6 +358,8 @@ __device__ __forceinline__ void finish(WaveState<Chunk, Elem, G, QL>& st, int la
 // a block's maximum exceeds it by more than 2^8 (log2 units), so the rescale of
 // the accumulators is rare; p stays below 256.
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 constexpr float kMfmaSlack = 8.f;
 
@@ -406,6 +408,11 @@ __device__ __forceinline__ void load_query_mfma(const DecodeArgs& a, int64_t row
 // One block's online softmax and O^T += V^T P^T for the matrix-core wave: s
 // holds the lane's scores (head i, tokens 4g .. 4g+3, masked ones -inf), v its
 // V chunks (tokens 4g .. 4g+3, dims 8i .. 8i+7).
+// v[r]: eight 16-bit V values (dims 8i .. 8i+7 of token 4g + r).  F16: v is
+// fp16 (exact for an fp8 cache), P is rounded once to fp16 and one
+// 16x16x16 f16 product per dim tile takes it; the row sum adds the same
+// rounded P.  Otherwise v is bf16 and P goes in as bf16 hi + lo, two products.
+template <bool F16 = false>
 __device__ __forceinline__ void softmax_pv_mfma(const DecodeArgs& a, MfmaState& st, f32x4_t s, const u32x4_t (&v)[4]) {
     float mx = maximum(maximum(s[0], s[1]), maximum(s[2], s[3]));
     mx = max_across_rows(mx);
@@ -422,6 +429,22 @@ __device__ __forceinline__ void softmax_pv_mfma(const DecodeArgs& a, MfmaState& 
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = __builtin_amdgcn_exp2f(fmaf(s[r], a.scale_log2, -msafe));
+    if constexpr (F16) {
+        const f16x2_t p01 = __builtin_convertvector(f32x2_t{p[0], p[1]}, f16x2_t);
+        const f16x2_t p23 = __builtin_convertvector(f32x2_t{p[2], p[3]}, f16x2_t);
+        const f16x2_t one = f16x2_t{(_Float16)1.f, (_Float16)1.f};
+        st.l = __builtin_amdgcn_fdot2(p23, one, __builtin_amdgcn_fdot2(p01, one, st.l * alpha, false), false);
+        const f16x4_t P = f16x4_t{p01.x, p01.y, p23.x, p23.y};
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt) {
+            const uint32_t sel = (dt & 1) ? 0x07060302u : 0x05040100u;
+            const int w = dt >> 1;
+            const u32x2_t av = u32x2_t{__builtin_amdgcn_perm(v[1][w], v[0][w], sel),
+                                       __builtin_amdgcn_perm(v[3][w], v[2][w], sel)};
+            st.acc[dt] = __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, av), P, st.acc[dt], 0, 0, 0);
+        }
+        return;
+    }
     st.l = st.l * alpha + ((p[0] + p[1]) + (p[2] + p[3]));
     uint32_t u[4];
 #pragma unroll
@@ -588,6 +611,14 @@ template <bool F8> struct KvBuf;
 template <> struct KvBuf<false> { u32x4_t k[4], v[4]; };
 template <> struct KvBuf<true> { u32x4_t k[2]; u32x2_t v[4]; };
 
+// Eight fp8 (E4M3) values in two words -> eight fp16, exactly (every E4M3
+// value is an fp16 value: at most 448, at least 2^-9), byte e -> element e.
+__device__ __forceinline__ u32x4_t fp8x8_to_f16(uint32_t w0, uint32_t w1) {
+    return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, true)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, false)),
+                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true))};
+}
 // Eight fp8 (E4M3) values in two words -> eight bf16, exactly (every E4M3
 // value is a bf16 value), byte e -> element e.
 __device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
@@ -737,7 +768,7 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const u32x2_t w = buf.v[r];
-                vb[r] = fp8x8_to_bf16(w.x, w.y);
+                vb[r] = fp8x8_to_f16(w.x, w.y);
             }
         } else {
 #pragma unroll
@@ -753,7 +784,7 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
                                                         __builtin_bit_cast(bf16x8_t, st.q[ks]), s, 0, 0, 0);
 #pragma unroll
         for (int r = 0; r < 4; ++r) s[r] = r < nval ? s[r] : -INFINITY;
-        softmax_pv_mfma(a, st, s, vb);
+        softmax_pv_mfma<F8>(a, st, s, vb);
     };
 
     for (c0 = 0; c0 < total; c0 = c1) {
