@@ -310,13 +310,30 @@ def cpu_baseline(w, nseq: int, fp8: bool = False):
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
     kvb = sub.kv_bytes(1 if fp8 else None)
+    # one thread, on the first 4 of those sequences: a per-core figure
+    one = W._subset(sub, np.arange(min(4, len(idx))), "cpu_sample_1t")
+    kv1 = one.kv_bytes(1 if fp8 else None)
+    threads = oracle.max_threads()
+    oracle.set_threads(1)
+    q1 = one.encode(one.queries())
+    t1 = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.attention(q1, kc, vc, one.block_table, one.cu_query_lens, one.seq_lens, one.num_heads,
+                         one.scale, one.causal, k_scale=ks if fp8 else 1.0, v_scale=vs if fp8 else 1.0)
+        t1.append(time.perf_counter() - t0)
+    oracle.set_threads(threads)
+    dt1 = float(np.median(t1))
     return {
         "value": round(kvb / dt / 1e9, 4),
         "unit": "GB/s",
         "seq_steps_per_s": round(len(idx) / dt, 3),
         "seconds": round(dt, 3),
-        "cores": oracle.max_threads(),
+        "cores": threads,
         "kind": "oracle",
+        "per_core": {"GBps": round(kv1 / dt1 / 1e9, 4), "seconds": round(dt1, 4),
+                     "sample": f"attention only, first {one.num_seqs} sequences ({int(one.seq_lens.sum())} KV "
+                               f"tokens), one thread, median of 3"},
         "sample": f"first {len(idx)} of {w.num_seqs} sequences ({int(sub.seq_lens.sum())} KV tokens, "
                   f"{kvb / 1e9:.3f} GB of KV), one step (slots + scatter + attention), fp64, median of 3",
     }
@@ -541,6 +558,7 @@ def main():
             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "avg_launch_us": round(dec_avg_ms * 1e3, 2),
+            "launch_us_median_p10_p90": [round(float(np.percentile(dec_ms, q)) * 1e3, 2) for q in (50, 10, 90)],
             "algorithmic_bytes_per_launch": kv,
         },
     }

@@ -56,6 +56,8 @@ def lib():
             L = ctypes.CDLL(path)
             L.oracle_max_threads.restype = ctypes.c_int32
             L.oracle_max_threads.argtypes = []
+            L.oracle_set_threads.restype = None
+            L.oracle_set_threads.argtypes = [ctypes.c_int32]
             L.oracle_slot.restype = ctypes.c_int64
             L.oracle_slot.argtypes = [_i32p, ctypes.c_int64, ctypes.c_int32]
             L.oracle_slot_mapping.restype = None
@@ -98,6 +100,11 @@ def lib():
 
 def max_threads() -> int:
     return int(lib().oracle_max_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads the attention loop uses from now on (for timing only)."""
+    lib().oracle_set_threads(int(n))
 
 
 def _p(a, t):

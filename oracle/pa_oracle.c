@@ -49,6 +49,17 @@ int oracle_max_threads(void)
 
 double oracle_e4m3_value(uint8_t code);
 
+/* Threads the attention loop may use from now on (OpenMP); for timing. */
+void oracle_set_threads(int32_t n)
+{
+#ifdef _OPENMP
+    if (n > 0)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 static double widen(const void *base, int64_t idx, int dtype)
 {
     if (dtype == ORACLE_F32)
