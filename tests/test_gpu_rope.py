@@ -214,3 +214,52 @@ def test_rope_graph_replays_match_eager(pa):
         assert torch.equal(qout.view(torch.int16), q_e.view(torch.int16)), seed
         assert torch.equal(kc.view(torch.int16), k_e.view(torch.int16)), seed
         assert torch.equal(vc.view(torch.int16), v_e.view(torch.int16)), seed
+
+
+def test_rope_scatter_then_decode_matches_oracle(pa):
+    """The input side end to end: a Llama-3-8B-shaped decode step whose 8 new
+    tokens come out of one fused projection row each.  pa_rope_reshape_and_cache
+    turns Q and K and scatters K, V next to the 8 sequences' earlier context;
+    pa_decode attends with the turned Q.  The oracle turns the same rows in
+    fp64 (rounded to bf16, as stored), writes them into its own cache and
+    attends: the bf16 bar."""
+    import workloads as W
+    dev = "cuda"
+    rng = np.random.default_rng(17)
+    hq, hkv, B = 32, 8, 8
+    lens = rng.integers(20, 700, B).astype(np.int32)
+    w = W.custom("rope_decode", seq_lens=lens, dtype="bf16", seed=17, sigma=1.0)
+    table = oracle.rope_table(1024, 128, BASE).astype(np.float32)
+    # earlier context through the library's plain scatter, the new token through the fused one
+    kc = torch.full((w.num_blocks, 16, hkv, D), float("nan"), dtype=torch.bfloat16, device=dev)
+    vc = torch.full_like(kc, float("nan"))
+    okc, okv = w.poisoned_cache(), w.poisoned_cache()
+    seq_h, pos_h = w.tokens("history")
+    slots_h = oracle.slot_mapping(w.block_table, seq_h, pos_h)
+    kh, vh = w.token_kv(seq_h, pos_h)
+    pa.pa_reshape_and_cache(torch.from_numpy(kh).to(dev).to(torch.bfloat16),
+                            torch.from_numpy(vh).to(dev).to(torch.bfloat16), kc, vc,
+                            torch.from_numpy(slots_h).to(dev))
+    oracle.reshape_and_cache(w.encode(kh), w.encode(vh), okc, okv, slots_h)
+    seq_n, pos_n = w.tokens("new")
+    slots_n = oracle.slot_mapping(w.block_table, seq_n, pos_n)
+    qkv = W.bf16_round(rng.standard_normal((B, (hq + 2 * hkv) * D), dtype=np.float32))
+    qkv_bits = W.bf16_bits(qkv)
+    q_d = torch.empty(B, hq, D, dtype=torch.bfloat16, device=dev)
+    pa.pa_rope_reshape_and_cache(q_d, torch.from_numpy(qkv).to(dev).to(torch.bfloat16),
+                                 torch.from_numpy(pos_n.astype(np.int64)).to(dev), torch.from_numpy(table).to(dev),
+                                 kc, vc, torch.from_numpy(slots_n).to(dev), hq, hkv)
+    out = torch.empty_like(q_d)
+    ws = pa.decode_workspace(B, hq, hkv, D, int(lens.max()), 0)
+    pa.pa_decode(out, q_d, kc, vc, torch.from_numpy(w.block_table).to(dev),
+                 torch.from_numpy(lens).to(dev), w.scale, int(lens.max()), 0, ws)
+    torch.cuda.synchronize()
+    # oracle: the same rows turned in fp64, stored as bf16, then attention
+    q_ex, k_ex, v_ex = oracle.rope_qkv(qkv_bits, pos_n, table, 128, True, hq, hkv, D)
+    oracle.reshape_and_cache(W.bf16_bits(k_ex.astype(np.float32)), W.bf16_bits(v_ex.astype(np.float32)),
+                             okc, okv, slots_n)
+    cu = np.arange(B + 1, dtype=np.int32)
+    ref = oracle.attention(W.bf16_bits(q_ex.astype(np.float32)), okc, okv, w.block_table, cu, lens, hq, w.scale,
+                           False)
+    from parity import assert_parity, to_numpy
+    assert_parity(to_numpy(out), ref, "bf16", "RoPE scatter then decode")
