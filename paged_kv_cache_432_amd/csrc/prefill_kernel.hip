@@ -324,8 +324,10 @@ prefill_kernel(PrefillArgs a) {
         const int w4 = __builtin_amdgcn_readfirstlane(tid >> 8);   // the same for a whole wave
         const uint32_t koff = ((tid >> 4) & 15) * tok_bytes + head_off + (tid & 15) * 16;
         const uint32_t voff = 4 * (kq & 3) * tok_bytes + head_off + dp * 4;
-        u32x4_t kreg[2];
-        uint32_t vw[2][4];
+        // two sets of staging registers: a tile's loads are issued two tiles
+        // before its commit, the set chosen at compile time (see run)
+        u32x4_t kreg[2][2];
+        uint32_t vw[2][2][4];
         // Block ids of the key range, 64 at a time (one per lane), broadcast with
         // v_readlane, so that the tile's 10 loads issue back to back instead of
         // each waiting on its own table read.
@@ -336,7 +338,8 @@ prefill_kernel(PrefillArgs a) {
             const int64_t id = __builtin_amdgcn_readlane(bid, blk - bid_base);
             return min(max(id, (int64_t)0), a.num_blocks - 1);
         };
-        auto stage = [&](int kt) {
+        auto stage = [&](int kt, auto set) {
+            constexpr int S = decltype(set)::value;
             if (4 * kt + 3 >= bid_base + kWave) {          // wave-uniform: the tile's ids are not all held
                 bid_base = 4 * kt;
                 bid = bid_base + lane < nblk_wg ? bt[bid_base + lane] : 0;
@@ -348,10 +351,10 @@ prefill_kernel(PrefillArgs a) {
                 const int nrec = __builtin_amdgcn_readfirstlane(min(max(kend_wg - blk * kBlock, 0), kBlock) * (int)tok_bytes);
                 const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
                 const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
-                kreg[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff, 0, 0));
+                kreg[S][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff, 0, 0));
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
-                    vw[j][i] = __builtin_amdgcn_raw_buffer_load_b32(rv, (int)(voff + i * tok_bytes), 0, 0);
+                    vw[S][j][i] = __builtin_amdgcn_raw_buffer_load_b32(rv, (int)(voff + i * tok_bytes), 0, 0);
             }
         };
         // V^T goes to LDS as bf16 (exact path) or fp16 (fast path).  The fp16
@@ -360,16 +363,17 @@ prefill_kernel(PrefillArgs a) {
         // largest magnitude staged so that a workgroup that met a larger one
         // can redo its segment on the exact path.
         float vmax = 0.f;
-        auto commit = [&](int buf, auto half) {
+        auto commit = [&](int buf, auto half, auto set) {
             constexpr bool kHalf = decltype(half)::value;
+            constexpr int S = decltype(set)::value;
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
                 const int c = tid + j * kThreads;
-                *reinterpret_cast<u32x4_t*>(&k_lds[buf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[j];
+                *reinterpret_cast<u32x4_t*>(&k_lds[buf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[S][j];
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) {
-                const uint32_t* w = vw[j];
+                const uint32_t* w = vw[S][j];
                 u32x2_t even, odd;
                 if constexpr (kHalf) {
                     float e[4], o[4];
@@ -408,15 +412,23 @@ prefill_kernel(PrefillArgs a) {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
             bid_base = -kWave;
+            using Set0 = std::integral_constant<int, 0>;
+            using Set1 = std::integral_constant<int, 1>;
             if (kt_begin < kt_end) {
-                stage(kt_begin);
-                commit(0, half);
+                stage(kt_begin, Set0{});
+                commit(0, half, Set0{});
             }
+            if (kt_begin + 1 < kt_end) stage(kt_begin + 1, Set1{});
             __syncthreads();
 
-            for (int kt = kt_begin; kt < kt_end; ++kt) {
+            // One key tile.  Tile kt + 1 is already in staging set `held`; tile kt + 2
+            // is loaded into the other set now and committed at the end of the next
+            // tile, so each tile's loads have two tiles' time to arrive.
+            auto tile = [&](int kt, auto held) {
+                constexpr int A = decltype(held)::value;
+                using Other = std::integral_constant<int, 1 - A>;
                 const int buf = (kt - kt_begin) & 1;
-                if (kt + 1 < kt_end) stage(kt + 1);
+                if (kt + 2 < kt_end) stage(kt + 2, Other{});
                 const int key0 = kt * kKeys;
                 // S^T = K Q^T over this tile: 2 key tiles of 32 x 8 dim steps of 16.
                 // sacc[mt][4b + e] is the score of key 32mt + 8b + 4h + e.
@@ -536,8 +548,12 @@ prefill_kernel(PrefillArgs a) {
                                                                            oacc[dt], 0, 0, 0);
                     }
                 }
-                if (kt + 1 < kt_end) commit(buf ^ 1, half);
+                if (kt + 1 < kt_end) commit(buf ^ 1, half, held);
                 __syncthreads();
+            };
+            for (int kt = kt_begin; kt < kt_end; kt += 2) {
+                tile(kt, Set1{});
+                if (kt + 1 < kt_end) tile(kt + 1, Set0{});
             }
         };
 
