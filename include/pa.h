@@ -91,6 +91,24 @@ pa_status pa_slot_mapping(int64_t *slot_mapping, const int32_t *block_table,
                           int64_t num_tokens, int32_t block_size, hipStream_t stream);
 
 /*
+ * pa_slot_mapping followed by pa_reshape_and_cache, fused into one launch:
+ * the slots of the tokens are computed as pa_slot_mapping does and written to
+ * slot_mapping (for the scatters of the other layers of the step), and each
+ * token's K and V rows are scattered to them as pa_reshape_and_cache does.
+ * Arguments as in those two calls; the results are identical to calling them
+ * in turn.
+ */
+pa_status pa_slot_mapping_and_cache(int64_t *slot_mapping, const int32_t *block_table,
+                                    int32_t max_blocks_per_req, int32_t num_seqs,
+                                    const int32_t *token_seq, const int32_t *token_pos,
+                                    const void *key, int64_t key_token_stride,
+                                    const void *value, int64_t value_token_stride,
+                                    void *key_cache, void *value_cache,
+                                    int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                                    int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                    hipStream_t stream);
+
+/*
  * pa_reshape_and_cache -- the scatter of section "Paged Attention" /
  * "Reshape & Cache": for each token i with s = slot_mapping[i] >= 0, copy
  *   key[i, :, :]   -> key_cache[s / block_size, s % block_size, :, :]

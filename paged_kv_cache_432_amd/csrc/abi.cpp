@@ -245,6 +245,39 @@ pa_status pa_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
                       "slot_mapping launch");
 }
 
+pa_status pa_slot_mapping_and_cache(int64_t* slot_mapping, const int32_t* block_table, int32_t max_blocks_per_req,
+                                    int32_t num_seqs, const int32_t* token_seq, const int32_t* token_pos,
+                                    const void* key, int64_t key_token_stride, const void* value,
+                                    int64_t value_token_stride, void* key_cache, void* value_cache,
+                                    int64_t num_tokens, int64_t num_blocks, int32_t block_size, int32_t num_kv_heads,
+                                    int32_t head_dim, pa_dtype dtype, hipStream_t stream) {
+    if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
+    if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_seqs < 0 ||
+        max_blocks_per_req < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size");
+    if (num_tokens == 0) return ok();
+    if (!slot_mapping || !token_seq || !token_pos || !key || !value || !key_cache || !value_cache)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (num_seqs > 0 && max_blocks_per_req > 0 && !block_table) return fail(PA_ERR_INVALID_ARG, "null block_table");
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t row_bytes = row_elems * eb;
+    if (row_bytes % 16 != 0 || row_bytes > (1 << 30))
+        return fail(PA_ERR_UNSUPPORTED, "row of %lld bytes (must be a multiple of 16)", (long long)row_bytes);
+    if (key_token_stride < row_elems || value_token_stride < row_elems)
+        return fail(PA_ERR_INVALID_ARG, "token stride smaller than num_kv_heads * head_dim");
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        (key_token_stride * eb) % 16 || (value_token_stride * eb) % 16)
+        return fail(PA_ERR_INVALID_ARG, "rows must start on 16-byte boundaries");
+    if (num_tokens > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "num_tokens too large");
+    return hip_status(pa::launch_slot_and_cache(slot_mapping, block_table, max_blocks_per_req, num_seqs, token_seq,
+                                                token_pos, key, key_token_stride * eb, value,
+                                                value_token_stride * eb, key_cache, value_cache, num_tokens,
+                                                num_blocks * 16, (int32_t)row_bytes, stream),
+                      "slot_and_cache launch");
+}
+
 pa_status pa_reshape_and_cache(const void* key, int64_t key_token_stride, const void* value,
                                int64_t value_token_stride, void* key_cache, void* value_cache,
                                const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,

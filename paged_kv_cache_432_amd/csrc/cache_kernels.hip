@@ -250,6 +250,56 @@ hipError_t launch_rope_cache(const RopeArgs& a, int dtype, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// Slots and scatter in one launch: workgroup `token` loads its K and V row
+// chunks first, then works out the slot exactly as slot_mapping_kernel does
+// (the two loads' latencies overlap), thread 0 writes slot_mapping[token],
+// and the rows go to cache[slot / 16, slot % 16] as in
+// reshape_and_cache_kernel.  The row is at most 256 threads x 16 bytes per
+// half (K on threads 0-127, V on 128-255), so each thread holds up to two
+// chunks.
+__global__ void __launch_bounds__(256)
+slot_and_cache_kernel(int64_t* __restrict__ slot_out, const int32_t* __restrict__ block_table,
+                      int32_t bt_stride, int32_t num_seqs, const int32_t* __restrict__ token_seq,
+                      const int32_t* __restrict__ token_pos, const char* __restrict__ key,
+                      int64_t key_stride_bytes, const char* __restrict__ value, int64_t value_stride_bytes,
+                      char* __restrict__ key_cache, char* __restrict__ value_cache, int64_t num_slots,
+                      int32_t row_bytes) {
+    const int64_t token = blockIdx.x;
+    const bool is_v = threadIdx.x >= 128;
+    const int32_t t = threadIdx.x & 127;
+    const int32_t chunks = row_bytes >> 4;
+    const char* src = is_v ? value + token * value_stride_bytes : key + token * key_stride_bytes;
+    u32x4_t c0 = u32x4_t{0u, 0u, 0u, 0u}, c1 = c0;
+    if (t < chunks) c0 = *reinterpret_cast<const u32x4_t*>(src + ((int64_t)t << 4));
+    if (t + 128 < chunks) c1 = *reinterpret_cast<const u32x4_t*>(src + ((int64_t)(t + 128) << 4));
+    const int32_t sq = token_seq[token];
+    const int32_t p = token_pos[token];
+    int64_t slot = -1;
+    if (sq >= 0 && sq < num_seqs && p >= 0 && p / kBlock < bt_stride) {
+        const int32_t physical = block_table[(int64_t)sq * bt_stride + p / kBlock];
+        if (physical >= 0) slot = (int64_t)physical * kBlock + p % kBlock;
+    }
+    if (threadIdx.x == 0) slot_out[token] = slot;
+    if (slot < 0 || slot >= num_slots) return;
+    char* dst = (is_v ? value_cache : key_cache) + slot * (int64_t)row_bytes;
+    if (t < chunks) *reinterpret_cast<u32x4_t*>(dst + ((int64_t)t << 4)) = c0;
+    if (t + 128 < chunks) *reinterpret_cast<u32x4_t*>(dst + ((int64_t)(t + 128) << 4)) = c1;
+    for (int32_t c = t + 256; c < chunks; c += 128)   // rows longer than 4 KiB
+        *reinterpret_cast<u32x4_t*>(dst + ((int64_t)c << 4)) = *reinterpret_cast<const u32x4_t*>(src + ((int64_t)c << 4));
+}
+
+hipError_t launch_slot_and_cache(int64_t* slot_mapping, const int32_t* block_table, int32_t max_blocks_per_req,
+                                 int32_t num_seqs, const int32_t* token_seq, const int32_t* token_pos,
+                                 const void* key, int64_t key_stride_bytes, const void* value,
+                                 int64_t value_stride_bytes, void* key_cache, void* value_cache, int64_t num_tokens,
+                                 int64_t num_slots, int32_t row_bytes, hipStream_t stream) {
+    hipLaunchKernelGGL(slot_and_cache_kernel, dim3((unsigned)num_tokens), dim3(256), 0, stream, slot_mapping,
+                       block_table, max_blocks_per_req, num_seqs, token_seq, token_pos, (const char*)key,
+                       key_stride_bytes, (const char*)value, value_stride_bytes, (char*)key_cache,
+                       (char*)value_cache, num_slots, row_bytes);
+    return hipGetLastError();
+}
+
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
                                int32_t max_blocks_per_req, int32_t num_seqs,
                                const int32_t* token_seq, const int32_t* token_pos,

@@ -47,6 +47,13 @@ struct RopeArgs {
 };
 hipError_t launch_rope_cache(const RopeArgs& a, int dtype, hipStream_t stream);
 
+// Slots and the scatter in one launch (slot_and_cache_kernel).
+hipError_t launch_slot_and_cache(int64_t* slot_mapping, const int32_t* block_table, int32_t max_blocks_per_req,
+                                 int32_t num_seqs, const int32_t* token_seq, const int32_t* token_pos,
+                                 const void* key, int64_t key_stride_bytes, const void* value,
+                                 int64_t value_stride_bytes, void* key_cache, void* value_cache, int64_t num_tokens,
+                                 int64_t num_slots, int32_t row_bytes, hipStream_t stream);
+
 hipError_t launch_reshape_and_cache(const void* key, int64_t key_stride, const void* value,
                                     int64_t value_stride, void* key_cache, void* value_cache,
                                     const int64_t* slot_mapping, int64_t num_tokens,

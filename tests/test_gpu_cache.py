@@ -90,3 +90,51 @@ def test_step_scatter_tiny_writes_slot_137(pa):
     okc, ovc = oracle.build_cache(w, "all")
     assert np.array_equal(storage_bits(dw.key_cache).view(np.uint8), okc.view(np.uint8))
     assert np.array_equal(storage_bits(dw.value_cache).view(np.uint8), ovc.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("hkv", [8, 1, 2])
+def test_fused_slots_and_scatter_bit_exact(pa, dtype, hkv):
+    """pa_slot_mapping_and_cache: the slots equal the oracle's, and the caches
+    equal the oracle's scatter through them, bit for bit; tokens of padding
+    requests, past the table or on unallocated entries are skipped."""
+    rng = np.random.default_rng(40 + hkv)
+    nb, d, n, B, width = 40, 128, 200, 6, 8
+    table = np.full((B, width), -1, np.int32)
+    perm = rng.permutation(nb)
+    for b in range(B):
+        k = int(rng.integers(1, width))
+        table[b, :k] = perm[b * 6:b * 6 + k]
+    seq = rng.integers(-1, B + 1, n).astype(np.int32)           # -1 and B: no such request
+    pos = rng.integers(-2, width * 16 + 3, n).astype(np.int32)   # some past the table
+
+    def expected():
+        # the page's formula (the oracle) for tokens inside the table; the
+        # library's range checks give -1 to the others
+        inside = (seq >= 0) & (seq < B) & (pos >= 0) & (pos // 16 < width)
+        out = np.full(n, -1, np.int64)
+        out[inside] = oracle.slot_mapping(table, seq[inside], pos[inside])
+        return out
+
+    # distinct valid slots only: keep the first token of any duplicated slot
+    seen = set()
+    for i, s in enumerate(expected()):
+        if s >= 0 and s in seen:
+            seq[i] = -1
+        seen.add(int(s))
+    slots_o = expected()
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    kv = torch.randn(2, n, hkv, d, generator=torch.Generator().manual_seed(hkv)).to(tdt)
+    sentinel = torch.randn(nb, 16, hkv, d, generator=torch.Generator().manual_seed(7)).to(tdt)
+    dev = "cuda"
+    kc, vc = sentinel.clone().to(dev), (-sentinel).to(dev)
+    slots = torch.empty(n, dtype=torch.int64, device=dev)
+    pa.pa_slot_mapping_and_cache(slots, torch.from_numpy(table).to(dev), torch.from_numpy(seq).to(dev),
+                                 torch.from_numpy(pos).to(dev), kv[0].to(dev), kv[1].to(dev), kc, vc)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(), slots_o)
+    store = (lambda t: t.view(torch.int16).numpy().view(np.uint16)) if dtype == "bf16" else (lambda t: t.numpy())
+    okc, ovc = store(sentinel).copy(), store(-sentinel).copy()
+    oracle.reshape_and_cache(store(kv[0]), store(kv[1]), okc, ovc, slots_o)
+    assert np.array_equal(storage_bits(kc).view(np.uint8), okc.view(np.uint8))
+    assert np.array_equal(storage_bits(vc).view(np.uint8), ovc.view(np.uint8))
