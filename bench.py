@@ -58,6 +58,9 @@ def parse():
     p.add_argument("--partition-tokens", type=int, default=0)
     p.add_argument("--kv-cache", default="bf16", choices=["bf16", "fp8"],
                    help="fp8: the caches hold E4M3 codes (pa_reshape_and_cache_fp8 / pa_decode_fp8)")
+    p.add_argument("--step", default="append", choices=["append", "two-call"],
+                   help="append: the step is one pa_decode_append call (bf16/fp32 caches, stream mode); "
+                        "two-call: pa_slot_mapping_and_cache, then pa_decode")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probes", action="store_true")
     p.add_argument("--cpu-sample-seqs", type=int, default=16)
@@ -493,8 +496,9 @@ def main():
           file=sys.stderr, flush=True)
 
     stream = torch.cuda.current_stream()
+    append = args.step == "append" and not fp8 and pt == 0
 
-    def step(ev=None):
+    def two_call_step(ev=None):
         # slots and scatter of the step's tokens (one launch), then decode
         dw.scatter_new(stream, fused=True)
         if ev is not None:
@@ -502,6 +506,16 @@ def main():
         dw.decode(out, args.partition_tokens, ws, stream)
         if ev is not None:
             ev[1].record(stream)
+
+    def append_step(ev=None):
+        # the newest tokens written to the cache and attended to, in one call
+        if ev is not None:
+            ev[0].record(stream)
+        dw.decode_append(out, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    step = append_step if append else two_call_step
 
     for _ in range(args.warmup):
         step()
@@ -523,6 +537,17 @@ def main():
     torch.cuda.synchronize()
     dec_ms = np.array([a.elapsed_time(b) for a, b in events])
     dec_avg_ms = float(dec_ms.mean())
+    two_call_ms = None
+    if append:
+        # the same step as two calls, for comparison (same values rewritten)
+        for _ in range(args.warmup):
+            two_call_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            two_call_step()
+        torch.cuda.synchronize()
+        two_call_ms = (time.perf_counter() - t0) * 1e3 / args.steps
 
     kv = w.kv_bytes(1 if fp8 else None)
     gbps = kv / (ms_step * 1e-3) / 1e9
@@ -555,11 +580,15 @@ def main():
             "kv_bytes_per_step": kv,
             "kv_cache": "fp8 E4M3 (1 byte/element), k_scale = v_scale = %.6g" % w.fp8_scales()[0] if fp8
                         else w.dtype,
+            "step": "pa_decode_append (slots, scatter and decode in one call)" if append
+                    else "pa_slot_mapping_and_cache + " + ("pa_decode_fp8" if fp8 else "pa_decode"),
         },
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "roofline": {
             "kernel": "pa_decode_fp8: decode_stream_kernel<fp8> + merge_stream_kernel (one call)" if fp8
+                      else "pa_decode_append: decode_stream_kernel<append> + merge_stream_kernel (one call)"
+                      if append
                       else "pa_decode: decode_stream_kernel + merge_stream_kernel (one call)" if pt == 0
                       else "pa_decode: decode_partition_kernel + merge_partitions_kernel (one call)",
             "bound": "hbm",
@@ -573,6 +602,10 @@ def main():
             "algorithmic_bytes_per_launch": kv,
         },
     }
+    if two_call_ms is not None:
+        res["two_call_step"] = {"what": "pa_slot_mapping_and_cache + pa_decode, same inputs, after the timed steps",
+                                "ms_per_step": round(two_call_ms, 5),
+                                "GBps": round(kv / (two_call_ms * 1e-3) / 1e9, 2)}
     if probe is not None:
         res["probes"] = probe
         res["roofline"]["frac_of_read_probe"] = round(dec_gbps / probe["stream_read"]["GBps"], 4)

@@ -364,6 +364,44 @@ pa_status pa_decode(void *out, const void *query, int64_t q_token_stride,
                     pa_dtype dtype, hipStream_t stream);
 
 /*
+ * pa_decode_append -- one decode step of sections "Paged Attention" and
+ * "Reshape & Cache" in one call: each sequence's newest token (position
+ * seq_lens[b] - 1) is written into the paged cache and then attended to
+ * with the rest of the sequence.  The results are those of
+ *   pa_slot_mapping_and_cache(slot_mapping, block_table, ..., token_seq = b,
+ *                             token_pos = seq_lens[b] - 1, key, value, ...)
+ * followed by pa_decode(..., partition_tokens = 0, ...): slot_mapping and the
+ * caches bit for bit, out within the rounding of pa_decode (the newest token's
+ * term is added in another order).  On bf16 with at most 4096 sequences it is
+ * one decode launch (plus the split merge): attention reads the newest token
+ * from its input row, and the same launch writes that row to its cache slot,
+ * which no workgroup of the launch reads.  Otherwise (fp32, more sequences)
+ * the scatter and pa_decode run one after the other.
+ *
+ * key, value    [num_seqs, num_kv_heads, head_dim]: row b is the newest token
+ *               of sequence b; rows key_token_stride / value_token_stride
+ *               ELEMENTS apart, 16-byte aligned.  Rows of sequences with
+ *               seq_lens[b] <= 0 are not read.
+ * slot_mapping  out, int64 [num_seqs] (may be NULL): the newest token's slot,
+ *               or -1 where the request has no block for it (then nothing is
+ *               written for that token), for the scatters of the other layers.
+ * key_cache, value_cache  written at those slots only.
+ * Other arguments as for pa_decode; the workspace is
+ * pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
+ * max_seq_len, 0) bytes.  seq_lens[b] counts the newest token.
+ */
+pa_status pa_decode_append(void *out, const void *query, int64_t q_token_stride,
+                           const void *key, int64_t key_token_stride,
+                           const void *value, int64_t value_token_stride,
+                           void *key_cache, void *value_cache, int64_t *slot_mapping,
+                           const int32_t *block_table, int32_t max_blocks_per_req,
+                           const int32_t *seq_lens, int32_t num_seqs,
+                           int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t block_size, int64_t num_blocks, float scale,
+                           int32_t max_seq_len, void *workspace, size_t workspace_bytes,
+                           pa_dtype dtype, hipStream_t stream);
+
+/*
  * pa_chunked_prefill -- attention of a mixed batch in one call: chunks of
  * query_len >= 2 rows (chunked prefill) next to single-row decodes, all
  * reading K/V from the paged cache after this step's rows were scattered

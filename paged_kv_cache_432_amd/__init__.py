@@ -20,7 +20,7 @@ __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
     "pa_slot_mapping", "pa_reshape_and_cache", "pa_slot_mapping_and_cache", "pa_rope_reshape_and_cache", "pa_reshape_and_cache_fp8",
     "pa_decode_fp8", "pa_copy_blocks", "KvManager", "pa_decode_workspace_bytes",
-    "pa_decode_partition_tokens", "pa_decode", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
+    "pa_decode_partition_tokens", "pa_decode", "pa_decode_append", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
     "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
 ]
 
@@ -121,6 +121,10 @@ def lib():
         L.pa_decode.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                 _i32, _i64, ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t,
                                 ctypes.c_int, _vp]
+        L.pa_decode_append.restype = ctypes.c_int
+        L.pa_decode_append.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                       _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _vp, ctypes.c_size_t,
+                                       ctypes.c_int, _vp]
         L.pa_chunked_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.pa_chunked_prefill_workspace_bytes.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32]
         L.pa_chunked_prefill.restype = ctypes.c_int
@@ -472,6 +476,46 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
                         0 if ws is None else ws.numel() * ws.element_size(), _dtype_code(query),
                         _stream(stream, out.device))
     _check(s, "pa_decode")
+    return out
+
+
+def pa_decode_append(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                     key_cache: torch.Tensor, value_cache: torch.Tensor, block_table: torch.Tensor,
+                     seq_lens: torch.Tensor, scale: float, max_seq_len: int, slot_mapping: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step: row b of key/value [B, Hkv, D] (sequence b's newest token,
+    at position seq_lens[b] - 1) is written into the caches and attended to with
+    the rest of the sequence; out [B, Hq, D].  slot_mapping (int64 [B], optional)
+    receives the newest tokens' slots."""
+    _need(query.dim() == 3 and out.shape == query.shape and out.is_contiguous(),
+          "query/out: [num_seqs, num_heads, head_dim], out contiguous")
+    _need(query.stride(2) == 1 and query.stride(1) == query.shape[2], "query heads/dims must be contiguous")
+    _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
+    _need(query.dtype == out.dtype == key.dtype == value.dtype == key_cache.dtype == value_cache.dtype,
+          "dtype mismatch")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
+          "block_table: contiguous int32 [num_seqs, max_blocks_per_req]")
+    _need(seq_lens.dtype == torch.int32 and seq_lens.is_contiguous(), "seq_lens: contiguous int32")
+    b, hq, d = query.shape
+    nb, bs, hkv, _ = key_cache.shape
+    _need(block_table.shape[0] >= b and seq_lens.numel() >= b, "block_table/seq_lens shorter than batch")
+    _need(key.dim() == 3 and value.dim() == 3 and key.shape[0] >= b and value.shape[0] >= b and
+          tuple(key.shape[1:]) == (hkv, d) and tuple(value.shape[1:]) == (hkv, d),
+          "key/value: [num_seqs, num_kv_heads, head_dim]")
+    _need(key.stride(2) == 1 and key.stride(1) == d and value.stride(2) == 1 and value.stride(1) == d,
+          "key/value heads and dims must be contiguous")
+    if slot_mapping is not None:
+        _need(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous() and slot_mapping.numel() >= b,
+              "slot_mapping: contiguous int64 [num_seqs]")
+    ws = workspace
+    s = lib().pa_decode_append(_ptr(out), _ptr(query), query.stride(0), _ptr(key), key.stride(0), _ptr(value),
+                               value.stride(0), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping),
+                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens), b, hq, hkv, d, bs, nb,
+                               float(scale), int(max_seq_len), _ptr(ws),
+                               0 if ws is None else ws.numel() * ws.element_size(), _dtype_code(query),
+                               _stream(stream, out.device))
+    _check(s, "pa_decode_append")
     return out
 
 

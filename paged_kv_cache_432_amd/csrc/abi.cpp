@@ -419,7 +419,7 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
     if (use_stream(num_seqs, partition_tokens)) {
         const int32_t group = num_heads / num_kv_heads;
         size_t bytes = 0;
-        for (int dtype = 0; dtype < 3; ++dtype) {          // the largest of the layouts (fp32, bf16, fp8 cache)
+        for (int dtype = 0; dtype < 4; ++dtype) {          // the largest of the layouts (fp32, bf16, fp8 cache, append)
             const size_t n = stream_ws_bytes(num_seqs, num_heads, num_kv_heads,
                                              stream_shape(dtype, group, num_kv_heads, num_seqs));
             bytes = n > bytes ? n : bytes;
@@ -441,8 +441,11 @@ pa_status decode_common(void* out, const void* query, int64_t q_token_stride, co
                         const int32_t* seq_lens, const int32_t* cu_q, int32_t num_seqs, int32_t num_heads,
                         int32_t num_kv_heads, int64_t num_blocks, float scale, int32_t max_seq_len,
                         int32_t partition_tokens, void* workspace, size_t workspace_bytes, int dt, float k_scale,
-                        float v_scale, hipStream_t stream) {
-    // dt: 0 fp32, 1 bf16, 2 fp8 cache (bf16 query and output, stream mode only)
+                        float v_scale, hipStream_t stream, const void* new_key = nullptr,
+                        int64_t new_key_stride_bytes = 0, const void* new_value = nullptr,
+                        int64_t new_value_stride_bytes = 0, int64_t* slot_out = nullptr) {
+    // dt: 0 fp32, 1 bf16, 2 fp8 cache (bf16 query and output, stream mode only),
+    // 3 bf16 in append mode (stream mode only; the new_* rows and slot_out)
     const int32_t group = num_heads / num_kv_heads;
     pa::DecodeArgs a{};
     a.out = out;
@@ -460,6 +463,11 @@ pa_status decode_common(void* out, const void* query, int64_t q_token_stride, co
     a.scale_log2 = (float)((double)scale * (double)k_scale * 1.4426950408889634);
     a.out_scale = v_scale;
     a.cu_q = cu_q;
+    a.new_key = static_cast<const char*>(new_key);
+    a.new_value = static_cast<const char*>(new_value);
+    a.new_key_stride = new_key_stride_bytes;
+    a.new_value_stride = new_value_stride_bytes;
+    a.slot_out = slot_out;
 
     size_t need = 0;
     if (use_stream(num_seqs, partition_tokens)) {
@@ -572,6 +580,55 @@ pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const 
     return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
                          seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len,
                          partition_tokens, workspace, workspace_bytes, dtype == PA_BF16 ? 1 : 0, 1.f, 1.f, stream);
+}
+
+pa_status pa_decode_append(void* out, const void* query, int64_t q_token_stride, const void* key,
+                           int64_t key_token_stride, const void* value, int64_t value_token_stride, void* key_cache,
+                           void* value_cache, int64_t* slot_mapping, const int32_t* block_table,
+                           int32_t max_blocks_per_req, const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int64_t num_blocks,
+                           float scale, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                           pa_dtype dtype, hipStream_t stream) {
+    if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
+    const pa_status hs = check_heads(num_heads, num_kv_heads, head_dim, block_size);
+    if (hs != PA_OK) return hs;
+    if (num_seqs < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_req < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative size");
+    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
+        return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
+    if (num_seqs == 0) return ok();
+    if (num_blocks == 0 && max_seq_len > 0) return fail(PA_ERR_INVALID_ARG, "empty cache pool");
+    if (!out || !query || !seq_lens || !key || !value || !key_cache || !value_cache ||
+        (max_seq_len > 0 && !block_table))
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    const int64_t eb = elem_bytes(dtype);
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    if (q_token_stride < (int64_t)num_heads * head_dim)
+        return fail(PA_ERR_INVALID_ARG, "q_token_stride smaller than num_heads * head_dim");
+    if (key_token_stride < row_elems || value_token_stride < row_elems)
+        return fail(PA_ERR_INVALID_ARG, "key/value token stride smaller than num_kv_heads * head_dim");
+    if (!aligned16(query) || (q_token_stride * eb) % 16 || !aligned16(out) || !aligned16(key_cache) ||
+        !aligned16(value_cache) || !aligned16(key) || !aligned16(value) || (key_token_stride * eb) % 16 ||
+        (value_token_stride * eb) % 16)
+        return fail(PA_ERR_INVALID_ARG, "query/out/key/value/cache rows must start on 16-byte boundaries");
+    if (dtype == PA_BF16 && use_stream(num_seqs, 0))
+        return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
+                             seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len, 0,
+                             workspace, workspace_bytes, 3, 1.f, 1.f, stream, key, key_token_stride * eb, value,
+                             value_token_stride * eb, slot_mapping);
+    // fp32, or more sequences than the stream mode takes: the newest rows are
+    // scattered first (token b of sequence b at position seq_lens[b] - 1), then
+    // the plain decode reads them from the cache
+    const pa_status st = hip_status(
+        pa::launch_slot_and_cache(slot_mapping, block_table, max_blocks_per_req, num_seqs, nullptr, seq_lens, key,
+                                  key_token_stride * eb, value, value_token_stride * eb, key_cache, value_cache,
+                                  num_seqs, num_blocks * 16, (int32_t)(row_elems * eb), stream),
+        "slot_and_cache launch");
+    if (st != PA_OK) return st;
+    return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
+                         seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len, 0,
+                         workspace, workspace_bytes, dtype == PA_BF16 ? 1 : 0, 1.f, 1.f, stream);
 }
 
 size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,

@@ -272,14 +272,16 @@ slot_and_cache_kernel(int64_t* __restrict__ slot_out, const int32_t* __restrict_
     u32x4_t c0 = u32x4_t{0u, 0u, 0u, 0u}, c1 = c0;
     if (t < chunks) c0 = *reinterpret_cast<const u32x4_t*>(src + ((int64_t)t << 4));
     if (t + 128 < chunks) c1 = *reinterpret_cast<const u32x4_t*>(src + ((int64_t)(t + 128) << 4));
-    const int32_t sq = token_seq[token];
-    const int32_t p = token_pos[token];
+    // token_seq null: token i is the newest token of sequence i, at position
+    // token_pos[i] - 1 (token_pos then holds the sequence lengths)
+    const int32_t sq = token_seq ? token_seq[token] : (int32_t)token;
+    const int32_t p = token_seq ? token_pos[token] : token_pos[token] - 1;
     int64_t slot = -1;
     if (sq >= 0 && sq < num_seqs && p >= 0 && p / kBlock < bt_stride) {
         const int32_t physical = block_table[(int64_t)sq * bt_stride + p / kBlock];
         if (physical >= 0) slot = (int64_t)physical * kBlock + p % kBlock;
     }
-    if (threadIdx.x == 0) slot_out[token] = slot;
+    if (threadIdx.x == 0 && slot_out) slot_out[token] = slot;
     if (slot < 0 || slot >= num_slots) return;
     char* dst = (is_v ? value_cache : key_cache) + slot * (int64_t)row_bytes;
     if (t < chunks) *reinterpret_cast<u32x4_t*>(dst + ((int64_t)t << 4)) = c0;

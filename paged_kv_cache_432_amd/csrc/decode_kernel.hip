@@ -601,6 +601,9 @@ __device__ __forceinline__ int seq_len_of(const DecodeArgs& a, int64_t b) {
 // and slot 1 for its last) and starts the next with its blocks in flight.
 constexpr int kShareTable = 1024;
 constexpr int kFirstBlock = 1 << 30;                  // table flag: block 0 of its sequence
+// Table flag (append mode): the unit is the sequence's newest token, read from
+// its input row (the unit's id field holds the row) as a one-token block.
+constexpr int kAppendUnit = 0x80;
 
 // One block's K and V rows of one KV head as a lane holds them in flight.
 // bf16: K dims 32ks + 8g .. +8 of token i for product step ks; V dims 8i .. +8
@@ -628,7 +631,7 @@ __device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
 }
 
-template <int G, bool NT, int NBUF, bool F8 = false>
+template <int G, bool NT, int NBUF, bool F8 = false, bool AP = false>
 __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int32_t* s_pref, int4* s_tab, int64_t u0,
                                                   int64_t u1, int W, int NG, int wi, int lane) {
     const int total = (int)(u1 - u0);                  // the same for every wave of the workgroup
@@ -646,24 +649,36 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
 
     int c0 = 0, c1 = 0;                                // the table holds blocks [c0, c1)
     // the table entry of block j in [c0, c1), the same address in every lane
-    auto entry = [&](int j, int& id, int& valid, int& grp) {
+    auto entry = [&](int j, int& id, int& valid, int& grp, bool& app) {
         const int2 e = *reinterpret_cast<const int2*>(&s_tab[j - c0]);
         id = __builtin_amdgcn_readfirstlane(e.x);
         const int vg = __builtin_amdgcn_readfirstlane(e.y);
-        valid = vg & 0xff;
+        valid = vg & (AP ? kAppendUnit - 1 : 0xff);
+        app = AP && (vg & kAppendUnit) != 0;
         grp = vg >> 8;
     };
 
     auto issue = [&](KvBuf<F8>& buf, int j) {
         int id = 0, valid = 0, grp = 0;
-        if (j < c1) entry(j, id, valid, grp);
+        bool app = false;
+        if (j < c1) entry(j, id, valid, grp, app);
         const int64_t phys = min(max((int64_t)id, (int64_t)0), a.num_blocks - 1);   // an id outside the pool: clamped
         // the resource spans the block's valid rows: past-the-end slots and
         // blocks past the table read as zeros without touching memory
-        const int nrec = valid * (int)tok_bytes;
-        const int64_t off = phys * (int64_t)blk_bytes + (int64_t)(grp * W + wi) * kHeadDim * kEb;
-        const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
-        const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
+        int nrec = valid * (int)tok_bytes;
+        const int64_t hoff = (int64_t)(grp * W + wi) * kHeadDim * kEb;
+        const int64_t off = phys * (int64_t)blk_bytes + hoff;
+        const char* kb = kc + off;
+        const char* vb = vc + off;
+        if constexpr (AP) {
+            // the newest token: its input row is token 0 of a one-token block
+            // (lanes of the other tokens read past the 256 bytes: zeros)
+            kb = app ? a.new_key + id * a.new_key_stride + hoff : kb;
+            vb = app ? a.new_value + id * a.new_value_stride + hoff : vb;
+            nrec = app ? kHeadDim * kEb : nrec;
+        }
+        const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)kb, (short)0, nrec, kRsrcWord3);
+        const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)vb, (short)0, nrec, kRsrcWord3);
         if constexpr (F8) {
 #pragma unroll
             for (int h = 0; h < 2; ++h)
@@ -755,7 +770,8 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
             start_segment(j);
         }
         int id, valid, grp;
-        entry(j, id, valid, grp);
+        bool app;
+        entry(j, id, valid, grp, app);
         const int nval = valid - 4 * g;                // this lane's tokens 4g .. 4g+3 of the block
         u32x4_t kb[4], vb[4];
         if constexpr (F8) {
@@ -801,9 +817,17 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
             const int nb = s_pref[lo + 1] - s_pref[lo];
             const int64_t r = u - (int64_t)NG * s_pref[lo];
             const int grp = (int)(r / nb), blk = (int)(r % nb);
-            const int id = a.block_table[(int64_t)lo * a.bt_stride + blk];
-            const int valid = min(max(seq_len_of(a, lo) - blk * kBlock, 0), kBlock);
             const int row = (int)decode_row(a, lo);    // >= 0: only decode rows own blocks
+            int id, valid;
+            if (AP && blk == nb - 1) {
+                // the newest token, from input row `row` (= lo)
+                id = row;
+                valid = 1 | kAppendUnit;
+            } else {
+                // in append mode the cached blocks hold the tokens before the newest
+                id = a.block_table[(int64_t)lo * a.bt_stride + blk];
+                valid = min(max(seq_len_of(a, lo) - (AP ? 1 : 0) - blk * kBlock, 0), kBlock);
+            }
             s_tab[t] = int4{id, valid | (grp << 8), row, (nb - blk) | (blk == 0 ? kFirstBlock : 0)};
         }
         __syncthreads();
@@ -880,7 +904,10 @@ __device__ __forceinline__ int64_t partition_record(const DecodeArgs& a, int64_t
 
 // ---- balanced stream mode --------------------------------------------------
 // Number of blocks per KV head of each sequence, as an inclusive prefix in
-// s_pref[0..B] (s_pref[0] = 0); computed by the whole workgroup.
+// s_pref[0..B] (s_pref[0] = 0); computed by the whole workgroup.  Append mode
+// (AP): the cached blocks of the L - 1 tokens before the newest, plus one unit
+// for the newest token.
+template <bool AP = false>
 __device__ __forceinline__ void block_prefix(const DecodeArgs& a, int32_t* s_pref, int32_t* s_wsum) {
     const int B = a.num_seqs;
     const int nthr = blockDim.x;
@@ -889,7 +916,9 @@ __device__ __forceinline__ void block_prefix(const DecodeArgs& a, int32_t* s_pre
     const int lo = min(tid * per, B), hi = min(lo + per, B);
     int sum = 0;
     for (int i = lo; i < hi; ++i) {
-        const int n = decode_row(a, i) < 0 ? 0 : (seq_len_of(a, i) + kBlock - 1) / kBlock;
+        const int L = seq_len_of(a, i);
+        const int n = decode_row(a, i) < 0 ? 0 : AP ? (L > 0 ? (L - 1 + kBlock - 1) / kBlock + 1 : 0)
+                                                    : (L + kBlock - 1) / kBlock;
         s_pref[i + 1] = n;
         sum += n;
     }
@@ -918,8 +947,38 @@ __device__ __forceinline__ int64_t stream_quantum(const DecodeArgs& a, int64_t u
     return q > a.min_quantum ? q : (int64_t)a.min_quantum;
 }
 
+// Append mode: sequence b's newest token (position seq_lens[b] - 1) as the
+// bf16 row b of new_key / new_value: it is written to its slot of the caches,
+// and the slot to slot_out[b], with the slot rule of the page-table lookup
+// (-1 when the request has no block for that position: nothing is written).
+// No workgroup of the launch reads that slot, so the writes may land at any
+// time in it; each workgroup writes the rows b = blockIdx.x (mod grid) when its
+// attention is done.
+__device__ __forceinline__ void append_rows(const DecodeArgs& a) {
+    const int64_t row_bytes = (int64_t)a.num_kv_heads * kHeadDim * 2;
+    const int chunks = (int)(row_bytes >> 4);
+    const int half = (int)blockDim.x >> 1;
+    const bool is_v = (int)threadIdx.x >= half;
+    const int t = (int)threadIdx.x - (is_v ? half : 0);
+    for (int b = blockIdx.x; b < a.num_seqs; b += gridDim.x) {
+        const int p = a.seq_lens[b] - 1;
+        int64_t slot = -1;
+        if (p >= 0 && p / kBlock < a.bt_stride) {
+            const int32_t physical = a.block_table[(int64_t)b * a.bt_stride + p / kBlock];
+            if (physical >= 0) slot = (int64_t)physical * kBlock + p % kBlock;
+        }
+        if (threadIdx.x == 0 && a.slot_out) a.slot_out[b] = slot;
+        if (slot < 0 || slot >= a.num_blocks * kBlock) continue;
+        const char* src = is_v ? a.new_value + b * a.new_value_stride : a.new_key + b * a.new_key_stride;
+        char* dst = reinterpret_cast<char*>(const_cast<void*>(is_v ? a.value_cache : a.key_cache)) + slot * row_bytes;
+        for (int c = t; c < chunks; c += half)
+            *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * 16);
+    }
+}
+
 // F8: the caches hold fp8 (E4M3) codes; query and output stay bf16.
-template <typename Chunk, typename Elem, int G, bool QL, bool NT, bool F8 = false>
+// AP: append mode (bf16 matrix-core path only).
+template <typename Chunk, typename Elem, int G, bool QL, bool NT, bool F8 = false, bool AP = false>
 __global__ void __launch_bounds__(512)
 decode_stream_kernel(DecodeArgs a) {
     extern __shared__ __attribute__((aligned(16))) int32_t s_pref[];          // [num_seqs + 1]
@@ -928,7 +987,7 @@ decode_stream_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float p_lds[MF ? 1 : 8][MF ? 4 : kBlock * G];
     __shared__ __attribute__((aligned(16))) Elem q_lds[QL && !MF ? 8 : 1][QL && !MF ? G * kHeadDim : 8];
     __shared__ int4 s_tab[MF ? kShareTable : 1];
-    block_prefix(a, s_pref, s_wsum);
+    block_prefix<AP>(a, s_pref, s_wsum);
     const int B = a.num_seqs;
     const int W = a.waves_per_group;
     const int NG = a.num_kv_heads / W;
@@ -941,8 +1000,10 @@ decode_stream_kernel(DecodeArgs a) {
     const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     float* pl = p_lds[MF ? 0 : wi];
+    static_assert(!AP || (MF && !F8), "append mode: bf16 matrix-core path");
     if constexpr (MF) {
-        stream_share_mfma<G, NT, F8 ? kFp8Depth : kMfmaDepth, F8>(a, s_pref, s_tab, u0, u1, W, NG, wi, lane);
+        stream_share_mfma<G, NT, F8 ? kFp8Depth : kMfmaDepth, F8, AP>(a, s_pref, s_tab, u0, u1, W, NG, wi, lane);
+        if constexpr (AP) append_rows(a);
         return;
     }
 
@@ -1119,12 +1180,12 @@ merge_stream_kernel(DecodeArgs a) {
 
 
 
-template <typename Chunk, typename Elem, int G, bool F8 = false>
+template <typename Chunk, typename Elem, int G, bool F8 = false, bool AP = false>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     constexpr bool QL = kQueryInLds<G>;
     if (a.mode == kDecodeStream) {
         const size_t lds = sizeof(int32_t) * ((size_t)a.num_seqs + 1);
-        hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, true, F8>), dim3((unsigned)a.num_wg),
+        hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, true, F8, AP>), dim3((unsigned)a.num_wg),
                            dim3(64 * a.waves_per_group), lds, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1134,7 +1195,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
                            stream, a);
         return hipGetLastError();
     }
-    if constexpr (F8) return hipErrorInvalidValue;       // an fp8 cache is read in the stream mode only
+    if constexpr (F8 || AP) return hipErrorInvalidValue; // an fp8 cache and append mode: stream mode only
     const int64_t items = (int64_t)a.num_seqs * a.max_partitions * a.num_kv_heads;
     const int64_t grid = (items + kWavesPerGroup - 1) / kWavesPerGroup;
     hipLaunchKernelGGL((decode_partition_kernel<Chunk, Elem, G, QL, true>), dim3((unsigned)grid), dim3(256), 0,
@@ -1147,41 +1208,43 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename Chunk, typename Elem, bool F8 = false>
+template <typename Chunk, typename Elem, bool F8 = false, bool AP = false>
 hipError_t launch_group(const DecodeArgs& a, int group, hipStream_t stream) {
     switch (group) {
-        case 1: return launch_typed<Chunk, Elem, 1, F8>(a, stream);
-        case 2: return launch_typed<Chunk, Elem, 2, F8>(a, stream);
-        case 4: return launch_typed<Chunk, Elem, 4, F8>(a, stream);
-        case 8: return launch_typed<Chunk, Elem, 8, F8>(a, stream);
+        case 1: return launch_typed<Chunk, Elem, 1, F8, AP>(a, stream);
+        case 2: return launch_typed<Chunk, Elem, 2, F8, AP>(a, stream);
+        case 4: return launch_typed<Chunk, Elem, 4, F8, AP>(a, stream);
+        case 8: return launch_typed<Chunk, Elem, 8, F8, AP>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename Chunk, typename Elem, int G, bool F8>
+template <typename Chunk, typename Elem, int G, bool F8, bool AP>
 int stream_blocks_per_cu(int waves_per_group, size_t lds) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, true, F8>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, true, F8, AP>,
                                                      64 * waves_per_group, lds) != hipSuccess)
         return 0;
     return n;
 }
 
-template <typename Chunk, typename Elem, bool F8 = false>
+template <typename Chunk, typename Elem, bool F8 = false, bool AP = false>
 int stream_blocks_group(int group, int waves_per_group, size_t lds) {
     switch (group) {
-        case 1: return stream_blocks_per_cu<Chunk, Elem, 1, F8>(waves_per_group, lds);
-        case 2: return stream_blocks_per_cu<Chunk, Elem, 2, F8>(waves_per_group, lds);
-        case 4: return stream_blocks_per_cu<Chunk, Elem, 4, F8>(waves_per_group, lds);
-        case 8: return stream_blocks_per_cu<Chunk, Elem, 8, F8>(waves_per_group, lds);
+        case 1: return stream_blocks_per_cu<Chunk, Elem, 1, F8, AP>(waves_per_group, lds);
+        case 2: return stream_blocks_per_cu<Chunk, Elem, 2, F8, AP>(waves_per_group, lds);
+        case 4: return stream_blocks_per_cu<Chunk, Elem, 4, F8, AP>(waves_per_group, lds);
+        case 8: return stream_blocks_per_cu<Chunk, Elem, 8, F8, AP>(waves_per_group, lds);
         default: return 0;
     }
 }
 
 }  // namespace
 
-// dtype: 0 fp32, 1 bf16, 2 fp8 (E4M3) cache with bf16 query and output.
+// dtype: 0 fp32, 1 bf16, 2 fp8 (E4M3) cache with bf16 query and output, 3 bf16
+// in append mode.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t stream) {
+    if (dtype == 3) return launch_group<ChunkBF16, uint16_t, false, true>(a, group, stream);
     if (dtype == 2) return launch_group<ChunkBF16, uint16_t, true>(a, group, stream);
     if (dtype == 1) return launch_group<ChunkBF16, uint16_t>(a, group, stream);
     return launch_group<ChunkF32, float>(a, group, stream);
@@ -1189,6 +1252,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t 
 
 int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int num_seqs) {
     const size_t lds = sizeof(int32_t) * ((size_t)num_seqs + 1);
+    if (dtype == 3) return stream_blocks_group<ChunkBF16, uint16_t, false, true>(group, waves_per_group, lds);
     if (dtype == 2) return stream_blocks_group<ChunkBF16, uint16_t, true>(group, waves_per_group, lds);
     if (dtype == 1) return stream_blocks_group<ChunkBF16, uint16_t>(group, waves_per_group, lds);
     return stream_blocks_group<ChunkF32, float>(group, waves_per_group, lds);

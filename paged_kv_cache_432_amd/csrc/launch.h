@@ -93,6 +93,15 @@ struct DecodeArgs {
     int32_t* prefix;               // [num_seqs + 1] blocks-per-KV-head prefix (written, then read)
     // partial records (split sequences only)
     float* part;
+    // Append mode (bf16 stream decode, internal dtype 3): sequence b's newest
+    // token, at position seq_lens[b] - 1, enters the attention from row b of
+    // new_key / new_value instead of from the cache, and the same launch writes
+    // that row to its cache slot (and the slot to slot_out[b], if set).
+    const char* new_key;           // [num_seqs] rows of num_kv_heads * 128 bf16
+    const char* new_value;
+    int64_t new_key_stride;        // bytes between rows
+    int64_t new_value_stride;
+    int64_t* slot_out;             // [num_seqs] or null
     // Mixed batches: when set, [num_seqs + 1] offsets of each sequence's query
     // rows; only sequences with exactly one query row are attended (their row
     // and output row are cu_q[b]), the others are left to the prefill kernel.
@@ -128,7 +137,8 @@ struct PrefillArgs {
                                    // the first slot) << 24, first row, (tokens << 8) | KV head
 };
 
-// dtype: 0 = fp32, 1 = bf16.  group = num_heads / num_kv_heads in {1,2,4,8}.
+// dtype: 0 = fp32, 1 = bf16, 2 = fp8 cache (bf16 query and output), 3 = bf16
+// in append mode.  group = num_heads / num_kv_heads in {1,2,4,8}.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t stream);
 
 // Workgroups of the stream-mode decode kernel one compute unit holds at once.
@@ -136,8 +146,14 @@ int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int n
 
 // Attention of every sequence with two or more query rows (bf16 only).
 hipError_t launch_prefill(const PrefillArgs& a, int group, hipStream_t stream);
+// Waves per prefill workgroup (4 or 8), each owning 32 query rows.
+#ifndef PA_PREFILL_WAVES
+#define PA_PREFILL_WAVES 8
+#endif
+constexpr int kPrefillWaves = PA_PREFILL_WAVES;
+static_assert(kPrefillWaves == 4 || kPrefillWaves == 8, "prefill waves");
 // Query rows (tokens x grouped heads) per prefill workgroup tile.
-constexpr int kPrefillRows = 256;
+constexpr int kPrefillRows = 32 * kPrefillWaves;
 // Prefill workgroups one compute unit holds at once (bf16, group size G).
 int prefill_blocks_per_cu(int group, int num_seqs);
 

@@ -65,7 +65,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-constexpr int kWaves = 8;
+constexpr int kWaves = kPrefillWaves;
 constexpr int kRowsPerWave = 32;
 static_assert(kWaves * kRowsPerWave == kPrefillRows, "tile rows");
 constexpr int kKeys = 64;                    // keys per K/V tile
@@ -74,6 +74,16 @@ constexpr int kVStride = kKeys + 4;          // bf16 per V^T row in LDS (136 B)
 constexpr int kKTileElems = kKeys * kKStride;
 constexpr int kVTileElems = kHeadDim * kVStride;
 constexpr int kThreads = kWaves * kWave;
+// Thread groups of 256: each stages one 16-token block of a K/V tile per step,
+// so every thread stages kBlkPerThr of the tile's 4 blocks.
+constexpr int kThrGroups = kThreads / 256;
+constexpr int kBlkPerThr = 4 / kThrGroups;
+// Sets of staging registers: with two, a tile's loads are issued two tiles
+// before its commit; with one (the 4-wave workgroup, whose threads stage twice
+// the blocks), one tile before.
+constexpr int kStageSets = kThrGroups == 2 ? 2 : 1;
+// Merge workgroups per listed tile (64 rows each).
+constexpr int kMergeParts = kPrefillRows / 64;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
 __device__ __forceinline__ f16x8_t as_f16x8(u32x4_t w) { return __builtin_bit_cast(f16x8_t, w); }
@@ -221,7 +231,7 @@ __device__ __forceinline__ int find_seq(const int32_t* pref, int B, int x) {
 }
 
 template <int G>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2)))
 prefill_kernel(PrefillArgs a) {
     constexpr int TQ = kPrefillRows / G;               // tokens per tile
     extern __shared__ __attribute__((aligned(16))) int32_t s_dyn[];
@@ -326,8 +336,8 @@ prefill_kernel(PrefillArgs a) {
         const uint32_t voff = 4 * (kq & 3) * tok_bytes + head_off + dp * 4;
         // two sets of staging registers: a tile's loads are issued two tiles
         // before its commit, the set chosen at compile time (see run)
-        u32x4_t kreg[2][2];
-        uint32_t vw[2][2][4];
+        u32x4_t kreg[kStageSets][kBlkPerThr];
+        uint32_t vw[kStageSets][kBlkPerThr][4];
         // Block ids of the key range, 64 at a time (one per lane), broadcast with
         // v_readlane, so that the tile's 10 loads issue back to back instead of
         // each waiting on its own table read.
@@ -345,8 +355,8 @@ prefill_kernel(PrefillArgs a) {
                 bid = bid_base + lane < nblk_wg ? bt[bid_base + lane] : 0;
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int blk = 4 * kt + w4 + 2 * j;
+            for (int j = 0; j < kBlkPerThr; ++j) {
+                const int blk = 4 * kt + w4 + kThrGroups * j;
                 const int64_t off = block_of(blk) * blk_bytes;
                 const int nrec = __builtin_amdgcn_readfirstlane(min(max(kend_wg - blk * kBlock, 0), kBlock) * (int)tok_bytes);
                 const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
@@ -367,12 +377,12 @@ prefill_kernel(PrefillArgs a) {
             constexpr bool kHalf = decltype(half)::value;
             constexpr int S = decltype(set)::value;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < kBlkPerThr; ++j) {
                 const int c = tid + j * kThreads;
                 *reinterpret_cast<u32x4_t*>(&k_lds[buf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[S][j];
             }
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < kBlkPerThr; ++j) {
                 const uint32_t* w = vw[S][j];
                 u32x2_t even, odd;
                 if constexpr (kHalf) {
@@ -391,7 +401,7 @@ prefill_kernel(PrefillArgs a) {
                 }
                 // 4-key run q of V^T row d sits at run q ^ ((d >> 4) & 1): the 16
                 // rows 2dp a write instruction covers per cycle then span all banks
-                uint16_t* vt = &v_lds[buf][(2 * dp) * kVStride + 4 * ((kq + 8 * j) ^ ((dp >> 3) & 1))];
+                uint16_t* vt = &v_lds[buf][(2 * dp) * kVStride + 4 * ((kq + 4 * kThrGroups * j) ^ ((dp >> 3) & 1))];
                 *reinterpret_cast<u32x2_t*>(vt) = even;
                 *reinterpret_cast<u32x2_t*>(vt + kVStride) = odd;
             }
@@ -418,7 +428,8 @@ prefill_kernel(PrefillArgs a) {
                 stage(kt_begin, Set0{});
                 commit(0, half, Set0{});
             }
-            if (kt_begin + 1 < kt_end) stage(kt_begin + 1, Set1{});
+            if constexpr (kStageSets == 2)
+                if (kt_begin + 1 < kt_end) stage(kt_begin + 1, Set1{});
             __syncthreads();
 
             // One key tile.  Tile kt + 1 is already in staging set `held`; tile kt + 2
@@ -428,7 +439,11 @@ prefill_kernel(PrefillArgs a) {
                 constexpr int A = decltype(held)::value;
                 using Other = std::integral_constant<int, 1 - A>;
                 const int buf = (kt - kt_begin) & 1;
-                if (kt + 2 < kt_end) stage(kt + 2, Other{});
+                if constexpr (kStageSets == 2) {
+                    if (kt + 2 < kt_end) stage(kt + 2, Other{});
+                } else {
+                    if (kt + 1 < kt_end) stage(kt + 1, Set0{});
+                }
                 const int key0 = kt * kKeys;
                 // S^T = K Q^T over this tile: 2 key tiles of 32 x 8 dim steps of 16.
                 // sacc[mt][4b + e] is the score of key 32mt + 8b + 4h + e.
@@ -548,7 +563,7 @@ prefill_kernel(PrefillArgs a) {
                                                                            oacc[dt], 0, 0, 0);
                     }
                 }
-                if (kt + 1 < kt_end) commit(buf ^ 1, half, held);
+                if (kt + 1 < kt_end) commit(buf ^ 1, half, std::integral_constant<int, kStageSets == 2 ? A : 0>{});
                 __syncthreads();
             };
             for (int kt = kt_begin; kt < kt_end; kt += 2) {
@@ -623,13 +638,13 @@ prefill_kernel(PrefillArgs a) {
 template <int G>
 __global__ void __launch_bounds__(256)
 prefill_merge_kernel(PrefillArgs a) {
-    const int e = (int)(blockIdx.x >> 2);
+    const int e = (int)(blockIdx.x / kMergeParts);
     if (e >= *a.split_count) return;
     const int4 d = a.split_list[e];
     const int s0 = d.x, np = d.y & 0xffffff, rec0 = d.y >> 24, row0 = d.z, ntok = d.w >> 8, kvh = d.w & 255;
     const int Hkv = a.num_kv_heads;
     const int d4 = 4 * (threadIdx.x & 31);
-    const int rbeg = 64 * (int)(blockIdx.x & 3);
+    const int rbeg = 64 * (int)(blockIdx.x % kMergeParts);
     for (int r = rbeg + (int)(threadIdx.x >> 5); r < rbeg + 64; r += 8) {
         const int tq = r / G;
         if (tq >= ntok) break;                         // rows are token-major: the rest are inactive
@@ -680,7 +695,7 @@ hipError_t launch_typed(const PrefillArgs& a, hipStream_t stream) {
     // KV head, each of which lies in one tile
     const int64_t listed = (int64_t)(a.slots_per_kvh - 1) * a.num_kv_heads;
     if (listed == 0) return hipSuccess;
-    hipLaunchKernelGGL((prefill_merge_kernel<G>), dim3((unsigned)(4 * listed)), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((prefill_merge_kernel<G>), dim3((unsigned)(kMergeParts * listed)), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -13,7 +13,8 @@ from __future__ import annotations
 import numpy as np
 import torch
 
-from . import (chunked_prefill_workspace, decode_workspace, pa_chunked_prefill, pa_decode, pa_decode_fp8,
+from . import (chunked_prefill_workspace, decode_workspace, pa_chunked_prefill, pa_decode, pa_decode_append,
+               pa_decode_fp8,
                pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_slot_mapping_and_cache)
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -116,6 +117,35 @@ class DeviceWorkload:
                                  stream)
         return pa_decode(out, self.query, self.key_cache, self.value_cache, self.block_table,
                          self.seq_lens, w.scale, w.max_seq_len, partition_tokens, workspace, stream)
+
+    def append_rows(self):
+        """This step's new K/V rows indexed by sequence ([num_seqs, Hkv, D], row b
+        the newest token of sequence b; zeros for sequences without one), as
+        pa_decode_append takes them."""
+        if not hasattr(self, "_append"):
+            w = self.w
+            L = np.asarray(w.seq_lens)
+            assert np.all((L == 0) | (L - np.asarray(w.history_lens) == 1)), "one new token per sequence"
+            idx = torch.from_numpy(np.flatnonzero(L > 0)).to(self.device)
+            k = torch.zeros((w.num_seqs, w.num_kv_heads, w.head_dim), dtype=self.dtype, device=self.device)
+            v = torch.zeros_like(k)
+            k[idx] = self.new_k
+            v[idx] = self.new_v
+            self._append = (k, v, torch.empty(w.num_seqs, dtype=torch.int64, device=self.device))
+        return self._append
+
+    def decode_append(self, out=None, workspace=None, stream=None) -> torch.Tensor:
+        """The whole decode step in one call (pa_decode_append): the newest
+        token of every sequence written to the cache and attended to."""
+        w = self.w
+        assert not self.kv_fp8, "pa_decode_append takes bf16/fp32 caches"
+        k, v, slots = self.append_rows()
+        if out is None:
+            out = torch.empty_like(self.query)
+        if workspace is None:
+            workspace = self.decode_workspace(0)
+        return pa_decode_append(out, self.query, k, v, self.key_cache, self.value_cache, self.block_table,
+                                self.seq_lens, w.scale, w.max_seq_len, slots, workspace, stream)
 
     def prefill_workspace(self):
         w = self.w
