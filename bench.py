@@ -1,12 +1,14 @@
 """Benchmark: one decode step of paged attention on one MI355X.
 
 A step is the whole hot path over one batch: compute the slots of this step's
-new tokens and scatter their K/V rows into the paged cache (both in one launch,
-pa_slot_mapping_and_cache), and run decode attention over every sequence's
-cache (pa_decode: the balanced stream kernel and the log-sum-exp merge of the
-sequences it splits).  The K timed steps run with nothing else on the stream;
-K more steps with HIP events around each pa_decode call give the kernel's own
-rate.  Inputs are synthetic, seeded, and resident in HBM before
+new tokens, scatter their K/V rows into the paged cache and run decode
+attention over every sequence, in one pa_decode_append call (the balanced
+stream kernel, which reads each newest token from its input row and writes it
+to its slot, and the log-sum-exp merge of the sequences it splits).  The K
+timed steps run with nothing else on the stream; K more steps with HIP events
+around each call give the kernel's own rate, and K steps of the two-call form
+(pa_slot_mapping_and_cache, then pa_decode; --step two-call to time it as the
+step) are reported beside it.  Inputs are synthetic, seeded, and resident in HBM before
 timing starts; the earlier context of every sequence is written before timing.
 
 Default workload: Llama-3-8B decode layer, batch 64, context lengths uniform
@@ -14,7 +16,7 @@ in [1024, 8192], bf16 (32 query heads, 8 KV heads, head_dim 128, 16-token
 blocks).  Prints one JSON line.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-cache bf16|fp8]
-                  [--no-cpu-baseline] [--no-probes]
+                  [--step append|two-call] [--no-cpu-baseline] [--no-probes]
 
 With --workload chunked_prefill_mix a step is the scatter plus one
 pa_chunked_prefill call over 4 prefill chunks and 96 decodes; the chunks are
@@ -76,17 +78,18 @@ def decode_sources_sha256() -> str:
     return h.hexdigest()
 
 
-def recorded_traffic(workload: str):
-    """HBM bytes per pa_decode call from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+def recorded_traffic(workload: str, call: str):
+    """HBM bytes per decode call from the rocprofv3 FETCH_SIZE / WRITE_SIZE
     passes recorded under profiles/ (already scaled by the copy-kernel
-    factors), or None if they were taken on other kernel sources or another
-    workload."""
+    factors), or None if they were taken on other kernel sources, another
+    workload or another entry point."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_sha256") != decode_sources_sha256() or rec.get("workload") != workload:
+    if (rec.get("source_sha256") != decode_sources_sha256() or rec.get("workload") != workload
+            or rec.get("call", "pa_decode") != call):
         return None
     return rec.get("hbm_bytes_per_call")
 
@@ -278,6 +281,28 @@ def mfma_probe(pa, torch, iters: int = 10):
     torch.cuda.synchronize()
     us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
     return {"TFLOPs": round(flops / us / 1e6, 1), "us": round(us, 1), "flops": flops, "workgroups": wgs}
+
+
+def device_info(torch) -> dict:
+    """The GPU the figures were measured on: name, architecture, compute units,
+    memory, the HIP runtime torch was built with, and the engine and memory
+    clock levels the driver lists (read from sysfs; '*' marks the current one
+    when the file is readable)."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_gib": round(p.total_memory / 2 ** 30, 1), "hip": torch.version.hip}
+    import glob
+    for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(f) as fh:
+                sclk = [ln.strip() for ln in fh if ln.strip()]
+            with open(f.replace("pp_dpm_sclk", "pp_dpm_mclk")) as fh:
+                mclk = [ln.strip() for ln in fh if ln.strip()]
+        except OSError:
+            continue
+        info["sclk_levels"], info["mclk_levels"] = sclk, mclk
+        break
+    return info
 
 
 def cpu_baseline(w, nseq: int, fp8: bool = False):
@@ -552,7 +577,7 @@ def main():
     kv = w.kv_bytes(1 if fp8 else None)
     gbps = kv / (ms_step * 1e-3) / 1e9
     dec_gbps = kv / (dec_avg_ms * 1e-3) / 1e9
-    traffic = None if fp8 else recorded_traffic(w.name)
+    traffic = None if fp8 else recorded_traffic(w.name, "pa_decode_append" if append else "pa_decode")
     probe = None if args.no_probes else probes(pa, torch)
     res = {
         "metric": METRIC,
@@ -612,6 +637,7 @@ def main():
         res["rope_reshape_and_cache"] = rope_scatter_timing(pa, torch)
         res["copy_blocks"] = copy_blocks_timing(pa, torch)
         res["kv_manager"] = kv_manager_timing(pa)
+    res["device"] = device_info(torch)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, fp8)
     print(json.dumps(res), flush=True)

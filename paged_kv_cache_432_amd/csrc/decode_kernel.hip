@@ -947,35 +947,6 @@ __device__ __forceinline__ int64_t stream_quantum(const DecodeArgs& a, int64_t u
     return q > a.min_quantum ? q : (int64_t)a.min_quantum;
 }
 
-// Append mode: sequence b's newest token (position seq_lens[b] - 1) as the
-// bf16 row b of new_key / new_value: it is written to its slot of the caches,
-// and the slot to slot_out[b], with the slot rule of the page-table lookup
-// (-1 when the request has no block for that position: nothing is written).
-// No workgroup of the launch reads that slot, so the writes may land at any
-// time in it; each workgroup writes the rows b = blockIdx.x (mod grid) when its
-// attention is done.
-__device__ __forceinline__ void append_rows(const DecodeArgs& a) {
-    const int64_t row_bytes = (int64_t)a.num_kv_heads * kHeadDim * 2;
-    const int chunks = (int)(row_bytes >> 4);
-    const int half = (int)blockDim.x >> 1;
-    const bool is_v = (int)threadIdx.x >= half;
-    const int t = (int)threadIdx.x - (is_v ? half : 0);
-    for (int b = blockIdx.x; b < a.num_seqs; b += gridDim.x) {
-        const int p = a.seq_lens[b] - 1;
-        int64_t slot = -1;
-        if (p >= 0 && p / kBlock < a.bt_stride) {
-            const int32_t physical = a.block_table[(int64_t)b * a.bt_stride + p / kBlock];
-            if (physical >= 0) slot = (int64_t)physical * kBlock + p % kBlock;
-        }
-        if (threadIdx.x == 0 && a.slot_out) a.slot_out[b] = slot;
-        if (slot < 0 || slot >= a.num_blocks * kBlock) continue;
-        const char* src = is_v ? a.new_value + b * a.new_value_stride : a.new_key + b * a.new_key_stride;
-        char* dst = reinterpret_cast<char*>(const_cast<void*>(is_v ? a.value_cache : a.key_cache)) + slot * row_bytes;
-        for (int c = t; c < chunks; c += half)
-            *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = *reinterpret_cast<const u32x4_t*>(src + (int64_t)c * 16);
-    }
-}
-
 // F8: the caches hold fp8 (E4M3) codes; query and output stay bf16.
 // AP: append mode (bf16 matrix-core path only).
 template <typename Chunk, typename Elem, int G, bool QL, bool NT, bool F8 = false, bool AP = false>
@@ -1003,7 +974,6 @@ decode_stream_kernel(DecodeArgs a) {
     static_assert(!AP || (MF && !F8), "append mode: bf16 matrix-core path");
     if constexpr (MF) {
         stream_share_mfma<G, NT, F8 ? kFp8Depth : kMfmaDepth, F8, AP>(a, s_pref, s_tab, u0, u1, W, NG, wi, lane);
-        if constexpr (AP) append_rows(a);
         return;
     }
 
@@ -1138,7 +1108,31 @@ merge_partitions_kernel(DecodeArgs a) {
                        reinterpret_cast<Elem*>(a.out) + (row * Hq + h) * kHeadDim);
 }
 
-template <typename Elem>
+// Append mode: sequence b's newest token (position seq_lens[b] - 1), row b of
+// new_key / new_value, is written to its slot of the caches, and the slot to
+// slot_out[b], with the slot rule of the page-table lookup (-1 when the request
+// has no block for that position: nothing is written).  The decode launch
+// before never reads that slot (it took the token from its input row), so the
+// copy is done here, one wave per (sequence, KV head): lanes 0-15 the K head's
+// 256 bytes, lanes 16-31 the V head's.
+__device__ __forceinline__ void append_head(const DecodeArgs& a, int64_t b, int kvh, int lane) {
+    const int p = a.seq_lens[b] - 1;
+    int64_t slot = -1;
+    if (p >= 0 && p / kBlock < a.bt_stride) {
+        const int32_t physical = a.block_table[b * a.bt_stride + p / kBlock];
+        if (physical >= 0) slot = (int64_t)physical * kBlock + p % kBlock;
+    }
+    if (kvh == 0 && lane == 0 && a.slot_out) a.slot_out[b] = slot;
+    if (slot < 0 || slot >= a.num_blocks * kBlock || lane >= 32) return;
+    const bool is_v = lane >= 16;
+    const int64_t off = (int64_t)kvh * kHeadDim * 2 + (lane & 15) * 16;
+    const char* src = (is_v ? a.new_value + b * a.new_value_stride : a.new_key + b * a.new_key_stride) + off;
+    char* dst = reinterpret_cast<char*>(const_cast<void*>(is_v ? a.value_cache : a.key_cache)) +
+                slot * ((int64_t)a.num_kv_heads * kHeadDim * 2) + off;
+    *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
+}
+
+template <typename Elem, bool AP = false>
 __global__ void __launch_bounds__(256)
 merge_stream_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1148,6 +1142,8 @@ merge_stream_kernel(DecodeArgs a) {
     const int64_t b = item / Hq;
     const int h = (int)(item % Hq);
     if (b >= a.num_seqs) return;
+    if constexpr (AP)
+        if (h < a.num_kv_heads) append_head(a, b, h, lane);
     const int G = Hq / a.num_kv_heads;
     const int W = a.waves_per_group;
     const int NG = a.num_kv_heads / W;
@@ -1190,7 +1186,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t mitems = (int64_t)a.num_seqs * a.num_heads;
-        hipLaunchKernelGGL((merge_stream_kernel<Elem>),
+        hipLaunchKernelGGL((merge_stream_kernel<Elem, AP>),
                            dim3((unsigned)((mitems + kWavesPerGroup - 1) / kWavesPerGroup)), dim3(256), 0,
                            stream, a);
         return hipGetLastError();
