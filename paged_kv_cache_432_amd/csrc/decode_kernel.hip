@@ -47,7 +47,12 @@
 //     flattened and every workgroup takes an equal contiguous share of it, one
 //     wave per KV head of a group.  A sequence cut between workgroups leaves
 //     a partial result in each, merged afterwards; a workgroup holds at most
-//     two such pieces (its first and its last).
+//     two such pieces (its first and its last).  A matrix-core wave keeps its
+//     first piece's record in LDS and writes both records when its share is
+//     done, so that no record write lands in the middle of the read stream.
+//   * append mode (pa_decode_append): each sequence's newest token is one more
+//     unit after its cached blocks, read from its input row; the merge launch
+//     copies it to its cache slot.
 #include <math.h>
 
 #include "device_common.h"
