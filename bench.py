@@ -22,9 +22,9 @@ With --workload chunked_prefill_mix a step is the scatter plus one
 pa_chunked_prefill call over 4 prefill chunks and 96 decodes; the chunks are
 also reported against the bf16 matrix peak.
 
-With --kv-cache fp8 the caches hold E4M3 codes: the step is pa_slot_mapping,
-pa_reshape_and_cache_fp8 and pa_decode_fp8, and KV bytes count one byte per
-element.
+With --kv-cache fp8 the caches hold E4M3 codes: the step is
+pa_slot_mapping_and_cache_fp8 (slots and quantising scatter in one launch) and
+pa_decode_fp8, and KV bytes count one byte per element.
 """
 from __future__ import annotations
 
@@ -606,7 +606,8 @@ def main():
             "kv_cache": "fp8 E4M3 (1 byte/element), k_scale = v_scale = %.6g" % w.fp8_scales()[0] if fp8
                         else w.dtype,
             "step": "pa_decode_append (slots, scatter and decode in one call)" if append
-                    else "pa_slot_mapping_and_cache + " + ("pa_decode_fp8" if fp8 else "pa_decode"),
+                    else ("pa_slot_mapping_and_cache_fp8 + pa_decode_fp8" if fp8
+                          else "pa_slot_mapping_and_cache + pa_decode"),
         },
         "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
         "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),

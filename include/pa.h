@@ -253,6 +253,24 @@ pa_status pa_reshape_and_cache_fp8(const void *key, int64_t key_token_stride,
                                    hipStream_t stream);
 
 /*
+ * pa_slot_mapping followed by pa_reshape_and_cache_fp8, fused into one launch
+ * (as pa_slot_mapping_and_cache is for bf16/fp32 caches): the tokens' slots
+ * are computed as pa_slot_mapping does and written to slot_mapping, and each
+ * token's K and V rows are quantised into them as pa_reshape_and_cache_fp8
+ * does.  Arguments as in those two calls; the results are identical to
+ * calling them in turn.
+ */
+pa_status pa_slot_mapping_and_cache_fp8(int64_t *slot_mapping, const int32_t *block_table,
+                                        int32_t max_blocks_per_req, int32_t num_seqs,
+                                        const int32_t *token_seq, const int32_t *token_pos,
+                                        const void *key, int64_t key_token_stride,
+                                        const void *value, int64_t value_token_stride,
+                                        void *key_cache, void *value_cache,
+                                        int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                                        int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                        float k_scale, float v_scale, hipStream_t stream);
+
+/*
  * fp8 KV cache: decode attention over caches written by
  * pa_reshape_and_cache_fp8.  Same operation and arguments as pa_decode with
  * query and out in bf16, each cached K element standing for value(code) *

@@ -18,7 +18,7 @@ import torch
 
 __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
-    "pa_slot_mapping", "pa_reshape_and_cache", "pa_slot_mapping_and_cache", "pa_rope_reshape_and_cache", "pa_reshape_and_cache_fp8",
+    "pa_slot_mapping", "pa_reshape_and_cache", "pa_slot_mapping_and_cache", "pa_rope_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_slot_mapping_and_cache_fp8",
     "pa_decode_fp8", "pa_copy_blocks", "KvManager", "pa_decode_workspace_bytes",
     "pa_decode_partition_tokens", "pa_decode", "pa_decode_append", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
     "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
@@ -106,6 +106,10 @@ def lib():
         L.pa_reshape_and_cache_fp8.restype = ctypes.c_int
         L.pa_reshape_and_cache_fp8.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32,
                                                _i32, _i32, ctypes.c_int, ctypes.c_float, ctypes.c_float, _vp]
+        L.pa_slot_mapping_and_cache_fp8.restype = ctypes.c_int
+        L.pa_slot_mapping_and_cache_fp8.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp,
+                                                    _i64, _i64, _i32, _i32, _i32, ctypes.c_int, ctypes.c_float,
+                                                    ctypes.c_float, _vp]
         L.pa_decode_fp8.restype = ctypes.c_int
         L.pa_decode_fp8.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, _i32, _vp,
@@ -370,6 +374,37 @@ def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: 
                                        key_cache.shape[0], key_cache.shape[1], hkv, d, _dtype_code(key),
                                        float(k_scale), float(v_scale), _stream(stream, key_cache.device))
     _check(s, "pa_reshape_and_cache_fp8")
+
+
+def pa_slot_mapping_and_cache_fp8(slot_mapping: torch.Tensor, block_table: torch.Tensor, token_seq: torch.Tensor,
+                                  token_pos: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                                  key_cache: torch.Tensor, value_cache: torch.Tensor, k_scale: float, v_scale: float,
+                                  stream=None) -> torch.Tensor:
+    """pa_slot_mapping then pa_reshape_and_cache_fp8 in one launch: slot_mapping
+    (int64, out) is written and the K/V rows are quantised into the E4M3 caches."""
+    _need(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous(), "slot_mapping: contiguous int64")
+    _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
+          "block_table: contiguous int32 [num_seqs, max_blocks_per_req]")
+    _need(token_seq.dtype == torch.int32 and token_pos.dtype == torch.int32, "token_seq/token_pos: int32")
+    _need(token_seq.is_contiguous() and token_pos.is_contiguous(), "token_seq/token_pos: contiguous")
+    _need(key.dim() == 3 and value.dim() == 3 and key.shape == value.shape, "key/value: [num_tokens, Hkv, D]")
+    _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
+    _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
+    _need(key_cache.dtype == value_cache.dtype == torch.uint8, "fp8 caches are uint8 (E4M3 codes)")
+    _need(key.dtype == value.dtype, "key/value dtype mismatch")
+    n, hkv, d = key.shape
+    _need(slot_mapping.numel() == n and token_seq.numel() == n and token_pos.numel() == n, "token lists differ")
+    _need(key_cache.shape[2] == hkv and key_cache.shape[3] == d, "cache head shape differs from key")
+    _need(key.stride(2) == 1 and key.stride(1) == d and value.stride(2) == 1 and value.stride(1) == d,
+          "key/value heads and dims must be contiguous")
+    s = lib().pa_slot_mapping_and_cache_fp8(_ptr(slot_mapping), _ptr(block_table), block_table.shape[1],
+                                            block_table.shape[0], _ptr(token_seq), _ptr(token_pos), _ptr(key),
+                                            key.stride(0), _ptr(value), value.stride(0), _ptr(key_cache),
+                                            _ptr(value_cache), n, key_cache.shape[0], key_cache.shape[1], hkv, d,
+                                            _dtype_code(key), float(k_scale), float(v_scale),
+                                            _stream(stream, key_cache.device))
+    _check(s, "pa_slot_mapping_and_cache_fp8")
+    return slot_mapping
 
 
 def pa_decode_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,

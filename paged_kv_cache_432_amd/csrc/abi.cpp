@@ -355,6 +355,42 @@ pa_status pa_reshape_and_cache_fp8(const void* key, int64_t key_token_stride, co
                       "reshape_and_cache_fp8 launch");
 }
 
+pa_status pa_slot_mapping_and_cache_fp8(int64_t* slot_mapping, const int32_t* block_table,
+                                        int32_t max_blocks_per_req, int32_t num_seqs, const int32_t* token_seq,
+                                        const int32_t* token_pos, const void* key, int64_t key_token_stride,
+                                        const void* value, int64_t value_token_stride, void* key_cache,
+                                        void* value_cache, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                                        int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype, float k_scale,
+                                        float v_scale, hipStream_t stream) {
+    if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "source dtype %d", (int)dtype);
+    if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
+    if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_seqs < 0 ||
+        max_blocks_per_req < 0)
+        return fail(PA_ERR_INVALID_ARG, "negative or zero size");
+    if (!(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
+        return fail(PA_ERR_INVALID_ARG, "scales must be finite and positive");
+    if (num_tokens == 0) return ok();
+    if (!slot_mapping || !token_seq || !token_pos || !key || !value || !key_cache || !value_cache)
+        return fail(PA_ERR_INVALID_ARG, "null pointer");
+    if (num_seqs > 0 && max_blocks_per_req > 0 && !block_table) return fail(PA_ERR_INVALID_ARG, "null block_table");
+    const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    const int64_t eb = elem_bytes(dtype);
+    if (row_elems % 16 != 0 || row_elems > (1 << 28))
+        return fail(PA_ERR_UNSUPPORTED, "row of %lld elements (must be a multiple of 16)", (long long)row_elems);
+    if (key_token_stride < row_elems || value_token_stride < row_elems)
+        return fail(PA_ERR_INVALID_ARG, "token stride smaller than num_kv_heads * head_dim");
+    if (!aligned16(key) || !aligned16(value) || !aligned16(key_cache) || !aligned16(value_cache) ||
+        (key_token_stride * eb) % 16 || (value_token_stride * eb) % 16)
+        return fail(PA_ERR_INVALID_ARG, "rows must start on 16-byte boundaries");
+    if (num_tokens > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "num_tokens too large");
+    return hip_status(pa::launch_slot_and_cache_fp8(slot_mapping, block_table, max_blocks_per_req, num_seqs, token_seq,
+                                                    token_pos, key, key_token_stride * eb, value,
+                                                    value_token_stride * eb, key_cache, value_cache, num_tokens,
+                                                    num_blocks * 16, (int32_t)row_elems, dtype == PA_BF16 ? 1 : 0,
+                                                    k_scale, v_scale, stream),
+                      "slot_and_cache_fp8 launch");
+}
+
 pa_status pa_rope_reshape_and_cache(void* query_out, int64_t q_out_token_stride, const void* qkv,
                                     int64_t qkv_token_stride, const int64_t* positions, const float* cos_sin_cache,
                                     int64_t max_position, int32_t rotary_dim, int32_t neox_style, void* key_cache,

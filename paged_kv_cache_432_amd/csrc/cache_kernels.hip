@@ -88,6 +88,30 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, int64_t layer_
 // the hardware conversion to the nearest code, ties to even.  One workgroup
 // per token: threads 0-127 take the K row, 128-255 the V row, 16 elements
 // (16 output bytes) per step.
+// 16 source elements (two chunks) -> their 16 E4M3 codes of x / scale.
+template <typename Chunk>
+__device__ __forceinline__ u32x4_t fp8_codes(const Chunk& x0, const Chunk& x1, float scale) {
+    float f[16];
+    to_f32(x0, f);
+    to_f32(x1, f + 8);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float y = f[e] / scale;
+        f[e] = __builtin_fabsf(y) > 448.f ? __builtin_copysignf(448.f, y) : y;
+    }
+    u32x4_t w;
+    int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+    p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], p0, true);
+    int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+    p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], p1, true);
+    int p2 = __builtin_amdgcn_cvt_pk_fp8_f32(f[8], f[9], 0, false);
+    p2 = __builtin_amdgcn_cvt_pk_fp8_f32(f[10], f[11], p2, true);
+    int p3 = __builtin_amdgcn_cvt_pk_fp8_f32(f[12], f[13], 0, false);
+    p3 = __builtin_amdgcn_cvt_pk_fp8_f32(f[14], f[15], p3, true);
+    w.x = (uint32_t)p0; w.y = (uint32_t)p1; w.z = (uint32_t)p2; w.w = (uint32_t)p3;
+    return w;
+}
+
 template <typename Chunk>
 __global__ void __launch_bounds__(256)
 reshape_and_cache_fp8_kernel(const char* __restrict__ key, int64_t key_stride_bytes,
@@ -106,26 +130,69 @@ reshape_and_cache_fp8_kernel(const char* __restrict__ key, int64_t key_stride_by
         Chunk x0, x1;
         load_chunk<false>(x0, src + (int64_t)c * 16 * Chunk::kBytes / 8);
         load_chunk<false>(x1, src + ((int64_t)c * 16 + 8) * Chunk::kBytes / 8);
-        float f[16];
-        to_f32(x0, f);
-        to_f32(x1, f + 8);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const float y = f[e] / scale;
-            f[e] = __builtin_fabsf(y) > 448.f ? __builtin_copysignf(448.f, y) : y;
-        }
-        u32x4_t w;
-        int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-        p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], p0, true);
-        int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-        p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], p1, true);
-        int p2 = __builtin_amdgcn_cvt_pk_fp8_f32(f[8], f[9], 0, false);
-        p2 = __builtin_amdgcn_cvt_pk_fp8_f32(f[10], f[11], p2, true);
-        int p3 = __builtin_amdgcn_cvt_pk_fp8_f32(f[12], f[13], 0, false);
-        p3 = __builtin_amdgcn_cvt_pk_fp8_f32(f[14], f[15], p3, true);
-        w.x = (uint32_t)p0; w.y = (uint32_t)p1; w.z = (uint32_t)p2; w.w = (uint32_t)p3;
-        *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = w;
+        *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = fp8_codes(x0, x1, scale);
     }
+}
+
+// The slot lookup of pa_slot_mapping and the fp8 scatter above in one launch:
+// token t's slot is computed from (token_seq[t], token_pos[t]) and the block
+// table (-1 for a padding or unallocated token), written to slot_out[t], and
+// the token's rows are quantised into it.  The first 16 elements a thread
+// handles are loaded before the slot is known.
+template <typename Chunk>
+__global__ void __launch_bounds__(256)
+slot_and_cache_fp8_kernel(int64_t* __restrict__ slot_out, const int32_t* __restrict__ block_table, int32_t bt_stride,
+                          int32_t num_seqs, const int32_t* __restrict__ token_seq,
+                          const int32_t* __restrict__ token_pos, const char* __restrict__ key,
+                          int64_t key_stride_bytes, const char* __restrict__ value, int64_t value_stride_bytes,
+                          uint8_t* __restrict__ key_cache, uint8_t* __restrict__ value_cache, int64_t num_slots,
+                          int32_t row_elems, float k_scale, float v_scale) {
+    const int64_t token = blockIdx.x;
+    const bool is_v = threadIdx.x >= 128;
+    const int32_t c0 = threadIdx.x & 127;
+    const int32_t chunks = row_elems / 16;
+    const char* src = is_v ? value + token * value_stride_bytes : key + token * key_stride_bytes;
+    Chunk x0, x1;
+    if (c0 < chunks) {
+        load_chunk<false>(x0, src + (int64_t)c0 * 16 * Chunk::kBytes / 8);
+        load_chunk<false>(x1, src + ((int64_t)c0 * 16 + 8) * Chunk::kBytes / 8);
+    }
+    const int32_t sq = token_seq[token];
+    const int32_t p = token_pos[token];
+    int64_t slot = -1;
+    if (sq >= 0 && sq < num_seqs && p >= 0 && p / kBlock < bt_stride) {
+        const int32_t physical = block_table[(int64_t)sq * bt_stride + p / kBlock];
+        if (physical >= 0) slot = (int64_t)physical * kBlock + p % kBlock;
+    }
+    if (threadIdx.x == 0) slot_out[token] = slot;
+    if (slot < 0 || slot >= num_slots) return;
+    uint8_t* dst = (is_v ? value_cache : key_cache) + slot * (int64_t)row_elems;
+    const float scale = is_v ? v_scale : k_scale;
+    if (c0 < chunks) *reinterpret_cast<u32x4_t*>(dst + (int64_t)c0 * 16) = fp8_codes(x0, x1, scale);
+    for (int32_t c = c0 + 128; c < chunks; c += 128) {      // rows longer than 2048 elements
+        load_chunk<false>(x0, src + (int64_t)c * 16 * Chunk::kBytes / 8);
+        load_chunk<false>(x1, src + ((int64_t)c * 16 + 8) * Chunk::kBytes / 8);
+        *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = fp8_codes(x0, x1, scale);
+    }
+}
+
+hipError_t launch_slot_and_cache_fp8(int64_t* slot_mapping, const int32_t* block_table, int32_t max_blocks_per_req,
+                                     int32_t num_seqs, const int32_t* token_seq, const int32_t* token_pos,
+                                     const void* key, int64_t key_stride_bytes, const void* value,
+                                     int64_t value_stride_bytes, void* key_cache, void* value_cache,
+                                     int64_t num_tokens, int64_t num_slots, int32_t row_elems, int dtype,
+                                     float k_scale, float v_scale, hipStream_t stream) {
+    if (dtype == 1)
+        hipLaunchKernelGGL(slot_and_cache_fp8_kernel<ChunkBF16>, dim3((unsigned)num_tokens), dim3(256), 0, stream,
+                           slot_mapping, block_table, max_blocks_per_req, num_seqs, token_seq, token_pos,
+                           (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
+                           (uint8_t*)key_cache, (uint8_t*)value_cache, num_slots, row_elems, k_scale, v_scale);
+    else
+        hipLaunchKernelGGL(slot_and_cache_fp8_kernel<ChunkF32>, dim3((unsigned)num_tokens), dim3(256), 0, stream,
+                           slot_mapping, block_table, max_blocks_per_req, num_seqs, token_seq, token_pos,
+                           (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
+                           (uint8_t*)key_cache, (uint8_t*)value_cache, num_slots, row_elems, k_scale, v_scale);
+    return hipGetLastError();
 }
 
 hipError_t launch_reshape_and_cache_fp8(const void* key, int64_t key_stride_bytes, const void* value,

@@ -20,6 +20,13 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, int64_t layer_
 
 // fp8 (E4M3) scatter: K/V rows of `dtype` (0 fp32, 1 bf16) divided by their
 // scale, stored one byte per element.
+// pa_slot_mapping and the fp8 scatter in one launch (dtype of the source rows: 0 fp32, 1 bf16).
+hipError_t launch_slot_and_cache_fp8(int64_t* slot_mapping, const int32_t* block_table, int32_t max_blocks_per_req,
+                                     int32_t num_seqs, const int32_t* token_seq, const int32_t* token_pos,
+                                     const void* key, int64_t key_stride_bytes, const void* value,
+                                     int64_t value_stride_bytes, void* key_cache, void* value_cache,
+                                     int64_t num_tokens, int64_t num_slots, int32_t row_elems, int dtype,
+                                     float k_scale, float v_scale, hipStream_t stream);
 hipError_t launch_reshape_and_cache_fp8(const void* key, int64_t key_stride_bytes, const void* value,
                                         int64_t value_stride_bytes, void* key_cache, void* value_cache,
                                         const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,

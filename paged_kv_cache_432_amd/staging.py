@@ -15,7 +15,8 @@ import torch
 
 from . import (chunked_prefill_workspace, decode_workspace, pa_chunked_prefill, pa_decode, pa_decode_append,
                pa_decode_fp8,
-               pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_slot_mapping_and_cache)
+               pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_slot_mapping_and_cache,
+               pa_slot_mapping_and_cache_fp8)
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
 
@@ -91,8 +92,14 @@ class DeviceWorkload:
     # ---- the step
     def scatter_new(self, stream=None, fused: bool = False) -> None:
         """Rows a1-a2 of the step: slots of this step's tokens, then their scatter
-        (fused: both in one launch, pa_slot_mapping_and_cache; bf16/fp32 caches)."""
-        if fused and not self.kv_fp8:
+        (fused: both in one launch, pa_slot_mapping_and_cache, or
+        pa_slot_mapping_and_cache_fp8 over an fp8 cache)."""
+        if fused and self.kv_fp8:
+            pa_slot_mapping_and_cache_fp8(self.slot_mapping, self.block_table, self.new_seq, self.new_pos,
+                                          self.new_k, self.new_v, self.key_cache, self.value_cache, self.k_scale,
+                                          self.v_scale, stream=stream)
+            return
+        if fused:
             pa_slot_mapping_and_cache(self.slot_mapping, self.block_table, self.new_seq, self.new_pos,
                                       self.new_k, self.new_v, self.key_cache, self.value_cache, stream=stream)
             return

@@ -87,6 +87,72 @@ def test_scatter_f32_source_and_padding(pa):
     assert np.array_equal(kc.cpu().numpy(), okc) and np.array_equal(vc.cpu().numpy(), ovc)
 
 
+@pytest.mark.parametrize("src", ["bf16", "f32"])
+@pytest.mark.parametrize("hkv", [8, 2, 16, 24])
+def test_fused_slots_and_fp8_scatter(pa, src, hkv):
+    """pa_slot_mapping_and_cache_fp8: the slots equal the oracle's, and the codes
+    equal the oracle's fp8 scatter through them, byte for byte; padding requests,
+    positions past the table and unallocated entries give slot -1 and write
+    nothing.  Hkv 24 gives rows of 3072 elements, more than one pass of the
+    workgroup."""
+    rng = np.random.default_rng(70 + hkv)
+    nb, d, n, B, width = 40, 128, 160, 6, 8
+    table = np.full((B, width), -1, np.int32)
+    perm = rng.permutation(nb)
+    for b in range(B):
+        k = int(rng.integers(1, width))
+        table[b, :k] = perm[b * 6:b * 6 + k]
+    seq = rng.integers(-1, B + 1, n).astype(np.int32)
+    pos = rng.integers(-2, width * 16 + 3, n).astype(np.int32)
+
+    def expected():
+        inside = (seq >= 0) & (seq < B) & (pos >= 0) & (pos // 16 < width)
+        out = np.full(n, -1, np.int64)
+        out[inside] = oracle.slot_mapping(table, seq[inside], pos[inside])
+        return out
+
+    seen = set()
+    for i, sl in enumerate(expected()):                # distinct valid slots only
+        if sl >= 0 and sl in seen:
+            seq[i] = -1
+        seen.add(int(sl))
+    slots_o = expected()
+    x = (rng.standard_normal((2, n, hkv, d)) * np.float32(30)).astype(np.float32)
+    if src == "bf16":
+        host = [W.bf16_bits(x[0]), W.bf16_bits(x[1])]
+        dev_rows = [torch.from_numpy(h.view(np.int16)).view(torch.bfloat16).cuda() for h in host]
+    else:
+        host = [x[0], x[1]]
+        dev_rows = [torch.from_numpy(h).cuda() for h in host]
+    kc = torch.full((nb, 16, hkv, d), 0x5A, dtype=torch.uint8, device="cuda")
+    vc = kc.clone()
+    slots = torch.empty(n, dtype=torch.int64, device="cuda")
+    pa.pa_slot_mapping_and_cache_fp8(slots, torch.from_numpy(table).cuda(), torch.from_numpy(seq).cuda(),
+                                     torch.from_numpy(pos).cuda(), dev_rows[0], dev_rows[1], kc, vc, 0.21, 0.43)
+    torch.cuda.synchronize()
+    assert np.array_equal(slots.cpu().numpy(), slots_o)
+    okc = np.full((nb, 16, hkv, d), 0x5A, np.uint8)
+    ovc = okc.copy()
+    oracle.reshape_and_cache_fp8(host[0], host[1], okc, ovc, slots_o, 0.21, 0.43)
+    assert np.array_equal(kc.cpu().numpy(), okc) and np.array_equal(vc.cpu().numpy(), ovc)
+
+
+def test_fused_step_matches_two_launch_step(staging):
+    """The fp8 decode step with the fused slots + scatter gives the same slots,
+    caches and output as with the two launches."""
+    w = W.custom("fp8_fused", seq_lens=[1, 17, 300, 1000, 0, 33], dtype="bf16", seed=71)
+    a = staging.DeviceWorkload(w, kv_fp8=True)
+    a.scatter_new(fused=True)
+    out_a = a.decode()
+    b = staging.DeviceWorkload(w, kv_fp8=True)
+    b.scatter_new()
+    out_b = b.decode()
+    torch.cuda.synchronize()
+    assert torch.equal(a.slot_mapping, b.slot_mapping)
+    assert torch.equal(a.key_cache, b.key_cache) and torch.equal(a.value_cache, b.value_cache)
+    assert torch.equal(out_a, out_b)
+
+
 def _decode(staging, w):
     dw = staging.DeviceWorkload(w, kv_fp8=True)
     dw.scatter_new()
