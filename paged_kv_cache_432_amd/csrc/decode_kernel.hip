@@ -636,11 +636,12 @@ __device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
                    __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
 }
 
-// s_first: this wave's LDS area of G records.  The record of the wave's first
-// segment, when that segment is cut, is kept there and written out with the
-// last one when the share is done: during the share the only global writes are
-// the rows of whole segments (records written in the middle of the read stream
-// measured 4-10% slower decode calls).
+// s_first: this wave's LDS area of 2 x G records.  The record of the wave's
+// first segment, when that segment is cut, is kept there and written out with
+// the last one when the share is done: during the share the only global writes
+// are the rows of whole segments (records written in the middle of the read
+// stream measured 4-10% slower decode calls).  The last segment's record, when
+// cut, is staged in the second half, so that both leave as coalesced stores.
 template <int G, bool NT, int NBUF, bool F8 = false, bool AP = false>
 __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int32_t* s_pref, int4* s_tab, int64_t u0,
                                                   int64_t u1, int W, int NG, int wi, int lane, float* s_first) {
@@ -863,12 +864,20 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
             }
         }
     }
-    finish_segment();
-    if (first_in_lds) {                                // wave-uniform; the same wave wrote the area
-        f32x4_t* dst = reinterpret_cast<f32x4_t*>(a.part + (((int64_t)blockIdx.x * 2) * W + wi) * G * kRec);
-        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(s_first);
+    // Records leave LDS as whole consecutive 16-byte pieces per lane (1 KB per
+    // store instruction); the last segment's record, when cut, goes the same way.
+    auto copy_out = [&](const float* src_lds, int slot) {
+        f32x4_t* dst = reinterpret_cast<f32x4_t*>(a.part + (((int64_t)blockIdx.x * 2 + slot) * W + wi) * G * kRec);
+        const f32x4_t* src = reinterpret_cast<const f32x4_t*>(src_lds);
         for (int c = lane; c < G * kRec / 4; c += kWave) dst[c] = src[c];
+    };
+    if (!seg_whole && !seg_first) {
+        finish_mfma<G, F8>(st, lane, nullptr, s_first + G * kRec, a.out_scale);
+        copy_out(s_first + G * kRec, 1);
+    } else {
+        finish_segment();
     }
+    if (first_in_lds) copy_out(s_first, 0);            // wave-uniform; the same wave wrote the areas
 }
 
 // ---- partitioned mode ------------------------------------------------------
@@ -995,7 +1004,7 @@ decode_stream_kernel(DecodeArgs a) {
     float* pl = p_lds[MF ? 0 : wi];
     static_assert(!AP || (MF && !F8), "append mode: bf16 matrix-core path");
     if constexpr (MF) {
-        float* s_first = reinterpret_cast<float*>(s_pref + ((B + 1 + 3) & ~3)) + wi * G * kRec;
+        float* s_first = reinterpret_cast<float*>(s_pref + ((B + 1 + 3) & ~3)) + wi * 2 * G * kRec;
         stream_share_mfma<G, NT, F8 ? kFp8Depth : kMfmaDepth, F8, AP>(a, s_pref, s_tab, u0, u1, W, NG, wi, lane,
                                                                       s_first);
         return;
@@ -1201,10 +1210,10 @@ merge_stream_kernel(DecodeArgs a) {
 
 
 // Dynamic LDS of the stream kernel: the block prefix, then (matrix-core waves)
-// each wave's G first-segment records.
+// each wave's 2 x G records (first and last segment).
 size_t stream_lds_bytes(int64_t num_seqs, int waves, int G, bool mf) {
     const size_t pref = (((size_t)num_seqs + 1 + 3) & ~(size_t)3) * sizeof(int32_t);
-    return pref + (mf ? (size_t)waves * G * kRec * sizeof(float) : 0);
+    return pref + (mf ? (size_t)waves * 2 * G * kRec * sizeof(float) : 0);
 }
 
 template <typename Chunk, typename Elem, int G, bool F8 = false, bool AP = false>
