@@ -383,6 +383,11 @@ constexpr bool kMfmaWave = sizeof(Elem) == 2 && G >= PA_DECODE_MFMA_FROM;
 #define PA_DECODE_MFMA_DEPTH 3
 #endif
 constexpr int kMfmaDepth = PA_DECODE_MFMA_DEPTH;
+// K/V loads of the stream decode with the streaming (non-temporal) cache hint.
+#ifndef PA_DECODE_NT
+#define PA_DECODE_NT 1
+#endif
+constexpr bool kDecodeNT = PA_DECODE_NT != 0;
 // Blocks in flight per wave over an fp8 cache: each holds half the bytes of a
 // bf16 block, so twice as many keep the same bytes in flight.
 #ifndef PA_DECODE_FP8_DEPTH
@@ -1221,7 +1226,7 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     constexpr bool QL = kQueryInLds<G>;
     if (a.mode == kDecodeStream) {
         const size_t lds = stream_lds_bytes(a.num_seqs, a.waves_per_group, G, kMfmaWave<Elem, G>);
-        hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, true, F8, AP>), dim3((unsigned)a.num_wg),
+        hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, kDecodeNT, F8, AP>), dim3((unsigned)a.num_wg),
                            dim3(64 * a.waves_per_group), lds, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1259,7 +1264,7 @@ template <typename Chunk, typename Elem, int G, bool F8, bool AP>
 int stream_blocks_per_cu(int waves_per_group, int64_t num_seqs) {
     const size_t lds = stream_lds_bytes(num_seqs, waves_per_group, G, kMfmaWave<Elem, G>);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, true, F8, AP>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, kDecodeNT, F8, AP>,
                                                      64 * waves_per_group, lds) != hipSuccess)
         return 0;
     return n;
