@@ -1,0 +1,86 @@
+"""The decode step replayed from a captured HIP graph (torch.cuda.CUDAGraph is
+PyTorch-ROCm's HIP graph API): pa_decode_append, and pa_slot_mapping_and_cache
+followed by pa_decode, captured once and replayed several times with eager work
+and synchronisations between the replays.  Every replay must give exactly the
+eager result (same kernels, same inputs), and the eager result matches the
+oracle.  The library issues no memset and allocates nothing, so the calls
+capture as they run."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import assert_parity, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def staging():
+    import paged_kv_cache_432_amd as pa
+    pa.lib()
+    from paged_kv_cache_432_amd import staging
+    return staging
+
+
+def _capture(fn):
+    """Warm up on a side stream, then capture fn() into a graph."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
+
+
+@pytest.mark.parametrize("mode", ["append", "two_call"])
+def test_decode_step_graph_replays(staging, mode):
+    w = W.custom("graph", seq_lens=[1, 40, 300, 1025, 2048, 0, 4097, 77], dtype="bf16", seed=80)
+    dw = staging.DeviceWorkload(w)
+    out = torch.empty_like(dw.query)
+    ws = dw.decode_workspace(0)
+    if mode == "append":
+        dw.append_rows()                                  # the newest rows, allocated before capture
+        step = lambda: dw.decode_append(out, ws)
+    else:
+        step = lambda: (dw.scatter_new(fused=True), dw.decode(out, 0, ws))
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert_parity(to_numpy(eager), oracle.run(w), "bf16", f"graph {mode}: eager step")
+    g = _capture(step)
+    for r in range(4):
+        out.fill_(float("nan"))                           # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        print(f"  replay {r}: max |diff| {(out.float() - eager.float()).abs().max().item():.3e}", flush=True)
+        assert torch.equal(out, eager), f"replay {r}"
+    # the caches hold exactly the oracle's scatter after the replays
+    okc, ovc = oracle.build_cache(w, "all")
+    assert np.array_equal(dw.key_cache.cpu().view(torch.int16).numpy().view(np.uint16), okc)
+    assert np.array_equal(dw.value_cache.cpu().view(torch.int16).numpy().view(np.uint16), ovc)
+
+
+def test_fp8_step_graph_replays(staging):
+    w = W.custom("graph_fp8", seq_lens=[3, 500, 1500, 16, 17], dtype="bf16", seed=81)
+    dw = staging.DeviceWorkload(w, kv_fp8=True)
+    out = torch.empty_like(dw.query)
+    ws = dw.decode_workspace(0)
+    step = lambda: (dw.scatter_new(fused=True), dw.decode(out, 0, ws))
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    g = _capture(step)
+    for r in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
