@@ -82,8 +82,10 @@ constexpr int kBlkPerThr = 4 / kThrGroups;
 // before its commit; with one (the 4-wave workgroup, whose threads stage twice
 // the blocks), one tile before.
 constexpr int kStageSets = kThrGroups == 2 ? 2 : 1;
-// Merge workgroups per listed tile (64 rows each).
-constexpr int kMergeParts = kPrefillRows / 64;
+// Merge workgroups per listed tile: 8 rows each, one per 32-thread group, so
+// that each thread merges one row (the merge is bound by reading the records).
+constexpr int kMergeRows = 8;
+constexpr int kMergeParts = kPrefillRows / kMergeRows;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
 __device__ __forceinline__ f16x8_t as_f16x8(u32x4_t w) { return __builtin_bit_cast(f16x8_t, w); }
@@ -633,8 +635,8 @@ prefill_kernel(PrefillArgs a) {
 
 // Log-sum-exp merge of the segments of every listed query tile: per row,
 // M = max_p m_p, out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p, taken in
-// one pass with a running max.  Four workgroups per listed (tile, KV head),
-// 64 rows each; thread i covers dims 4(i % 32) .. +4 of rows i / 32 + 8k.
+// one pass with a running max.  kMergeParts workgroups per listed (tile, KV
+// head), 8 rows each; thread i covers dims 4(i % 32) .. +4 of row i / 32.
 template <int G>
 __global__ void __launch_bounds__(256)
 prefill_merge_kernel(PrefillArgs a) {
@@ -644,8 +646,8 @@ prefill_merge_kernel(PrefillArgs a) {
     const int s0 = d.x, np = d.y & 0xffffff, rec0 = d.y >> 24, row0 = d.z, ntok = d.w >> 8, kvh = d.w & 255;
     const int Hkv = a.num_kv_heads;
     const int d4 = 4 * (threadIdx.x & 31);
-    const int rbeg = 64 * (int)(blockIdx.x % kMergeParts);
-    for (int r = rbeg + (int)(threadIdx.x >> 5); r < rbeg + 64; r += 8) {
+    const int rbeg = kMergeRows * (int)(blockIdx.x % kMergeParts);
+    for (int r = rbeg + (int)(threadIdx.x >> 5); r < rbeg + kMergeRows; r += 8) {
         const int tq = r / G;
         if (tq >= ntok) break;                         // rows are token-major: the rest are inactive
         float mrun = -INFINITY, lrun = 0.f;
