@@ -1,7 +1,8 @@
-"""The decode step replayed from a captured HIP graph (torch.cuda.CUDAGraph is
-PyTorch-ROCm's HIP graph API): pa_decode_append, and pa_slot_mapping_and_cache
-followed by pa_decode, captured once and replayed several times with eager work
-and synchronisations between the replays.  Every replay must give exactly the
+"""Steps replayed from a captured HIP graph (torch.cuda.CUDAGraph is
+PyTorch-ROCm's HIP graph API): pa_decode_append; pa_slot_mapping_and_cache
+followed by pa_decode (bf16 and fp8 caches); and pa_chunked_prefill. Each is
+captured once and replayed several times, with eager work and synchronisations
+between the replays.  Every replay must give exactly the
 eager result (same kernels, same inputs), and the eager result matches the
 oracle.  The library issues no memset and allocates nothing, so the calls
 capture as they run."""
@@ -80,6 +81,31 @@ def test_fp8_step_graph_replays(staging):
     g = _capture(step)
     for r in range(3):
         out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {r}"
+
+
+def test_chunked_prefill_graph_replays(staging):
+    """The mixed call (prefill chunks split over several tiles, decodes, a
+    request with no rows this step) captured and replayed: the split-tile merge
+    reads only what the same replay wrote into the workspace."""
+    w = W.custom("graph_prefill", seq_lens=[600, 90, 1, 64, 1300, 2], query_lens=[600, 17, 1, 0, 300, 2],
+                 dtype="bf16", seed=82, causal=True)
+    dw = staging.DeviceWorkload(w)
+    dw.scatter_new()
+    out = torch.empty_like(dw.query)
+    ws = dw.prefill_workspace()
+    step = lambda: dw.chunked_prefill(out, ws)
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    assert_parity(to_numpy(eager), oracle.run(w), "bf16", "graph prefill: eager call")
+    g = _capture(step)
+    for r in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(255)                                     # stale workspace between replays
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
