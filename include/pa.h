@@ -38,6 +38,11 @@
  *   - Supported now: block_size 16, head_dim 128, num_heads / num_kv_heads in
  *     {1, 2, 4, 8}, dtype PA_F32 or PA_BF16 (Q, K, V, caches and outputs all of
  *     that dtype; arithmetic in fp32).  Other values return PA_ERR_UNSUPPORTED.
+ *   - The softmax scale of every attention call (pa_decode, pa_decode_append,
+ *     pa_decode_fp8, pa_chunked_prefill) must be finite and > 0 (the pages'
+ *     1 / sqrt(d_k)); anything else returns PA_ERR_INVALID_ARG.  The kernels
+ *     take the running maximum of the raw scores as the softmax reference,
+ *     which is the maximum of the scaled scores only for a positive scale.
  *   - Functions are thread-safe; the only global state is a per-thread error
  *     message.
  */
@@ -406,7 +411,10 @@ pa_status pa_decode(void *out, const void *query, int64_t q_token_stride,
  * key_cache, value_cache  written at those slots only.
  * Other arguments as for pa_decode; the workspace is
  * pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim,
- * max_seq_len, 0) bytes.  seq_lens[b] counts the newest token.
+ * max_seq_len, 0) bytes.  seq_lens[b] counts the newest token.  Every check
+ * (the workspace's size and alignment included) runs before the first launch
+ * on both routes: a call that returns an error has written neither the caches
+ * nor slot_mapping.
  */
 pa_status pa_decode_append(void *out, const void *query, int64_t q_token_stride,
                            const void *key, int64_t key_token_stride,

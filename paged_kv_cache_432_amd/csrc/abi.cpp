@@ -470,20 +470,32 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
 
 namespace {
 
-// Checks shared by pa_decode and pa_chunked_prefill, then the decode launch
-// (cu_q != nullptr: only the single-row sequences of a mixed batch).
-pa_status decode_common(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+// A decode launch whose arguments have passed every check: what
+// plan_decode fills in and launch_planned enqueues.
+struct DecodePlan {
+    pa::DecodeArgs a;
+    int dt;
+    int group;
+};
+
+// Checks shared by pa_decode and pa_chunked_prefill (grid, workspace size and
+// alignment) and the kernel arguments, without launching anything (cu_q !=
+// nullptr: only the single-row sequences of a mixed batch).
+pa_status plan_decode(DecodePlan& plan, void* out, const void* query, int64_t q_token_stride, const void* key_cache,
                         const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
                         const int32_t* seq_lens, const int32_t* cu_q, int32_t num_seqs, int32_t num_heads,
                         int32_t num_kv_heads, int64_t num_blocks, float scale, int32_t max_seq_len,
                         int32_t partition_tokens, void* workspace, size_t workspace_bytes, int dt, float k_scale,
-                        float v_scale, hipStream_t stream, const void* new_key = nullptr,
-                        int64_t new_key_stride_bytes = 0, const void* new_value = nullptr,
-                        int64_t new_value_stride_bytes = 0, int64_t* slot_out = nullptr) {
+                        float v_scale, const void* new_key = nullptr, int64_t new_key_stride_bytes = 0,
+                        const void* new_value = nullptr, int64_t new_value_stride_bytes = 0,
+                        int64_t* slot_out = nullptr) {
     // dt: 0 fp32, 1 bf16, 2 fp8 cache (bf16 query and output, stream mode only),
     // 3 bf16 in append mode (stream mode only; the new_* rows and slot_out)
     const int32_t group = num_heads / num_kv_heads;
-    pa::DecodeArgs a{};
+    plan.dt = dt;
+    plan.group = group;
+    pa::DecodeArgs& a = plan.a;
+    a = pa::DecodeArgs{};
     a.out = out;
     a.query = query;
     a.q_stride = q_token_stride;
@@ -534,7 +546,30 @@ pa_status decode_common(void* out, const void* query, int64_t q_token_stride, co
         return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0,
                     need);
     if (need > 0 && !aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
-    return hip_status(pa::launch_decode(a, dt, group, stream), "decode launch");
+    return PA_OK;
+}
+
+pa_status launch_planned(const DecodePlan& plan, hipStream_t stream) {
+    return hip_status(pa::launch_decode(plan.a, plan.dt, plan.group, stream), "decode launch");
+}
+
+// plan_decode, then its launch.
+pa_status decode_common(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+                        const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
+                        const int32_t* seq_lens, const int32_t* cu_q, int32_t num_seqs, int32_t num_heads,
+                        int32_t num_kv_heads, int64_t num_blocks, float scale, int32_t max_seq_len,
+                        int32_t partition_tokens, void* workspace, size_t workspace_bytes, int dt, float k_scale,
+                        float v_scale, hipStream_t stream, const void* new_key = nullptr,
+                        int64_t new_key_stride_bytes = 0, const void* new_value = nullptr,
+                        int64_t new_value_stride_bytes = 0, int64_t* slot_out = nullptr) {
+    DecodePlan plan;
+    const pa_status st = plan_decode(plan, out, query, q_token_stride, key_cache, value_cache, block_table,
+                                     max_blocks_per_req, seq_lens, cu_q, num_seqs, num_heads, num_kv_heads,
+                                     num_blocks, scale, max_seq_len, partition_tokens, workspace, workspace_bytes,
+                                     dt, k_scale, v_scale, new_key, new_key_stride_bytes, new_value,
+                                     new_value_stride_bytes, slot_out);
+    if (st != PA_OK) return st;
+    return launch_planned(plan, stream);
 }
 
 // Shape checks shared by the attention entry points.
@@ -564,7 +599,7 @@ pa_status pa_decode_fp8(void* out, const void* query, int64_t q_token_stride, co
     if (hs != PA_OK) return hs;
     if (num_seqs < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_req < 0)
         return fail(PA_ERR_INVALID_ARG, "negative size");
-    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if (!(isfinite(scale) && scale > 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and positive");
     if (!(isfinite(k_scale) && k_scale > 0.f && isfinite(v_scale) && v_scale > 0.f))
         return fail(PA_ERR_INVALID_ARG, "scales must be finite and positive");
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
@@ -600,7 +635,7 @@ pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const 
     if (partition_tokens < -1 || (partition_tokens > 0 && partition_tokens % 16))
         return fail(PA_ERR_INVALID_ARG, "partition_tokens %d (0, -1 or a positive multiple of 16)",
                     partition_tokens);
-    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if (!(isfinite(scale) && scale > 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and positive");
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
         return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
     if (num_seqs == 0) return ok();
@@ -630,7 +665,7 @@ pa_status pa_decode_append(void* out, const void* query, int64_t q_token_stride,
     if (hs != PA_OK) return hs;
     if (num_seqs < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_req < 0)
         return fail(PA_ERR_INVALID_ARG, "negative size");
-    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if (!(isfinite(scale) && scale > 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and positive");
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
         return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
     if (num_seqs == 0) return ok();
@@ -655,16 +690,21 @@ pa_status pa_decode_append(void* out, const void* query, int64_t q_token_stride,
                              value_token_stride * eb, slot_mapping);
     // fp32, or more sequences than the stream mode takes: the newest rows are
     // scattered first (token b of sequence b at position seq_lens[b] - 1), then
-    // the plain decode reads them from the cache
-    const pa_status st = hip_status(
+    // the plain decode reads them from the cache.  The decode is planned (grid,
+    // workspace) before the scatter is enqueued, so a failed check writes
+    // nothing.
+    DecodePlan plan;
+    pa_status st = plan_decode(plan, out, query, q_token_stride, key_cache, value_cache, block_table,
+                               max_blocks_per_req, seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks,
+                               scale, max_seq_len, 0, workspace, workspace_bytes, dtype == PA_BF16 ? 1 : 0, 1.f, 1.f);
+    if (st != PA_OK) return st;
+    st = hip_status(
         pa::launch_slot_and_cache(slot_mapping, block_table, max_blocks_per_req, num_seqs, nullptr, seq_lens, key,
                                   key_token_stride * eb, value, value_token_stride * eb, key_cache, value_cache,
                                   num_seqs, num_blocks * 16, (int32_t)(row_elems * eb), stream),
         "slot_and_cache launch");
     if (st != PA_OK) return st;
-    return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
-                         seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len, 0,
-                         workspace, workspace_bytes, dtype == PA_BF16 ? 1 : 0, 1.f, 1.f, stream);
+    return launch_planned(plan, stream);
 }
 
 size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,
@@ -693,7 +733,7 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
         return fail(PA_ERR_INVALID_ARG, "negative size");
     if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal %d (0 or 1)", causal);
     if (num_kv_heads > 255) return fail(PA_ERR_UNSUPPORTED, "num_kv_heads %d (at most 255)", num_kv_heads);
-    if (!isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale is not finite");
+    if (!(isfinite(scale) && scale > 0.f)) return fail(PA_ERR_INVALID_ARG, "scale must be finite and positive");
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
         return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
     if (num_seqs == 0 || num_q_tokens == 0) return ok();

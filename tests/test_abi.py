@@ -59,6 +59,8 @@ def _decode(L, **kw):
     (dict(q_token_stride=100), pa.PA_ERR_INVALID_ARG),
     (dict(query=24), pa.PA_ERR_INVALID_ARG),                           # misaligned
     (dict(scale=float("nan")), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=0.0), pa.PA_ERR_INVALID_ARG),                          # the scale must be > 0
+    (dict(scale=-0.088), pa.PA_ERR_INVALID_ARG),
     (dict(partition_tokens=32), pa.PA_ERR_WORKSPACE),                  # split without workspace
     (dict(num_seqs=-1), pa.PA_ERR_INVALID_ARG),
 ])
@@ -93,6 +95,8 @@ def _decode_append(L, **kw):
     (dict(key=24), pa.PA_ERR_INVALID_ARG),                             # misaligned
     (dict(max_seq_len=200), pa.PA_ERR_INVALID_ARG),                    # beyond the table
     (dict(scale=float("nan")), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=0.0), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=-0.088), pa.PA_ERR_INVALID_ARG),
     (dict(num_seqs=-1), pa.PA_ERR_INVALID_ARG),
 ])
 def test_decode_append_rejects_before_launch(L, kw, status):
@@ -168,6 +172,8 @@ def _prefill(L, **kw):
     (dict(query=8), pa.PA_ERR_INVALID_ARG),
     (dict(num_q_tokens=-1), pa.PA_ERR_INVALID_ARG),
     (dict(scale=float("inf")), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=0.0), pa.PA_ERR_INVALID_ARG),
+    (dict(scale=-0.088), pa.PA_ERR_INVALID_ARG),
 ])
 def test_chunked_prefill_rejects_before_launch(L, kw, status):
     assert _prefill(L, **kw) == status
@@ -247,6 +253,8 @@ def test_fp8_entries_reject_before_launch(L):
 
     assert dec(b=0) == pa.PA_OK
     assert dec(ks=-1.0) == pa.PA_ERR_INVALID_ARG
+    assert dec(scale=-0.088) == pa.PA_ERR_INVALID_ARG        # the softmax scale must be > 0
+    assert dec(scale=0.0) == pa.PA_ERR_INVALID_ARG
     assert dec(vs=float("nan")) == pa.PA_ERR_INVALID_ARG
     assert dec(b=5000) == pa.PA_ERR_UNSUPPORTED              # past the stream mode's sequence limit
     assert dec(d=64) == pa.PA_ERR_UNSUPPORTED
