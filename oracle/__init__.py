@@ -285,12 +285,23 @@ def build_cache(w, which: str = "all", caches=None):
         kc, vc = w.poisoned_cache(), w.poisoned_cache()
     else:
         kc, vc = caches
-    seq, pos = w.tokens(which)
-    if len(seq):
-        slots = slot_mapping(w.block_table, seq, pos, w.block_size)
-        k, v = w.token_kv(seq, pos)
-        reshape_and_cache(w.encode(k), w.encode(v), kc, vc, slots, w.block_size)
+    for _, k, v, slots in _token_rows(w, which):
+        reshape_and_cache(k, v, kc, vc, slots, w.block_size)
     return kc, vc
+
+
+def _token_rows(w, which: str):
+    """Per sequence with tokens to write: (b, K rows, V rows, slots), the rows
+    in storage format, the slots from this module's slot function over the
+    workload's block table.  Values are drawn a few sequences ahead on worker
+    threads (workloads.iter_kv), so a full-size pool is built in seconds."""
+    seq, pos = w.tokens(which)
+    if not len(seq):
+        return
+    for b, k, v in w.iter_kv(np.unique(seq), encode=True):
+        p = pos[seq == b]
+        slots = slot_mapping(w.block_table, np.full(len(p), b, np.int32), p, w.block_size)
+        yield b, k[p], v[p], slots
 
 
 def build_cache_fp8(w, k_scale: float, v_scale: float, which: str = "all"):
@@ -298,11 +309,8 @@ def build_cache_fp8(w, k_scale: float, v_scale: float, which: str = "all"):
     first) through the fp8 scatter."""
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
     kc, vc = np.full(shape, 0x7F, np.uint8), np.full(shape, 0x7F, np.uint8)
-    seq, pos = w.tokens(which)
-    if len(seq):
-        slots = slot_mapping(w.block_table, seq, pos, w.block_size)
-        k, v = w.token_kv(seq, pos)
-        reshape_and_cache_fp8(w.encode(k), w.encode(v), kc, vc, slots, k_scale, v_scale, w.block_size)
+    for _, k, v, slots in _token_rows(w, which):
+        reshape_and_cache_fp8(k, v, kc, vc, slots, k_scale, v_scale, w.block_size)
     return kc, vc
 
 
@@ -330,8 +338,7 @@ def run_sequences(w, seqs, fp8_scales=None):
     the whole pool.  With fp8_scales = (k_scale, v_scale) the cache is E4M3.
     Returns {seq: [query_len, Hq, D] fp64}."""
     res = {}
-    for b in seqs:
-        b = int(b)
+    for b, k, v in w.iter_kv(seqs, encode=True):
         L = int(w.seq_lens[b])
         nblk = (L + w.block_size - 1) // w.block_size
         table = np.arange(max(nblk, 1), dtype=np.int32)[None, :]
@@ -343,14 +350,12 @@ def run_sequences(w, seqs, fp8_scales=None):
         else:
             kc = np.full(shape, np.nan, np.float32)
         vc = kc.copy()
-        k, v = w.kv(b)
         pos = np.arange(L, dtype=np.int32)
         slots = slot_mapping(table, np.zeros(L, np.int32), pos, w.block_size)
         if fp8_scales is not None:
-            reshape_and_cache_fp8(w.encode(k), w.encode(v), kc, vc, slots, fp8_scales[0], fp8_scales[1],
-                                  w.block_size)
+            reshape_and_cache_fp8(k, v, kc, vc, slots, fp8_scales[0], fp8_scales[1], w.block_size)
         else:
-            reshape_and_cache(w.encode(k), w.encode(v), kc, vc, slots, w.block_size)
+            reshape_and_cache(k, v, kc, vc, slots, w.block_size)
         q = w.encode(w.query(b))
         cu = np.array([0, q.shape[0]], np.int32)
         ks, vs = fp8_scales if fp8_scales is not None else (1.0, 1.0)

@@ -365,12 +365,37 @@ void oracle_reshape_and_cache_fp8(const void *key, int64_t key_stride, const voi
                                   int32_t dtype, float k_scale, float v_scale)
 {
     const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+    /* bf16 sources have 65536 bit patterns: the code of each (the same
+     * encode(x / scale) as below) is worked out once per pair of scales, and
+     * looked up.  Not thread-safe: the oracle's scatter runs on one thread. */
+    static uint8_t kcode_memo[65536], vcode_memo[65536];
+    static float memo_k = 0.f, memo_v = 0.f;
+    static int memo_valid = 0;
+    const uint8_t *kcode = NULL, *vcode = NULL;
+    if (dtype == ORACLE_BF16) {
+        if (!memo_valid || memo_k != k_scale || memo_v != v_scale) {
+            for (int32_t u = 0; u < 65536; u++) {
+                uint16_t bits = (uint16_t)u;
+                float x = (float)widen(&bits, 0, ORACLE_BF16);
+                kcode_memo[u] = oracle_e4m3_encode(x / k_scale);
+                vcode_memo[u] = oracle_e4m3_encode(x / v_scale);
+            }
+            memo_k = k_scale, memo_v = v_scale, memo_valid = 1;
+        }
+        kcode = kcode_memo;
+        vcode = vcode_memo;
+    }
     for (int64_t i = 0; i < num_tokens; i++) {
         int64_t s = slot_mapping[i];
         if (s < 0)
             continue;
         int64_t dst = ((s / block_size) * block_size + s % block_size) * row_elems;
         for (int64_t e = 0; e < row_elems; e++) {
+            if (kcode) {
+                key_cache[dst + e] = kcode[((const uint16_t *)key)[i * key_stride + e]];
+                value_cache[dst + e] = vcode[((const uint16_t *)value)[i * value_stride + e]];
+                continue;
+            }
             float k = (float)widen(key, i * key_stride + e, dtype);
             float v = (float)widen(value, i * value_stride + e, dtype);
             key_cache[dst + e] = oracle_e4m3_encode(k / k_scale);

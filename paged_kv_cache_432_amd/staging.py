@@ -26,12 +26,38 @@ def _upload(x: np.ndarray, dtype, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x)).to(device).to(dtype)
 
 
+GUARD_BYTE = 0xA5
+
+
+class Guarded:
+    """A contiguous device tensor placed inside a larger byte buffer whose
+    margins (guard_bytes before and after it, rounded up to 256) hold a fixed
+    byte pattern: a kernel that writes outside the tensor changes the pattern,
+    which intact() reports.  The tensor starts 256-byte aligned."""
+
+    def __init__(self, shape, dtype, device, guard_bytes: int = 4096):
+        self.shape = tuple(int(x) for x in shape)
+        itemsize = torch.empty(0, dtype=dtype).element_size()
+        self.nbytes = int(np.prod(self.shape, dtype=np.int64)) * itemsize
+        self.guard = ((int(guard_bytes) + 255) // 256) * 256
+        self.buf = torch.full((self.guard + self.nbytes + self.guard,), GUARD_BYTE, dtype=torch.uint8,
+                              device=device)
+        self.t = self.buf[self.guard:self.guard + self.nbytes].view(dtype).view(self.shape)
+
+    def intact(self) -> bool:
+        return bool(torch.all(self.buf[:self.guard] == GUARD_BYTE).item()
+                    and torch.all(self.buf[self.guard + self.nbytes:] == GUARD_BYTE).item())
+
+
 class DeviceWorkload:
     """Device-resident inputs and paged cache of one workload step."""
 
-    def __init__(self, w, device="cuda", fill_history: bool = True, poison: bool = True, kv_fp8: bool = False):
+    def __init__(self, w, device="cuda", fill_history: bool = True, poison: bool = True, kv_fp8: bool = False,
+                 guard_bytes: int = 0):
         """kv_fp8: the caches hold E4M3 codes (uint8) written by the fp8 scatter
-        with the workload's fp8_scales(); queries and outputs stay bf16."""
+        with the workload's fp8_scales(); queries and outputs stay bf16.
+        guard_bytes > 0: each cache sits between guard zones (Guarded), checked
+        by guards_intact()."""
         self.w = w
         self.device = torch.device(device)
         self.dtype = _TORCH_DTYPE[w.dtype]
@@ -40,13 +66,20 @@ class DeviceWorkload:
             assert w.dtype == "bf16", "an fp8 cache goes with bf16 queries"
             self.k_scale, self.v_scale = w.fp8_scales()
         shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
-        if kv_fp8:
-            self.key_cache = torch.full(shape, 0x7F if poison else 0, dtype=torch.uint8, device=self.device)
-            self.value_cache = torch.full(shape, 0x7F if poison else 0, dtype=torch.uint8, device=self.device)
+        cdt = torch.uint8 if kv_fp8 else self.dtype
+        if guard_bytes > 0:
+            self._guards = [Guarded(shape, cdt, self.device, guard_bytes) for _ in range(2)]
+            self.key_cache, self.value_cache = (g.t for g in self._guards)
         else:
-            fill = float("nan") if poison else 0.0
-            self.key_cache = torch.full(shape, fill, dtype=self.dtype, device=self.device)
-            self.value_cache = torch.full(shape, fill, dtype=self.dtype, device=self.device)
+            self._guards = []
+            self.key_cache = torch.empty(shape, dtype=cdt, device=self.device)
+            self.value_cache = torch.empty(shape, dtype=cdt, device=self.device)
+        if kv_fp8:
+            self.key_cache.fill_(0x7F if poison else 0)
+            self.value_cache.fill_(0x7F if poison else 0)
+        else:
+            self.key_cache.fill_(float("nan") if poison else 0.0)
+            self.value_cache.fill_(float("nan") if poison else 0.0)
         self.block_table = torch.from_numpy(np.ascontiguousarray(w.block_table, np.int32)).to(self.device)
         self.seq_lens = torch.from_numpy(np.ascontiguousarray(w.seq_lens, np.int32)).to(self.device)
         self.cu_query_lens = torch.from_numpy(w.cu_query_lens).to(self.device)
@@ -59,11 +92,10 @@ class DeviceWorkload:
         new_k = np.empty((n, hkv, d), np.float32)
         new_v = np.empty((n, hkv, d), np.float32)
         cursor = 0
-        for b in range(w.num_seqs):
+        # values drawn a few sequences ahead on host threads; uploads and
+        # scatters stay in order on this thread
+        for b, k, v in w.iter_kv(np.flatnonzero(np.asarray(w.seq_lens) > 0)):
             h, L = int(w.history_lens[b]), int(w.seq_lens[b])
-            if L == 0:
-                continue
-            k, v = w.kv(b)
             if fill_history and h > 0:
                 self._write(b, k[:h], v[:h], 0)
             q = L - h
@@ -73,6 +105,11 @@ class DeviceWorkload:
         assert cursor == n
         self.new_k = _upload(new_k, self.dtype, self.device)
         self.new_v = _upload(new_v, self.dtype, self.device)
+
+    def guards_intact(self) -> bool:
+        """True when the guard zones around both caches are unchanged (always
+        True without guards)."""
+        return all(g.intact() for g in self._guards)
 
     def _write(self, b: int, k: np.ndarray, v: np.ndarray, start: int) -> None:
         n = k.shape[0]

@@ -24,12 +24,51 @@ Value recipe (documented once here, used everywhere):
 from __future__ import annotations
 
 import math
+import os
+from collections import deque
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field
 
 import numpy as np
 
 BLOCK_SIZE = 16
 BF16_NAN_BITS = 0x7FC0
+
+
+# ------------------------------------------------------------ parallel draws --
+def draw_threads() -> int:
+    """Threads for drawing values: the OpenMP share of the job if one is set,
+    else the CPUs this process may run on (at most 16)."""
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        return int(env)
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def prefetch_map(fn, items, threads: int | None = None, depth: int | None = None):
+    """Yield fn(item) for each item, in order, computed on a thread pool at most
+    `depth` items ahead of the consumer (numpy's generators and array
+    arithmetic release the GIL, so the draws of different sequences overlap).
+    The bounded look-ahead keeps only a few sequences' values in memory."""
+    items = list(items)
+    threads = threads or draw_threads()
+    depth = depth or 2 * threads
+    if threads <= 1 or len(items) <= 1:
+        for it in items:
+            yield fn(it)
+        return
+    with ThreadPoolExecutor(threads) as ex:
+        pending = deque()
+        nxt = 0
+        while nxt < len(items) and len(pending) < depth:
+            pending.append(ex.submit(fn, items[nxt]))
+            nxt += 1
+        while pending:
+            res = pending.popleft().result()
+            if nxt < len(items):
+                pending.append(ex.submit(fn, items[nxt]))
+                nxt += 1
+            yield res
 
 
 # ---------------------------------------------------------------- encodings --
@@ -152,6 +191,18 @@ class Workload:
             self._kv_cache[key] = (k, v)
         return k, v
 
+    def iter_kv(self, seqs=None, encode: bool = False):
+        """Yield (b, k, v) for each sequence b of `seqs` (default: all), in order,
+        with each sequence's K and V as kv(b) draws them (or their storage
+        encoding if `encode`), drawn a few sequences ahead on worker threads."""
+        seqs = range(self.num_seqs) if seqs is None else [int(b) for b in seqs]
+
+        def one(b):
+            k, v = self.kv(b)
+            return (b, self.encode(k), self.encode(v)) if encode else (b, k, v)
+
+        yield from prefetch_map(one, seqs)
+
     def query(self, b: int) -> np.ndarray:
         """Q rows of sequence b for this step: float32 [query_len_b, Hq, D]."""
         h = int(self.history_lens[b])
@@ -188,9 +239,10 @@ class Workload:
         n = len(seq)
         k = np.empty((n, self.num_kv_heads, self.head_dim), np.float32)
         v = np.empty_like(k)
-        for b in np.unique(seq):
+        seq = np.asarray(seq)
+        pos = np.asarray(pos)
+        for b, kb, vb in self.iter_kv(np.unique(seq)):
             idx = np.nonzero(seq == b)[0]
-            kb, vb = self.kv(int(b))
             k[idx] = kb[pos[idx]]
             v[idx] = vb[pos[idx]]
         return k, v
