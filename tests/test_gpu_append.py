@@ -5,12 +5,14 @@ copy of section "Reshape & Cache") and attends over the whole sequence.
 
 The slots and the caches are compared bit for bit with the oracle's slot
 function and scatter; the outputs element by element with the oracle's
-attention (small workloads) or on sampled sequences (full sizes), and with the
+attention, at small sizes and at the full workload sizes (every row, with
+guard zones around the output, the workspace and the caches), and with the
 two-call step (pa_slot_mapping_and_cache, then pa_decode) on the same inputs."""
 import numpy as np
 import pytest
 import torch
 
+import fullsize
 import oracle
 import workloads as W
 from parity import assert_parity, storage_bits, to_numpy
@@ -145,32 +147,68 @@ def test_many_sequences_take_two_launches(staging):
     _step(staging, w, "4100 sequences")
 
 
-def _sampled(staging, w, seqs):
-    """Full-size workload: outputs of sampled sequences against the oracle, and
-    the whole caches against the two-call step's."""
-    print(f"  full size {w.name}: sequences {seqs}", flush=True)
-    a = staging.DeviceWorkload(w)
-    out = a.decode_append()
-    b = staging.DeviceWorkload(w)
-    b.scatter_new(fused=True)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_failed_workspace_check_writes_nothing(staging, dtype):
+    """fp32 takes two launches (the scatter, then the decode), bf16 one.  On
+    both routes an undersized workspace is found before anything is enqueued:
+    the call fails with PA_ERR_WORKSPACE and the caches and slot_mapping are
+    unchanged byte for byte."""
+    import paged_kv_cache_432_amd as pa
+    w = W.custom("ws_check", seq_lens=[40, 700, 1300, 17], dtype=dtype, seed=55)
+    dw = staging.DeviceWorkload(w)
+    _, _, slots = dw.append_rows()
+    slots.fill_(-7)
+    before = [t.clone() for t in (dw.key_cache, dw.value_cache, slots)]
+    nbytes = dw.decode_workspace(0).numel()
+    assert nbytes > 16
+    small = torch.empty(nbytes - 16, dtype=torch.uint8, device=dw.device)
+    with pytest.raises(pa.PaError) as e:
+        dw.decode_append(workspace=small)
+    assert e.value.status == pa.PA_ERR_WORKSPACE, e.value
     torch.cuda.synchronize()
-    _, _, slots = a.append_rows()
-    assert torch.equal(slots, b.slot_mapping)        # every sequence has L > 0 here
+    for a, b in zip(before, (dw.key_cache, dw.value_cache, slots)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    # the same call with the full workspace then writes and attends as usual
+    out = dw.decode_append(workspace=torch.empty(nbytes, dtype=torch.uint8, device=dw.device))
+    torch.cuda.synchronize()
     assert np.array_equal(slots.cpu().numpy(), _expected_slots(w))
-    assert torch.equal(a.key_cache.view(torch.int16), b.key_cache.view(torch.int16))
-    assert torch.equal(a.value_cache.view(torch.int16), b.value_cache.view(torch.int16))
-    del b
-    o = to_numpy(out)
-    ref = oracle.run_sequences(w, seqs)
-    for s in seqs:
-        assert_parity(o[s:s + 1], ref[s], w.dtype, f"{w.name} seq {s} (L={int(w.seq_lens[s])})")
+    assert_parity(to_numpy(out), oracle.run(w), w.dtype, f"ws_check {dtype}")
+
+
+def _full(staging, w):
+    """Full-size workload in the benchmark's launch configuration: slots bit
+    for bit against the oracle's slot function, both whole caches byte for byte
+    against the oracle's scatter of every token (history and newest), every
+    output row against the oracle; out, workspace and caches between guard
+    zones."""
+    print(f"  full size {w.name}: B={w.num_seqs} Hq={w.num_heads} KV tokens {int(w.seq_lens.sum())}", flush=True)
+    dw = staging.DeviceWorkload(w, guard_bytes=1 << 16)
+    out = staging.Guarded(dw.query.shape, dw.query.dtype, dw.device)
+    nbytes = dw.decode_workspace(0).numel()
+    ws = staging.Guarded((nbytes,), torch.uint8, dw.device, 1 << 16)
+    dw.decode_append(out.t, ws.t)
+    torch.cuda.synchronize()
+    assert out.intact() and ws.intact() and dw.guards_intact(), f"{w.name}: guard zone written"
+    _, _, slots = dw.append_rows()
+    assert np.array_equal(slots.cpu().numpy(), _expected_slots(w))
+    okc, ovc = fullsize.oracle_cache(w)
+    assert fullsize.same_bytes(dw.key_cache, okc), f"{w.name}: key cache"
+    assert fullsize.same_bytes(dw.value_cache, ovc), f"{w.name}: value cache"
+    del okc, ovc
+    fullsize.assert_rows(out.t, fullsize.oracle_output(w), w, f"{w.name} append")
 
 
 def test_llama8b_decode_full_size(staging):
-    w = W.llama8b_decode()
-    _sampled(staging, w, [int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 7, 33])
+    _full(staging, W.llama8b_decode())
+
+
+def test_llama8b_decode_8k_full_size(staging):
+    _full(staging, W.llama8b_decode_8k())
+
+
+def test_long_context_full_size(staging):
+    _full(staging, W.long_context())
 
 
 def test_continuous_batching_full_size(staging):
-    w = W.continuous_batching()
-    _sampled(staging, w, [int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 100, 200])
+    _full(staging, W.continuous_batching())

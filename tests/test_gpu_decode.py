@@ -1,10 +1,12 @@
 """Rows a3-a9 on the GPU: paged decode attention (single pass and split +
-merge) against the oracle, element by element at small sizes and on sampled
-sequences at the full workload sizes."""
+merge) against the oracle, element by element, at small sizes and at the full
+workload sizes (every output row), with guard zones around the output, the
+workspace and the caches."""
 import numpy as np
 import pytest
 import torch
 
+import fullsize
 import oracle
 import workloads as W
 from parity import assert_parity, storage_bits, to_numpy
@@ -114,45 +116,56 @@ def test_single_token_returns_value_row(staging):
         assert np.array_equal(got[b], want)
 
 
-def _sampled(staging, w, seqs, pt=0):
-    """Full-size workload on the GPU in the benchmark's launch configuration;
-    the oracle recomputes a few sequences one by one."""
-    dw, out = _run(staging, w, pt)
-    o = to_numpy(out)
-    assert np.all(np.isfinite(o))
-    ref = oracle.run_sequences(w, seqs)
-    for b in seqs:
-        assert_parity(o[b:b + 1], ref[b], w.dtype, f"{w.name} seq {b} (L={int(w.seq_lens[b])})")
-    return dw, o
+def _full(staging, w, pts=(0,)):
+    """Full-size workload on the GPU in the benchmark's launch configuration,
+    every output row against the oracle; out, workspace and caches between
+    guard zones."""
+    print(f"  full size {w.name}: B={w.num_seqs} Hq={w.num_heads} KV tokens {int(w.seq_lens.sum())}", flush=True)
+    dw = staging.DeviceWorkload(w, guard_bytes=1 << 16)
+    dw.scatter_new()
+    ref = fullsize.oracle_output(w)
+    for pt in pts:
+        out = staging.Guarded(dw.query.shape, dw.query.dtype, dw.device)
+        nbytes = dw.decode_workspace(pt).numel()
+        ws = staging.Guarded((nbytes,), torch.uint8, dw.device, 1 << 16)
+        dw.decode(out.t, pt, ws.t)
+        torch.cuda.synchronize()
+        assert out.intact() and ws.intact() and dw.guards_intact(), f"{w.name} pt={pt}: guard zone written"
+        fullsize.assert_rows(out.t, ref, w, f"{w.name} pt={pt}")
 
 
 def test_llama8b_decode_full_size(staging):
-    w = W.llama8b_decode()
-    seqs = [int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 7, 33]
-    _sampled(staging, w, seqs)
+    _full(staging, W.llama8b_decode())
 
 
 def test_llama8b_decode_8k_full_size(staging):
-    w = W.llama8b_decode_8k()
-    _sampled(staging, w, [0, 63])
+    _full(staging, W.llama8b_decode_8k())
 
 
 def test_long_context_full_size(staging):
-    w = W.long_context()
-    for pt in (0, 2048):
-        _sampled(staging, w, [0, 15], pt)
+    _full(staging, W.long_context(), pts=(0, 2048))
 
 
 def test_continuous_batching_full_size(staging):
-    w = W.continuous_batching()
-    seqs = [int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 100, 200]
-    _sampled(staging, w, seqs)
+    _full(staging, W.continuous_batching(), pts=(0, 512))
 
 
 def test_chunked_mix_decode_part_split_mode(staging):
-    """The decodes of the mixed batch, run through pa_decode (split-call mode)."""
-    w = W.decode_part(W.chunked_prefill_mix())
-    _sampled(staging, w, [0, 50, 95])
+    """The 96 decodes of the mixed batch, run through pa_decode (split-call
+    mode), every row against the oracle's rows of the whole mixed batch."""
+    mix = W.chunked_prefill_mix()
+    w = W.decode_part(mix)
+    print(f"  decodes of {mix.name}: {w.num_seqs}", flush=True)
+    dw = staging.DeviceWorkload(w, guard_bytes=1 << 16)
+    dw.scatter_new()
+    out = staging.Guarded(dw.query.shape, dw.query.dtype, dw.device)
+    nbytes = dw.decode_workspace(0).numel()
+    ws = staging.Guarded((nbytes,), torch.uint8, dw.device, 1 << 16)
+    dw.decode(out.t, 0, ws.t)
+    torch.cuda.synchronize()
+    assert out.intact() and ws.intact() and dw.guards_intact()
+    rows = mix.cu_query_lens[:-1][mix.query_lens == 1]
+    fullsize.assert_rows(out.t, fullsize.oracle_output(mix)[rows], w, "mixed batch decodes, split mode")
 
 
 @pytest.mark.parametrize("hq,hkv", [(32, 8), (64, 8), (8, 8)])

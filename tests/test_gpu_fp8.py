@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import fullsize
 import oracle
 import workloads as W
 from parity import assert_parity, to_numpy
@@ -207,12 +208,22 @@ def test_decode_values_beyond_the_code_range(staging):
 
 
 @pytest.mark.parametrize("name", ["llama8b_decode", "continuous_batching"])
-def test_decode_full_size_sampled(staging, name):
+def test_decode_full_size(staging, name):
+    """Full-size workload over an E4M3 cache in the benchmark's launch
+    configuration: the step's fused slots + quantising scatter, both whole
+    caches byte for byte against the oracle's fp8 scatter of every token, and
+    every output row against the oracle's attention over the codes; out,
+    workspace and caches between guard zones."""
     w = W.CONFIGS[name]()
-    _, out = _decode(staging, w)
-    o = to_numpy(out)
-    assert np.all(np.isfinite(o))
-    seqs = [int(np.argmax(w.seq_lens)), int(np.argmin(w.seq_lens)), 7, 33]
-    ref = oracle.run_sequences(w, seqs, fp8_scales=w.fp8_scales())
-    for b in seqs:
-        assert_parity(o[b:b + 1], ref[b], "bf16", f"fp8 {name} seq {b} (L={int(w.seq_lens[b])})")
+    dw = staging.DeviceWorkload(w, kv_fp8=True, guard_bytes=1 << 16)
+    dw.scatter_new(fused=True)
+    out = staging.Guarded(dw.query.shape, dw.query.dtype, dw.device)
+    ws = staging.Guarded((dw.decode_workspace(0).numel(),), torch.uint8, dw.device, 1 << 16)
+    dw.decode(out.t, 0, ws.t)
+    torch.cuda.synchronize()
+    assert out.intact() and ws.intact() and dw.guards_intact(), "guard zone written"
+    okc, ovc = fullsize.oracle_cache(w, fp8=True)
+    assert fullsize.same_bytes(dw.key_cache, okc), "key cache"
+    assert fullsize.same_bytes(dw.value_cache, ovc), "value cache"
+    del okc, ovc
+    fullsize.assert_rows(out.t, fullsize.oracle_output(w, fp8=True), w, f"fp8 {name}")

@@ -1,10 +1,11 @@
 """Row a10 on the GPU: chunked prefill (query_len > 1, causal, MFMA) mixed with
 single-row decodes in one pa_chunked_prefill call, against the oracle, element
-by element at small sizes and on sampled rows of the full mixed batch."""
+by element at small sizes and on every row of the full mixed batch."""
 import numpy as np
 import pytest
 import torch
 
+import fullsize
 import oracle
 import workloads as W
 from parity import assert_parity, to_numpy
@@ -81,35 +82,40 @@ def test_split_call_mode_matches_unified(staging):
     assert_parity(to_numpy(out_dec), ref[rows_dec], "bf16", "split: decodes")
 
 
-def _oracle_last_rows(w, b, k):
-    """Oracle output of the last k query rows of request b: a request with the
-    same context whose query is only those rows sits at the same positions."""
-    L, q = int(w.seq_lens[b]), int(w.query_lens[b])
-    sub = W._subset(w, np.array([b]), "rows")
-    sub.query_lens = np.array([k], np.int32)
-    sub.query = lambda _b: w.query(b)[q - k:]
-    return oracle.run_sequences(sub, [0])[0]
-
-
 def test_chunked_prefill_mix_full_size(staging):
     """The full mixed batch (4 x 512-row chunks at prior contexts 0, 2048,
-    4096, 7680 plus 96 decodes) in the benchmark's launch configuration; the
-    oracle recomputes whole short chunks, the last rows of the long ones, and
-    sampled decodes."""
+    4096, 7680 plus 96 decodes) in the benchmark's launch configuration: the
+    step's scatter of all 2144 new rows against the oracle's scatter (both
+    whole caches byte for byte), and every one of the 2144 output rows of the
+    unified call against the oracle; out, workspace and caches between guard
+    zones.  Then the chunks alone (the split-call mode), every row."""
     w = W.chunked_prefill_mix()
-    dw, out = _run(staging, w)
-    o = to_numpy(out)
-    assert np.all(np.isfinite(o))
+    dw = staging.DeviceWorkload(w, guard_bytes=1 << 16)
+    dw.scatter_new(fused=True)
+    out = staging.Guarded(dw.query.shape, dw.query.dtype, dw.device)
+    nbytes = dw.prefill_workspace().numel()
+    ws = staging.Guarded((nbytes,), torch.uint8, dw.device, 1 << 16)
+    dw.chunked_prefill(out.t, ws.t)
+    torch.cuda.synchronize()
+    assert out.intact() and ws.intact() and dw.guards_intact(), "guard zone written"
+    okc, ovc = fullsize.oracle_cache(w)
+    assert fullsize.same_bytes(dw.key_cache, okc), "key cache"
+    assert fullsize.same_bytes(dw.value_cache, ovc), "value cache"
+    del okc, ovc, dw
+    ref = fullsize.oracle_output(w)
+    fullsize.assert_rows(out.t, ref, w, "chunked_prefill_mix unified")
+
+    pre = W.prefill_part(w)
+    dpre = staging.DeviceWorkload(pre, guard_bytes=1 << 16)
+    dpre.scatter_new()
+    out = staging.Guarded(dpre.query.shape, dpre.query.dtype, dpre.device)
+    ws = staging.Guarded((dpre.prefill_workspace().numel(),), torch.uint8, dpre.device, 1 << 16)
+    dpre.chunked_prefill(out.t, ws.t)
+    torch.cuda.synchronize()
+    assert out.intact() and ws.intact() and dpre.guards_intact(), "guard zone written (chunks alone)"
     cu = w.cu_query_lens
-    ref = oracle.run_sequences(w, [0, 1, 10, 57, 99])
-    for b in (0, 1):
-        assert_parity(o[cu[b]:cu[b + 1]], ref[b], "bf16", f"chunk {b} (L={int(w.seq_lens[b])})")
-    for b in (2, 3):
-        k = 64
-        assert_parity(o[cu[b + 1] - k:cu[b + 1]], _oracle_last_rows(w, b, k), "bf16",
-                      f"chunk {b} last {k} rows (L={int(w.seq_lens[b])})")
-    for b in (10, 57, 99):
-        assert_parity(o[cu[b]:cu[b + 1]], ref[b], "bf16", f"decode {b} (L={int(w.seq_lens[b])})")
+    rows = np.concatenate([np.arange(cu[b], cu[b + 1]) for b in range(w.num_seqs) if w.query_lens[b] > 1])
+    fullsize.assert_rows(out.t, ref[rows], pre, "chunked_prefill_mix chunks, split mode")
 
 
 def _with_values(w, kv_fn, q_fn=None):
