@@ -8,22 +8,25 @@ to its slot, and the log-sum-exp merge of the sequences it splits).  The K
 timed steps run with nothing else on the stream; K more steps with HIP events
 around each call give the kernel's own rate, and K steps of the two-call form
 (pa_slot_mapping_and_cache, then pa_decode; --step two-call to time it as the
-step) are reported beside it.  Inputs are synthetic, seeded, and resident in HBM before
-timing starts; the earlier context of every sequence is written before timing.
+step) are reported beside it.  Inputs are synthetic, seeded, and resident in
+HBM before timing starts; the earlier context of every sequence is written
+before timing.
 
-Default workload: Llama-3-8B decode layer, batch 64, context lengths uniform
-in [1024, 8192], bf16 (32 query heads, 8 KV heads, head_dim 128, 16-token
-blocks).  Prints one JSON line.
+Headline workload: Llama-3-8B decode layer, batch 64 with every context at 8192
+tokens, bf16 (32 query heads, 8 KV heads, head_dim 128, 16-token blocks).
+Prints one JSON line.  The same run also times, under "workloads": batch 64
+with contexts uniform in [1024, 8192]; batch 16 at 32768; 256 sequences of
+log-normal length with 64 query heads; the chunked-prefill mix (4 x 512-row
+chunks + 96 decodes: the unified call, then the chunks against the bf16 matrix
+peak and the decodes against HBM); and the headline batch over an fp8 (E4M3)
+cache.  The CPU baseline runs the oracle over the whole headline workload.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-cache bf16|fp8]
-                  [--step append|two-call] [--no-cpu-baseline] [--no-probes]
+                  [--step append|two-call] [--no-cpu-baseline] [--no-probes] [--no-extra]
 
-With --workload chunked_prefill_mix a step is the scatter plus one
-pa_chunked_prefill call over 4 prefill chunks and 96 decodes; the chunks are
-also reported against the bf16 matrix peak.
-
-With --kv-cache fp8 the caches hold E4M3 codes: the step is
-pa_slot_mapping_and_cache_fp8 (slots and quantising scatter in one launch) and
+With --workload chunked_prefill_mix the headline step is the scatter plus one
+pa_chunked_prefill call over 4 prefill chunks and 96 decodes.  With --kv-cache
+fp8 the caches hold E4M3 codes: the step is pa_slot_mapping_and_cache_fp8 and
 pa_decode_fp8, and KV bytes count one byte per element.
 """
 from __future__ import annotations
@@ -42,11 +45,14 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode attention KV-read GB/s (% of HBM peak) + seq-steps/s, 1 GPU"
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
-# Sources that define the decode kernels; the HBM traffic recorded under
-# profiles/ is reported only while they hash to the value recorded with it.
+# Sources that define the decode kernels and their launch (grid, shares,
+# partition choice); the HBM traffic recorded under profiles/ is reported only
+# while they hash to the value recorded with it.
 DECODE_SOURCES = ["paged_kv_cache_432_amd/csrc/decode_kernel.hip", "paged_kv_cache_432_amd/csrc/device_common.h",
-                  "paged_kv_cache_432_amd/csrc/launch.h"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_llama8b_b64_1k-8k_traffic.json")
+                  "paged_kv_cache_432_amd/csrc/launch.h", "paged_kv_cache_432_amd/csrc/abi.cpp"]
+# HBM traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE of the decode call),
+# one file per workload.
+TRAFFIC_GLOB = os.path.join(ROOT, "profiles", "decode_*_traffic.json")
 
 
 def parse():
@@ -54,7 +60,7 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=500)
     p.add_argument("--warmup", type=int, default=50)
-    p.add_argument("--workload", default="llama8b_decode",
+    p.add_argument("--workload", default="llama8b_decode_8k",
                    choices=["llama8b_decode", "llama8b_decode_8k", "long_context", "continuous_batching",
                             "chunked_prefill_mix"])
     p.add_argument("--partition-tokens", type=int, default=0)
@@ -65,7 +71,8 @@ def parse():
                         "two-call: pa_slot_mapping_and_cache, then pa_decode")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probes", action="store_true")
-    p.add_argument("--cpu-sample-seqs", type=int, default=16)
+    p.add_argument("--no-extra", action="store_true",
+                   help="time only the headline workload (not the other configurations and the fp8 cache)")
     return p.parse_args()
 
 
@@ -78,20 +85,30 @@ def decode_sources_sha256() -> str:
     return h.hexdigest()
 
 
+def traffic_records() -> list:
+    """Every HBM traffic record under profiles/, as (path, record)."""
+    import glob
+    out = []
+    for path in sorted(glob.glob(TRAFFIC_GLOB)):
+        try:
+            with open(path) as f:
+                out.append((path, json.load(f)))
+        except (OSError, ValueError):
+            continue
+    return out
+
+
 def recorded_traffic(workload: str, call: str):
     """HBM bytes per decode call from the rocprofv3 FETCH_SIZE / WRITE_SIZE
-    passes recorded under profiles/ (already scaled by the copy-kernel
-    factors), or None if they were taken on other kernel sources, another
-    workload or another entry point."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
-        return None
-    if (rec.get("source_sha256") != decode_sources_sha256() or rec.get("workload") != workload
-            or rec.get("call", "pa_decode") != call):
-        return None
-    return rec.get("hbm_bytes_per_call")
+    passes recorded under profiles/ for this workload and entry point (already
+    scaled by the copy-kernel factors), or None if there is none or it was
+    taken on other kernel or launch sources."""
+    sha = decode_sources_sha256()
+    for _, rec in traffic_records():
+        if (rec.get("source_sha256") == sha and rec.get("workload") == workload
+                and rec.get("call", "pa_decode") == call):
+            return rec.get("hbm_bytes_per_call")
+    return None
 
 
 def probes(pa, torch, nbytes: int = 4 << 30, iters: int = 10):
@@ -305,66 +322,90 @@ def device_info(torch) -> dict:
     return info
 
 
-def cpu_baseline(w, nseq: int, fp8: bool = False):
-    """The oracle, untuned, on the host cores: the first `nseq` sequences of the
-    workload (their K/V gathered through block tables into a compact pool built
-    before timing), timed over the same step: slots and scatter of their new
-    tokens, then attention (over E4M3 codes when fp8)."""
+def cpu_info() -> dict:
+    """The host the CPU baseline ran on: the CPU model (/proc/cpuinfo), the CPUs
+    this process may run on (sched_getaffinity) and the OpenMP share of the job
+    (OMP_NUM_THREADS), if set."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    env = os.environ.get("OMP_NUM_THREADS")
+    return {"cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)),
+            "omp_num_threads_env": int(env) if env and env.isdigit() else None}
+
+
+def cpu_baseline(w, fp8: bool = False, one_thread_seqs: int = 4):
+    """The oracle, untuned, on the host cores, over the WHOLE workload of the
+    headline line: one step (slots and scatter of the step's new tokens, then
+    attention over every sequence; over E4M3 codes when fp8), its caches
+    holding every sequence's earlier context (built before timing).  It runs
+    with OpenMP over (query row, head) on the job's CPU share: every CPU the
+    process may run on, capped by OMP_NUM_THREADS where the job sets it.  A
+    per-core figure times the attention of the first few sequences on one
+    thread."""
     import oracle
     import workloads as W
-    idx = np.arange(min(nseq, w.num_seqs))
-    sub = W._subset(w, idx, "cpu_sample")
-    counts = W.blocks_needed(sub.seq_lens)
-    table = np.full((len(idx), int(counts.max())), -1, np.int32)
-    cursor = 0
-    for i, c in enumerate(counts):
-        table[i, :c] = np.arange(cursor, cursor + c)
-        cursor += c
-    sub = sub.with_block_table(table, num_blocks=int(cursor))
-    ks, vs = sub.fp8_scales()
-    kc, vc = oracle.build_cache_fp8(sub, ks, vs, "history") if fp8 else oracle.build_cache(sub, "history")
-    seq, pos = sub.tokens("new")
-    k_new, v_new = (sub.encode(x) for x in sub.token_kv(seq, pos))
-    q = sub.encode(sub.queries())
-    oracle.lib()
+    info = cpu_info()
+    threads = info["affinity_cores"]
+    if info["omp_num_threads_env"]:
+        threads = min(threads, info["omp_num_threads_env"])
+    oracle.set_threads(threads)
+    t_setup = time.perf_counter()
+    ks, vs = w.fp8_scales()
+    kc, vc = oracle.build_cache_fp8(w, ks, vs, "history") if fp8 else oracle.build_cache(w, "history")
+    seq, pos = w.tokens("new")
+    k_new, v_new = (w.encode(x) for x in w.token_kv(seq, pos))
+    q = w.encode(w.queries())
+    setup_s = time.perf_counter() - t_setup
+    sc = dict(k_scale=ks, v_scale=vs) if fp8 else {}
     times = []
     for _ in range(3):                               # median of three runs of the step
         t0 = time.perf_counter()
-        slots = oracle.slot_mapping(sub.block_table, seq, pos)
+        slots = oracle.slot_mapping(w.block_table, seq, pos)
         if fp8:
             oracle.reshape_and_cache_fp8(k_new, v_new, kc, vc, slots, ks, vs)
         else:
             oracle.reshape_and_cache(k_new, v_new, kc, vc, slots)
-        oracle.attention(q, kc, vc, sub.block_table, sub.cu_query_lens, sub.seq_lens, sub.num_heads,
-                         sub.scale, sub.causal, k_scale=ks if fp8 else 1.0, v_scale=vs if fp8 else 1.0)
+        oracle.attention(q, kc, vc, w.block_table, w.cu_query_lens, w.seq_lens, w.num_heads, w.scale,
+                         w.causal, **sc)
         times.append(time.perf_counter() - t0)
     dt = float(np.median(times))
-    kvb = sub.kv_bytes(1 if fp8 else None)
-    # one thread, on the first 4 of those sequences: a per-core figure
-    one = W._subset(sub, np.arange(min(4, len(idx))), "cpu_sample_1t")
+    kvb = w.kv_bytes(1 if fp8 else None)
+    # one thread, on the first few sequences: a per-core figure
+    one = W._subset(w, np.arange(min(one_thread_seqs, w.num_seqs)), "cpu_sample_1t")
     kv1 = one.kv_bytes(1 if fp8 else None)
-    threads = oracle.max_threads()
-    oracle.set_threads(1)
     q1 = one.encode(one.queries())
+    oracle.set_threads(1)
     t1 = []
     for _ in range(3):
         t0 = time.perf_counter()
         oracle.attention(q1, kc, vc, one.block_table, one.cu_query_lens, one.seq_lens, one.num_heads,
-                         one.scale, one.causal, k_scale=ks if fp8 else 1.0, v_scale=vs if fp8 else 1.0)
+                         one.scale, one.causal, **sc)
         t1.append(time.perf_counter() - t0)
     oracle.set_threads(threads)
     dt1 = float(np.median(t1))
+    del kc, vc
     return {
         "value": round(kvb / dt / 1e9, 4),
         "unit": "GB/s",
-        "seq_steps_per_s": round(len(idx) / dt, 3),
+        "seq_steps_per_s": round(w.num_seqs / dt, 3),
         "seconds": round(dt, 3),
-        "cores": threads,
+        "cores": int(oracle.max_threads()),
         "kind": "oracle",
+        "cpu_model": info["cpu_model"],
+        "affinity_cores": info["affinity_cores"],
+        "omp_num_threads_env": info["omp_num_threads_env"],
+        "setup_seconds": round(setup_s, 2),
         "per_core": {"GBps": round(kv1 / dt1 / 1e9, 4), "seconds": round(dt1, 4),
                      "sample": f"attention only, first {one.num_seqs} sequences ({int(one.seq_lens.sum())} KV "
                                f"tokens), one thread, median of 3"},
-        "sample": f"first {len(idx)} of {w.num_seqs} sequences ({int(sub.seq_lens.sum())} KV tokens, "
+        "sample": f"the whole workload: all {w.num_seqs} sequences ({int(w.seq_lens.sum())} KV tokens, "
                   f"{kvb / 1e9:.3f} GB of KV), one step (slots + scatter + attention), fp64, median of 3",
     }
 
@@ -396,7 +437,7 @@ def causal_flops(w) -> int:
     return pairs * w.num_heads * w.head_dim * 4
 
 
-def main_mixed(args, w, torch, pa, W, DeviceWorkload):
+def measure_mixed(w, steps: int, warmup: int, torch, pa, W, DeviceWorkload, mfma: bool = True) -> dict:
     """The chunked-prefill + decode mix: one step is the scatter of every new
     row and one pa_chunked_prefill call over the whole batch.  The chunks and
     the decodes are also timed as the two calls of the split-call mode, the
@@ -415,16 +456,16 @@ def main_mixed(args, w, torch, pa, W, DeviceWorkload):
         if ev is not None:
             ev[1].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step()
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for i in range(args.steps):
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
         step(events[i])
     torch.cuda.synchronize()
     call_ms = float(np.mean([a.elapsed_time(b) for a, b in events]))
@@ -435,58 +476,155 @@ def main_mixed(args, w, torch, pa, W, DeviceWorkload):
     dpre = DeviceWorkload(pre)
     dpre.scatter_new(stream)
     opre, wspre = torch.empty_like(dpre.query), dpre.prefill_workspace()
-    pre_ms = event_timed(torch, lambda: dpre.chunked_prefill(opre, wspre, stream), args.steps, args.warmup, stream)
+    pre_ms = event_timed(torch, lambda: dpre.chunked_prefill(opre, wspre, stream), steps, warmup, stream)
     del dpre, opre, wspre
     torch.cuda.empty_cache()
     ddec = DeviceWorkload(dec)
     ddec.scatter_new(stream)
     odec, wsdec = torch.empty_like(ddec.query), ddec.decode_workspace(0)
-    dec_ms = event_timed(torch, lambda: ddec.decode(odec, 0, wsdec, stream), args.steps, args.warmup, stream)
+    dec_ms = event_timed(torch, lambda: ddec.decode(odec, 0, wsdec, stream), steps, warmup, stream)
     del ddec, odec, wsdec
     torch.cuda.empty_cache()
 
     kv = w.kv_bytes()
     flops = causal_flops(pre)
     tflops = flops / (pre_ms * 1e-3) / 1e12
-    mprobe = None if args.no_probes else mfma_probe(pa, torch)
-    res = {
-        "metric": METRIC,
-        "value": round(kv / (ms_step * 1e-3) / 1e9, 2),
-        "unit": "GB/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
-        "data": "synthetic (seeded N(0,1) values, random block placement; no dataset)",
-        "config": {
-            "workload": w.name, "batch": w.num_seqs, "query_rows": int(w.num_q_tokens),
-            "chunks": int(np.sum(w.query_lens > 1)), "decodes": int(np.sum(w.query_lens == 1)),
-            "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
-            "block_size": w.block_size, "pool_blocks": w.num_blocks, "kv_bytes_per_step": kv,
-        },
+    mprobe = mfma_probe(pa, torch) if mfma else None
+    r = {
+        "workload": w.name, "kv_bytes_per_step": kv, "ms_per_step": round(ms_step, 5),
+        "GBps": round(kv / (ms_step * 1e-3) / 1e9, 2),
+        "step": "pa_slot_mapping_and_cache (2144 rows) + pa_chunked_prefill (chunks and decodes, one call)",
         "unified_call_us": round(call_ms * 1e3, 2),
-        "roofline": {
+        "chunks": {
             "kernel": "pa_chunked_prefill over the chunks: prefill_kernel + prefill_merge_kernel",
-            "bound": "mfma",
-            "achieved": round(tflops, 2),
-            "peak": BF16_MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
-            "traffic": None,
-            "avg_launch_us": round(pre_ms * 1e3, 2),
-            "algorithmic_flops_per_launch": flops,
+            "bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None,
+            "avg_launch_us": round(pre_ms * 1e3, 2), "algorithmic_flops_per_launch": flops,
         },
-        "probes": {"mfma_32x32x16_bf16": mprobe} if mprobe else None,
-        "decode_part": {
+        "decodes": {
             "kernel": "pa_decode over the single-row requests",
             "bound": "hbm", "avg_launch_us": round(dec_ms * 1e3, 2),
             "GBps": round(dec.kv_bytes() / (dec_ms * 1e-3) / 1e9, 2),
             "frac": round(dec.kv_bytes() / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "algorithmic_bytes_per_launch": dec.kv_bytes(),
         },
+        "config": {
+            "workload": w.name, "batch": w.num_seqs, "query_rows": int(w.num_q_tokens),
+            "chunks": int(np.sum(w.query_lens > 1)), "decodes": int(np.sum(w.query_lens == 1)),
+            "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
+            "block_size": w.block_size, "pool_blocks": w.num_blocks, "kv_bytes_per_step": kv,
+        },
     }
     if mprobe:
-        res["roofline"]["frac_of_mfma_probe"] = round(tflops / mprobe["TFLOPs"], 4)
-    print(json.dumps(res), flush=True)
+        r["probes"] = {"mfma_32x32x16_bf16": mprobe}
+        r["chunks"]["frac_of_mfma_probe"] = round(tflops / mprobe["TFLOPs"], 4)
+    return r
+
+
+def measure_decode(w, steps: int, warmup: int, torch, pa, DeviceWorkload, fp8: bool = False,
+                   step_kind: str = "append", partition_tokens: int = 0) -> dict:
+    """One decode workload: K timed steps with nothing else on the stream (the
+    step: pa_decode_append, or the two-call form / fp8 step), then K more with
+    HIP events around each attention call (the kernel's own rate), then K
+    steps of the two-call form for comparison when the step is the one call."""
+    dw = DeviceWorkload(w, kv_fp8=fp8)
+    pt = pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_seq_len, partition_tokens)
+    ws = dw.decode_workspace(partition_tokens)
+    out = torch.empty_like(dw.query)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    append = step_kind == "append" and not fp8 and pt == 0
+
+    def two_call_step(ev=None):
+        # slots and scatter of the step's tokens (one launch), then decode
+        dw.scatter_new(stream, fused=True)
+        if ev is not None:
+            ev[0].record(stream)
+        dw.decode(out, partition_tokens, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    def append_step(ev=None):
+        # the newest tokens written to the cache and attended to, in one call
+        if ev is not None:
+            ev[0].record(stream)
+        dw.decode_append(out, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+
+    step = append_step if append else two_call_step
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    # the K timed steps, nothing else on the stream
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / steps
+    # then K more steps with HIP events around each attention call, for the
+    # kernel's own rate (the events' stream gaps stay out of the step time)
+    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    call_ms = np.array([a.elapsed_time(b) for a, b in events])
+    two_call_ms = None
+    if append:
+        # the same step as two calls, for comparison (same values rewritten)
+        for _ in range(warmup):
+            two_call_step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            two_call_step()
+        torch.cuda.synchronize()
+        two_call_ms = (time.perf_counter() - t0) * 1e3 / steps
+    del dw, ws, out
+    torch.cuda.empty_cache()
+    kv = w.kv_bytes(1 if fp8 else None)
+    gbps = kv / (ms_step * 1e-3) / 1e9
+    call_gbps = kv / (float(call_ms.mean()) * 1e-3) / 1e9
+    r = {
+        "workload": w.name,
+        "kv_bytes_per_step": kv,
+        "ms_per_step": round(ms_step, 5),
+        "GBps": round(gbps, 2),
+        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
+        "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "append": append,
+        "partition_tokens": pt,
+        "step": "pa_decode_append (slots, scatter and decode in one call)" if append
+                else ("pa_slot_mapping_and_cache_fp8 + pa_decode_fp8" if fp8
+                      else "pa_slot_mapping_and_cache + pa_decode"),
+        "kernel": "pa_decode_fp8: decode_stream_kernel<fp8> + merge_stream_kernel (one call)" if fp8
+                  else "pa_decode_append: decode_stream_kernel<append> + merge_stream_kernel (one call)" if append
+                  else "pa_decode: decode_stream_kernel + merge_stream_kernel (one call)" if pt == 0
+                  else "pa_decode: decode_partition_kernel + merge_partitions_kernel (one call)",
+        "call": "pa_decode_append" if append else ("pa_decode_fp8" if fp8 else "pa_decode"),
+        "call_us_mean": round(float(call_ms.mean()) * 1e3, 2),
+        "call_us_median_p10_p90": [round(float(np.percentile(call_ms, q)) * 1e3, 2) for q in (50, 10, 90)],
+        "call_GBps": round(call_gbps, 2),
+        "call_frac": round(call_gbps / HBM_PEAK_GBPS, 4),
+    }
+    if two_call_ms is not None:
+        r["two_call_step"] = {"what": "pa_slot_mapping_and_cache + pa_decode, same inputs, after the timed steps",
+                              "ms_per_step": round(two_call_ms, 5),
+                              "GBps": round(kv / (two_call_ms * 1e-3) / 1e9, 2)}
+    return r
+
+
+def _brief(r: dict) -> dict:
+    """The figures of an extra workload that go into the JSON line."""
+    keys = ("workload", "step", "ms_per_step", "GBps", "pct_hbm_peak", "seq_steps_per_s", "call_us_mean",
+            "call_GBps", "call_frac", "kv_bytes_per_step", "two_call_step", "unified_call_us", "chunks", "decodes")
+    return {k: r[k] for k in keys if k in r}
+
+
+# The workloads timed in the same run as the headline (bench.py --no-extra
+# skips them): the other decode configurations, the chunked-prefill mix, and
+# the headline workload over an fp8 cache.
+EXTRA_DECODE = ["llama8b_decode", "long_context", "continuous_batching"]
 
 
 def main():
@@ -504,94 +642,36 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pa.lib()
     w = W.CONFIGS[args.workload]()
-    if not w.is_decode:
-        return main_mixed(args, w, torch, pa, W, DeviceWorkload)
-    t_setup = time.perf_counter()
     fp8 = args.kv_cache == "fp8"
     if fp8 and args.partition_tokens != 0:
         print("an fp8 cache is read in the stream mode only (--partition-tokens 0)", file=sys.stderr)
         sys.exit(2)
-    dw = DeviceWorkload(w, kv_fp8=fp8)
-    pt = pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_seq_len, args.partition_tokens)
-    ws = dw.decode_workspace(args.partition_tokens)
-    out = torch.empty_like(dw.query)
-    torch.cuda.synchronize()
-    print(f"# setup {time.perf_counter() - t_setup:.1f}s: {w.name}, {w.num_seqs} seqs, "
-          f"{w.kv_bytes() / 1e9:.3f} GB KV, partition {pt} tokens (0: balanced stream)",
-          file=sys.stderr, flush=True)
-
-    stream = torch.cuda.current_stream()
-    append = args.step == "append" and not fp8 and pt == 0
-
-    def two_call_step(ev=None):
-        # slots and scatter of the step's tokens (one launch), then decode
-        dw.scatter_new(stream, fused=True)
-        if ev is not None:
-            ev[0].record(stream)
-        dw.decode(out, args.partition_tokens, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-
-    def append_step(ev=None):
-        # the newest tokens written to the cache and attended to, in one call
-        if ev is not None:
-            ev[0].record(stream)
-        dw.decode_append(out, ws, stream)
-        if ev is not None:
-            ev[1].record(stream)
-
-    step = append_step if append else two_call_step
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # the K timed steps, nothing else on the stream
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
-    # then K more steps with HIP events around each pa_decode call, for the
-    # kernel's own rate (the events' stream gaps stay out of the step time)
-    events = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(args.steps)]
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    dec_ms = np.array([a.elapsed_time(b) for a, b in events])
-    dec_avg_ms = float(dec_ms.mean())
-    two_call_ms = None
-    if append:
-        # the same step as two calls, for comparison (same values rewritten)
-        for _ in range(args.warmup):
-            two_call_step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for i in range(args.steps):
-            two_call_step()
-        torch.cuda.synchronize()
-        two_call_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    kv = w.kv_bytes(1 if fp8 else None)
-    gbps = kv / (ms_step * 1e-3) / 1e9
-    dec_gbps = kv / (dec_avg_ms * 1e-3) / 1e9
-    traffic = None if fp8 else recorded_traffic(w.name, "pa_decode_append" if append else "pa_decode")
-    probe = None if args.no_probes else probes(pa, torch)
-    res = {
-        "metric": METRIC,
-        "value": round(gbps, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8_e4m3 KV, bf16 Q/out" if fp8 else w.dtype,
+    t_setup = time.perf_counter()
+    print(f"# {w.name}: {w.num_seqs} seqs, {w.kv_bytes() / 1e9:.3f} GB KV", file=sys.stderr, flush=True)
+    common = {
+        "metric": METRIC, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "data": "synthetic (seeded N(0,1)*sigma values, random block placement; no dataset)",
+    }
+    if not w.is_decode:
+        r = measure_mixed(w, args.steps, args.warmup, torch, pa, W, DeviceWorkload, mfma=not args.no_probes)
+        res = dict(common, value=r["GBps"], ms_per_step=r["ms_per_step"], dtype=w.dtype, config=r["config"],
+                   unified_call_us=r["unified_call_us"], roofline=r["chunks"], decode_part=r["decodes"])
+        if "probes" in r:
+            res["probes"] = r["probes"]
+        res["device"] = device_info(torch)
+        print(json.dumps(res), flush=True)
+        return
+
+    r = measure_decode(w, args.steps, args.warmup, torch, pa, DeviceWorkload, fp8, args.step, args.partition_tokens)
+    print(f"# {w.name}: {r['ms_per_step'] * 1e3:.1f} us/step ({time.perf_counter() - t_setup:.1f}s)",
+          file=sys.stderr, flush=True)
+    traffic = None if fp8 else recorded_traffic(w.name, r["call"])
+    res = dict(common)
+    res.update({
+        "value": r["GBps"],
+        "ms_per_step": r["ms_per_step"],
+        "dtype": "fp8_e4m3 KV, bf16 Q/out" if fp8 else w.dtype,
         "config": {
             "workload": w.name,
             "batch": w.num_seqs,
@@ -600,47 +680,59 @@ def main():
             "num_heads": w.num_heads, "num_kv_heads": w.num_kv_heads, "head_dim": w.head_dim,
             "block_size": w.block_size, "pool_blocks": w.num_blocks,
             "new_tokens_per_step": int(w.num_q_tokens),
-            "decode_split": "balanced stream (equal block shares per workgroup)" if pt == 0
-                            else f"partitions of {pt} tokens",
-            "kv_bytes_per_step": kv,
+            "decode_split": "balanced stream (equal block shares per workgroup)" if r["partition_tokens"] == 0
+                            else f"partitions of {r['partition_tokens']} tokens",
+            "kv_bytes_per_step": r["kv_bytes_per_step"],
             "kv_cache": "fp8 E4M3 (1 byte/element), k_scale = v_scale = %.6g" % w.fp8_scales()[0] if fp8
                         else w.dtype,
-            "step": "pa_decode_append (slots, scatter and decode in one call)" if append
-                    else ("pa_slot_mapping_and_cache_fp8 + pa_decode_fp8" if fp8
-                          else "pa_slot_mapping_and_cache + pa_decode"),
+            "step": r["step"],
         },
-        "pct_hbm_peak": round(100.0 * gbps / HBM_PEAK_GBPS, 2),
-        "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
+        "pct_hbm_peak": r["pct_hbm_peak"],
+        "seq_steps_per_s": r["seq_steps_per_s"],
         "roofline": {
-            "kernel": "pa_decode_fp8: decode_stream_kernel<fp8> + merge_stream_kernel (one call)" if fp8
-                      else "pa_decode_append: decode_stream_kernel<append> + merge_stream_kernel (one call)"
-                      if append
-                      else "pa_decode: decode_stream_kernel + merge_stream_kernel (one call)" if pt == 0
-                      else "pa_decode: decode_partition_kernel + merge_partitions_kernel (one call)",
+            "kernel": r["kernel"],
             "bound": "hbm",
-            "achieved": round(dec_gbps, 2),
+            "achieved": r["call_GBps"],
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
-            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+            "frac": r["call_frac"],
             "traffic": traffic,
-            "avg_launch_us": round(dec_avg_ms * 1e3, 2),
-            "launch_us_median_p10_p90": [round(float(np.percentile(dec_ms, q)) * 1e3, 2) for q in (50, 10, 90)],
-            "algorithmic_bytes_per_launch": kv,
+            "avg_launch_us": r["call_us_mean"],
+            "launch_us_median_p10_p90": r["call_us_median_p10_p90"],
+            "algorithmic_bytes_per_launch": r["kv_bytes_per_step"],
         },
-    }
-    if two_call_ms is not None:
-        res["two_call_step"] = {"what": "pa_slot_mapping_and_cache + pa_decode, same inputs, after the timed steps",
-                                "ms_per_step": round(two_call_ms, 5),
-                                "GBps": round(kv / (two_call_ms * 1e-3) / 1e9, 2)}
-    if probe is not None:
+    })
+    if "two_call_step" in r:
+        res["two_call_step"] = r["two_call_step"]
+    if not args.no_extra:
+        extra_steps, extra_warmup = min(args.steps, 200), min(args.warmup, 20)
+        extra = {}
+        for name in EXTRA_DECODE:
+            if name == args.workload:
+                continue
+            wx = W.CONFIGS[name]()
+            extra[wx.name] = _brief(measure_decode(wx, extra_steps, extra_warmup, torch, pa, DeviceWorkload))
+            print(f"# {wx.name}: {extra[wx.name]['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        wm = W.chunked_prefill_mix()
+        extra[wm.name] = _brief(measure_mixed(wm, extra_steps, extra_warmup, torch, pa, W, DeviceWorkload,
+                                              mfma=False))
+        print(f"# {wm.name}: {extra[wm.name]['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        if not fp8:
+            f = _brief(measure_decode(w, extra_steps, extra_warmup, torch, pa, DeviceWorkload, fp8=True))
+            f["kv_cache"] = "fp8 E4M3 (1 byte/element), k_scale = v_scale = %.6g" % w.fp8_scales()[0]
+            extra[w.name + ":fp8"] = f
+            print(f"# {w.name} fp8: {f['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        res["workloads"] = extra
+    if not args.no_probes:
+        probe = probes(pa, torch)
         res["probes"] = probe
-        res["roofline"]["frac_of_read_probe"] = round(dec_gbps / probe["stream_read"]["GBps"], 4)
+        res["roofline"]["frac_of_read_probe"] = round(r["call_GBps"] / probe["stream_read"]["GBps"], 4)
         res["rope_reshape_and_cache"] = rope_scatter_timing(pa, torch)
         res["copy_blocks"] = copy_blocks_timing(pa, torch)
         res["kv_manager"] = kv_manager_timing(pa)
     res["device"] = device_info(torch)
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_sample_seqs, fp8)
+        res["cpu_baseline"] = cpu_baseline(w, fp8)
     print(json.dumps(res), flush=True)
 
 
