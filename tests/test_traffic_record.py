@@ -50,3 +50,11 @@ def test_bench_drops_a_record_taken_on_other_sources(monkeypatch):
     assert bench.recorded_traffic("no_such_workload", rec["call"]) is None
     monkeypatch.setattr(bench, "decode_sources_sha256", lambda: "0" * 64)
     assert bench.recorded_traffic(rec["workload"], rec["call"]) is None
+
+
+def test_headline_workload_has_a_current_record():
+    """The bench's headline workload (batch 64, every context 8192) has a
+    traffic record of its one-call step taken on the current decode sources,
+    so its line carries roofline.traffic."""
+    w = W.llama8b_decode_8k()
+    assert bench.recorded_traffic(w.name, "pa_decode_append") is not None
