@@ -65,10 +65,20 @@ typedef enum {
     PA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, inconsistent shapes, misaligned rows */
     PA_ERR_UNSUPPORTED = 2,   /* a shape or dtype this build does not implement */
     PA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the query function's size */
-    PA_ERR_HIP = 4            /* a kernel launch failed (hipGetLastError) */
+    PA_ERR_HIP = 4,           /* a kernel launch failed (hipGetLastError) */
+    PA_STATUS_RESERVED_MIN_ = -0x7fffffff - 1,   /* range widened to every int, as for pa_dtype */
+    PA_STATUS_RESERVED_MAX_ = 0x7fffffff
 } pa_status;
 
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+/* The two reserved values widen the enumeration's range to every int, so that
+ * a caller's out-of-range value is a valid pa_dtype that the checks reject
+ * (PA_ERR_UNSUPPORTED) rather than undefined behaviour in the C++ library. */
+typedef enum {
+    PA_F32 = 0,
+    PA_BF16 = 1,
+    PA_DTYPE_RESERVED_MIN_ = -0x7fffffff - 1,
+    PA_DTYPE_RESERVED_MAX_ = 0x7fffffff
+} pa_dtype;
 
 int32_t pa_abi_version(void);
 const char *pa_status_string(pa_status status);

@@ -45,6 +45,17 @@ def build(force: bool = True) -> str:
     return _LIB_PATH
 
 
+def build_sanitized(out: str) -> str:
+    """The oracle under gcc's ASan and UBSan (for the sanitizer tests, which load
+    it through PA_ORACLE_LIB with gcc's runtimes preloaded)."""
+    tmp = out + f".tmp{os.getpid()}"
+    subprocess.run(["gcc", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                    "-fno-sanitize-recover=undefined", "-fopenmp", "-fPIC", "-shared", "-std=c99", _SRC,
+                    "-o", tmp, "-lm"], check=True)
+    os.replace(tmp, out)
+    return out
+
+
 def lib():
     global _lib
     with _lock:

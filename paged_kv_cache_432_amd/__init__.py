@@ -51,7 +51,9 @@ class PaError(RuntimeError):
 
 
 def lib_path() -> str:
-    return os.path.join(_DIR, "libpa.so")
+    """The in-tree libpa.so, or the build named by the PA_LIB environment
+    variable (e.g. one whose host code carries sanitizers)."""
+    return os.environ.get("PA_LIB") or os.path.join(_DIR, "libpa.so")
 
 
 def lib():
@@ -514,14 +516,8 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
     return out
 
 
-def pa_decode_append(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
-                     key_cache: torch.Tensor, value_cache: torch.Tensor, block_table: torch.Tensor,
-                     seq_lens: torch.Tensor, scale: float, max_seq_len: int, slot_mapping: torch.Tensor | None = None,
-                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """One decode step: row b of key/value [B, Hkv, D] (sequence b's newest token,
-    at position seq_lens[b] - 1) is written into the caches and attended to with
-    the rest of the sequence; out [B, Hq, D].  slot_mapping (int64 [B], optional)
-    receives the newest tokens' slots."""
+def _check_decode_append(out, query, key, value, key_cache, value_cache, block_table, seq_lens, slot_mapping):
+    """Tensor checks of pa_decode_append."""
     _need(query.dim() == 3 and out.shape == query.shape and out.is_contiguous(),
           "query/out: [num_seqs, num_heads, head_dim], out contiguous")
     _need(query.stride(2) == 1 and query.stride(1) == query.shape[2], "query heads/dims must be contiguous")
@@ -543,6 +539,19 @@ def pa_decode_append(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, 
     if slot_mapping is not None:
         _need(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous() and slot_mapping.numel() >= b,
               "slot_mapping: contiguous int64 [num_seqs]")
+
+
+def pa_decode_append(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                     key_cache: torch.Tensor, value_cache: torch.Tensor, block_table: torch.Tensor,
+                     seq_lens: torch.Tensor, scale: float, max_seq_len: int, slot_mapping: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step: row b of key/value [B, Hkv, D] (sequence b's newest token,
+    at position seq_lens[b] - 1) is written into the caches and attended to with
+    the rest of the sequence; out [B, Hq, D].  slot_mapping (int64 [B], optional)
+    receives the newest tokens' slots."""
+    _check_decode_append(out, query, key, value, key_cache, value_cache, block_table, seq_lens, slot_mapping)
+    b, hq, d = query.shape
+    nb, bs, hkv, _ = key_cache.shape
     ws = workspace
     s = lib().pa_decode_append(_ptr(out), _ptr(query), query.stride(0), _ptr(key), key.stride(0), _ptr(value),
                                value.stride(0), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping),

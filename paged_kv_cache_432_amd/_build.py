@@ -28,10 +28,20 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libpa.so)")
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source into paged_kv_cache_432_amd/libpa.so; returns its path."""
-    tmp = LIB + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *DEVICE_FLAGS, *(extra_flags or []), "-shared", f"-I{INCLUDE}", f"-I{CSRC}",
+# Host-side AddressSanitizer and UndefinedBehaviorSanitizer (device code is
+# compiled as usual); each -fsanitize= goes to the host compilation only.
+HOST_SANITIZER_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                        "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def build(verbose: bool = False, extra_flags=None, out: str = LIB, sanitize: bool = False) -> str:
+    """Compile every source into `out` (default paged_kv_cache_432_amd/libpa.so);
+    returns its path.  sanitize: host code under ASan and UBSan, for a build
+    that a process loads with the compiler's ASan runtime preloaded (the
+    sanitizer tests point PA_LIB at it)."""
+    tmp = out + f".tmp{os.getpid()}"
+    flags = [*DEVICE_FLAGS, *(HOST_SANITIZER_FLAGS if sanitize else []), *(extra_flags or [])]
+    cmd = [hipcc(), *flags, "-shared", f"-I{INCLUDE}", f"-I{CSRC}",
            "-o", tmp] + [os.path.join(CSRC, s) for s in SOURCES]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -42,8 +52,20 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def asan_runtime() -> str:
+    """The compiler's shared ASan runtime (it carries the UBSan handlers too)."""
+    import glob
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    for pat in (os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux", "libclang_rt.asan-x86_64.so"),
+                "/opt/rocm/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"):
+        hits = sorted(glob.glob(pat))
+        if hits:
+            return hits[-1]
+    raise RuntimeError("clang's ASan runtime (libclang_rt.asan-x86_64.so) not found")
 
 
 if __name__ == "__main__":
