@@ -438,6 +438,34 @@ pa_status pa_decode_append(void *out, const void *query, int64_t q_token_stride,
                            pa_dtype dtype, hipStream_t stream);
 
 /*
+ * pa_decode_append_noalloc -- pa_decode_append for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same operation, arguments and results
+ * as pa_decode_append, without the workspace: the decode's scratch (block
+ * prefix and partial records) is a file-scope device array of the library,
+ * PA_NOALLOC_SCRATCH_BYTES (32 MiB) per device, 256-byte aligned, which each
+ * device the library runs on holds from its first call until the process
+ * ends.  The call allocates nothing (no hipMalloc or allocating library
+ * routine).  A call that needs more scratch than that (pa_decode_workspace_bytes
+ * above it: many sequences with explicit partitions, or a very wide stream
+ * grid) returns PA_ERR_WORKSPACE and launches nothing.  The scratch needs no
+ * initialisation (every byte read is first written by the same call); every
+ * call on one device shares that device's array, so calls that overlap on one
+ * device (on different streams, or from different threads without ordering)
+ * race and give undefined results.
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+pa_status pa_decode_append_noalloc(void *out, const void *query, int64_t q_token_stride,
+                                   const void *key, int64_t key_token_stride,
+                                   const void *value, int64_t value_token_stride,
+                                   void *key_cache, void *value_cache, int64_t *slot_mapping,
+                                   const int32_t *block_table, int32_t max_blocks_per_req,
+                                   const int32_t *seq_lens, int32_t num_seqs,
+                                   int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t block_size, int64_t num_blocks, float scale,
+                                   int32_t max_seq_len, pa_dtype dtype, hipStream_t stream);
+
+/*
  * pa_chunked_prefill -- attention of a mixed batch in one call: chunks of
  * query_len >= 2 rows (chunked prefill) next to single-row decodes, all
  * reading K/V from the paged cache after this step's rows were scattered

@@ -20,7 +20,7 @@ __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
     "pa_slot_mapping", "pa_reshape_and_cache", "pa_slot_mapping_and_cache", "pa_rope_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_slot_mapping_and_cache_fp8",
     "pa_decode_fp8", "pa_copy_blocks", "KvManager", "pa_decode_workspace_bytes",
-    "pa_decode_partition_tokens", "pa_decode", "pa_decode_append", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
+    "pa_decode_partition_tokens", "pa_decode", "pa_decode_append", "pa_decode_append_noalloc", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
     "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
 ]
 
@@ -131,6 +131,10 @@ def lib():
         L.pa_decode_append.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                        _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _vp, ctypes.c_size_t,
                                        ctypes.c_int, _vp]
+        L.pa_decode_append_noalloc.restype = ctypes.c_int
+        L.pa_decode_append_noalloc.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
+                                               _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _i32,
+                                               ctypes.c_int, _vp]
         L.pa_chunked_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.pa_chunked_prefill_workspace_bytes.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32]
         L.pa_chunked_prefill.restype = ctypes.c_int
@@ -517,7 +521,7 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
 
 
 def _check_decode_append(out, query, key, value, key_cache, value_cache, block_table, seq_lens, slot_mapping):
-    """Tensor checks of pa_decode_append."""
+    """Tensor checks shared by pa_decode_append and pa_decode_append_noalloc."""
     _need(query.dim() == 3 and out.shape == query.shape and out.is_contiguous(),
           "query/out: [num_seqs, num_heads, head_dim], out contiguous")
     _need(query.stride(2) == 1 and query.stride(1) == query.shape[2], "query heads/dims must be contiguous")
@@ -560,6 +564,25 @@ def pa_decode_append(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, 
                                0 if ws is None else ws.numel() * ws.element_size(), _dtype_code(query),
                                _stream(stream, out.device))
     _check(s, "pa_decode_append")
+    return out
+
+
+def pa_decode_append_noalloc(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                             key_cache: torch.Tensor, value_cache: torch.Tensor, block_table: torch.Tensor,
+                             seq_lens: torch.Tensor, scale: float, max_seq_len: int,
+                             slot_mapping: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """pa_decode_append without a workspace: the library's own per-device
+    scratch array serves instead, and nothing is allocated.  Calls that overlap
+    on one device race on that array."""
+    _check_decode_append(out, query, key, value, key_cache, value_cache, block_table, seq_lens, slot_mapping)
+    b, hq, d = query.shape
+    nb, bs, hkv, _ = key_cache.shape
+    s = lib().pa_decode_append_noalloc(_ptr(out), _ptr(query), query.stride(0), _ptr(key), key.stride(0),
+                                       _ptr(value), value.stride(0), _ptr(key_cache), _ptr(value_cache),
+                                       _ptr(slot_mapping), _ptr(block_table), block_table.shape[1], _ptr(seq_lens),
+                                       b, hq, hkv, d, bs, nb, float(scale), int(max_seq_len), _dtype_code(query),
+                                       _stream(stream, out.device))
+    _check(s, "pa_decode_append_noalloc")
     return out
 
 
