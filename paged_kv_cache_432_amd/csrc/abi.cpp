@@ -222,6 +222,7 @@ const char* pa_status_string(pa_status s) {
         case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
         case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE";
         case PA_ERR_HIP: return "PA_ERR_HIP";
+        default: break;
     }
     return "PA_ERR_UNKNOWN";
 }

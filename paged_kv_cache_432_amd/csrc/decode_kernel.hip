@@ -1285,15 +1285,26 @@ int stream_blocks_group(int group, int waves_per_group, int64_t num_seqs) {
 
 // dtype: 0 fp32, 1 bf16, 2 fp8 (E4M3) cache with bf16 query and output, 3 bf16
 // in append mode.
+// The append form runs on the matrix-core wave only: a build that moves the
+// bf16 decode to the vector wave (PA_DECODE_MFMA_FROM > 1, for measurement)
+// leaves it out, and its launches fail.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t stream) {
+#if PA_DECODE_MFMA_FROM <= 1
     if (dtype == 3) return launch_group<ChunkBF16, uint16_t, false, true>(a, group, stream);
+#else
+    if (dtype == 3) return hipErrorInvalidDeviceFunction;
+#endif
     if (dtype == 2) return launch_group<ChunkBF16, uint16_t, true>(a, group, stream);
     if (dtype == 1) return launch_group<ChunkBF16, uint16_t>(a, group, stream);
     return launch_group<ChunkF32, float>(a, group, stream);
 }
 
 int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int num_seqs) {
+#if PA_DECODE_MFMA_FROM <= 1
     if (dtype == 3) return stream_blocks_group<ChunkBF16, uint16_t, false, true>(group, waves_per_group, num_seqs);
+#else
+    if (dtype == 3) return stream_blocks_group<ChunkBF16, uint16_t>(group, waves_per_group, num_seqs);
+#endif
     if (dtype == 2) return stream_blocks_group<ChunkBF16, uint16_t, true>(group, waves_per_group, num_seqs);
     if (dtype == 1) return stream_blocks_group<ChunkBF16, uint16_t>(group, waves_per_group, num_seqs);
     return stream_blocks_group<ChunkF32, float>(group, waves_per_group, num_seqs);
