@@ -28,7 +28,8 @@ _LIB_PATH = os.path.join(_HERE, "libpa_oracle.so")
 _lib = None
 _lock = threading.Lock()
 
-F32, BF16, E4M3 = 0, 1, 2
+F32, BF16, E4M3, E5M2 = 0, 1, 2, 3
+FP8_FORMATS = {"e4m3": E4M3, "e5m2": E5M2}
 
 _i32p = ctypes.POINTER(ctypes.c_int32)
 _i64p = ctypes.POINTER(ctypes.c_int64)
@@ -90,11 +91,16 @@ def lib():
             L.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
             L.oracle_e4m3_encode.restype = ctypes.c_uint8
             L.oracle_e4m3_encode.argtypes = [ctypes.c_float]
+            L.oracle_e5m2_value.restype = ctypes.c_double
+            L.oracle_e5m2_value.argtypes = [ctypes.c_uint8]
+            L.oracle_e5m2_encode.restype = ctypes.c_uint8
+            L.oracle_e5m2_encode.argtypes = [ctypes.c_float]
             L.oracle_reshape_and_cache_fp8.restype = None
             L.oracle_reshape_and_cache_fp8.argtypes = [
                 ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
                 ctypes.c_void_p, ctypes.c_void_p, _i64p, ctypes.c_int64,
-                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float]
+                ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_float, ctypes.c_float,
+                ctypes.c_int32]
             L.oracle_rope_table.restype = None
             L.oracle_rope_table.argtypes = [_f64p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double]
             L.oracle_rope_qkv.restype = None
@@ -170,16 +176,19 @@ def _dtype_of(a):
 
 def attention(query, key_cache, value_cache, block_table, cu_query_lens, seq_lens,
               num_heads: int, scale: float, causal: bool, return_probs: bool = False,
-              k_scale: float = 1.0, v_scale: float = 1.0):
+              k_scale: float = 1.0, v_scale: float = 1.0, fp8_format: str = "e4m3"):
     """fp64 attention over the paged cache; returns out [num_q_tokens, Hq, D]
     (and the probability rows [num_q_tokens, Hq, max_seq_len] if asked).
 
     The query is bf16 bits (uint16) or float32; the caches are the same dtype,
-    or E4M3 codes (uint8) standing for code value * k_scale / v_scale."""
+    or fp8 codes (uint8, in fp8_format: "e4m3" or "e5m2") standing for code
+    value * k_scale / v_scale."""
     dtype = _dtype_of(query)
     kv_dtype = _dtype_of(key_cache)
+    if kv_dtype == E4M3:
+        kv_dtype = FP8_FORMATS[fp8_format]
     assert value_cache.dtype == key_cache.dtype and dtype != E4M3
-    assert kv_dtype == dtype or kv_dtype == E4M3
+    assert kv_dtype == dtype or kv_dtype in (E4M3, E5M2)
     q = query
     assert q.strides[1:] == (q.shape[2] * q.itemsize, q.itemsize)
     bt = _c(block_table, np.int32)
@@ -231,11 +240,25 @@ def e4m3_encode(y) -> np.ndarray:
     return np.array([enc(float(v)) for v in y.ravel()], np.uint8).reshape(y.shape)
 
 
+def e5m2_value(code: int) -> float:
+    """The number an OCP E5M2 code stands for (+-inf for 0x7C / 0xFC, NaN for
+    the other codes of exponent field 31)."""
+    return float(lib().oracle_e5m2_value(int(code)))
+
+
+def e5m2_encode(y) -> np.ndarray:
+    """E5M2 codes of float32 values: nearest, ties to even, saturating at 57344."""
+    y = np.ascontiguousarray(y, np.float32)
+    enc = lib().oracle_e5m2_encode
+    return np.array([enc(float(v)) for v in y.ravel()], np.uint8).reshape(y.shape)
+
+
 def reshape_and_cache_fp8(key, value, key_cache, value_cache, slots, k_scale: float, v_scale: float,
-                          block_size: int = 16):
+                          block_size: int = 16, fp8_format: str = "e4m3"):
     """In-place fp8 scatter into uint8 caches [num_blocks, block_size, Hkv, D]:
-    code = encode(x / scale) with the division in float32.  key/value are
-    bf16 bits (uint16) or float32, token rows may be strided."""
+    code = encode(x / scale) in fp8_format ("e4m3" or "e5m2") with the
+    division in float32.  key/value are bf16 bits (uint16) or float32, token
+    rows may be strided."""
     assert key_cache.dtype == value_cache.dtype == np.uint8
     assert key_cache.flags.c_contiguous and value_cache.flags.c_contiguous
     assert key.dtype == value.dtype
@@ -249,7 +272,8 @@ def reshape_and_cache_fp8(key, value, key_cache, value_cache, slots, k_scale: fl
     lib().oracle_reshape_and_cache_fp8(
         key.ctypes.data, key.strides[0] // key.itemsize, value.ctypes.data,
         value.strides[0] // value.itemsize, key_cache.ctypes.data, value_cache.ctypes.data,
-        _p(sm, _i64p), n, int(block_size), hkv, d, _dtype_of(key), float(k_scale), float(v_scale))
+        _p(sm, _i64p), n, int(block_size), hkv, d, _dtype_of(key), float(k_scale), float(v_scale),
+        {"e4m3": 0, "e5m2": 1}[fp8_format])
 
 
 # ------------------------------------------------------ RoPE + QKV split --
@@ -315,22 +339,22 @@ def _token_rows(w, which: str):
         yield b, k[p], v[p], slots
 
 
-def build_cache_fp8(w, k_scale: float, v_scale: float, which: str = "all"):
-    """As build_cache, into E4M3 caches (uint8, every byte the NaN code 0x7F
-    first) through the fp8 scatter."""
+def build_cache_fp8(w, k_scale: float, v_scale: float, which: str = "all", fp8_format: str = "e4m3"):
+    """As build_cache, into fp8 caches (uint8, every byte 0x7F first, a NaN code
+    in both formats) through the fp8 scatter."""
     shape = (w.num_blocks, w.block_size, w.num_kv_heads, w.head_dim)
     kc, vc = np.full(shape, 0x7F, np.uint8), np.full(shape, 0x7F, np.uint8)
     for _, k, v, slots in _token_rows(w, which):
-        reshape_and_cache_fp8(k, v, kc, vc, slots, k_scale, v_scale, w.block_size)
+        reshape_and_cache_fp8(k, v, kc, vc, slots, k_scale, v_scale, w.block_size, fp8_format)
     return kc, vc
 
 
-def run_fp8(w, k_scale: float, v_scale: float):
+def run_fp8(w, k_scale: float, v_scale: float, fp8_format: str = "e4m3"):
     """Oracle output over an fp8 cache of the workload: [num_q_tokens, Hq, D] fp64."""
-    kc, vc = build_cache_fp8(w, k_scale, v_scale, "all")
+    kc, vc = build_cache_fp8(w, k_scale, v_scale, "all", fp8_format)
     q = w.encode(w.queries())
     return attention(q, kc, vc, w.block_table, w.cu_query_lens, w.seq_lens, w.num_heads, w.scale, w.causal,
-                     k_scale=k_scale, v_scale=v_scale)
+                     k_scale=k_scale, v_scale=v_scale, fp8_format=fp8_format)
 
 
 def run(w, return_probs: bool = False):
@@ -341,7 +365,7 @@ def run(w, return_probs: bool = False):
                      w.scale, w.causal, return_probs)
 
 
-def run_sequences(w, seqs, fp8_scales=None):
+def run_sequences(w, seqs, fp8_scales=None, fp8_format: str = "e4m3"):
     """Oracle output for a few sequences of a large workload.
 
     The chosen sequences' blocks are relabelled into a compact pool (the result
@@ -364,12 +388,12 @@ def run_sequences(w, seqs, fp8_scales=None):
         pos = np.arange(L, dtype=np.int32)
         slots = slot_mapping(table, np.zeros(L, np.int32), pos, w.block_size)
         if fp8_scales is not None:
-            reshape_and_cache_fp8(k, v, kc, vc, slots, fp8_scales[0], fp8_scales[1], w.block_size)
+            reshape_and_cache_fp8(k, v, kc, vc, slots, fp8_scales[0], fp8_scales[1], w.block_size, fp8_format)
         else:
             reshape_and_cache(k, v, kc, vc, slots, w.block_size)
         q = w.encode(w.query(b))
         cu = np.array([0, q.shape[0]], np.int32)
         ks, vs = fp8_scales if fp8_scales is not None else (1.0, 1.0)
         res[b] = attention(q, kc, vc, table, cu, np.array([L], np.int32), w.num_heads,
-                           w.scale, w.causal, k_scale=ks, v_scale=vs)
+                           w.scale, w.causal, k_scale=ks, v_scale=vs, fp8_format=fp8_format)
     return res

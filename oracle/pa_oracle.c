@@ -36,6 +36,7 @@
 #define ORACLE_F32 0
 #define ORACLE_BF16 1
 #define ORACLE_E4M3 2
+#define ORACLE_E5M2 3
 
 /* Number of threads the attention loop uses (OpenMP), for reporting. */
 int oracle_max_threads(void)
@@ -48,6 +49,7 @@ int oracle_max_threads(void)
 }
 
 double oracle_e4m3_value(uint8_t code);
+double oracle_e5m2_value(uint8_t code);
 
 /* Threads the attention loop may use from now on (OpenMP); for timing. */
 void oracle_set_threads(int32_t n)
@@ -66,6 +68,8 @@ static double widen(const void *base, int64_t idx, int dtype)
         return (double)((const float *)base)[idx];
     if (dtype == ORACLE_E4M3)
         return oracle_e4m3_value(((const uint8_t *)base)[idx]);
+    if (dtype == ORACLE_E5M2)
+        return oracle_e5m2_value(((const uint8_t *)base)[idx]);
     uint32_t u = (uint32_t)((const uint16_t *)base)[idx] << 16;   /* bf16 is the top half of a float32 */
     float f;
     memcpy(&f, &u, sizeof f);
@@ -355,14 +359,64 @@ uint8_t oracle_e4m3_encode(float y)
     return sign | (uint8_t)best;
 }
 
+/* The other 8-bit format the pages name, from the same specification: OCP
+ * E5M2 -- sign, 5 exponent bits with bias 15, 2 mantissa bits; exponent field
+ * 0 holds the subnormals m * 2^-16; exponent field 31 holds infinity (mantissa
+ * 0) and NaN (mantissa 1 .. 3); the largest finite value is 1.75 * 2^15 =
+ * 57344. */
+double oracle_e5m2_value(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 2) & 31;
+    int m = code & 3;
+    double v;
+    if (e == 31)
+        v = m ? NAN : INFINITY;
+    else if (e == 0)
+        v = ldexp((double)m, -16);
+    else
+        v = ldexp(1.0 + m / 4.0, e - 15);
+    return sign ? -v : v;
+}
+
+/* Encode y as E5M2: the nearest of the finite magnitudes 0x00 .. 0x7B, a tie
+ * going to the code whose mantissa is even, and magnitudes beyond 57344
+ * (infinity included) saturated to 57344, as for E4M3, so that a stored code
+ * is always finite; NaN gives the NaN code 0x7F.  The sign bit is y's. */
+uint8_t oracle_e5m2_encode(float y)
+{
+    uint8_t sign = signbit(y) ? 0x80 : 0;
+    if (isnan(y))
+        return sign | 0x7F;
+    double a = fabs((double)y);
+    if (a >= 57344.0)
+        return sign | 0x7B;
+    int best = 0;
+    double best_d = INFINITY;
+    for (int c = 0; c <= 0x7B; c++) {
+        double d = fabs(oracle_e5m2_value((uint8_t)c) - a);
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return sign | (uint8_t)best;
+}
+
+static uint8_t encode_fp8(float y, int32_t fmt)
+{
+    return fmt == 1 ? oracle_e5m2_encode(y) : oracle_e4m3_encode(y);
+}
+
 /* The fp8 scatter: like oracle_reshape_and_cache, but each element x of the
- * token's K (V) row is stored as oracle_e4m3_encode(x / k_scale) (v_scale),
- * the division done in float32.  key/value are float32 (dtype 0) or bf16 bits
- * (dtype 1); the caches hold one byte per element. */
+ * token's K (V) row is stored as the code of x / k_scale (v_scale), the
+ * division done in float32, in the format fmt (0: E4M3, encoded by
+ * oracle_e4m3_encode; 1: E5M2, by oracle_e5m2_encode).  key/value are float32
+ * (dtype 0) or bf16 bits (dtype 1); the caches hold one byte per element. */
 void oracle_reshape_and_cache_fp8(const void *key, int64_t key_stride, const void *value, int64_t value_stride,
                                   uint8_t *key_cache, uint8_t *value_cache, const int64_t *slot_mapping,
                                   int64_t num_tokens, int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
-                                  int32_t dtype, float k_scale, float v_scale)
+                                  int32_t dtype, float k_scale, float v_scale, int32_t fmt)
 {
     const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
     /* bf16 sources have 65536 bit patterns: the code of each (the same
@@ -370,17 +424,17 @@ void oracle_reshape_and_cache_fp8(const void *key, int64_t key_stride, const voi
      * looked up.  Not thread-safe: the oracle's scatter runs on one thread. */
     static uint8_t kcode_memo[65536], vcode_memo[65536];
     static float memo_k = 0.f, memo_v = 0.f;
-    static int memo_valid = 0;
+    static int32_t memo_fmt = -1;
     const uint8_t *kcode = NULL, *vcode = NULL;
     if (dtype == ORACLE_BF16) {
-        if (!memo_valid || memo_k != k_scale || memo_v != v_scale) {
+        if (memo_fmt != fmt || memo_k != k_scale || memo_v != v_scale) {
             for (int32_t u = 0; u < 65536; u++) {
                 uint16_t bits = (uint16_t)u;
                 float x = (float)widen(&bits, 0, ORACLE_BF16);
-                kcode_memo[u] = oracle_e4m3_encode(x / k_scale);
-                vcode_memo[u] = oracle_e4m3_encode(x / v_scale);
+                kcode_memo[u] = encode_fp8(x / k_scale, fmt);
+                vcode_memo[u] = encode_fp8(x / v_scale, fmt);
             }
-            memo_k = k_scale, memo_v = v_scale, memo_valid = 1;
+            memo_k = k_scale, memo_v = v_scale, memo_fmt = fmt;
         }
         kcode = kcode_memo;
         vcode = vcode_memo;
@@ -398,8 +452,8 @@ void oracle_reshape_and_cache_fp8(const void *key, int64_t key_stride, const voi
             }
             float k = (float)widen(key, i * key_stride + e, dtype);
             float v = (float)widen(value, i * value_stride + e, dtype);
-            key_cache[dst + e] = oracle_e4m3_encode(k / k_scale);
-            value_cache[dst + e] = oracle_e4m3_encode(v / v_scale);
+            key_cache[dst + e] = encode_fp8(k / k_scale, fmt);
+            value_cache[dst + e] = encode_fp8(v / v_scale, fmt);
         }
     }
 }

@@ -40,7 +40,14 @@ MUTANTS = {
     "e4m3_saturation_point": ("if (a >= 448.0)", "if (a >= 240.0)"),
     "fp8_k_scale_dropped": ("(widen(key_cache, kbase + d, kv_dtype) * k_scale)",
                             "widen(key_cache, kbase + d, kv_dtype)"),
-    "fp8_scatter_multiplies": ("oracle_e4m3_encode(k / k_scale)", "oracle_e4m3_encode(k * k_scale)"),
+    "fp8_scatter_multiplies": ("encode_fp8(x / k_scale, fmt)", "encode_fp8(x * k_scale, fmt)"),
+    "e5m2_bias": ("v = ldexp(1.0 + m / 4.0, e - 15);", "v = ldexp(1.0 + m / 4.0, e - 16);"),
+    "e5m2_subnormal_step": ("v = ldexp((double)m, -16);", "v = ldexp((double)m, -17);"),
+    "e5m2_ties_to_odd": ("if (d < best_d || (d == best_d && (c & 1) == 0)) {\n            best = c;\n            best_d = d;\n        }\n    }\n    return sign | (uint8_t)best;\n}\n\nstatic",
+                         "if (d < best_d || (d == best_d && (c & 1) == 1)) {\n            best = c;\n            best_d = d;\n        }\n    }\n    return sign | (uint8_t)best;\n}\n\nstatic"),
+    "e5m2_saturates_to_infinity": ("        return sign | 0x7B;", "        return sign | 0x7C;"),
+    "e5m2_format_ignored": ("return fmt == 1 ? oracle_e5m2_encode(y) : oracle_e4m3_encode(y);",
+                            "return oracle_e4m3_encode(y);"),
     "copy_direction": ("memmove(k + dst * block_bytes, k + src * block_bytes, (size_t)block_bytes);",
                        "memmove(k + src * block_bytes, k + dst * block_bytes, (size_t)block_bytes);"),
     "copy_first_layer_only": ("for (int32_t l = 0; l < num_layers; l++) {\n            char *k",
