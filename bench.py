@@ -18,16 +18,17 @@ Prints one JSON line.  The same run also times, under "workloads": batch 64
 with contexts uniform in [1024, 8192]; batch 16 at 32768; 256 sequences of
 log-normal length with 64 query heads; the chunked-prefill mix (4 x 512-row
 chunks + 96 decodes: the unified call, then the chunks against the bf16 matrix
-peak and the decodes against HBM); and the headline batch over an fp8 (E4M3)
-cache.  The CPU baseline runs the oracle over the whole headline workload.
+peak and the decodes against HBM); and the headline batch over fp8 caches
+(E4M3 and E5M2).  The CPU baseline runs the oracle over the whole headline workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-cache bf16|fp8]
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--kv-cache bf16|fp8|e5m2]
                   [--step append|two-call] [--no-cpu-baseline] [--no-probes] [--no-extra]
 
 With --workload chunked_prefill_mix the headline step is the scatter plus one
 pa_chunked_prefill call over 4 prefill chunks and 96 decodes.  With --kv-cache
-fp8 the caches hold E4M3 codes: the step is pa_slot_mapping_and_cache_fp8 and
-pa_decode_fp8, and KV bytes count one byte per element.
+fp8 the caches hold E4M3 codes (--kv-cache e5m2: E5M2 codes): the step is
+pa_slot_mapping_and_cache_fp8 and pa_decode_fp8, and KV bytes count one byte
+per element.
 """
 from __future__ import annotations
 
@@ -64,15 +65,16 @@ def parse():
                    choices=["llama8b_decode", "llama8b_decode_8k", "long_context", "continuous_batching",
                             "chunked_prefill_mix"])
     p.add_argument("--partition-tokens", type=int, default=0)
-    p.add_argument("--kv-cache", default="bf16", choices=["bf16", "fp8"],
-                   help="fp8: the caches hold E4M3 codes (pa_reshape_and_cache_fp8 / pa_decode_fp8)")
+    p.add_argument("--kv-cache", default="bf16", choices=["bf16", "fp8", "e5m2"],
+                   help="fp8: the caches hold E4M3 codes (pa_slot_mapping_and_cache_fp8 / pa_decode_fp8); "
+                        "e5m2: E5M2 codes through the same calls' _ex forms")
     p.add_argument("--step", default="append", choices=["append", "two-call"],
                    help="append: the step is one pa_decode_append call (bf16/fp32 caches, stream mode); "
                         "two-call: pa_slot_mapping_and_cache, then pa_decode")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probes", action="store_true")
     p.add_argument("--no-extra", action="store_true",
-                   help="time only the headline workload (not the other configurations and the fp8 cache)")
+                   help="time only the headline workload (not the other configurations and the fp8 caches)")
     return p.parse_args()
 
 
@@ -340,10 +342,10 @@ def cpu_info() -> dict:
             "omp_num_threads_env": int(env) if env and env.isdigit() else None}
 
 
-def cpu_baseline(w, fp8: bool = False, one_thread_seqs: int = 4):
+def cpu_baseline(w, fp8=None, one_thread_seqs: int = 4):
     """The oracle, untuned, on the host cores, over the WHOLE workload of the
     headline line: one step (slots and scatter of the step's new tokens, then
-    attention over every sequence; over E4M3 codes when fp8), its caches
+    attention over every sequence; over fp8 codes when fp8 names a format), its caches
     holding every sequence's earlier context (built before timing).  It runs
     with OpenMP over (query row, head) on the job's CPU share: every CPU the
     process may run on, capped by OMP_NUM_THREADS where the job sets it.  A
@@ -358,18 +360,18 @@ def cpu_baseline(w, fp8: bool = False, one_thread_seqs: int = 4):
     oracle.set_threads(threads)
     t_setup = time.perf_counter()
     ks, vs = w.fp8_scales()
-    kc, vc = oracle.build_cache_fp8(w, ks, vs, "history") if fp8 else oracle.build_cache(w, "history")
+    kc, vc = oracle.build_cache_fp8(w, ks, vs, "history", fp8) if fp8 else oracle.build_cache(w, "history")
     seq, pos = w.tokens("new")
     k_new, v_new = (w.encode(x) for x in w.token_kv(seq, pos))
     q = w.encode(w.queries())
     setup_s = time.perf_counter() - t_setup
-    sc = dict(k_scale=ks, v_scale=vs) if fp8 else {}
+    sc = dict(k_scale=ks, v_scale=vs, fp8_format=fp8) if fp8 else {}
     times = []
     for _ in range(3):                               # median of three runs of the step
         t0 = time.perf_counter()
         slots = oracle.slot_mapping(w.block_table, seq, pos)
         if fp8:
-            oracle.reshape_and_cache_fp8(k_new, v_new, kc, vc, slots, ks, vs)
+            oracle.reshape_and_cache_fp8(k_new, v_new, kc, vc, slots, ks, vs, fp8_format=fp8)
         else:
             oracle.reshape_and_cache(k_new, v_new, kc, vc, slots)
         oracle.attention(q, kc, vc, w.block_table, w.cu_query_lens, w.seq_lens, w.num_heads, w.scale,
@@ -521,13 +523,14 @@ def measure_mixed(w, steps: int, warmup: int, torch, pa, W, DeviceWorkload, mfma
     return r
 
 
-def measure_decode(w, steps: int, warmup: int, torch, pa, DeviceWorkload, fp8: bool = False,
+def measure_decode(w, steps: int, warmup: int, torch, pa, DeviceWorkload, fp8=None,
                    step_kind: str = "append", partition_tokens: int = 0) -> dict:
     """One decode workload: K timed steps with nothing else on the stream (the
     step: pa_decode_append, or the two-call form / fp8 step), then K more with
     HIP events around each attention call (the kernel's own rate), then K
-    steps of the two-call form for comparison when the step is the one call."""
-    dw = DeviceWorkload(w, kv_fp8=fp8)
+    steps of the two-call form for comparison when the step is the one call.
+    fp8: None (a bf16 cache) or the fp8 format of the cache, "e4m3" / "e5m2"."""
+    dw = DeviceWorkload(w, kv_fp8=bool(fp8), fp8_format=fp8 or "e4m3")
     pt = pa.pa_decode_partition_tokens(w.num_seqs, w.num_kv_heads, w.max_seq_len, partition_tokens)
     ws = dw.decode_workspace(partition_tokens)
     out = torch.empty_like(dw.query)
@@ -595,9 +598,9 @@ def measure_decode(w, steps: int, warmup: int, torch, pa, DeviceWorkload, fp8: b
         "append": append,
         "partition_tokens": pt,
         "step": "pa_decode_append (slots, scatter and decode in one call)" if append
-                else ("pa_slot_mapping_and_cache_fp8 + pa_decode_fp8" if fp8
+                else ((f"pa_slot_mapping_and_cache_fp8 + pa_decode_fp8 ({fp8})") if fp8
                       else "pa_slot_mapping_and_cache + pa_decode"),
-        "kernel": "pa_decode_fp8: decode_stream_kernel<fp8> + merge_stream_kernel (one call)" if fp8
+        "kernel": f"pa_decode_fp8 ({fp8}): decode_stream_kernel<fp8> + merge_stream_kernel (one call)" if fp8
                   else "pa_decode_append: decode_stream_kernel<append> + merge_stream_kernel (one call)" if append
                   else "pa_decode: decode_stream_kernel + merge_stream_kernel (one call)" if pt == 0
                   else "pa_decode: decode_partition_kernel + merge_partitions_kernel (one call)",
@@ -642,7 +645,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     pa.lib()
     w = W.CONFIGS[args.workload]()
-    fp8 = args.kv_cache == "fp8"
+    fp8 = {"bf16": None, "fp8": "e4m3", "e5m2": "e5m2"}[args.kv_cache]
     if fp8 and args.partition_tokens != 0:
         print("an fp8 cache is read in the stream mode only (--partition-tokens 0)", file=sys.stderr)
         sys.exit(2)
@@ -671,7 +674,7 @@ def main():
     res.update({
         "value": r["GBps"],
         "ms_per_step": r["ms_per_step"],
-        "dtype": "fp8_e4m3 KV, bf16 Q/out" if fp8 else w.dtype,
+        "dtype": f"fp8_{fp8} KV, bf16 Q/out" if fp8 else w.dtype,
         "config": {
             "workload": w.name,
             "batch": w.num_seqs,
@@ -683,8 +686,8 @@ def main():
             "decode_split": "balanced stream (equal block shares per workgroup)" if r["partition_tokens"] == 0
                             else f"partitions of {r['partition_tokens']} tokens",
             "kv_bytes_per_step": r["kv_bytes_per_step"],
-            "kv_cache": "fp8 E4M3 (1 byte/element), k_scale = v_scale = %.6g" % w.fp8_scales()[0] if fp8
-                        else w.dtype,
+            "kv_cache": "fp8 %s (1 byte/element), k_scale = v_scale = %.6g" % (fp8.upper(), w.fp8_scales()[0])
+                        if fp8 else w.dtype,
             "step": r["step"],
         },
         "pct_hbm_peak": r["pct_hbm_peak"],
@@ -717,11 +720,13 @@ def main():
         extra[wm.name] = _brief(measure_mixed(wm, extra_steps, extra_warmup, torch, pa, W, DeviceWorkload,
                                               mfma=False))
         print(f"# {wm.name}: {extra[wm.name]['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
-        if not fp8:
-            f = _brief(measure_decode(w, extra_steps, extra_warmup, torch, pa, DeviceWorkload, fp8=True))
-            f["kv_cache"] = "fp8 E4M3 (1 byte/element), k_scale = v_scale = %.6g" % w.fp8_scales()[0]
-            extra[w.name + ":fp8"] = f
-            print(f"# {w.name} fp8: {f['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+        for fmt in ("e4m3", "e5m2"):
+            if fmt == fp8:
+                continue
+            f = _brief(measure_decode(w, extra_steps, extra_warmup, torch, pa, DeviceWorkload, fp8=fmt))
+            f["kv_cache"] = "fp8 %s (1 byte/element), k_scale = v_scale = %.6g" % (fmt.upper(), w.fp8_scales()[0])
+            extra[w.name + ":" + fmt] = f
+            print(f"# {w.name} {fmt}: {f['ms_per_step'] * 1e3:.1f} us/step", file=sys.stderr, flush=True)
         res["workloads"] = extra
     if not args.no_probes:
         probe = probes(pa, torch)

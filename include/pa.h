@@ -306,6 +306,56 @@ pa_status pa_decode_fp8(void *out, const void *query, int64_t q_token_stride,
                         hipStream_t stream);
 
 /*
+ * The other 8-bit format of the pages' fp8 KV cache.  The three calls above
+ * store and read E4M3 codes; each has an _ex form that takes the format:
+ *   PA_FP8_E4M3  as above;
+ *   PA_FP8_E5M2  OCP E5M2: bias 15, 2 mantissa bits, subnormals m * 2^-16,
+ *                infinity at S.11111.00 and NaN at S.11111.{01,10,11}, largest
+ *                finite 57344.  The scatter stores E5M2(x / scale) with the
+ *                same rules as E4M3 (float32 division, nearest code, ties to
+ *                the even mantissa, NaN kept), magnitudes beyond 57344
+ *                (infinity included) saturating to 57344, so that stored codes
+ *                are finite; the decode widens the codes exactly (every finite
+ *                E5M2 value is a bf16 and an fp16 value) and then computes as
+ *                pa_decode_fp8 does.
+ * A cache must be read in the format it was written in.  Other format values
+ * return PA_ERR_UNSUPPORTED.
+ */
+typedef enum {
+    PA_FP8_E4M3 = 0,
+    PA_FP8_E5M2 = 1,
+    PA_FP8_FORMAT_RESERVED_MIN_ = -0x7fffffff - 1,   /* range widened to every int, as for pa_dtype */
+    PA_FP8_FORMAT_RESERVED_MAX_ = 0x7fffffff
+} pa_fp8_format;
+
+pa_status pa_reshape_and_cache_fp8_ex(const void *key, int64_t key_token_stride,
+                                      const void *value, int64_t value_token_stride,
+                                      void *key_cache, void *value_cache,
+                                      const int64_t *slot_mapping, int64_t num_tokens,
+                                      int64_t num_blocks, int32_t block_size,
+                                      int32_t num_kv_heads, int32_t head_dim,
+                                      pa_dtype dtype, pa_fp8_format format,
+                                      float k_scale, float v_scale, hipStream_t stream);
+pa_status pa_slot_mapping_and_cache_fp8_ex(int64_t *slot_mapping, const int32_t *block_table,
+                                           int32_t max_blocks_per_req, int32_t num_seqs,
+                                           const int32_t *token_seq, const int32_t *token_pos,
+                                           const void *key, int64_t key_token_stride,
+                                           const void *value, int64_t value_token_stride,
+                                           void *key_cache, void *value_cache,
+                                           int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                                           int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                           pa_fp8_format format, float k_scale, float v_scale,
+                                           hipStream_t stream);
+pa_status pa_decode_fp8_ex(void *out, const void *query, int64_t q_token_stride,
+                           const void *key_cache, const void *value_cache,
+                           const int32_t *block_table, int32_t max_blocks_per_req,
+                           const int32_t *seq_lens, int32_t num_seqs, int32_t num_heads,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                           int64_t num_blocks, float scale, pa_fp8_format format,
+                           float k_scale, float v_scale, int32_t max_seq_len,
+                           void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The step just before attention, fused into one pass ("AI Infra入门干货总结：
  * 大模型是如何高效推理的", section "Reshape & Cache" and its table, and the RoPE
  * summary near its opening): split each token's fused QKV projection row into

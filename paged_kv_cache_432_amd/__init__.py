@@ -26,6 +26,7 @@ __all__ = [
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
 PA_F32, PA_BF16 = 0, 1
+PA_FP8_FORMATS = {"e4m3": 0, "e5m2": 1}
 BLOCK_SIZE = 16
 
 _DIR = os.path.dirname(os.path.abspath(__file__))
@@ -112,6 +113,18 @@ def lib():
         L.pa_slot_mapping_and_cache_fp8.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp, _vp,
                                                     _i64, _i64, _i32, _i32, _i32, ctypes.c_int, ctypes.c_float,
                                                     ctypes.c_float, _vp]
+        L.pa_reshape_and_cache_fp8_ex.restype = ctypes.c_int
+        L.pa_reshape_and_cache_fp8_ex.argtypes = [_vp, _i64, _vp, _i64, _vp, _vp, _vp, _i64, _i64, _i32,
+                                                  _i32, _i32, ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                                  ctypes.c_float, _vp]
+        L.pa_slot_mapping_and_cache_fp8_ex.restype = ctypes.c_int
+        L.pa_slot_mapping_and_cache_fp8_ex.argtypes = [_vp, _vp, _i32, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp,
+                                                       _vp, _i64, _i64, _i32, _i32, _i32, ctypes.c_int, ctypes.c_int,
+                                                       ctypes.c_float, ctypes.c_float, _vp]
+        L.pa_decode_fp8_ex.restype = ctypes.c_int
+        L.pa_decode_fp8_ex.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                       _i32, _i64, ctypes.c_float, ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                       _i32, _vp, ctypes.c_size_t, _vp]
         L.pa_decode_fp8.restype = ctypes.c_int
         L.pa_decode_fp8.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                     _i32, _i64, ctypes.c_float, ctypes.c_float, ctypes.c_float, _i32, _vp,
@@ -359,11 +372,17 @@ def pa_copy_blocks(kv_cache: torch.Tensor, block_mapping: torch.Tensor, stream=N
     _check(s, "pa_copy_blocks")
 
 
+def _fp8_format(name: str) -> int:
+    _need(name in PA_FP8_FORMATS, f"fp8_format {name!r}: 'e4m3' or 'e5m2'")
+    return PA_FP8_FORMATS[name]
+
+
 def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: torch.Tensor,
                              value_cache: torch.Tensor, slot_mapping: torch.Tensor, k_scale: float, v_scale: float,
-                             stream=None) -> None:
+                             stream=None, fp8_format: str = "e4m3") -> None:
     """Scatter key/value [num_tokens, Hkv, D] (bf16 or fp32, token stride free)
-    into uint8 E4M3 caches [num_blocks, 16, Hkv, D] as codes of x / scale."""
+    into uint8 fp8 caches [num_blocks, 16, Hkv, D] as codes of x / scale, in
+    fp8_format ("e4m3" or "e5m2")."""
     _need(key.dim() == 3 and value.dim() == 3 and key.shape == value.shape, "key/value: [num_tokens, Hkv, D]")
     _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
     _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
@@ -375,19 +394,21 @@ def pa_reshape_and_cache_fp8(key: torch.Tensor, value: torch.Tensor, key_cache: 
           "key/value heads and dims must be contiguous")
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.numel() == n and slot_mapping.is_contiguous(),
           "slot_mapping: contiguous int64 [num_tokens]")
-    s = lib().pa_reshape_and_cache_fp8(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
-                                       _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), n,
-                                       key_cache.shape[0], key_cache.shape[1], hkv, d, _dtype_code(key),
-                                       float(k_scale), float(v_scale), _stream(stream, key_cache.device))
-    _check(s, "pa_reshape_and_cache_fp8")
+    s = lib().pa_reshape_and_cache_fp8_ex(_ptr(key), key.stride(0), _ptr(value), value.stride(0),
+                                          _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping), n,
+                                          key_cache.shape[0], key_cache.shape[1], hkv, d, _dtype_code(key),
+                                          _fp8_format(fp8_format), float(k_scale), float(v_scale),
+                                          _stream(stream, key_cache.device))
+    _check(s, "pa_reshape_and_cache_fp8_ex")
 
 
 def pa_slot_mapping_and_cache_fp8(slot_mapping: torch.Tensor, block_table: torch.Tensor, token_seq: torch.Tensor,
                                   token_pos: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
                                   key_cache: torch.Tensor, value_cache: torch.Tensor, k_scale: float, v_scale: float,
-                                  stream=None) -> torch.Tensor:
+                                  stream=None, fp8_format: str = "e4m3") -> torch.Tensor:
     """pa_slot_mapping then pa_reshape_and_cache_fp8 in one launch: slot_mapping
-    (int64, out) is written and the K/V rows are quantised into the E4M3 caches."""
+    (int64, out) is written and the K/V rows are quantised into the fp8 caches
+    (fp8_format "e4m3" or "e5m2")."""
     _need(slot_mapping.dtype == torch.int64 and slot_mapping.is_contiguous(), "slot_mapping: contiguous int64")
     _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
           "block_table: contiguous int32 [num_seqs, max_blocks_per_req]")
@@ -403,21 +424,23 @@ def pa_slot_mapping_and_cache_fp8(slot_mapping: torch.Tensor, block_table: torch
     _need(key_cache.shape[2] == hkv and key_cache.shape[3] == d, "cache head shape differs from key")
     _need(key.stride(2) == 1 and key.stride(1) == d and value.stride(2) == 1 and value.stride(1) == d,
           "key/value heads and dims must be contiguous")
-    s = lib().pa_slot_mapping_and_cache_fp8(_ptr(slot_mapping), _ptr(block_table), block_table.shape[1],
-                                            block_table.shape[0], _ptr(token_seq), _ptr(token_pos), _ptr(key),
-                                            key.stride(0), _ptr(value), value.stride(0), _ptr(key_cache),
-                                            _ptr(value_cache), n, key_cache.shape[0], key_cache.shape[1], hkv, d,
-                                            _dtype_code(key), float(k_scale), float(v_scale),
-                                            _stream(stream, key_cache.device))
-    _check(s, "pa_slot_mapping_and_cache_fp8")
+    s = lib().pa_slot_mapping_and_cache_fp8_ex(_ptr(slot_mapping), _ptr(block_table), block_table.shape[1],
+                                               block_table.shape[0], _ptr(token_seq), _ptr(token_pos), _ptr(key),
+                                               key.stride(0), _ptr(value), value.stride(0), _ptr(key_cache),
+                                               _ptr(value_cache), n, key_cache.shape[0], key_cache.shape[1], hkv, d,
+                                               _dtype_code(key), _fp8_format(fp8_format), float(k_scale),
+                                               float(v_scale), _stream(stream, key_cache.device))
+    _check(s, "pa_slot_mapping_and_cache_fp8_ex")
     return slot_mapping
 
 
 def pa_decode_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, value_cache: torch.Tensor,
                   block_table: torch.Tensor, seq_lens: torch.Tensor, scale: float, k_scale: float, v_scale: float,
-                  max_seq_len: int, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Decode attention over uint8 E4M3 caches: out [B, Hq, D] bf16 for query
-    [B, Hq, D] bf16; cached codes stand for value * k_scale / v_scale."""
+                  max_seq_len: int, workspace: torch.Tensor | None = None, stream=None,
+                  fp8_format: str = "e4m3") -> torch.Tensor:
+    """Decode attention over uint8 fp8 caches (fp8_format "e4m3" or "e5m2"):
+    out [B, Hq, D] bf16 for query [B, Hq, D] bf16; cached codes stand for
+    value * k_scale / v_scale."""
     _need(query.dim() == 3 and out.shape == query.shape and out.is_contiguous(),
           "query/out: [num_seqs, num_heads, head_dim], out contiguous")
     _need(query.stride(2) == 1 and query.stride(1) == query.shape[2], "query heads/dims must be contiguous")
@@ -432,11 +455,12 @@ def pa_decode_fp8(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tenso
     _need(block_table.shape[0] >= b and seq_lens.numel() >= b, "block_table/seq_lens shorter than batch")
     nb, bs, hkv, _ = key_cache.shape
     ws = workspace
-    s = lib().pa_decode_fp8(_ptr(out), _ptr(query), query.stride(0), _ptr(key_cache), _ptr(value_cache),
-                            _ptr(block_table), block_table.shape[1], _ptr(seq_lens), b, hq, hkv, d, bs, nb,
-                            float(scale), float(k_scale), float(v_scale), int(max_seq_len), _ptr(ws),
-                            0 if ws is None else ws.numel() * ws.element_size(), _stream(stream, out.device))
-    _check(s, "pa_decode_fp8")
+    s = lib().pa_decode_fp8_ex(_ptr(out), _ptr(query), query.stride(0), _ptr(key_cache), _ptr(value_cache),
+                               _ptr(block_table), block_table.shape[1], _ptr(seq_lens), b, hq, hkv, d, bs, nb,
+                               float(scale), _fp8_format(fp8_format), float(k_scale), float(v_scale),
+                               int(max_seq_len), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                               _stream(stream, out.device))
+    _check(s, "pa_decode_fp8_ex")
     return out
 
 

@@ -326,12 +326,13 @@ pa_status pa_copy_blocks(void* key_cache, void* value_cache, int64_t layer_strid
                       "copy_blocks launch");
 }
 
-pa_status pa_reshape_and_cache_fp8(const void* key, int64_t key_token_stride, const void* value,
-                                   int64_t value_token_stride, void* key_cache, void* value_cache,
-                                   const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
-                                   int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
-                                   float k_scale, float v_scale, hipStream_t stream) {
+pa_status pa_reshape_and_cache_fp8_ex(const void* key, int64_t key_token_stride, const void* value,
+                                      int64_t value_token_stride, void* key_cache, void* value_cache,
+                                      const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                                      int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                      pa_fp8_format format, float k_scale, float v_scale, hipStream_t stream) {
     if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "source dtype %d", (int)dtype);
+    if (format != PA_FP8_E4M3 && format != PA_FP8_E5M2) return fail(PA_ERR_UNSUPPORTED, "fp8 format %d", (int)format);
     if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
     if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0)
         return fail(PA_ERR_INVALID_ARG, "negative or zero size");
@@ -352,18 +353,30 @@ pa_status pa_reshape_and_cache_fp8(const void* key, int64_t key_token_stride, co
     return hip_status(pa::launch_reshape_and_cache_fp8(key, key_token_stride * eb, value, value_token_stride * eb,
                                                        key_cache, value_cache, slot_mapping, num_tokens,
                                                        num_blocks * 16, (int32_t)row_elems,
-                                                       dtype == PA_BF16 ? 1 : 0, k_scale, v_scale, stream),
+                                                       dtype == PA_BF16 ? 1 : 0, format == PA_FP8_E5M2 ? 1 : 0,
+                                                       k_scale, v_scale, stream),
                       "reshape_and_cache_fp8 launch");
 }
 
-pa_status pa_slot_mapping_and_cache_fp8(int64_t* slot_mapping, const int32_t* block_table,
-                                        int32_t max_blocks_per_req, int32_t num_seqs, const int32_t* token_seq,
-                                        const int32_t* token_pos, const void* key, int64_t key_token_stride,
-                                        const void* value, int64_t value_token_stride, void* key_cache,
-                                        void* value_cache, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
-                                        int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype, float k_scale,
-                                        float v_scale, hipStream_t stream) {
+pa_status pa_reshape_and_cache_fp8(const void* key, int64_t key_token_stride, const void* value,
+                                   int64_t value_token_stride, void* key_cache, void* value_cache,
+                                   const int64_t* slot_mapping, int64_t num_tokens, int64_t num_blocks,
+                                   int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                   float k_scale, float v_scale, hipStream_t stream) {
+    return pa_reshape_and_cache_fp8_ex(key, key_token_stride, value, value_token_stride, key_cache, value_cache,
+                                       slot_mapping, num_tokens, num_blocks, block_size, num_kv_heads, head_dim,
+                                       dtype, PA_FP8_E4M3, k_scale, v_scale, stream);
+}
+
+pa_status pa_slot_mapping_and_cache_fp8_ex(int64_t* slot_mapping, const int32_t* block_table,
+                                           int32_t max_blocks_per_req, int32_t num_seqs, const int32_t* token_seq,
+                                           const int32_t* token_pos, const void* key, int64_t key_token_stride,
+                                           const void* value, int64_t value_token_stride, void* key_cache,
+                                           void* value_cache, int64_t num_tokens, int64_t num_blocks,
+                                           int32_t block_size, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                           pa_fp8_format format, float k_scale, float v_scale, hipStream_t stream) {
     if (dtype != PA_F32 && dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "source dtype %d", (int)dtype);
+    if (format != PA_FP8_E4M3 && format != PA_FP8_E5M2) return fail(PA_ERR_UNSUPPORTED, "fp8 format %d", (int)format);
     if (block_size != 16) return fail(PA_ERR_UNSUPPORTED, "block_size %d (only 16)", block_size);
     if (num_tokens < 0 || num_blocks < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_seqs < 0 ||
         max_blocks_per_req < 0)
@@ -388,8 +401,21 @@ pa_status pa_slot_mapping_and_cache_fp8(int64_t* slot_mapping, const int32_t* bl
                                                     token_pos, key, key_token_stride * eb, value,
                                                     value_token_stride * eb, key_cache, value_cache, num_tokens,
                                                     num_blocks * 16, (int32_t)row_elems, dtype == PA_BF16 ? 1 : 0,
-                                                    k_scale, v_scale, stream),
+                                                    format == PA_FP8_E5M2 ? 1 : 0, k_scale, v_scale, stream),
                       "slot_and_cache_fp8 launch");
+}
+
+pa_status pa_slot_mapping_and_cache_fp8(int64_t* slot_mapping, const int32_t* block_table,
+                                        int32_t max_blocks_per_req, int32_t num_seqs, const int32_t* token_seq,
+                                        const int32_t* token_pos, const void* key, int64_t key_token_stride,
+                                        const void* value, int64_t value_token_stride, void* key_cache,
+                                        void* value_cache, int64_t num_tokens, int64_t num_blocks, int32_t block_size,
+                                        int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype, float k_scale,
+                                        float v_scale, hipStream_t stream) {
+    return pa_slot_mapping_and_cache_fp8_ex(slot_mapping, block_table, max_blocks_per_req, num_seqs, token_seq,
+                                            token_pos, key, key_token_stride, value, value_token_stride, key_cache,
+                                            value_cache, num_tokens, num_blocks, block_size, num_kv_heads, head_dim,
+                                            dtype, PA_FP8_E4M3, k_scale, v_scale, stream);
 }
 
 pa_status pa_rope_reshape_and_cache(void* query_out, int64_t q_out_token_stride, const void* qkv,
@@ -456,7 +482,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
     if (use_stream(num_seqs, partition_tokens)) {
         const int32_t group = num_heads / num_kv_heads;
         size_t bytes = 0;
-        for (int dtype = 0; dtype < 4; ++dtype) {          // the largest of the layouts (fp32, bf16, fp8 cache, append)
+        for (int dtype = 0; dtype < 5; ++dtype) {          // the largest of the layouts (fp32, bf16, E4M3 cache,
+                                                           // append, E5M2 cache)
             const size_t n = stream_ws_bytes(num_seqs, num_heads, num_kv_heads,
                                              stream_shape(dtype, group, num_kv_heads, num_seqs));
             bytes = n > bytes ? n : bytes;
@@ -490,7 +517,7 @@ pa_status plan_decode(DecodePlan& plan, void* out, const void* query, int64_t q_
                         float v_scale, const void* new_key = nullptr, int64_t new_key_stride_bytes = 0,
                         const void* new_value = nullptr, int64_t new_value_stride_bytes = 0,
                         int64_t* slot_out = nullptr) {
-    // dt: 0 fp32, 1 bf16, 2 fp8 cache (bf16 query and output, stream mode only),
+    // dt: 0 fp32, 1 bf16, 2 E4M3 / 4 E5M2 cache (bf16 query and output, stream mode only),
     // 3 bf16 in append mode (stream mode only; the new_* rows and slot_out)
     const int32_t group = num_heads / num_kv_heads;
     plan.dt = dt;
@@ -590,12 +617,13 @@ pa_status check_heads(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
 
 extern "C" {
 
-pa_status pa_decode_fp8(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
-                        const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
-                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                        int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, float k_scale,
-                        float v_scale, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
-                        hipStream_t stream) {
+pa_status pa_decode_fp8_ex(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+                           const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                           pa_fp8_format format, float k_scale, float v_scale, int32_t max_seq_len, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    if (format != PA_FP8_E4M3 && format != PA_FP8_E5M2) return fail(PA_ERR_UNSUPPORTED, "fp8 format %d", (int)format);
     const pa_status hs = check_heads(num_heads, num_kv_heads, head_dim, block_size);
     if (hs != PA_OK) return hs;
     if (num_seqs < 0 || num_blocks < 0 || max_seq_len < 0 || max_blocks_per_req < 0)
@@ -619,7 +647,18 @@ pa_status pa_decode_fp8(void* out, const void* query, int64_t q_token_stride, co
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
     return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
                          seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len, 0,
-                         workspace, workspace_bytes, 2, k_scale, v_scale, stream);
+                         workspace, workspace_bytes, format == PA_FP8_E5M2 ? 4 : 2, k_scale, v_scale, stream);
+}
+
+pa_status pa_decode_fp8(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+                        const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
+                        const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale, float k_scale,
+                        float v_scale, int32_t max_seq_len, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+    return pa_decode_fp8_ex(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
+                            seq_lens, num_seqs, num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale,
+                            PA_FP8_E4M3, k_scale, v_scale, max_seq_len, workspace, workspace_bytes, stream);
 }
 
 pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const void* key_cache,

@@ -6,6 +6,8 @@
 // the token's [num_kv_heads, head_dim] K and V rows to cache[slot / block_size,
 // slot % block_size].  Both are pure index / copy work: no rounding is involved
 // and results are bit-exact.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -81,38 +83,48 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, int64_t layer_
     return hipGetLastError();
 }
 
-// ---- fp8 (E4M3) scatter ------------------------------------------------------
+// ---- fp8 (E4M3 or E5M2) scatter -------------------------------------------
 // As reshape_and_cache_kernel, but each element x of a K (V) row is stored as
-// the OCP E4M3 code of x / k_scale (v_scale): the division in float32
-// (correctly rounded), magnitudes beyond 448 saturated to 448, NaN kept, then
-// the hardware conversion to the nearest code, ties to even.  One workgroup
-// per token: threads 0-127 take the K row, 128-255 the V row, 16 elements
-// (16 output bytes) per step.
-// 16 source elements (two chunks) -> their 16 E4M3 codes of x / scale.
-template <typename Chunk>
+// the OCP E4M3 (E5 = false) or E5M2 (E5 = true) code of x / k_scale
+// (v_scale): the division in float32 (correctly rounded), magnitudes beyond
+// the format's largest finite value (448; 57344) saturated to it, NaN kept,
+// then the hardware conversion to the nearest code, ties to even.  One
+// workgroup per token: threads 0-127 take the K row, 128-255 the V row, 16
+// elements (16 output bytes) per step.
+template <bool E5, bool HI>
+__device__ __forceinline__ int cvt_pk_fp8(float a, float b, int old) {
+    if constexpr (E5)
+        return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+    else
+        return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+// 16 source elements (two chunks) -> their 16 codes of x / scale.
+template <typename Chunk, bool E5>
 __device__ __forceinline__ u32x4_t fp8_codes(const Chunk& x0, const Chunk& x1, float scale) {
+    constexpr float kMax = E5 ? 57344.f : 448.f;
     float f[16];
     to_f32(x0, f);
     to_f32(x1, f + 8);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         const float y = f[e] / scale;
-        f[e] = __builtin_fabsf(y) > 448.f ? __builtin_copysignf(448.f, y) : y;
+        f[e] = __builtin_fabsf(y) > kMax ? __builtin_copysignf(kMax, y) : y;
     }
     u32x4_t w;
-    int p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    p0 = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], p0, true);
-    int p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-    p1 = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], p1, true);
-    int p2 = __builtin_amdgcn_cvt_pk_fp8_f32(f[8], f[9], 0, false);
-    p2 = __builtin_amdgcn_cvt_pk_fp8_f32(f[10], f[11], p2, true);
-    int p3 = __builtin_amdgcn_cvt_pk_fp8_f32(f[12], f[13], 0, false);
-    p3 = __builtin_amdgcn_cvt_pk_fp8_f32(f[14], f[15], p3, true);
+    int p0 = cvt_pk_fp8<E5, false>(f[0], f[1], 0);
+    p0 = cvt_pk_fp8<E5, true>(f[2], f[3], p0);
+    int p1 = cvt_pk_fp8<E5, false>(f[4], f[5], 0);
+    p1 = cvt_pk_fp8<E5, true>(f[6], f[7], p1);
+    int p2 = cvt_pk_fp8<E5, false>(f[8], f[9], 0);
+    p2 = cvt_pk_fp8<E5, true>(f[10], f[11], p2);
+    int p3 = cvt_pk_fp8<E5, false>(f[12], f[13], 0);
+    p3 = cvt_pk_fp8<E5, true>(f[14], f[15], p3);
     w.x = (uint32_t)p0; w.y = (uint32_t)p1; w.z = (uint32_t)p2; w.w = (uint32_t)p3;
     return w;
 }
 
-template <typename Chunk>
+template <typename Chunk, bool E5>
 __global__ void __launch_bounds__(256)
 reshape_and_cache_fp8_kernel(const char* __restrict__ key, int64_t key_stride_bytes,
                              const char* __restrict__ value, int64_t value_stride_bytes,
@@ -130,7 +142,7 @@ reshape_and_cache_fp8_kernel(const char* __restrict__ key, int64_t key_stride_by
         Chunk x0, x1;
         load_chunk<false>(x0, src + (int64_t)c * 16 * Chunk::kBytes / 8);
         load_chunk<false>(x1, src + ((int64_t)c * 16 + 8) * Chunk::kBytes / 8);
-        *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = fp8_codes(x0, x1, scale);
+        *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = fp8_codes<Chunk, E5>(x0, x1, scale);
     }
 }
 
@@ -139,7 +151,7 @@ reshape_and_cache_fp8_kernel(const char* __restrict__ key, int64_t key_stride_by
 // table (-1 for a padding or unallocated token), written to slot_out[t], and
 // the token's rows are quantised into it.  The first 16 elements a thread
 // handles are loaded before the slot is known.
-template <typename Chunk>
+template <typename Chunk, bool E5>
 __global__ void __launch_bounds__(256)
 slot_and_cache_fp8_kernel(int64_t* __restrict__ slot_out, const int32_t* __restrict__ block_table, int32_t bt_stride,
                           int32_t num_seqs, const int32_t* __restrict__ token_seq,
@@ -168,48 +180,72 @@ slot_and_cache_fp8_kernel(int64_t* __restrict__ slot_out, const int32_t* __restr
     if (slot < 0 || slot >= num_slots) return;
     uint8_t* dst = (is_v ? value_cache : key_cache) + slot * (int64_t)row_elems;
     const float scale = is_v ? v_scale : k_scale;
-    if (c0 < chunks) *reinterpret_cast<u32x4_t*>(dst + (int64_t)c0 * 16) = fp8_codes(x0, x1, scale);
+    if (c0 < chunks) *reinterpret_cast<u32x4_t*>(dst + (int64_t)c0 * 16) = fp8_codes<Chunk, E5>(x0, x1, scale);
     for (int32_t c = c0 + 128; c < chunks; c += 128) {      // rows longer than 2048 elements
         load_chunk<false>(x0, src + (int64_t)c * 16 * Chunk::kBytes / 8);
         load_chunk<false>(x1, src + ((int64_t)c * 16 + 8) * Chunk::kBytes / 8);
-        *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = fp8_codes(x0, x1, scale);
+        *reinterpret_cast<u32x4_t*>(dst + (int64_t)c * 16) = fp8_codes<Chunk, E5>(x0, x1, scale);
     }
+}
+
+template <typename Chunk, bool E5>
+void slot_and_cache_fp8_typed(int64_t* slot_mapping, const int32_t* block_table, int32_t max_blocks_per_req,
+                              int32_t num_seqs, const int32_t* token_seq, const int32_t* token_pos, const void* key,
+                              int64_t key_stride_bytes, const void* value, int64_t value_stride_bytes, void* key_cache,
+                              void* value_cache, int64_t num_tokens, int64_t num_slots, int32_t row_elems,
+                              float k_scale, float v_scale, hipStream_t stream) {
+    hipLaunchKernelGGL((slot_and_cache_fp8_kernel<Chunk, E5>), dim3((unsigned)num_tokens), dim3(256), 0, stream,
+                       slot_mapping, block_table, max_blocks_per_req, num_seqs, token_seq, token_pos,
+                       (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
+                       (uint8_t*)key_cache, (uint8_t*)value_cache, num_slots, row_elems, k_scale, v_scale);
+}
+
+template <typename Chunk, bool E5>
+void reshape_and_cache_fp8_typed(const void* key, int64_t key_stride_bytes, const void* value,
+                                 int64_t value_stride_bytes, void* key_cache, void* value_cache,
+                                 const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,
+                                 int32_t row_elems, float k_scale, float v_scale, hipStream_t stream) {
+    hipLaunchKernelGGL((reshape_and_cache_fp8_kernel<Chunk, E5>), dim3((unsigned)num_tokens), dim3(256), 0, stream,
+                       (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
+                       (uint8_t*)key_cache, (uint8_t*)value_cache, slot_mapping, num_slots, row_elems, k_scale,
+                       v_scale);
 }
 
 hipError_t launch_slot_and_cache_fp8(int64_t* slot_mapping, const int32_t* block_table, int32_t max_blocks_per_req,
                                      int32_t num_seqs, const int32_t* token_seq, const int32_t* token_pos,
                                      const void* key, int64_t key_stride_bytes, const void* value,
                                      int64_t value_stride_bytes, void* key_cache, void* value_cache,
-                                     int64_t num_tokens, int64_t num_slots, int32_t row_elems, int dtype,
+                                     int64_t num_tokens, int64_t num_slots, int32_t row_elems, int dtype, int fmt,
                                      float k_scale, float v_scale, hipStream_t stream) {
-    if (dtype == 1)
-        hipLaunchKernelGGL(slot_and_cache_fp8_kernel<ChunkBF16>, dim3((unsigned)num_tokens), dim3(256), 0, stream,
-                           slot_mapping, block_table, max_blocks_per_req, num_seqs, token_seq, token_pos,
-                           (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
-                           (uint8_t*)key_cache, (uint8_t*)value_cache, num_slots, row_elems, k_scale, v_scale);
-    else
-        hipLaunchKernelGGL(slot_and_cache_fp8_kernel<ChunkF32>, dim3((unsigned)num_tokens), dim3(256), 0, stream,
-                           slot_mapping, block_table, max_blocks_per_req, num_seqs, token_seq, token_pos,
-                           (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
-                           (uint8_t*)key_cache, (uint8_t*)value_cache, num_slots, row_elems, k_scale, v_scale);
+    auto run = [&](auto chunk, auto e5) {
+        slot_and_cache_fp8_typed<decltype(chunk), decltype(e5)::value>(
+            slot_mapping, block_table, max_blocks_per_req, num_seqs, token_seq, token_pos, key, key_stride_bytes,
+            value, value_stride_bytes, key_cache, value_cache, num_tokens, num_slots, row_elems, k_scale, v_scale,
+            stream);
+    };
+    if (dtype == 1) {
+        if (fmt == 1) run(ChunkBF16{}, std::true_type{}); else run(ChunkBF16{}, std::false_type{});
+    } else {
+        if (fmt == 1) run(ChunkF32{}, std::true_type{}); else run(ChunkF32{}, std::false_type{});
+    }
     return hipGetLastError();
 }
 
 hipError_t launch_reshape_and_cache_fp8(const void* key, int64_t key_stride_bytes, const void* value,
                                         int64_t value_stride_bytes, void* key_cache, void* value_cache,
                                         const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,
-                                        int32_t row_elems, int dtype, float k_scale, float v_scale,
+                                        int32_t row_elems, int dtype, int fmt, float k_scale, float v_scale,
                                         hipStream_t stream) {
-    if (dtype == 1)
-        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<ChunkBF16>, dim3((unsigned)num_tokens), dim3(256), 0,
-                           stream, (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
-                           (uint8_t*)key_cache, (uint8_t*)value_cache, slot_mapping, num_slots, row_elems,
-                           k_scale, v_scale);
-    else
-        hipLaunchKernelGGL(reshape_and_cache_fp8_kernel<ChunkF32>, dim3((unsigned)num_tokens), dim3(256), 0,
-                           stream, (const char*)key, key_stride_bytes, (const char*)value, value_stride_bytes,
-                           (uint8_t*)key_cache, (uint8_t*)value_cache, slot_mapping, num_slots, row_elems,
-                           k_scale, v_scale);
+    auto run = [&](auto chunk, auto e5) {
+        reshape_and_cache_fp8_typed<decltype(chunk), decltype(e5)::value>(
+            key, key_stride_bytes, value, value_stride_bytes, key_cache, value_cache, slot_mapping, num_tokens,
+            num_slots, row_elems, k_scale, v_scale, stream);
+    };
+    if (dtype == 1) {
+        if (fmt == 1) run(ChunkBF16{}, std::true_type{}); else run(ChunkBF16{}, std::false_type{});
+    } else {
+        if (fmt == 1) run(ChunkF32{}, std::true_type{}); else run(ChunkF32{}, std::false_type{});
+    }
     return hipGetLastError();
 }
 

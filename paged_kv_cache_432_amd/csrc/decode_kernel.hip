@@ -624,21 +624,37 @@ template <bool F8> struct KvBuf;
 template <> struct KvBuf<false> { u32x4_t k[4], v[4]; };
 template <> struct KvBuf<true> { u32x4_t k[2]; u32x2_t v[4]; };
 
-// Eight fp8 (E4M3) values in two words -> eight fp16, exactly (every E4M3
-// value is an fp16 value: at most 448, at least 2^-9), byte e -> element e.
-__device__ __forceinline__ u32x4_t fp8x8_to_f16(uint32_t w0, uint32_t w1) {
-    return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, false)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.f, true)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, false)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.f, true))};
+// Two fp8 codes (the low or high half of a word) -> two fp16 / two bf16, for
+// E4M3 (E5 = false) or E5M2 (E5 = true) codes.
+template <bool E5, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_f16(uint32_t w) {
+    if constexpr (E5)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_bf8(w, 1.f, HI));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.f, HI));
 }
-// Eight fp8 (E4M3) values in two words -> eight bf16, exactly (every E4M3
-// value is a bf16 value), byte e -> element e.
+template <bool E5, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16(uint32_t w) {
+    if constexpr (E5)
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.f, HI));
+    else
+        return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.f, HI));
+}
+// Eight fp8 values in two words -> eight fp16, exactly, byte e -> element e:
+// every E4M3 value is an fp16 value (at most 448, at least 2^-9), and so is
+// every finite E5M2 value (the same exponent range as fp16, fewer mantissa
+// bits).
+template <bool E5>
+__device__ __forceinline__ u32x4_t fp8x8_to_f16(uint32_t w0, uint32_t w1) {
+    return u32x4_t{fp8x2_to_f16<E5, false>(w0), fp8x2_to_f16<E5, true>(w0), fp8x2_to_f16<E5, false>(w1),
+                   fp8x2_to_f16<E5, true>(w1)};
+}
+// Eight fp8 values in two words -> eight bf16, exactly (every E4M3 and every
+// finite E5M2 value is a bf16 value), byte e -> element e.
+template <bool E5>
 __device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-    return u32x4_t{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, false)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.f, true)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, false)),
-                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.f, true))};
+    return u32x4_t{fp8x2_to_bf16<E5, false>(w0), fp8x2_to_bf16<E5, true>(w0), fp8x2_to_bf16<E5, false>(w1),
+                   fp8x2_to_bf16<E5, true>(w1)};
 }
 
 // s_first: this wave's LDS area of 2 x G records.  The record of the wave's
@@ -647,7 +663,7 @@ __device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 // are the rows of whole segments (records written in the middle of the read
 // stream measured 4-10% slower decode calls).  The last segment's record, when
 // cut, is staged in the second half, so that both leave as coalesced stores.
-template <int G, bool NT, int NBUF, bool F8 = false, bool AP = false>
+template <int G, bool NT, int NBUF, bool F8 = false, bool AP = false, bool E5 = false>
 __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int32_t* s_pref, int4* s_tab, int64_t u0,
                                                   int64_t u1, int W, int NG, int wi, int lane, float* s_first) {
     const int total = (int)(u1 - u0);                  // the same for every wave of the workgroup
@@ -800,13 +816,13 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const u32x4_t w = buf.k[h];
-                kb[2 * h] = fp8x8_to_bf16(w.x, w.y);
-                kb[2 * h + 1] = fp8x8_to_bf16(w.z, w.w);
+                kb[2 * h] = fp8x8_to_bf16<E5>(w.x, w.y);
+                kb[2 * h + 1] = fp8x8_to_bf16<E5>(w.z, w.w);
             }
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const u32x2_t w = buf.v[r];
-                vb[r] = fp8x8_to_f16(w.x, w.y);
+                vb[r] = fp8x8_to_f16<E5>(w.x, w.y);
             }
         } else {
 #pragma unroll
@@ -982,9 +998,9 @@ __device__ __forceinline__ int64_t stream_quantum(const DecodeArgs& a, int64_t u
     return q > a.min_quantum ? q : (int64_t)a.min_quantum;
 }
 
-// F8: the caches hold fp8 (E4M3) codes; query and output stay bf16.
+// F8: the caches hold fp8 codes, E4M3 or (E5) E5M2; query and output stay bf16.
 // AP: append mode (bf16 matrix-core path only).
-template <typename Chunk, typename Elem, int G, bool QL, bool NT, bool F8 = false, bool AP = false>
+template <typename Chunk, typename Elem, int G, bool QL, bool NT, bool F8 = false, bool AP = false, bool E5 = false>
 __global__ void __launch_bounds__(512)
 decode_stream_kernel(DecodeArgs a) {
     // [num_seqs + 1] block prefix, then (matrix-core waves) G records per wave
@@ -1010,8 +1026,8 @@ decode_stream_kernel(DecodeArgs a) {
     static_assert(!AP || (MF && !F8), "append mode: bf16 matrix-core path");
     if constexpr (MF) {
         float* s_first = reinterpret_cast<float*>(s_pref + ((B + 1 + 3) & ~3)) + wi * 2 * G * kRec;
-        stream_share_mfma<G, NT, F8 ? kFp8Depth : kMfmaDepth, F8, AP>(a, s_pref, s_tab, u0, u1, W, NG, wi, lane,
-                                                                      s_first);
+        stream_share_mfma<G, NT, F8 ? kFp8Depth : kMfmaDepth, F8, AP, E5>(a, s_pref, s_tab, u0, u1, W, NG, wi,
+                                                                          lane, s_first);
         return;
     }
 
@@ -1221,12 +1237,12 @@ size_t stream_lds_bytes(int64_t num_seqs, int waves, int G, bool mf) {
     return pref + (mf ? (size_t)waves * 2 * G * kRec * sizeof(float) : 0);
 }
 
-template <typename Chunk, typename Elem, int G, bool F8 = false, bool AP = false>
+template <typename Chunk, typename Elem, int G, bool F8 = false, bool AP = false, bool E5 = false>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     constexpr bool QL = kQueryInLds<G>;
     if (a.mode == kDecodeStream) {
         const size_t lds = stream_lds_bytes(a.num_seqs, a.waves_per_group, G, kMfmaWave<Elem, G>);
-        hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, kDecodeNT, F8, AP>), dim3((unsigned)a.num_wg),
+        hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, kDecodeNT, F8, AP, E5>), dim3((unsigned)a.num_wg),
                            dim3(64 * a.waves_per_group), lds, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1249,42 +1265,43 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <typename Chunk, typename Elem, bool F8 = false, bool AP = false>
+template <typename Chunk, typename Elem, bool F8 = false, bool AP = false, bool E5 = false>
 hipError_t launch_group(const DecodeArgs& a, int group, hipStream_t stream) {
     switch (group) {
-        case 1: return launch_typed<Chunk, Elem, 1, F8, AP>(a, stream);
-        case 2: return launch_typed<Chunk, Elem, 2, F8, AP>(a, stream);
-        case 4: return launch_typed<Chunk, Elem, 4, F8, AP>(a, stream);
-        case 8: return launch_typed<Chunk, Elem, 8, F8, AP>(a, stream);
+        case 1: return launch_typed<Chunk, Elem, 1, F8, AP, E5>(a, stream);
+        case 2: return launch_typed<Chunk, Elem, 2, F8, AP, E5>(a, stream);
+        case 4: return launch_typed<Chunk, Elem, 4, F8, AP, E5>(a, stream);
+        case 8: return launch_typed<Chunk, Elem, 8, F8, AP, E5>(a, stream);
         default: return hipErrorInvalidValue;
     }
 }
 
-template <typename Chunk, typename Elem, int G, bool F8, bool AP>
+template <typename Chunk, typename Elem, int G, bool F8, bool AP, bool E5>
 int stream_blocks_per_cu(int waves_per_group, int64_t num_seqs) {
     const size_t lds = stream_lds_bytes(num_seqs, waves_per_group, G, kMfmaWave<Elem, G>);
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, kDecodeNT, F8, AP>,
-                                                     64 * waves_per_group, lds) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, kDecodeNT, F8, AP, E5>, 64 * waves_per_group,
+            lds) != hipSuccess)
         return 0;
     return n;
 }
 
-template <typename Chunk, typename Elem, bool F8 = false, bool AP = false>
+template <typename Chunk, typename Elem, bool F8 = false, bool AP = false, bool E5 = false>
 int stream_blocks_group(int group, int waves_per_group, int64_t num_seqs) {
     switch (group) {
-        case 1: return stream_blocks_per_cu<Chunk, Elem, 1, F8, AP>(waves_per_group, num_seqs);
-        case 2: return stream_blocks_per_cu<Chunk, Elem, 2, F8, AP>(waves_per_group, num_seqs);
-        case 4: return stream_blocks_per_cu<Chunk, Elem, 4, F8, AP>(waves_per_group, num_seqs);
-        case 8: return stream_blocks_per_cu<Chunk, Elem, 8, F8, AP>(waves_per_group, num_seqs);
+        case 1: return stream_blocks_per_cu<Chunk, Elem, 1, F8, AP, E5>(waves_per_group, num_seqs);
+        case 2: return stream_blocks_per_cu<Chunk, Elem, 2, F8, AP, E5>(waves_per_group, num_seqs);
+        case 4: return stream_blocks_per_cu<Chunk, Elem, 4, F8, AP, E5>(waves_per_group, num_seqs);
+        case 8: return stream_blocks_per_cu<Chunk, Elem, 8, F8, AP, E5>(waves_per_group, num_seqs);
         default: return 0;
     }
 }
 
 }  // namespace
 
-// dtype: 0 fp32, 1 bf16, 2 fp8 (E4M3) cache with bf16 query and output, 3 bf16
-// in append mode.
+// dtype: 0 fp32, 1 bf16, 2 E4M3 cache with bf16 query and output, 3 bf16 in
+// append mode, 4 E5M2 cache with bf16 query and output.
 // The append form runs on the matrix-core wave only: a build that moves the
 // bf16 decode to the vector wave (PA_DECODE_MFMA_FROM > 1, for measurement)
 // leaves it out, and its launches fail.
@@ -1294,6 +1311,7 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t 
 #else
     if (dtype == 3) return hipErrorInvalidDeviceFunction;
 #endif
+    if (dtype == 4) return launch_group<ChunkBF16, uint16_t, true, false, true>(a, group, stream);
     if (dtype == 2) return launch_group<ChunkBF16, uint16_t, true>(a, group, stream);
     if (dtype == 1) return launch_group<ChunkBF16, uint16_t>(a, group, stream);
     return launch_group<ChunkF32, float>(a, group, stream);
@@ -1305,6 +1323,7 @@ int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int n
 #else
     if (dtype == 3) return stream_blocks_group<ChunkBF16, uint16_t>(group, waves_per_group, num_seqs);
 #endif
+    if (dtype == 4) return stream_blocks_group<ChunkBF16, uint16_t, true, false, true>(group, waves_per_group, num_seqs);
     if (dtype == 2) return stream_blocks_group<ChunkBF16, uint16_t, true>(group, waves_per_group, num_seqs);
     if (dtype == 1) return stream_blocks_group<ChunkBF16, uint16_t>(group, waves_per_group, num_seqs);
     return stream_blocks_group<ChunkF32, float>(group, waves_per_group, num_seqs);

@@ -18,19 +18,19 @@ hipError_t launch_copy_blocks(void* key_cache, void* value_cache, int64_t layer_
                               int64_t num_blocks, int64_t block_bytes, const int64_t* block_mapping,
                               int64_t num_pairs, hipStream_t stream);
 
-// fp8 (E4M3) scatter: K/V rows of `dtype` (0 fp32, 1 bf16) divided by their
-// scale, stored one byte per element.
-// pa_slot_mapping and the fp8 scatter in one launch (dtype of the source rows: 0 fp32, 1 bf16).
+// fp8 scatter: K/V rows of `dtype` (0 fp32, 1 bf16) divided by their scale,
+// stored one byte per element as E4M3 (fmt 0) or E5M2 (fmt 1) codes.
+// pa_slot_mapping and the fp8 scatter in one launch.
 hipError_t launch_slot_and_cache_fp8(int64_t* slot_mapping, const int32_t* block_table, int32_t max_blocks_per_req,
                                      int32_t num_seqs, const int32_t* token_seq, const int32_t* token_pos,
                                      const void* key, int64_t key_stride_bytes, const void* value,
                                      int64_t value_stride_bytes, void* key_cache, void* value_cache,
                                      int64_t num_tokens, int64_t num_slots, int32_t row_elems, int dtype,
-                                     float k_scale, float v_scale, hipStream_t stream);
+                                     int fmt, float k_scale, float v_scale, hipStream_t stream);
 hipError_t launch_reshape_and_cache_fp8(const void* key, int64_t key_stride_bytes, const void* value,
                                         int64_t value_stride_bytes, void* key_cache, void* value_cache,
                                         const int64_t* slot_mapping, int64_t num_tokens, int64_t num_slots,
-                                        int32_t row_elems, int dtype, float k_scale, float v_scale,
+                                        int32_t row_elems, int dtype, int fmt, float k_scale, float v_scale,
                                         hipStream_t stream);
 
 // RoPE + QKV split + scatter (rope_cache_kernel); sizes in elements.
@@ -144,8 +144,9 @@ struct PrefillArgs {
                                    // the first slot) << 24, first row, (tokens << 8) | KV head
 };
 
-// dtype: 0 = fp32, 1 = bf16, 2 = fp8 cache (bf16 query and output), 3 = bf16
-// in append mode.  group = num_heads / num_kv_heads in {1,2,4,8}.
+// dtype: 0 = fp32, 1 = bf16, 2 = E4M3 cache (bf16 query and output), 3 = bf16
+// in append mode, 4 = E5M2 cache (bf16 query and output).  group =
+// num_heads / num_kv_heads in {1,2,4,8}.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t stream);
 
 // Workgroups of the stream-mode decode kernel one compute unit holds at once.

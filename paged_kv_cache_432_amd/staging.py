@@ -53,15 +53,17 @@ class DeviceWorkload:
     """Device-resident inputs and paged cache of one workload step."""
 
     def __init__(self, w, device="cuda", fill_history: bool = True, poison: bool = True, kv_fp8: bool = False,
-                 guard_bytes: int = 0):
-        """kv_fp8: the caches hold E4M3 codes (uint8) written by the fp8 scatter
-        with the workload's fp8_scales(); queries and outputs stay bf16.
+                 guard_bytes: int = 0, fp8_format: str = "e4m3"):
+        """kv_fp8: the caches hold fp8 codes (uint8, fp8_format "e4m3" or
+        "e5m2") written by the fp8 scatter with the workload's fp8_scales();
+        queries and outputs stay bf16.
         guard_bytes > 0: each cache sits between guard zones (Guarded), checked
         by guards_intact()."""
         self.w = w
         self.device = torch.device(device)
         self.dtype = _TORCH_DTYPE[w.dtype]
         self.kv_fp8 = kv_fp8
+        self.fp8_format = fp8_format
         if kv_fp8:
             assert w.dtype == "bf16", "an fp8 cache goes with bf16 queries"
             self.k_scale, self.v_scale = w.fp8_scales()
@@ -122,7 +124,7 @@ class DeviceWorkload:
     def _scatter(self, k, v, slots, stream=None) -> None:
         if self.kv_fp8:
             pa_reshape_and_cache_fp8(k, v, self.key_cache, self.value_cache, slots, self.k_scale, self.v_scale,
-                                     stream=stream)
+                                     stream=stream, fp8_format=self.fp8_format)
         else:
             pa_reshape_and_cache(k, v, self.key_cache, self.value_cache, slots, stream=stream)
 
@@ -134,7 +136,7 @@ class DeviceWorkload:
         if fused and self.kv_fp8:
             pa_slot_mapping_and_cache_fp8(self.slot_mapping, self.block_table, self.new_seq, self.new_pos,
                                           self.new_k, self.new_v, self.key_cache, self.value_cache, self.k_scale,
-                                          self.v_scale, stream=stream)
+                                          self.v_scale, stream=stream, fp8_format=self.fp8_format)
             return
         if fused:
             pa_slot_mapping_and_cache(self.slot_mapping, self.block_table, self.new_seq, self.new_pos,
@@ -158,7 +160,7 @@ class DeviceWorkload:
             assert partition_tokens == 0, "an fp8 cache is read in the stream mode only"
             return pa_decode_fp8(out, self.query, self.key_cache, self.value_cache, self.block_table,
                                  self.seq_lens, w.scale, self.k_scale, self.v_scale, w.max_seq_len, workspace,
-                                 stream)
+                                 stream, fp8_format=self.fp8_format)
         return pa_decode(out, self.query, self.key_cache, self.value_cache, self.block_table,
                          self.seq_lens, w.scale, w.max_seq_len, partition_tokens, workspace, stream)
 

@@ -20,33 +20,41 @@ from parity import assert_parity, storage_bits, to_numpy
 _OUT = {}
 
 
-def _key(w, fp8: bool):
-    return (w.name, int(w.num_seqs), int(np.asarray(w.seq_lens, np.int64).sum()), bool(fp8))
+def _fmt(fp8):
+    """False (a bf16/fp32 cache), True (E4M3) or a format name -> None or the name."""
+    if fp8 is False or fp8 is None:
+        return None
+    return "e4m3" if fp8 is True else fp8
 
 
-def _attend(w, kc, vc, fp8: bool):
-    ks, vs = w.fp8_scales() if fp8 else (1.0, 1.0)
+def _key(w, fp8):
+    return (w.name, int(w.num_seqs), int(np.asarray(w.seq_lens, np.int64).sum()), _fmt(fp8))
+
+
+def _attend(w, kc, vc, fmt):
+    ks, vs = w.fp8_scales() if fmt else (1.0, 1.0)
     q = w.encode(w.queries())
     return oracle.attention(q, kc, vc, w.block_table, w.cu_query_lens, w.seq_lens, w.num_heads, w.scale,
-                            w.causal, k_scale=ks, v_scale=vs)
+                            w.causal, k_scale=ks, v_scale=vs, fp8_format=fmt or "e4m3")
 
 
-def oracle_cache(w, fp8: bool = False):
+def oracle_cache(w, fp8=False):
     """The oracle's caches after every token of the workload (history and this
-    step's) is scattered; the output over them is remembered for
-    oracle_output()."""
+    step's) is scattered (fp8: False, True for E4M3, or "e4m3" / "e5m2"); the
+    output over them is remembered for oracle_output()."""
+    fmt = _fmt(fp8)
     t0 = time.perf_counter()
-    kc, vc = oracle.build_cache_fp8(w, *w.fp8_scales(), "all") if fp8 else oracle.build_cache(w, "all")
+    kc, vc = oracle.build_cache_fp8(w, *w.fp8_scales(), "all", fmt) if fmt else oracle.build_cache(w, "all")
     t1 = time.perf_counter()
     key = _key(w, fp8)
     if key not in _OUT:
-        _OUT[key] = _attend(w, kc, vc, fp8)
-    print(f"  oracle {w.name}{' fp8' if fp8 else ''}: cache {t1 - t0:.1f}s, attention "
+        _OUT[key] = _attend(w, kc, vc, fmt)
+    print(f"  oracle {w.name}{' ' + fmt if fmt else ''}: cache {t1 - t0:.1f}s, attention "
           f"{time.perf_counter() - t1:.1f}s", flush=True)
     return kc, vc
 
 
-def oracle_output(w, fp8: bool = False) -> np.ndarray:
+def oracle_output(w, fp8=False) -> np.ndarray:
     """fp64 oracle output [num_q_tokens, Hq, D] of the whole workload."""
     key = _key(w, fp8)
     if key not in _OUT:

@@ -262,6 +262,24 @@ def test_fp8_entries_reject_before_launch(L):
     assert dec(msl=8193) == pa.PA_ERR_INVALID_ARG
 
 
+def test_fp8_format_is_checked(L):
+    """The _ex forms take the fp8 format: E4M3 (0) and E5M2 (1); anything else
+    is refused before any launch."""
+    sc = L.pa_reshape_and_cache_fp8_ex
+    assert sc(16, 1024, 16, 1024, 16, 16, 16, 5, 10, 16, 8, 128, 1, 2, 1.0, 1.0, None) == pa.PA_ERR_UNSUPPORTED
+    assert sc(16, 1024, 16, 1024, 16, 16, 16, 5, 10, 16, 8, 128, 1, -1, 1.0, 1.0, None) == pa.PA_ERR_UNSUPPORTED
+    assert sc(16, 1024, 16, 1024, 16, 16, 16, 0, 10, 16, 8, 128, 1, 1, 1.0, 1.0, None) == pa.PA_OK
+    fs = L.pa_slot_mapping_and_cache_fp8_ex
+    assert fs(16, 16, 4, 2, 16, 16, 16, 1024, 16, 1024, 16, 16, 3, 10, 16, 8, 128, 1, 7, 0.5, 0.5,
+              None) == pa.PA_ERR_UNSUPPORTED
+    dc = L.pa_decode_fp8_ex
+    args = [16, 16, 4096, 16, 16, 16, 512, 16, 4, 32, 8, 128, 16, 100, 0.088]
+    assert dc(*args, 5, 1.0, 1.0, 8192, None, 0, None) == pa.PA_ERR_UNSUPPORTED
+    assert dc(*args, 1, -1.0, 1.0, 8192, None, 0, None) == pa.PA_ERR_INVALID_ARG    # scales checked as for E4M3
+    with pytest.raises(ValueError):
+        pa._fp8_format("e3m4")
+
+
 def test_copy_blocks_rejects_before_launch(L):
     cb = L.pa_copy_blocks
     assert cb(16, 16, 0, 1, 10, 32768, 16, 0, None) == pa.PA_OK                 # no pairs
