@@ -1,0 +1,141 @@
+"""Parity at the edges of the sizes the library takes, on the GPU, against the
+oracle:
+  - a cache pool larger than 4 GiB with the sequences' blocks all past the
+    4 GiB mark, so every block address needs 64 bits (decode in both split
+    modes, the one-call step, chunked prefill, and an fp8 cache of more than
+    4 GiB of codes);
+  - exactly 4096 sequences, the most the balanced stream mode takes, next to
+    4097, which moves to fixed partitions;
+  - one sequence of 262,144 tokens (16,384 blocks) beside short ones.
+The oracle relabels each sequence's blocks into a compact pool of its own
+(the result does not depend on physical block ids), so it never holds the
+large pools."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import assert_parity, storage_bits, to_numpy
+
+pytestmark = pytest.mark.gpu
+GIB4 = 1 << 32
+
+
+@pytest.fixture(scope="module")
+def staging():
+    import paged_kv_cache_432_amd as pa
+    pa.lib()
+    from paged_kv_cache_432_amd import staging
+    return staging
+
+
+def _high_blocks(w, num_blocks, first_high, seed):
+    """w with its blocks dealt from [first_high, num_blocks) only."""
+    rng = np.random.default_rng(seed)
+    counts = W.blocks_needed(w.seq_lens)
+    ids = first_high + rng.permutation(num_blocks - first_high)
+    table = np.full(w.block_table.shape, -1, np.int32)
+    cur = 0
+    for b, c in enumerate(counts):
+        table[b, :c] = ids[cur:cur + c]
+        cur += c
+    return w.with_block_table(table, num_blocks=num_blocks)
+
+
+def _ref(w, fp8_format=None):
+    res = oracle.run_sequences(w, range(w.num_seqs), fp8_scales=w.fp8_scales() if fp8_format else None,
+                               fp8_format=fp8_format or "e4m3")
+    return np.concatenate([res[b] for b in range(w.num_seqs)], axis=0)
+
+
+def test_pool_beyond_4gib_bf16(staging):
+    """bf16, Llama-3-8B heads: 32 KiB blocks, a 150,000-block pool (4.9 GB per
+    cache), every used block id >= 131,072 (byte offset >= 4 GiB)."""
+    nb, first = 150_000, 131_072
+    assert first * 16 * 8 * 128 * 2 >= GIB4
+    w = _high_blocks(W.custom("high", seq_lens=[3000, 17, 8192, 1, 600], dtype="bf16", seed=90, sigma=0.5),
+                     nb, first, 91)
+    ref = _ref(w)
+    dw = staging.DeviceWorkload(w)
+    dw.scatter_new(fused=True)
+    for pt in (0, 512):
+        out = dw.decode(partition_tokens=pt)
+        torch.cuda.synchronize()
+        assert_parity(to_numpy(out), ref, "bf16", f"pool > 4 GiB, decode pt={pt}")
+    # the one-call step on a second copy: the newest rows land at their
+    # slots (past 4 GiB) bit for bit, and the output matches
+    da = staging.DeviceWorkload(w)
+    out = da.decode_append()
+    torch.cuda.synchronize()
+    k, v, slots = da.append_rows()
+    s = slots.cpu().numpy()
+    want = [oracle.slot(w.block_table[b], int(w.seq_lens[b]) - 1) for b in range(w.num_seqs)]
+    assert s.tolist() == want and min(want) * 8 * 128 * 2 >= GIB4
+    kc = da.key_cache.view(-1, w.num_kv_heads, w.head_dim)
+    vc = da.value_cache.view(-1, w.num_kv_heads, w.head_dim)
+    idx = torch.from_numpy(s).to(kc.device)
+    assert torch.equal(kc[idx].view(torch.int16), k.view(torch.int16))
+    assert torch.equal(vc[idx].view(torch.int16), v.view(torch.int16))
+    assert_parity(to_numpy(out), ref, "bf16", "pool > 4 GiB, pa_decode_append")
+
+
+def test_pool_beyond_4gib_chunked_prefill(staging):
+    nb, first = 150_000, 131_072
+    w = _high_blocks(W.custom("high_mix", seq_lens=[2500, 700, 90], query_lens=[300, 1, 64], dtype="bf16",
+                              seed=92, causal=True), nb, first, 93)
+    dw = staging.DeviceWorkload(w)
+    dw.scatter_new(fused=True)
+    out = dw.chunked_prefill()
+    torch.cuda.synchronize()
+    assert_parity(to_numpy(out), _ref(w), "bf16", "pool > 4 GiB, chunked prefill")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_pool_beyond_4gib_fp8(staging, fmt):
+    """fp8: 16 KiB blocks, a 300,000-block pool, every used block id >= 262,144."""
+    nb, first = 300_000, 262_144
+    assert first * 16 * 8 * 128 >= GIB4
+    w = _high_blocks(W.custom("high_fp8", seq_lens=[4100, 33, 9000], dtype="bf16", seed=94), nb, first, 95)
+    dw = staging.DeviceWorkload(w, kv_fp8=True, fp8_format=fmt)
+    dw.scatter_new(fused=True)
+    out = dw.decode()
+    torch.cuda.synchronize()
+    assert_parity(to_numpy(out), _ref(w, fmt), "bf16", f"pool > 4 GiB, {fmt} decode")
+
+
+def test_stream_mode_limit(staging):
+    """4096 sequences take the balanced stream mode and 4097 take fixed
+    partitions; both match the oracle."""
+    import paged_kv_cache_432_amd as pa
+    rng = np.random.default_rng(96)
+    lens = rng.integers(1, 60, 4097).astype(np.int32)
+    lens[::101] = 0
+    for n in (4096, 4097):
+        w = W.custom("limit", seq_lens=lens[:n], num_heads=8, num_kv_heads=8, dtype="bf16", seed=96 + n)
+        pt = pa.pa_decode_partition_tokens(n, 8, w.max_seq_len, 0)
+        assert (pt == 0) == (n == 4096)
+        dw = staging.DeviceWorkload(w)
+        dw.scatter_new()
+        out = dw.decode()
+        torch.cuda.synchronize()
+        assert_parity(to_numpy(out), oracle.run(w), "bf16", f"{n} sequences (partition tokens {pt})")
+
+
+def test_quarter_million_token_sequence(staging):
+    """One sequence of 262,144 tokens (1 GiB of bf16 K/V over 16,384 blocks)
+    next to short ones: the stream mode cuts it over many workgroups, the
+    partition mode into 64 partitions of 4096; the one-call step too."""
+    w = W.custom("long1", seq_lens=[262_144, 5, 1000], dtype="bf16", seed=97, sigma=0.5)
+    ref = _ref(w)
+    dw = staging.DeviceWorkload(w)
+    dw.scatter_new()
+    for pt in (0, 4096):
+        out = dw.decode(partition_tokens=pt)
+        torch.cuda.synchronize()
+        assert_parity(to_numpy(out), ref, "bf16", f"262144 tokens, pt={pt}")
+    del dw
+    da = staging.DeviceWorkload(w)
+    out = da.decode_append()
+    torch.cuda.synchronize()
+    assert_parity(to_numpy(out), ref, "bf16", "262144 tokens, pa_decode_append")
