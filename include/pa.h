@@ -567,6 +567,39 @@ pa_status pa_chunked_prefill(void *out, const void *query, int64_t q_token_strid
                              pa_dtype dtype, hipStream_t stream);
 
 /*
+ * Checks of the device-array contract (see the conventions at the top), on
+ * HOST copies of the arrays: the launch path cannot check array contents
+ * without a host synchronisation, so a harness or a debugging caller runs
+ * these.  Each returns PA_OK, or PA_ERR_INVALID_ARG with the first offending
+ * entry named in pa_last_error_message().
+ *
+ * pa_validate_block_tables: 0 <= seq_lens[b] <= max_seq_len <=
+ *   max_blocks_per_req * block_size, and block_table[b][i] in [0, num_blocks)
+ *   for every block a sequence uses (i < ceil(seq_lens[b] / block_size)).
+ *   Several tables may name the same block (shared prefixes).
+ * pa_validate_slot_mapping: no two tokens write the same slot (slots < 0 or
+ *   past the pool are skipped by the scatters and ignored here).
+ * pa_validate_query_lens: cu_query_lens[0] = 0, non-decreasing, ending at
+ *   num_q_tokens; each request's rows at most max_query_len and at most its
+ *   seq_lens.
+ *
+ * With PA_DEBUG=1 in the environment, pa_decode, pa_decode_append (and its
+ * allocation-free form), pa_decode_fp8(_ex), pa_chunked_prefill,
+ * pa_reshape_and_cache and pa_reshape_and_cache_fp8(_ex) copy their arrays to
+ * the host (synchronising `stream`), run these checks and return their status
+ * before launching anything.  pa_decode_append checks the blocks of each
+ * sequence's tokens before its newest one (the newest token may have no block;
+ * then it is not written).  Skipped while `stream` records a graph.
+ */
+pa_status pa_validate_block_tables(const int32_t *block_table, int32_t max_blocks_per_req,
+                                   const int32_t *seq_lens, int32_t num_seqs, int64_t num_blocks,
+                                   int32_t block_size, int32_t max_seq_len);
+pa_status pa_validate_slot_mapping(const int64_t *slot_mapping, int64_t num_tokens,
+                                   int64_t num_blocks, int32_t block_size);
+pa_status pa_validate_query_lens(const int32_t *cu_query_lens, const int32_t *seq_lens,
+                                 int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len);
+
+/*
  * Memory probes.  They are not part of the attention path: they give its
  * HBM-bound roofline a measured denominator on the same GPU (decode reads the
  * whole KV cache and is bound by memory, per the article's section "Attention

@@ -22,6 +22,7 @@ __all__ = [
     "pa_decode_fp8", "pa_copy_blocks", "KvManager", "pa_decode_workspace_bytes",
     "pa_decode_partition_tokens", "pa_decode", "pa_decode_append", "pa_decode_append_noalloc", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
     "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
+    "pa_validate_block_tables", "pa_validate_slot_mapping", "pa_validate_query_lens",
 ]
 
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_WORKSPACE, PA_ERR_HIP = range(5)
@@ -154,6 +155,12 @@ def lib():
         L.pa_chunked_prefill.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32,
                                          _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _vp,
                                          ctypes.c_size_t, ctypes.c_int, _vp]
+        L.pa_validate_block_tables.restype = ctypes.c_int
+        L.pa_validate_block_tables.argtypes = [_vp, _i32, _vp, _i32, _i64, _i32, _i32]
+        L.pa_validate_slot_mapping.restype = ctypes.c_int
+        L.pa_validate_slot_mapping.argtypes = [_vp, _i64, _i64, _i32]
+        L.pa_validate_query_lens.restype = ctypes.c_int
+        L.pa_validate_query_lens.argtypes = [_vp, _vp, _i32, _i64, _i32]
         L.pa_probe_stream_read.restype = ctypes.c_int
         L.pa_probe_stream_read.argtypes = [_vp, _i64, _vp, _i32, _vp]
         L.pa_probe_copy.restype = ctypes.c_int
@@ -651,6 +658,41 @@ def pa_chunked_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.
                                  _dtype_code(query), _stream(stream, out.device))
     _check(s, "pa_chunked_prefill")
     return out
+
+
+# ------------------------------------------------- contract checks (host) --
+def _host(a, dtype):
+    if isinstance(a, torch.Tensor):
+        a = a.detach().cpu().numpy()
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def pa_validate_block_tables(block_table, seq_lens, num_blocks: int, max_seq_len: int,
+                             block_size: int = BLOCK_SIZE) -> None:
+    """Check host copies of block_table [num_seqs, max_blocks_per_req] and
+    seq_lens against the device-array contract; raises PaError naming the first
+    offending entry."""
+    bt = _host(block_table, np.int32)
+    sl = _host(seq_lens, np.int32)
+    _need(bt.ndim == 2 and bt.shape[0] >= sl.shape[0], "block_table: [num_seqs, max_blocks_per_req]")
+    _check(lib().pa_validate_block_tables(bt.ctypes.data, bt.shape[1], sl.ctypes.data, sl.shape[0], int(num_blocks),
+                                          int(block_size), int(max_seq_len)), "pa_validate_block_tables")
+
+
+def pa_validate_slot_mapping(slot_mapping, num_blocks: int, block_size: int = BLOCK_SIZE) -> None:
+    """No two tokens of one scatter write the same slot (host copy)."""
+    sm = _host(slot_mapping, np.int64)
+    _check(lib().pa_validate_slot_mapping(sm.ctypes.data, sm.shape[0], int(num_blocks), int(block_size)),
+           "pa_validate_slot_mapping")
+
+
+def pa_validate_query_lens(cu_query_lens, seq_lens, num_q_tokens: int, max_query_len: int) -> None:
+    """cu_query_lens [num_seqs + 1] against seq_lens and the host bounds (host copies)."""
+    cu = _host(cu_query_lens, np.int32)
+    sl = _host(seq_lens, np.int32)
+    _need(cu.shape[0] == sl.shape[0] + 1, "cu_query_lens: [num_seqs + 1]")
+    _check(lib().pa_validate_query_lens(cu.ctypes.data, sl.ctypes.data, sl.shape[0], int(num_q_tokens),
+                                        int(max_query_len)), "pa_validate_query_lens")
 
 
 # ------------------------------------------------------------------ probes --

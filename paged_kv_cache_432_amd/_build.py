@@ -12,7 +12,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libpa.so")
 
 SOURCES = ["abi.cpp", "kv_manager.cpp", "cache_kernels.hip", "decode_kernel.hip", "prefill_kernel.hip",
-           "probe_kernels.hip", "noalloc.hip"]
+           "probe_kernels.hip", "noalloc.hip", "validate.cpp"]
 
 # Packed fp32 VALU ops are disabled for all device code: scalar and float2 code
 # is compiled to plain v_fma/v_mul/v_add.

@@ -12,6 +12,7 @@
 
 #include "host_status.h"
 #include "launch.h"
+#include "validate.h"
 
 namespace {
 
@@ -302,6 +303,10 @@ pa_status pa_reshape_and_cache(const void* key, int64_t key_token_stride, const 
         (key_token_stride * eb) % 16 || (value_token_stride * eb) % 16)
         return fail(PA_ERR_INVALID_ARG, "rows must start on 16-byte boundaries");
     if (num_tokens > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "num_tokens too large");
+    if (pa::debug_checks_enabled(stream)) {
+        const pa_status dc = pa::debug_check_slots(slot_mapping, num_tokens, num_blocks, stream);
+        if (dc != PA_OK) return dc;
+    }
     return hip_status(pa::launch_reshape_and_cache(key, key_token_stride * eb, value,
                                                    value_token_stride * eb, key_cache, value_cache,
                                                    slot_mapping, num_tokens, num_blocks * 16,
@@ -350,6 +355,10 @@ pa_status pa_reshape_and_cache_fp8_ex(const void* key, int64_t key_token_stride,
         (key_token_stride * eb) % 16 || (value_token_stride * eb) % 16)
         return fail(PA_ERR_INVALID_ARG, "rows must start on 16-byte boundaries");
     if (num_tokens > 0x7fffffff) return fail(PA_ERR_INVALID_ARG, "num_tokens too large");
+    if (pa::debug_checks_enabled(stream)) {
+        const pa_status dc = pa::debug_check_slots(slot_mapping, num_tokens, num_blocks, stream);
+        if (dc != PA_OK) return dc;
+    }
     return hip_status(pa::launch_reshape_and_cache_fp8(key, key_token_stride * eb, value, value_token_stride * eb,
                                                        key_cache, value_cache, slot_mapping, num_tokens,
                                                        num_blocks * 16, (int32_t)row_elems,
@@ -645,6 +654,11 @@ pa_status pa_decode_fp8_ex(void* out, const void* query, int64_t q_token_stride,
     if (!aligned16(query) || (q_token_stride * 2) % 16 || !aligned16(out) || !aligned16(key_cache) ||
         !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
+    if (pa::debug_checks_enabled(stream)) {
+        const pa_status dc = pa::debug_check_tables(block_table, max_blocks_per_req, seq_lens, num_seqs, num_blocks,
+                                                    max_seq_len, stream);
+        if (dc != PA_OK) return dc;
+    }
     return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
                          seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len, 0,
                          workspace, workspace_bytes, format == PA_FP8_E5M2 ? 4 : 2, k_scale, v_scale, stream);
@@ -688,6 +702,11 @@ pa_status pa_decode(void* out, const void* query, int64_t q_token_stride, const 
     if (!aligned16(query) || (q_token_stride * eb) % 16 || !aligned16(out) || !aligned16(key_cache) ||
         !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
+    if (pa::debug_checks_enabled(stream)) {
+        const pa_status dc = pa::debug_check_tables(block_table, max_blocks_per_req, seq_lens, num_seqs, num_blocks,
+                                                    max_seq_len, stream);
+        if (dc != PA_OK) return dc;
+    }
     return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
                          seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len,
                          partition_tokens, workspace, workspace_bytes, dtype == PA_BF16 ? 1 : 0, 1.f, 1.f, stream);
@@ -723,6 +742,11 @@ pa_status pa_decode_append(void* out, const void* query, int64_t q_token_stride,
         !aligned16(value_cache) || !aligned16(key) || !aligned16(value) || (key_token_stride * eb) % 16 ||
         (value_token_stride * eb) % 16)
         return fail(PA_ERR_INVALID_ARG, "query/out/key/value/cache rows must start on 16-byte boundaries");
+    if (pa::debug_checks_enabled(stream)) {
+        const pa_status dc = pa::debug_check_tables(block_table, max_blocks_per_req, seq_lens, num_seqs, num_blocks,
+                                                    max_seq_len, stream, true);
+        if (dc != PA_OK) return dc;
+    }
     if (dtype == PA_BF16 && use_stream(num_seqs, 0))
         return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
                              seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len, 0,
@@ -787,6 +811,14 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
     if (!aligned16(query) || (q_token_stride * 2) % 16 || !aligned16(out) || !aligned16(key_cache) ||
         !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
+
+    if (pa::debug_checks_enabled(stream)) {
+        pa_status dc = pa::debug_check_query_lens(cu_query_lens, seq_lens, num_seqs, num_q_tokens, max_query_len, stream);
+        if (dc == PA_OK)
+            dc = pa::debug_check_tables(block_table, max_blocks_per_req, seq_lens, num_seqs, num_blocks, max_seq_len,
+                                        stream);
+        if (dc != PA_OK) return dc;
+    }
 
     // workspace: the decode part's, then the prefill partial records and merge list
     const size_t dec_bytes =

@@ -1,0 +1,98 @@
+"""PA_DEBUG=1 on the GPU: with the variable set, each entry point copies its
+tables to the host and checks them before launching anything.  A valid step
+still matches the oracle; a bad block id, a bad query offset or two tokens on
+one slot come back as PA_ERR_INVALID_ARG naming the entry, with the output and
+the caches untouched (no kernel ran).  Every bad case is caught on the host:
+none of them reaches a kernel."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from parity import assert_parity, to_numpy
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture()
+def debug(monkeypatch):
+    import paged_kv_cache_432_amd as pa
+    pa.lib()
+    monkeypatch.setenv("PA_DEBUG", "1")
+    import ctypes
+    libc = ctypes.CDLL(None)
+    libc.getenv.restype = ctypes.c_char_p
+    # the library reads the C environment: the bad tables below must never
+    # reach a kernel, so stop here if the setting is not visible to it
+    assert libc.getenv(b"PA_DEBUG") == b"1"
+    from paged_kv_cache_432_amd import staging
+    return pa, staging
+
+
+def _rejects(pa, fn, match):
+    with pytest.raises(pa.PaError) as e:
+        fn()
+    assert e.value.status == pa.PA_ERR_INVALID_ARG and match in str(e.value), str(e.value)
+
+
+def _bytes(t):
+    return t.view(torch.uint8).cpu().clone() if t.dtype != torch.uint8 else t.cpu().clone()
+
+
+def test_valid_step_passes(debug):
+    pa, staging = debug
+    w = W.tiny("B")
+    dw = staging.DeviceWorkload(w)
+    dw.scatter_new()
+    out = dw.decode()
+    torch.cuda.synchronize()
+    assert_parity(to_numpy(out), oracle.run(w), w.dtype, "PA_DEBUG=1 decode")
+    da = staging.DeviceWorkload(w)
+    out = da.decode_append()
+    torch.cuda.synchronize()
+    assert_parity(to_numpy(out), oracle.run(w), w.dtype, "PA_DEBUG=1 pa_decode_append")
+
+
+def test_bad_block_id_is_caught(debug):
+    pa, staging = debug
+    w = W.custom("dbg", seq_lens=[40, 17, 300], dtype="bf16", seed=5)
+    dw = staging.DeviceWorkload(w)
+    dw.scatter_new()
+    dw.block_table[2, 7] = w.num_blocks                 # a block sequence 2 reads, outside the pool
+    out = torch.full_like(dw.query, 3.0)
+    _rejects(pa, lambda: dw.decode(out=out), "block_table[2][7]")
+    kc = _bytes(dw.key_cache)
+    _rejects(pa, lambda: dw.decode_append(out=out), "block_table[2][7]")
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()) and torch.equal(_bytes(dw.key_cache), kc)
+
+
+def test_bad_query_offsets_are_caught(debug):
+    pa, staging = debug
+    w = W.custom("dbg_mix", seq_lens=[200, 50, 9], query_lens=[64, 1, 9], dtype="bf16", seed=6, causal=True)
+    dw = staging.DeviceWorkload(w)
+    dw.scatter_new()
+    out = dw.chunked_prefill()
+    torch.cuda.synchronize()
+    assert_parity(to_numpy(out), oracle.run(w), w.dtype, "PA_DEBUG=1 chunked prefill")
+    dw.cu_query_lens[2] = 60                            # offsets go down
+    out.fill_(3.0)
+    _rejects(pa, lambda: dw.chunked_prefill(out=out), "decreases")
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all())
+
+
+def test_duplicate_slots_are_caught(debug):
+    pa, staging = debug
+    w = W.tiny("B")
+    dw = staging.DeviceWorkload(w)
+    n = int(dw.new_k.shape[0])
+    assert n >= 2
+    slots = torch.arange(n, dtype=torch.int64, device=dw.key_cache.device) * 3
+    slots[-1] = slots[0]
+    kc = _bytes(dw.key_cache)
+    _rejects(pa, lambda: pa.pa_reshape_and_cache(dw.new_k, dw.new_v, dw.key_cache, dw.value_cache, slots),
+             f"slot_mapping[{n - 1}]")
+    torch.cuda.synchronize()
+    assert torch.equal(_bytes(dw.key_cache), kc)

@@ -5,7 +5,8 @@ subprocess with the matching sanitizer runtime preloaded:
   - libpa.so with its host code instrumented (hipcc, -fsanitize=address and
     undefined for the host compilation only; device code as usual): the block
     manager's random runs and rule tests (test_kv_manager.py) and the C ABI's
-    argument checks (test_abi.py), which return before any launch;
+    argument checks (test_abi.py), which return before any launch, and the
+    contract checks on host copies (test_validate.py);
   - the C oracle (gcc): its pins (test_oracle.py, test_oracle_rope.py,
     test_oracle_fp8.py) and the input draws (test_workloads.py).
 Any sanitizer report ends the subprocess with an error and fails the test.
@@ -46,7 +47,7 @@ def outdir():
 def test_library_host_code_under_asan_ubsan(outdir):
     from paged_kv_cache_432_amd import _build
     lib = _build.build(out=os.path.join(outdir, "libpa.so"), sanitize=True)
-    out = _run({"LD_PRELOAD": _build.asan_runtime(), "PA_LIB": lib}, ["test_kv_manager.py", "test_abi.py"],
+    out = _run({"LD_PRELOAD": _build.asan_runtime(), "PA_LIB": lib}, ["test_kv_manager.py", "test_abi.py", "test_validate.py"],
                os.path.join(outdir, "asan_lib"))
     assert " passed" in out
 
