@@ -78,10 +78,17 @@ constexpr int kThreads = kWaves * kWave;
 // so every thread stages kBlkPerThr of the tile's 4 blocks.
 constexpr int kThrGroups = kThreads / 256;
 constexpr int kBlkPerThr = 4 / kThrGroups;
-// Sets of staging registers: with two, a tile's loads are issued two tiles
-// before its commit; with one (the 4-wave workgroup, whose threads stage twice
-// the blocks), one tile before.
-constexpr int kStageSets = kThrGroups == 2 ? 2 : 1;
+// Sets of staging registers.  With one (the default), a tile's loads are issued
+// as the tile before it starts and committed at its end, a whole tile of
+// compute later.  With two (8-wave workgroups only, a build parameter kept for
+// measurement), they are issued two tiles before their commit; that costs 18
+// more VGPRs and measured no faster once every wait covers only the loads it
+// needs.
+#ifndef PA_PREFILL_STAGE_SETS
+#define PA_PREFILL_STAGE_SETS 1
+#endif
+constexpr int kStageSets = kThrGroups == 2 ? PA_PREFILL_STAGE_SETS : 1;
+static_assert(kStageSets == 1 || kStageSets == 2, "staging sets");
 // Merge workgroups per listed tile: 8 rows each, one per 32-thread group, so
 // that each thread merges one row (the merge is bound by reading the records).
 constexpr int kMergeRows = 8;
@@ -301,8 +308,13 @@ prefill_kernel(PrefillArgs a) {
                                  (int64_t)(q0 + tok_begin + (active ? tq : 0)) * a.q_stride +
                                  (int64_t)(kvh * G + r % G) * kHeadDim + 8 * h;
 #pragma unroll
+            for (int ks = 0; ks < 8; ++ks) qop[ks] = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+            // loaded unconditionally (an inactive row reads the tile's first row,
+            // then zeroes it): a load under a branch leaves the wait counts
+            // unknown, and the loop would then wait on every load in flight
+#pragma unroll
             for (int ks = 0; ks < 8; ++ks)
-                qop[ks] = active ? *reinterpret_cast<const u32x4_t*>(qp + 16 * ks) : u32x4_t{0u, 0u, 0u, 0u};
+                if (!active) qop[ks] = u32x4_t{0u, 0u, 0u, 0u};
         }
         // wave-wide key limit: tiles ending past kmin need the mask.  (A tile
         // wholly past the wave's rows is still computed, its scores all masked:
@@ -340,27 +352,31 @@ prefill_kernel(PrefillArgs a) {
         // before its commit, the set chosen at compile time (see run)
         u32x4_t kreg[kStageSets][kBlkPerThr];
         uint32_t vw[kStageSets][kBlkPerThr][4];
-        // Block ids of the key range, 64 at a time (one per lane), broadcast with
-        // v_readlane, so that the tile's 10 loads issue back to back instead of
-        // each waiting on its own table read.
+        // Block ids, per staging set: bid[S] holds (lanes 0-3) the ids of the
+        // next tile staged into set S, loaded when the set's previous tile was
+        // staged, and broadcast with v_readlane, so that a tile's 10 loads issue
+        // back to back.  Every load of the loop (ids and K/V) is issued
+        // unconditionally -- tiles past the segment read through empty buffer
+        // resources, which return zeros without touching memory -- so that the
+        // number of loads issued after any one of them is the same on every
+        // path, and each wait covers exactly the loads it needs.
         const int nblk_wg = (kend_wg + kBlock - 1) / kBlock;
-        int bid_base = -kWave;                             // first block held in bid
-        int bid = 0;
-        auto block_of = [&](int blk) -> int64_t {          // blk in [bid_base, bid_base + 64)
-            const int64_t id = __builtin_amdgcn_readlane(bid, blk - bid_base);
-            return min(max(id, (int64_t)0), a.num_blocks - 1);
+        const rsrc_t rbt = __builtin_amdgcn_make_buffer_rsrc((void*)bt, (short)0, nblk_wg * 4, kRsrcWord3);
+        int bid[kStageSets];
+        auto load_ids = [&](int kt, auto set) {
+            constexpr int S = decltype(set)::value;
+            bid[S] = __builtin_amdgcn_raw_buffer_load_b32(rbt, (4 * kt + (lane & 3)) * 4, 0, 0);
         };
         auto stage = [&](int kt, auto set) {
             constexpr int S = decltype(set)::value;
-            if (4 * kt + 3 >= bid_base + kWave) {          // wave-uniform: the tile's ids are not all held
-                bid_base = 4 * kt;
-                bid = bid_base + lane < nblk_wg ? bt[bid_base + lane] : 0;
-            }
+            const bool live = kt < kt_end;                 // wave-uniform
 #pragma unroll
             for (int j = 0; j < kBlkPerThr; ++j) {
                 const int blk = 4 * kt + w4 + kThrGroups * j;
-                const int64_t off = block_of(blk) * blk_bytes;
-                const int nrec = __builtin_amdgcn_readfirstlane(min(max(kend_wg - blk * kBlock, 0), kBlock) * (int)tok_bytes);
+                const int64_t id = __builtin_amdgcn_readlane(bid[S], w4 + kThrGroups * j);
+                const int64_t off = min(max(id, (int64_t)0), a.num_blocks - 1) * blk_bytes;
+                const int nrec = __builtin_amdgcn_readfirstlane(
+                    live ? min(max(kend_wg - blk * kBlock, 0), kBlock) * (int)tok_bytes : 0);
                 const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
                 const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
                 kreg[S][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff, 0, 0));
@@ -423,15 +439,22 @@ prefill_kernel(PrefillArgs a) {
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
-            bid_base = -kWave;
             using Set0 = std::integral_constant<int, 0>;
             using Set1 = std::integral_constant<int, 1>;
-            if (kt_begin < kt_end) {
+            if constexpr (kStageSets == 2) {
+                load_ids(kt_begin, Set0{});
+                load_ids(kt_begin + 1, Set1{});
                 stage(kt_begin, Set0{});
+                load_ids(kt_begin + 2, Set0{});
+                commit(0, half, Set0{});
+                stage(kt_begin + 1, Set1{});
+                load_ids(kt_begin + 3, Set1{});
+            } else {
+                load_ids(kt_begin, Set0{});
+                stage(kt_begin, Set0{});
+                load_ids(kt_begin + 1, Set0{});
                 commit(0, half, Set0{});
             }
-            if constexpr (kStageSets == 2)
-                if (kt_begin + 1 < kt_end) stage(kt_begin + 1, Set1{});
             __syncthreads();
 
             // One key tile.  Tile kt + 1 is already in staging set `held`; tile kt + 2
@@ -442,9 +465,11 @@ prefill_kernel(PrefillArgs a) {
                 using Other = std::integral_constant<int, 1 - A>;
                 const int buf = (kt - kt_begin) & 1;
                 if constexpr (kStageSets == 2) {
-                    if (kt + 2 < kt_end) stage(kt + 2, Other{});
+                    stage(kt + 2, Other{});
+                    load_ids(kt + 4, Other{});
                 } else {
-                    if (kt + 1 < kt_end) stage(kt + 1, Set0{});
+                    stage(kt + 1, Set0{});
+                    load_ids(kt + 2, Set0{});
                 }
                 const int key0 = kt * kKeys;
                 // S^T = K Q^T over this tile: 2 key tiles of 32 x 8 dim steps of 16.
