@@ -88,15 +88,16 @@ __device__ __forceinline__ void buffer_chunk(ChunkF32& c, rsrc_t r, uint32_t off
 // them per lane (16 copies of each, one per token lane) and leave one wave per
 // SIMD.  At G = 4 they stay in registers: LDS reads on every block cost more
 // than the third wave per SIMD they would free (measured on the Llama-3-8B
-// decode shapes).
-template <int G>
-constexpr bool kQueryInLds = G >= PA_DECODE_QUERY_IN_LDS_FROM;
+// decode shapes).  fp32 rows, twice the registers, move to LDS from G = 4.
+template <typename Elem, int G>
+constexpr bool kQueryInLds = G >= (sizeof(Elem) == 4 ? 4 : PA_DECODE_QUERY_IN_LDS_FROM);
 
 // Blocks each wave keeps in flight.  Three also fit two waves per SIMD (252
 // VGPRs at G = 4) but measured the same as two on the Llama-3-8B and G = 8
-// decode shapes, so two it is (239 VGPRs).
-template <int G>
-constexpr int kPipelineDepth = PA_DECODE_PIPELINE_DEPTH;
+// decode shapes, so two it is (239 VGPRs).  An fp32 block holds twice the
+// registers: at G = 8 two of them spill, so those waves keep one.
+template <typename Elem, int G>
+constexpr int kPipelineDepth = sizeof(Elem) == 4 && G >= 8 ? 1 : PA_DECODE_PIPELINE_DEPTH;
 
 // Per-wave state of one (sequence, KV head) range: the G query rows (in
 // registers, in the K layout, or -- QL -- in the wave's LDS slot, read back
@@ -940,7 +941,7 @@ decode_partition_kernel(DecodeArgs a) {
         WaveState<Chunk, Elem, G, QL> st;
         st.qs = q_lds[QL ? wave : 0];
         load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
-        attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, bt, nblk, tok_begin, L, p_lds[wave], lane, st);
+        attend<Chunk, Elem, G, QL, NT, kPipelineDepth<Elem, G>>(a, kvh, bt, nblk, tok_begin, L, p_lds[wave], lane, st);
         if (nparts == 1) finish<Chunk, Elem, G, QL>(st, lane, reinterpret_cast<Elem*>(a.out) + h0 * kHeadDim, nullptr);
         else finish<Chunk, Elem, G, QL>(st, lane, nullptr, a.part + r0 * kRec);
     }
@@ -1055,7 +1056,7 @@ decode_stream_kernel(DecodeArgs a) {
         WaveState<Chunk, Elem, G, QL> st;
         st.qs = q_lds[QL ? wi : 0];
         load_query<Chunk, Elem, G, QL>(a, row, kvh, lane, st);
-        attend<Chunk, Elem, G, QL, NT, kPipelineDepth<G>>(a, kvh, bt, n, blk0 * kBlock, L, pl, lane, st);
+        attend<Chunk, Elem, G, QL, NT, kPipelineDepth<Elem, G>>(a, kvh, bt, n, blk0 * kBlock, L, pl, lane, st);
         finish<Chunk, Elem, G, QL>(st, lane, whole ? out : nullptr, whole ? nullptr : rec);
         u += n;
     }
@@ -1239,7 +1240,7 @@ size_t stream_lds_bytes(int64_t num_seqs, int waves, int G, bool mf) {
 
 template <typename Chunk, typename Elem, int G, bool F8 = false, bool AP = false, bool E5 = false>
 hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
-    constexpr bool QL = kQueryInLds<G>;
+    constexpr bool QL = kQueryInLds<Elem, G>;
     if (a.mode == kDecodeStream) {
         const size_t lds = stream_lds_bytes(a.num_seqs, a.waves_per_group, G, kMfmaWave<Elem, G>);
         hipLaunchKernelGGL((decode_stream_kernel<Chunk, Elem, G, QL, kDecodeNT, F8, AP, E5>), dim3((unsigned)a.num_wg),
@@ -1281,7 +1282,7 @@ int stream_blocks_per_cu(int waves_per_group, int64_t num_seqs) {
     const size_t lds = stream_lds_bytes(num_seqs, waves_per_group, G, kMfmaWave<Elem, G>);
     int n = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<G>, kDecodeNT, F8, AP, E5>, 64 * waves_per_group,
+            &n, decode_stream_kernel<Chunk, Elem, G, kQueryInLds<Elem, G>, kDecodeNT, F8, AP, E5>, 64 * waves_per_group,
             lds) != hipSuccess)
         return 0;
     return n;
