@@ -536,10 +536,14 @@ pa_status pa_decode_append_noalloc(void *out, const void *query, int64_t q_token
  * probabilities carried as a bf16 hi/lo pair), their (query tile, key tile)
  * work shared evenly by the resident workgroups and tiles cut by a share
  * boundary merged with log-sum-exp weights; q_b == 0 requests produce
- * nothing.
+ * nothing.  Over an fp32 cache every query row runs as a decode row of its
+ * own: a first kernel writes, into the workspace, each row's key count under
+ * the mask (L_b - q_b + j + 1, or L_b) and a copy of its request's
+ * block-table row, and the fp32 decode (as pa_decode) reads them, each row
+ * re-reading its keys (a path for accuracy, not for speed).
  *
- * out          [num_q_tokens, num_heads, head_dim] bf16, contiguous
- * query        [num_q_tokens, num_heads, head_dim] bf16; rows q_token_stride
+ * out          [num_q_tokens, num_heads, head_dim] of dtype, contiguous
+ * query        [num_q_tokens, num_heads, head_dim] of dtype; rows q_token_stride
  *              ELEMENTS apart (heads/dims contiguous, rows 16-byte aligned)
  * key_cache, value_cache, block_table, block_size, num_blocks: as pa_decode
  * cu_query_lens int32 [num_seqs + 1], cu_query_lens[0] == 0,
@@ -548,14 +552,20 @@ pa_status pa_decode_append_noalloc(void *out, const void *query, int64_t q_token
  *              step's rows included (seq_lens[b] >= q_b)
  * max_query_len, max_seq_len: host-side upper bounds of q_b and seq_lens
  * causal       1 (the chunked-prefill case) or 0
- * workspace    >= pa_chunked_prefill_workspace_bytes(...) bytes of device
- *              scratch (no initialisation needed; 16-byte aligned); required
- *              even when no request is split
- * dtype        PA_BF16 only (PA_ERR_UNSUPPORTED otherwise)
+ * workspace    >= pa_chunked_prefill_workspace_bytes_ex(..., dtype) bytes of
+ *              device scratch (no initialisation needed; 16-byte aligned);
+ *              required even when no request is split
+ * dtype        PA_BF16 or PA_F32 (caches, query and out alike)
+ *
+ * pa_chunked_prefill_workspace_bytes is the PA_BF16 size; 0 for an invalid
+ * shape.
  */
 size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,
                                           int32_t max_seq_len, int32_t num_heads, int32_t num_kv_heads,
                                           int32_t head_dim);
+size_t pa_chunked_prefill_workspace_bytes_ex(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,
+                                             int32_t max_seq_len, int32_t num_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, pa_dtype dtype);
 pa_status pa_chunked_prefill(void *out, const void *query, int64_t q_token_stride,
                              const void *key_cache, const void *value_cache,
                              const int32_t *block_table, int32_t max_blocks_per_req,

@@ -151,6 +151,8 @@ def lib():
                                                ctypes.c_int, _vp]
         L.pa_chunked_prefill_workspace_bytes.restype = ctypes.c_size_t
         L.pa_chunked_prefill_workspace_bytes.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32]
+        L.pa_chunked_prefill_workspace_bytes_ex.restype = ctypes.c_size_t
+        L.pa_chunked_prefill_workspace_bytes_ex.argtypes = [_i32, _i64, _i32, _i32, _i32, _i32, _i32, ctypes.c_int]
         L.pa_chunked_prefill.restype = ctypes.c_int
         L.pa_chunked_prefill.argtypes = [_vp, _vp, _i64, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i64, _i32,
                                          _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _vp,
@@ -618,15 +620,19 @@ def pa_decode_append_noalloc(out: torch.Tensor, query: torch.Tensor, key: torch.
 
 
 def pa_chunked_prefill_workspace_bytes(num_seqs: int, num_q_tokens: int, max_query_len: int, max_seq_len: int,
-                                       num_heads: int, num_kv_heads: int, head_dim: int) -> int:
-    return int(lib().pa_chunked_prefill_workspace_bytes(num_seqs, num_q_tokens, max_query_len, max_seq_len,
-                                                        num_heads, num_kv_heads, head_dim))
+                                       num_heads: int, num_kv_heads: int, head_dim: int, dtype=None) -> int:
+    """Workspace bytes of pa_chunked_prefill; dtype None or torch.bfloat16 gives
+    the bf16 size, torch.float32 the fp32 route's."""
+    code = PA_BF16 if dtype is None else _dtype_code(torch.empty(0, dtype=dtype))
+    return int(lib().pa_chunked_prefill_workspace_bytes_ex(num_seqs, num_q_tokens, max_query_len, max_seq_len,
+                                                           num_heads, num_kv_heads, head_dim, code))
 
 
 def chunked_prefill_workspace(num_seqs: int, num_q_tokens: int, max_query_len: int, max_seq_len: int,
-                              num_heads: int, num_kv_heads: int, head_dim: int, device="cuda") -> torch.Tensor:
+                              num_heads: int, num_kv_heads: int, head_dim: int, device="cuda",
+                              dtype=None) -> torch.Tensor:
     nbytes = pa_chunked_prefill_workspace_bytes(num_seqs, num_q_tokens, max_query_len, max_seq_len, num_heads,
-                                                num_kv_heads, head_dim)
+                                                num_kv_heads, head_dim, dtype)
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
 
 
@@ -635,7 +641,7 @@ def pa_chunked_prefill(out: torch.Tensor, query: torch.Tensor, key_cache: torch.
                        seq_lens: torch.Tensor, scale: float, max_query_len: int, max_seq_len: int,
                        causal: bool = True, workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """Mixed-batch attention: out [num_q_tokens, Hq, D] for flattened query rows
-    [num_q_tokens, Hq, D] (bf16), requests delimited by cu_query_lens."""
+    [num_q_tokens, Hq, D] (bf16 or fp32), requests delimited by cu_query_lens."""
     _need(query.dim() == 3 and out.shape == query.shape and out.is_contiguous(),
           "query/out: [num_q_tokens, num_heads, head_dim], out contiguous")
     _need(query.stride(2) == 1 and query.stride(1) == query.shape[2], "query heads/dims must be contiguous")

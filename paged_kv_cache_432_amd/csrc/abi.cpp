@@ -622,6 +622,21 @@ pa_status check_heads(int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
     return PA_OK;
 }
 
+// Workspace of the fp32 mixed batch: one decode row per query row, its key
+// count and block-table row (stride: the blocks of max_seq_len), then the
+// decode's own workspace.
+struct F32Rows {
+    int32_t row_stride;
+    size_t table_off, table_bytes;
+};
+F32Rows f32_rows(int64_t rows, int32_t max_seq_len) {
+    F32Rows f;
+    f.row_stride = std::max((max_seq_len + 15) / 16, 1);
+    f.table_off = align256((size_t)rows * sizeof(int32_t));
+    f.table_bytes = align256((size_t)rows * (size_t)f.row_stride * sizeof(int32_t));
+    return f;
+}
+
 }  // namespace
 
 extern "C" {
@@ -774,8 +789,22 @@ pa_status pa_decode_append(void* out, const void* query, int64_t q_token_stride,
 size_t pa_chunked_prefill_workspace_bytes(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,
                                           int32_t max_seq_len, int32_t num_heads, int32_t num_kv_heads,
                                           int32_t head_dim) {
+    return pa_chunked_prefill_workspace_bytes_ex(num_seqs, num_q_tokens, max_query_len, max_seq_len, num_heads,
+                                                 num_kv_heads, head_dim, PA_BF16);
+}
+
+size_t pa_chunked_prefill_workspace_bytes_ex(int32_t num_seqs, int64_t num_q_tokens, int32_t max_query_len,
+                                             int32_t max_seq_len, int32_t num_heads, int32_t num_kv_heads,
+                                             int32_t head_dim, pa_dtype dtype) {
     if (num_seqs <= 0 || num_q_tokens <= 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads)
         return 0;
+    if (dtype == PA_F32) {
+        if (num_q_tokens > 0x7fffffff || max_seq_len < 0) return 0;
+        const F32Rows fr = f32_rows(num_q_tokens, max_seq_len);
+        return fr.table_off + fr.table_bytes +
+               align256(pa_decode_workspace_bytes((int32_t)num_q_tokens, num_heads, num_kv_heads, head_dim,
+                                                  max_seq_len, 0));
+    }
     const size_t dec = align256(pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads, head_dim, max_seq_len, 0));
     if (max_query_len < 2) return dec;
     const PrefillShape ps = prefill_shape(num_seqs, num_q_tokens, max_query_len, num_heads, num_kv_heads);
@@ -789,7 +818,7 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
                              int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
                              int64_t num_blocks, float scale, int32_t causal, void* workspace,
                              size_t workspace_bytes, pa_dtype dtype, hipStream_t stream) {
-    if (dtype != PA_BF16) return fail(PA_ERR_UNSUPPORTED, "dtype %d (chunked prefill is bf16 only)", (int)dtype);
+    if (dtype != PA_BF16 && dtype != PA_F32) return fail(PA_ERR_UNSUPPORTED, "dtype %d", (int)dtype);
     const pa_status hs = check_heads(num_heads, num_kv_heads, head_dim, block_size);
     if (hs != PA_OK) return hs;
     if (num_seqs < 0 || num_q_tokens < 0 || num_blocks < 0 || max_seq_len < 0 || max_query_len < 0 ||
@@ -808,7 +837,7 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
         return fail(PA_ERR_INVALID_ARG, "null pointer");
     if (q_token_stride < (int64_t)num_heads * head_dim)
         return fail(PA_ERR_INVALID_ARG, "q_token_stride smaller than num_heads * head_dim");
-    if (!aligned16(query) || (q_token_stride * 2) % 16 || !aligned16(out) || !aligned16(key_cache) ||
+    if (!aligned16(query) || (q_token_stride * elem_bytes(dtype)) % 16 || !aligned16(out) || !aligned16(key_cache) ||
         !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
 
@@ -818,6 +847,34 @@ pa_status pa_chunked_prefill(void* out, const void* query, int64_t q_token_strid
             dc = pa::debug_check_tables(block_table, max_blocks_per_req, seq_lens, num_seqs, num_blocks, max_seq_len,
                                         stream);
         if (dc != PA_OK) return dc;
+    }
+
+    if (dtype == PA_F32) {
+        // fp32: every query row as a decode row of its own -- its key count
+        // under the mask and its request's table row, expanded into the
+        // workspace -- read by the fp32 decode.  Planned before either launch.
+        const F32Rows fr = f32_rows(num_q_tokens, max_seq_len);
+        if (!workspace || workspace_bytes < fr.table_off + fr.table_bytes)
+            return fail(PA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace ? workspace_bytes : 0,
+                        pa_chunked_prefill_workspace_bytes_ex(num_seqs, num_q_tokens, max_query_len, max_seq_len,
+                                                              num_heads, num_kv_heads, head_dim, dtype));
+        if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+        char* w = static_cast<char*>(workspace);
+        int32_t* row_lens = reinterpret_cast<int32_t*>(w);
+        int32_t* row_table = reinterpret_cast<int32_t*>(w + fr.table_off);
+        const size_t dec_off = fr.table_off + fr.table_bytes;
+        DecodePlan plan;
+        const pa_status st = plan_decode(plan, out, query, q_token_stride, key_cache, value_cache, row_table,
+                                         fr.row_stride, row_lens, nullptr, (int32_t)num_q_tokens, num_heads,
+                                         num_kv_heads, num_blocks, scale, max_seq_len, 0, w + dec_off,
+                                         workspace_bytes - dec_off, 0, 1.f, 1.f);
+        if (st != PA_OK) return st;
+        const pa_status ex = hip_status(pa::launch_expand_rows(cu_query_lens, seq_lens, block_table, max_blocks_per_req,
+                                                               num_seqs, num_q_tokens, causal, row_lens, row_table,
+                                                               fr.row_stride, stream),
+                                        "expand_rows launch");
+        if (ex != PA_OK) return ex;
+        return launch_planned(plan, stream);
     }
 
     // workspace: the decode part's, then the prefill partial records and merge list

@@ -405,6 +405,45 @@ hipError_t launch_slot_and_cache(int64_t* slot_mapping, const int32_t* block_tab
     return hipGetLastError();
 }
 
+// Mixed-batch attention over an fp32 cache, as one decode row per query row
+// (the causal mask of section "Attention (FlashAttention, Scaled Dot-Product
+// Attention)" of the same article): row cu_q[b] + j of request b, with
+// q = cu_q[b+1] - cu_q[b] rows and L = seq_lens[b] keys, attends keys
+// 0 .. L - q + j when causal (all L otherwise), so its decode row has that
+// many keys and a copy of the request's block-table row.  One workgroup per
+// request; rows outside [0, num_rows) and table entries past the row's keys
+// are left alone.
+__global__ void __launch_bounds__(256)
+expand_rows_kernel(const int32_t* __restrict__ cu_q, const int32_t* __restrict__ seq_lens,
+                   const int32_t* __restrict__ block_table, int32_t bt_stride, int64_t num_rows, int32_t causal,
+                   int32_t* __restrict__ row_lens, int32_t* __restrict__ row_table, int32_t row_stride) {
+    const int b = blockIdx.x;
+    const int64_t q0 = cu_q[b], q1 = cu_q[b + 1];
+    const int64_t lo = max(q0, (int64_t)0), hi = min(q1, num_rows);
+    const int64_t n = hi > lo ? hi - lo : 0;
+    const int64_t q = q1 - q0;
+    const int32_t L = max(min(seq_lens[b], min(bt_stride, row_stride) * kBlock), 0);
+    const int32_t nb = (L + kBlock - 1) / kBlock;
+    for (int64_t r = threadIdx.x; r < n; r += blockDim.x) {
+        const int64_t j = lo + r - q0;                     // the row's index within the request
+        row_lens[lo + r] = causal ? (int32_t)max(min((int64_t)L - q + j + 1, (int64_t)L), (int64_t)0) : L;
+    }
+    const int32_t* src = block_table + (int64_t)b * bt_stride;
+    for (int64_t e = threadIdx.x; e < n * nb; e += blockDim.x) {
+        const int64_t r = e / nb;
+        const int32_t i = (int32_t)(e - r * nb);
+        row_table[(lo + r) * row_stride + i] = src[i];
+    }
+}
+
+hipError_t launch_expand_rows(const int32_t* cu_query_lens, const int32_t* seq_lens, const int32_t* block_table,
+                              int32_t max_blocks_per_req, int32_t num_seqs, int64_t num_rows, int32_t causal,
+                              int32_t* row_lens, int32_t* row_table, int32_t row_stride, hipStream_t stream) {
+    hipLaunchKernelGGL(expand_rows_kernel, dim3((unsigned)num_seqs), dim3(256), 0, stream, cu_query_lens, seq_lens,
+                       block_table, max_blocks_per_req, num_rows, causal, row_lens, row_table, row_stride);
+    return hipGetLastError();
+}
+
 hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table,
                                int32_t max_blocks_per_req, int32_t num_seqs,
                                const int32_t* token_seq, const int32_t* token_pos,

@@ -13,6 +13,13 @@ hipError_t launch_slot_mapping(int64_t* slot_mapping, const int32_t* block_table
                                const int32_t* token_seq, const int32_t* token_pos,
                                int64_t num_tokens, hipStream_t stream);
 
+// One decode row per query row of a mixed batch: row_lens [num_rows] (the
+// row's keys under the causal mask or all of the request's) and row_table
+// [num_rows, row_stride] (the request's block-table row).
+hipError_t launch_expand_rows(const int32_t* cu_query_lens, const int32_t* seq_lens, const int32_t* block_table,
+                              int32_t max_blocks_per_req, int32_t num_seqs, int64_t num_rows, int32_t causal,
+                              int32_t* row_lens, int32_t* row_table, int32_t row_stride, hipStream_t stream);
+
 // Copy-on-write: block pairs (src, dst) of every layer's K and V caches.
 hipError_t launch_copy_blocks(void* key_cache, void* value_cache, int64_t layer_stride_bytes, int32_t num_layers,
                               int64_t num_blocks, int64_t block_bytes, const int64_t* block_mapping,

@@ -196,7 +196,8 @@ class DeviceWorkload:
     def prefill_workspace(self):
         w = self.w
         return chunked_prefill_workspace(w.num_seqs, w.num_q_tokens, w.max_query_len, w.max_seq_len,
-                                         w.num_heads, w.num_kv_heads, w.head_dim, device=self.device)
+                                         w.num_heads, w.num_kv_heads, w.head_dim, device=self.device,
+                                         dtype=self.dtype)
 
     def chunked_prefill(self, out=None, workspace=None, stream=None) -> torch.Tensor:
         """Row a10: one call over the whole mixed batch (chunks and decodes)."""

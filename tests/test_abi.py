@@ -162,7 +162,8 @@ def _prefill(L, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(dtype=0), pa.PA_ERR_UNSUPPORTED),                            # bf16 only
+    (dict(dtype=2), pa.PA_ERR_UNSUPPORTED),                            # bf16 or fp32
+    (dict(dtype=0), pa.PA_ERR_WORKSPACE),                              # fp32: its row table is needed
     (dict(head_dim=64), pa.PA_ERR_UNSUPPORTED),
     (dict(block_size=8), pa.PA_ERR_UNSUPPORTED),
     (dict(num_heads=24), pa.PA_ERR_UNSUPPORTED),
@@ -178,6 +179,22 @@ def _prefill(L, **kw):
 def test_chunked_prefill_rejects_before_launch(L, kw, status):
     assert _prefill(L, **kw) == status
     assert pa.pa_last_error_message()
+
+
+def test_chunked_prefill_workspace_by_dtype(L):
+    """The bf16 size is the plain query's; the fp32 route holds a key count and
+    a block-table row (the blocks of max_seq_len) per query row, then a decode
+    workspace for that many rows."""
+    shape = (3, 700, 512, 4000, 32, 8, 128)
+    bf = L.pa_chunked_prefill_workspace_bytes(*shape)
+    assert bf > 0 and L.pa_chunked_prefill_workspace_bytes_ex(*shape, pa.PA_BF16) == bf
+    f32 = L.pa_chunked_prefill_workspace_bytes_ex(*shape, pa.PA_F32)
+    align = lambda n: (n + 255) // 256 * 256
+    assert f32 >= align(4 * 700) + align(4 * 700 * 250) + L.pa_decode_workspace_bytes(700, 32, 8, 128, 4000, 0)
+    assert L.pa_chunked_prefill_workspace_bytes_ex(0, 700, 512, 4000, 32, 8, 128, pa.PA_F32) == 0
+    # a workspace of the fp32 size passes the workspace check (null data
+    # pointers then fail the argument check, still before any launch)
+    assert _prefill(L, dtype=0, workspace=256, workspace_bytes=f32, out=None) == pa.PA_ERR_INVALID_ARG
 
 
 def test_chunked_prefill_empty_is_ok(L):
