@@ -292,9 +292,11 @@ pa_status pa_slot_mapping_and_cache_fp8(int64_t *slot_mapping, const int32_t *bl
  * k_scale and each V element for value(code) * v_scale.  The codes are widened
  * to bf16 exactly; k_scale is folded into the softmax scale and v_scale into
  * the output, so the arithmetic is that of the bf16 path.  It always uses the
- * balanced stream mode (no partition_tokens): num_seqs must be at most 4096.
- * Workspace: pa_decode_workspace_bytes(num_seqs, num_heads, num_kv_heads,
- * head_dim, max_seq_len, 0) bytes, 16-byte aligned.
+ * balanced stream mode (no partition_tokens), which takes up to 4096
+ * sequences per launch: a larger batch runs as consecutive launches over
+ * groups of 4096 sequences on the same workspace, all checked before the
+ * first.  Workspace: pa_decode_workspace_bytes(num_seqs, num_heads,
+ * num_kv_heads, head_dim, max_seq_len, 0) bytes, 16-byte aligned.
  */
 pa_status pa_decode_fp8(void *out, const void *query, int64_t q_token_stride,
                         const void *key_cache, const void *value_cache,
@@ -405,7 +407,8 @@ pa_status pa_rope_reshape_and_cache(void *query_out, int64_t q_out_token_stride,
  * Workspace bytes pa_decode needs for these arguments (0 when no sequence is
  * split).  Same partition rule as pa_decode: partition_tokens > 0 is used as
  * given (a multiple of block_size), 0 picks a size from the shapes, -1 never
- * splits.
+ * splits.  With partition_tokens 0 the size also covers pa_decode_append and
+ * pa_decode_fp8(_ex) (past 4096 sequences: their groups of 4096).
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
                                  int32_t head_dim, int32_t max_seq_len,

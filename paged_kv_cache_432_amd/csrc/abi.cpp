@@ -9,6 +9,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <vector>
 
 #include "host_status.h"
 #include "launch.h"
@@ -500,7 +501,18 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
         return bytes;
     }
     const int32_t pt = choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
-    return partition_ws_bytes(num_seqs, num_heads, num_partitions(max_seq_len, pt));
+    size_t bytes = partition_ws_bytes(num_seqs, num_heads, num_partitions(max_seq_len, pt));
+    if (partition_tokens == 0) {
+        // pa_decode_fp8 reads a larger batch in groups of kStreamMaxSeqs
+        // sequences, one stream-mode launch each, on this one workspace
+        const int32_t group = num_heads / num_kv_heads;
+        for (int dtype : {2, 4}) {
+            const size_t n = stream_ws_bytes(kStreamMaxSeqs, num_heads, num_kv_heads,
+                                             stream_shape(dtype, group, num_kv_heads, kStreamMaxSeqs));
+            bytes = n > bytes ? n : bytes;
+        }
+    }
+    return bytes;
 }
 
 }  // extern "C"
@@ -658,9 +670,6 @@ pa_status pa_decode_fp8_ex(void* out, const void* query, int64_t q_token_stride,
     if ((int64_t)max_seq_len > (int64_t)max_blocks_per_req * 16)
         return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
     if (num_seqs == 0) return ok();
-    if (!use_stream(num_seqs, 0))
-        return fail(PA_ERR_UNSUPPORTED, "%d sequences: an fp8 cache is read in the stream mode, at most %d",
-                    num_seqs, kStreamMaxSeqs);
     if (num_blocks == 0 && max_seq_len > 0) return fail(PA_ERR_INVALID_ARG, "empty cache pool");
     if (!out || !query || !seq_lens || !key_cache || !value_cache || (max_seq_len > 0 && !block_table))
         return fail(PA_ERR_INVALID_ARG, "null pointer");
@@ -674,9 +683,29 @@ pa_status pa_decode_fp8_ex(void* out, const void* query, int64_t q_token_stride,
                                                     max_seq_len, stream);
         if (dc != PA_OK) return dc;
     }
-    return decode_common(out, query, q_token_stride, key_cache, value_cache, block_table, max_blocks_per_req,
-                         seq_lens, nullptr, num_seqs, num_heads, num_kv_heads, num_blocks, scale, max_seq_len, 0,
-                         workspace, workspace_bytes, format == PA_FP8_E5M2 ? 4 : 2, k_scale, v_scale, stream);
+    // An fp8 cache is read in the stream mode only, which takes at most
+    // kStreamMaxSeqs sequences: a larger batch runs as consecutive launches
+    // over groups of that many, each reusing the workspace after the one
+    // before it on the stream.  Every group is planned before the first
+    // launch.
+    const int dt = format == PA_FP8_E5M2 ? 4 : 2;
+    std::vector<DecodePlan> plans((size_t)((num_seqs + kStreamMaxSeqs - 1) / kStreamMaxSeqs));
+    for (size_t g = 0; g < plans.size(); ++g) {
+        const int32_t c0 = (int32_t)g * kStreamMaxSeqs;
+        const int32_t n = std::min(kStreamMaxSeqs, num_seqs - c0);
+        const pa_status st =
+            plan_decode(plans[g], static_cast<char*>(out) + (int64_t)c0 * num_heads * head_dim * 2,
+                        static_cast<const char*>(query) + (int64_t)c0 * q_token_stride * 2, q_token_stride,
+                        key_cache, value_cache, block_table ? block_table + (int64_t)c0 * max_blocks_per_req : nullptr,
+                        max_blocks_per_req, seq_lens + c0, nullptr, n, num_heads, num_kv_heads, num_blocks, scale,
+                        max_seq_len, 0, workspace, workspace_bytes, dt, k_scale, v_scale);
+        if (st != PA_OK) return st;
+    }
+    for (const DecodePlan& plan : plans) {
+        const pa_status st = launch_planned(plan, stream);
+        if (st != PA_OK) return st;
+    }
+    return ok();
 }
 
 pa_status pa_decode_fp8(void* out, const void* query, int64_t q_token_stride, const void* key_cache,

@@ -5,7 +5,8 @@ oracle:
     modes, the one-call step, chunked prefill, and an fp8 cache of more than
     4 GiB of codes);
   - exactly 4096 sequences, the most the balanced stream mode takes, next to
-    4097, which moves to fixed partitions;
+    4097, which moves to fixed partitions; over an fp8 cache (stream mode
+    only), 8193 sequences in groups of 4096;
   - one sequence of 262,144 tokens (16,384 blocks) beside short ones.
 The oracle relabels each sequence's blocks into a compact pool of its own
 (the result does not depend on physical block ids), so it never holds the
@@ -120,6 +121,27 @@ def test_stream_mode_limit(staging):
         out = dw.decode()
         torch.cuda.synchronize()
         assert_parity(to_numpy(out), oracle.run(w), "bf16", f"{n} sequences (partition tokens {pt})")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_past_the_stream_mode_limit(staging, fmt):
+    """An fp8 cache is read in the stream mode only (4096 sequences a launch):
+    8193 sequences run as groups of 4096, 4096 and 1 on one workspace, every
+    output row against the oracle over the codes."""
+    rng = np.random.default_rng(98)
+    lens = rng.integers(1, 60, 8193).astype(np.int32)
+    lens[::97] = 0
+    for n in (8193,):
+        # sigma 0.5 as in the decode configs: outputs of a few short rows reach
+        # 3.5 at most, where the bf16 rounding of the output stays below the
+        # 1e-2 bar (at sigma 1 they reach 7, and rounding alone can exceed it)
+        w = W.custom("limit_fp8", seq_lens=lens[:n], num_heads=8, num_kv_heads=8, dtype="bf16", seed=98 + n,
+                     sigma=0.5)
+        dw = staging.DeviceWorkload(w, kv_fp8=True, fp8_format=fmt)
+        dw.scatter_new()
+        out = dw.decode()
+        torch.cuda.synchronize()
+        assert_parity(to_numpy(out), _ref(w, fmt), "bf16", f"{fmt}, {n} sequences")
 
 
 def test_quarter_million_token_sequence(staging):
