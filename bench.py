@@ -114,16 +114,17 @@ def recorded_traffic(workload: str, call: str):
 
 
 def probes(pa, torch, nbytes: int = 4 << 30, iters: int = 10):
-    """The library's streaming read probe (all of a 4 GiB buffer, 16384
-    workgroups) and copy probe (1 GiB each way) on the same GPU: the achievable
-    HBM rates the decode kernel is set against.  The copy is also the transfer
-    of known size that the traffic counters are scaled by."""
+    """The library's streaming read probe (all of a 4 GiB buffer; the best of
+    16384, 32768 and 65536 workgroups, the grid that reads fastest differing
+    from GPU to GPU) and copy probe (1 GiB each way) on the same GPU: the
+    achievable HBM rates the decode kernel is set against.  The copy is also
+    the transfer of known size that the traffic counters are scaled by."""
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     gib = 1 << 30
     out = {}
-    for name, fn, moved in (("stream_read", lambda: pa.pa_probe_stream_read(buf, sink, 16384), nbytes),
-                            ("copy", lambda: pa.pa_probe_copy(buf[gib:2 * gib], buf[:gib], 8192), 2 * gib)):
+
+    def timed(fn):
         fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
@@ -132,8 +133,16 @@ def probes(pa, torch, nbytes: int = 4 << 30, iters: int = 10):
             fn()
             b.record()
         torch.cuda.synchronize()
-        us = float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
-        out[name] = {"GBps": round(moved / us / 1e3, 1), "us": round(us, 1), "bytes": moved}
+        return float(np.median([a.elapsed_time(b) for a, b in ev])) * 1e3
+
+    grids = {g: timed(lambda: pa.pa_probe_stream_read(buf, sink, g)) for g in (16384, 32768, 65536)}
+    g_best = min(grids, key=grids.get)
+    us = grids[g_best]
+    out["stream_read"] = {"GBps": round(nbytes / us / 1e3, 1), "us": round(us, 1), "bytes": nbytes,
+                          "workgroups": g_best,
+                          "GBps_by_workgroups": {str(g): round(nbytes / t / 1e3, 1) for g, t in grids.items()}}
+    us = timed(lambda: pa.pa_probe_copy(buf[gib:2 * gib], buf[:gib], 8192))
+    out["copy"] = {"GBps": round(2 * gib / us / 1e3, 1), "us": round(us, 1), "bytes": 2 * gib}
     del buf
     torch.cuda.empty_cache()
     return out
