@@ -27,7 +27,7 @@
 //     goes through LDS.  32x32x16 products sustain the matrix rate with one or
 //     two independent accumulators per wave, where 16x16x32 products need
 //     twelve or more (measured on MI355X).
-//   * P.V runs in fp16 (v_mfma_f32_16x16x32_f16): V^T is staged to LDS as
+//   * P.V runs in fp16 (v_mfma_f32_32x32x16_f16): V^T is staged to LDS as
 //     fp16, exact for bf16 magnitudes below 2^16, and p in [0, 1] is rounded
 //     once to fp16 (11 significant bits, subnormals kept).  A single bf16
 //     rounding of p would use most of the output's error budget on top of the
@@ -348,8 +348,8 @@ prefill_kernel(PrefillArgs a) {
         const int w4 = __builtin_amdgcn_readfirstlane(tid >> 8);   // the same for a whole wave
         const uint32_t koff = ((tid >> 4) & 15) * tok_bytes + head_off + (tid & 15) * 16;
         const uint32_t voff = 4 * (kq & 3) * tok_bytes + head_off + dp * 4;
-        // two sets of staging registers: a tile's loads are issued two tiles
-        // before its commit, the set chosen at compile time (see run)
+        // staging registers, kStageSets sets of them (the set chosen at compile
+        // time, see run)
         u32x4_t kreg[kStageSets][kBlkPerThr];
         uint32_t vw[kStageSets][kBlkPerThr][4];
         // Block ids, per staging set: bid[S] holds (lanes 0-3) the ids of the
@@ -457,9 +457,10 @@ prefill_kernel(PrefillArgs a) {
             }
             __syncthreads();
 
-            // One key tile.  Tile kt + 1 is already in staging set `held`; tile kt + 2
-            // is loaded into the other set now and committed at the end of the next
-            // tile, so each tile's loads have two tiles' time to arrive.
+            // One key tile.  With one staging set, tile kt + 1 is loaded now and
+            // committed at the end of this tile.  With two, tile kt + 1 is already
+            // in set `held` and tile kt + 2 is loaded into the other set now, to be
+            // committed at the end of the next tile.
             auto tile = [&](int kt, auto held) {
                 constexpr int A = decltype(held)::value;
                 using Other = std::integral_constant<int, 1 - A>;

@@ -96,3 +96,33 @@ def test_duplicate_slots_are_caught(debug):
              f"slot_mapping[{n - 1}]")
     torch.cuda.synchronize()
     assert torch.equal(_bytes(dw.key_cache), kc)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_fp8_entry_points_are_checked(debug, fmt):
+    """The fp8 decode and the fp8 scatter run the same checks: a block id
+    outside the pool, and two tokens on one slot, come back as errors with the
+    output and the cache codes untouched."""
+    pa, staging = debug
+    w = W.custom("dbg8", seq_lens=[40, 17, 300], dtype="bf16", seed=7, sigma=0.5)
+    dw = staging.DeviceWorkload(w, kv_fp8=True, fp8_format=fmt)
+    dw.scatter_new()
+    out = dw.decode()
+    torch.cuda.synchronize()
+    assert_parity(to_numpy(out), _fp8_ref(w, fmt), "bf16", f"PA_DEBUG=1 {fmt} decode")
+    dw.block_table[1, 0] = -3                          # a block sequence 1 reads, outside the pool
+    out.fill_(3.0)
+    _rejects(pa, lambda: dw.decode(out=out), "block_table[1][0]")
+    n = int(dw.new_k.shape[0])
+    slots = torch.arange(n, dtype=torch.int64, device=dw.key_cache.device) * 5
+    slots[1] = slots[0]
+    kc = _bytes(dw.key_cache)
+    _rejects(pa, lambda: pa.pa_reshape_and_cache_fp8(dw.new_k, dw.new_v, dw.key_cache, dw.value_cache, slots,
+                                                     dw.k_scale, dw.v_scale, fp8_format=fmt), "slot_mapping[1]")
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()) and torch.equal(_bytes(dw.key_cache), kc)
+
+
+def _fp8_ref(w, fmt):
+    res = oracle.run_sequences(w, range(w.num_seqs), fp8_scales=w.fp8_scales(), fp8_format=fmt)
+    return np.concatenate([res[b] for b in range(w.num_seqs)], axis=0)
