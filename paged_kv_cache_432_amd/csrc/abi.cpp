@@ -643,7 +643,7 @@ struct F32Rows {
 };
 F32Rows f32_rows(int64_t rows, int32_t max_seq_len) {
     F32Rows f;
-    f.row_stride = std::max((max_seq_len + 15) / 16, 1);
+    f.row_stride = (int32_t)std::max<int64_t>(((int64_t)max_seq_len + 15) / 16, 1);
     f.table_off = align256((size_t)rows * sizeof(int32_t));
     f.table_bytes = align256((size_t)rows * (size_t)f.row_stride * sizeof(int32_t));
     return f;
