@@ -89,10 +89,8 @@ constexpr int kBlkPerThr = 4 / kThrGroups;
 #endif
 constexpr int kStageSets = kThrGroups == 2 ? PA_PREFILL_STAGE_SETS : 1;
 static_assert(kStageSets == 1 || kStageSets == 2, "staging sets");
-// Merge workgroups per listed tile: 8 rows each, one per 32-thread group, so
-// that each thread merges one row (the merge is bound by reading the records).
-constexpr int kMergeRows = 8;
-constexpr int kMergeParts = kPrefillRows / kMergeRows;
+// Merge workgroups per listed tile: one per wave block of 32 rows.
+constexpr int kMergeParts = kPrefillRows / kRowsPerWave;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t w) { return __builtin_bit_cast(bf16x8_t, w); }
 __device__ __forceinline__ f16x8_t as_f16x8(u32x4_t w) { return __builtin_bit_cast(f16x8_t, w); }
@@ -103,7 +101,7 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, f16x2_t));
 }
 
-constexpr int kRec = 132;                    // partial record floats per row: 128 O, max, sum, pad
+constexpr int kRec = 132;                    // record floats per row: 128 O, max, sum, 2 unused
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
 constexpr float kSlack = 8.f;                // log2 headroom of the softmax reference max
 
@@ -302,19 +300,19 @@ prefill_kernel(PrefillArgs a) {
         const int tq = r / G;
         const bool active = tq < ntok;
         const int kend = !active ? 0 : (a.causal ? max(min(L, prior + tok_begin + tq + 1), 0) : L);
-        u32x4_t qop[8];                                    // B operand of S^T, dim step ks: dims 16ks + 8h .. +8
+        // B operand of S^T, dim step ks: dims 16ks + 8h .. +8.  Loaded on every
+        // path (a load under a branch leaves the wait counts unknown, and the
+        // loop would then wait on every load in flight): an inactive row reads
+        // the tile's first token, and its limit kend = 0 masks every score, so
+        // its p are all 0.  The values are not otherwise touched before the
+        // first product, so their wait falls there, behind the K/V prologue.
+        u32x4_t qop[8];
         {
             const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
                                  (int64_t)(q0 + tok_begin + (active ? tq : 0)) * a.q_stride +
                                  (int64_t)(kvh * G + r % G) * kHeadDim + 8 * h;
 #pragma unroll
             for (int ks = 0; ks < 8; ++ks) qop[ks] = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
-            // loaded unconditionally (an inactive row reads the tile's first row,
-            // then zeroes it): a load under a branch leaves the wait counts
-            // unknown, and the loop would then wait on every load in flight
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks)
-                if (!active) qop[ks] = u32x4_t{0u, 0u, 0u, 0u};
         }
         // wave-wide key limit: tiles ending past kmin need the mask.  (A tile
         // wholly past the wave's rows is still computed, its scores all masked:
@@ -603,38 +601,57 @@ prefill_kernel(PrefillArgs a) {
         run(std::true_type{});
         // a V magnitude beyond fp16 (or a NaN, which the exact path propagates)
         if (__syncthreads_or(!(vmax <= 65504.f))) run(std::false_type{});
-        // ---- finish: lane holds dims 32dt + 8b + 4h .. +4 of its row.  A tile
-        // within the share normalises and writes bf16 rows.  A segment of a tile
-        // that crosses a share boundary writes its (unnormalised rows, max, sum)
-        // record, in the workgroup's record 0 if the segment is its first, else in
-        // record 1; the segment holding the tile's first unit lists the tile for
-        // the merge kernel.
+        // ---- finish: lane holds dims 32dt + 8b + 4h .. +4 of its row.
+        //  * A tile within the share normalises its rows to bf16 and writes them
+        //    through LDS (the K/V buffers are free once every wave has passed the
+        //    last barrier of the loop): each wave stages its 32 rows, then writes
+        //    4 whole rows per store instruction, 16 bytes a lane.
+        //  * A segment of a tile that crosses a share boundary writes its record
+        //    (unnormalised rows, max, sum) in the workgroup's record 0 if the
+        //    segment is its first, else in record 1, in the order of the
+        //    accumulator fragments: store (dt, b) of a wave covers 1 KB of
+        //    consecutive floats.  The segment holding the tile's first unit
+        //    lists the tile for the merge kernel.
         {
             const float l = sum_across_halves(lp);
-            if (active) {
-                if (!split) {
-                    const float inv = l > 0.f ? 1.f / l : 0.f;
-                    uint16_t* o = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(q0 + tok_begin + tq) * Hq * kHeadDim +
-                                  (int64_t)(kvh * G + r % G) * kHeadDim + 4 * h;
+            if (!split) {
+                const float inv = l > 0.f ? 1.f / l : 0.f;
+                uint16_t* st = (wave < 4 ? &k_lds[0][0] : &v_lds[0][0]) + (wave & 3) * kRowsPerWave * kKStride;
 #pragma unroll
-                    for (int dt = 0; dt < 4; ++dt)
+                for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                        for (int b4 = 0; b4 < 4; ++b4) {
-                            const f32x16_t& v = oacc[dt];
-                            *reinterpret_cast<u32x2_t*>(o + 32 * dt + 8 * b4) =
-                                u32x2_t{pack_bf16x2(v[4 * b4] * inv, v[4 * b4 + 1] * inv),
-                                        pack_bf16x2(v[4 * b4 + 2] * inv, v[4 * b4 + 3] * inv)};
-                        }
-                } else {
-                    float* rec = a.part + (((int64_t)blockIdx.x * 2 + (first ? 0 : 1)) * kPrefillRows + r) * kRec;
+                    for (int b4 = 0; b4 < 4; ++b4) {
+                        const f32x16_t& v = oacc[dt];
+                        *reinterpret_cast<u32x2_t*>(st + lr * kKStride + 32 * dt + 8 * b4 + 4 * h) =
+                            u32x2_t{pack_bf16x2(v[4 * b4] * inv, v[4 * b4 + 1] * inv),
+                                    pack_bf16x2(v[4 * b4 + 2] * inv, v[4 * b4 + 3] * inv)};
+                    }
+                // the wave reads back only what it wrote: LDS keeps one wave's
+                // accesses in order, and the compiler keeps the reads after the
+                // writes
+                __builtin_amdgcn_wave_barrier();
 #pragma unroll
-                    for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-                        for (int b4 = 0; b4 < 4; ++b4)
-                            *reinterpret_cast<f32x4_t*>(rec + 32 * dt + 8 * b4 + 4 * h) =
-                                f32x4_t{oacc[dt][4 * b4], oacc[dt][4 * b4 + 1], oacc[dt][4 * b4 + 2], oacc[dt][4 * b4 + 3]};
-                    if (h == 0) *reinterpret_cast<float2*>(rec + kHeadDim) = make_float2(m, l);
+                for (int j = 0; j < kRowsPerWave / 4; ++j) {
+                    const int wr = 4 * j + (lane >> 4);        // row within the wave
+                    const int rr = wave * kRowsPerWave + wr;
+                    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(st + wr * kKStride + 8 * (lane & 15));
+                    if (rr / G < ntok) {
+                        uint16_t* o = reinterpret_cast<uint16_t*>(a.out) +
+                                      (int64_t)(q0 + tok_begin + rr / G) * Hq * kHeadDim +
+                                      (int64_t)(kvh * G + rr % G) * kHeadDim + 8 * (lane & 15);
+                        *reinterpret_cast<u32x4_t*>(o) = v;
+                    }
                 }
+                __syncthreads();                           // staging read before the next segment's commit
+            } else if (active) {
+                float* rec = a.part + ((int64_t)blockIdx.x * 2 + (first ? 0 : 1)) * kPrefillRows * kRec;
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                    for (int b4 = 0; b4 < 4; ++b4)
+                        *reinterpret_cast<f32x4_t*>(rec + ((wave * 16 + 4 * dt + b4) * kWave + lane) * 4) =
+                            f32x4_t{oacc[dt][4 * b4], oacc[dt][4 * b4 + 1], oacc[dt][4 * b4 + 2], oacc[dt][4 * b4 + 3]};
+                if (h == 0) *reinterpret_cast<float2*>(rec + kPrefillRows * kHeadDim + 2 * r) = make_float2(m, l);
             }
         }
         // list entry: first slot, slots | (record of the first slot) << 24, first
@@ -661,54 +678,66 @@ prefill_kernel(PrefillArgs a) {
 
 // Log-sum-exp merge of the segments of every listed query tile: per row,
 // M = max_p m_p, out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p, taken in
-// one pass with a running max.  kMergeParts workgroups per listed (tile, KV
-// head), 8 rows each; thread i covers dims 4(i % 32) .. +4 of row i / 32.
+// one pass with a running max.  One workgroup per 32-row wave block of a
+// listed (tile, KV head); the records hold each block's rows in accumulator
+// fragment order (16 fragments of 64 lanes x 4 floats), so thread t reads
+// fragments t / 64 + 4i (i < 4) of lane t % 64, 1 KB per wave and fragment,
+// and stages its bf16 results in LDS so that whole rows leave together.
 template <int G>
 __global__ void __launch_bounds__(256)
 prefill_merge_kernel(PrefillArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t s_out[kRowsPerWave * kKStride];
     const int e = (int)(blockIdx.x / kMergeParts);
     if (e >= *a.split_count) return;
     const int4 d = a.split_list[e];
     const int s0 = d.x, np = d.y & 0xffffff, rec0 = d.y >> 24, row0 = d.z, ntok = d.w >> 8, kvh = d.w & 255;
+    const int w = (int)(blockIdx.x % kMergeParts);     // wave block: rows 32w .. 32w + 31
+    if ((w * kRowsPerWave) / G >= ntok) return;        // rows are token-major: the whole block is inactive
     const int Hkv = a.num_kv_heads;
-    const int d4 = 4 * (threadIdx.x & 31);
-    const int rbeg = kMergeRows * (int)(blockIdx.x % kMergeParts);
-    for (int r = rbeg + (int)(threadIdx.x >> 5); r < rbeg + kMergeRows; r += 8) {
-        const int tq = r / G;
-        if (tq >= ntok) break;                         // rows are token-major: the rest are inactive
-        float mrun = -INFINITY, lrun = 0.f;
-        f32x4_t o = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        for (int p0 = 0; p0 < np; p0 += 4) {
-            float2 ml[4];
-            f32x4_t ov[4];
+    const int t = threadIdx.x, lane = t & 63, j = t >> 6;
+    const int lr = lane & 31, h = lane >> 5;
+    const int r = w * kRowsPerWave + lr;
+    float mrun = -INFINITY, lrun = 0.f;
+    f32x4_t o[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (p0 + i < np) {
-                    // segment p: slot s0 + p, record rec0 for p = 0 (the tile may
-                    // start inside that slot's share), else record 0
-                    const int p = p0 + i;
-                    const int64_t wg = (int64_t)(s0 + p) * Hkv + kvh;
-                    const float* rec = a.part + ((wg * 2 + (p == 0 ? rec0 : 0)) * kPrefillRows + r) * kRec;
-                    ml[i] = *reinterpret_cast<const float2*>(rec + kHeadDim);
-                    ov[i] = *reinterpret_cast<const f32x4_t*>(rec + d4);
-                }
-            }
+    for (int i = 0; i < 4; ++i) o[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < np; ++p) {
+        // segment p: slot s0 + p, record rec0 for p = 0 (the tile may start
+        // inside that slot's share), else record 0
+        const int64_t wg = (int64_t)(s0 + p) * Hkv + kvh;
+        const float* rec = a.part + (wg * 2 + (p == 0 ? rec0 : 0)) * kPrefillRows * kRec;
+        const float2 ml = *reinterpret_cast<const float2*>(rec + kPrefillRows * kHeadDim + 2 * r);
+        f32x4_t ov[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                if (p0 + i < np) {
-                    const float mn = fmaxf(mrun, ml[i].x);
-                    const float wa = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
-                    const float wb = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[i].x - mn);
-                    lrun = wa * lrun + wb * ml[i].y;
-                    o = wa * o + wb * ov[i];
-                    mrun = mn;
-                }
-            }
+        for (int i = 0; i < 4; ++i)
+            ov[i] = *reinterpret_cast<const f32x4_t*>(rec + ((w * 16 + j + 4 * i) * kWave + lane) * 4);
+        const float mn = fmaxf(mrun, ml.x);
+        const float wa = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
+        const float wb = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - mn);
+        lrun = wa * lrun + wb * ml.y;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = wa * o[i] + wb * ov[i];
+        mrun = mn;
+    }
+    const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
+    // fragment (dt, b) = j + 4i holds dims 32dt + 8b + 4h .. +4 of row lr
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int f = j + 4 * i, dt = f >> 2, b4 = f & 3;
+        *reinterpret_cast<u32x2_t*>(&s_out[lr * kKStride + 32 * dt + 8 * b4 + 4 * h]) =
+            u32x2_t{pack_bf16x2(o[i].x * inv, o[i].y * inv), pack_bf16x2(o[i].z * inv, o[i].w * inv)};
+    }
+    __syncthreads();
+    // 32 rows of 256 bytes: 16 threads a row, 16 rows per pass
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int wr = 16 * pass + (t >> 4);
+        const int rr = w * kRowsPerWave + wr;
+        if (rr / G < ntok) {
+            uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(row0 + rr / G) * a.num_heads * kHeadDim +
+                            (int64_t)(kvh * G + rr % G) * kHeadDim + 8 * (t & 15);
+            *reinterpret_cast<u32x4_t*>(out) = *reinterpret_cast<const u32x4_t*>(&s_out[wr * kKStride + 8 * (t & 15)]);
         }
-        const float inv = lrun > 0.f ? 1.f / lrun : 0.f;
-        uint16_t* out = reinterpret_cast<uint16_t*>(a.out) + (int64_t)(row0 + tq) * a.num_heads * kHeadDim +
-                        (int64_t)(kvh * G + r % G) * kHeadDim + d4;
-        *reinterpret_cast<u32x2_t*>(out) = u32x2_t{pack_bf16x2(o.x * inv, o.y * inv), pack_bf16x2(o.z * inv, o.w * inv)};
     }
 }
 
