@@ -193,7 +193,9 @@ PrefillShape prefill_shape(int32_t num_seqs, int64_t num_q_tokens, int32_t max_q
         }
     }
     const int64_t slots = (int64_t)per_cu * device_cus();
-    p.slots_per_kvh = slots > 0 ? (int32_t)std::max<int64_t>(1, slots / num_kv_heads) : 0;
+    p.slots_per_kvh = slots > 0 ? (int32_t)std::min<int64_t>(std::max<int64_t>(1, slots / num_kv_heads),
+                                                            pa::kPrefillMaxSlots)
+                                : 0;
     return p;
 }
 

@@ -140,10 +140,11 @@ struct PrefillArgs {
     int32_t causal;
     // Work split: the (query tile, 64-key tile) units of a KV head, U of them
     // in (sequence, tile, key tile) order, are shared by slots_per_kvh
-    // workgroups, max(min_share, ceil(U / slots_per_kvh)) consecutive units
-    // each; grid = slots_per_kvh * num_kv_heads, KV head fastest.
+    // workgroups (at most kPrefillMaxSlots), consecutive units each, balanced
+    // on units plus a fixed set-up cost per query tile; grid = slots_per_kvh *
+    // num_kv_heads, KV head fastest.
     int32_t slots_per_kvh;
-    int32_t min_share;             // fewest units per workgroup
+    int32_t min_share;             // fewest cost units per workgroup
     float* part;                   // [grid][2][256 rows][132] partial records (a workgroup's first and
                                    // last segment)
     int32_t* split_count;          // number of listed (tile, KV head) pairs (written by workgroup 0)
@@ -169,6 +170,8 @@ constexpr int kPrefillWaves = PA_PREFILL_WAVES;
 static_assert(kPrefillWaves == 4 || kPrefillWaves == 8, "prefill waves");
 // Query rows (tokens x grouped heads) per prefill workgroup tile.
 constexpr int kPrefillRows = 32 * kPrefillWaves;
+// Most prefill workgroups per KV head (the share boundaries live in LDS).
+constexpr int kPrefillMaxSlots = 1024;
 // Prefill workgroups one compute unit holds at once (bf16, group size G).
 int prefill_blocks_per_cu(int group, int num_seqs);
 

@@ -40,13 +40,15 @@
 //     0 * NaN is NaN).
 //   * Work is balanced over the resident workgroups: the units of one KV
 //     head are its (query tile, 64-key tile) pairs in (sequence, tile, key
-//     tile) order, U of them, and each of the slots_per_kvh workgroups of a KV
-//     head takes a contiguous share of max(min_share, ceil(U / slots_per_kvh))
-//     units, one segment per query tile it touches.  A tile inside one share
-//     writes its rows; the segments of a tile that crosses a share boundary
-//     leave (max, sum, unnormalised output) records per row, merged by a
-//     second kernel (log-sum-exp weights, the same merge as split decode)
-//     over a compact list of those tiles (slot: such tiles before it).
+//     tile) order, and each of the slots_per_kvh workgroups of a KV head takes
+//     a contiguous share of them, one segment per query tile it touches.  The
+//     shares are equal in a cost that adds a fixed set-up charge per query
+//     tile to its key tiles, so that a workgroup whose share spans many short
+//     tiles takes fewer units.  A tile inside one share writes its rows; the
+//     segments of a tile that crosses a share boundary leave (max, sum,
+//     unnormalised output) records per row, merged by a second kernel
+//     (log-sum-exp weights, the same merge as split decode) over a compact
+//     list of those tiles (slot: such tiles before it).
 //   * The KV head is the fastest index of the workgroup number, so the shares
 //     of one KV head land on one XCD and share its L2.
 #include <math.h>
@@ -173,45 +175,104 @@ __device__ __forceinline__ int tile_units(const PrefillArgs& a, const SeqShape& 
     return max(1, (tile_kend(a, sh, t, tq) + kKeys - 1) / kKeys);
 }
 
-// Does a tile whose units are [u0, u0 + n) cross a share boundary?
-__device__ __forceinline__ bool crosses(int u0, int n, int share) { return u0 / share != (u0 + n - 1) / share; }
+// Set-up and finish of a segment (its query rows, the first tile's K/V round
+// trip, the output or record writes, two barriers), in key-tile units: about
+// two tiles' time, measured per workgroup on MI355X.
+#ifndef PA_PREFILL_SEGMENT_UNITS
+#define PA_PREFILL_SEGMENT_UNITS 2
+#endif
+constexpr int kSegUnits = PA_PREFILL_SEGMENT_UNITS;
+
+// The slot whose share holds unit x: the largest s < slots with bnd[s] <= x
+// (bnd[0] = 0 <= x).
+__device__ __forceinline__ int slot_of(const int32_t* bnd, int slots, int x) {
+    int lo = 0, hi = slots - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (bnd[mid] <= x) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Does the tile of units [u0, u0 + n) cross a share boundary?
+__device__ __forceinline__ bool cut(const int32_t* bnd, int slots, int u0, int n) {
+    return slot_of(bnd, slots, u0) != slot_of(bnd, slots, u0 + n - 1);
+}
 
 // The batch's unit map, built by every workgroup.  Units are the (query tile,
 // key tile) pairs of one KV head in (sequence, tile, key tile) order;
-// s_pu[b] = first unit of sequence b (s_pu[B] = U), s_sp[b] = tiles before
-// sequence b that cross a share boundary (s_sp[B] = total).  Returns the
-// share: the units each workgroup of a KV head takes,
-// max(min_share, ceil(U / slots_per_kvh)).
-__device__ __forceinline__ int build_unit_map(const PrefillArgs& a, int tq, int32_t* s_pu, int32_t* s_sp,
-                                              int32_t* s_wsum) {
-    const int B = a.num_seqs;
+// s_pu[b] = first unit of sequence b (s_pu[B] = U).  The shares balance a
+// cost in which each query tile also counts kSegUnits for its set-up and
+// finish: the cost line is cut into slots_per_kvh shares of
+// max(min_share, ceil(C / slots_per_kvh)), and a cut that falls in a tile's
+// set-up moves to the tile's first unit, so that the tile stays whole.
+// s_bnd[s] = first unit of slot s's share (s_bnd[slots_per_kvh] = U; trailing
+// shares may be empty).  s_sp[b] = tiles before sequence b that cross a share
+// boundary (s_sp[B] = total).
+__device__ __forceinline__ void build_unit_map(const PrefillArgs& a, int tq, int32_t* s_pu, int32_t* s_sp,
+                                               int32_t* s_bnd, int32_t* s_wsum) {
+    const int B = a.num_seqs, slots = a.slots_per_kvh;
     const int nthr = blockDim.x;
     const int per = (B + nthr - 1) / nthr;
     const int lo = min((int)threadIdx.x * per, B), hi = min(lo + per, B);
-    int units = 0;
+    // units and query tiles per sequence; s_sp holds the tile prefix until the
+    // boundaries are placed
+    int units = 0, tiles = 0;
     for (int b = lo; b < hi; ++b) {
         const SeqShape sh = seq_shape(a, b);
+        const int nt = tiles_of(sh, tq);
         int ub = 0;
-        for (int t = 0, nt = tiles_of(sh, tq); t < nt; ++t) ub += tile_units(a, sh, t, tq);
+        for (int t = 0; t < nt; ++t) ub += tile_units(a, sh, t, tq);
         s_pu[b + 1] = ub;
+        s_sp[b + 1] = nt;
         units += ub;
+        tiles += nt;
     }
     int run = block_exclusive_scan(units, s_wsum);
+    int runt = block_exclusive_scan(tiles, s_wsum);
     for (int b = lo; b < hi; ++b) {
         run += s_pu[b + 1];
         s_pu[b + 1] = run;
+        runt += s_sp[b + 1];
+        s_sp[b + 1] = runt;
     }
-    if (threadIdx.x == 0) s_pu[0] = 0;
+    if (threadIdx.x == 0) s_pu[0] = s_sp[0] = 0;
     __syncthreads();
     const int U = s_pu[B];
-    const int share = max(a.min_share, (U + a.slots_per_kvh - 1) / a.slots_per_kvh);
+    const int64_t C = (int64_t)U + (int64_t)kSegUnits * s_sp[B];
+    const int64_t cs = max((int64_t)a.min_share, (C + slots - 1) / slots);
+    for (int sl = threadIdx.x; sl <= slots; sl += nthr) {
+        const int64_t x = (int64_t)sl * cs;
+        int bnd = U;
+        if (x < C) {
+            // the sequence whose cost range holds x: the largest b with
+            // s_pu[b] + kSegUnits * s_sp[b] <= x (it has tiles, as x < C)
+            int l = 0, h = B - 1;
+            while (l < h) {
+                const int mid = (l + h + 1) >> 1;
+                if ((int64_t)s_pu[mid] + (int64_t)kSegUnits * s_sp[mid] <= x) l = mid; else h = mid - 1;
+            }
+            const SeqShape sh = seq_shape(a, l);
+            int64_t c = (int64_t)s_pu[l] + (int64_t)kSegUnits * s_sp[l];
+            int u = s_pu[l];
+            for (int t = 0, nt = tiles_of(sh, tq); t < nt; ++t) {
+                const int n = tile_units(a, sh, t, tq);
+                if (x < c + kSegUnits) { bnd = u; break; }
+                if (x < c + kSegUnits + n) { bnd = u + (int)(x - c - kSegUnits); break; }
+                c += kSegUnits + n;
+                u += n;
+            }
+        }
+        s_bnd[sl] = bnd;
+    }
+    __syncthreads();                                   // every read of the tile prefix is done
     int splits = 0;
     for (int b = lo; b < hi; ++b) {
         const SeqShape sh = seq_shape(a, b);
         int u = s_pu[b], sb = 0;
         for (int t = 0, nt = tiles_of(sh, tq); t < nt; ++t) {
             const int n = tile_units(a, sh, t, tq);
-            sb += crosses(u, n, share);
+            sb += cut(s_bnd, slots, u, n);
             u += n;
         }
         s_sp[b + 1] = sb;
@@ -222,9 +283,7 @@ __device__ __forceinline__ int build_unit_map(const PrefillArgs& a, int tq, int3
         run += s_sp[b + 1];
         s_sp[b + 1] = run;
     }
-    if (threadIdx.x == 0) s_sp[0] = 0;
     __syncthreads();
-    return share;
 }
 
 // The largest b with pref[b] <= x (pref non-decreasing, pref[0] = 0 <= x).
@@ -245,19 +304,21 @@ prefill_kernel(PrefillArgs a) {
     int32_t* s_pu = s_dyn;                             // [num_seqs + 1] unit prefix
     int32_t* s_sp = s_dyn + a.num_seqs + 1;            // [num_seqs + 1] split-tile prefix
     __shared__ int32_t s_wsum[kWaves];
+    __shared__ int32_t s_bnd[kPrefillMaxSlots + 1];    // first unit of each slot's share
     __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kKTileElems];
     __shared__ __attribute__((aligned(16))) uint16_t v_lds[2][kVTileElems];
 
-    // values read from LDS are the same in every lane: kept in scalar registers
-    const int share = __builtin_amdgcn_readfirstlane(build_unit_map(a, TQ, s_pu, s_sp, s_wsum));
+    build_unit_map(a, TQ, s_pu, s_sp, s_bnd, s_wsum);
     const int B = a.num_seqs;
     const int Hkv = a.num_kv_heads;
-    const int U = __builtin_amdgcn_readfirstlane(s_pu[B]);
+    const int slots = a.slots_per_kvh;
     if (blockIdx.x == 0 && threadIdx.x == 0) *a.split_count = s_sp[B] * Hkv;
     const int kvh = (int)(blockIdx.x % Hkv);
     const int slot = (int)(blockIdx.x / Hkv);
-    if ((int64_t)slot * share >= U) return;            // whole workgroup: no barrier is left behind
-    const int ub = slot * share, ue = min(U, ub + share);
+    // values read from LDS are the same in every lane: kept in scalar registers
+    const int ub = __builtin_amdgcn_readfirstlane(s_bnd[slot]);
+    const int ue = __builtin_amdgcn_readfirstlane(s_bnd[slot + 1]);
+    if (ub >= ue) return;                              // whole workgroup: no barrier is left behind
 
     // the tile holding unit ub
     int b = __builtin_amdgcn_readfirstlane(find_seq(s_pu, B, ub));
@@ -266,7 +327,7 @@ prefill_kernel(PrefillArgs a) {
     int tu0 = __builtin_amdgcn_readfirstlane(s_pu[b]);  // first unit of the tile
     int split_before = __builtin_amdgcn_readfirstlane(s_sp[b]);
     for (int n = tile_units(a, sh, 0, TQ); ub >= tu0 + n; n = tile_units(a, sh, tile, TQ)) {
-        split_before += crosses(tu0, n, share);
+        split_before += cut(s_bnd, slots, tu0, n);
         tu0 += n;
         ++tile;
     }
@@ -287,7 +348,7 @@ prefill_kernel(PrefillArgs a) {
         const int kt_begin = u - tu0;
         const int seg_end = min(ue, tu0 + units) - tu0;
         const int kt_end = min(seg_end, nkt);
-        const bool split = crosses(tu0, units, share);
+        const bool split = tu0 < ub || tu0 + units > ue; // the tile reaches past this share
         const int q0 = sh.q0, qlen = sh.qlen, L = sh.L;
         const int tok_begin = tile * TQ;
         const int ntok = min(TQ, qlen - tok_begin);
@@ -300,20 +361,6 @@ prefill_kernel(PrefillArgs a) {
         const int tq = r / G;
         const bool active = tq < ntok;
         const int kend = !active ? 0 : (a.causal ? max(min(L, prior + tok_begin + tq + 1), 0) : L);
-        // B operand of S^T, dim step ks: dims 16ks + 8h .. +8.  Loaded on every
-        // path (a load under a branch leaves the wait counts unknown, and the
-        // loop would then wait on every load in flight): an inactive row reads
-        // the tile's first token, and its limit kend = 0 masks every score, so
-        // its p are all 0.  The values are not otherwise touched before the
-        // first product, so their wait falls there, behind the K/V prologue.
-        u32x4_t qop[8];
-        {
-            const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
-                                 (int64_t)(q0 + tok_begin + (active ? tq : 0)) * a.q_stride +
-                                 (int64_t)(kvh * G + r % G) * kHeadDim + 8 * h;
-#pragma unroll
-            for (int ks = 0; ks < 8; ++ks) qop[ks] = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
-        }
         // wave-wide key limit: tiles ending past kmin need the mask.  (A tile
         // wholly past the wave's rows is still computed, its scores all masked:
         // skipping it would merge two versions of the accumulators at the join,
@@ -365,6 +412,28 @@ prefill_kernel(PrefillArgs a) {
             constexpr int S = decltype(set)::value;
             bid[S] = __builtin_amdgcn_raw_buffer_load_b32(rbt, (4 * kt + (lane & 3)) * 4, 0, 0);
         };
+        // The segment's first block ids are loaded before the query rows, so
+        // that the wait for them (before the first tile's K/V loads) does not
+        // cover the query loads as well: the query latency then overlaps the
+        // first tile's.
+        using Set0 = std::integral_constant<int, 0>;
+        using Set1 = std::integral_constant<int, 1>;
+        load_ids(kt_begin, Set0{});
+        __builtin_amdgcn_sched_barrier(0);
+        // B operand of S^T, dim step ks: dims 16ks + 8h .. +8.  Loaded on every
+        // path (a load under a branch leaves the wait counts unknown, and the
+        // loop would then wait on every load in flight): an inactive row reads
+        // the tile's first token, and its limit kend = 0 masks every score, so
+        // its p are all 0.  The values are not otherwise touched before the
+        // first product, so their wait falls there, behind the K/V prologue.
+        u32x4_t qop[8];
+        {
+            const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.query) +
+                                 (int64_t)(q0 + tok_begin + (active ? tq : 0)) * a.q_stride +
+                                 (int64_t)(kvh * G + r % G) * kHeadDim + 8 * h;
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) qop[ks] = *reinterpret_cast<const u32x4_t*>(qp + 16 * ks);
+        }
         auto stage = [&](int kt, auto set) {
             constexpr int S = decltype(set)::value;
             const bool live = kt < kt_end;                 // wave-uniform
@@ -429,18 +498,19 @@ prefill_kernel(PrefillArgs a) {
         // lo = bf16(p - hi), keeping ~16 bits of p; a single bf16 rounding of p
         // would use most of the output's error budget on top of the bf16 output
         // rounding.
-        auto run = [&](auto half) {
+        // ids_loaded: the ids of the segment's first tile are already in bid[0]
+        // (the first pass; the exact pass reloads them).
+        auto run = [&](auto half, auto ids_loaded) {
             constexpr bool kHalf = decltype(half)::value;
+            constexpr bool kIdsLoaded = decltype(ids_loaded)::value;
             m = -INFINITY;
             lp = 0.f;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
-            using Set0 = std::integral_constant<int, 0>;
-            using Set1 = std::integral_constant<int, 1>;
             if constexpr (kStageSets == 2) {
-                load_ids(kt_begin, Set0{});
+                if constexpr (!kIdsLoaded) load_ids(kt_begin, Set0{});
                 load_ids(kt_begin + 1, Set1{});
                 stage(kt_begin, Set0{});
                 load_ids(kt_begin + 2, Set0{});
@@ -448,7 +518,7 @@ prefill_kernel(PrefillArgs a) {
                 stage(kt_begin + 1, Set1{});
                 load_ids(kt_begin + 3, Set1{});
             } else {
-                load_ids(kt_begin, Set0{});
+                if constexpr (!kIdsLoaded) load_ids(kt_begin, Set0{});
                 stage(kt_begin, Set0{});
                 load_ids(kt_begin + 1, Set0{});
                 commit(0, half, Set0{});
@@ -598,9 +668,9 @@ prefill_kernel(PrefillArgs a) {
             }
         };
 
-        run(std::true_type{});
+        run(std::true_type{}, std::true_type{});
         // a V magnitude beyond fp16 (or a NaN, which the exact path propagates)
-        if (__syncthreads_or(!(vmax <= 65504.f))) run(std::false_type{});
+        if (__syncthreads_or(!(vmax <= 65504.f))) run(std::false_type{}, std::false_type{});
         // ---- finish: lane holds dims 32dt + 8b + 4h .. +4 of its row.
         //  * A tile within the share normalises its rows to bf16 and writes them
         //    through LDS (the K/V buffers are free once every wave has passed the
@@ -657,9 +727,9 @@ prefill_kernel(PrefillArgs a) {
         // list entry: first slot, slots | (record of the first slot) << 24, first
         // row, (tokens << 8) | KV head
         if (split && u == tu0 && tid == 0) {
-            const int s0 = tu0 / share, s1 = (tu0 + units - 1) / share;
+            const int s1 = slot_of(s_bnd, slots, tu0 + units - 1);
             a.split_list[split_before * Hkv + kvh] =
-                int4{s0, (s1 - s0 + 1) | ((tu0 % share != 0) << 24), q0 + tok_begin, (ntok << 8) | kvh};
+                int4{slot, (s1 - slot + 1) | ((tu0 != ub) << 24), q0 + tok_begin, (ntok << 8) | kvh};
         }
 
         u = tu0 + seg_end;
