@@ -537,7 +537,8 @@ pa_status pa_decode_append_noalloc(void *out, const void *query, int64_t q_token
  * (Q.K^T in bf16 MFMA, P.V in fp16 MFMA with V exact in fp16, fp32
  * accumulation; a workgroup that meets |V| >= 2^16 redoes its work with the
  * probabilities carried as a bf16 hi/lo pair), their (query tile, key tile)
- * work shared evenly by the resident workgroups and tiles cut by a share
+ * work shared by the resident workgroups in equal parts of a cost that also
+ * charges each query tile a fixed set-up, and tiles cut by a share
  * boundary merged with log-sum-exp weights; q_b == 0 requests produce
  * nothing.  Over an fp32 cache every query row runs as a decode row of its
  * own: a first kernel writes, into the workspace, each row's key count under

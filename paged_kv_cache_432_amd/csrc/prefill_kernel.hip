@@ -89,6 +89,7 @@ constexpr int kBlkPerThr = 4 / kThrGroups;
 #ifndef PA_PREFILL_STAGE_SETS
 #define PA_PREFILL_STAGE_SETS 1
 #endif
+
 constexpr int kStageSets = kThrGroups == 2 ? PA_PREFILL_STAGE_SETS : 1;
 static_assert(kStageSets == 1 || kStageSets == 2, "staging sets");
 // Merge workgroups per listed tile: one per wave block of 32 rows.
@@ -458,13 +459,13 @@ prefill_kernel(PrefillArgs a) {
         // largest magnitude staged so that a workgroup that met a larger one
         // can redo its segment on the exact path.
         float vmax = 0.f;
-        auto commit = [&](int buf, auto half, auto set) {
+        auto commit = [&](int kbuf, int vbuf, auto half, auto set) {
             constexpr bool kHalf = decltype(half)::value;
             constexpr int S = decltype(set)::value;
 #pragma unroll
             for (int j = 0; j < kBlkPerThr; ++j) {
                 const int c = tid + j * kThreads;
-                *reinterpret_cast<u32x4_t*>(&k_lds[buf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[S][j];
+                *reinterpret_cast<u32x4_t*>(&k_lds[kbuf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[S][j];
             }
 #pragma unroll
             for (int j = 0; j < kBlkPerThr; ++j) {
@@ -486,42 +487,168 @@ prefill_kernel(PrefillArgs a) {
                 }
                 // 4-key run q of V^T row d sits at run q ^ ((d >> 4) & 1): the 16
                 // rows 2dp a write instruction covers per cycle then span all banks
-                uint16_t* vt = &v_lds[buf][(2 * dp) * kVStride + 4 * ((kq + 4 * kThrGroups * j) ^ ((dp >> 3) & 1))];
+                uint16_t* vt = &v_lds[vbuf][(2 * dp) * kVStride + 4 * ((kq + 4 * kThrGroups * j) ^ ((dp >> 3) & 1))];
                 *reinterpret_cast<u32x2_t*>(vt) = even;
                 *reinterpret_cast<u32x2_t*>(vt + kVStride) = odd;
             }
         };
 
-        // One pass over the segment's key tiles.  Fast path: P is rounded once to
-        // fp16 (11 significant bits) against V^T in fp16.  Exact path: P is fed as
-        // two bf16 operands against V^T in bf16, hi = p truncated to bf16 and
-        // lo = bf16(p - hi), keeping ~16 bits of p; a single bf16 rounding of p
-        // would use most of the output's error budget on top of the bf16 output
-        // rounding.
-        // ids_loaded: the ids of the segment's first tile are already in bid[0]
-        // (the first pass; the exact pass reloads them).
-        auto run = [&](auto half, auto ids_loaded) {
+        // ---- the pieces of a key tile.
+        // S^T = K Q^T over the tile in K buffer kbuf: 2 key tiles of 32 x 8 dim
+        // steps of 16.  sacc[mt][4b + e] is the score of key 32mt + 8b + 4h + e.
+        auto s_products = [&](int kbuf, f32x16_t (&sacc)[2]) {
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sacc[mt][v] = 0.f;
+            // operands read one step ahead of the products that use them
+            const uint16_t* kl = &k_lds[kbuf][lr * kKStride + 8 * h];
+            auto k_operand = [&](int i) {                  // step i: dim step i / 2, key tile i % 2
+                return *reinterpret_cast<const u32x4_t*>(kl + (i & 1) * 32 * kKStride + 16 * (i >> 1));
+            };
+            u32x4_t ka[2];
+            ka[0] = k_operand(0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
+                sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i & 1]), as_bf16x8(qop[i >> 1]),
+                                                                      sacc[i & 1], 0, 0, 0);
+            }
+        };
+        // Online softmax of tile kt's scores.  The max is taken on raw scores
+        // (scale > 0) and the scale folded into the exponent: p = 2^(s *
+        // scale_log2 - m).  The reference m is raised only when a tile's maximum
+        // exceeds it by more than kSlack (log2 units), so p <= 2^kSlack (exact in
+        // fp16 and fp32) and the accumulator rescale is rare after the first
+        // tiles; the result is the same softmax, as O and l share the reference.
+        // P^T as the B operand of key step s (keys 16s .. 16s+15): the 8 scores
+        // sacc[s / 2][8 (s % 2) .. +8] of this lane, i.e. keys 16s + 8c + 4h + e
+        // for c, e -- the k order the V^T operand follows.  Fast path: p rounded
+        // once to fp16.  Exact path: hi = p truncated to bf16, lo = bf16(p - hi).
+        auto softmax = [&](int kt, f32x16_t (&sacc)[2], u32x4_t (&phi)[4], u32x4_t (&plo)[4], auto half) {
             constexpr bool kHalf = decltype(half)::value;
-            constexpr bool kIdsLoaded = decltype(ids_loaded)::value;
+            const int key0 = kt * kKeys;
+            if (key0 + kKeys > kmin) {                     // a row's limit falls in this tile
+#pragma unroll
+                for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        if (key0 + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3) >= kend) sacc[mt][v] = -INFINITY;
+            }
+            float mx = -INFINITY;
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+                for (int v = 0; v < 16; v += 4)
+                    mx = maximum(maximum(mx, maximum(sacc[mt][v], sacc[mt][v + 1])),
+                                 maximum(sacc[mt][v + 2], sacc[mt][v + 3]));
+            mx = max_across_halves(mx);
+            const float mtile = mx * a.scale_log2;
+            const bool bump = mtile > m + kSlack;
+            const float mn = bump ? mtile : m;
+            const bool none = mn == -INFINITY;             // nothing visible yet in this row
+            const float msafe = none ? 0.f : mn;           // then every score is -inf and p = 0
+            const float alpha = bump ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
+            const bool rescale = bump && m != -INFINITY;
+            m = mn;
+            float sum = 0.f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                float pv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], a.scale_log2, -msafe));
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                    if constexpr (kHalf) {
+                        // the row sum adds the fp16 p that P.V uses
+                        hw[e2] = pack_f16x2(pv[2 * e2], pv[2 * e2 + 1]);
+                        sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hw[e2]), f16x2_t{1.f16, 1.f16}, sum,
+                                                     false);
+                    } else {
+                        // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
+                        const uint32_t u0 = __float_as_uint(pv[2 * e2]), u1 = __float_as_uint(pv[2 * e2 + 1]);
+                        hw[e2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+                        lw[e2] = pack_bf16x2(pv[2 * e2] - __uint_as_float(u0 & 0xffff0000u),
+                                             pv[2 * e2 + 1] - __uint_as_float(u1 & 0xffff0000u));
+                        sum += pv[2 * e2] + pv[2 * e2 + 1];
+                    }
+                }
+                phi[s] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+                if constexpr (!kHalf) plo[s] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+            }
+            lp = lp * alpha + sum;
+            if (__builtin_amdgcn_ballot_w64(rescale)) {
+#pragma unroll
+                for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+            }
+        };
+        // O^T += V^T P^T with the tile in V buffer vbuf: 4 key steps x 4 dim tiles
+        // of 32 (x hi and lo parts of P on the exact path).  The V^T operand of
+        // (dim tile dt, key step s): dim 32dt + l % 32, keys 16s + 4h .. +4 and
+        // 16s + 8 + 4h .. +4, i.e. 4-key runs 4s + h and 4s + 2 + h of the row,
+        // each swizzled by bit 4 of the dim (see commit).
+        auto pv_products = [&](int vbuf, const u32x4_t (&phi)[4], const u32x4_t (&plo)[4], auto half) {
+            constexpr bool kHalf = decltype(half)::value;
+            const int sw = (lr >> 4) & 1;
+            const uint16_t* vl = &v_lds[vbuf][lr * kVStride];
+            auto v_operand = [&](int i) {                  // step i: key step i / 4, dim tile i % 4
+                const uint16_t* vrow = vl + (i & 3) * 32 * kVStride;
+                const int s = i >> 2;
+                const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow + 4 * ((4 * s + h) ^ sw));
+                const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 4 * ((4 * s + 2 + h) ^ sw));
+                return u32x4_t{v0.x, v0.y, v1.x, v1.y};
+            };
+            u32x4_t va[2];
+            va[0] = v_operand(0);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
+                const int dt = i & 3, s = i >> 2;
+                const u32x4_t vop = va[i & 1];
+                if constexpr (kHalf) {
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(vop), as_f16x8(phi[s]), oacc[dt], 0, 0, 0);
+                } else {
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop), as_bf16x8(phi[s]), oacc[dt], 0, 0,
+                                                                       0);
+                    oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(vop), as_bf16x8(plo[s]), oacc[dt], 0, 0,
+                                                                       0);
+                }
+            }
+        };
+        auto init_row = [&]() {
             m = -INFINITY;
             lp = 0.f;
 #pragma unroll
             for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
+        };
+
+        // One pass over the segment's key tiles.  Fast path: P is rounded once to fp16
+        // (11 significant bits) against V^T in fp16.  Exact path: P is fed as two
+        // bf16 operands against V^T in bf16, keeping ~16 bits of p; a single
+        // bf16 rounding of p would use most of the output's error budget on top
+        // of the bf16 output rounding.  ids_loaded: the ids of the segment's
+        // first tile are already in bid[0] (the first pass; the exact pass
+        // reloads them).
+        auto run = [&](auto half, auto ids_loaded) {
+            constexpr bool kIdsLoaded = decltype(ids_loaded)::value;
+            init_row();
             if constexpr (kStageSets == 2) {
                 if constexpr (!kIdsLoaded) load_ids(kt_begin, Set0{});
                 load_ids(kt_begin + 1, Set1{});
                 stage(kt_begin, Set0{});
                 load_ids(kt_begin + 2, Set0{});
-                commit(0, half, Set0{});
+                commit(0, 0, half, Set0{});
                 stage(kt_begin + 1, Set1{});
                 load_ids(kt_begin + 3, Set1{});
             } else {
                 if constexpr (!kIdsLoaded) load_ids(kt_begin, Set0{});
                 stage(kt_begin, Set0{});
                 load_ids(kt_begin + 1, Set0{});
-                commit(0, half, Set0{});
+                commit(0, 0, half, Set0{});
             }
             __syncthreads();
 
@@ -540,126 +667,13 @@ prefill_kernel(PrefillArgs a) {
                     stage(kt + 1, Set0{});
                     load_ids(kt + 2, Set0{});
                 }
-                const int key0 = kt * kKeys;
-                // S^T = K Q^T over this tile: 2 key tiles of 32 x 8 dim steps of 16.
-                // sacc[mt][4b + e] is the score of key 32mt + 8b + 4h + e.
                 f32x16_t sacc[2];
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) sacc[mt][v] = 0.f;
-                // operands read one step ahead of the products that use them
-                const uint16_t* kl = &k_lds[buf][lr * kKStride + 8 * h];
-                auto k_operand = [&](int i) {              // step i: dim step i / 2, key tile i % 2
-                    return *reinterpret_cast<const u32x4_t*>(kl + (i & 1) * 32 * kKStride + 16 * (i >> 1));
-                };
-                u32x4_t ka[2];
-                ka[0] = k_operand(0);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (i + 1 < 16) ka[(i + 1) & 1] = k_operand(i + 1);
-                    sacc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[i & 1]), as_bf16x8(qop[i >> 1]),
-                                                                          sacc[i & 1], 0, 0, 0);
-                }
-
-                // online softmax of the row.  The max is taken on raw scores (scale
-                // > 0) and the scale folded into the exponent: p = 2^(s *
-                // scale_log2 - m).  The reference m is raised only when a tile's
-                // maximum exceeds it by more than kSlack (log2 units), so p <=
-                // 2^kSlack (exact in fp16 and fp32) and the accumulator rescale is
-                // rare after the first tiles; the result is the same softmax, as O
-                // and l share the reference.
-                if (key0 + kKeys > kmin) {                 // a row's limit falls in this tile
-#pragma unroll
-                    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                        for (int v = 0; v < 16; ++v)
-                            if (key0 + 32 * mt + 8 * (v >> 2) + 4 * h + (v & 3) >= kend) sacc[mt][v] = -INFINITY;
-                }
-                float mx = -INFINITY;
-#pragma unroll
-                for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-                    for (int v = 0; v < 16; v += 4)
-                        mx = maximum(maximum(mx, maximum(sacc[mt][v], sacc[mt][v + 1])),
-                                     maximum(sacc[mt][v + 2], sacc[mt][v + 3]));
-                mx = max_across_halves(mx);
-                const float mtile = mx * a.scale_log2;
-                const bool bump = mtile > m + kSlack;
-                const float mn = bump ? mtile : m;
-                const bool none = mn == -INFINITY;         // nothing visible yet in this row
-                const float msafe = none ? 0.f : mn;       // then every score is -inf and p = 0
-                const float alpha = bump ? __builtin_amdgcn_exp2f(m - mn) : 1.f;
-                const bool rescale = bump && m != -INFINITY;
-                m = mn;
-                // P^T as the B operand of key step s (keys 16s .. 16s+15): the 8
-                // scores sacc[s / 2][8 (s % 2) .. +8] of this lane, i.e. keys 16s +
-                // 8c + 4h + e for c, e -- the k order the V^T operand follows
                 u32x4_t phi[4], plo[4];
-                float sum = 0.f;
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    float pv[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        pv[e] = __builtin_amdgcn_exp2f(fmaf(sacc[s >> 1][8 * (s & 1) + e], a.scale_log2, -msafe));
-                    uint32_t hw[4], lw[4];
-#pragma unroll
-                    for (int e2 = 0; e2 < 4; ++e2) {
-                        if constexpr (kHalf) {
-                            // the row sum adds the fp16 p that P.V uses
-                            hw[e2] = pack_f16x2(pv[2 * e2], pv[2 * e2 + 1]);
-                            sum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hw[e2]), f16x2_t{1.f16, 1.f16}, sum,
-                                                         false);
-                        } else {
-                            // p - hi is exact in fp32 and lo keeps p to ~2^-16 relative
-                            const uint32_t u0 = __float_as_uint(pv[2 * e2]), u1 = __float_as_uint(pv[2 * e2 + 1]);
-                            hw[e2] = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
-                            lw[e2] = pack_bf16x2(pv[2 * e2] - __uint_as_float(u0 & 0xffff0000u),
-                                                 pv[2 * e2 + 1] - __uint_as_float(u1 & 0xffff0000u));
-                            sum += pv[2 * e2] + pv[2 * e2 + 1];
-                        }
-                    }
-                    phi[s] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-                    if constexpr (!kHalf) plo[s] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
-                }
-                lp = lp * alpha + sum;
-                if (__builtin_amdgcn_ballot_w64(rescale)) {
-#pragma unroll
-                    for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
-                }
-
-                // O^T += V^T P^T: 4 key steps x 4 dim tiles of 32 (x hi and lo
-                // parts of P on the exact path).  The V^T operand of (dim tile dt,
-                // key step s): dim 32dt + l % 32, keys 16s + 4h .. +4 and
-                // 16s + 8 + 4h .. +4, i.e. 4-key runs 4s + h and 4s + 2 + h of the
-                // row, each swizzled by bit 4 of the dim (see commit).
-                const int sw = (lr >> 4) & 1;
-                const uint16_t* vl = &v_lds[buf][lr * kVStride];
-                auto v_operand = [&](int i) {              // step i: key step i / 4, dim tile i % 4
-                    const uint16_t* vrow = vl + (i & 3) * 32 * kVStride;
-                    const int s = i >> 2;
-                    const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow + 4 * ((4 * s + h) ^ sw));
-                    const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 4 * ((4 * s + 2 + h) ^ sw));
-                    return u32x4_t{v0.x, v0.y, v1.x, v1.y};
-                };
-                u32x4_t va[2];
-                va[0] = v_operand(0);
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    if (i + 1 < 16) va[(i + 1) & 1] = v_operand(i + 1);
-                    const int dt = i & 3, s = i >> 2;
-                    if constexpr (kHalf) {
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(va[i & 1]), as_f16x8(phi[s]), oacc[dt],
-                                                                          0, 0, 0);
-                    } else {
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[i & 1]), as_bf16x8(phi[s]),
-                                                                           oacc[dt], 0, 0, 0);
-                        oacc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(va[i & 1]), as_bf16x8(plo[s]),
-                                                                           oacc[dt], 0, 0, 0);
-                    }
-                }
-                if (kt + 1 < kt_end) commit(buf ^ 1, half, std::integral_constant<int, kStageSets == 2 ? A : 0>{});
+                s_products(buf, sacc);
+                softmax(kt, sacc, phi, plo, half);
+                pv_products(buf, phi, plo, half);
+                if (kt + 1 < kt_end)
+                    commit(buf ^ 1, buf ^ 1, half, std::integral_constant<int, kStageSets == 2 ? A : 0>{});
                 __syncthreads();
             };
             for (int kt = kt_begin; kt < kt_end; kt += 2) {
