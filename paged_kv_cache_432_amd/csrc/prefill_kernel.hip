@@ -17,7 +17,8 @@
 //     32 rows each, one 32-row MFMA tile.
 //   * K/V advance in tiles of 64 keys (4 cache blocks), double-buffered in LDS:
 //     K row-major with a padded row (conflict-free 16-byte operand reads), V
-//     transposed (dims x keys), as the P.V contraction runs over keys.
+//     transposed (dims x keys), as the P.V contraction runs over keys, with the
+//     keys of each 16-key group ordered so that an operand is one 16-byte read.
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K rows from LDS, B = the
 //     wave's query rows held in registers): lane l then holds query row l % 32
 //     and 16 of the tile's 32 keys per key tile, the lane pair (l, l ^ 32)
@@ -72,7 +73,7 @@ constexpr int kRowsPerWave = 32;
 static_assert(kWaves * kRowsPerWave == kPrefillRows, "tile rows");
 constexpr int kKeys = 64;                    // keys per K/V tile
 constexpr int kKStride = kHeadDim + 8;       // bf16 per K row in LDS (272 B)
-constexpr int kVStride = kKeys + 4;          // bf16 per V^T row in LDS (136 B)
+constexpr int kVStride = kKeys + 8;          // bf16 per V^T row in LDS (144 B)
 constexpr int kKTileElems = kKeys * kKStride;
 constexpr int kVTileElems = kHeadDim * kVStride;
 constexpr int kThreads = kWaves * kWave;
@@ -80,6 +81,9 @@ constexpr int kThreads = kWaves * kWave;
 // so every thread stages kBlkPerThr of the tile's 4 blocks.
 constexpr int kThrGroups = kThreads / 256;
 constexpr int kBlkPerThr = 4 / kThrGroups;
+// V staging: a tile's 4 blocks x 2 quad pairs (quads 0 and 2, or 1 and 3, of a
+// block) over the waves, kVPerThr of them per thread.
+constexpr int kVPerThr = 8 / kWaves;
 // Sets of staging registers.  With one (the default), a tile's loads are issued
 // as the tile before it starts and committed at its end, a whole tile of
 // compute later.  With two (8-wave workgroups only, a build parameter kept for
@@ -375,15 +379,20 @@ prefill_kernel(PrefillArgs a) {
         f32x16_t oacc[4];                                  // O^T: oacc[dt][4b + e] = dim 32dt + 8b + 4h + e
 
         // ---- K/V tile staging.  K: 1024 16-byte chunks (row, 16-byte part), two per
-        // thread, stored row-major.  V: thread (dim pair dp, key quads kq, kq + 8)
-        // loads the 4-byte (dims 2dp, 2dp+1) word of each key of its quads -- a
-        // wave reads whole 256-byte rows -- and packs them into 4-key runs of the
-        // two V^T rows, stored with 8-byte writes.  A wave's loads of tile kt all
-        // fall in cache blocks 4kt + w4 and 4kt + w4 + 2 (w4 = wave / 4), at
-        // offsets within the block that do not change from tile to tile; each
-        // block is read through a buffer resource whose size is its valid keys'
-        // rows, so that keys past the range read as zeros (never stale data)
-        // without a branch or a per-lane test.
+        // thread, stored row-major.  V^T: each 16-key group of a row (one cache
+        // block) is stored as two 16-byte chunks, keys 0-3 and 8-11, then 4-7
+        // and 12-15: the 8 keys that lane half h feeds to one P.V step (see
+        // pv_products), so each operand is one 16-byte read, and rows 144 bytes
+        // apart put the 16 rows such a read covers per cycle on all banks.
+        // Thread (dim pair dp, wave w) loads, of block w / 2 (w / 2 and
+        // w / 2 + 2 with 4 waves), the 4-byte (dims 2dp, 2dp+1) word of keys
+        // 4q .. 4q + 3 and 4q + 8 .. 4q + 11 (q = w % 2) -- a wave reads whole
+        // 256-byte rows -- and writes one chunk to each of its two V^T rows.  A
+        // wave's loads of tile kt fall in a fixed set of cache blocks of the
+        // tile, at offsets within the block that do not change from tile to
+        // tile; each block is read through a buffer resource whose size is its
+        // valid keys' rows, so that keys past the range read as zeros (never
+        // stale data) without a branch or a per-lane test.
         const char* kc = reinterpret_cast<const char*>(a.key_cache);
         const char* vc = reinterpret_cast<const char*>(a.value_cache);
         const int32_t* bt = a.block_table + (int64_t)b * a.bt_stride;
@@ -393,11 +402,13 @@ prefill_kernel(PrefillArgs a) {
         const int dp = tid & 63, kq = tid >> 6;
         const int w4 = __builtin_amdgcn_readfirstlane(tid >> 8);   // the same for a whole wave
         const uint32_t koff = ((tid >> 4) & 15) * tok_bytes + head_off + (tid & 15) * 16;
-        const uint32_t voff = 4 * (kq & 3) * tok_bytes + head_off + dp * 4;
+        const int vq = kq & 1;                             // V quad pair, the same for a whole wave
+        const uint32_t voff = 4 * vq * tok_bytes + head_off + dp * 4;
+        auto v_block = [&](int jv) { return __builtin_amdgcn_readfirstlane((kq >> 1) + (kWaves / 2) * jv); };
         // staging registers, kStageSets sets of them (the set chosen at compile
         // time, see run)
         u32x4_t kreg[kStageSets][kBlkPerThr];
-        uint32_t vw[kStageSets][kBlkPerThr][4];
+        uint32_t vw[kStageSets][kVPerThr][8];
         // Block ids, per staging set: bid[S] holds (lanes 0-3) the ids of the
         // next tile staged into set S, loaded when the set's previous tile was
         // staged, and broadcast with v_readlane, so that a tile's 10 loads issue
@@ -446,11 +457,21 @@ prefill_kernel(PrefillArgs a) {
                 const int nrec = __builtin_amdgcn_readfirstlane(
                     live ? min(max(kend_wg - blk * kBlock, 0), kBlock) * (int)tok_bytes : 0);
                 const rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + off), (short)0, nrec, kRsrcWord3);
-                const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
                 kreg[S][j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rk, (int)koff, 0, 0));
+            }
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    vw[S][j][i] = __builtin_amdgcn_raw_buffer_load_b32(rv, (int)(voff + i * tok_bytes), 0, 0);
+            for (int jv = 0; jv < kVPerThr; ++jv) {
+                const int vb = v_block(jv);
+                const int blk = 4 * kt + vb;
+                const int64_t id = __builtin_amdgcn_readlane(bid[S], vb);
+                const int64_t off = min(max(id, (int64_t)0), a.num_blocks - 1) * blk_bytes;
+                const int nrec = __builtin_amdgcn_readfirstlane(
+                    live ? min(max(kend_wg - blk * kBlock, 0), kBlock) * (int)tok_bytes : 0);
+                const rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vc + off), (short)0, nrec, kRsrcWord3);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    vw[S][jv][i] = __builtin_amdgcn_raw_buffer_load_b32(
+                        rv, (int)(voff + ((i & 3) + 8 * (i >> 2)) * tok_bytes), 0, 0);
             }
         };
         // V^T goes to LDS as bf16 (exact path) or fp16 (fast path).  The fp16
@@ -468,28 +489,31 @@ prefill_kernel(PrefillArgs a) {
                 *reinterpret_cast<u32x4_t*>(&k_lds[kbuf][(c >> 4) * kKStride + (c & 15) * 8]) = kreg[S][j];
             }
 #pragma unroll
-            for (int j = 0; j < kBlkPerThr; ++j) {
-                const uint32_t* w = vw[S][j];
-                u32x2_t even, odd;
+            for (int jv = 0; jv < kVPerThr; ++jv) {
+                const uint32_t* w = vw[S][jv];
+                u32x4_t even, odd;                         // V^T rows 2dp and 2dp + 1
                 if constexpr (kHalf) {
-                    float e[4], o[4];
+                    float e[8], o[8];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
+                    for (int i = 0; i < 8; ++i) {
                         e[i] = bf16_lo(w[i]);
                         o[i] = bf16_hi(w[i]);
                         vmax = maximum(vmax, maximum(fabsf(e[i]), fabsf(o[i])));
                     }
-                    even = u32x2_t{pack_f16x2(e[0], e[1]), pack_f16x2(e[2], e[3])};
-                    odd = u32x2_t{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3])};
+                    even = u32x4_t{pack_f16x2(e[0], e[1]), pack_f16x2(e[2], e[3]), pack_f16x2(e[4], e[5]),
+                                   pack_f16x2(e[6], e[7])};
+                    odd = u32x4_t{pack_f16x2(o[0], o[1]), pack_f16x2(o[2], o[3]), pack_f16x2(o[4], o[5]),
+                                  pack_f16x2(o[6], o[7])};
                 } else {
-                    even = u32x2_t{(w[0] & 0xffffu) | (w[1] << 16), (w[2] & 0xffffu) | (w[3] << 16)};
-                    odd = u32x2_t{(w[0] >> 16) | (w[1] & 0xffff0000u), (w[2] >> 16) | (w[3] & 0xffff0000u)};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        even[i] = (w[2 * i] & 0xffffu) | (w[2 * i + 1] << 16);
+                        odd[i] = (w[2 * i] >> 16) | (w[2 * i + 1] & 0xffff0000u);
+                    }
                 }
-                // 4-key run q of V^T row d sits at run q ^ ((d >> 4) & 1): the 16
-                // rows 2dp a write instruction covers per cycle then span all banks
-                uint16_t* vt = &v_lds[vbuf][(2 * dp) * kVStride + 4 * ((kq + 4 * kThrGroups * j) ^ ((dp >> 3) & 1))];
-                *reinterpret_cast<u32x2_t*>(vt) = even;
-                *reinterpret_cast<u32x2_t*>(vt + kVStride) = odd;
+                uint16_t* vt = &v_lds[vbuf][(2 * dp) * kVStride + 8 * (2 * v_block(jv) + vq)];
+                *reinterpret_cast<u32x4_t*>(vt) = even;
+                *reinterpret_cast<u32x4_t*>(vt + kVStride) = odd;
             }
         };
 
@@ -587,18 +611,12 @@ prefill_kernel(PrefillArgs a) {
         // O^T += V^T P^T with the tile in V buffer vbuf: 4 key steps x 4 dim tiles
         // of 32 (x hi and lo parts of P on the exact path).  The V^T operand of
         // (dim tile dt, key step s): dim 32dt + l % 32, keys 16s + 4h .. +4 and
-        // 16s + 8 + 4h .. +4, i.e. 4-key runs 4s + h and 4s + 2 + h of the row,
-        // each swizzled by bit 4 of the dim (see commit).
+        // 16s + 8 + 4h .. +4, i.e. chunk 2s + h of the row (see the staging).
         auto pv_products = [&](int vbuf, const u32x4_t (&phi)[4], const u32x4_t (&plo)[4], auto half) {
             constexpr bool kHalf = decltype(half)::value;
-            const int sw = (lr >> 4) & 1;
-            const uint16_t* vl = &v_lds[vbuf][lr * kVStride];
+            const uint16_t* vl = &v_lds[vbuf][lr * kVStride + 8 * h];
             auto v_operand = [&](int i) {                  // step i: key step i / 4, dim tile i % 4
-                const uint16_t* vrow = vl + (i & 3) * 32 * kVStride;
-                const int s = i >> 2;
-                const u32x2_t v0 = *reinterpret_cast<const u32x2_t*>(vrow + 4 * ((4 * s + h) ^ sw));
-                const u32x2_t v1 = *reinterpret_cast<const u32x2_t*>(vrow + 4 * ((4 * s + 2 + h) ^ sw));
-                return u32x4_t{v0.x, v0.y, v1.x, v1.y};
+                return *reinterpret_cast<const u32x4_t*>(vl + (i & 3) * 32 * kVStride + 16 * (i >> 2));
             };
             u32x4_t va[2];
             va[0] = v_operand(0);
