@@ -66,6 +66,7 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kWaves = kPrefillWaves;
@@ -109,6 +110,9 @@ __device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
 }
 
 constexpr int kRec = 132;                    // record floats per row: 128 O, max, sum, 2 unused
+// A record's format flag (0: fp16 normalised rows, 1: fp32 unnormalised rows),
+// after its (max, sum) pairs.
+constexpr int kRecFlag = kPrefillRows * (kHeadDim + 2);
 constexpr uint32_t kRsrcWord3 = 0x00020000u; // raw buffer, 32-bit data format
 constexpr float kSlack = 8.f;                // log2 headroom of the softmax reference max
 
@@ -702,18 +706,22 @@ prefill_kernel(PrefillArgs a) {
 
         run(std::true_type{}, std::true_type{});
         // a V magnitude beyond fp16 (or a NaN, which the exact path propagates)
-        if (__syncthreads_or(!(vmax <= 65504.f))) run(std::false_type{}, std::false_type{});
+        const bool exact = __syncthreads_or(!(vmax <= 65504.f));
+        if (exact) run(std::false_type{}, std::false_type{});
         // ---- finish: lane holds dims 32dt + 8b + 4h .. +4 of its row.
         //  * A tile within the share normalises its rows to bf16 and writes them
         //    through LDS (the K/V buffers are free once every wave has passed the
         //    last barrier of the loop): each wave stages its 32 rows, then writes
         //    4 whole rows per store instruction, 16 bytes a lane.
         //  * A segment of a tile that crosses a share boundary writes its record
-        //    (unnormalised rows, max, sum) in the workgroup's record 0 if the
-        //    segment is its first, else in record 1, in the order of the
-        //    accumulator fragments: store (dt, b) of a wave covers 1 KB of
-        //    consecutive floats.  The segment holding the tile's first unit
-        //    lists the tile for the merge kernel.
+        //    (rows, max, sum) in the workgroup's record 0 if the segment is its
+        //    first, else in record 1, in the order of the accumulator fragments.
+        //    Fast path: the rows normalised by their sum, in fp16 (every V
+        //    magnitude was below 65504, so is every normalised value; 11
+        //    significant bits); store (dt, b) of a wave covers 512 consecutive
+        //    bytes.  Exact path: the unnormalised rows in fp32, 1 KB per store.
+        //    A flag after the record's (max, sum) pairs says which.  The segment
+        //    holding the tile's first unit lists the tile for the merge kernel.
         {
             const float l = sum_across_halves(lp);
             if (!split) {
@@ -745,15 +753,33 @@ prefill_kernel(PrefillArgs a) {
                     }
                 }
                 __syncthreads();                           // staging read before the next segment's commit
-            } else if (active) {
+            } else {
                 float* rec = a.part + ((int64_t)blockIdx.x * 2 + (first ? 0 : 1)) * kPrefillRows * kRec;
+                if (active) {
+                    if (!exact) {
+                        const float inv = l > 0.f ? 1.f / l : 0.f;
+                        uint32_t* rh = reinterpret_cast<uint32_t*>(rec);
 #pragma unroll
-                for (int dt = 0; dt < 4; ++dt)
+                        for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-                    for (int b4 = 0; b4 < 4; ++b4)
-                        *reinterpret_cast<f32x4_t*>(rec + ((wave * 16 + 4 * dt + b4) * kWave + lane) * 4) =
-                            f32x4_t{oacc[dt][4 * b4], oacc[dt][4 * b4 + 1], oacc[dt][4 * b4 + 2], oacc[dt][4 * b4 + 3]};
-                if (h == 0) *reinterpret_cast<float2*>(rec + kPrefillRows * kHeadDim + 2 * r) = make_float2(m, l);
+                            for (int b4 = 0; b4 < 4; ++b4) {
+                                const f32x16_t& v = oacc[dt];
+                                *reinterpret_cast<u32x2_t*>(rh + ((wave * 16 + 4 * dt + b4) * kWave + lane) * 2) =
+                                    u32x2_t{pack_f16x2(v[4 * b4] * inv, v[4 * b4 + 1] * inv),
+                                            pack_f16x2(v[4 * b4 + 2] * inv, v[4 * b4 + 3] * inv)};
+                            }
+                    } else {
+#pragma unroll
+                        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+                            for (int b4 = 0; b4 < 4; ++b4)
+                                *reinterpret_cast<f32x4_t*>(rec + ((wave * 16 + 4 * dt + b4) * kWave + lane) * 4) =
+                                    f32x4_t{oacc[dt][4 * b4], oacc[dt][4 * b4 + 1], oacc[dt][4 * b4 + 2],
+                                            oacc[dt][4 * b4 + 3]};
+                    }
+                    if (h == 0) *reinterpret_cast<float2*>(rec + kPrefillRows * kHeadDim + 2 * r) = make_float2(m, l);
+                }
+                if (tid == 0) rec[kRecFlag] = exact ? 1.f : 0.f;
             }
         }
         // list entry: first slot, slots | (record of the first slot) << 24, first
@@ -782,9 +808,11 @@ prefill_kernel(PrefillArgs a) {
 // M = max_p m_p, out = sum_p 2^(m_p - M) O_p / sum_p 2^(m_p - M) l_p, taken in
 // one pass with a running max.  One workgroup per 32-row wave block of a
 // listed (tile, KV head); the records hold each block's rows in accumulator
-// fragment order (16 fragments of 64 lanes x 4 floats), so thread t reads
-// fragments t / 64 + 4i (i < 4) of lane t % 64, 1 KB per wave and fragment,
-// and stages its bf16 results in LDS so that whole rows leave together.
+// fragment order (16 fragments of 64 lanes x 4 values, fp16 normalised rows
+// or fp32 unnormalised ones by the record's flag), so thread t reads
+// fragments t / 64 + 4i (i < 4) of lane t % 64, contiguous per wave and
+// fragment, and stages its bf16 results in LDS so that whole rows leave
+// together.
 template <int G>
 __global__ void __launch_bounds__(256)
 prefill_merge_kernel(PrefillArgs a) {
@@ -810,9 +838,18 @@ prefill_merge_kernel(PrefillArgs a) {
         const float* rec = a.part + (wg * 2 + (p == 0 ? rec0 : 0)) * kPrefillRows * kRec;
         const float2 ml = *reinterpret_cast<const float2*>(rec + kPrefillRows * kHeadDim + 2 * r);
         f32x4_t ov[4];
+        if (rec[kRecFlag] == 0.f) {                    // fp16 rows normalised by their sum
+            // read as an fp16 x 4 vector: hipcc 7.2 compiles a bit cast of one
+            // component of a loaded vector (v.y) from the vector's first component
+            const f16x4_t* rh = reinterpret_cast<const f16x4_t*>(rec);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            ov[i] = *reinterpret_cast<const f32x4_t*>(rec + ((w * 16 + j + 4 * i) * kWave + lane) * 4);
+            for (int i = 0; i < 4; ++i)
+                ov[i] = __builtin_convertvector(rh[(w * 16 + j + 4 * i) * kWave + lane], f32x4_t) * ml.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                ov[i] = *reinterpret_cast<const f32x4_t*>(rec + ((w * 16 + j + 4 * i) * kWave + lane) * 4);
+        }
         const float mn = fmaxf(mrun, ml.x);
         const float wa = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mrun - mn);
         const float wb = mn == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - mn);

@@ -220,6 +220,32 @@ def test_values_beyond_half_range(staging, hq, hkv):
     assert_parity(o, ref, "bf16", f"V x 2^17 in sequence 0, G={hq // hkv}")
 
 
+def test_mixed_record_formats(staging):
+    """The tiles of one long chunk (6000 keys, 512 rows) are cut over several
+    workgroups.  V of keys 4000 and up is scaled by 2^17, so the segments that
+    stage those keys run the exact path and leave fp32 records, while the
+    earlier segments of the same tiles leave fp16 ones; the merge combines
+    both.  Those keys' K (dim 0 = -1000 against a query dim 0 of 10) puts
+    their scores some 1300 log2 units down, so their probabilities are 0 in
+    fp32 and fp64 alike and the outputs keep their usual magnitude."""
+    w = W.custom("mixrec", seq_lens=[6000, 700], query_lens=[512, 700], dtype="bf16", seed=19, causal=True)
+
+    def kv_fn(b, k, v):
+        if b == 0:
+            k[4000:, :, 0] = np.float32(-1000.0)
+            v[4000:] = v[4000:] * np.float32(2.0 ** 17)
+        return k, v
+
+    def q_fn(b, q):
+        if b == 0:
+            q[:, :, 0] = np.float32(10.0)
+        return q
+
+    w = _with_values(w, kv_fn, q_fn)
+    _, out = _run(staging, w)
+    assert_parity(to_numpy(out), oracle.run(w), "bf16", "fp16 and fp32 records in one merge")
+
+
 def test_rising_scores_rescale(staging):
     """Chunk rows whose scores rise along the keys (~40 log2 units over the
     context): the softmax reference is raised, and the accumulators rescaled,
