@@ -1067,13 +1067,12 @@ decode_stream_kernel(DecodeArgs a) {
 //   M = max_p m_p,  out = sum_p 2^(m_p - M) acc_p / sum_p 2^(m_p - M) l_p.
 // One wave per (sequence, head), two dims per lane; `rec_of(p)` gives the
 // record index of piece p of n.
-template <typename Elem, typename RecOf>
-__device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec_of, int lane, Elem* o) {
-    constexpr int kFew = 8;
-    if (n <= kFew) {
-        // Few pieces (the usual case): every load is issued at once -- lane p's
-        // (max, sum) of piece p and this lane's two dims of every piece -- so
-        // the merge takes one round trip to memory.
+// Up to kFew pieces: every load is issued at once -- lane p's (max, sum) of
+// piece p and this lane's two dims of every piece -- so the merge takes one
+// round trip to memory (2 kFew registers for the rows).
+template <int kFew, typename Elem, typename RecOf>
+__device__ __forceinline__ void merge_few(const float* part, int n, RecOf rec_of, int lane, Elem* o) {
+    {
         float2 v[kFew];
 #pragma unroll
         for (int q = 0; q < kFew; ++q)
@@ -1082,7 +1081,7 @@ __device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec
                                    : make_float2(-INFINITY, 0.f);
         float M = ml.x;
 #pragma unroll
-        for (int d = 1; d < kFew; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));   // lanes >= 8 hold -inf
+        for (int d = 1; d < kFew; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));   // lanes >= n hold -inf
         M = readlane_f(M, 0);
         const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
         float lsum = w * ml.y, o0 = 0.f, o1 = 0.f;
@@ -1103,8 +1102,15 @@ __device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec
         } else {
             *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(o0 * inv, o1 * inv);
         }
-        return;
     }
+}
+
+template <typename Elem, typename RecOf>
+__device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec_of, int lane, Elem* o) {
+    // 8 pieces or fewer (the usual case), up to 32 (long contexts cut over
+    // many workgroups), or a loop for more
+    if (n <= 8) return merge_few<8>(part, n, rec_of, lane, o);
+    if (n <= 32) return merge_few<32>(part, n, rec_of, lane, o);
     // pass over the pieces' (max, sum), 64 at a time, one per lane
     float M = -INFINITY;
     for (int p0 = 0; p0 < n; p0 += kWave) {
