@@ -1107,10 +1107,11 @@ __device__ __forceinline__ void merge_few(const float* part, int n, RecOf rec_of
 
 template <typename Elem, typename RecOf>
 __device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec_of, int lane, Elem* o) {
-    // 8 pieces or fewer (the usual case), up to 32 (long contexts cut over
-    // many workgroups), or a loop for more
+    // 8 pieces or fewer (the usual case), up to 24 (long contexts cut over
+    // many workgroups; 48 registers of rows keep the kernel at 8 waves per
+    // SIMD), or a loop for more
     if (n <= 8) return merge_few<8>(part, n, rec_of, lane, o);
-    if (n <= 32) return merge_few<32>(part, n, rec_of, lane, o);
+    if (n <= 24) return merge_few<24>(part, n, rec_of, lane, o);
     // pass over the pieces' (max, sum), 64 at a time, one per lane
     float M = -INFINITY;
     for (int p0 = 0; p0 < n; p0 += kWave) {
