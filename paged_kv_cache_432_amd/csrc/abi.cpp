@@ -577,6 +577,10 @@ pa_status plan_decode(DecodePlan& plan, void* out, const void* query, int64_t q_
         a.waves_per_group = sh.waves;
         a.num_wg = sh.num_wg;
         a.min_quantum = kStreamMinQuantum;
+        // The merge runs one wave per (sequence, query head), 8 resident per
+        // SIMD.  Beyond one round of them (32 per compute unit), a wave takes
+        // two heads of a KV head (group >= 2), one per half.
+        a.merge_pair = group >= 2 && (int64_t)num_seqs * num_heads > 32LL * device_cus();
         if (workspace) {
             a.prefix = reinterpret_cast<int32_t*>(workspace);
             a.part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) +

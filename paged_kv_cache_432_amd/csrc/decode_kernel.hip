@@ -1105,6 +1105,49 @@ __device__ __forceinline__ void merge_few(const float* part, int n, RecOf rec_of
     }
 }
 
+// Two heads per wave, one per 32-lane half: lane half hh merges the pieces
+// rec_of(q, hh) of its head, and lane l holds dims 4 (l % 32) .. +4 of it; o
+// is the lane's head's output row.  n <= kFew <= 32 pieces, every load issued
+// at once, so the merge is one round trip.
+template <int kFew, typename Elem, typename RecOf>
+__device__ __forceinline__ void merge_pair(const float* part, int n, RecOf rec_of, int lane, Elem* o) {
+    const int hh = lane >> 5, ln = lane & 31;
+    f32x4_t v[kFew];
+#pragma unroll
+    for (int q = 0; q < kFew; ++q)
+        v[q] = q < n ? *reinterpret_cast<const f32x4_t*>(part + rec_of(q, hh) * kRec + 4 * ln)
+                     : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const float2 ml = ln < n ? *reinterpret_cast<const float2*>(part + rec_of(ln, hh) * kRec + kHeadDim)
+                             : make_float2(-INFINITY, 0.f);
+    float M = ml.x;
+#pragma unroll
+    for (int d = 1; d < kFew; d <<= 1) M = fmaxf(M, shfl_xor_f(M, d));   // within the half; lanes >= n hold -inf
+    M = hh ? readlane_f(M, 32) : readlane_f(M, 0);
+    const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+    float lsum = w * ml.y;
+#pragma unroll
+    for (int d = 1; d < kFew; d <<= 1) lsum += shfl_xor_f(lsum, d);
+    lsum = hh ? readlane_f(lsum, 32) : readlane_f(lsum, 0);
+    float o0 = 0.f, o1 = 0.f, o2 = 0.f, o3 = 0.f;
+#pragma unroll
+    for (int q = 0; q < kFew; ++q) {
+        if (q < n) {
+            const float wq = hh ? readlane_f(w, 32 + q) : readlane_f(w, q);
+            o0 = fmaf(wq, v[q].x, o0);
+            o1 = fmaf(wq, v[q].y, o1);
+            o2 = fmaf(wq, v[q].z, o2);
+            o3 = fmaf(wq, v[q].w, o3);
+        }
+    }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    if constexpr (sizeof(Elem) == 2) {
+        *reinterpret_cast<u32x2_t*>(o + 4 * ln) =
+            u32x2_t{pack_bf16x2(o0 * inv, o1 * inv), pack_bf16x2(o2 * inv, o3 * inv)};
+    } else {
+        *reinterpret_cast<f32x4_t*>(o + 4 * ln) = f32x4_t{o0 * inv, o1 * inv, o2 * inv, o3 * inv};
+    }
+}
+
 template <typename Elem, typename RecOf>
 __device__ __forceinline__ void merge_pieces(const float* part, int n, RecOf rec_of, int lane, Elem* o) {
     // 8 pieces or fewer (the usual case), up to 24 (long contexts cut over
@@ -1194,30 +1237,42 @@ __device__ __forceinline__ void append_head(const DecodeArgs& a, int64_t b, int 
     *reinterpret_cast<u32x4_t*>(dst) = *reinterpret_cast<const u32x4_t*>(src);
 }
 
-template <typename Elem, bool AP = false>
+// The stream mode's split merge: one wave per (sequence, query head), or (PR)
+// per (sequence, two query heads of one KV head), a head to each half of the
+// wave, which halves the waves of a large batch.  A pair whose sequence was cut
+// into more than 8 pieces is merged one head after the other by the whole wave.
+template <typename Elem, bool AP = false, bool PR = false>
 __global__ void __launch_bounds__(256)
 merge_stream_kernel(DecodeArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int Hq = a.num_heads;
+    const int HI = PR ? Hq / 2 : Hq;                   // items per sequence
     const int64_t item = (int64_t)blockIdx.x * kWavesPerGroup + wave;
-    const int64_t b = item / Hq;
-    const int h = (int)(item % Hq);
+    const int64_t b = item / HI;
+    const int hi = (int)(item % HI);
     if (b >= a.num_seqs) return;
     if constexpr (AP)
-        if (h < a.num_kv_heads) append_head(a, b, h, lane);
+        if (hi < a.num_kv_heads) append_head(a, b, hi, lane);
     const int G = Hq / a.num_kv_heads;
     const int W = a.waves_per_group;
     const int NG = a.num_kv_heads / W;
-    const int kvh = h / G, hg = h % G, grp = kvh / W, wi = kvh % W;
+    const int h0 = PR ? 2 * hi : hi;                   // the wave's (first) head
+    const int kvh = h0 / G, hg = h0 % G, grp = kvh / W, wi = kvh % W;
     const int64_t row = decode_row(a, b);
     if (row < 0) return;
     const int32_t pb = a.prefix[b];
     const int nblk = a.prefix[b + 1] - pb;
-    Elem* o = reinterpret_cast<Elem*>(a.out) + (row * Hq + h) * kHeadDim;
+    Elem* o = reinterpret_cast<Elem*>(a.out) + (row * Hq + h0) * kHeadDim;
     if (nblk == 0) {                                   // empty sequence: zeros
-        if constexpr (sizeof(Elem) == 2) *reinterpret_cast<uint32_t*>(o + 2 * lane) = 0u;
-        else *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(0.f, 0.f);
+        if constexpr (PR) {
+            Elem* oh = o + (lane >> 5) * kHeadDim + 4 * (lane & 31);
+            if constexpr (sizeof(Elem) == 2) *reinterpret_cast<u32x2_t*>(oh) = u32x2_t{0u, 0u};
+            else *reinterpret_cast<f32x4_t*>(oh) = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        } else {
+            if constexpr (sizeof(Elem) == 2) *reinterpret_cast<uint32_t*>(o + 2 * lane) = 0u;
+            else *reinterpret_cast<float2*>(o + 2 * lane) = make_float2(0.f, 0.f);
+        }
         return;
     }
     const int64_t units = (int64_t)a.prefix[a.num_seqs] * NG;
@@ -1227,13 +1282,22 @@ merge_stream_kernel(DecodeArgs a) {
     const int64_t w_lo = S / Q, w_hi = (E - 1) / Q;
     if (w_lo == w_hi) return;                          // one workgroup wrote it whole
     const bool lo_is_last = S != w_lo * Q;             // the piece in w_lo is that workgroup's second
-    merge_pieces<Elem>(a.part, (int)(w_hi - w_lo + 1),
-                       [&](int p) {
-                           const int64_t w = w_lo + p;
-                           const int slot = (p == 0 && lo_is_last) ? 1 : 0;
-                           return (((w * 2 + slot) * W + wi) * G + hg);
-                       },
-                       lane, o);
+    const int n = (int)(w_hi - w_lo + 1);
+    auto rec = [&](int p, int x) {                     // piece p of head h0 + x
+        const int64_t w = w_lo + p;
+        const int slot = (p == 0 && lo_is_last) ? 1 : 0;
+        return (((w * 2 + slot) * W + wi) * G + hg + x);
+    };
+    if constexpr (PR) {
+        if (n <= 8) {
+            merge_pair<8, Elem>(a.part, n, rec, lane, o + (lane >> 5) * kHeadDim);
+        } else {
+            merge_pieces<Elem>(a.part, n, [&](int p) { return rec(p, 0); }, lane, o);
+            merge_pieces<Elem>(a.part, n, [&](int p) { return rec(p, 1); }, lane, o + kHeadDim);
+        }
+    } else {
+        merge_pieces<Elem>(a.part, n, [&](int p) { return rec(p, 0); }, lane, o);
+    }
 }
 
 
@@ -1255,9 +1319,15 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t mitems = (int64_t)a.num_seqs * a.num_heads;
-        hipLaunchKernelGGL((merge_stream_kernel<Elem, AP>),
-                           dim3((unsigned)((mitems + kWavesPerGroup - 1) / kWavesPerGroup)), dim3(256), 0,
-                           stream, a);
+        if (a.merge_pair) {
+            hipLaunchKernelGGL((merge_stream_kernel<Elem, AP, true>),
+                               dim3((unsigned)((mitems / 2 + kWavesPerGroup - 1) / kWavesPerGroup)), dim3(256), 0,
+                               stream, a);
+        } else {
+            hipLaunchKernelGGL((merge_stream_kernel<Elem, AP>),
+                               dim3((unsigned)((mitems + kWavesPerGroup - 1) / kWavesPerGroup)), dim3(256), 0,
+                               stream, a);
+        }
         return hipGetLastError();
     }
     if constexpr (F8 || AP) return hipErrorInvalidValue; // an fp8 cache and append mode: stream mode only

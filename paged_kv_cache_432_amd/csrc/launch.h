@@ -105,6 +105,7 @@ struct DecodeArgs {
     int32_t num_wg;                // grid size: workgroups resident at once
     int32_t min_quantum;           // fewest blocks per workgroup
     int32_t* prefix;               // [num_seqs + 1] blocks-per-KV-head prefix (written, then read)
+    int32_t merge_pair;            // nonzero: the split merge takes two query heads per wave
     // partial records (split sequences only)
     float* part;
     // Append mode (bf16 stream decode, internal dtype 3): sequence b's newest

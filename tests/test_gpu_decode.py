@@ -96,6 +96,34 @@ def test_stream_mode_edges(staging, lens):
     assert_parity(o, ref, "bf16", f"stream {len(lens)} seqs")
 
 
+@pytest.mark.parametrize("dtype,form", [("bf16", "decode"), ("bf16", "append"), ("f32", "decode")])
+def test_paired_merge(staging, dtype, form):
+    """More (sequence, query head) pairs than one round of merge waves (32 per
+    compute unit) with a group of 4: the split merge takes two heads of a KV
+    head per wave.  Short sequences (one or two pieces) and empty ones, beside
+    sequences cut into a few pieces, into 9-24 and into more than 64 (which
+    the pair merges one head after the other)."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    n = max(1100, 2 * cus + 64)
+    rng = np.random.default_rng(99)
+    lens = rng.integers(1, 300, n).astype(np.int32)
+    lens[::53] = 0
+    lens[7], lens[500], lens[900] = 65536, 6000, 2000
+    assert n * 16 > 32 * cus
+    w = W.custom("pairs", seq_lens=lens, num_heads=16, num_kv_heads=4, dtype=dtype, seed=99, sigma=0.5)
+    dw = staging.DeviceWorkload(w)
+    if form == "append":
+        out = dw.decode_append()
+    else:
+        dw.scatter_new()
+        out = dw.decode()
+    torch.cuda.synchronize()
+    o = to_numpy(out)
+    for b in np.nonzero(lens == 0)[0]:
+        assert np.all(o[b] == 0)
+    assert_parity(o, oracle.run(w), dtype, f"paired merge, {dtype} {form}")
+
+
 def test_many_sequences_use_partitions(staging):
     """Past 4096 sequences the automatic choice is fixed partitions."""
     import paged_kv_cache_432_amd as pa
