@@ -26,9 +26,9 @@ peak and the decodes against HBM); and the headline batch over fp8 caches
 
 With --workload chunked_prefill_mix the headline step is the scatter plus one
 pa_chunked_prefill call over 4 prefill chunks and 96 decodes.  With --kv-cache
-fp8 the caches hold E4M3 codes (--kv-cache e5m2: E5M2 codes): the step is
-pa_slot_mapping_and_cache_fp8 and pa_decode_fp8, and KV bytes count one byte
-per element.
+fp8 the caches hold E4M3 codes (--kv-cache e5m2: E5M2 codes): the step is one
+pa_decode_append_fp8 call (--step two-call: pa_slot_mapping_and_cache_fp8,
+then pa_decode_fp8), and KV bytes count one byte per element.
 """
 from __future__ import annotations
 
@@ -66,11 +66,11 @@ def parse():
                             "chunked_prefill_mix"])
     p.add_argument("--partition-tokens", type=int, default=0)
     p.add_argument("--kv-cache", default="bf16", choices=["bf16", "fp8", "e5m2"],
-                   help="fp8: the caches hold E4M3 codes (pa_slot_mapping_and_cache_fp8 / pa_decode_fp8); "
-                        "e5m2: E5M2 codes through the same calls' _ex forms")
+                   help="fp8: the caches hold E4M3 codes (pa_decode_append_fp8, or pa_slot_mapping_and_cache_fp8 "
+                        "/ pa_decode_fp8); e5m2: E5M2 codes through the same calls' format argument")
     p.add_argument("--step", default="append", choices=["append", "two-call"],
-                   help="append: the step is one pa_decode_append call (bf16/fp32 caches, stream mode); "
-                        "two-call: pa_slot_mapping_and_cache, then pa_decode")
+                   help="append: the step is one pa_decode_append (fp8: pa_decode_append_fp8) call, stream mode; "
+                        "two-call: pa_slot_mapping_and_cache(_fp8), then pa_decode(_fp8)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-probes", action="store_true")
     p.add_argument("--no-extra", action="store_true",
@@ -545,7 +545,7 @@ def measure_decode(w, steps: int, warmup: int, torch, pa, DeviceWorkload, fp8=No
     out = torch.empty_like(dw.query)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    append = step_kind == "append" and not fp8 and pt == 0
+    append = step_kind == "append" and pt == 0
 
     def two_call_step(ev=None):
         # slots and scatter of the step's tokens (one launch), then decode
@@ -606,21 +606,27 @@ def measure_decode(w, steps: int, warmup: int, torch, pa, DeviceWorkload, fp8=No
         "seq_steps_per_s": round(w.num_seqs / (ms_step * 1e-3), 1),
         "append": append,
         "partition_tokens": pt,
-        "step": "pa_decode_append (slots, scatter and decode in one call)" if append
+        "step": (f"pa_decode_append_fp8 ({fp8}): slots, quantising scatter and decode in one call" if fp8
+                 else "pa_decode_append (slots, scatter and decode in one call)") if append
                 else ((f"pa_slot_mapping_and_cache_fp8 + pa_decode_fp8 ({fp8})") if fp8
                       else "pa_slot_mapping_and_cache + pa_decode"),
-        "kernel": f"pa_decode_fp8 ({fp8}): decode_stream_kernel<fp8> + merge_stream_kernel (one call)" if fp8
+        "kernel": (f"pa_decode_append_fp8 ({fp8}): decode_stream_kernel<fp8, append> + merge_stream_kernel "
+                   "(one call)" if append else
+                   f"pa_decode_fp8 ({fp8}): decode_stream_kernel<fp8> + merge_stream_kernel (one call)") if fp8
                   else "pa_decode_append: decode_stream_kernel<append> + merge_stream_kernel (one call)" if append
                   else "pa_decode: decode_stream_kernel + merge_stream_kernel (one call)" if pt == 0
                   else "pa_decode: decode_partition_kernel + merge_partitions_kernel (one call)",
-        "call": "pa_decode_append" if append else ("pa_decode_fp8" if fp8 else "pa_decode"),
+        "call": ("pa_decode_append_fp8" if fp8 else "pa_decode_append") if append
+                else ("pa_decode_fp8" if fp8 else "pa_decode"),
         "call_us_mean": round(float(call_ms.mean()) * 1e3, 2),
         "call_us_median_p10_p90": [round(float(np.percentile(call_ms, q)) * 1e3, 2) for q in (50, 10, 90)],
         "call_GBps": round(call_gbps, 2),
         "call_frac": round(call_gbps / HBM_PEAK_GBPS, 4),
     }
     if two_call_ms is not None:
-        r["two_call_step"] = {"what": "pa_slot_mapping_and_cache + pa_decode, same inputs, after the timed steps",
+        r["two_call_step"] = {"what": ("pa_slot_mapping_and_cache_fp8 + pa_decode_fp8" if fp8
+                                       else "pa_slot_mapping_and_cache + pa_decode") +
+                                      ", same inputs, after the timed steps",
                               "ms_per_step": round(two_call_ms, 5),
                               "GBps": round(kv / (two_call_ms * 1e-3) / 1e9, 2)}
     return r

@@ -358,6 +358,39 @@ pa_status pa_decode_fp8_ex(void *out, const void *query, int64_t q_token_stride,
                            void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * pa_decode_append_fp8 -- the decode step over an fp8 cache in one call, as
+ * pa_decode_append is for bf16 (the article's sections "Paged Attention" and
+ * "Reshape & Cache": this step's K/V rows are written to their slots, then
+ * attention reads the cache).  Row b of key / value (bf16, [num_seqs,
+ * num_kv_heads, head_dim], the newest token of sequence b, at position
+ * seq_lens[b] - 1) is stored as fp8 codes in its slot and attended to with the
+ * rest of the sequence.  The results are those of
+ *   pa_slot_mapping_and_cache_fp8_ex(slot_mapping, block_table, ...,
+ *       token_seq = b, token_pos = seq_lens[b] - 1, key, value, ..., PA_BF16,
+ *       format, k_scale, v_scale)
+ * followed by pa_decode_fp8_ex(...): slot_mapping, the caches and out bit for
+ * bit.  The decode launch stores the codes itself: each workgroup, before it
+ * reads any block, stores the newest token of the sequences whose last block
+ * it will read (no other workgroup reads that block).  Arguments as for
+ * pa_decode_append (key_token_stride / value_token_stride in elements; rows
+ * 16-byte aligned; slot_mapping may be NULL) and pa_decode_fp8_ex (format,
+ * scales, the stream mode in groups of 4096 sequences, the workspace of
+ * pa_decode_workspace_bytes(..., 0)).  Every check runs before the first
+ * launch: a call that returns an error has written nothing.
+ */
+pa_status pa_decode_append_fp8(void *out, const void *query, int64_t q_token_stride,
+                               const void *key, int64_t key_token_stride,
+                               const void *value, int64_t value_token_stride,
+                               void *key_cache, void *value_cache, int64_t *slot_mapping,
+                               const int32_t *block_table, int32_t max_blocks_per_req,
+                               const int32_t *seq_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t block_size, int64_t num_blocks, float scale,
+                               pa_fp8_format format, float k_scale, float v_scale,
+                               int32_t max_seq_len, void *workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+/*
  * The step just before attention, fused into one pass ("AI Infra入门干货总结：
  * 大模型是如何高效推理的", section "Reshape & Cache" and its table, and the RoPE
  * summary near its opening): split each token's fused QKV projection row into

@@ -20,7 +20,7 @@ __all__ = [
     "PaError", "lib", "lib_path", "pa_abi_version", "pa_status_string", "pa_last_error_message",
     "pa_slot_mapping", "pa_reshape_and_cache", "pa_slot_mapping_and_cache", "pa_rope_reshape_and_cache", "pa_reshape_and_cache_fp8", "pa_slot_mapping_and_cache_fp8",
     "pa_decode_fp8", "pa_copy_blocks", "KvManager", "pa_decode_workspace_bytes",
-    "pa_decode_partition_tokens", "pa_decode", "pa_decode_append", "pa_decode_append_noalloc", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
+    "pa_decode_partition_tokens", "pa_decode", "pa_decode_append", "pa_decode_append_noalloc", "pa_decode_append_fp8", "decode_workspace", "pa_chunked_prefill_workspace_bytes",
     "pa_chunked_prefill", "chunked_prefill_workspace", "pa_probe_stream_read", "pa_probe_copy", "pa_probe_mfma",
     "pa_validate_block_tables", "pa_validate_slot_mapping", "pa_validate_query_lens",
 ]
@@ -145,6 +145,10 @@ def lib():
         L.pa_decode_append.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                        _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _i32, _vp, ctypes.c_size_t,
                                        ctypes.c_int, _vp]
+        L.pa_decode_append_fp8.restype = ctypes.c_int
+        L.pa_decode_append_fp8.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
+                                           _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, ctypes.c_int,
+                                           ctypes.c_float, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]
         L.pa_decode_append_noalloc.restype = ctypes.c_int
         L.pa_decode_append_noalloc.argtypes = [_vp, _vp, _i64, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp, _i32, _vp,
                                                _i32, _i32, _i32, _i32, _i32, _i64, ctypes.c_float, _i32,
@@ -553,15 +557,22 @@ def pa_decode(out: torch.Tensor, query: torch.Tensor, key_cache: torch.Tensor, v
     return out
 
 
-def _check_decode_append(out, query, key, value, key_cache, value_cache, block_table, seq_lens, slot_mapping):
-    """Tensor checks shared by pa_decode_append and pa_decode_append_noalloc."""
+def _check_decode_append(out, query, key, value, key_cache, value_cache, block_table, seq_lens, slot_mapping,
+                         fp8=False):
+    """Tensor checks shared by pa_decode_append, pa_decode_append_noalloc and
+    (fp8: bf16 rows, uint8 caches) pa_decode_append_fp8."""
     _need(query.dim() == 3 and out.shape == query.shape and out.is_contiguous(),
           "query/out: [num_seqs, num_heads, head_dim], out contiguous")
     _need(query.stride(2) == 1 and query.stride(1) == query.shape[2], "query heads/dims must be contiguous")
     _need(key_cache.dim() == 4 and key_cache.shape == value_cache.shape, "caches: [num_blocks, 16, Hkv, D]")
     _need(key_cache.is_contiguous() and value_cache.is_contiguous(), "caches must be contiguous")
-    _need(query.dtype == out.dtype == key.dtype == value.dtype == key_cache.dtype == value_cache.dtype,
-          "dtype mismatch")
+    if fp8:
+        _need(query.dtype == out.dtype == key.dtype == value.dtype == torch.bfloat16,
+              "query/out/key/value: bfloat16")
+        _need(key_cache.dtype == value_cache.dtype == torch.uint8, "fp8 caches are uint8 codes")
+    else:
+        _need(query.dtype == out.dtype == key.dtype == value.dtype == key_cache.dtype == value_cache.dtype,
+              "dtype mismatch")
     _need(block_table.dtype == torch.int32 and block_table.dim() == 2 and block_table.is_contiguous(),
           "block_table: contiguous int32 [num_seqs, max_blocks_per_req]")
     _need(seq_lens.dtype == torch.int32 and seq_lens.is_contiguous(), "seq_lens: contiguous int32")
@@ -597,6 +608,31 @@ def pa_decode_append(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, 
                                0 if ws is None else ws.numel() * ws.element_size(), _dtype_code(query),
                                _stream(stream, out.device))
     _check(s, "pa_decode_append")
+    return out
+
+
+def pa_decode_append_fp8(out: torch.Tensor, query: torch.Tensor, key: torch.Tensor, value: torch.Tensor,
+                         key_cache: torch.Tensor, value_cache: torch.Tensor, block_table: torch.Tensor,
+                         seq_lens: torch.Tensor, scale: float, k_scale: float, v_scale: float, max_seq_len: int,
+                         slot_mapping: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                         stream=None, fp8_format: str = "e4m3") -> torch.Tensor:
+    """The decode step over uint8 fp8 caches in one call: row b of key/value
+    [B, Hkv, D] bf16 (sequence b's newest token) is stored as fp8 codes of
+    x / k_scale (x / v_scale) in its slot and attended to with the rest of the
+    sequence; out [B, Hq, D] bf16.  slot_mapping (int64 [B], optional) receives
+    the newest tokens' slots."""
+    _check_decode_append(out, query, key, value, key_cache, value_cache, block_table, seq_lens, slot_mapping,
+                         fp8=True)
+    b, hq, d = query.shape
+    nb, bs, hkv, _ = key_cache.shape
+    ws = workspace
+    s = lib().pa_decode_append_fp8(_ptr(out), _ptr(query), query.stride(0), _ptr(key), key.stride(0), _ptr(value),
+                                   value.stride(0), _ptr(key_cache), _ptr(value_cache), _ptr(slot_mapping),
+                                   _ptr(block_table), block_table.shape[1], _ptr(seq_lens), b, hq, hkv, d, bs, nb,
+                                   float(scale), _fp8_format(fp8_format), float(k_scale), float(v_scale),
+                                   int(max_seq_len), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+                                   _stream(stream, out.device))
+    _check(s, "pa_decode_append_fp8")
     return out
 
 

@@ -494,8 +494,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
     if (use_stream(num_seqs, partition_tokens)) {
         const int32_t group = num_heads / num_kv_heads;
         size_t bytes = 0;
-        for (int dtype = 0; dtype < 5; ++dtype) {          // the largest of the layouts (fp32, bf16, E4M3 cache,
-                                                           // append, E5M2 cache)
+        for (int dtype = 0; dtype < 7; ++dtype) {          // the largest of the layouts (fp32, bf16, E4M3 cache,
+                                                           // append, E5M2 cache, the fp8 append forms)
             const size_t n = stream_ws_bytes(num_seqs, num_heads, num_kv_heads,
                                              stream_shape(dtype, group, num_kv_heads, num_seqs));
             bytes = n > bytes ? n : bytes;
@@ -505,10 +505,11 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_heads, int32_t nu
     const int32_t pt = choose_partition(num_seqs, num_kv_heads, max_seq_len, partition_tokens);
     size_t bytes = partition_ws_bytes(num_seqs, num_heads, num_partitions(max_seq_len, pt));
     if (partition_tokens == 0) {
-        // pa_decode_fp8 reads a larger batch in groups of kStreamMaxSeqs
-        // sequences, one stream-mode launch each, on this one workspace
+        // pa_decode_fp8 and pa_decode_append_fp8 read a larger batch in
+        // groups of kStreamMaxSeqs sequences, one stream-mode launch each, on
+        // this one workspace
         const int32_t group = num_heads / num_kv_heads;
-        for (int dtype : {2, 4}) {
+        for (int dtype : {2, 4, 5, 6}) {
             const size_t n = stream_ws_bytes(kStreamMaxSeqs, num_heads, num_kv_heads,
                                              stream_shape(dtype, group, num_kv_heads, kStreamMaxSeqs));
             bytes = n > bytes ? n : bytes;
@@ -541,7 +542,8 @@ pa_status plan_decode(DecodePlan& plan, void* out, const void* query, int64_t q_
                         const void* new_value = nullptr, int64_t new_value_stride_bytes = 0,
                         int64_t* slot_out = nullptr) {
     // dt: 0 fp32, 1 bf16, 2 E4M3 / 4 E5M2 cache (bf16 query and output, stream mode only),
-    // 3 bf16 in append mode (stream mode only; the new_* rows and slot_out)
+    // 3 bf16 in append mode (stream mode only; the new_* rows and slot_out), 5 E4M3 / 6 E5M2
+    // cache in append mode (the same, and the rows stored as codes before they are read)
     const int32_t group = num_heads / num_kv_heads;
     plan.dt = dt;
     plan.group = group;
@@ -567,6 +569,8 @@ pa_status plan_decode(DecodePlan& plan, void* out, const void* query, int64_t q_
     a.new_key_stride = new_key_stride_bytes;
     a.new_value_stride = new_value_stride_bytes;
     a.slot_out = slot_out;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
 
     size_t need = 0;
     if (use_stream(num_seqs, partition_tokens)) {
@@ -655,16 +659,16 @@ F32Rows f32_rows(int64_t rows, int32_t max_seq_len) {
     return f;
 }
 
-}  // namespace
-
-extern "C" {
-
-pa_status pa_decode_fp8_ex(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
-                           const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
-                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
-                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
-                           pa_fp8_format format, float k_scale, float v_scale, int32_t max_seq_len, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+// pa_decode_fp8_ex, and with append pa_decode_append_fp8 (the newest rows
+// stored as codes by the decode launch itself).
+pa_status decode_fp8_common(void* out, const void* query, int64_t q_token_stride, const void* key,
+                            int64_t key_token_stride, const void* value, int64_t value_token_stride,
+                            const void* key_cache, const void* value_cache, int64_t* slot_mapping,
+                            const int32_t* block_table, int32_t max_blocks_per_req, const int32_t* seq_lens,
+                            int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t block_size, int64_t num_blocks, float scale, pa_fp8_format format,
+                            float k_scale, float v_scale, int32_t max_seq_len, void* workspace,
+                            size_t workspace_bytes, bool append, hipStream_t stream) {
     if (format != PA_FP8_E4M3 && format != PA_FP8_E5M2) return fail(PA_ERR_UNSUPPORTED, "fp8 format %d", (int)format);
     const pa_status hs = check_heads(num_heads, num_kv_heads, head_dim, block_size);
     if (hs != PA_OK) return hs;
@@ -677,14 +681,23 @@ pa_status pa_decode_fp8_ex(void* out, const void* query, int64_t q_token_stride,
         return fail(PA_ERR_INVALID_ARG, "max_seq_len %d exceeds max_blocks_per_req * 16", max_seq_len);
     if (num_seqs == 0) return ok();
     if (num_blocks == 0 && max_seq_len > 0) return fail(PA_ERR_INVALID_ARG, "empty cache pool");
-    if (!out || !query || !seq_lens || !key_cache || !value_cache || (max_seq_len > 0 && !block_table))
+    if (!out || !query || !seq_lens || !key_cache || !value_cache || (max_seq_len > 0 && !block_table) ||
+        (append && (!key || !value)))
         return fail(PA_ERR_INVALID_ARG, "null pointer");
     if (q_token_stride < (int64_t)num_heads * head_dim)
         return fail(PA_ERR_INVALID_ARG, "q_token_stride smaller than num_heads * head_dim");
     if (!aligned16(query) || (q_token_stride * 2) % 16 || !aligned16(out) || !aligned16(key_cache) ||
         !aligned16(value_cache))
         return fail(PA_ERR_INVALID_ARG, "query/out/cache rows must start on 16-byte boundaries");
+    if (append) {
+        const int64_t row_elems = (int64_t)num_kv_heads * head_dim;
+        if (key_token_stride < row_elems || value_token_stride < row_elems)
+            return fail(PA_ERR_INVALID_ARG, "key/value token stride smaller than num_kv_heads * head_dim");
+        if (!aligned16(key) || !aligned16(value) || (key_token_stride * 2) % 16 || (value_token_stride * 2) % 16)
+            return fail(PA_ERR_INVALID_ARG, "key/value rows must start on 16-byte boundaries");
+    }
     if (pa::debug_checks_enabled(stream)) {
+        // (append: the newest token is read from the cache, so it needs its block)
         const pa_status dc = pa::debug_check_tables(block_table, max_blocks_per_req, seq_lens, num_seqs, num_blocks,
                                                     max_seq_len, stream);
         if (dc != PA_OK) return dc;
@@ -694,17 +707,21 @@ pa_status pa_decode_fp8_ex(void* out, const void* query, int64_t q_token_stride,
     // over groups of that many, each reusing the workspace after the one
     // before it on the stream.  Every group is planned before the first
     // launch.
-    const int dt = format == PA_FP8_E5M2 ? 4 : 2;
+    const int dt = append ? (format == PA_FP8_E5M2 ? 6 : 5) : (format == PA_FP8_E5M2 ? 4 : 2);
     std::vector<DecodePlan> plans((size_t)((num_seqs + kStreamMaxSeqs - 1) / kStreamMaxSeqs));
     for (size_t g = 0; g < plans.size(); ++g) {
         const int32_t c0 = (int32_t)g * kStreamMaxSeqs;
         const int32_t n = std::min(kStreamMaxSeqs, num_seqs - c0);
-        const pa_status st =
-            plan_decode(plans[g], static_cast<char*>(out) + (int64_t)c0 * num_heads * head_dim * 2,
-                        static_cast<const char*>(query) + (int64_t)c0 * q_token_stride * 2, q_token_stride,
-                        key_cache, value_cache, block_table ? block_table + (int64_t)c0 * max_blocks_per_req : nullptr,
-                        max_blocks_per_req, seq_lens + c0, nullptr, n, num_heads, num_kv_heads, num_blocks, scale,
-                        max_seq_len, 0, workspace, workspace_bytes, dt, k_scale, v_scale);
+        const pa_status st = plan_decode(
+            plans[g], static_cast<char*>(out) + (int64_t)c0 * num_heads * head_dim * 2,
+            static_cast<const char*>(query) + (int64_t)c0 * q_token_stride * 2, q_token_stride, key_cache,
+            value_cache, block_table ? block_table + (int64_t)c0 * max_blocks_per_req : nullptr, max_blocks_per_req,
+            seq_lens + c0, nullptr, n, num_heads, num_kv_heads, num_blocks, scale, max_seq_len, 0, workspace,
+            workspace_bytes, dt, k_scale, v_scale,
+            append ? static_cast<const char*>(key) + (int64_t)c0 * key_token_stride * 2 : nullptr,
+            key_token_stride * 2,
+            append ? static_cast<const char*>(value) + (int64_t)c0 * value_token_stride * 2 : nullptr,
+            value_token_stride * 2, append && slot_mapping ? slot_mapping + c0 : nullptr);
         if (st != PA_OK) return st;
     }
     for (const DecodePlan& plan : plans) {
@@ -712,6 +729,35 @@ pa_status pa_decode_fp8_ex(void* out, const void* query, int64_t q_token_stride,
         if (st != PA_OK) return st;
     }
     return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+pa_status pa_decode_fp8_ex(void* out, const void* query, int64_t q_token_stride, const void* key_cache,
+                           const void* value_cache, const int32_t* block_table, int32_t max_blocks_per_req,
+                           const int32_t* seq_lens, int32_t num_seqs, int32_t num_heads, int32_t num_kv_heads,
+                           int32_t head_dim, int32_t block_size, int64_t num_blocks, float scale,
+                           pa_fp8_format format, float k_scale, float v_scale, int32_t max_seq_len, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+    return decode_fp8_common(out, query, q_token_stride, nullptr, 0, nullptr, 0, key_cache, value_cache, nullptr,
+                             block_table, max_blocks_per_req, seq_lens, num_seqs, num_heads, num_kv_heads, head_dim,
+                             block_size, num_blocks, scale, format, k_scale, v_scale, max_seq_len, workspace,
+                             workspace_bytes, false, stream);
+}
+
+pa_status pa_decode_append_fp8(void* out, const void* query, int64_t q_token_stride, const void* key,
+                               int64_t key_token_stride, const void* value, int64_t value_token_stride,
+                               void* key_cache, void* value_cache, int64_t* slot_mapping, const int32_t* block_table,
+                               int32_t max_blocks_per_req, const int32_t* seq_lens, int32_t num_seqs,
+                               int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t block_size,
+                               int64_t num_blocks, float scale, pa_fp8_format format, float k_scale, float v_scale,
+                               int32_t max_seq_len, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return decode_fp8_common(out, query, q_token_stride, key, key_token_stride, value, value_token_stride, key_cache,
+                             value_cache, slot_mapping, block_table, max_blocks_per_req, seq_lens, num_seqs,
+                             num_heads, num_kv_heads, head_dim, block_size, num_blocks, scale, format, k_scale,
+                             v_scale, max_seq_len, workspace, workspace_bytes, true, stream);
 }
 
 pa_status pa_decode_fp8(void* out, const void* query, int64_t q_token_stride, const void* key_cache,

@@ -671,6 +671,9 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
     if (total <= 0) return;
     const int B = a.num_seqs;
     constexpr int kEb = F8 ? 1 : 2;                    // cache bytes per element
+    // the newest token as a unit of its own, read from its input row (bf16
+    // append); the fp8 append form has stored it in the cache before the walk
+    constexpr bool APR = AP && !F8;
     const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * kEb;
     const uint32_t blk_bytes = tok_bytes * kBlock;
     const int i = lane & 15, g = lane >> 4;
@@ -686,8 +689,8 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
         const int2 e = *reinterpret_cast<const int2*>(&s_tab[j - c0]);
         id = __builtin_amdgcn_readfirstlane(e.x);
         const int vg = __builtin_amdgcn_readfirstlane(e.y);
-        valid = vg & (AP ? kAppendUnit - 1 : 0xff);
-        app = AP && (vg & kAppendUnit) != 0;
+        valid = vg & (APR ? kAppendUnit - 1 : 0xff);
+        app = APR && (vg & kAppendUnit) != 0;
         grp = vg >> 8;
     };
 
@@ -703,7 +706,7 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
         const int64_t off = phys * (int64_t)blk_bytes + hoff;
         const char* kb = kc + off;
         const char* vb = vc + off;
-        if constexpr (AP) {
+        if constexpr (APR) {
             // the newest token: its input row is token 0 of a one-token block
             // (lanes of the other tokens read past the 256 bytes: zeros)
             kb = app ? a.new_key + id * a.new_key_stride + hoff : kb;
@@ -844,7 +847,9 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
 
     for (c0 = 0; c0 < total; c0 = c1) {
         c1 = min(total, c0 + kShareTable);
-        __syncthreads();                               // the previous table is no longer read
+        // the previous table is no longer read (and, first, the fp8 append
+        // form's stores of the newest rows are complete)
+        __syncthreads();
         for (int t = threadIdx.x; t < c1 - c0; t += blockDim.x) {
             // unit -> (sequence b, group, block of b): b is the largest with NG * prefix[b] <= u
             const int64_t u = u0 + c0 + t;
@@ -858,14 +863,14 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
             const int grp = (int)(r / nb), blk = (int)(r % nb);
             const int row = (int)decode_row(a, lo);    // >= 0: only decode rows own blocks
             int id, valid;
-            if (AP && blk == nb - 1) {
+            if (APR && blk == nb - 1) {
                 // the newest token, from input row `row` (= lo)
                 id = row;
                 valid = 1 | kAppendUnit;
             } else {
                 // in append mode the cached blocks hold the tokens before the newest
                 id = a.block_table[(int64_t)lo * a.bt_stride + blk];
-                valid = min(max(seq_len_of(a, lo) - (AP ? 1 : 0) - blk * kBlock, 0), kBlock);
+                valid = min(max(seq_len_of(a, lo) - (APR ? 1 : 0) - blk * kBlock, 0), kBlock);
             }
             s_tab[t] = int4{id, valid | (grp << 8), row, (nb - blk) | (blk == 0 ? kFirstBlock : 0)};
         }
@@ -994,13 +999,76 @@ __device__ __forceinline__ void block_prefix(const DecodeArgs& a, int32_t* s_pre
     __syncthreads();
 }
 
+// fp8 append form: before any block is read, each workgroup quantises the
+// newest token (position seq_lens[b] - 1, input row b) of every sequence whose
+// last block of a KV-head group falls in its share [u0, u1) into its slot, for
+// the group's KV heads, with the scatter's encoder; the walk then reads it as a
+// cached token of that block, which no other workgroup reads.  The slot rule
+// is the page-table lookup's (-1, and nothing stored, without a block); the
+// owner of group 0's last block writes slot_out[b], workgroup 0 writes -1 for
+// sequences without tokens.  Tasks: (sequence, group, head of the group, K or
+// V, 16-element chunk of the 128).
+template <bool E5>
+__device__ void store_newest_fp8(const DecodeArgs& a, const int32_t* s_pref, int64_t u0, int64_t u1, int NG,
+                                 int W) {
+    const int B = a.num_seqs;
+    if (blockIdx.x == 0 && a.slot_out)
+        for (int b = threadIdx.x; b < B; b += blockDim.x)
+            if (s_pref[b + 1] == s_pref[b]) a.slot_out[b] = -1;
+    if (u1 <= u0) return;
+    auto seq_of = [&](int64_t u) {                     // the largest b with NG * prefix[b] <= u
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if ((int64_t)NG * s_pref[mid] <= u) lo = mid; else hi = mid - 1;
+        }
+        return lo;
+    };
+    const int b_lo = seq_of(u0), b_hi = seq_of(u1 - 1);
+    const int per_seq = NG * W * 2 * (kHeadDim / 16);
+    const int tasks = (b_hi - b_lo + 1) * per_seq;
+    const int64_t num_slots = a.num_blocks * kBlock;
+    const int64_t tok_bytes = (int64_t)a.num_kv_heads * kHeadDim;   // one byte per code
+    for (int t = threadIdx.x; t < tasks; t += blockDim.x) {
+        const int b = b_lo + t / per_seq;
+        int r = t % per_seq;
+        const int c = r % (kHeadDim / 16);
+        r /= kHeadDim / 16;
+        const bool is_v = (r & 1) != 0;
+        r >>= 1;
+        const int hw = r % W, g = r / W;
+        const int nb = s_pref[b + 1] - s_pref[b];
+        if (nb == 0) continue;
+        const int64_t last = (int64_t)NG * s_pref[b] + (int64_t)g * nb + nb - 1;
+        if (last < u0 || last >= u1) continue;
+        const int p = seq_len_of(a, b) - 1;            // >= 0: the sequence has blocks
+        int64_t slot = -1;
+        if (p / kBlock < a.bt_stride) {
+            const int32_t physical = a.block_table[(int64_t)b * a.bt_stride + p / kBlock];
+            if (physical >= 0) slot = (int64_t)physical * kBlock + p % kBlock;
+        }
+        if (g == 0 && hw == 0 && !is_v && c == 0 && a.slot_out) a.slot_out[b] = slot;
+        if (slot < 0 || slot >= num_slots) continue;
+        const int kvh = g * W + hw;
+        const char* src = (is_v ? a.new_value + b * a.new_value_stride : a.new_key + b * a.new_key_stride) +
+                          ((int64_t)kvh * kHeadDim + 16 * c) * 2;
+        ChunkBF16 x0, x1;
+        load_chunk<false>(x0, src);
+        load_chunk<false>(x1, src + 16);
+        uint8_t* dst = reinterpret_cast<uint8_t*>(const_cast<void*>(is_v ? a.value_cache : a.key_cache)) +
+                       slot * tok_bytes + (int64_t)kvh * kHeadDim + 16 * c;
+        *reinterpret_cast<u32x4_t*>(dst) = fp8_codes<ChunkBF16, E5>(x0, x1, is_v ? a.v_scale : a.k_scale);
+    }
+}
+
 __device__ __forceinline__ int64_t stream_quantum(const DecodeArgs& a, int64_t units) {
     const int64_t q = (units + a.num_wg - 1) / a.num_wg;
     return q > a.min_quantum ? q : (int64_t)a.min_quantum;
 }
 
 // F8: the caches hold fp8 codes, E4M3 or (E5) E5M2; query and output stay bf16.
-// AP: append mode (bf16 matrix-core path only).
+// AP: append mode (matrix-core path only): bf16 reads the newest token from
+// its input row; fp8 (F8 and AP) stores it into the cache first.
 template <typename Chunk, typename Elem, int G, bool QL, bool NT, bool F8 = false, bool AP = false, bool E5 = false>
 __global__ void __launch_bounds__(512)
 decode_stream_kernel(DecodeArgs a) {
@@ -1011,7 +1079,7 @@ decode_stream_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float p_lds[MF ? 1 : 8][MF ? 4 : kBlock * G];
     __shared__ __attribute__((aligned(16))) Elem q_lds[QL && !MF ? 8 : 1][QL && !MF ? G * kHeadDim : 8];
     __shared__ int4 s_tab[MF ? kShareTable : 1];
-    block_prefix<AP>(a, s_pref, s_wsum);
+    block_prefix<AP && !F8>(a, s_pref, s_wsum);
     const int B = a.num_seqs;
     const int W = a.waves_per_group;
     const int NG = a.num_kv_heads / W;
@@ -1024,7 +1092,10 @@ decode_stream_kernel(DecodeArgs a) {
     const int wi = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     float* pl = p_lds[MF ? 0 : wi];
-    static_assert(!AP || (MF && !F8), "append mode: bf16 matrix-core path");
+    static_assert(!AP || MF, "append mode: matrix-core path");
+    // (the stores are complete before any block is read: the walk's first
+    // table build starts with a workgroup barrier)
+    if constexpr (F8 && AP) store_newest_fp8<E5>(a, s_pref, u0, u1, NG, W);
     if constexpr (MF) {
         float* s_first = reinterpret_cast<float*>(s_pref + ((B + 1 + 3) & ~3)) + wi * 2 * G * kRec;
         stream_share_mfma<G, NT, F8 ? kFp8Depth : kMfmaDepth, F8, AP, E5>(a, s_pref, s_tab, u0, u1, W, NG, wi,
@@ -1319,12 +1390,13 @@ hipError_t launch_typed(const DecodeArgs& a, hipStream_t stream) {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t mitems = (int64_t)a.num_seqs * a.num_heads;
+        constexpr bool MAP = AP && !F8;                // the merge writes the newest rows (bf16 append)
         if (a.merge_pair) {
-            hipLaunchKernelGGL((merge_stream_kernel<Elem, AP, true>),
+            hipLaunchKernelGGL((merge_stream_kernel<Elem, MAP, true>),
                                dim3((unsigned)((mitems / 2 + kWavesPerGroup - 1) / kWavesPerGroup)), dim3(256), 0,
                                stream, a);
         } else {
-            hipLaunchKernelGGL((merge_stream_kernel<Elem, AP>),
+            hipLaunchKernelGGL((merge_stream_kernel<Elem, MAP>),
                                dim3((unsigned)((mitems + kWavesPerGroup - 1) / kWavesPerGroup)), dim3(256), 0,
                                stream, a);
         }
@@ -1379,15 +1451,18 @@ int stream_blocks_group(int group, int waves_per_group, int64_t num_seqs) {
 }  // namespace
 
 // dtype: 0 fp32, 1 bf16, 2 E4M3 cache with bf16 query and output, 3 bf16 in
-// append mode, 4 E5M2 cache with bf16 query and output.
+// append mode, 4 E5M2 cache with bf16 query and output, 5 and 6 the E4M3 and
+// E5M2 caches in append mode.
 // The append form runs on the matrix-core wave only: a build that moves the
 // bf16 decode to the vector wave (PA_DECODE_MFMA_FROM > 1, for measurement)
 // leaves it out, and its launches fail.
 hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t stream) {
 #if PA_DECODE_MFMA_FROM <= 1
     if (dtype == 3) return launch_group<ChunkBF16, uint16_t, false, true>(a, group, stream);
+    if (dtype == 5) return launch_group<ChunkBF16, uint16_t, true, true>(a, group, stream);
+    if (dtype == 6) return launch_group<ChunkBF16, uint16_t, true, true, true>(a, group, stream);
 #else
-    if (dtype == 3) return hipErrorInvalidDeviceFunction;
+    if (dtype == 3 || dtype == 5 || dtype == 6) return hipErrorInvalidDeviceFunction;
 #endif
     if (dtype == 4) return launch_group<ChunkBF16, uint16_t, true, false, true>(a, group, stream);
     if (dtype == 2) return launch_group<ChunkBF16, uint16_t, true>(a, group, stream);
@@ -1398,8 +1473,13 @@ hipError_t launch_decode(const DecodeArgs& a, int dtype, int group, hipStream_t 
 int decode_stream_blocks_per_cu(int dtype, int group, int waves_per_group, int num_seqs) {
 #if PA_DECODE_MFMA_FROM <= 1
     if (dtype == 3) return stream_blocks_group<ChunkBF16, uint16_t, false, true>(group, waves_per_group, num_seqs);
+    if (dtype == 5) return stream_blocks_group<ChunkBF16, uint16_t, true, true>(group, waves_per_group, num_seqs);
+    if (dtype == 6)
+        return stream_blocks_group<ChunkBF16, uint16_t, true, true, true>(group, waves_per_group, num_seqs);
 #else
     if (dtype == 3) return stream_blocks_group<ChunkBF16, uint16_t>(group, waves_per_group, num_seqs);
+    if (dtype == 5) return stream_blocks_group<ChunkBF16, uint16_t, true>(group, waves_per_group, num_seqs);
+    if (dtype == 6) return stream_blocks_group<ChunkBF16, uint16_t, true, false, true>(group, waves_per_group, num_seqs);
 #endif
     if (dtype == 4) return stream_blocks_group<ChunkBF16, uint16_t, true, false, true>(group, waves_per_group, num_seqs);
     if (dtype == 2) return stream_blocks_group<ChunkBF16, uint16_t, true>(group, waves_per_group, num_seqs);

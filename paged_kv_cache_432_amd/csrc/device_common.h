@@ -147,4 +147,42 @@ __device__ __forceinline__ float readlane_f(float x, int lane) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
 }
 
+// ---- fp8 encoding (the fp8 scatters, and the decode's fp8 append form) ----
+// Each element x is stored as the OCP E4M3 (E5 = false) or E5M2 (E5 = true)
+// code of x / scale: the division in float32 (correctly rounded), magnitudes
+// beyond the format's largest finite value (448; 57344) saturated to it, NaN
+// kept, then the hardware conversion to the nearest code, ties to even.
+template <bool E5, bool HI>
+__device__ __forceinline__ int cvt_pk_fp8(float a, float b, int old) {
+    if constexpr (E5)
+        return __builtin_amdgcn_cvt_pk_bf8_f32(a, b, old, HI);
+    else
+        return __builtin_amdgcn_cvt_pk_fp8_f32(a, b, old, HI);
+}
+
+// 16 source elements (two chunks) -> their 16 codes of x / scale.
+template <typename Chunk, bool E5>
+__device__ __forceinline__ u32x4_t fp8_codes(const Chunk& x0, const Chunk& x1, float scale) {
+    constexpr float kMax = E5 ? 57344.f : 448.f;
+    float f[16];
+    to_f32(x0, f);
+    to_f32(x1, f + 8);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+        const float y = f[e] / scale;
+        f[e] = __builtin_fabsf(y) > kMax ? __builtin_copysignf(kMax, y) : y;
+    }
+    u32x4_t w;
+    int p0 = cvt_pk_fp8<E5, false>(f[0], f[1], 0);
+    p0 = cvt_pk_fp8<E5, true>(f[2], f[3], p0);
+    int p1 = cvt_pk_fp8<E5, false>(f[4], f[5], 0);
+    p1 = cvt_pk_fp8<E5, true>(f[6], f[7], p1);
+    int p2 = cvt_pk_fp8<E5, false>(f[8], f[9], 0);
+    p2 = cvt_pk_fp8<E5, true>(f[10], f[11], p2);
+    int p3 = cvt_pk_fp8<E5, false>(f[12], f[13], 0);
+    p3 = cvt_pk_fp8<E5, true>(f[14], f[15], p3);
+    w.x = (uint32_t)p0; w.y = (uint32_t)p1; w.z = (uint32_t)p2; w.w = (uint32_t)p3;
+    return w;
+}
+
 }  // namespace pa

@@ -117,6 +117,10 @@ struct DecodeArgs {
     int64_t new_key_stride;        // bytes between rows
     int64_t new_value_stride;
     int64_t* slot_out;             // [num_seqs] or null
+    // fp8 append (internal dtypes 5, 6): the same rows are stored as codes of
+    // x / k_scale and x / v_scale into the fp8 caches before they are read
+    float k_scale;
+    float v_scale;
     // Mixed batches: when set, [num_seqs + 1] offsets of each sequence's query
     // rows; only sequences with exactly one query row are attended (their row
     // and output row are cu_q[b]), the others are left to the prefill kernel.

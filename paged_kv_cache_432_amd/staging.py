@@ -14,8 +14,7 @@ import numpy as np
 import torch
 
 from . import (chunked_prefill_workspace, decode_workspace, pa_chunked_prefill, pa_decode, pa_decode_append,
-               pa_decode_fp8,
-               pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_slot_mapping_and_cache,
+               pa_decode_append_fp8, pa_decode_fp8, pa_reshape_and_cache, pa_reshape_and_cache_fp8, pa_slot_mapping, pa_slot_mapping_and_cache,
                pa_slot_mapping_and_cache_fp8)
 
 _TORCH_DTYPE = {"bf16": torch.bfloat16, "f32": torch.float32}
@@ -181,15 +180,19 @@ class DeviceWorkload:
         return self._append
 
     def decode_append(self, out=None, workspace=None, stream=None) -> torch.Tensor:
-        """The whole decode step in one call (pa_decode_append): the newest
-        token of every sequence written to the cache and attended to."""
+        """The whole decode step in one call (pa_decode_append, or
+        pa_decode_append_fp8 over an fp8 cache): the newest token of every
+        sequence written to the cache and attended to."""
         w = self.w
-        assert not self.kv_fp8, "pa_decode_append takes bf16/fp32 caches"
         k, v, slots = self.append_rows()
         if out is None:
             out = torch.empty_like(self.query)
         if workspace is None:
             workspace = self.decode_workspace(0)
+        if self.kv_fp8:
+            return pa_decode_append_fp8(out, self.query, k, v, self.key_cache, self.value_cache, self.block_table,
+                                        self.seq_lens, w.scale, self.k_scale, self.v_scale, w.max_seq_len, slots,
+                                        workspace, stream, fp8_format=self.fp8_format)
         return pa_decode_append(out, self.query, k, v, self.key_cache, self.value_cache, self.block_table,
                                 self.seq_lens, w.scale, w.max_seq_len, slots, workspace, stream)
 

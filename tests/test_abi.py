@@ -108,6 +108,42 @@ def test_decode_append_empty_batch_is_ok(L):
     assert _decode_append(L, num_seqs=0) == pa.PA_OK
 
 
+def _decode_append_fp8(L, **kw):
+    args = dict(out=16, query=16, q_token_stride=4096, key=16, key_token_stride=1024, value=16,
+                value_token_stride=1024, key_cache=16, value_cache=16, slot_mapping=16, block_table=16,
+                max_blocks_per_req=8, seq_lens=16, num_seqs=2, num_heads=32, num_kv_heads=8, head_dim=128,
+                block_size=16, num_blocks=10, scale=0.088, format=0, k_scale=0.5, v_scale=0.5, max_seq_len=100,
+                workspace=None, workspace_bytes=0, stream=None)
+    args.update(kw)
+    return L.pa_decode_append_fp8(*args.values())
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(head_dim=64), pa.PA_ERR_UNSUPPORTED),
+    (dict(block_size=32), pa.PA_ERR_UNSUPPORTED),
+    (dict(num_heads=24, num_kv_heads=8), pa.PA_ERR_UNSUPPORTED),       # group 3
+    (dict(format=2), pa.PA_ERR_UNSUPPORTED),
+    (dict(key=None), pa.PA_ERR_INVALID_ARG),
+    (dict(value=None), pa.PA_ERR_INVALID_ARG),
+    (dict(key_token_stride=1000), pa.PA_ERR_INVALID_ARG),              # shorter than a row
+    (dict(value_token_stride=1028), pa.PA_ERR_INVALID_ARG),            # rows not 16-byte aligned
+    (dict(key=24), pa.PA_ERR_INVALID_ARG),                             # misaligned
+    (dict(max_seq_len=200), pa.PA_ERR_INVALID_ARG),                    # beyond the table
+    (dict(scale=0.0), pa.PA_ERR_INVALID_ARG),
+    (dict(k_scale=-1.0), pa.PA_ERR_INVALID_ARG),
+    (dict(v_scale=float("inf")), pa.PA_ERR_INVALID_ARG),
+    (dict(num_seqs=-1), pa.PA_ERR_INVALID_ARG),
+])
+def test_decode_append_fp8_rejects_before_launch(L, kw, status):
+    assert _decode_append_fp8(L, **kw) == status
+    assert pa.pa_last_error_message()
+
+
+def test_decode_append_fp8_empty_batch_is_ok(L):
+    assert _decode_append_fp8(L, num_seqs=0) == pa.PA_OK
+    assert _decode_append_fp8(L, num_seqs=0, format=1) == pa.PA_OK
+
+
 def test_fused_fp8_scatter_checks(L):
     args = dict(slot_mapping=16, block_table=16, max_blocks_per_req=4, num_seqs=2, token_seq=16, token_pos=16,
                 key=16, key_token_stride=1024, value=16, value_token_stride=1024, key_cache=16, value_cache=16,
