@@ -1,6 +1,7 @@
 """Steps replayed from a captured HIP graph (torch.cuda.CUDAGraph is
 PyTorch-ROCm's HIP graph API): pa_decode_append; pa_slot_mapping_and_cache
-followed by pa_decode (bf16 and fp8 caches); and pa_chunked_prefill. Each is
+followed by pa_decode (bf16 and fp8 caches); pa_decode_append_fp8; and
+pa_chunked_prefill. Each is
 captured once and replayed several times, with eager work and synchronisations
 between the replays.  Every replay must give exactly the
 eager result (same kernels, same inputs), and the eager result matches the
@@ -69,12 +70,17 @@ def test_decode_step_graph_replays(staging, mode):
     assert np.array_equal(dw.value_cache.cpu().view(torch.int16).numpy().view(np.uint16), ovc)
 
 
-def test_fp8_step_graph_replays(staging):
-    w = W.custom("graph_fp8", seq_lens=[3, 500, 1500, 16, 17], dtype="bf16", seed=81)
+@pytest.mark.parametrize("mode", ["two_call", "append"])
+def test_fp8_step_graph_replays(staging, mode):
+    w = W.custom("graph_fp8", seq_lens=[3, 500, 1500, 16, 17, 0], dtype="bf16", seed=81)
     dw = staging.DeviceWorkload(w, kv_fp8=True)
     out = torch.empty_like(dw.query)
     ws = dw.decode_workspace(0)
-    step = lambda: (dw.scatter_new(fused=True), dw.decode(out, 0, ws))
+    if mode == "append":
+        dw.append_rows()                                  # the newest rows, allocated before capture
+        step = lambda: dw.decode_append(out, ws)
+    else:
+        step = lambda: (dw.scatter_new(fused=True), dw.decode(out, 0, ws))
     step()
     torch.cuda.synchronize()
     eager = out.clone()
@@ -85,6 +91,7 @@ def test_fp8_step_graph_replays(staging):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, eager), f"replay {r}"
+    assert_parity(to_numpy(eager), oracle.run_fp8(w, *w.fp8_scales()), "bf16", f"graph fp8 {mode}")
 
 
 def test_chunked_prefill_graph_replays(staging):
