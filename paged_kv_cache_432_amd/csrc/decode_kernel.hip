@@ -616,6 +616,47 @@ constexpr int kFirstBlock = 1 << 30;                  // table flag: block 0 of 
 // its input row (the unit's id field holds the row) as a one-token block.
 constexpr int kAppendUnit = 0x80;
 
+// fp8 append form: the newest token of each sequence (position seq_lens[b] -
+// 1, input row b) is quantised into its slot by the workgroup whose share holds
+// the sequence's last block, once that block's table window is built and before
+// any of the window's blocks is read (no other workgroup reads that block).
+// s_last[0] counts the window's last blocks (of a sequence and KV-head group),
+// s_last[1..] are their table indices.  The table entry gives the block id, the
+// block's token count (the newest token is the last of them) and the group; the
+// slot rule is the page-table lookup's (-1, and nothing stored, without a
+// block).  The owner of group 0's last block writes slot_out[b].  Tasks: (last
+// block, head of the group, K or V, 16-element chunk of the 128), each a
+// 32-byte load of the bf16 row, the scatter's encoder and a 16-byte store.
+template <bool E5>
+__device__ void store_newest_fp8(const DecodeArgs& a, const int4* s_tab, const int32_t* s_last, int W) {
+    const int per = W * 2 * (kHeadDim / 16);
+    const int tasks = s_last[0] * per;
+    const int64_t num_slots = a.num_blocks * kBlock;
+    const int64_t tok_bytes = (int64_t)a.num_kv_heads * kHeadDim;   // one byte per code
+    for (int t = threadIdx.x; t < tasks; t += blockDim.x) {
+        const int4 e = s_tab[s_last[1 + t / per]];
+        int r = t % per;
+        const int c = r % (kHeadDim / 16);
+        r /= kHeadDim / 16;
+        const bool is_v = (r & 1) != 0;
+        const int hw = r >> 1;
+        const int grp = e.y >> 8, valid = e.y & 0xff;
+        const int64_t b = e.z;                         // the input row: the sequence (no mixed batch here)
+        const int kvh = grp * W + hw;
+        const char* src = (is_v ? a.new_value + b * a.new_value_stride : a.new_key + b * a.new_key_stride) +
+                          ((int64_t)kvh * kHeadDim + 16 * c) * 2;
+        ChunkBF16 x0, x1;
+        load_chunk<false>(x0, src);
+        load_chunk<false>(x1, src + 16);
+        const int64_t slot = e.x >= 0 ? (int64_t)e.x * kBlock + valid - 1 : -1;
+        if (grp == 0 && hw == 0 && !is_v && c == 0 && a.slot_out) a.slot_out[b] = slot;
+        if (slot < 0 || slot >= num_slots) continue;
+        uint8_t* dst = reinterpret_cast<uint8_t*>(const_cast<void*>(is_v ? a.value_cache : a.key_cache)) +
+                       slot * tok_bytes + (int64_t)kvh * kHeadDim + 16 * c;
+        *reinterpret_cast<u32x4_t*>(dst) = fp8_codes<ChunkBF16, E5>(x0, x1, is_v ? a.v_scale : a.k_scale);
+    }
+}
+
 // One block's K and V rows of one KV head as a lane holds them in flight.
 // bf16: K dims 32ks + 8g .. +8 of token i for product step ks; V dims 8i .. +8
 // of tokens 4g .. 4g+3.  fp8 (one byte per element): K bytes 32g .. 32g+31 of
@@ -666,14 +707,17 @@ __device__ __forceinline__ u32x4_t fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 // cut, is staged in the second half, so that both leave as coalesced stores.
 template <int G, bool NT, int NBUF, bool F8 = false, bool AP = false, bool E5 = false>
 __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int32_t* s_pref, int4* s_tab, int64_t u0,
-                                                  int64_t u1, int W, int NG, int wi, int lane, float* s_first) {
+                                                  int64_t u1, int W, int NG, int wi, int lane, float* s_first,
+                                                  int32_t* s_last) {
     const int total = (int)(u1 - u0);                  // the same for every wave of the workgroup
     if (total <= 0) return;
     const int B = a.num_seqs;
     constexpr int kEb = F8 ? 1 : 2;                    // cache bytes per element
     // the newest token as a unit of its own, read from its input row (bf16
-    // append); the fp8 append form has stored it in the cache before the walk
+    // append); or (fp8 append) stored into the cache as codes after each table
+    // window is built, before any of its blocks is read
     constexpr bool APR = AP && !F8;
+    constexpr bool APS = AP && F8;
     const uint32_t tok_bytes = (uint32_t)a.num_kv_heads * kHeadDim * kEb;
     const uint32_t blk_bytes = tok_bytes * kBlock;
     const int i = lane & 15, g = lane >> 4;
@@ -847,9 +891,10 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
 
     for (c0 = 0; c0 < total; c0 = c1) {
         c1 = min(total, c0 + kShareTable);
-        // the previous table is no longer read (and, first, the fp8 append
-        // form's stores of the newest rows are complete)
-        __syncthreads();
+        // (the previous window's list was last read before the barrier that
+        // ended its stores)
+        if (APS && threadIdx.x == 0) s_last[0] = 0;
+        __syncthreads();                               // the previous table is no longer read
         for (int t = threadIdx.x; t < c1 - c0; t += blockDim.x) {
             // unit -> (sequence b, group, block of b): b is the largest with NG * prefix[b] <= u
             const int64_t u = u0 + c0 + t;
@@ -873,8 +918,13 @@ __device__ __forceinline__ void stream_share_mfma(const DecodeArgs& a, const int
                 valid = min(max(seq_len_of(a, lo) - (APR ? 1 : 0) - blk * kBlock, 0), kBlock);
             }
             s_tab[t] = int4{id, valid | (grp << 8), row, (nb - blk) | (blk == 0 ? kFirstBlock : 0)};
+            if (APS && blk == nb - 1) s_last[1 + atomicAdd(&s_last[0], 1)] = t;
         }
         __syncthreads();
+        if constexpr (APS) {
+            store_newest_fp8<E5>(a, s_tab, s_last, W);
+            __syncthreads();                           // stored before the window's blocks are read
+        }
         if (c0 > 0 && qn_at < 0) prefetch_query();    // the segment running on ends in this table
         KvBuf<F8> buf[NBUF];
 #pragma unroll
@@ -999,68 +1049,6 @@ __device__ __forceinline__ void block_prefix(const DecodeArgs& a, int32_t* s_pre
     __syncthreads();
 }
 
-// fp8 append form: before any block is read, each workgroup quantises the
-// newest token (position seq_lens[b] - 1, input row b) of every sequence whose
-// last block of a KV-head group falls in its share [u0, u1) into its slot, for
-// the group's KV heads, with the scatter's encoder; the walk then reads it as a
-// cached token of that block, which no other workgroup reads.  The slot rule
-// is the page-table lookup's (-1, and nothing stored, without a block); the
-// owner of group 0's last block writes slot_out[b], workgroup 0 writes -1 for
-// sequences without tokens.  Tasks: (sequence, group, head of the group, K or
-// V, 16-element chunk of the 128).
-template <bool E5>
-__device__ void store_newest_fp8(const DecodeArgs& a, const int32_t* s_pref, int64_t u0, int64_t u1, int NG,
-                                 int W) {
-    const int B = a.num_seqs;
-    if (blockIdx.x == 0 && a.slot_out)
-        for (int b = threadIdx.x; b < B; b += blockDim.x)
-            if (s_pref[b + 1] == s_pref[b]) a.slot_out[b] = -1;
-    if (u1 <= u0) return;
-    auto seq_of = [&](int64_t u) {                     // the largest b with NG * prefix[b] <= u
-        int lo = 0, hi = B - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if ((int64_t)NG * s_pref[mid] <= u) lo = mid; else hi = mid - 1;
-        }
-        return lo;
-    };
-    const int b_lo = seq_of(u0), b_hi = seq_of(u1 - 1);
-    const int per_seq = NG * W * 2 * (kHeadDim / 16);
-    const int tasks = (b_hi - b_lo + 1) * per_seq;
-    const int64_t num_slots = a.num_blocks * kBlock;
-    const int64_t tok_bytes = (int64_t)a.num_kv_heads * kHeadDim;   // one byte per code
-    for (int t = threadIdx.x; t < tasks; t += blockDim.x) {
-        const int b = b_lo + t / per_seq;
-        int r = t % per_seq;
-        const int c = r % (kHeadDim / 16);
-        r /= kHeadDim / 16;
-        const bool is_v = (r & 1) != 0;
-        r >>= 1;
-        const int hw = r % W, g = r / W;
-        const int nb = s_pref[b + 1] - s_pref[b];
-        if (nb == 0) continue;
-        const int64_t last = (int64_t)NG * s_pref[b] + (int64_t)g * nb + nb - 1;
-        if (last < u0 || last >= u1) continue;
-        const int p = seq_len_of(a, b) - 1;            // >= 0: the sequence has blocks
-        int64_t slot = -1;
-        if (p / kBlock < a.bt_stride) {
-            const int32_t physical = a.block_table[(int64_t)b * a.bt_stride + p / kBlock];
-            if (physical >= 0) slot = (int64_t)physical * kBlock + p % kBlock;
-        }
-        if (g == 0 && hw == 0 && !is_v && c == 0 && a.slot_out) a.slot_out[b] = slot;
-        if (slot < 0 || slot >= num_slots) continue;
-        const int kvh = g * W + hw;
-        const char* src = (is_v ? a.new_value + b * a.new_value_stride : a.new_key + b * a.new_key_stride) +
-                          ((int64_t)kvh * kHeadDim + 16 * c) * 2;
-        ChunkBF16 x0, x1;
-        load_chunk<false>(x0, src);
-        load_chunk<false>(x1, src + 16);
-        uint8_t* dst = reinterpret_cast<uint8_t*>(const_cast<void*>(is_v ? a.value_cache : a.key_cache)) +
-                       slot * tok_bytes + (int64_t)kvh * kHeadDim + 16 * c;
-        *reinterpret_cast<u32x4_t*>(dst) = fp8_codes<ChunkBF16, E5>(x0, x1, is_v ? a.v_scale : a.k_scale);
-    }
-}
-
 __device__ __forceinline__ int64_t stream_quantum(const DecodeArgs& a, int64_t units) {
     const int64_t q = (units + a.num_wg - 1) / a.num_wg;
     return q > a.min_quantum ? q : (int64_t)a.min_quantum;
@@ -1079,6 +1067,7 @@ decode_stream_kernel(DecodeArgs a) {
     __shared__ __attribute__((aligned(16))) float p_lds[MF ? 1 : 8][MF ? 4 : kBlock * G];
     __shared__ __attribute__((aligned(16))) Elem q_lds[QL && !MF ? 8 : 1][QL && !MF ? G * kHeadDim : 8];
     __shared__ int4 s_tab[MF ? kShareTable : 1];
+    __shared__ int32_t s_last[F8 && AP ? kShareTable + 1 : 1];   // fp8 append: the window's last blocks
     block_prefix<AP && !F8>(a, s_pref, s_wsum);
     const int B = a.num_seqs;
     const int W = a.waves_per_group;
@@ -1093,13 +1082,17 @@ decode_stream_kernel(DecodeArgs a) {
     const int lane = threadIdx.x & 63;
     float* pl = p_lds[MF ? 0 : wi];
     static_assert(!AP || MF, "append mode: matrix-core path");
-    // (the stores are complete before any block is read: the walk's first
-    // table build starts with a workgroup barrier)
-    if constexpr (F8 && AP) store_newest_fp8<E5>(a, s_pref, u0, u1, NG, W);
+    if constexpr (F8 && AP) {
+        // the slot of a sequence without tokens is -1 (the others' slots are
+        // written with their newest rows)
+        if (blockIdx.x == 0 && a.slot_out)
+            for (int b = threadIdx.x; b < B; b += blockDim.x)
+                if (s_pref[b + 1] == s_pref[b]) a.slot_out[b] = -1;
+    }
     if constexpr (MF) {
         float* s_first = reinterpret_cast<float*>(s_pref + ((B + 1 + 3) & ~3)) + wi * 2 * G * kRec;
         stream_share_mfma<G, NT, F8 ? kFp8Depth : kMfmaDepth, F8, AP, E5>(a, s_pref, s_tab, u0, u1, W, NG, wi,
-                                                                          lane, s_first);
+                                                                          lane, s_first, s_last);
         return;
     }
 
