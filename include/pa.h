@@ -369,9 +369,9 @@ pa_status pa_decode_fp8_ex(void *out, const void *query, int64_t q_token_stride,
  *       token_seq = b, token_pos = seq_lens[b] - 1, key, value, ..., PA_BF16,
  *       format, k_scale, v_scale)
  * followed by pa_decode_fp8_ex(...): slot_mapping, the caches and out bit for
- * bit.  The decode launch stores the codes itself: each workgroup, before it
- * reads any block, stores the newest token of the sequences whose last block
- * it will read (no other workgroup reads that block).  Arguments as for
+ * bit.  The decode launch stores the codes itself: the workgroup that reads a
+ * sequence's last block stores the newest token into it first (no other
+ * workgroup reads that block).  Arguments as for
  * pa_decode_append (key_token_stride / value_token_stride in elements; rows
  * 16-byte aligned; slot_mapping may be NULL) and pa_decode_fp8_ex (format,
  * scales, the stream mode in groups of 4096 sequences, the workspace of

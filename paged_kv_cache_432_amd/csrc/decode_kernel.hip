@@ -52,7 +52,11 @@
 //     done, so that no record write lands in the middle of the read stream.
 //   * append mode (pa_decode_append): each sequence's newest token is one more
 //     unit after its cached blocks, read from its input row; the merge launch
-//     copies it to its cache slot.
+//     copies it to its cache slot.  Over an fp8 cache (pa_decode_append_fp8)
+//     the workgroup that reads a sequence's last block first stores the newest
+//     token's codes into it, and the walk is the plain one.
+//   * the split merge takes one wave per (sequence, query head), or, past one
+//     round of resident waves, two heads of a KV head per wave.
 #include <math.h>
 
 #include "device_common.h"

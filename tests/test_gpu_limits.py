@@ -3,7 +3,7 @@ oracle:
   - a cache pool larger than 4 GiB with the sequences' blocks all past the
     4 GiB mark, so every block address needs 64 bits (decode in both split
     modes, the one-call step, chunked prefill, and an fp8 cache of more than
-    4 GiB of codes);
+    4 GiB of codes, with its one-call step too);
   - exactly 4096 sequences, the most the balanced stream mode takes, next to
     4097, which moves to fixed partitions; over an fp8 cache (stream mode
     only), 8193 sequences in groups of 4096;
@@ -103,6 +103,17 @@ def test_pool_beyond_4gib_fp8(staging, fmt):
     out = dw.decode()
     torch.cuda.synchronize()
     assert_parity(to_numpy(out), _ref(w, fmt), "bf16", f"pool > 4 GiB, {fmt} decode")
+    # the one-call step on a second copy: the newest rows stored as codes at
+    # their slots (past 4 GiB) by the decode launch; slots, caches and output
+    # bit for bit as the two-call step's
+    da = staging.DeviceWorkload(w, kv_fp8=True, fp8_format=fmt)
+    out_a = da.decode_append()
+    torch.cuda.synchronize()
+    _, _, slots = da.append_rows()
+    want = [oracle.slot(w.block_table[b], int(w.seq_lens[b]) - 1) for b in range(w.num_seqs)]
+    assert slots.cpu().numpy().tolist() == want and min(want) * 8 * 128 >= GIB4
+    assert torch.equal(da.key_cache, dw.key_cache) and torch.equal(da.value_cache, dw.value_cache)
+    assert torch.equal(out_a.view(torch.int16), out.view(torch.int16))
 
 
 def test_stream_mode_limit(staging):
